@@ -1,0 +1,141 @@
+"""Python access to the plain fp64 CPU oracle (``liboracle.so``).
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the library path never does.  The oracle is
+C compiled with gcc (``build()``); it shares no source with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC = os.path.join(_HERE, "spec_oracle.c")
+
+F32, BF16 = 0, 1
+TREE_GREEDY, TREE_SAMPLING = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (OpenMP over requests, IEEE double arithmetic)."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ip = ctypes.c_void_p, ctypes.c_int
+        L.oracle_verify_greedy.argtypes = [vp, ip, vp, ip, ip, ip, vp, vp]
+        L.oracle_verify_chain.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp, vp, vp]
+        L.oracle_verify_tree.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, ip,
+                                         ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp]
+        for f in (L.oracle_verify_greedy, L.oracle_verify_chain, L.oracle_verify_tree):
+            f.restype = ctypes.c_int
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(dtype: str) -> int:
+    return BF16 if dtype == "bf16" else F32
+
+
+def _logits_array(logits, dtype):
+    want = np.uint16 if dtype == "bf16" else np.float32
+    a = np.ascontiguousarray(logits)
+    if a.dtype != want:
+        if dtype == "bf16" and a.dtype == np.int16:
+            a = a.view(np.uint16)
+        else:
+            raise TypeError(f"logits must be {want} for dtype {dtype}, got {a.dtype}")
+    return a
+
+
+def verify_greedy(logits, dtype, draft_tokens, B=None, G=None, V=None):
+    """Returns (accept_len [B], out_tokens [B][G+1])."""
+    lg = _logits_array(logits, dtype)
+    dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    B = dt.shape[0] if B is None else B
+    G = dt.shape[1] if G is None else G
+    V = lg.shape[-1] if V is None else V
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, G + 1), np.int32)
+    rc = lib().oracle_verify_greedy(_ptr(lg), _dtype_code(dtype), _ptr(dt), B, G, V,
+                                    _ptr(acc), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_greedy rejected its arguments ({rc})")
+    return acc, out
+
+
+def verify_chain(logits, dtype, draft_probs, draft_tokens, coins, temperature, *, beta=False):
+    """Returns dict(accept_len, out_tokens, probs, margin[, beta])."""
+    lg = _logits_array(logits, dtype)
+    q = np.ascontiguousarray(draft_probs, dtype=np.float32)
+    dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    cn = np.ascontiguousarray(coins, dtype=np.float32)
+    tp = np.ascontiguousarray(temperature, dtype=np.float32)
+    B, G = dt.shape
+    V = lg.shape[-1]
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, G + 1), np.int32)
+    probs = np.empty((B, G + 1), np.float64)
+    margin = np.empty(B, np.float64)
+    bt = np.empty((B, G), np.float64) if beta else None
+    rc = lib().oracle_verify_chain(_ptr(lg), _dtype_code(dtype), _ptr(q), _ptr(dt), _ptr(cn),
+                                   _ptr(tp), B, G, V, _ptr(acc), _ptr(out), _ptr(probs),
+                                   _ptr(margin), _ptr(bt))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_chain rejected its arguments ({rc})")
+    res = dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin)
+    if beta:
+        res["beta"] = bt
+    return res
+
+
+def verify_tree(logits, dtype, node_tokens, parents, coins, temperature, D, mode,
+                threshold_single=1.0, threshold_acc=1.0):
+    """Returns dict(accept_len, out_tokens, accepted_nodes, probs, margin)."""
+    lg = _logits_array(logits, dtype)
+    tk = np.ascontiguousarray(node_tokens, dtype=np.int32)
+    pa = np.ascontiguousarray(parents, dtype=np.int32)
+    cn = None if coins is None else np.ascontiguousarray(coins, dtype=np.float32)
+    tp = None if temperature is None else np.ascontiguousarray(temperature, dtype=np.float32)
+    B, N = tk.shape
+    V = lg.shape[-1]
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, D + 1), np.int32)
+    nodes = np.empty((B, D), np.int32)
+    probs = np.empty((B, D + 1), np.float64)
+    margin = np.empty(B, np.float64)
+    rc = lib().oracle_verify_tree(_ptr(lg), _dtype_code(dtype), _ptr(tk), _ptr(pa), _ptr(cn),
+                                  _ptr(tp), B, N, V, D, mode, float(threshold_single),
+                                  float(threshold_acc), _ptr(acc), _ptr(out), _ptr(nodes),
+                                  _ptr(probs), _ptr(margin))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree rejected its arguments ({rc})")
+    return dict(accept_len=acc, out_tokens=out, accepted_nodes=nodes, probs=probs,
+                margin=margin)

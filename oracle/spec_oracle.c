@@ -1,0 +1,469 @@
+/* spec_oracle.c -- plain fp64 CPU oracle of the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the library path.  Slow on purpose:
+ * scalar loops in ascending index order, double arithmetic, libm exp, no blocking.
+ *
+ * Sources (web pages on speculative decoding):
+ *   [atlas]   llm-infra-atlas, "Speculative Decoding -- lossless acceleration of
+ *             autoregressive decode": section 0 (core idea), section 2 (notation:
+ *             bonus token, correction/residual norm(max(0, p - q)), tau counts the bonus).
+ *   [ricardo] ricardokevins, "Speculative Decoding: real gains, correction sampling and
+ *             production limits": "mechanism" (draft / verify / accept / correct),
+ *             "correction sampling" with Eq. a(x) = min(1, p(x)/q(x)) and
+ *             Eq. r(x) = max(p(x) - q(x), 0) / sum_y max(p(y) - q(y), 0).
+ *   [origins] zdszero, "spec_origins": "Blockwise Parallel Decoding" (verify: accept the
+ *             longest prefix that equals the scorer's argmax, always advance >= 1 token),
+ *             "Speculative Decoding" -> acceptance rule items 1-3 (accept with prob
+ *             min(1, p/q); on rejection resample from norm(max(0, p - q)) and stop; if
+ *             all gamma accepted draw a bonus from position gamma+1), "in SGLang"
+ *             (target-only tree walk: per level, accumulate sibling target probabilities
+ *             prob_acc, accept when coin <= prob_acc / threshold_acc or a single
+ *             probability >= threshold_single; rejected children are removed from the
+ *             final distribution relu(target - draft_probs)).
+ *
+ * Readings where the pages are silent (each one is also taken by the HIP library):
+ *   - p = softmax(logits / T) with the row maximum subtracted; q arrives as fp32
+ *     probabilities at T and is used as given.
+ *   - coins lie in (0, 1]; every comparison is "coin <= threshold"; a token with p = 0 is
+ *     never accepted.
+ *   - the correction / bonus / final draw uses its own coin (chain: coins[G],
+ *     tree: coins[D]); the draw is the inverse CDF in ascending token id: the first j
+ *     with w_j > 0 and u * S <= C_j, C_j the inclusive prefix sum of w.
+ *   - if the residual mass S is not positive the draw falls back to w = p of that row.
+ *   - greedy argmax ties go to the lowest token id.
+ *   - tree: node 0 is the root, parents[i] < i, siblings are tried in ascending node id,
+ *     one coin per level coins[d] and a final coin coins[D]; a leaf draws its bonus
+ *     from its own row.
+ */
+#include "spec_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- reading the inputs ------------------------------------------------------- */
+
+typedef struct {
+    const void* base;
+    int dtype;
+    size_t offset; /* element offset of the row start */
+    int V;
+} Row;
+
+static Row row_of(const void* logits, int dtype, size_t row_index, int V) {
+    Row r;
+    r.base = logits;
+    r.dtype = dtype;
+    r.offset = row_index * (size_t)V;
+    r.V = V;
+    return r;
+}
+
+/* One logit, widened exactly to double (a bf16 value is the high half of an fp32). */
+static double logit(Row r, int x) {
+    size_t i = r.offset + (size_t)x;
+    if (r.dtype == ORACLE_F32) return (double)((const float*)r.base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t*)r.base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double row_max(Row r) {
+    double m = -INFINITY;
+    for (int x = 0; x < r.V; ++x)
+        if (logit(r, x) > m) m = logit(r, x);
+    return m;
+}
+
+/* Lowest token id attaining the row maximum (greedy reading: ties -> lowest id). */
+static int row_argmax(Row r) {
+    int best = 0;
+    for (int x = 1; x < r.V; ++x)
+        if (logit(r, x) > logit(r, best)) best = x;
+    return best;
+}
+
+/* Normaliser of the temperature softmax, Z = sum_x exp((l_x - m) / T). */
+static double row_partition(Row r, double m, double T) {
+    double Z = 0.0;
+    for (int x = 0; x < r.V; ++x) Z += exp((logit(r, x) - m) / T);
+    return Z;
+}
+
+/* Target probability p(x) = exp((l_x - m) / T) / Z. */
+static double row_prob(Row r, int x, double m, double Z, double T) {
+    return exp((logit(r, x) - m) / T) / Z;
+}
+
+static void note_margin(double* mm, double margin) {
+    if (margin < *mm) *mm = margin;
+}
+
+static int coin_ok(float u) { return u > 0.0f && u <= 1.0f; }
+
+static int temperature_ok(float T) { return isfinite(T) && T > 0.0f; }
+
+/* ---- the final draw --------------------------------------------------------------
+ * Inverse CDF over w (probability units): t = u * S, the first token with positive weight
+ * whose inclusive prefix reaches t.  The distances of t to both ends of the chosen bucket
+ * are recorded as margins.  If rounding left t beyond the last bucket the last token with
+ * positive weight is returned and a zero margin recorded. */
+static int draw_inverse_cdf(const double* w, int V, double u, double* mm) {
+    double S = 0.0;
+    for (int j = 0; j < V; ++j) S += w[j];
+    double t = u * S;
+    double C = 0.0;
+    int last = -1;
+    for (int j = 0; j < V; ++j) {
+        if (w[j] > 0.0) {
+            double before = C;
+            C += w[j];
+            last = j;
+            if (t <= C) {
+                note_margin(mm, t - before);
+                note_margin(mm, C - t);
+                return j;
+            }
+        }
+    }
+    note_margin(mm, 0.0);
+    return last;
+}
+
+/* ---- greedy chain ------------------------------------------------------------------
+ * [origins] Blockwise Parallel Decoding, verify: the scorer checks the k proposals in
+ * parallel and keeps the longest prefix that agrees with its own argmax, so every step
+ * advances by at least one token and the result equals token-by-token greedy decoding.
+ * The token emitted after the prefix is the scorer's argmax at the first mismatch (or
+ * at position G+1 when every proposal matched). */
+static void greedy_one(const void* logits, int dtype, const int32_t* draft, int G, int V,
+                       size_t b, int32_t* accept_len, int32_t* out) {
+    int R = G + 1;
+    int valid = 1;
+    for (int i = 0; i < G; ++i)
+        if (draft[i] < 0 || draft[i] >= V) valid = 0;
+    for (int i = 0; i < R && valid; ++i)
+        if (row_max(row_of(logits, dtype, b * (size_t)R + (size_t)i, V)) == -INFINITY) valid = 0;
+    if (!valid) {
+        *accept_len = -1;
+        for (int i = 0; i < R; ++i) out[i] = -1;
+        return;
+    }
+    int k = G;
+    for (int i = 0; i < G; ++i) {
+        int a = row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)i, V));
+        if (draft[i] != a) {
+            k = i;
+            break;
+        }
+    }
+    for (int i = 0; i < k; ++i) out[i] = draft[i];
+    out[k] = row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)k, V));
+    for (int i = k + 1; i < R; ++i) out[i] = -1;
+    *accept_len = k;
+}
+
+int oracle_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
+                         int B, int G, int V, int32_t* accept_len, int32_t* out_tokens) {
+    if (!logits || !draft_tokens || !accept_len || !out_tokens) return -1;
+    if (B < 0 || G < 1 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        greedy_one(logits, dtype, draft_tokens + (size_t)b * G, G, V, (size_t)b,
+                   accept_len + b, out_tokens + (size_t)b * (G + 1));
+    return 0;
+}
+
+/* ---- chain rejection sampling --------------------------------------------------------
+ * [origins] acceptance rule: (1) accept x ~ q with probability min(1, p(x)/q(x));
+ * (2) at the first rejection resample from p' = norm(max(0, p - q)) and stop;
+ * (3) when all gamma drafts are accepted, draw a bonus token from position gamma+1.
+ * [ricardo] correction sampling: Eq. a(x) and Eq. r(x) state the same two steps.
+ * With coin u_i the test "accept with probability min(1, p/q)" reads u_i <= p/q. */
+static void chain_one(const void* logits, int dtype, const float* q, const int32_t* draft,
+                      const float* coins, float temperature, int G, int V, size_t b,
+                      int32_t* accept_len, int32_t* out, double* probs, double* margin,
+                      double* beta, double* w) {
+    int R = G + 1;
+    double T = (double)temperature;
+    double m[R > 0 ? R : 1], Z[R > 0 ? R : 1];
+    int valid = temperature_ok(temperature);
+    for (int i = 0; i < G; ++i)
+        if (draft[i] < 0 || draft[i] >= V) valid = 0;
+    for (int i = 0; i < R; ++i)
+        if (!coin_ok(coins[i])) valid = 0;
+    for (int i = 0; i < R && valid; ++i) {
+        m[i] = row_max(row_of(logits, dtype, b * (size_t)R + (size_t)i, V));
+        if (m[i] == -INFINITY) valid = 0;
+    }
+    for (int i = 0; i < G && valid; ++i) {
+        float qx = q[(size_t)i * V + (size_t)draft[i]];
+        if (!(qx >= 0.0f) || !isfinite(qx)) valid = 0;
+    }
+    *margin = INFINITY;
+    if (!valid) {
+        *accept_len = -1;
+        for (int i = 0; i < R; ++i) out[i] = -1;
+        if (probs)
+            for (int i = 0; i < R; ++i) probs[i] = 0.0;
+        if (beta)
+            for (int i = 0; i < G; ++i) beta[i] = 0.0;
+        return;
+    }
+    for (int i = 0; i < R; ++i)
+        Z[i] = row_partition(row_of(logits, dtype, b * (size_t)R + (size_t)i, V), m[i], T);
+
+    if (beta) { /* beta_i = sum_x min(p_i(x), q_i(x)): per-position acceptance rate */
+        for (int i = 0; i < G; ++i) {
+            Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
+            double s = 0.0;
+            for (int x = 0; x < V; ++x) {
+                double p = row_prob(r, x, m[i], Z[i], T);
+                double qq = (double)q[(size_t)i * V + (size_t)x];
+                s += p < qq ? p : qq;
+            }
+            beta[i] = s;
+        }
+    }
+
+    int k = G;
+    double pacc[R > 0 ? R : 1];
+    for (int i = 0; i < G; ++i) {
+        Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
+        int x = draft[i];
+        double p = row_prob(r, x, m[i], Z[i], T);
+        double qx = (double)q[(size_t)i * V + (size_t)x];
+        double u = (double)coins[i];
+        int accept;
+        if (qx > 0.0) {
+            double ratio = p / qx;
+            note_margin(margin, fabs(u - ratio));
+            accept = p > 0.0 && u <= ratio;
+        } else {
+            accept = p > 0.0; /* q(x) = 0 < p(x): ratio is +inf */
+        }
+        if (!accept) {
+            k = i;
+            break;
+        }
+        pacc[i] = p;
+    }
+
+    /* Weights of the final draw: residual max(0, p_k - q_k) after a rejection, the
+     * target row G itself for the bonus. */
+    Row rk = row_of(logits, dtype, b * (size_t)R + (size_t)k, V);
+    double S = 0.0;
+    for (int x = 0; x < V; ++x) {
+        double p = row_prob(rk, x, m[k], Z[k], T);
+        if (k < G) {
+            double d = p - (double)q[(size_t)k * V + (size_t)x];
+            w[x] = d > 0.0 ? d : 0.0;
+        } else {
+            w[x] = p;
+        }
+        S += w[x];
+    }
+    if (k < G) note_margin(margin, S);
+    if (!(S > 0.0))
+        for (int x = 0; x < V; ++x) w[x] = row_prob(rk, x, m[k], Z[k], T);
+    int y = draw_inverse_cdf(w, V, (double)coins[G], margin);
+
+    for (int i = 0; i < k; ++i) out[i] = draft[i];
+    out[k] = y;
+    for (int i = k + 1; i < R; ++i) out[i] = -1;
+    *accept_len = k;
+    if (probs) {
+        for (int i = 0; i < k; ++i) probs[i] = pacc[i];
+        probs[k] = row_prob(rk, y, m[k], Z[k], T);
+        for (int i = k + 1; i < R; ++i) probs[i] = 0.0;
+    }
+}
+
+int oracle_verify_chain(const void* logits, int dtype, const float* draft_probs,
+                        const int32_t* draft_tokens, const float* coins,
+                        const float* temperature, int B, int G, int V,
+                        int32_t* accept_len, int32_t* out_tokens, double* probs_out,
+                        double* min_margin, double* beta_out) {
+    if (!logits || !draft_probs || !draft_tokens || !coins || !temperature || !accept_len ||
+        !out_tokens || !min_margin)
+        return -1;
+    if (B < 0 || G < 1 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    int R = G + 1;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; ++b)
+            chain_one(logits, dtype, draft_probs + (size_t)b * G * V, draft_tokens + (size_t)b * G,
+                      coins + (size_t)b * R, temperature[b], G, V, (size_t)b, accept_len + b,
+                      out_tokens + (size_t)b * R, probs_out ? probs_out + (size_t)b * R : NULL,
+                      min_margin + b, beta_out ? beta_out + (size_t)b * G : NULL, w);
+        free(w);
+    }
+    return 0;
+}
+
+/* ---- token tree, target only ----------------------------------------------------------
+ * [origins] "in SGLang": walk down the tree; at each level add up the target
+ * probabilities of the siblings tried so far (prob_acc) and accept a child when
+ * coin <= prob_acc / threshold_acc or its own probability >= threshold_single (both
+ * thresholds 1.0 by default, which amounts to drawing one child from the target
+ * distribution and checking whether it is on the tree).  A rejected child's target
+ * probability is written into draft_probs, and the final token is drawn from
+ * relu(target - draft_probs): the children tried and rejected at the last level are
+ * removed.  At a leaf nothing was rejected and the draw is from the leaf's own row.
+ * [origins] SpecInfer: the tree is flattened, each node sees only its ancestors; here the
+ * ancestry is the parent array and row j holds the target distribution after node j.
+ * Greedy mode follows the child whose token equals the argmax of the current row. */
+static void tree_one(const void* logits, int dtype, const int32_t* tok, const int32_t* par,
+                     const float* coins, float temperature, int N, int V, int D, int mode,
+                     double th_single, double th_acc, size_t b, int32_t* accept_len,
+                     int32_t* out, int32_t* nodes, double* probs, double* margin, double* w,
+                     int* depth, int32_t* excl) {
+    int sampling = mode == ORACLE_TREE_SAMPLING;
+    int valid = par[0] == -1;
+    depth[0] = 0;
+    for (int i = 1; i < N && valid; ++i) {
+        if (par[i] < 0 || par[i] >= i) {
+            valid = 0;
+            break;
+        }
+        depth[i] = depth[par[i]] + 1;
+        if (depth[i] > D) valid = 0;
+        if (tok[i] < 0 || tok[i] >= V) valid = 0;
+    }
+    if (sampling) {
+        if (!temperature_ok(temperature)) valid = 0;
+        for (int d = 0; d <= D; ++d)
+            if (!coin_ok(coins[d])) valid = 0;
+    }
+    for (int j = 0; j < N && valid; ++j)
+        if (row_max(row_of(logits, dtype, b * (size_t)N + (size_t)j, V)) == -INFINITY) valid = 0;
+    *margin = INFINITY;
+    if (!valid) {
+        *accept_len = -1;
+        for (int d = 0; d <= D; ++d) out[d] = -1;
+        for (int d = 0; d < D; ++d) nodes[d] = -1;
+        if (probs)
+            for (int d = 0; d <= D; ++d) probs[d] = 0.0;
+        return;
+    }
+
+    double T = (double)temperature;
+    int cur = 0, d = 0, nexcl = 0;
+    for (;;) {
+        Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
+        int any_child = 0;
+        for (int c = cur + 1; c < N; ++c)
+            if (par[c] == cur) any_child = 1;
+        if (!any_child) break; /* leaf: bonus from its own row */
+        int chosen = -1;
+        double pchosen = 0.0;
+        if (!sampling) {
+            int a = row_argmax(r);
+            for (int c = cur + 1; c < N; ++c)
+                if (par[c] == cur && tok[c] == a) {
+                    chosen = c;
+                    break;
+                }
+        } else {
+            double m = row_max(r), Z = row_partition(r, m, T);
+            double u = (double)coins[d];
+            double acc = 0.0;
+            nexcl = 0;
+            for (int c = cur + 1; c < N; ++c) {
+                if (par[c] != cur) continue;
+                double pc = row_prob(r, tok[c], m, Z, T);
+                acc += pc;
+                note_margin(margin, fabs(u - acc / th_acc));
+                note_margin(margin, fabs(pc - th_single));
+                if (u <= acc / th_acc || pc >= th_single) {
+                    chosen = c;
+                    pchosen = pc;
+                    break;
+                }
+                excl[nexcl++] = tok[c];
+            }
+        }
+        if (chosen < 0) break;
+        out[d] = tok[chosen];
+        nodes[d] = chosen;
+        if (probs) probs[d] = pchosen;
+        cur = chosen;
+        ++d;
+        nexcl = 0;
+    }
+
+    Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
+    int y;
+    double py = 0.0;
+    if (!sampling) {
+        y = row_argmax(r);
+    } else {
+        double m = row_max(r), Z = row_partition(r, m, T);
+        double S = 0.0;
+        for (int x = 0; x < V; ++x) w[x] = row_prob(r, x, m, Z, T);
+        for (int e = 0; e < nexcl; ++e) w[excl[e]] = 0.0;
+        for (int x = 0; x < V; ++x) S += w[x];
+        if (nexcl > 0) note_margin(margin, S);
+        if (!(S > 0.0))
+            for (int x = 0; x < V; ++x) w[x] = row_prob(r, x, m, Z, T);
+        y = draw_inverse_cdf(w, V, (double)coins[D], margin);
+        py = row_prob(r, y, m, Z, T);
+    }
+    out[d] = y;
+    if (probs) probs[d] = py;
+    for (int e = d + 1; e <= D; ++e) out[e] = -1;
+    for (int e = d; e < D; ++e) nodes[e] = -1;
+    if (probs)
+        for (int e = d + 1; e <= D; ++e) probs[e] = 0.0;
+    *accept_len = d;
+}
+
+int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
+                       const int32_t* parents, const float* coins, const float* temperature,
+                       int B, int N, int V, int D, int mode, float threshold_single,
+                       float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
+                       int32_t* accepted_nodes, double* probs_out, double* min_margin) {
+    if (!logits || !node_tokens || !parents || !accept_len || !out_tokens || !accepted_nodes ||
+        !min_margin)
+        return -1;
+    if (B < 0 || N < 1 || V < 1 || D < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (mode != ORACLE_TREE_GREEDY && mode != ORACLE_TREE_SAMPLING) return -1;
+    if (mode == ORACLE_TREE_SAMPLING &&
+        (!coins || !temperature || !(threshold_single > 0.0f) || !(threshold_acc > 0.0f)))
+        return -1;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)V);
+        int* depth = (int*)malloc(sizeof(int) * (size_t)N);
+        int32_t* excl = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; ++b)
+            tree_one(logits, dtype, node_tokens + (size_t)b * N, parents + (size_t)b * N,
+                     coins ? coins + (size_t)b * (D + 1) : NULL,
+                     temperature ? temperature[b] : 1.0f, N, V, D, mode,
+                     (double)threshold_single, (double)threshold_acc, (size_t)b,
+                     accept_len + b, out_tokens + (size_t)b * (D + 1),
+                     accepted_nodes + (size_t)b * D,
+                     probs_out ? probs_out + (size_t)b * (D + 1) : NULL, min_margin + b, w,
+                     depth, excl);
+        free(w);
+        free(depth);
+        free(excl);
+    }
+    return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,65 @@
+/* spec_oracle.h -- plain fp64 CPU oracle of the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  It shares no source with the HIP
+ * library: no header, helper, table or constant.
+ *
+ * All pointers are host pointers.  Logits are stored row-major [B][R][V] as fp32
+ * (dtype 0) or as raw bf16 bit patterns (dtype 1).  Everything is widened to double;
+ * sums run sequentially in ascending index order; exp() is libm's double exp.
+ *
+ * min_margin[b] receives the smallest distance, in probability units, between a coin
+ * and the threshold it was compared against along request b's decision trace (the
+ * accept tests, the tree's sibling tests and the final inverse-CDF step), or +inf when
+ * no coin decided anything (greedy).  A request whose margin is below a small band can
+ * legitimately come out differently under another rounding order.
+ *
+ * Invalid requests (a token outside [0,V), a temperature that is not finite and > 0, a
+ * coin outside (0,1], a row whose maximum is -inf, a drafted token whose q is negative
+ * or not finite, a malformed parent array or a node deeper than D) get accept_len = -1
+ * and every output slot of the request set to -1 (tokens, nodes) or 0 (probs).
+ *
+ * Return value: 0, or -1 if an argument is unusable (NULL pointer, non-positive size).
+ */
+#ifndef SPEC_ORACLE_H
+#define SPEC_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_TREE_GREEDY 0
+#define ORACLE_TREE_SAMPLING 1
+
+/* Greedy chain verify: accept the longest draft prefix equal to the target argmax,
+ * then emit the target argmax at the first mismatch (or at position G). */
+int oracle_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
+                         int B, int G, int V, int32_t* accept_len, int32_t* out_tokens);
+
+/* Chain rejection sampling.  probs_out [B][G+1] (may be NULL): target probability of each
+ * emitted token under the row it was emitted from, 0 past the last emitted token.
+ * beta_out [B][G] (may be NULL): beta_i = sum_x min(p_i(x), q_i(x)) per drafted position. */
+int oracle_verify_chain(const void* logits, int dtype, const float* draft_probs,
+                        const int32_t* draft_tokens, const float* coins,
+                        const float* temperature, int B, int G, int V,
+                        int32_t* accept_len, int32_t* out_tokens, double* probs_out,
+                        double* min_margin, double* beta_out);
+
+/* Token-tree verify, target-only.  mode 0 = greedy, mode 1 = sampling.
+ * out_tokens [B][D+1], accepted_nodes [B][D], probs_out [B][D+1] (may be NULL). */
+int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
+                       const int32_t* parents, const float* coins, const float* temperature,
+                       int B, int N, int V, int D, int mode, float threshold_single,
+                       float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
+                       int32_t* accepted_nodes, double* probs_out, double* min_margin);
+
+/* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,97 @@
+"""The oracle's pins catch plausible mistakes (mutation test, CPU only).
+
+Each mutant is a copy of the oracle source with one plausible slip planted in it (a
+transposed operand, a wrong sign, a dropped term, an off-by-one row, a reused coin,
+...).  It is compiled into a temporary directory and swapped in for the real library;
+at least one pin from the law, closed-form, special-case or golden tests must then fail.
+The real oracle is restored afterwards.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+
+import test_golden_cases as golden
+import test_oracle_law as law
+import test_oracle_tree_greedy as tg
+
+SRC = open(oracle.SRC).read()
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("ratio transposed", "double ratio = p / qx;", "double ratio = qx / p;"),
+    ("residual sign flipped", "double d = p - (double)q[(size_t)k * V + (size_t)x];",
+     "double d = (double)q[(size_t)k * V + (size_t)x] - p;"),
+    ("residual replaced by p", "w[x] = d > 0.0 ? d : 0.0;", "w[x] = p; (void)d;"),
+    ("final draw from the row before",
+     "Row rk = row_of(logits, dtype, b * (size_t)R + (size_t)k, V);",
+     "Row rk = row_of(logits, dtype, b * (size_t)R + (size_t)(k > 0 ? k - 1 : 0), V);"),
+    ("rejection coin reused for the draw", "int y = draw_inverse_cdf(w, V, (double)coins[G], margin);",
+     "int y = draw_inverse_cdf(w, V, (double)coins[k], margin);"),
+    ("temperature ignored", "for (int x = 0; x < r.V; ++x) Z += exp((logit(r, x) - m) / T);",
+     "for (int x = 0; x < r.V; ++x) Z += exp((logit(r, x) - m));"),
+    ("partition misses token 0", "for (int x = 0; x < r.V; ++x) Z += exp(",
+     "for (int x = 1; x < r.V; ++x) Z += exp("),
+    ("argmax ties to highest id", "if (logit(r, x) > logit(r, best)) best = x;",
+     "if (logit(r, x) >= logit(r, best)) best = x;"),
+    ("greedy emits the draft at the mismatch",
+     "out[k] = row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)k, V));",
+     "out[k] = k < G ? draft[k] : row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)k, V));"),
+    ("bucket edge exclusive", "if (t <= C) {", "if (t < C) {"),
+    ("tree prob_acc not accumulated", "acc += pc;", "acc = pc;"),
+    ("tree exclusions dropped", "for (int e = 0; e < nexcl; ++e) w[excl[e]] = 0.0;", ""),
+    ("tree coin of level 0 reused", "double u = (double)coins[d];", "double u = (double)coins[0];"),
+    ("tree greedy follows first child", "par[c] == cur && tok[c] == a", "par[c] == cur"),
+    ("accept test on q instead of p", "accept = p > 0.0 && u <= ratio;", "accept = u <= qx;"),
+]
+
+
+def _pins():
+    """Callables that raise AssertionError when a pin fails."""
+    yield lambda: law.test_chain_round_emits_target_law(0, 0.0, 1.0)
+    yield lambda: law.test_chain_round_emits_target_law(2, 0.0, 0.7)
+    yield law.test_chain_acceptance_rate_and_residual_law
+    yield lambda: law.test_expected_tokens_closed_form(22, 3)
+    yield lambda: law.test_probs_match_scipy_softmax("bf16", 0.7)
+    yield law.test_bonus_draw_is_inverse_cdf
+    yield law.test_degenerate_p_q_cases
+    yield lambda: tg.test_greedy_chain_equals_autoregressive(1, 4, 0.7)
+    yield tg.test_greedy_ties_go_to_lowest_id
+    yield tg.test_greedy_tree_equals_autoregressive
+    yield lambda: tg.test_tree_walk_emits_target_law(0, 1.0)
+    yield lambda: tg.test_tree_walk_emits_target_law(1, 1.0)
+    yield tg.test_tree_rejected_children_are_removed_from_final_draw
+    for case in golden.CASES["chain"]:
+        yield lambda case=case: golden.test_chain_hand_case(case)
+    for case in golden.CASES["tree"]:
+        yield lambda case=case: golden.test_tree_hand_case(case)
+
+
+@pytest.mark.parametrize("name,orig,mutation", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, orig, mutation, tmp_path):
+    assert SRC.count(orig) == 1, f"mutation anchor not unique/found: {orig}"
+    src = tmp_path / "spec_oracle.c"
+    src.write_text(SRC.replace(orig, mutation))
+    hdr = os.path.join(os.path.dirname(oracle.SRC), "spec_oracle.h")
+    (tmp_path / "spec_oracle.h").write_text(open(hdr).read())
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-w", "-o", str(so), str(src), "-lm"], check=True)
+    saved_lib, saved_path = oracle._lib, oracle.LIB_PATH
+    try:
+        oracle._lib = None
+        oracle.LIB_PATH = str(so)
+        caught = []
+        for pin in _pins():
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                caught.append(pin)
+                break
+        assert caught, f"no pin caught mutant '{name}'"
+    finally:
+        oracle._lib, oracle.LIB_PATH = saved_lib, saved_path

@@ -1,0 +1,257 @@
+"""Pins of the oracle's greedy verify and token-tree walk (CPU only).
+
+  - greedy verify keeps exactly what token-by-token greedy decoding would produce
+    (zdszero spec_origins, "Blockwise Parallel Decoding", verify), checked against a
+    numpy argmax decode of a toy LM, for chains and for trees;
+  - the target-only tree walk with both thresholds at 1.0 amounts to drawing a child from
+    the target distribution and checking it is on the tree (spec_origins, "in SGLang"),
+    so the first emitted token follows the root row and each later token follows the row
+    of the node it extends: checked exactly over the coin lattice;
+  - a chain-shaped tree with target-only sampling equals chain verify with one-hot draft
+    distributions (two independent code paths of the oracle, bit for bit);
+  - invalid inputs give accept_len = -1 and padded rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from lossless_rejection_sampling_verify_amd import workloads as wl
+
+import lawengine as le
+
+
+def softmax64(x, T=1.0):
+    return scipy.special.softmax(np.asarray(x, np.float64) / T, axis=-1)
+
+
+# ----------------------------------------------------------------------------------
+# greedy == autoregressive argmax
+
+class HashLM:
+    """Deterministic prefix -> logits map with deliberate ties (small integer logits)."""
+
+    def __init__(self, V, seed, levels=6):
+        self.V, self.seed, self.levels = V, seed, levels
+
+    def logits(self, prefix):
+        rng = np.random.default_rng([self.seed, len(prefix)] + list(prefix))
+        return rng.integers(0, self.levels, size=self.V).astype(np.float32)
+
+
+def ar_greedy(lm, n):
+    seq = []
+    while len(seq) < n:
+        seq.append(int(np.argmax(lm.logits(tuple(seq)))))   # numpy: first maximum
+    return seq
+
+
+@pytest.mark.parametrize("seed,G,hit", [(0, 4, 0.0), (1, 4, 0.7), (2, 8, 0.9), (3, 1, 0.5)])
+def test_greedy_chain_equals_autoregressive(seed, G, hit):
+    lm = HashLM(V=7, seed=seed)
+    n = 40
+    ref = ar_greedy(lm, n + G + 1)
+    rng = np.random.default_rng(100 + seed)
+    seq, rounds = [], 0
+    while len(seq) < n:
+        # drafts: the true continuation with probability `hit`, otherwise a random token
+        x = [ref[len(seq) + i] if rng.random() < hit else int(rng.integers(0, lm.V))
+             for i in range(G)]
+        rows = np.stack([lm.logits(tuple(seq) + tuple(x[:i])) for i in range(G + 1)])
+        acc, out = oracle.verify_greedy(rows[None], "f32", np.array([x], np.int32))
+        k = int(acc[0])
+        assert 0 <= k <= G
+        seq.extend(int(t) for t in out[0, : k + 1])
+        rounds += 1
+    assert seq[:n] == ref[:n]
+    if hit == 0.0:
+        assert rounds >= n // 2
+
+
+def test_greedy_tree_equals_autoregressive():
+    lm = HashLM(V=6, seed=9)
+    n = 30
+    ref = ar_greedy(lm, n + 10)
+    rng = np.random.default_rng(7)
+    seq = []
+    while len(seq) < n:
+        # a random tree of depth <= 3 whose first branch may follow the true continuation
+        N, D = 9, 3
+        parents = [-1, 0, 0, 1, 1, 2, 3, 3, 5]
+        tokens = [-1] * N
+        prefix_of = {0: ()}
+        for c in range(1, N):
+            sib = [s for s in range(1, c) if parents[s] == parents[c]]
+            used = {tokens[s] for s in sib}
+            pos = len(seq) + len(prefix_of[parents[c]])
+            want = ref[pos] if rng.random() < 0.6 else int(rng.integers(0, lm.V))
+            if want in used:
+                want = next(t for t in range(lm.V) if t not in used)
+            tokens[c] = want
+            prefix_of[c] = prefix_of[parents[c]] + (want,)
+        rows = np.stack([lm.logits(tuple(seq) + prefix_of[j]) for j in range(N)])
+        r = oracle.verify_tree(rows[None], "f32", np.array([tokens], np.int32),
+                               np.array([parents], np.int32), None, None, D,
+                               oracle.TREE_GREEDY)
+        k = int(r["accept_len"][0])
+        seq.extend(int(t) for t in r["out_tokens"][0, : k + 1])
+    assert seq[:n] == ref[:n]
+
+
+def test_greedy_ties_go_to_lowest_id():
+    B, G, V = 64, 3, 40
+    rng = np.random.default_rng(3)
+    logits = rng.integers(0, 3, size=(B, G + 1, V)).astype(np.float32)   # many ties
+    want = np.argmax(logits, axis=-1)                                      # first maximum
+    drafts = want[:, :G].copy()
+    flip = rng.random((B, G)) < 0.3
+    drafts[flip] = (drafts[flip] + 1) % V
+    acc, out = oracle.verify_greedy(logits, "f32", drafts.astype(np.int32))
+    for b in range(B):
+        mism = np.nonzero(drafts[b] != want[b, :G])[0]
+        k = int(mism[0]) if len(mism) else G
+        assert acc[b] == k
+        assert list(out[b, :k]) == list(drafts[b, :k])
+        assert out[b, k] == want[b, k]
+        assert (out[b, k + 1:] == -1).all()
+
+
+# ----------------------------------------------------------------------------------
+# target-only tree walk: exact law
+
+TREES = [
+    # parents, tokens (siblings distinct), D
+    ([-1, 0, 0, 0, 1, 1, 2], [-1, 3, 0, 5, 1, 4, 2], 2),
+    ([-1, 0, 1, 2, 0, 4, 1], [-1, 2, 2, 2, 1, 0, 3], 3),
+    ([-1, 0], [-1, 4], 1),
+]
+
+
+@pytest.mark.parametrize("tree", range(len(TREES)))
+@pytest.mark.parametrize("T", [1.0, 0.8])
+def test_tree_walk_emits_target_law(tree, T):
+    parents, tokens, D = TREES[tree]
+    N, V = len(parents), 6
+    rng = np.random.default_rng(40 + tree)
+    logits = (rng.standard_normal((N, V)) * 1.5).astype(np.float32)
+    p = softmax64(logits, float(np.float32(T)))
+    law = le.tree_law(logits, "f32", tokens, parents, T, D)
+    assert abs(sum(law.values()) - 1.0) < 1e-6
+    # first emitted token ~ root row
+    first = np.zeros(V)
+    for out, pr in law.items():
+        first[out[1]] += pr
+    np.testing.assert_allclose(first, p[0], atol=2e-6)
+    # token j+1 given the accepted node path ~ row of the last accepted node
+    cond = {}
+    for out, pr in law.items():
+        k = out[0]
+        toks, nodes = out[1: 2 + k], out[2 + k:]
+        for j in range(k):
+            cond.setdefault(nodes[: j + 1], np.zeros(V))[toks[j + 1]] += pr
+    for nodes, dist in cond.items():
+        if dist.sum() < 1e-3:
+            continue
+        np.testing.assert_allclose(dist / dist.sum(), p[nodes[-1]], atol=1e-5 / dist.sum())
+
+
+def test_tree_rejected_children_are_removed_from_final_draw():
+    """All children rejected: the final token never equals a tried sibling, and follows
+    p restricted to the non-child tokens."""
+    parents, tokens, D = [-1, 0, 0, 0], [-1, 1, 3, 4], 1
+    V = 6
+    rng = np.random.default_rng(5)
+    logits = (rng.standard_normal((4, V))).astype(np.float32)
+    p = softmax64(logits)[0]
+    law = le.tree_law(logits, "f32", tokens, parents, 1.0, D)
+    stop = {out[1]: pr for out, pr in law.items() if out[0] == 0}
+    assert not ({1, 3, 4} & set(stop))
+    mass = 1.0 - p[[1, 3, 4]].sum()
+    for t in (0, 2, 5):
+        assert abs(stop[t] - p[t]) < 2e-6            # = mass * p_t / mass
+    assert abs(sum(stop.values()) - mass) < 2e-6
+
+
+# ----------------------------------------------------------------------------------
+# chain-shaped tree == chain with one-hot drafts (independent oracle paths)
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1.0), ("bf16", 0.7)])
+def test_chain_shaped_tree_equals_chain_one_hot(dtype, T):
+    c = wl.make_chain(2, seed=31, B=64, G=5, V=3000, dtype=dtype, T=T)
+    B, G, V = c.B, c.G, c.V
+    q1 = np.zeros((B, G, V), np.float32)
+    for i in range(G):
+        q1[np.arange(B), i, c.draft_tokens[:, i]] = 1.0
+    rc = oracle.verify_chain(c.logits, c.dtype, q1, c.draft_tokens, c.coins, c.temperature)
+    parents = np.tile(np.arange(-1, G, dtype=np.int32), (B, 1))
+    tokens = np.concatenate([np.full((B, 1), -1, np.int32), c.draft_tokens], 1)
+    rt = oracle.verify_tree(c.logits, c.dtype, tokens, parents, c.coins, c.temperature, G,
+                            oracle.TREE_SAMPLING)
+    np.testing.assert_array_equal(rc["accept_len"], rt["accept_len"])
+    np.testing.assert_array_equal(rc["out_tokens"], rt["out_tokens"])
+    for b in range(B):
+        k = rt["accept_len"][b]
+        assert list(rt["accepted_nodes"][b, :k]) == list(range(1, k + 1))
+    np.testing.assert_allclose(rc["probs"], rt["probs"], rtol=1e-14, atol=0)
+    # greedy: chain-shaped greedy tree == greedy chain
+    ga, go = oracle.verify_greedy(c.logits, c.dtype, c.greedy_tokens)
+    tokens_g = np.concatenate([np.full((B, 1), -1, np.int32), c.greedy_tokens], 1)
+    rg = oracle.verify_tree(c.logits, c.dtype, tokens_g, parents, None, None, G,
+                            oracle.TREE_GREEDY)
+    np.testing.assert_array_equal(ga, rg["accept_len"])
+    np.testing.assert_array_equal(go, rg["out_tokens"])
+
+
+def test_threshold_single_accepts_dominant_child():
+    """threshold_single < 1: a child whose own probability reaches it is always accepted."""
+    parents, tokens, D = [-1, 0, 0], [-1, 1, 2], 1
+    logits = np.array([[0.0, 0.0, 4.0, 0.0], [0, 0, 0, 0], [0, 0, 0, 0]], np.float32)
+    p2 = softmax64(logits[0])[2]
+    assert p2 > 0.9
+    coins = np.array([[1.0, 0.5]], np.float32)       # coin 1.0: no cumulative acceptance
+    r = oracle.verify_tree(logits[None], "f32", np.array([tokens], np.int32),
+                           np.array([parents], np.int32), coins, np.ones(1, np.float32), D,
+                           oracle.TREE_SAMPLING, threshold_single=0.9, threshold_acc=2.0)
+    assert r["accept_len"][0] == 1 and r["accepted_nodes"][0, 0] == 2
+
+
+# ----------------------------------------------------------------------------------
+# invalid inputs
+
+def test_invalid_requests_are_flagged():
+    c = wl.make_chain(2, seed=2, B=8, G=3, V=100)
+    lg, q, x, u, T = (c.logits.copy(), c.draft_probs.copy(), c.draft_tokens.copy(),
+                      c.coins.copy(), c.temperature.copy())
+    x[1, 2] = 100                 # token out of range
+    T[2] = 0.0                    # temperature not > 0
+    u[3, 0] = 0.0                 # coin outside (0, 1]
+    lg[4, 3, :] = -np.inf         # a row with no finite logit
+    q[5, 1, x[5, 1]] = np.nan     # q of a drafted token not finite
+    T[6] = np.inf
+    r = oracle.verify_chain(lg, c.dtype, q, x, u, T)
+    bad = [1, 2, 3, 4, 5, 6]
+    assert (r["accept_len"][bad] == -1).all()
+    assert (r["out_tokens"][bad] == -1).all()
+    assert (r["probs"][bad] == 0).all()
+    assert (r["accept_len"][[0, 7]] >= 0).all()
+    ga, go = oracle.verify_greedy(lg, c.dtype, x)
+    assert ga[1] == -1 and ga[4] == -1 and (go[[1, 4]] == -1).all()
+    assert ga[2] >= 0               # greedy ignores temperature and coins
+
+    t = wl.make_tree(4, seed=1, B=6, N=12, V=200, D=3, max_children=4)
+    par, tok, cn = t.parents.copy(), t.node_tokens.copy(), t.coins.copy()
+    par[1, 5] = 5                 # parent not before the node
+    tok[2, 3] = -2                # token out of range
+    par[3, 0] = 0                 # root must have parent -1
+    cn[4, 3] = 1.5                # coin outside (0, 1]
+    r = oracle.verify_tree(t.logits, t.dtype, tok, par, cn, t.temperature, t.D,
+                           oracle.TREE_SAMPLING)
+    assert (r["accept_len"][[1, 2, 3, 4]] == -1).all()
+    assert (r["out_tokens"][[1, 2, 3, 4]] == -1).all()
+    assert (r["accepted_nodes"][[1, 2, 3, 4]] == -1).all()
+    assert (r["accept_len"][[0, 5]] >= 0).all()
+    r2 = oracle.verify_tree(t.logits, t.dtype, t.node_tokens, t.parents, None, None, 2,
+                            oracle.TREE_GREEDY)          # depth 3 > D = 2
+    assert (r2["accept_len"] == -1).all()
