@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched speculative-decoding verify step on one MI355X.
+
+One step = one pass of the whole chain/greedy verify path over the large-batch workload
+(B=256 requests, gamma=4, V=152064, bf16 target logits ~ N(0, 3^2), draft = target +
+N(0,1), T=1): spec_verify_greedy and spec_verify_chain on the same batch.  Inputs are
+synthetic, seeded, and resident in HBM before timing starts; three copies rotate so
+consecutive steps never find the logits in the 256 MB Infinity Cache.
+
+Prints ONE JSON line: verified positions/s (whole step), the roofline of the dominant
+kernel (HBM bytes per launch / launch time measured with HIP events on the launch
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD published peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 5])
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--tree", action="store_true", help="also time the tree workload")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the verify path is single-GPU here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lossless_rejection_sampling_verify_amd as pkg
+    from lossless_rejection_sampling_verify_amd import _lib as L
+    from lossless_rejection_sampling_verify_amd import api
+    from lossless_rejection_sampling_verify_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    c = wl.make_chain(args.workload)
+    gen_s = time.time() - t0
+    B, G, V, R = c.B, c.G, c.V, c.R
+    esize = 2 if c.dtype == wl.BF16 else 4
+
+    def logits_dev(a):
+        a = np.ascontiguousarray(a)
+        if c.dtype == wl.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    base = dict(logits=logits_dev(c.logits), q=torch.from_numpy(c.draft_probs).to(dev),
+                x=torch.from_numpy(c.draft_tokens).to(dev), xg=torch.from_numpy(c.greedy_tokens).to(dev),
+                u=torch.from_numpy(c.coins).to(dev), T=torch.from_numpy(c.temperature).to(dev))
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.copies - 1)]
+    ws_g = api.workspace(L.SPEC_OP_GREEDY, B, R, V, dev)
+    ws_c = api.workspace(L.SPEC_OP_CHAIN, B, R, V, dev)
+    out_g = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, R, dtype=torch.int32, device=dev))
+    out_c = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, R, dtype=torch.int32, device=dev),
+             torch.empty(B, R, dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        d = copies[i % len(copies)]
+        if ev is not None:
+            ev[0].record(stream)
+        api.spec_verify_greedy(d["logits"], d["xg"], ws=ws_g, out=out_g)
+        if ev is not None:
+            ev[1].record(stream)
+        api.spec_verify_chain(d["logits"], d["q"], d["x"], d["u"], d["T"], ws=ws_c, out=out_c)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    greedy_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    chain_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    acc_c = out_c[0].cpu().numpy()
+    rejected = int((acc_c < G).sum())
+
+    logit_bytes = B * R * V * esize
+    greedy_bytes = logit_bytes + B * G * 4 + B * 4 + B * R * 4
+    chain_bytes = (logit_bytes + rejected * V * 4 +                 # q row at each rejection
+                   B * (G + R + 1) * 4 + B * G * 4 +                 # tokens, coins, T, q gathers
+                   B * 4 + 2 * B * R * 4)                            # outputs
+    positions = 2 * B * R
+    value = positions * args.steps / elapsed
+
+    chain_gbs = chain_bytes / (chain_ms.mean() * 1e-3) / 1e9
+    greedy_gbs = greedy_bytes / (greedy_ms.mean() * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == args.workload and tj.get("kernel_source_sha") == _source_sha():
+                traffic = tj.get("chain_call_bytes")
+        except Exception:
+            traffic = None
+
+    result = {
+        "metric": "verified positions/sec and logit-read GB/s (% of HBM peak), 1 MI355X",
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c.dtype == wl.BF16 else "f32",
+        "data": "synthetic (seeded; shapes and distributions of the large-batch workload)",
+        "config": {"workload": c.name, "B": B, "gamma": G, "V": V, "positions_per_step": positions,
+                   "step": "spec_verify_greedy + spec_verify_chain", "input_copies": args.copies},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "spec_verify_chain (k_rows sampling + k_residual)",
+            "achieved": chain_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": chain_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": chain_bytes,
+            "avg_launch_ms": float(chain_ms.mean()),
+        },
+        "modes": {
+            "greedy": {"avg_ms": float(greedy_ms.mean()), "p90_ms": float(np.percentile(greedy_ms, 90)),
+                       "GB/s": greedy_gbs, "frac": greedy_gbs / HBM_PEAK_GBS,
+                       "positions/s": B * R / (greedy_ms.mean() * 1e-3)},
+            "chain": {"avg_ms": float(chain_ms.mean()), "p90_ms": float(np.percentile(chain_ms, 90)),
+                      "GB/s": chain_gbs, "frac": chain_gbs / HBM_PEAK_GBS,
+                      "positions/s": B * R / (chain_ms.mean() * 1e-3),
+                      "rejected_requests": rejected,
+                      "tokens/s": float((acc_c + 1).sum()) / (chain_ms.mean() * 1e-3)},
+        },
+        "input_generation_s": gen_s,
+    }
+
+    if args.tree:
+        result["modes"].update(_tree_modes(args, torch, dev, api, wl))
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(c, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _source_sha():
+    import hashlib
+    p = os.path.join(ROOT, "lossless_rejection_sampling_verify_amd", "csrc", "spec_verify.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _tree_modes(args, torch, dev, api, wl):
+    t = wl.make_tree(4)
+    lg = torch.from_numpy(np.ascontiguousarray(t.logits).view(np.int16)).view(torch.bfloat16).to(dev)
+    copies = [lg] + [lg.clone() for _ in range(args.copies - 1)]
+    tok, par = torch.from_numpy(t.node_tokens).to(dev), torch.from_numpy(t.parents).to(dev)
+    cn, tp = torch.from_numpy(t.coins).to(dev), torch.from_numpy(t.temperature).to(dev)
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    for mode, name in ((0, "tree_greedy"), (1, "tree_sampling")):
+        for i in range(5):
+            api.spec_verify_tree(copies[i % len(copies)], tok, par, cn, tp, t.D, mode)
+        torch.cuda.synchronize()
+        ms = []
+        for i in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            acc, _, _, _ = api.spec_verify_tree(copies[i % len(copies)], tok, par, cn, tp, t.D, mode)
+            e1.record(stream)
+            ms.append((e0, e1, acc))
+        torch.cuda.synchronize()
+        d = np.array([a.elapsed_time(b) for a, b, _ in ms])
+        acc = ms[-1][2].cpu().numpy()
+        eager = t.B * t.N * t.V * 2
+        path = int((acc + 1).sum()) * t.V * 2
+        out[name] = {"workload": t.name, "avg_ms": float(d.mean()),
+                     "positions/s": t.B * t.N / (d.mean() * 1e-3),
+                     "GB/s_eager": eager / (d.mean() * 1e-3) / 1e9,
+                     "frac_eager": eager / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "path_only_bytes": path, "eager_bytes": eager}
+    return out
+
+
+def _cpu_baseline(c, seconds):
+    """The fp64 oracle on a bounded sample (the first 64 requests), greedy + chain, repeated
+    for about `seconds` seconds on the host's cores."""
+    import oracle
+    nb = min(64, c.B)
+    lg = np.ascontiguousarray(c.logits[:nb])
+    q = np.ascontiguousarray(c.draft_probs[:nb])
+    x, xg = np.ascontiguousarray(c.draft_tokens[:nb]), np.ascontiguousarray(c.greedy_tokens[:nb])
+    u, T = np.ascontiguousarray(c.coins[:nb]), np.ascontiguousarray(c.temperature[:nb])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify_greedy(lg, c.dtype, xg)
+        oracle.verify_chain(lg, c.dtype, q, x, u, T)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    pos = reps * 2 * nb * c.R
+    return {"value": pos / el, "unit": "positions/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {nb} of {c.B} requests of '{c.name}', greedy + chain verify, "
+                      f"{reps} repetitions in {el:.1f} s (fp64 C oracle, OpenMP over requests)"}
+
+
+if __name__ == "__main__":
+    main()

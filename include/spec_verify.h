@@ -1,0 +1,157 @@
+/* spec_verify.h -- C ABI of the MI355X (gfx950) speculative-decoding verify library.
+ *
+ * The verify step of speculative decoding: a cheap drafter proposes tokens, the target
+ * model scores every proposed position in one forward pass, and the verifier decides
+ * which proposals to keep and which single extra token to emit so that the output
+ * follows the target distribution exactly.  Sources:
+ *   llm-infra-atlas, "Speculative Decoding -- lossless acceleration of autoregressive
+ *     decode", section 0 (target logits for gamma+1 positions from one forward;
+ *     rejection sampling keeps the output law equal to the target's) and section 2
+ *     (notation: bonus token, correction from norm(max(0, p - q)), tau counts the bonus);
+ *   ricardokevins, "Speculative Decoding: real gains, correction sampling and production
+ *     limits", "mechanism" (draft / verify / accept / correct) and "correction sampling"
+ *     (Eq. a(x) = min(1, p(x)/q(x)), Eq. r(x) = norm(max(p - q, 0)));
+ *   zdszero, "spec_origins": "Blockwise Parallel Decoding" (greedy verify keeps the
+ *     longest prefix equal to the scorer's argmax), "Speculative Decoding" acceptance
+ *     rule items 1-3, "SpecInfer" (token tree flattened with an ancestor-only mask) and
+ *     "in SGLang" (greedy tree verify; the target-only tree walk with prob_acc, per-level
+ *     coin, threshold_single and threshold_acc, rejected children removed from the final
+ *     distribution relu(target - draft_probs); chain p/q rejection sampling with topk 1).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises, and keeps no pointer after the call returns.
+ *     Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = default stream)
+ *     and the call returns immediately.  No host synchronisation and no allocation
+ *     happen inside a call, so calls can be captured into a HIP graph.
+ *   - Layouts are dense row-major with the last dimension contiguous.  Target logits are
+ *     fp32 (SPEC_F32) or bf16 (SPEC_BF16, raw 16-bit patterns) and must be aligned to
+ *     their element size; rows need not be 16-byte aligned (a scalar head/tail handles
+ *     that), but 16-byte aligned rows (V * element size a multiple of 16 and an aligned
+ *     base) take the fast path.  Draft probabilities are fp32.  Token ids and parents
+ *     are int32.  Coins are fp32 uniforms in (0, 1] supplied by the caller.
+ *   - Target distribution: p = softmax(logits / T) per row, T > 0 per request.  Draft
+ *     probabilities q are used exactly as given (already at temperature T).
+ *   - Return value: SPEC_OK, or a negative status for an argument error found on the
+ *     host before anything is enqueued (nothing is written), or SPEC_ERR_HIP if a launch
+ *     failed.  Errors in the data are reported in-band per request: accept_len[b] = -1,
+ *     token / node rows of that request filled with -1 and probability rows with 0.
+ *     A request is invalid when a token id is outside [0, V), the temperature is not
+ *     finite and > 0, a coin is outside (0, 1], a row has no finite logit (all -inf),
+ *     a drafted token's q is negative or not finite, or (tree) the parent array is
+ *     malformed or a node lies deeper than D.  NaN or +inf logits are undefined.
+ *   - Workspace: a device buffer of at least spec_workspace_bytes(op, B, R, V) bytes,
+ *     256-byte aligned, ZERO-FILLED before its first use (e.g. by
+ *     spec_workspace_init or a zeroing allocation).  Every completed call leaves it
+ *     zero-filled again where it matters (the arrival counters), so it can be reused
+ *     by later calls on the same stream.  Calls that may overlap need separate
+ *     workspaces.
+ *   - Determinism: identical inputs give bitwise-identical outputs.
+ *   - Coin convention: every comparison is coin <= threshold.  The final draw (the
+ *     correction, the bonus, or the tree's last token) is the inverse CDF in ascending
+ *     token id with its own coin: the first token j with weight w_j > 0 and
+ *     u * sum(w) <= w_0 + ... + w_j.  If the residual mass is not positive the draw
+ *     falls back to the target row itself.  Greedy argmax ties go to the lowest id.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SPEC_OK = 0,
+    SPEC_ERR_NULL = -1,      /* a required pointer is NULL */
+    SPEC_ERR_SHAPE = -2,     /* B, G, N, V or D outside the supported range */
+    SPEC_ERR_DTYPE = -3,     /* unknown logit dtype */
+    SPEC_ERR_PARAM = -4,     /* bad mode / threshold / misaligned pointer */
+    SPEC_ERR_WORKSPACE = -5, /* workspace too small or not 256-byte aligned */
+    SPEC_ERR_HIP = -6        /* a HIP launch failed */
+};
+
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };                   /* target-logit dtype */
+enum { SPEC_TREE_GREEDY = 0, SPEC_TREE_SAMPLING = 1 };  /* spec_verify_tree mode */
+enum { SPEC_OP_GREEDY = 0, SPEC_OP_CHAIN = 1, SPEC_OP_TREE = 2 };
+
+#define SPEC_MAX_G 64     /* drafted positions per request (chain) */
+#define SPEC_MAX_N 1024   /* tree nodes per request, root included */
+
+/* Bytes of workspace a call of kind `op` needs for B requests, R logit rows per request
+ * (G+1 for the chain calls, N for the tree) and vocabulary V.  0 for unusable sizes. */
+size_t spec_workspace_bytes(int op, int B, int R, int V);
+
+/* Human-readable name of a status code (static string). */
+const char* spec_status_str(int status);
+
+/* Enqueue a kernel that zero-fills `ws_bytes` bytes of `workspace` on `stream`. */
+int spec_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* Greedy chain verify (spec_origins, "Blockwise Parallel Decoding", verify).
+ *   logits       [B][G+1][V] target logits; row i scores the token after draft i-1.
+ *   draft_tokens [B][G]      proposed tokens.
+ * Per request: a_i = lowest id attaining max_x logits[b][i][x] (raw logits, no
+ * temperature); k = the first i < G with draft_tokens[b][i] != a_i, else G.
+ *   accept_len [B]    = k;
+ *   out_tokens [B][G+1] = draft_tokens[b][0..k-1], then a_k, then -1 padding. */
+int spec_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
+                       int B, int G, int V, int32_t* accept_len, int32_t* out_tokens,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* Chain rejection sampling (spec_origins, "Speculative Decoding", acceptance rule;
+ * ricardokevins, "correction sampling", Eq. a(x) and Eq. r(x)).
+ *   logits       [B][G+1][V] target logits;
+ *   draft_probs  [B][G][V]   draft distribution q_i at each drafted position (fp32);
+ *   draft_tokens [B][G]      x_i ~ q_i;
+ *   coins        [B][G+1]    coins[b][i] (i < G) decides position i: x_i is accepted iff
+ *                            p_i(x_i) > 0 and coins[b][i] <= p_i(x_i) / q_i(x_i);
+ *                            coins[b][G] drives the final draw;
+ *   temperature  [B].
+ * k = the first rejected position, else G.  The final token is drawn from
+ * norm(max(0, p_k - q_k)) if k < G (the correction), else from p_G (the bonus).
+ *   accept_len [B] = k; out_tokens [B][G+1] = x_0..x_{k-1}, final token, -1 padding;
+ *   probs_out  [B][G+1] (optional, may be NULL) = target probability of each emitted
+ *              token under the row it was emitted from, 0 for padding. */
+int spec_verify_chain(const void* logits, int dtype, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* coins,
+                      const float* temperature, int B, int G, int V, int32_t* accept_len,
+                      int32_t* out_tokens, float* probs_out, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Token-tree verify (spec_origins, "SpecInfer" and "in SGLang").
+ *   logits      [B][N][V] row j = target logits of the token after node j (node 0 is the
+ *               root, i.e. the last committed token);
+ *   node_tokens [B][N]    token carried by each node ([b][0] unused);
+ *   parents     [B][N]    parents[b][0] = -1 and 0 <= parents[b][i] < i; siblings should
+ *               carry distinct tokens (duplicates are accumulated as given);
+ *   coins       [B][D+1]  sampling mode: coins[b][d] decides level d, coins[b][D] drives
+ *               the final draw (NULL allowed in greedy mode);
+ *   temperature [B]       sampling mode (NULL allowed in greedy mode);
+ *   D           maximum depth, 1 <= D <= SPEC_MAX_N: every node must lie at depth <= D.
+ * Sampling (target-only): from cur = root, level d: try the children of cur in ascending
+ * node id, adding their target probabilities p_cur(token) into acc; the first child with
+ * coins[b][d] <= acc / threshold_acc or p_cur(token) >= threshold_single is accepted and
+ * the walk moves to it; if none is, the walk stops.  The final token is drawn from p_cur
+ * with the tokens of the children tried at the last level removed (a leaf keeps its whole
+ * row).  threshold_single = threshold_acc = 1.0 is the lossless setting.
+ * Greedy: follow the first child whose token equals the argmax of row cur; emit the argmax
+ * of the row where the walk stops.
+ *   accept_len [B] = number of accepted nodes d; out_tokens [B][D+1] = their tokens, then
+ *   the final token, -1 padding; accepted_nodes [B][D] = accepted node ids, -1 padding;
+ *   probs_out [B][D+1] (optional) = target probability of each emitted token under the row
+ *   it was emitted from (sampling mode; 0 in greedy mode and for padding). */
+int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
+                     const int32_t* parents, const float* coins, const float* temperature,
+                     int B, int N, int V, int D, int mode, float threshold_single,
+                     float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
+                     int32_t* accepted_nodes, float* probs_out, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,69 @@
+"""ctypes loader of the HIP library ``libspecverify.so`` (argument marshalling only).
+
+The library must have been built (``python -m lossless_rejection_sampling_verify_amd.build``
+or ``__graft_entry__.build()``); there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "spec_verify.h")
+
+SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_DTYPE = 0, -1, -2, -3
+SPEC_ERR_PARAM, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = -4, -5, -6
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_TREE_GREEDY, SPEC_TREE_SAMPLING = 0, 1
+SPEC_OP_GREEDY, SPEC_OP_CHAIN, SPEC_OP_TREE = 0, 1, 2
+SPEC_MAX_G, SPEC_MAX_N = 64, 1024
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/spec_verify.h declares."""
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:size_t|int|const char\*)\s+(spec_\w+)\s*\(", text, re.M)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ip, fp, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.spec_workspace_bytes.argtypes = [ip, ip, ip, ip]
+        L.spec_workspace_bytes.restype = sz
+        L.spec_status_str.argtypes = [ip]
+        L.spec_status_str.restype = ctypes.c_char_p
+        L.spec_workspace_init.argtypes = [vp, sz, vp]
+        L.spec_workspace_init.restype = ip
+        L.spec_verify_greedy.argtypes = [vp, ip, vp, ip, ip, ip, vp, vp, vp, sz, vp]
+        L.spec_verify_greedy.restype = ip
+        L.spec_verify_chain.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_chain.restype = ip
+        L.spec_verify_tree.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, fp,
+                                       vp, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_tree.restype = ip
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().spec_status_str(int(status)).decode()
+
+
+def workspace_bytes(op: int, B: int, R: int, V: int) -> int:
+    return int(lib().spec_workspace_bytes(op, B, R, V))

@@ -1,0 +1,159 @@
+"""Torch-facing binding of the verify library: same names as the C ABI.
+
+PyTorch provides device memory and the current stream; every step of the verify runs in
+the HIP kernels of ``libspecverify.so``.  Inputs must already be contiguous device tensors
+of the documented dtypes (fp32 or bf16 logits, fp32 draft probabilities / coins /
+temperatures, int32 tokens and parents); nothing is converted or computed here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+_WORKSPACES: dict = {}
+
+
+def _check(t: torch.Tensor, name: str, dtype, dims: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _logit_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return L.SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return L.SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def workspace(op: int, B: int, R: int, V: int, device) -> torch.Tensor:
+    """A zero-filled workspace big enough for the call, cached per device and kind.
+
+    The library leaves the workspace's counters at zero after every completed call, so a
+    cached buffer can be reused by later calls issued on the same stream."""
+    need = L.workspace_bytes(op, B, R, V)
+    if need == 0:
+        raise ValueError("unsupported sizes")
+    key = (torch.device(device), op)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def spec_verify_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, *, ws=None,
+                       stream=None, out=None):
+    """Greedy chain verify.  logits [B][G+1][V] fp32/bf16, draft_tokens [B][G] int32.
+
+    Returns (accept_len [B] int32, out_tokens [B][G+1] int32)."""
+    _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
+    _check(draft_tokens, "draft_tokens", torch.int32, 2)
+    B, R, V = logits.shape
+    G = R - 1
+    if draft_tokens.shape != (B, G):
+        raise ValueError("draft_tokens must be [B][G]")
+    dev = logits.device
+    ws = workspace(L.SPEC_OP_GREEDY, B, R, V, dev) if ws is None else ws
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, R, dtype=torch.int32, device=dev)
+    else:
+        acc, toks = out
+    rc = L.lib().spec_verify_greedy(_ptr(logits), _logit_dtype(logits), _ptr(draft_tokens), B, G, V,
+                                    _ptr(acc), _ptr(toks), _ptr(ws), ws.numel(),
+                                    _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_verify_greedy", rc)
+    return acc, toks
+
+
+def spec_verify_chain(logits: torch.Tensor, draft_probs: torch.Tensor, draft_tokens: torch.Tensor,
+                      coins: torch.Tensor, temperature: torch.Tensor, *, want_probs: bool = False,
+                      ws=None, stream=None, out=None):
+    """Chain rejection sampling.  logits [B][G+1][V], draft_probs [B][G][V] fp32,
+    draft_tokens [B][G] int32, coins [B][G+1] fp32, temperature [B] fp32.
+
+    Returns (accept_len [B], out_tokens [B][G+1], probs [B][G+1] or None)."""
+    _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
+    _check(draft_probs, "draft_probs", torch.float32, 3)
+    _check(draft_tokens, "draft_tokens", torch.int32, 2)
+    _check(coins, "coins", torch.float32, 2)
+    _check(temperature, "temperature", torch.float32, 1)
+    B, R, V = logits.shape
+    G = R - 1
+    if draft_probs.shape != (B, G, V) or draft_tokens.shape != (B, G) or \
+            coins.shape != (B, R) or temperature.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    dev = logits.device
+    ws = workspace(L.SPEC_OP_CHAIN, B, R, V, dev) if ws is None else ws
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, R, dtype=torch.int32, device=dev)
+        probs = torch.empty(B, R, dtype=torch.float32, device=dev) if want_probs else None
+    else:
+        acc, toks, probs = out
+    rc = L.lib().spec_verify_chain(_ptr(logits), _logit_dtype(logits), _ptr(draft_probs),
+                                   _ptr(draft_tokens), _ptr(coins), _ptr(temperature), B, G, V,
+                                   _ptr(acc), _ptr(toks), _ptr(probs), _ptr(ws), ws.numel(),
+                                   _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_verify_chain", rc)
+    return acc, toks, probs
+
+
+def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
+                     coins, temperature, D: int, mode: int, threshold_single: float = 1.0,
+                     threshold_acc: float = 1.0, *, want_probs: bool = False, ws=None,
+                     stream=None, out=None):
+    """Token-tree verify.  logits [B][N][V], node_tokens/parents [B][N] int32,
+    coins [B][D+1] fp32 and temperature [B] fp32 (sampling mode; None in greedy mode).
+
+    Returns (accept_len [B], out_tokens [B][D+1], accepted_nodes [B][D], probs or None)."""
+    _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
+    _check(node_tokens, "node_tokens", torch.int32, 2)
+    _check(parents, "parents", torch.int32, 2)
+    B, N, V = logits.shape
+    if node_tokens.shape != (B, N) or parents.shape != (B, N):
+        raise ValueError("node_tokens / parents must be [B][N]")
+    if coins is not None:
+        _check(coins, "coins", torch.float32, 2)
+        if coins.shape != (B, D + 1):
+            raise ValueError("coins must be [B][D+1]")
+    if temperature is not None:
+        _check(temperature, "temperature", torch.float32, 1)
+    dev = logits.device
+    ws = workspace(L.SPEC_OP_TREE, B, N, V, dev) if ws is None else ws
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
+        nodes = torch.empty(B, D, dtype=torch.int32, device=dev)
+        probs = torch.empty(B, D + 1, dtype=torch.float32, device=dev) if want_probs else None
+    else:
+        acc, toks, nodes, probs = out
+    rc = L.lib().spec_verify_tree(_ptr(logits), _logit_dtype(logits), _ptr(node_tokens),
+                                  _ptr(parents), _ptr(coins), _ptr(temperature), B, N, V, D,
+                                  int(mode), float(threshold_single), float(threshold_acc),
+                                  _ptr(acc), _ptr(toks), _ptr(nodes), _ptr(probs), _ptr(ws),
+                                  ws.numel(), _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_verify_tree", rc)
+    return acc, toks, nodes, probs

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares, sizes
+its workspace, and rejects bad arguments on the host before anything is enqueued.
+
+Every call below fails validation, so no kernel is ever launched (the pointers are
+placeholders that are never dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+from lossless_rejection_sampling_verify_amd import _lib as L
+
+P = 1 << 20          # a 256-byte aligned placeholder address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = L.declared_functions()
+    assert set(names) >= {"spec_verify_greedy", "spec_verify_chain", "spec_verify_tree",
+                          "spec_workspace_bytes", "spec_status_str", "spec_workspace_init"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.status_str(code) and L.status_str(code) != "unknown status"
+    assert L.status_str(17) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    a = L.workspace_bytes(L.SPEC_OP_CHAIN, 256, 5, 152064)
+    assert a > 0 and a % 256 == 0
+    assert L.workspace_bytes(L.SPEC_OP_CHAIN, 512, 5, 152064) > a
+    assert L.workspace_bytes(L.SPEC_OP_GREEDY, 1, 65, 10) > 0
+    assert L.workspace_bytes(L.SPEC_OP_GREEDY, 1, 66, 10) == 0       # G > 64
+    assert L.workspace_bytes(L.SPEC_OP_CHAIN, 1, 1, 10) == 0         # G = 0
+    assert L.workspace_bytes(L.SPEC_OP_TREE, 4, 1024, 10) > 0
+    assert L.workspace_bytes(L.SPEC_OP_TREE, 4, 1025, 10) == 0
+    assert L.workspace_bytes(7, 4, 5, 10) == 0
+    assert L.workspace_bytes(L.SPEC_OP_CHAIN, 4, 5, 0) == 0
+
+
+def _greedy(lib, logits=P, dtype=L.SPEC_BF16, tokens=P, B=2, G=4, V=1000, acc=P, out=P,
+            ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.workspace_bytes(L.SPEC_OP_GREEDY, max(B, 1), G + 1, max(V, 1)) or 1 << 20
+    return lib.spec_verify_greedy(logits, dtype, tokens, B, G, V, acc, out, ws, ws_bytes, None)
+
+
+def test_greedy_rejects_bad_arguments(lib):
+    assert _greedy(lib, logits=None) == L.SPEC_ERR_NULL
+    assert _greedy(lib, tokens=None) == L.SPEC_ERR_NULL
+    assert _greedy(lib, acc=None) == L.SPEC_ERR_NULL
+    assert _greedy(lib, ws=None) == L.SPEC_ERR_NULL
+    assert _greedy(lib, dtype=5) == L.SPEC_ERR_DTYPE
+    assert _greedy(lib, G=0) == L.SPEC_ERR_SHAPE
+    assert _greedy(lib, G=65) == L.SPEC_ERR_SHAPE
+    assert _greedy(lib, V=0) == L.SPEC_ERR_SHAPE
+    assert _greedy(lib, B=-1) == L.SPEC_ERR_SHAPE
+    assert _greedy(lib, logits=P + 1) == L.SPEC_ERR_PARAM                 # not bf16-aligned
+    assert _greedy(lib, logits=P + 2, dtype=L.SPEC_F32) == L.SPEC_ERR_PARAM
+    assert _greedy(lib, ws=P + 16) == L.SPEC_ERR_WORKSPACE
+    assert _greedy(lib, ws_bytes=64) == L.SPEC_ERR_WORKSPACE
+    assert _greedy(lib, B=0) == L.SPEC_OK                                 # nothing to do
+
+
+def _chain(lib, **kw):
+    a = dict(logits=P, dtype=L.SPEC_BF16, q=P, tokens=P, coins=P, temp=P, B=3, G=4, V=2000,
+             acc=P, out=P, probs=None, ws=P, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = L.workspace_bytes(L.SPEC_OP_CHAIN, max(a["B"], 1), a["G"] + 1, max(a["V"], 1)) or 1 << 20
+    return lib.spec_verify_chain(a["logits"], a["dtype"], a["q"], a["tokens"], a["coins"],
+                                 a["temp"], a["B"], a["G"], a["V"], a["acc"], a["out"],
+                                 a["probs"], a["ws"], a["ws_bytes"], None)
+
+
+def test_chain_rejects_bad_arguments(lib):
+    for k in ("logits", "q", "tokens", "coins", "temp", "acc", "out", "ws"):
+        assert _chain(lib, **{k: None}) == L.SPEC_ERR_NULL, k
+    assert _chain(lib, dtype=2) == L.SPEC_ERR_DTYPE
+    assert _chain(lib, G=0) == L.SPEC_ERR_SHAPE
+    assert _chain(lib, G=65) == L.SPEC_ERR_SHAPE
+    assert _chain(lib, q=P + 2) == L.SPEC_ERR_PARAM
+    assert _chain(lib, ws_bytes=1024) == L.SPEC_ERR_WORKSPACE
+    assert _chain(lib, B=0) == L.SPEC_OK
+
+
+def _tree(lib, **kw):
+    a = dict(logits=P, dtype=L.SPEC_F32, tok=P, par=P, coins=P, temp=P, B=2, N=64, V=500, D=6,
+             mode=L.SPEC_TREE_SAMPLING, ts=1.0, ta=1.0, acc=P, out=P, nodes=P, probs=None,
+             ws=P, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = L.workspace_bytes(L.SPEC_OP_TREE, max(a["B"], 1), max(a["N"], 1), max(a["V"], 1)) or 1 << 20
+    return lib.spec_verify_tree(a["logits"], a["dtype"], a["tok"], a["par"], a["coins"], a["temp"],
+                                a["B"], a["N"], a["V"], a["D"], a["mode"], a["ts"], a["ta"],
+                                a["acc"], a["out"], a["nodes"], a["probs"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+def test_tree_rejects_bad_arguments(lib):
+    for k in ("logits", "tok", "par", "acc", "out", "nodes", "ws", "coins", "temp"):
+        assert _tree(lib, **{k: None}) == L.SPEC_ERR_NULL, k
+    assert _tree(lib, mode=2) == L.SPEC_ERR_PARAM
+    assert _tree(lib, ts=0.0) == L.SPEC_ERR_PARAM
+    assert _tree(lib, ta=-1.0) == L.SPEC_ERR_PARAM
+    assert _tree(lib, ta=float("nan")) == L.SPEC_ERR_PARAM
+    assert _tree(lib, N=1025) == L.SPEC_ERR_SHAPE
+    assert _tree(lib, N=0) == L.SPEC_ERR_SHAPE
+    assert _tree(lib, D=0) == L.SPEC_ERR_SHAPE
+    assert _tree(lib, dtype=9) == L.SPEC_ERR_DTYPE
+    assert _tree(lib, ws_bytes=1000) == L.SPEC_ERR_WORKSPACE
+    # greedy mode needs neither coins nor temperature: check only up to validation
+    assert _tree(lib, mode=L.SPEC_TREE_GREEDY, coins=None, temp=None, ws=None) == L.SPEC_ERR_NULL
+    assert _tree(lib, B=0, mode=L.SPEC_TREE_GREEDY, coins=None, temp=None) == L.SPEC_OK
+
+
+def test_workspace_init_validation(lib):
+    assert lib.spec_workspace_init(None, 16, None) == L.SPEC_ERR_NULL
+    assert lib.spec_workspace_init(P + 2, 16, None) == L.SPEC_ERR_PARAM
+    assert lib.spec_workspace_init(P, 0, None) == L.SPEC_OK

@@ -1,0 +1,337 @@
+"""HIP path vs the fp64 oracle, element by element, on identical seeded inputs.
+
+Bar (per request): accept_len and emitted tokens (and accepted node ids) bit-exact,
+except requests whose oracle decision trace passes within 1e-6 of a threshold
+(coin-vs-threshold near-ties), which are counted and reported.  Greedy verify has no
+coins and must be bit-exact everywhere.  Probabilities of emitted tokens agree within
+1e-5 relative (fp32 accumulation; values below 1e-30 compared absolutely).
+
+Covers the five named workloads at full size, in the launch configuration the benchmark
+uses, plus ragged and degenerate shapes (V not a multiple of the vector width, V below
+one vector, V = 1, G = 64, N = 1024, deep trees), invalid requests, determinism, and the
+chain-shaped-tree == chain cross-check.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+from lossless_rejection_sampling_verify_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+BAND = 1e-6
+PROB_RTOL = 1e-5
+
+
+def _api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_rejection_sampling_verify_amd import api
+    return api
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_logits(arr, dtype):
+    a = np.ascontiguousarray(arr)
+    if dtype == wl.BF16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a.astype(np.float32, copy=False)).cuda()
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------------------------
+# runners
+
+def gpu_greedy(logits, dtype, tokens):
+    api = _api()
+    acc, out = api.spec_verify_greedy(dev_logits(logits, dtype), dev(tokens.astype(np.int32)))
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.cpu().numpy()
+
+
+def gpu_chain(logits, dtype, q, x, coins, T):
+    api = _api()
+    acc, out, probs = api.spec_verify_chain(dev_logits(logits, dtype), dev(q.astype(np.float32)),
+                                            dev(x.astype(np.int32)), dev(coins.astype(np.float32)),
+                                            dev(T.astype(np.float32)), want_probs=True)
+    torch.cuda.synchronize()
+    return dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
+                probs=probs.cpu().numpy())
+
+
+def gpu_tree(t, mode, D=None, th_single=1.0, th_acc=1.0, parents=None, tokens=None, coins=None,
+             temperature=None):
+    api = _api()
+    D = t.D if D is None else D
+    parents = t.parents if parents is None else parents
+    tokens = t.node_tokens if tokens is None else tokens
+    coins = t.coins if coins is None else coins
+    temperature = t.temperature if temperature is None else temperature
+    sampling = mode == oracle.TREE_SAMPLING
+    acc, out, nodes, probs = api.spec_verify_tree(
+        dev_logits(t.logits, t.dtype), dev(tokens.astype(np.int32)), dev(parents.astype(np.int32)),
+        dev(coins.astype(np.float32)) if sampling else None,
+        dev(temperature.astype(np.float32)) if sampling else None, D, mode, th_single, th_acc,
+        want_probs=True)
+    torch.cuda.synchronize()
+    return dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
+                accepted_nodes=nodes.cpu().numpy(), probs=probs.cpu().numpy())
+
+
+# ------------------------------------------------------------------------------------
+# comparison
+
+def compare(g, o, keys, margin=None, probs=True, label=""):
+    """Bit-exact on `keys` outside the near-tie band; probs within 1e-5 relative."""
+    B = len(o["accept_len"])
+    mism = np.zeros(B, bool)
+    for k in keys:
+        a, b = np.asarray(g[k]), np.asarray(o[k])
+        mism |= (a != b).reshape(B, -1).any(1)
+    near = np.zeros(B, bool) if margin is None else margin <= BAND
+    bad = mism & ~near
+    if bad.any():
+        i = int(np.nonzero(bad)[0][0])
+        detail = {k: (np.asarray(g[k])[i], np.asarray(o[k])[i]) for k in keys}
+        raise AssertionError(f"{label}: {int(bad.sum())} requests differ outside the near-tie "
+                             f"band; first b={i}: {detail}, margin={None if margin is None else margin[i]}")
+    if probs and "probs" in g:
+        ok = ~mism
+        gp, op = g["probs"][ok].astype(np.float64), o["probs"][ok]
+        big = np.abs(op) >= 1e-30
+        rel = np.abs(gp[big] - op[big]) / np.abs(op[big])
+        assert rel.size == 0 or rel.max() <= PROB_RTOL, f"{label}: prob rel err {rel.max():.3g}"
+        assert np.all(np.abs(gp[~big] - op[~big]) <= 1e-30), f"{label}: tiny probs differ"
+    stats = dict(n=B, near=int(near.sum()), near_mismatch=int((mism & near).sum()))
+    say(f"{label}: {stats}")
+    return stats
+
+
+def check_chain(c, label):
+    say(f"chain {label}: B={c.B} G={c.G} V={c.V} {c.dtype}")
+    g = gpu_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
+    o = oracle.verify_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
+    return compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=label)
+
+
+def check_greedy(c, label, tokens=None):
+    tokens = c.greedy_tokens if tokens is None else tokens
+    say(f"greedy {label}: B={c.B} G={c.G} V={c.V} {c.dtype}")
+    ga, go = gpu_greedy(c.logits, c.dtype, tokens)
+    oa, oo = oracle.verify_greedy(c.logits, c.dtype, tokens)
+    return compare(dict(accept_len=ga, out_tokens=go), dict(accept_len=oa, out_tokens=oo),
+                   ["accept_len", "out_tokens"], None, probs=False, label=label)
+
+
+def check_tree(t, mode, label, **kw):
+    say(f"tree {label}: B={t.B} N={t.N} D={kw.get('D', t.D)} V={t.V} mode={mode}")
+    g = gpu_tree(t, mode, **kw)
+    D = kw.get("D", t.D)
+    o = oracle.verify_tree(t.logits, t.dtype, kw.get("tokens", t.node_tokens),
+                           kw.get("parents", t.parents), kw.get("coins", t.coins),
+                           kw.get("temperature", t.temperature), D, mode,
+                           kw.get("th_single", 1.0), kw.get("th_acc", 1.0))
+    if mode == oracle.TREE_GREEDY:
+        g["probs"] = np.zeros_like(g["probs"])
+        o["probs"] = np.zeros_like(o["probs"])
+    return compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"],
+                   o["margin"] if mode == oracle.TREE_SAMPLING else None, label=label)
+
+
+# ------------------------------------------------------------------------------------
+# the five workloads at full size
+
+_cache = {}
+
+
+def chain_cfg(i):
+    if i not in _cache:
+        _cache[i] = wl.make_chain(i)
+    return _cache[i]
+
+
+def tree_cfg():
+    if 4 not in _cache:
+        _cache[4] = wl.make_tree(4)
+    return _cache[4]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_chain_workloads(cfg):
+    check_chain(chain_cfg(cfg), f"workload {cfg}")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_greedy_workloads(cfg):
+    check_greedy(chain_cfg(cfg), f"workload {cfg}")
+
+
+@pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
+def test_tree_workload(mode):
+    check_tree(tree_cfg(), mode, f"workload 4 mode {mode}")
+
+
+def test_tiny_chain_10k_trials_parity_and_law():
+    """Workload 1 as 10k trials (rows replicated, drafts and coins per trial): parity, then
+    chi-square of the GPU's first emitted token against the target row."""
+    c = chain_cfg(1)
+    trials = 10_000
+    rng = np.random.default_rng(2024)
+    q = c.draft_probs[0].astype(np.float64)
+    q /= q.sum(-1, keepdims=True)
+    x = np.stack([rng.choice(c.V, size=trials, p=q[i]) for i in range(c.G)], 1).astype(np.int32)
+    coins = wl.draw_coins(rng, (trials, c.G + 1))
+    lg = np.ascontiguousarray(np.broadcast_to(c.logits[0], (trials,) + c.logits.shape[1:]))
+    qq = np.ascontiguousarray(np.broadcast_to(c.draft_probs[0], (trials,) + c.draft_probs.shape[1:]))
+    T = np.ones(trials, np.float32)
+    say("chain workload 1 x 10k trials")
+    g = gpu_chain(lg, c.dtype, qq, x, coins, T)
+    o = oracle.verify_chain(lg, c.dtype, qq, x, coins, T)
+    compare(g, o, ["accept_len", "out_tokens"], o["margin"], label="workload 1 x10k")
+    p0 = scipy.special.softmax(c.logits[0, 0].astype(np.float64))
+    counts = np.bincount(g["out_tokens"][:, 0], minlength=c.V)
+    exp = p0 * trials
+    keep = exp >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    ex = np.append(exp[keep], exp[~keep].sum())
+    assert scipy.stats.chisquare(obs, ex).pvalue > 1e-3
+
+
+# ------------------------------------------------------------------------------------
+# ragged and degenerate shapes
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("B,G,V", [(5, 3, 50021), (7, 2, 7), (3, 4, 1), (2, 64, 300),
+                                   (9, 5, 4099), (40, 1, 32768)])
+def test_chain_ragged(dtype, B, G, V):
+    c = wl.make_chain(2, seed=B * 1000 + G, B=B, G=G, V=V, dtype=dtype)
+    check_chain(c, f"ragged {dtype} B={B} G={G} V={V}")
+    check_greedy(c, f"ragged {dtype} B={B} G={G} V={V}")
+
+
+@pytest.mark.parametrize("T", [0.3, 0.7, 2.0])
+def test_chain_temperatures_boosted(T):
+    c = wl.make_chain(3, seed=5, B=16, G=6, V=20000, T=T)
+    check_chain(c, f"boosted T={T}")
+
+
+def test_greedy_ties_bf16():
+    """Many tied maxima (small-integer logits in bf16): lowest id must win everywhere."""
+    rng = np.random.default_rng(17)
+    B, G, V = 64, 4, 70000
+    lg = rng.integers(0, 4, size=(B, G + 1, V)).astype(np.float32)
+    bits = wl.f32_to_bf16_bits(lg)
+    want = np.argmax(lg, -1)
+    x = want[:, :G].copy()
+    flip = rng.random((B, G)) < 0.25
+    x[flip] = (x[flip] + 1) % V
+    ga, go = gpu_greedy(bits, wl.BF16, x.astype(np.int32))
+    oa, oo = oracle.verify_greedy(bits, wl.BF16, x.astype(np.int32))
+    np.testing.assert_array_equal(ga, oa)
+    np.testing.assert_array_equal(go, oo)
+
+
+def test_tree_low_entropy_deep_walks():
+    """Sharper target rows so the walk goes deep (workload 4 shape, sigma 8, T 0.5)."""
+    t = wl.make_tree(4, seed=3, B=48, V=30000, sigma=8.0, T=0.5)
+    s = check_tree(t, oracle.TREE_SAMPLING, "tree sigma=8 T=0.5")
+    check_tree(t, oracle.TREE_GREEDY, "tree sigma=8 greedy")
+    o = oracle.verify_tree(t.logits, t.dtype, t.node_tokens, t.parents, t.coins, t.temperature,
+                           t.D, oracle.TREE_SAMPLING)
+    assert o["accept_len"].max() >= 2, "walks too shallow to exercise the levels"
+    assert s["n"] == 48
+
+
+@pytest.mark.parametrize("th_single,th_acc", [(0.3, 1.0), (1.0, 0.6), (0.05, 2.0)])
+def test_tree_thresholds(th_single, th_acc):
+    t = wl.make_tree(4, seed=9, B=32, V=5000, sigma=5.0)
+    check_tree(t, oracle.TREE_SAMPLING, f"tree thresholds {th_single}/{th_acc}",
+               th_single=th_single, th_acc=th_acc)
+
+
+def test_tree_max_nodes_and_deep_chain():
+    t = wl.make_tree(4, seed=4, B=6, N=1024, D=40, max_children=64, V=3000, sigma=6.0, T=0.6)
+    check_tree(t, oracle.TREE_SAMPLING, "tree N=1024 D=40")
+    check_tree(t, oracle.TREE_GREEDY, "tree N=1024 D=40 greedy")
+    # chain-shaped tree with 200 nodes: depth 199
+    N = 200
+    tc = wl.make_tree(4, seed=5, B=3, N=N, D=N - 1, max_children=1, V=500, sigma=10.0, T=0.3)
+    check_tree(tc, oracle.TREE_SAMPLING, "chain-shaped tree N=200")
+    check_tree(tc, oracle.TREE_GREEDY, "chain-shaped tree N=200 greedy")
+
+
+def test_chain_shaped_tree_equals_chain_on_gpu():
+    c = wl.make_chain(5, seed=8, B=32, G=4, V=40000)
+    B, G, V = c.B, c.G, c.V
+    q1 = np.zeros((B, G, V), np.float32)
+    for i in range(G):
+        q1[np.arange(B), i, c.draft_tokens[:, i]] = 1.0
+    gc = gpu_chain(c.logits, c.dtype, q1, c.draft_tokens, c.coins, c.temperature)
+    t = wl.TreeInputs(name="chain-shaped", B=B, N=G + 1, V=V, D=G, dtype=c.dtype, logits=c.logits,
+                      node_tokens=np.concatenate([np.full((B, 1), -1, np.int32), c.draft_tokens], 1),
+                      parents=np.tile(np.arange(-1, G, dtype=np.int32), (B, 1)), coins=c.coins,
+                      temperature=c.temperature)
+    gt = gpu_tree(t, oracle.TREE_SAMPLING)
+    o = oracle.verify_chain(c.logits, c.dtype, q1, c.draft_tokens, c.coins, c.temperature)
+    near = o["margin"] <= BAND
+    same = (gc["accept_len"] == gt["accept_len"]) & (gc["out_tokens"] == gt["out_tokens"]).all(1)
+    assert (same | near).all()
+
+
+# ------------------------------------------------------------------------------------
+# invalid requests, determinism
+
+def test_invalid_requests_match_oracle():
+    c = wl.make_chain(2, seed=2, B=8, G=3, V=3000)
+    lg, q, x, u, T = (c.logits.copy(), c.draft_probs.copy(), c.draft_tokens.copy(),
+                      c.coins.copy(), c.temperature.copy())
+    x[1, 2] = 3000
+    T[2] = 0.0
+    u[3, 0] = 0.0
+    lg[4, 3, :] = -np.inf
+    q[5, 1, x[5, 1]] = np.nan
+    T[6] = np.inf
+    say("invalid chain requests")
+    g = gpu_chain(lg, c.dtype, q, x, u, T)
+    o = oracle.verify_chain(lg, c.dtype, q, x, u, T)
+    compare(g, o, ["accept_len", "out_tokens"], o["margin"], label="invalid chain")
+    assert (g["accept_len"][[1, 2, 3, 4, 5, 6]] == -1).all()
+    assert (g["probs"][[1, 2, 3, 4, 5, 6]] == 0).all()
+    ga, go = gpu_greedy(lg, c.dtype, x)
+    oa, oo = oracle.verify_greedy(lg, c.dtype, x)
+    np.testing.assert_array_equal(ga, oa)
+    np.testing.assert_array_equal(go, oo)
+
+    t = wl.make_tree(4, seed=1, B=6, N=12, V=200, D=3, max_children=4)
+    par, tok, cn = t.parents.copy(), t.node_tokens.copy(), t.coins.copy()
+    par[1, 5] = 5
+    tok[2, 3] = -2
+    par[3, 0] = 0
+    cn[4, 3] = 1.5
+    say("invalid tree requests")
+    g = gpu_tree(t, oracle.TREE_SAMPLING, parents=par, tokens=tok, coins=cn)
+    o = oracle.verify_tree(t.logits, t.dtype, tok, par, cn, t.temperature, t.D, oracle.TREE_SAMPLING)
+    compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"], o["margin"], label="invalid tree")
+    assert (g["accept_len"][[1, 2, 3, 4]] == -1).all()
+    g2 = gpu_tree(t, oracle.TREE_GREEDY, D=2)
+    assert (g2["accept_len"] == -1).all()
+
+
+def test_deterministic_bits():
+    c = chain_cfg(3)
+    say("determinism workload 3")
+    a = gpu_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
+    b = gpu_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
