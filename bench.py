@@ -147,7 +147,7 @@ def main():
                    "step": "spec_verify_greedy + spec_verify_chain", "input_copies": args.copies},
         "roofline": {
             "bound": "hbm",
-            "kernel": "spec_verify_chain (k_rows sampling + k_residual)",
+            "kernel": "spec_verify_chain (k_rows sampling pass + k_chain_accept + k_chain_draw)",
             "achieved": chain_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -41,11 +41,11 @@
  *     a drafted token's q is negative or not finite, or (tree) the parent array is
  *     malformed or a node lies deeper than D.  NaN or +inf logits are undefined.
  *   - Workspace: a device buffer of at least spec_workspace_bytes(op, B, R, V) bytes,
- *     256-byte aligned, ZERO-FILLED before its first use (e.g. by
- *     spec_workspace_init or a zeroing allocation).  Every completed call leaves it
- *     zero-filled again where it matters (the arrival counters), so it can be reused
- *     by later calls on the same stream.  Calls that may overlap need separate
- *     workspaces.
+ *     256-byte aligned, owned by the caller.  Its contents need no initialisation: each
+ *     call writes what it reads later in the same call (per-row partial records, the
+ *     per-request acceptance state and residual chunk sums).  Calls that may run at the
+ *     same time (on different streams) need separate workspaces; calls issued in order
+ *     on one stream can share one.
  *   - Determinism: identical inputs give bitwise-identical outputs.
  *   - Coin convention: every comparison is coin <= threshold.  The final draw (the
  *     correction, the bonus, or the tree's last token) is the inverse CDF in ascending
@@ -86,9 +86,6 @@ size_t spec_workspace_bytes(int op, int B, int R, int V);
 
 /* Human-readable name of a status code (static string). */
 const char* spec_status_str(int status);
-
-/* Enqueue a kernel that zero-fills `ws_bytes` bytes of `workspace` on `stream`. */
-int spec_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
 /* Greedy chain verify (spec_origins, "Blockwise Parallel Decoding", verify).
  *   logits       [B][G+1][V] target logits; row i scores the token after draft i-1.

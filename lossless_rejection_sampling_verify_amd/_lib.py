@@ -48,8 +48,6 @@ def lib():
         L.spec_workspace_bytes.restype = sz
         L.spec_status_str.argtypes = [ip]
         L.spec_status_str.restype = ctypes.c_char_p
-        L.spec_workspace_init.argtypes = [vp, sz, vp]
-        L.spec_workspace_init.restype = ip
         L.spec_verify_greedy.argtypes = [vp, ip, vp, ip, ip, ip, vp, vp, vp, sz, vp]
         L.spec_verify_greedy.restype = ip
         L.spec_verify_chain.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp, vp, sz, vp]

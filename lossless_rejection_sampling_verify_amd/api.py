@@ -45,17 +45,17 @@ def _stream(device, stream):
 
 
 def workspace(op: int, B: int, R: int, V: int, device) -> torch.Tensor:
-    """A zero-filled workspace big enough for the call, cached per device and kind.
+    """A workspace big enough for the call, cached per device and kind.
 
-    The library leaves the workspace's counters at zero after every completed call, so a
-    cached buffer can be reused by later calls issued on the same stream."""
+    The library needs no initialised contents, so one cached buffer serves every later
+    call issued on the same stream."""
     need = L.workspace_bytes(op, B, R, V)
     if need == 0:
         raise ValueError("unsupported sizes")
     key = (torch.device(device), op)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 

@@ -1,22 +1,26 @@
 // spec_verify.hip -- HIP kernels for CDNA4 (gfx950) and the C ABI of the speculative
 // decoding verify library (include/spec_verify.h).
 //
-// Kernels
-//   k_rows      streams every target-logit row once from HBM (16-byte vector loads,
-//               kUnroll loads in flight per lane), split over `S` workgroups per row.
-//               Each workgroup reduces its chunk to one 16-byte record: the chunk max,
-//               the lowest index attaining it (greedy) and sum exp((l - m)/T) relative to
-//               the chunk max (sampling), accumulated in fp32 per batch and fp64 across
-//               batches.  Wave64 butterfly shuffles, then LDS across the 4 waves.
-//               For the chain calls the last workgroup of a request to finish (arrival
-//               counter per request) merges that request's records in split order and
-//               runs the acceptance scan; greedy requests and bonus draws end there.
-//   k_residual  chain requests rejected at position k: sum of max(0, p_k - q_k) over each
-//               chunk of row k (target row re-read from cache, q row from HBM); the last
-//               workgroup of the request locates the chunk holding u * S and scans it.
-//   k_tree      one workgroup per request: validates the parent array (pointer jumping
-//               for depths), walks the tree level by level from the records, then draws
-//               the last token with the tried children removed.
+// Kernels (consecutive launches on the caller's stream; every hand-off between workgroups
+// goes through global memory at a kernel boundary, never through fences inside a kernel:
+// on a multi-XCD part an agent-scope fence writes back and invalidates the whole L2)
+//   k_rows          streams every target-logit row once from HBM (16-byte non-temporal
+//                   vector loads, kUnroll loads in flight per lane), split over `S`
+//                   workgroups per row.  Each workgroup reduces its chunk to one 16-byte
+//                   record: the chunk max, the lowest index attaining it (greedy) and
+//                   sum exp((l - m)/T) relative to the chunk max (sampling).
+//   k_greedy_merge  one workgroup per request: row argmax from the records, first
+//                   mismatch with the drafts, emitted tokens.
+//   k_chain_accept  one workgroup per request: row max and normaliser from the records,
+//                   p(x_i) / q(x_i) acceptance scan in fp64, accepted prefix, and the
+//                   state of the final draw (correction from row k, or bonus from row G).
+//   k_tree          one workgroup per request: validates the parent array (pointer
+//                   jumping for depths), row statistics of every node and the target
+//                   probability of every node's token, then the level-by-level walk.
+//   k_mass          one workgroup per (request, fine chunk of ~4096 elements): weight of
+//                   the chunk in the row the final token is drawn from.
+//   k_draw          one workgroup per request: locates the fine chunk holding u * total
+//                   and scans it in an LDS tile (inverse CDF in ascending token id).
 //
 // Sources: llm-infra-atlas "Speculative Decoding" section 0 and section 2; ricardokevins
 // "Speculative Decoding", correction sampling, Eq. a(x) and Eq. r(x); zdszero
@@ -38,10 +42,12 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kUnroll = 4;
 constexpr int kMaxSplits = 64;
+constexpr long kChunkBytes = 64 * 1024;  // target logit bytes per row-pass workgroup
+constexpr int kTile = 4096;     // weights per LDS tile of the final draw
+constexpr int kMaxFine = 256;  // fine chunks per row in the final draw
 constexpr int kMaxRows = SPEC_MAX_G + 1;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-enum RowMode { kGreedyChain = 0, kSamplingChain = 1, kRowsOnlyGreedy = 2, kRowsOnlySampling = 3 };
 
 // One record per (row, split): chunk max, lowest index attaining it, and the chunk's
 // sum of exp2((l - m) * log2(e) / T) relative to that max (sampling only).
@@ -51,14 +57,20 @@ struct alignas(16) Part {
     double z;
 };
 
-// Handed from the acceptance scan to the residual pass of a rejected chain request.
-struct alignas(16) ResidState {
-    int k;
-    float M;     // max of row k
-    float s2;    // log2(e) / T
-    float invZ;  // 1 / Z rounded to fp32 (residual weights)
-    double Z;    // sum exp((l - M) / T) over row k
-    double T;
+// What the last token of a request is drawn from, handed from the acceptance scan (chain)
+// or the walk (tree) to k_mass and k_draw.  Every call writes it for every request.
+enum DrawKind { kDrawNone = -1, kDrawResidual = 0, kDrawTarget = 1 };
+struct alignas(16) DrawState {
+    int kind;    // kDrawNone: nothing to draw (invalid request, greedy tree)
+    int row;     // logit row b * R + k (chain) or b * N + cur (tree)
+    int qrow;    // kDrawResidual: q row b * G + k
+    int out;     // index of the drawn token in out_tokens / probs_out
+    int coin;    // index of its coin in coins
+    int nexcl;   // tree: distinct tokens of the children tried last, in excl[b][...]
+    float M;     // row max
+    float invZ;  // 1 / Z rounded to fp32 (weights)
+    double Z;    // sum exp((l - M) / T) over the row
+    double T;    // temperature
 };
 
 struct KArgs {
@@ -69,20 +81,26 @@ struct KArgs {
     const float* coins;
     const float* temperature;
     int B, R, V, S, chunk, D;
+    int S2, fine;        // fine chunks of the final draw: S2 chunks of `fine` elements
     float th_single, th_acc;
     int32_t* accept_len;
     int32_t* out_tokens;
     int32_t* accepted_nodes;
     float* probs;
-    uint32_t* ticketA;
-    uint32_t* ticketB;
-    Part* parts;
-    ResidState* state;
-    double* resid;
+    Part* parts;         // [rows][S] records of the row pass
+    DrawState* dstate;   // [B]
+    double* mass;        // [B][kMaxFine] weight of each fine chunk
+    double* massfb;      // [B][kMaxFine] fallback weight (the plain target row)
+    int32_t* excl;       // [B][SPEC_MAX_N] tree: excluded tokens of the final draw
 };
 
 // ---------------------------------------------------------------------------------------
 // element access
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load that does not displace reusable lines from the caches.
+__device__ inline u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
 template <typename T>
 struct Ld;
@@ -91,7 +109,7 @@ template <>
 struct Ld<float> {
     static constexpr int kVec = 4;
     __device__ static float one(const float* p) { return *p; }
-    __device__ static void unpack(const uint4& v, float* f) {
+    __device__ static void unpack(const u32x4& v, float* f) {
         f[0] = __uint_as_float(v.x);
         f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z);
@@ -103,7 +121,7 @@ template <>
 struct Ld<uint16_t> {  // bf16 bit patterns: the value is the high half of an fp32
     static constexpr int kVec = 8;
     __device__ static float one(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
-    __device__ static void unpack(const uint4& v, float* f) {
+    __device__ static void unpack(const u32x4& v, float* f) {
         f[0] = __uint_as_float(v.x << 16);
         f[1] = __uint_as_float(v.x & 0xffff0000u);
         f[2] = __uint_as_float(v.y << 16);
@@ -145,24 +163,6 @@ __device__ inline void wave_argmax(float& v, int& i) {
     }
 }
 
-// (m, z) with z relative to m: merge two partial softmax sums.
-__device__ inline void soft_merge(float& m, double& z, float m2, double z2, float s2) {
-    float M = fmaxf(m, m2);
-    if (M == -INFINITY) return;
-    double a = (m == M) ? z : z * (double)ex2((m - M) * s2);
-    double c = (m2 == M) ? z2 : z2 * (double)ex2((m2 - M) * s2);
-    m = M;
-    z = a + c;
-}
-
-__device__ inline void wave_soft(float& m, double& z, float s2) {
-    for (int o = 32; o > 0; o >>= 1) {
-        float m2 = __shfl_xor(m, o);
-        double z2 = __shfl_xor(z, o);
-        soft_merge(m, z, m2, z2, s2);
-    }
-}
-
 struct Smem {
     float M[kMaxRows];
     double Z[kMaxRows];
@@ -172,14 +172,8 @@ struct Smem {
     float l[kMaxRows];
     float qx[kMaxRows];
     float u[kMaxRows];
-    double P[kMaxSplits];   // chunk masses of the row being drawn from
-    double f[kMaxSplits];   // chunk scale exp((m_s - M) / T)
+    double cm[kMaxFine];    // fine-chunk weights of the row being drawn from
     double wtot[kWaves];
-    float rm[kWaves];
-    double rz[kWaves];
-    int ri[kWaves];
-    int ex_local[64];
-    int n_ex_local;
     int k;
     int sstar;
     int fallback;
@@ -187,334 +181,236 @@ struct Smem {
     int found;
     int lastthr;
     int result;
-    int last;
 };
 
 // ---------------------------------------------------------------------------------------
 // the row pass of one chunk: per-thread streaming state, then a block reduction
+//
+// Each lane takes kUnroll 16-byte vectors per batch, strided by the block so that every
+// load instruction of the wave is one contiguous 1 KB segment.  Within a lane, batches
+// arrive in ascending index order, and so do the vectors within a batch.
+//   sampling: online (m, z): per batch the batch max, one rescale of z if it grew, then
+//             sum exp2((l - m) * log2(e) / T) in fp32 over the batch, added to z in fp64.
+//   greedy:   only the running max and the first batch that reached it; the exact lowest
+//             index is resolved once per workgroup, after the block max is known, by the
+//             lanes that hold it re-reading that one batch.
 
-template <typename T, bool kSampling>
-struct RowState {
-    float m = -INFINITY;
-    int idx = INT_MAX;
-    double z = 0.0;
-
-    // elements must arrive in ascending index order per thread (greedy keeps the first)
-    __device__ void push(float x, int j, float s2) {
-        if (kSampling) {
-            if (x > m) {
-                z *= (double)ex2((m - x) * s2);
-                m = x;
-            }
-            if (m != -INFINITY) z += (double)ex2((x - m) * s2);
-        } else if (x > m) {
-            m = x;
-            idx = j;
-        }
-    }
-
-    template <int kN>
-    __device__ void push_batch(const float* f, const int* vec_base, float s2) {
-        float bm = f[0];
-#pragma unroll
-        for (int e = 1; e < kN; ++e) bm = fmaxf(bm, f[e]);
-        if (kSampling) {
-            if (bm > m) {
-                z *= (double)ex2((m - bm) * s2);
-                m = bm;
-            }
-            if (m != -INFINITY) {
-                constexpr int kVec = Ld<T>::kVec;
-                float acc = 0.f;
-#pragma unroll
-                for (int u = 0; u < kN / kVec; ++u) {
-                    float e8[kVec];
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) e8[e] = ex2((f[u * kVec + e] - m) * s2);
-                    float s;
-                    if (kVec == 8)
-                        s = ((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7]));
-                    else
-                        s = (e8[0] + e8[1]) + (e8[2] + e8[3]);
-                    acc += s;
-                }
-                z += (double)acc;
-            }
-        } else if (bm > m) {
-            constexpr int kVec = Ld<T>::kVec;
-#pragma unroll
-            for (int e = 0; e < kN; ++e) {
-                if (f[e] == bm) {
-                    m = bm;
-                    idx = vec_base[e / kVec] + (e % kVec);
-                    break;
-                }
-            }
-        }
-    }
+struct RowSmem {
+    float rm[kWaves];
+    double rz[kWaves];
+    int ri[kWaves];
 };
 
-// Reduces chunk [c0, c1) of a row into one record (valid in thread 0).
+// Block-wide max of v (every thread gets it).
+__device__ inline float block_max(float v, RowSmem& sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max(v);
+    if (lane == 0) sm.rm[wave] = v;
+    __syncthreads();
+    float r = sm.rm[0];
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, sm.rm[w]);
+    return r;
+}
+
+// Block-wide min of v (every thread gets it).
+__device__ inline int block_min(int v, RowSmem& sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    if (lane == 0) sm.ri[wave] = v;
+    __syncthreads();
+    int r = sm.ri[0];
+    for (int w = 1; w < kWaves; ++w) r = min(r, sm.ri[w]);
+    return r;
+}
+
+// Reduces chunk [c0, c1) of a row into one record (valid in every thread).
 template <typename T, bool kSampling>
-__device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1, float s2, Smem& sm) {
+__device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
+                                                            float s2, RowSmem& sm) {
     constexpr int kVec = Ld<T>::kVec;
+    constexpr int kN = kUnroll * kVec;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    RowState<T, kSampling> st;
     const int n = c1 > c0 ? c1 - c0 : 0;
     const T* p = rowp + c0;
     int head = (int)(((16u - ((uint32_t)(uintptr_t)p & 15u)) & 15u) / sizeof(T));
     if (head > n) head = n;
     const int nv = (n - head) / kVec;
     const int tail0 = head + nv * kVec;
-    if (tid < head) st.push(Ld<T>::one(p + tid), c0 + tid, s2);
-    const uint4* vp = reinterpret_cast<const uint4*>(p + head);
-    const int ebase = c0 + head;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(p + head);
+    const int ebase = c0 + head;  // row index of the first vector element
+
+    float m = -INFINITY;   // running max (sampling: reference of z)
+    double z = 0.0;        // sampling: sum exp2((l - m) * s2)
+    int bfirst = -1;       // greedy: first vector of the batch that first reached m
+    int bcount = 0;        //         vectors in that batch (kUnroll, or 1 in the remainder)
+    float ms = -INFINITY;  // greedy: max over this lane's scalar head / tail elements
+    int is = INT_MAX;      //         lowest index attaining ms
+
+    auto scalar = [&](int e) {  // one element at chunk offset e (head or tail)
+        const float x = Ld<T>::one(p + e);
+        if (kSampling) {
+            if (x > m) {
+                z *= (double)ex2((m - x) * s2);
+                m = x;
+            }
+            if (m != -INFINITY) z += (double)ex2((x - m) * s2);
+        } else if (x > ms) {
+            ms = x;
+            is = c0 + e;
+        }
+    };
+    auto batch = [&](const float* f, int cnt, int vfirst) {
+        float bm = f[0];
+        for (int e = 1; e < cnt; ++e) bm = fmaxf(bm, f[e]);
+        if (kSampling) {
+            if (bm > m) {
+                z *= (double)ex2((m - bm) * s2);
+                m = bm;
+            }
+            if (m != -INFINITY) {
+                float acc = 0.f;
+                for (int u = 0; u < cnt / kVec; ++u) {
+                    float e8[kVec];
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) e8[e] = ex2((f[u * kVec + e] - m) * s2);
+                    float t;
+                    if (kVec == 8)
+                        t = ((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7]));
+                    else
+                        t = (e8[0] + e8[1]) + (e8[2] + e8[3]);
+                    acc += t;
+                }
+                z += (double)acc;
+            }
+        } else if (bm > m) {
+            m = bm;
+            bfirst = vfirst;
+            bcount = cnt / kVec;
+        }
+    };
+
+    if (tid < head) scalar(tid);
     int v = tid;
     for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
-        uint4 raw[kUnroll];
+        u32x4 raw[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) raw[u] = vp[v + u * kBlock];
-        float f[kUnroll * kVec];
-        int vb[kUnroll];
+        for (int u = 0; u < kUnroll; ++u) raw[u] = ld_stream(vp + v + u * kBlock);
+        float f[kN];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            Ld<T>::unpack(raw[u], f + u * kVec);
-            vb[u] = ebase + (v + u * kBlock) * kVec;
-        }
-        st.template push_batch<kUnroll * kVec>(f, vb, s2);
+        for (int u = 0; u < kUnroll; ++u) Ld<T>::unpack(raw[u], f + u * kVec);
+        batch(f, kN, v);
     }
     for (; v < nv; v += kBlock) {
-        uint4 raw = vp[v];
+        const u32x4 raw = ld_stream(vp + v);
         float f[kVec];
         Ld<T>::unpack(raw, f);
-        int vb[1] = {ebase + v * kVec};
-        st.template push_batch<kVec>(f, vb, s2);
+        batch(f, kVec, v);
     }
-    if (tail0 + tid < n) st.push(Ld<T>::one(p + tail0 + tid), c0 + tail0 + tid, s2);
+    if (tail0 + tid < n) scalar(tail0 + tid);
 
-    float m = st.m;
-    int idx = st.idx;
-    double z = st.z;
-    if (kSampling)
-        wave_soft(m, z, s2);
-    else
-        wave_argmax(m, idx);
-    if (lane == 0) {
-        sm.rm[wave] = m;
-        sm.ri[wave] = idx;
-        sm.rz[wave] = z;
-    }
-    __syncthreads();
     Part r;
-    r.m = sm.rm[0];
-    r.idx = sm.ri[0];
-    r.z = sm.rz[0];
-    for (int w = 1; w < kWaves; ++w) {
-        if (kSampling)
-            soft_merge(r.m, r.z, sm.rm[w], sm.rz[w], s2);
-        else
-            arg_merge(r.m, r.idx, sm.rm[w], sm.ri[w]);
+    if (kSampling) {  // block max, then every lane rescales its sum to it once
+        const float M = block_max(m, sm);
+        double zz = 0.0;
+        if (m != -INFINITY) zz = m == M ? z : z * (double)ex2((m - M) * s2);
+        zz = wave_sum(zz);
+        if (lane == 0) sm.rz[wave] = zz;
+        __syncthreads();
+        double Z = sm.rz[0];
+        for (int w = 1; w < kWaves; ++w) Z += sm.rz[w];
+        r.m = M;
+        r.z = Z;
+        r.idx = INT_MAX;
+        return r;
     }
+    const float M = block_max(fmaxf(m, ms), sm);
+    int idx = INT_MAX;
+    if (M != -INFINITY) {
+        if (ms == M) idx = is;
+        if (m == M) {  // re-read the batch that first reached M; the lowest index wins
+            for (int u = 0; u < bcount; ++u) {
+                const int vv = bfirst + u * kBlock;
+                float f[kVec];
+                Ld<T>::unpack(vp[vv], f);
+                int hit = -1;
+                for (int e = kVec - 1; e >= 0; --e)
+                    if (f[e] == M) hit = e;
+                if (hit >= 0) {
+                    idx = min(idx, ebase + vv * kVec + hit);
+                    break;
+                }
+            }
+        }
+    }
+    r.m = M;
+    r.idx = block_min(idx, sm);
+    r.z = 0.0;
     return r;
 }
 
 // ---------------------------------------------------------------------------------------
-// block helpers for the final draw
+// per-row merges of the split records (one full wave; every lane gets the result bits)
 
-__device__ inline double block_excl_scan(double v, Smem& sm) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    double x = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        double y = __shfl_up(x, o);
-        if (lane >= o) x += y;
+// Row max M and Z = sum exp((l - M) / T) over the row, from its S records.
+__device__ inline void row_softmax_stats(const Part* pr, int S, double Td, float& M, double& Z) {
+    const int lane = threadIdx.x & 63;
+    float m = -INFINITY;
+    double z = 0.0;
+    if (lane < S) {
+        m = pr[lane].m;
+        z = pr[lane].z;
     }
-    double ex = __shfl_up(x, 1);
-    if (lane == 0) ex = 0.0;
-    if (lane == 63) sm.wtot[wave] = x;
-    __syncthreads();
-    double off = 0.0;
-    for (int w = 0; w < wave; ++w) off += sm.wtot[w];
-    __syncthreads();
-    return off + ex;
+    M = wave_max(m);
+    double term = 0.0;
+    if (lane < S && m != -INFINITY) term = z * exp(((double)m - (double)M) / Td);
+    Z = wave_sum(term);
 }
 
-// First j in [c0, c1) with w(j) > 0 whose inclusive prefix sum (from c0) reaches tau.
-// If rounding leaves tau beyond the total, the last j with w(j) > 0.  -1 if none is
-// positive.  Every thread of the block must call it; all get the result.
-template <typename WF>
-__device__ int scan_find(const WF& wf, int c0, int c1, double tau, Smem& sm) {
-    const int tid = threadIdx.x;
-    const int L = c1 > c0 ? c1 - c0 : 0;
-    const int len = (L + kBlock - 1) / kBlock;
-    const int j0 = c0 + tid * len;
-    const int j1 = min(c1, j0 + len);
-    double sum = 0.0;
-    int last = -1;
-    for (int j = j0; j < j1; ++j) {
-        float w = wf(j);
-        if (w > 0.f) {
-            sum += (double)w;
-            last = j;
-        }
+// Lowest index attaining the row max, or -1 when the row has no finite logit.
+__device__ inline int row_argmax(const Part* pr, int S) {
+    const int lane = threadIdx.x & 63;
+    float v = -INFINITY;
+    int ix = INT_MAX;
+    if (lane < S) {
+        v = pr[lane].m;
+        ix = pr[lane].idx;
     }
-    double ex = block_excl_scan(sum, sm);
-    if (tid == 0) {
-        sm.found = INT_MAX;
-        sm.lastthr = -1;
-        sm.result = -1;
-    }
-    __syncthreads();
-    if (sum > 0.0 && tau <= ex + sum) atomicMin(&sm.found, tid);
-    if (sum > 0.0) atomicMax(&sm.lastthr, tid);
-    __syncthreads();
-    const int found = sm.found;
-    const int who = found != INT_MAX ? found : sm.lastthr;
-    if (tid == who) {
-        int y = last;
-        if (found != INT_MAX) {
-            double C = ex;
-            for (int j = j0; j < j1; ++j) {
-                float w = wf(j);
-                if (w > 0.f) {
-                    C += (double)w;
-                    if (tau <= C) {
-                        y = j;
-                        break;
-                    }
-                }
-            }
-        }
-        sm.result = y;
-    }
-    __syncthreads();
-    const int y = sm.result;
-    __syncthreads();
-    return y;
-}
-
-template <typename T>
-struct RowWeight {  // exp2((l_j - ref) * s2), excluded tokens -> 0
-    const T* row;
-    float ref, s2;
-    const int* ex;
-    int nex;
-    __device__ float operator()(int j) const {
-        for (int e = 0; e < nex; ++e)
-            if (ex[e] == j) return 0.f;
-        return ex2((Ld<T>::one(row + j) - ref) * s2);
-    }
-};
-
-template <typename T>
-struct ResidualWeight {  // max(0, p_j - q_j) with p_j = exp2((l_j - M) * s2) / Z in fp32
-    const T* row;
-    const float* q;
-    float M, s2, invZ;
-    __device__ float operator()(int j) const {
-        float p = ex2((Ld<T>::one(row + j) - M) * s2) * invZ;
-        return fmaxf(p - q[j], 0.f);
-    }
-};
-
-// Inverse-CDF draw from the target row (temperature T) with the tokens excl[0..nexcl)
-// removed, using the row's split records for the chunk masses.  Falls back to the whole
-// row when the remaining mass is not positive.  Block-wide; every thread gets the token.
-template <typename T>
-__device__ __attribute__((always_inline)) int draw_row(const T* rowp, int V, int chunk, int S, const Part* pr, float M,
-                        float s2, double Td, double u, const int* excl, int nexcl, Smem& sm) {
-    const int tid = threadIdx.x;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        const int nx = attempt == 0 ? nexcl : 0;
-        if (tid < S) {
-            const float ms = pr[tid].m;
-            double zs = pr[tid].z;
-            const double fs = ms == -INFINITY ? 0.0 : exp(((double)ms - (double)M) / Td);
-            if (nx > 0 && ms != -INFINITY) {
-                const int c0 = tid * chunk, c1 = min(V, c0 + chunk);
-                double ex = 0.0;
-                for (int e = 0; e < nx; ++e) {
-                    const int t = excl[e];
-                    if (t >= c0 && t < c1) ex += (double)ex2((Ld<T>::one(rowp + t) - ms) * s2);
-                }
-                if (ex > 0.0) {
-                    double rem = zs - ex;
-                    zs = rem > zs * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
-                }
-            }
-            sm.P[tid] = zs * fs;
-            sm.f[tid] = fs;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double tot = 0.0;
-            for (int s = 0; s < S; ++s) tot += sm.P[s];
-            sm.fallback = !(tot > 0.0);
-            if (!sm.fallback) {
-                const double t = u * tot;
-                double pre = 0.0, before = 0.0;
-                int ss = -1, lastpos = -1;
-                for (int s = 0; s < S; ++s) {
-                    if (sm.P[s] > 0.0) {
-                        lastpos = s;
-                        if (t <= pre + sm.P[s]) {
-                            ss = s;
-                            before = pre;
-                            break;
-                        }
-                    }
-                    pre += sm.P[s];
-                }
-                if (ss < 0) {
-                    ss = lastpos;
-                    before = pre - sm.P[ss];
-                }
-                sm.sstar = ss;
-                sm.tau = (t - before) / sm.f[ss];
-                int nl = 0;
-                const int c0 = ss * chunk, c1 = min(V, c0 + chunk);
-                for (int e = 0; e < nx; ++e)
-                    if (excl[e] >= c0 && excl[e] < c1) {
-                        if (nl < 64) sm.ex_local[nl] = excl[e];
-                        ++nl;
-                    }
-                sm.n_ex_local = nl;
-            }
-        }
-        __syncthreads();
-        if (sm.fallback) {
-            __syncthreads();
-            if (nexcl == 0 || attempt == 1) return -1;  // no finite logit at all
-            continue;
-        }
-        const int ss = sm.sstar;
-        const bool local = sm.n_ex_local <= 64;
-        RowWeight<T> wf{rowp, pr[ss].m, s2, local ? sm.ex_local : excl,
-                        local ? sm.n_ex_local : nx};
-        const int c0 = ss * chunk, c1 = min(V, c0 + chunk);
-        int y = scan_find(wf, c0, c1, sm.tau, sm);
-        if (y < 0) y = pr[ss].idx >= 0 && pr[ss].idx < V ? pr[ss].idx : c0;
-        return y;
-    }
-    return -1;
+    wave_argmax(v, ix);
+    return v == -INFINITY ? -1 : ix;
 }
 
 // ---------------------------------------------------------------------------------------
-// merges run by the last workgroup of a chain request
+// k_rows: one workgroup per (row, split)
+
+template <typename T, bool kSampling>
+__global__ __launch_bounds__(kBlock) void k_rows(KArgs a) {
+    __shared__ RowSmem sm;
+    const int S = a.S;
+    const int blk = blockIdx.x;
+    const int row = blk / S;
+    const int s = blk - row * S;
+    const int b = row / a.R;
+    const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)row * a.V;
+    const int c0 = s * a.chunk;
+    const int c1 = min(a.V, c0 + a.chunk);
+    float s2 = 0.f;
+    if (kSampling) s2 = kLog2e / a.temperature[b];
+    const Part r = chunk_record<T, kSampling>(rowp, c0, c1, s2, sm);
+    if (threadIdx.x == 0) a.parts[(size_t)row * S + s] = r;
+}
+
+// ---------------------------------------------------------------------------------------
+// k_greedy_merge: one workgroup per request
 
 template <typename T>
-__device__ void merge_greedy_chain(const KArgs& a, int b, Smem& sm) {
+__global__ __launch_bounds__(kBlock) void k_greedy_merge(KArgs a) {
+    __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = a.R, G = R - 1, S = a.S;
+    const int b = blockIdx.x;
     for (int i = wave; i < R; i += kWaves) {
-        const Part* pr = a.parts + ((size_t)b * R + i) * kMaxSplits;
-        float v = -INFINITY;
-        int ix = INT_MAX;
-        if (lane < S) {
-            v = pr[lane].m;
-            ix = pr[lane].idx;
-        }
-        wave_argmax(v, ix);
-        if (lane == 0) sm.arg[i] = v == -INFINITY ? -1 : ix;
+        const int ix = row_argmax(a.parts + ((size_t)b * R + i) * S, S);
+        if (lane == 0) sm.arg[i] = ix;
     }
     for (int i = tid; i < G; i += kBlock) sm.x[i] = a.tokens[(size_t)b * G + i];
     __syncthreads();
@@ -545,26 +441,49 @@ __device__ void merge_greedy_chain(const KArgs& a, int b, Smem& sm) {
     }
 }
 
+// Four consecutive target logits as one load (8 bytes of bf16 or 16 bytes of fp32).
 template <typename T>
-__device__ void merge_sampling_chain(const KArgs& a, int b, Smem& sm) {
+struct Quad;
+template <>
+struct Quad<float> {
+    typedef u32x4 Raw;
+    Raw raw;
+    __device__ static void unpack(const Raw& r, float* l) {
+        l[0] = __uint_as_float(r.x);
+        l[1] = __uint_as_float(r.y);
+        l[2] = __uint_as_float(r.z);
+        l[3] = __uint_as_float(r.w);
+    }
+};
+template <>
+struct Quad<uint16_t> {
+    typedef unsigned int Raw __attribute__((ext_vector_type(2)));
+    Raw raw;
+    __device__ static void unpack(const Raw& r, float* l) {
+        l[0] = __uint_as_float(r.x << 16);
+        l[1] = __uint_as_float(r.x & 0xffff0000u);
+        l[2] = __uint_as_float(r.y << 16);
+        l[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+};
+
+// ---------------------------------------------------------------------------------------
+// k_chain_accept: one workgroup per request
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
+    __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = a.R, G = R - 1, S = a.S, V = a.V;
+    const int b = blockIdx.x;
     const float Tf = a.temperature[b];
     const bool t_ok = isfinite(Tf) && Tf > 0.f;
     const double Td = (double)Tf;
-    const float s2 = kLog2e / Tf;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
     for (int i = wave; i < R; i += kWaves) {
-        const Part* pr = a.parts + ((size_t)b * R + i) * kMaxSplits;
-        float m = -INFINITY;
-        double z = 0.0;
-        if (lane < S) {
-            m = pr[lane].m;
-            z = pr[lane].z;
-        }
-        const float M = wave_max(m);
-        double term = 0.0;
-        if (lane < S && m != -INFINITY) term = z * exp(((double)m - (double)M) / Td);
-        const double Z = wave_sum(term);
+        float M;
+        double Z;
+        row_softmax_stats(a.parts + ((size_t)b * R + i) * S, S, Td, M, Z);
         if (lane == 0) {
             sm.M[i] = M;
             sm.Z[i] = Z;
@@ -576,7 +495,7 @@ __device__ void merge_sampling_chain(const KArgs& a, int b, Smem& sm) {
             const int xi = a.tokens[(size_t)b * G + i];
             sm.x[i] = xi;
             if (xi >= 0 && xi < V) {
-                sm.l[i] = Ld<T>::one(reinterpret_cast<const T*>(a.logits) + ((size_t)b * R + i) * V + xi);
+                sm.l[i] = Ld<T>::one(logits + ((size_t)b * R + i) * V + xi);
                 sm.qx[i] = a.q[((size_t)b * G + i) * V + xi];
             }
         }
@@ -610,16 +529,21 @@ __device__ void merge_sampling_chain(const KArgs& a, int b, Smem& sm) {
         }
         sm.k = valid ? k : -1;
         a.accept_len[b] = sm.k;
-        if (valid && k < G) {
-            ResidState st;
-            st.k = k;
+        DrawState st = {};
+        st.kind = kDrawNone;
+        if (valid) {
+            st.kind = k < G ? kDrawResidual : kDrawTarget;
+            st.row = b * R + k;
+            st.qrow = b * G + k;
+            st.out = b * R + k;
+            st.coin = b * R + G;
+            st.nexcl = 0;
             st.M = sm.M[k];
-            st.s2 = s2;
             st.Z = sm.Z[k];
             st.invZ = (float)(1.0 / sm.Z[k]);
             st.T = Td;
-            a.state[b] = st;
         }
+        a.dstate[b] = st;
     }
     __syncthreads();
     const int k = sm.k;
@@ -630,174 +554,9 @@ __device__ void merge_sampling_chain(const KArgs& a, int b, Smem& sm) {
             t = sm.x[i];
             pr = (float)sm.p[i];
         }
-        if (i != k) {  // slot k is written by the final draw (bonus here, residual pass later)
+        if (i != k) {  // slot k is written by the final draw
             a.out_tokens[(size_t)b * R + i] = t;
             if (a.probs) a.probs[(size_t)b * R + i] = pr;
-        }
-    }
-    if (k != G) return;
-    // bonus: every draft accepted, draw from row G
-    const T* rowp = reinterpret_cast<const T*>(a.logits) + ((size_t)b * R + G) * V;
-    const Part* pr = a.parts + ((size_t)b * R + G) * kMaxSplits;
-    const double u = (double)sm.u[G];
-    const int y = draw_row<T>(rowp, V, a.chunk, S, pr, sm.M[G], s2, Td, u, nullptr, 0, sm);
-    if (tid == 0) {
-        a.out_tokens[(size_t)b * R + G] = y;
-        if (a.probs) {
-            const double l = (double)Ld<T>::one(rowp + y);
-            a.probs[(size_t)b * R + G] = (float)(exp((l - (double)sm.M[G]) / Td) / sm.Z[G]);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// k_rows: one workgroup per (row, split)
-
-template <typename T, int kMode>
-__global__ __launch_bounds__(kBlock) void k_rows(KArgs a) {
-    constexpr bool kSampling = kMode == kSamplingChain || kMode == kRowsOnlySampling;
-    __shared__ Smem sm;
-    const int S = a.S;
-    const int blk = blockIdx.x;
-    const int row = blk / S;
-    const int s = blk - row * S;
-    const int b = row / a.R;
-    const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)row * a.V;
-    const int c0 = s * a.chunk;
-    const int c1 = min(a.V, c0 + a.chunk);
-    float s2 = 0.f;
-    if (kSampling) s2 = kLog2e / a.temperature[b];
-    const Part r = chunk_record<T, kSampling>(rowp, c0, c1, s2, sm);
-    if (threadIdx.x == 0) a.parts[(size_t)row * kMaxSplits + s] = r;
-    if (kMode == kRowsOnlyGreedy || kMode == kRowsOnlySampling) return;
-
-    // the last workgroup of request b to finish merges its records
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t t = atomicAdd(&a.ticketA[b], 1u);
-        sm.last = t == (uint32_t)(a.R * S - 1);
-    }
-    __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
-    if (threadIdx.x == 0) a.ticketA[b] = 0u;  // every other arrival has happened
-    if (kMode == kGreedyChain)
-        merge_greedy_chain<T>(a, b, sm);
-    else
-        merge_sampling_chain<T>(a, b, sm);
-}
-
-// ---------------------------------------------------------------------------------------
-// k_residual: chain requests rejected at k < G
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_residual(KArgs a) {
-    __shared__ Smem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int S = a.S, R = a.R, G = R - 1, V = a.V;
-    const int b = blockIdx.x / S;
-    const int s = blockIdx.x - b * S;
-    const ResidState st = a.state[b];
-    const int acc = a.accept_len[b];
-    if (acc < 0 || acc >= G) return;  // invalid, or the bonus was already drawn
-    const int k = st.k;
-    const T* rowp = reinterpret_cast<const T*>(a.logits) + ((size_t)b * R + k) * V;
-    const float* qrow = a.q + ((size_t)b * G + k) * V;
-    const ResidualWeight<T> wf{rowp, qrow, st.M, st.s2, st.invZ};
-    const int c0 = s * a.chunk, c1 = min(V, c0 + a.chunk);
-
-    double sum = 0.0;
-    const int n = c1 > c0 ? c1 - c0 : 0;
-    const bool aligned = (((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0) &&
-                         (((uintptr_t)(qrow + c0)) % 16 == 0);
-    int done = 0;
-    if (aligned) {
-        const int nv = n / 4;
-        for (int v = tid; v < nv; v += kBlock) {
-            const float4 qv = *reinterpret_cast<const float4*>(qrow + c0 + 4 * v);
-            float l[4];
-            if (sizeof(T) == 4) {
-                const float4 lv = *reinterpret_cast<const float4*>(rowp + c0 + 4 * v);
-                l[0] = lv.x; l[1] = lv.y; l[2] = lv.z; l[3] = lv.w;
-            } else {
-                const uint2 lv = *reinterpret_cast<const uint2*>(rowp + c0 + 4 * v);
-                l[0] = __uint_as_float(lv.x << 16);
-                l[1] = __uint_as_float(lv.x & 0xffff0000u);
-                l[2] = __uint_as_float(lv.y << 16);
-                l[3] = __uint_as_float(lv.y & 0xffff0000u);
-            }
-            const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
-            float w4 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p = ex2((l[e] - st.M) * st.s2) * st.invZ;
-                w4 += fmaxf(p - qq[e], 0.f);
-            }
-            sum += (double)w4;
-        }
-        done = nv * 4;
-    }
-    for (int j = c0 + done + tid; j < c1; j += kBlock) sum += (double)wf(j);
-    sum = wave_sum(sum);
-    if (lane == 0) sm.wtot[wave] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        double tot = 0.0;
-        for (int w = 0; w < kWaves; ++w) tot += sm.wtot[w];
-        a.resid[(size_t)b * kMaxSplits + s] = tot;
-        __threadfence();
-        const uint32_t t = atomicAdd(&a.ticketB[b], 1u);
-        sm.last = t == (uint32_t)(S - 1);
-    }
-    __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
-    const double u = (double)a.coins[(size_t)b * R + G];
-    if (tid == 0) {
-        a.ticketB[b] = 0u;
-        double tot = 0.0;
-        for (int c = 0; c < S; ++c) tot += a.resid[(size_t)b * kMaxSplits + c];
-        sm.fallback = !(tot > 0.0);
-        if (!sm.fallback) {
-            const double t = u * tot;
-            double pre = 0.0, before = 0.0;
-            int ss = -1, lastpos = -1;
-            for (int c = 0; c < S; ++c) {
-                const double Pc = a.resid[(size_t)b * kMaxSplits + c];
-                if (Pc > 0.0) {
-                    lastpos = c;
-                    if (t <= pre + Pc) {
-                        ss = c;
-                        before = pre;
-                        break;
-                    }
-                }
-                pre += Pc;
-            }
-            if (ss < 0) {
-                ss = lastpos;
-                before = pre - a.resid[(size_t)b * kMaxSplits + ss];
-            }
-            sm.sstar = ss;
-            sm.tau = t - before;
-        }
-    }
-    __syncthreads();
-    int y;
-    if (sm.fallback) {  // residual mass not positive: draw from p_k itself
-        const Part* pr = a.parts + ((size_t)b * R + k) * kMaxSplits;
-        y = draw_row<T>(rowp, V, a.chunk, S, pr, st.M, st.s2, st.T, u, nullptr, 0, sm);
-    } else {
-        const int ss = sm.sstar;
-        const int cs0 = ss * a.chunk, cs1 = min(V, cs0 + a.chunk);
-        y = scan_find(wf, cs0, cs1, sm.tau, sm);
-        if (y < 0) y = cs0;  // unreachable for a positive chunk mass
-    }
-    if (tid == 0) {
-        a.out_tokens[(size_t)b * R + k] = y;
-        if (a.probs) {
-            const double l = (double)Ld<T>::one(rowp + y);
-            a.probs[(size_t)b * R + k] = (float)(exp((l - (double)st.M) / st.T) / st.Z);
         }
     }
 }
@@ -808,63 +567,79 @@ __global__ __launch_bounds__(kBlock) void k_residual(KArgs a) {
 struct TreeSmem {
     int par[SPEC_MAX_N];
     int tok[SPEC_MAX_N];
-    int anc[SPEC_MAX_N];
-    int dep[SPEC_MAX_N];
-    int kids[SPEC_MAX_N];
-    int excl[SPEC_MAX_N];
-    double pc[SPEC_MAX_N];
+    union {
+        struct {  // validation: pointer-jumping state
+            int anc[SPEC_MAX_N];
+            int dep[SPEC_MAX_N];
+        };
+        struct {  // the walk: children of the current node, tokens to exclude
+            int kids[SPEC_MAX_N];
+            int excl[SPEC_MAX_N];
+        };
+    };
+    float M[SPEC_MAX_N];     // row max
+    int arg[SPEC_MAX_N];     // greedy: row argmax (lowest id), -1 if no finite logit
+    double Z[SPEC_MAX_N];    // sampling: sum exp((l - M) / T) over the row
+    double pc[SPEC_MAX_N];   // sampling: p_parent(token of node c), by node id
     int wcnt[kWaves];
     int chosen;
-    int nkids;
-    float M;
-    double Z;
-    int arg;
 };
 
-template <typename T>
-__device__ void tree_row_stats(const KArgs& a, int b, int j, bool sampling, double Td, float s2,
-                               TreeSmem& ts) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    if (tid < 64) {
-        const Part* pr = a.parts + ((size_t)b * a.R + j) * kMaxSplits;
+// Statistics of all N rows of request b from their records, g = 2^ceil(log2 S) lanes per
+// row, 64 / g rows per wave at a time.  The butterflies use only xor offsets below g, so
+// the sums are the same bits as a full-wave butterfly with zero padding.
+__device__ void tree_row_stats(const KArgs& a, int b, bool sampling, double Td, TreeSmem& ts) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int S = a.S, N = a.R;
+    int g = 1;
+    while (g < S) g <<= 1;
+    const int per_wave = 64 / g;
+    const int sub = lane / g, s = lane - sub * g;
+    for (int j0 = wave * per_wave; j0 < N; j0 += kWaves * per_wave) {  // uniform per wave
+        const int j = j0 + sub;
+        const bool have = j < N && s < S;
         float m = -INFINITY;
         int ix = INT_MAX;
         double z = 0.0;
-        if (lane < a.S) {
-            m = pr[lane].m;
-            ix = pr[lane].idx;
-            z = pr[lane].z;
+        if (have) {
+            const Part pr = a.parts[((size_t)b * N + j) * S + s];
+            m = pr.m;
+            ix = pr.idx;
+            z = pr.z;
         }
         if (sampling) {
-            const float M = wave_max(m);
-            double term = 0.0;
-            if (lane < a.S && m != -INFINITY) term = z * exp(((double)m - (double)M) / Td);
-            const double Z = wave_sum(term);
-            if (lane == 0) {
-                ts.M = M;
-                ts.Z = Z;
+            float M = m;
+            for (int o = g >> 1; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+            double term = (have && m != -INFINITY) ? z * exp(((double)m - (double)M) / Td) : 0.0;
+            for (int o = g >> 1; o > 0; o >>= 1) term += __shfl_xor(term, o);
+            if (s == 0 && j < N) {
+                ts.M[j] = M;
+                ts.Z[j] = term;
             }
         } else {
-            wave_argmax(m, ix);
-            if (lane == 0) {
-                ts.M = m;
-                ts.arg = ix;
+            for (int o = g >> 1; o > 0; o >>= 1) {
+                const float v2 = __shfl_xor(m, o);
+                const int i2 = __shfl_xor(ix, o);
+                arg_merge(m, ix, v2, i2);
+            }
+            if (s == 0 && j < N) {
+                ts.M[j] = m;
+                ts.arg[j] = m == -INFINITY ? -1 : ix;
             }
         }
     }
-    (void)s2;
     __syncthreads();
 }
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
     __shared__ TreeSmem ts;
-    __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
-    const int N = a.R, V = a.V, D = a.D, S = a.S;
+    const int N = a.R, V = a.V, D = a.D;
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
     bool bad = false;
     for (int i = tid; i < N; i += kBlock) {
         const int p = par_g[i];
@@ -887,8 +662,10 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
             if (!(u > 0.f && u <= 1.f)) bad = true;
         }
     }
+    const double Td = (double)Tf;
     bad = __syncthreads_or(bad);
-    if (!bad) {  // depths by pointer jumping (parents[i] < i: every chain ends at the root)
+    if (!bad) {
+        // depths by pointer jumping (parents[i] < i: every chain ends at the root)
         for (int i = tid; i < N; i += kBlock) {
             ts.anc[i] = i == 0 ? 0 : ts.par[i];
             ts.dep[i] = i == 0 ? 0 : 1;
@@ -914,13 +691,10 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
         __syncthreads();
         for (int i = tid; i < N; i += kBlock)
             if (ts.dep[i] > D) bad = true;
-        // every row needs a finite logit
-        for (int j = tid; j < N; j += kBlock) {
-            const Part* pr = a.parts + ((size_t)b * N + j) * kMaxSplits;
-            float m = -INFINITY;
-            for (int s = 0; s < S; ++s) m = fmaxf(m, pr[s].m);
-            if (m == -INFINITY) bad = true;
-        }
+        // every row's statistics; each row needs a finite logit
+        tree_row_stats(a, b, sampling != 0, Td, ts);
+        for (int j = tid; j < N; j += kBlock)
+            if (ts.M[j] == -INFINITY) bad = true;
         bad = __syncthreads_or(bad);
     }
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
@@ -932,13 +706,25 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
             if (d < D) nodes[d] = -1;
             if (probs) probs[d] = 0.f;
         }
-        if (tid == 0) a.accept_len[b] = -1;
+        if (tid == 0) {
+            a.accept_len[b] = -1;
+            if (sampling) {
+                DrawState st = {};
+                st.kind = kDrawNone;
+                a.dstate[b] = st;
+            }
+        }
         return;
     }
+    if (sampling) {  // target probability of every node's token under its parent's row
+        for (int c = 1 + tid; c < N; c += kBlock) {
+            const int pp = ts.par[c];
+            const double l = (double)Ld<T>::one(logits + ((size_t)b * N + pp) * V + ts.tok[c]);
+            ts.pc[c] = exp((l - (double)ts.M[pp]) / Td) / ts.Z[pp];
+        }
+        __syncthreads();
+    }
 
-    const T* logits = reinterpret_cast<const T*>(a.logits);
-    const double Td = (double)Tf;
-    const float s2 = kLog2e / Tf;
     int cur = 0, d = 0, nexcl = 0;
     for (;;) {
         // children of cur in ascending node id (ordered compaction)
@@ -962,35 +748,27 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
             nexcl = 0;
             break;
         }
-        tree_row_stats<T>(a, b, cur, sampling != 0, Td, s2, ts);
-        const T* rowp = logits + ((size_t)b * N + cur) * V;
-        if (sampling) {
-            for (int j = tid; j < count; j += kBlock) {
-                const double l = (double)Ld<T>::one(rowp + ts.tok[ts.kids[j]]);
-                ts.pc[j] = exp((l - (double)ts.M) / Td) / ts.Z;
-            }
-            __syncthreads();
-            if (tid == 0) {
+        if (tid == 0) {
+            int ch = -1;
+            if (sampling) {
                 const double u = (double)a.coins[(size_t)b * (D + 1) + d];
                 const double tha = (double)a.th_acc, ths = (double)a.th_single;
                 double acc = 0.0;
-                int ch = -1;
                 for (int j = 0; j < count; ++j) {
-                    acc += ts.pc[j];
-                    if (u <= acc / tha || ts.pc[j] >= ths) {
+                    const double pc = ts.pc[ts.kids[j]];
+                    acc += pc;
+                    if (u <= acc / tha || pc >= ths) {
                         ch = j;
                         break;
                     }
                 }
-                ts.chosen = ch;
+            } else {
+                for (int j = 0; j < count; ++j)
+                    if (ts.tok[ts.kids[j]] == ts.arg[cur]) {
+                        ch = j;
+                        break;
+                    }
             }
-        } else if (tid == 0) {
-            int ch = -1;
-            for (int j = 0; j < count; ++j)
-                if (ts.tok[ts.kids[j]] == ts.arg) {
-                    ch = j;
-                    break;
-                }
             ts.chosen = ch;
         }
         __syncthreads();
@@ -1005,31 +783,45 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
         if (tid == 0) {
             out[d] = ts.tok[c];
             nodes[d] = c;
-            if (probs) probs[d] = sampling ? (float)ts.pc[ch] : 0.f;
+            if (probs) probs[d] = sampling ? (float)ts.pc[c] : 0.f;
         }
         __syncthreads();
         cur = c;
         ++d;
     }
 
-    // final token from row cur
-    tree_row_stats<T>(a, b, cur, sampling != 0, Td, s2, ts);
-    const T* rowp = logits + ((size_t)b * N + cur) * V;
-    int y;
-    float py = 0.f;
+    // the last token: greedy emits the argmax of row cur; sampling hands row cur and the
+    // distinct tokens of the children tried last to the final draw
     if (sampling) {
-        const Part* pr = a.parts + ((size_t)b * N + cur) * kMaxSplits;
-        const double u = (double)a.coins[(size_t)b * (D + 1) + D];
-        y = draw_row<T>(rowp, V, a.chunk, S, pr, ts.M, s2, Td, u, ts.excl, nexcl, sm);
-        if (y >= 0) py = (float)(exp(((double)Ld<T>::one(rowp + y) - (double)ts.M) / Td) / ts.Z);
-    } else {
-        y = ts.arg;
+        int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
+        for (int j = tid; j < nexcl; j += kBlock) {  // keep the first copy of each token
+            const int t = ts.excl[j];
+            bool dup = false;
+            for (int i = 0; i < j && !dup; ++i) dup = ts.excl[i] == t;
+            ts.kids[j] = dup ? -1 : t;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int n = 0;
+            for (int j = 0; j < nexcl; ++j)
+                if (ts.kids[j] >= 0) ex[n++] = ts.kids[j];
+            DrawState st = {};
+            st.kind = kDrawTarget;
+            st.row = b * N + cur;
+            st.out = b * (D + 1) + d;
+            st.coin = b * (D + 1) + D;
+            st.nexcl = n;
+            st.M = ts.M[cur];
+            st.Z = ts.Z[cur];
+            st.invZ = (float)(1.0 / ts.Z[cur]);
+            st.T = Td;
+            a.dstate[b] = st;
+        }
+    } else if (tid == 0) {
+        out[d] = ts.arg[cur];
+        if (probs) probs[d] = 0.f;
     }
-    if (tid == 0) {
-        out[d] = y;
-        if (probs) probs[d] = py;
-        a.accept_len[b] = d;
-    }
+    if (tid == 0) a.accept_len[b] = d;
     for (int e = d + 1 + tid; e <= D; e += kBlock) {
         out[e] = -1;
         if (probs) probs[e] = 0.f;
@@ -1037,10 +829,357 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
     for (int e = d + tid; e < D; e += kBlock) nodes[e] = -1;
 }
 
-__global__ void k_fill_zero(uint32_t* p, size_t n) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+// ---------------------------------------------------------------------------------------
+// block helpers for the final draw
+
+__device__ inline double block_excl_scan(double v, Smem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        double y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    double ex = __shfl_up(x, 1);
+    if (lane == 0) ex = 0.0;
+    if (lane == 63) sm.wtot[wave] = x;
+    __syncthreads();
+    double off = 0.0;
+    for (int w = 0; w < wave; ++w) off += sm.wtot[w];
+    __syncthreads();
+    return off + ex;
+}
+
+// First j in [c0, c1) with w(j) > 0 whose inclusive prefix sum (from c0) reaches tau.
+// If rounding leaves tau beyond the total, the last j with w(j) > 0.  -1 if none is
+// positive.  Every thread of the block must call it; all get the result.
+//
+// The range is taken in LDS tiles of kTile weights: all lanes load and weigh a tile with
+// coalesced accesses, then each lane sums a contiguous run of kTile / kBlock weights, a
+// block exclusive scan of those run sums locates the run that crosses tau, and that
+// run's lane walks it.  Prefix sums are fp64, element by element in ascending order.
+template <typename WF>
+__device__ int scan_find(const WF& wf, int c0, int c1, double tau, const int* excl, int nexcl,
+                         float* tile, Smem& sm) {
+    constexpr int kRun = kTile / kBlock;
+    const int tid = threadIdx.x;
+    double base = 0.0;  // total weight of the tiles before this one
+    int last_pos = -1;  // last positive index seen so far
+    for (int t0 = c0; t0 < c1; t0 += kTile) {
+        const int len = min(kTile, c1 - t0);
+        {  // every lane issues all of its kRun loads before using any (clamped indices)
+            float w[kRun];
+#pragma unroll
+            for (int i = 0; i < kRun; ++i) w[i] = wf(t0 + min(tid + i * kBlock, len - 1));
+#pragma unroll
+            for (int i = 0; i < kRun; ++i)
+                if (tid + i * kBlock < len) tile[tid + i * kBlock] = w[i];
+        }
+        __syncthreads();
+        for (int e = tid; e < nexcl; e += kBlock) {  // excluded tokens weigh nothing
+            const int j = excl[e] - t0;
+            if (j >= 0 && j < len) tile[j] = 0.f;
+        }
+        __syncthreads();
+        const int r0 = tid * kRun;
+        const int r1 = min(len, r0 + kRun);
+        double sum = 0.0;
+        int last = -1;
+        for (int e = r0; e < r1; ++e) {
+            const float w = tile[e];
+            if (w > 0.f) {
+                sum += (double)w;
+                last = t0 + e;
+            }
+        }
+        const double ex = base + block_excl_scan(sum, sm);
+        if (tid == 0) {
+            sm.found = INT_MAX;
+            sm.lastthr = -1;
+        }
+        __syncthreads();
+        if (sum > 0.0 && tau <= ex + sum) atomicMin(&sm.found, tid);
+        if (sum > 0.0) atomicMax(&sm.lastthr, tid);
+        if (tid == kBlock - 1) sm.tau = ex + sum;  // running total through this tile
+        __syncthreads();
+        const int found = sm.found;
+        if (found != INT_MAX) {
+            if (tid == found) {
+                double C = ex;
+                int y = last;
+                for (int e = r0; e < r1; ++e) {
+                    const float w = tile[e];
+                    if (w > 0.f) {
+                        C += (double)w;
+                        if (tau <= C) {
+                            y = t0 + e;
+                            break;
+                        }
+                    }
+                }
+                sm.result = y;
+            }
+            __syncthreads();
+            const int y = sm.result;
+            __syncthreads();
+            return y;
+        }
+        if (sm.lastthr >= 0 && tid == sm.lastthr) sm.result = last;
+        __syncthreads();
+        if (sm.lastthr >= 0) last_pos = sm.result;
+        base = sm.tau;
+        __syncthreads();  // the tile and the scan scratch are reused
+    }
+    return last_pos;
+}
+
+// ---------------------------------------------------------------------------------------
+// the final draw: k_mass sums the weights of each fine chunk of the row the token is drawn
+// from, k_draw locates the chunk that holds u * total and scans it
+//
+// Weights, computed identically in both kernels (fp32, no contraction):
+//   p_j = exp2((l_j - M) * log2(e) / T) * (1/Z)
+//   residual (chain, rejected at k):   w_j = max(0, p_j - q_j)
+//   target (chain bonus, tree):        w_j = p_j, with the excluded tokens at 0 (tree)
+// Fallback when the total weight is not positive: w_j = p_j (the plain target row).
+
+template <typename T, bool kResidual>
+struct DrawWeight {
+    const T* row;
+    const float* q;  // residual: the draft row; otherwise unused
+    float M, s2, invZ;
+    __device__ float operator()(int j) const {
+        const float p = ex2((Ld<T>::one(row + j) - M) * s2) * invZ;
+        return kResidual ? fmaxf(p - q[j], 0.f) : p;
+    }
+};
+
+// Weights of four consecutive elements: `pw` gets the sum of the plain p_j, `ww` the sum
+// of the draw weights (residual: max(0, p_j - q_j); otherwise p_j).
+template <typename T, bool kResidual>
+__device__ inline void weigh4(const typename Quad<T>::Raw& lr, const u32x4& qr, float M,
+                              float s2, float invZ, float& pw, float& ww) {
+    float l[4];
+    Quad<T>::unpack(lr, l);
+    const float qv[4] = {__uint_as_float(qr.x), __uint_as_float(qr.y), __uint_as_float(qr.z),
+                         __uint_as_float(qr.w)};
+    float ps = 0.f, ws = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float p = ex2((l[e] - M) * s2) * invZ;
+        ps += p;
+        if (kResidual) ws += fmaxf(p - qv[e], 0.f);
+    }
+    pw = ps;
+    ww = kResidual ? ws : ps;
+}
+
+// Sums over the 16-byte aligned part of a fine chunk (4 elements per lane per step,
+// kUnroll steps in flight).  Returns the number of elements covered.
+template <typename T, bool kResidual>
+__device__ inline int mass_vec(const T* rowp, const float* qrow, int n, float M, float s2,
+                               float invZ, double& psum, double& wsum) {
+    const int tid = threadIdx.x;
+    const int nv = n / 4;
+    const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
+    const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    int v = tid;
+    for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
+        typename Quad<T>::Raw lr[kUnroll];
+        u32x4 qr[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            lr[u] = lq[v + u * kBlock].raw;
+            qr[u] = kResidual ? ld_stream(qq + v + u * kBlock) : zero;
+        }
+        float pw = 0.f, ww = 0.f;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float p4, w4;
+            weigh4<T, kResidual>(lr[u], qr[u], M, s2, invZ, p4, w4);
+            pw += p4;
+            ww += w4;
+        }
+        psum += (double)pw;
+        wsum += (double)ww;
+    }
+    for (; v < nv; v += kBlock) {
+        const u32x4 qr = kResidual ? ld_stream(qq + v) : zero;
+        float p4, w4;
+        weigh4<T, kResidual>(lq[v].raw, qr, M, s2, invZ, p4, w4);
+        psum += (double)p4;
+        wsum += (double)w4;
+    }
+    return nv * 4;
+}
+
+struct MassSmem {
+    double w[kWaves];
+    double p[kWaves];
+};
+
+// One workgroup per (request, fine chunk).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
+    __shared__ MassSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S2 = a.S2, V = a.V;
+    const int b = blockIdx.x / S2;
+    const int c = blockIdx.x - b * S2;
+    const DrawState st = a.dstate[b];
+    if (st.kind == kDrawNone) return;
+    const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
+    const float* qrow = st.kind == kDrawResidual ? a.q + (size_t)st.qrow * V : nullptr;
+    const float s2 = kLog2e / (float)st.T;
+    const int c0 = c * a.fine, c1 = min(V, c0 + a.fine);
+    const int n = c1 > c0 ? c1 - c0 : 0;
+    double wsum = 0.0, psum = 0.0;
+    const bool aligned = (((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0) &&
+                         (!qrow || ((uintptr_t)(qrow + c0)) % 16 == 0);
+    int done = 0;
+    if (aligned) {
+        if (qrow)
+            done = mass_vec<T, true>(rowp + c0, qrow + c0, n, st.M, s2, st.invZ, psum, wsum);
+        else
+            done = mass_vec<T, false>(rowp + c0, nullptr, n, st.M, s2, st.invZ, psum, wsum);
+    }
+    const DrawWeight<T, false> pf{rowp, nullptr, st.M, s2, st.invZ};
+    const DrawWeight<T, true> rf{rowp, qrow, st.M, s2, st.invZ};
+    for (int j = c0 + done + tid; j < c1; j += kBlock) {
+        const float p = pf(j);
+        psum += (double)p;
+        wsum += (double)(qrow ? rf(j) : p);
+    }
+    wsum = wave_sum(wsum);
+    psum = wave_sum(psum);
+    if (lane == 0) {
+        sm.w[wave] = wsum;
+        sm.p[wave] = psum;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double W = 0.0, P = 0.0;
+        for (int w = 0; w < kWaves; ++w) {
+            W += sm.w[w];
+            P += sm.p[w];
+        }
+        if (st.nexcl > 0) {  // tree: remove the rejected children's weight from this chunk
+            const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
+            double x = 0.0;
+            for (int e = 0; e < st.nexcl; ++e) {
+                const int t = ex[e];
+                if (t >= c0 && t < c1) x += (double)pf(t);
+            }
+            if (x > 0.0) {
+                const double rem = W - x;
+                W = rem > W * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
+            }
+        }
+        a.mass[(size_t)b * kMaxFine + c] = W;
+        a.massfb[(size_t)b * kMaxFine + c] = P;
+    }
+}
+
+// First chunk c (of n, weights in LDS) with cm[c] > 0 whose inclusive prefix reaches t;
+// if rounding leaves t beyond the total, the last positive chunk.  Wave 0 only; every
+// lane returns the chunk and the weight before it.
+__device__ inline int wave_locate(const double* cm, int n, double t, double& before) {
+    const int lane = threadIdx.x & 63;
+    double carry = 0.0, last_before = 0.0;
+    int last = -1;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const double x = i < n ? cm[i] : 0.0;
+        double incl = x;
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const double excl = incl - x;
+        const unsigned long long hit = __ballot(x > 0.0 && t <= carry + incl);
+        if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            before = carry + __shfl(excl, l);
+            return i0 + l;
+        }
+        const unsigned long long pos = __ballot(x > 0.0);
+        if (pos) {
+            const int l = 63 - __clzll((long long)pos);
+            last = i0 + l;
+            last_before = carry + __shfl(excl, l);
+        }
+        carry += __shfl(incl, 63);
+    }
+    before = last_before;
+    return last;
+}
+
+// One workgroup per request.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_draw(KArgs a) {
+    __shared__ Smem sm;
+    __shared__ float tile[kTile];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int S2 = a.S2, V = a.V;
+    const int b = blockIdx.x;
+    const DrawState st = a.dstate[b];
+    if (st.kind == kDrawNone) return;
+    const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
+    const float s2 = kLog2e / (float)st.T;
+    const double u = (double)a.coins[st.coin];
+    for (int c = tid; c < S2; c += kBlock) sm.cm[c] = a.mass[(size_t)b * kMaxFine + c];
+    __syncthreads();
+    if (wave == 0) {
+        double tot = 0.0;
+        for (int i0 = 0; i0 < S2; i0 += 64) {
+            const int i = i0 + (tid & 63);
+            tot += wave_sum(i < S2 ? sm.cm[i] : 0.0);
+        }
+        const bool fallback = !(tot > 0.0);
+        if (fallback) {  // every lane sees the same total: reload the plain target weights
+            tot = 0.0;
+            for (int i0 = 0; i0 < S2; i0 += 64) {
+                const int i = i0 + (tid & 63);
+                const double x = i < S2 ? a.massfb[(size_t)b * kMaxFine + i] : 0.0;
+                if (i < S2) sm.cm[i] = x;
+                tot += wave_sum(x);
+            }
+        }
+        double before = 0.0;
+        const double t = u * tot;
+        const int c = wave_locate(sm.cm, S2, t, before);
+        if (tid == 0) {
+            sm.fallback = fallback;
+            sm.sstar = c;
+            sm.tau = t - before;
+        }
+    }
+    __syncthreads();
+    const int c = sm.sstar;
+    const bool fallback = sm.fallback;
+    int y = -1;
+    if (c >= 0) {
+        const int nx = fallback ? 0 : st.nexcl;
+        const int c0 = c * a.fine, c1 = min(V, c0 + a.fine);
+        const int32_t* ex = nx > 0 ? a.excl + (size_t)b * SPEC_MAX_N : nullptr;
+        if (st.kind == kDrawResidual && !fallback) {
+            const DrawWeight<T, true> wf{rowp, a.q + (size_t)st.qrow * V, st.M, s2, st.invZ};
+            y = scan_find(wf, c0, c1, sm.tau, ex, nx, tile, sm);
+        } else {
+            const DrawWeight<T, false> wf{rowp, nullptr, st.M, s2, st.invZ};
+            y = scan_find(wf, c0, c1, sm.tau, ex, nx, tile, sm);
+        }
+        if (y < 0) y = c0;  // unreachable for a positive chunk weight
+    }
+    if (tid == 0) {
+        a.out_tokens[st.out] = y;
+        if (a.probs) {
+            float py = 0.f;
+            if (y >= 0 && y < V)
+                py = (float)(exp(((double)Ld<T>::one(rowp + y) - (double)st.M) / st.T) / st.Z);
+            a.probs[st.out] = py;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1049,42 +1188,44 @@ __global__ void k_fill_zero(uint32_t* p, size_t n) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t ticketA, ticketB, parts, state, resid, total;
+    size_t parts, dstate, mass, massfb, excl, total;
 };
 
-Layout layout_for(int B, int R) {
+// Records are stored with a row stride of S (the split count of the call), but the
+// workspace is sized for the largest split count so that its size depends on op, B, R.
+Layout layout_for(int op, int B, int R) {
     Layout L;
     size_t off = 0;
-    L.ticketA = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)B);
-    L.ticketB = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)B);
     L.parts = off;
     off = align256(off + sizeof(Part) * (size_t)B * R * kMaxSplits);
-    L.state = off;
-    off = align256(off + sizeof(ResidState) * (size_t)B);
-    L.resid = off;
-    off = align256(off + sizeof(double) * (size_t)B * kMaxSplits);
+    L.dstate = off;
+    off = align256(off + sizeof(DrawState) * (size_t)B);
+    L.mass = off;
+    off = align256(off + sizeof(double) * (size_t)B * kMaxFine);
+    L.massfb = off;
+    off = align256(off + sizeof(double) * (size_t)B * kMaxFine);
+    L.excl = off;
+    if (op == SPEC_OP_TREE) off = align256(off + sizeof(int32_t) * (size_t)B * SPEC_MAX_N);
     L.total = off;
     return L;
 }
 
-void bind_workspace(KArgs& a, void* ws, int B, int R) {
-    const Layout L = layout_for(B, R);
+void bind_workspace(KArgs& a, void* ws, int op, int B, int R) {
+    const Layout L = layout_for(op, B, R);
     char* base = static_cast<char*>(ws);
-    a.ticketA = reinterpret_cast<uint32_t*>(base + L.ticketA);
-    a.ticketB = reinterpret_cast<uint32_t*>(base + L.ticketB);
     a.parts = reinterpret_cast<Part*>(base + L.parts);
-    a.state = reinterpret_cast<ResidState*>(base + L.state);
-    a.resid = reinterpret_cast<double*>(base + L.resid);
+    a.dstate = reinterpret_cast<DrawState*>(base + L.dstate);
+    a.mass = reinterpret_cast<double*>(base + L.mass);
+    a.massfb = reinterpret_cast<double*>(base + L.massfb);
+    a.excl = op == SPEC_OP_TREE ? reinterpret_cast<int32_t*>(base + L.excl) : nullptr;
 }
 
-// Split each row into S chunks of `chunk` elements (a multiple of 8): about 32 KB of
+// Split each row into S chunks of `chunk` elements (a multiple of 8): about 64 KB of
 // logits per workgroup, at least ~2048 workgroups in flight, and at least 1024
 // elements per chunk.  SPEC_VERIFY_SPLITS overrides the count (launch-shape sweeps).
 void choose_split(long rows, int V, int esize, int* S_out, int* chunk_out) {
     const long row_bytes = (long)V * esize;
-    long s = (row_bytes + 32 * 1024 - 1) / (32 * 1024);
+    long s = (row_bytes + kChunkBytes - 1) / kChunkBytes;
     const long min_wgs = 2048;
     if (rows * s < min_wgs) s = (min_wgs + rows - 1) / rows;
     const long by_size = V / 1024 > 1 ? V / 1024 : 1;
@@ -1102,6 +1243,24 @@ void choose_split(long rows, int V, int esize, int* S_out, int* chunk_out) {
     *chunk_out = (int)ch;
 }
 
+// Fine chunks of the final draw: one LDS tile each (kTile elements), or more per chunk
+// when the row has more than kMaxFine tiles.
+void choose_fine(int V, int* S2_out, int* fine_out) {
+    long fine = kTile;
+    if ((long)V > (long)kMaxFine * kTile) fine = (((long)V + kMaxFine - 1) / kMaxFine + 7) / 8 * 8;
+    *fine_out = (int)fine;
+    *S2_out = (int)(((long)V + fine - 1) / fine);
+}
+
+// Launch shapes of a call; SPEC_ERR_SHAPE when a grid would exceed 2^32 work-items.
+int setup_shapes(KArgs& a, int esize) {
+    choose_split((long)a.B * a.R, a.V, esize, &a.S, &a.chunk);
+    choose_fine(a.V, &a.S2, &a.fine);
+    const long long lim = 0xffffffffLL / kBlock;
+    if ((long long)a.B * a.R * a.S > lim || (long long)a.B * a.S2 > lim) return SPEC_ERR_SHAPE;
+    return SPEC_OK;
+}
+
 int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t ws_bytes,
                  int op, int R) {
     if (!logits || (B > 0 && !ws)) return SPEC_ERR_NULL;
@@ -1110,6 +1269,7 @@ int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t w
     const size_t es = dtype == SPEC_F32 ? 4 : 2;
     if (((uintptr_t)logits) % es) return SPEC_ERR_PARAM;
     if ((long long)B * R * kMaxSplits > (long long)INT_MAX) return SPEC_ERR_SHAPE;
+    if ((long long)B * kMaxFine > (long long)INT_MAX) return SPEC_ERR_SHAPE;
     if (B > 0) {
         if (((uintptr_t)ws) % 256) return SPEC_ERR_WORKSPACE;
         if (ws_bytes < spec_workspace_bytes(op, B, R, V)) return SPEC_ERR_WORKSPACE;
@@ -1121,29 +1281,45 @@ int launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ER
 
 template <typename T>
 int run_greedy(KArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_rows<T, kGreedyChain>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((k_rows<T, false>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
+    int rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    hipLaunchKernelGGL((k_greedy_merge<T>), dim3(a.B), dim3(kBlock), 0, st, a);
+    return launch_status();
+}
+
+template <typename T>
+int run_draw(KArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((k_mass<T>), dim3(a.B * a.S2), dim3(kBlock), 0, st, a);
+    int rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    hipLaunchKernelGGL((k_draw<T>), dim3(a.B), dim3(kBlock), 0, st, a);
     return launch_status();
 }
 
 template <typename T>
 int run_chain(KArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_rows<T, kSamplingChain>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((k_rows<T, true>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
-    hipLaunchKernelGGL((k_residual<T>), dim3(a.B * a.S), dim3(kBlock), 0, st, a);
-    return launch_status();
+    hipLaunchKernelGGL((k_chain_accept<T>), dim3(a.B), dim3(kBlock), 0, st, a);
+    rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    return run_draw<T>(a, st);
 }
 
 template <typename T>
 int run_tree(KArgs& a, int sampling, hipStream_t st) {
     if (sampling)
-        hipLaunchKernelGGL((k_rows<T, kRowsOnlySampling>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_rows<T, true>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
     else
-        hipLaunchKernelGGL((k_rows<T, kRowsOnlyGreedy>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_rows<T, false>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
     hipLaunchKernelGGL((k_tree<T>), dim3(a.B), dim3(kBlock), 0, st, a, sampling);
-    return launch_status();
+    rc = launch_status();
+    if (rc != SPEC_OK || !sampling) return rc;
+    return run_draw<T>(a, st);
 }
 
 }  // namespace
@@ -1160,7 +1336,7 @@ extern "C" size_t spec_workspace_bytes(int op, int B, int R, int V) {
     } else {
         return 0;
     }
-    return layout_for(B, R).total;
+    return layout_for(op, B, R).total;
 }
 
 extern "C" const char* spec_status_str(int status) {
@@ -1174,18 +1350,6 @@ extern "C" const char* spec_status_str(int status) {
         case SPEC_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }
-}
-
-extern "C" int spec_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
-    if (!workspace) return SPEC_ERR_NULL;
-    if (((uintptr_t)workspace) % 4) return SPEC_ERR_PARAM;
-    const size_t n = ws_bytes / 4;
-    if (n == 0) return SPEC_OK;
-    size_t blocks = (n + kBlock - 1) / kBlock;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(kBlock), 0,
-                       static_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace), n);
-    return launch_status();
 }
 
 extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
@@ -1203,8 +1367,9 @@ extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* 
     a.V = V;
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
-    choose_split((long)B * a.R, V, dtype == SPEC_F32 ? 4 : 2, &a.S, &a.chunk);
-    bind_workspace(a, workspace, B, a.R);
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    if (rc != SPEC_OK) return rc;
+    bind_workspace(a, workspace, SPEC_OP_GREEDY, B, a.R);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_greedy<float>(a, st) : run_greedy<uint16_t>(a, st);
 }
@@ -1232,8 +1397,9 @@ extern "C" int spec_verify_chain(const void* logits, int dtype, const float* dra
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
     a.probs = probs_out;
-    choose_split((long)B * a.R, V, dtype == SPEC_F32 ? 4 : 2, &a.S, &a.chunk);
-    bind_workspace(a, workspace, B, a.R);
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    if (rc != SPEC_OK) return rc;
+    bind_workspace(a, workspace, SPEC_OP_CHAIN, B, a.R);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_chain<float>(a, st) : run_chain<uint16_t>(a, st);
 }
@@ -1271,8 +1437,9 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     a.out_tokens = out_tokens;
     a.accepted_nodes = accepted_nodes;
     a.probs = probs_out;
-    choose_split((long)B * N, V, dtype == SPEC_F32 ? 4 : 2, &a.S, &a.chunk);
-    bind_workspace(a, workspace, B, N);
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    if (rc != SPEC_OK) return rc;
+    bind_workspace(a, workspace, SPEC_OP_TREE, B, N);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_tree<float>(a, mode, st) : run_tree<uint16_t>(a, mode, st);
 }

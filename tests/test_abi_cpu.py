@@ -22,7 +22,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.declared_functions()
     assert set(names) >= {"spec_verify_greedy", "spec_verify_chain", "spec_verify_tree",
-                          "spec_workspace_bytes", "spec_status_str", "spec_workspace_init"}
+                          "spec_workspace_bytes", "spec_status_str"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -121,9 +121,3 @@ def test_tree_rejects_bad_arguments(lib):
     # greedy mode needs neither coins nor temperature: check only up to validation
     assert _tree(lib, mode=L.SPEC_TREE_GREEDY, coins=None, temp=None, ws=None) == L.SPEC_ERR_NULL
     assert _tree(lib, B=0, mode=L.SPEC_TREE_GREEDY, coins=None, temp=None) == L.SPEC_OK
-
-
-def test_workspace_init_validation(lib):
-    assert lib.spec_workspace_init(None, 16, None) == L.SPEC_ERR_NULL
-    assert lib.spec_workspace_init(P + 2, 16, None) == L.SPEC_ERR_PARAM
-    assert lib.spec_workspace_init(P, 0, None) == L.SPEC_OK
