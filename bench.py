@@ -8,8 +8,15 @@ synthetic, seeded, and resident in HBM before timing starts; three copies rotate
 consecutive steps never find the logits in the 256 MB Infinity Cache.
 
 Prints ONE JSON line: verified positions/s (whole step), the roofline of the dominant
-kernel (HBM bytes per launch / launch time measured with HIP events on the launch
-stream), and the CPU oracle timed on a bounded sample of the same workload.
+call (spec_verify_chain: algorithmic HBM bytes per call / call time measured with HIP
+events on the launch stream), and the CPU oracle timed on a bounded sample of the same
+workload.
+
+HBM traffic: two rocprofv3 counter passes over this script (FETCH_SIZE, then WRITE_SIZE,
+with --calib-copy-mib so that a plain device copy of known size runs after the timed
+region) are reduced by ``bench.py --traffic-from FETCH_DIR WRITE_DIR``, which scales each
+counter by what it reads for the copy and writes profiles/traffic.json; later runs report
+that traffic while the kernel source is unchanged (its hash is stored with it).
 """
 from __future__ import annotations
 
@@ -25,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD published peak
+CHAIN_KERNELS = ["k_rows<sampling>", "k_chain_accept", "k_mass", "k_draw"]
+GREEDY_KERNELS = ["k_rows<greedy>", "k_greedy_merge"]
 
 
 def parse():
@@ -38,11 +47,18 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--tree", action="store_true", help="also time the tree workload")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB 3 times (counter scale)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="reduce two rocprofv3 --pmc runs (csv) into --traffic-json and exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        _traffic_from(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the verify path is single-GPU here)", file=sys.stderr)
@@ -123,12 +139,9 @@ def main():
 
     traffic = None
     if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == args.workload and tj.get("kernel_source_sha") == _source_sha():
-                traffic = tj.get("chain_call_bytes")
-        except Exception:
-            traffic = None
+        tj = json.load(open(args.traffic_json))
+        if tj.get("workload") == c.name and tj.get("kernel_source_sha") == _source_sha():
+            traffic = tj.get("calls", {}).get("spec_verify_chain", {}).get("bytes")
 
     result = {
         "metric": "verified positions/sec and logit-read GB/s (% of HBM peak), 1 MI355X",
@@ -147,7 +160,7 @@ def main():
                    "step": "spec_verify_greedy + spec_verify_chain", "input_copies": args.copies},
         "roofline": {
             "bound": "hbm",
-            "kernel": "spec_verify_chain (k_rows sampling pass + k_chain_accept + k_chain_draw)",
+            "kernel": "spec_verify_chain call: " + " + ".join(CHAIN_KERNELS),
             "achieved": chain_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -172,9 +185,81 @@ def main():
     if args.tree:
         result["modes"].update(_tree_modes(args, torch, dev, api, wl))
 
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n
+        del src, dst
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(c, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _kernel_key(name):
+    """Short kernel name as used in CHAIN_KERNELS / GREEDY_KERNELS."""
+    if "copyBuffer" in name:
+        return "copy"
+    base = name.split("::")[1].split("(")[0] if "::" in name else name
+    if base.startswith("k_rows<"):
+        return "k_rows<sampling>" if base.rstrip(">").endswith("true") else "k_rows<greedy>"
+    return base.split("<")[0]
+
+
+def _read_counter_csv(d, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def _traffic_from(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel of the timed calls, scaled
+    by the ratio of known bytes to what the same counter reads for the calibration copy
+    (the last three device copies of the run)."""
+    out = {"kernel_source_sha": _source_sha(), "unit": "bytes per dispatch"}
+    per = {}
+    for counter, d in (("FETCH_SIZE", args.traffic_from[0]), ("WRITE_SIZE", args.traffic_from[1])):
+        rows = _read_counter_csv(d, counter)
+        copies = [v for _, n, v in rows if _kernel_key(n) == "copy"][-3:]
+        lines = [ln for ln in open(os.path.join(d, "bench.json")) if ln.startswith("{")]
+        meta = json.loads(lines[-1])
+        known = meta["calib_copy_bytes"] / 1024.0
+        scale = known / (sum(copies) / len(copies))
+        out.setdefault("workload", meta["config"]["workload"])
+        out[f"{counter}_copy_KiB"] = sum(copies) / len(copies)
+        out[f"{counter}_scale"] = scale
+        for _, n, v in rows:
+            k = _kernel_key(n)
+            if k != "copy":
+                per.setdefault(k, {}).setdefault(counter, []).append(v)
+    kernels = {}
+    for k, cv in per.items():
+        f = float(np.mean(cv.get("FETCH_SIZE", [0.0]))) * 1024 * out["FETCH_SIZE_scale"]
+        w = float(np.mean(cv.get("WRITE_SIZE", [0.0]))) * 1024 * out["WRITE_SIZE_scale"]
+        kernels[k] = {"fetch_bytes": f, "write_bytes": w, "dispatches": len(cv.get("FETCH_SIZE", []))}
+    out["kernels"] = kernels
+    out["calls"] = {
+        name: {"bytes": sum(kernels[k]["fetch_bytes"] + kernels[k]["write_bytes"] for k in ks),
+               "kernels": ks}
+        for name, ks in (("spec_verify_chain", CHAIN_KERNELS), ("spec_verify_greedy", GREEDY_KERNELS))
+        if all(k in kernels for k in ks)}
+    os.makedirs(os.path.dirname(args.traffic_json), exist_ok=True)
+    json.dump(out, open(args.traffic_json, "w"), indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def _source_sha():
