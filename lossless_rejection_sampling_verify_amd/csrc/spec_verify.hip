@@ -11,16 +11,18 @@
 //                   sum exp((l - m)/T) relative to the chunk max (sampling).
 //   k_greedy_merge  one workgroup per request: row argmax from the records, first
 //                   mismatch with the drafts, emitted tokens.
-//   k_chain_accept  one workgroup per request: row max and normaliser from the records,
-//                   p(x_i) / q(x_i) acceptance scan in fp64, accepted prefix, and the
-//                   state of the final draw (correction from row k, or bonus from row G).
 //   k_tree          one workgroup per request: validates the parent array (pointer
 //                   jumping for depths), row statistics of every node and the target
-//                   probability of every node's token, then the level-by-level walk.
-//   k_mass          one workgroup per (request, fine chunk of ~4096 elements): weight of
-//                   the chunk in the row the final token is drawn from.
-//   k_draw          one workgroup per request: locates the fine chunk holding u * total
-//                   and scans it in an LDS tile (inverse CDF in ascending token id).
+//                   probability of every node's token, then the level-by-level walk; it
+//                   hands the row and the excluded tokens of the last draw to k_mass.
+//   k_chain_accept  one workgroup per chain request: row max and normaliser from the
+//                   records, p(x_i) / q(x_i) tests in fp64, the accepted prefix, and the
+//                   state of the last draw (correction from row k, or bonus from row G).
+//   k_mass          one workgroup per (request, fine chunk of 4096 elements): weight of
+//                   the chunk and of each of its 64 segments of 64 elements in the row the
+//                   last token is drawn from.
+//   k_draw          one wave per request: locates the chunk, then the segment, then the
+//                   token holding u * total (inverse CDF in ascending token id).
 //
 // Sources: llm-infra-atlas "Speculative Decoding" section 0 and section 2; ricardokevins
 // "Speculative Decoding", correction sampling, Eq. a(x) and Eq. r(x); zdszero
@@ -43,8 +45,9 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kUnroll = 4;
 constexpr int kMaxSplits = 64;
 constexpr long kChunkBytes = 64 * 1024;  // target logit bytes per row-pass workgroup
-constexpr int kTile = 4096;     // weights per LDS tile of the final draw
-constexpr int kMaxFine = 256;  // fine chunks per row in the final draw
+constexpr int kFine = 4 * 4 * kBlock;  // elements per fine chunk of the final draw (4096)
+constexpr int kSeg = 64;               // elements per segment: one per lane of a wave
+constexpr int kSegs = kFine / kSeg;    // segments per fine chunk (64)
 constexpr int kMaxRows = SPEC_MAX_G + 1;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -81,7 +84,7 @@ struct KArgs {
     const float* coins;
     const float* temperature;
     int B, R, V, S, chunk, D;
-    int S2, fine;        // fine chunks of the final draw: S2 chunks of `fine` elements
+    int S2;              // fine chunks of kFine elements per row (final draw)
     float th_single, th_acc;
     int32_t* accept_len;
     int32_t* out_tokens;
@@ -89,8 +92,9 @@ struct KArgs {
     float* probs;
     Part* parts;         // [rows][S] records of the row pass
     DrawState* dstate;   // [B]
-    double* mass;        // [B][kMaxFine] weight of each fine chunk
-    double* massfb;      // [B][kMaxFine] fallback weight (the plain target row)
+    double* mass;        // [B][S2] draw weight of each fine chunk
+    double* massfb;      // [B][S2] fallback weight (the plain target row)
+    double* seg;         // [B][S2][kSegs] draw weight of each segment
     int32_t* excl;       // [B][SPEC_MAX_N] tree: excluded tokens of the final draw
 };
 
@@ -163,7 +167,16 @@ __device__ inline void wave_argmax(float& v, int& i) {
     }
 }
 
-struct Smem {
+// The split records of one request, staged in LDS by the per-request merges.
+struct RecSmem {
+    float m[kMaxRows * kMaxSplits];
+    union {
+        double z[kMaxRows * kMaxSplits];  // sampling: exp-sums
+        int i[kMaxRows * kMaxSplits];     // greedy: argmax indices
+    };
+};
+
+struct Smem {  // per-request merges: row statistics, drafts, coins, decisions
     float M[kMaxRows];
     double Z[kMaxRows];
     double p[kMaxRows];
@@ -172,15 +185,8 @@ struct Smem {
     float l[kMaxRows];
     float qx[kMaxRows];
     float u[kMaxRows];
-    double cm[kMaxFine];    // fine-chunk weights of the row being drawn from
-    double wtot[kWaves];
+    DrawState st;
     int k;
-    int sstar;
-    int fallback;
-    double tau;
-    int found;
-    int lastthr;
-    int result;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -349,37 +355,6 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
 }
 
 // ---------------------------------------------------------------------------------------
-// per-row merges of the split records (one full wave; every lane gets the result bits)
-
-// Row max M and Z = sum exp((l - M) / T) over the row, from its S records.
-__device__ inline void row_softmax_stats(const Part* pr, int S, double Td, float& M, double& Z) {
-    const int lane = threadIdx.x & 63;
-    float m = -INFINITY;
-    double z = 0.0;
-    if (lane < S) {
-        m = pr[lane].m;
-        z = pr[lane].z;
-    }
-    M = wave_max(m);
-    double term = 0.0;
-    if (lane < S && m != -INFINITY) term = z * exp(((double)m - (double)M) / Td);
-    Z = wave_sum(term);
-}
-
-// Lowest index attaining the row max, or -1 when the row has no finite logit.
-__device__ inline int row_argmax(const Part* pr, int S) {
-    const int lane = threadIdx.x & 63;
-    float v = -INFINITY;
-    int ix = INT_MAX;
-    if (lane < S) {
-        v = pr[lane].m;
-        ix = pr[lane].idx;
-    }
-    wave_argmax(v, ix);
-    return v == -INFINITY ? -1 : ix;
-}
-
-// ---------------------------------------------------------------------------------------
 // k_rows: one workgroup per (row, split)
 
 template <typename T, bool kSampling>
@@ -405,14 +380,28 @@ __global__ __launch_bounds__(kBlock) void k_rows(KArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_greedy_merge(KArgs a) {
     __shared__ Smem sm;
+    __shared__ RecSmem rs;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = a.R, G = R - 1, S = a.S;
     const int b = blockIdx.x;
-    for (int i = wave; i < R; i += kWaves) {
-        const int ix = row_argmax(a.parts + ((size_t)b * R + i) * S, S);
-        if (lane == 0) sm.arg[i] = ix;
+    const Part* pr = a.parts + (size_t)b * R * S;
+    for (int r = tid; r < R * S; r += kBlock) {  // records and drafts, all loads at once
+        const Part p = pr[r];
+        rs.m[r] = p.m;
+        rs.i[r] = p.idx;
     }
-    for (int i = tid; i < G; i += kBlock) sm.x[i] = a.tokens[(size_t)b * G + i];
+    if (tid < G) sm.x[tid] = a.tokens[(size_t)b * G + tid];
+    __syncthreads();
+    for (int i = wave; i < R; i += kWaves) {  // row argmax (lowest index), one wave per row
+        float v = -INFINITY;
+        int ix = INT_MAX;
+        if (lane < S) {
+            v = rs.m[i * S + lane];
+            ix = rs.i[i * S + lane];
+        }
+        wave_argmax(v, ix);
+        if (lane == 0) sm.arg[i] = v == -INFINITY ? -1 : ix;
+    }
     __syncthreads();
     if (tid == 0) {
         const int* x = sm.x;
@@ -468,67 +457,83 @@ struct Quad<uint16_t> {
 };
 
 // ---------------------------------------------------------------------------------------
-// k_chain_accept: one workgroup per request
+// the acceptance scan of a chain request (block-wide; identical bits in every caller)
+//
+// Row max and normaliser from the records, p(x_i) / q(x_i) tests in fp64 with the
+// request's coins, and the state of the final draw (the correction from row k, or the
+// bonus from row G).  With `emit`, the accepted prefix, accept_len and probs are written.
 
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
-    __shared__ Smem sm;
+__device__ DrawState chain_accept(const KArgs& a, int b, bool emit, Smem& sm, RecSmem& rs) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = a.R, G = R - 1, S = a.S, V = a.V;
-    const int b = blockIdx.x;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    // every load of the request at once: records, coins, drafts, and the two gathers
+    const Part* pr = a.parts + (size_t)b * R * S;
+    for (int r = tid; r < R * S; r += kBlock) {
+        const Part p = pr[r];
+        rs.m[r] = p.m;
+        rs.z[r] = p.z;
+    }
+    if (tid < R) sm.u[tid] = a.coins[(size_t)b * R + tid];
+    if (tid < G) {
+        const int xi = a.tokens[(size_t)b * G + tid];
+        sm.x[tid] = xi;
+        if (xi >= 0 && xi < V) {
+            sm.l[tid] = Ld<T>::one(logits + ((size_t)b * R + tid) * V + xi);
+            sm.qx[tid] = a.q[((size_t)b * G + tid) * V + xi];
+        }
+    }
     const float Tf = a.temperature[b];
     const bool t_ok = isfinite(Tf) && Tf > 0.f;
     const double Td = (double)Tf;
-    const T* logits = reinterpret_cast<const T*>(a.logits);
-    for (int i = wave; i < R; i += kWaves) {
-        float M;
-        double Z;
-        row_softmax_stats(a.parts + ((size_t)b * R + i) * S, S, Td, M, Z);
+    __syncthreads();
+    for (int i = wave; i < R; i += kWaves) {  // row max and normaliser, one wave per row
+        float m = -INFINITY;
+        double z = 0.0;
+        if (lane < S) {
+            m = rs.m[i * S + lane];
+            z = rs.z[i * S + lane];
+        }
+        const float M = wave_max(m);
+        double term = 0.0;
+        if (lane < S && m != -INFINITY) term = z * exp(((double)m - (double)M) / Td);
+        const double Z = wave_sum(term);
         if (lane == 0) {
             sm.M[i] = M;
             sm.Z[i] = Z;
         }
     }
-    for (int i = tid; i < R; i += kBlock) {
-        sm.u[i] = a.coins[(size_t)b * R + i];
-        if (i < G) {
-            const int xi = a.tokens[(size_t)b * G + i];
-            sm.x[i] = xi;
-            if (xi >= 0 && xi < V) {
-                sm.l[i] = Ld<T>::one(logits + ((size_t)b * R + i) * V + xi);
-                sm.qx[i] = a.q[((size_t)b * G + i) * V + xi];
+    __syncthreads();
+    if (tid < R) {  // lane i: is everything position i consults usable, and is x_i kept?
+        bool ok = sm.M[tid] != -INFINITY && sm.u[tid] > 0.f && sm.u[tid] <= 1.f;
+        bool keep = false;
+        if (tid < G) {
+            const int xi = sm.x[tid];
+            ok = ok && xi >= 0 && xi < V;
+            if (ok) ok = sm.qx[tid] >= 0.f && isfinite(sm.qx[tid]);
+            if (ok && t_ok) {
+                const double p = exp(((double)sm.l[tid] - (double)sm.M[tid]) / Td) / sm.Z[tid];
+                const double qx = (double)sm.qx[tid];
+                keep = qx > 0.0 ? (p > 0.0 && (double)sm.u[tid] <= p / qx) : p > 0.0;
+                sm.p[tid] = p;
             }
         }
+        sm.arg[tid] = (ok ? 1 : 0) | (keep ? 2 : 0);
     }
     __syncthreads();
     if (tid == 0) {
-        const int* x = sm.x;
-        const float* u = sm.u;
         bool valid = t_ok;
-        for (int i = 0; i < G; ++i)
-            if (x[i] < 0 || x[i] >= V) valid = false;
-        for (int i = 0; i < R; ++i) {
-            if (!(u[i] > 0.f && u[i] <= 1.f)) valid = false;
-            if (sm.M[i] == -INFINITY) valid = false;
-        }
-        for (int i = 0; i < G && valid; ++i)
-            if (!(sm.qx[i] >= 0.f) || !isfinite(sm.qx[i])) valid = false;
+        for (int i = 0; i < R; ++i)
+            if (!(sm.arg[i] & 1)) valid = false;
         int k = G;
-        if (valid) {
-            for (int i = 0; i < G; ++i) {
-                const double l = (double)sm.l[i];
-                const double p = exp((l - (double)sm.M[i]) / Td) / sm.Z[i];
-                const double qx = (double)sm.qx[i];
-                const bool accept = qx > 0.0 ? (p > 0.0 && (double)u[i] <= p / qx) : p > 0.0;
-                sm.p[i] = p;
-                if (!accept) {
-                    k = i;
-                    break;
-                }
+        for (int i = 0; i < G && valid; ++i)
+            if (!(sm.arg[i] & 2)) {
+                k = i;
+                break;
             }
-        }
         sm.k = valid ? k : -1;
-        a.accept_len[b] = sm.k;
+        if (emit) a.accept_len[b] = sm.k;
         DrawState st = {};
         st.kind = kDrawNone;
         if (valid) {
@@ -543,22 +548,25 @@ __global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
             st.invZ = (float)(1.0 / sm.Z[k]);
             st.T = Td;
         }
-        a.dstate[b] = st;
+        sm.st = st;
     }
     __syncthreads();
+    const DrawState st = sm.st;
     const int k = sm.k;
-    for (int i = tid; i < R; i += kBlock) {
+    for (int i = tid; i < R && emit; i += kBlock) {
         int t = -1;
-        float pr = 0.f;
+        float pr2 = 0.f;
         if (k >= 0 && i < k) {
             t = sm.x[i];
-            pr = (float)sm.p[i];
+            pr2 = (float)sm.p[i];
         }
         if (i != k) {  // slot k is written by the final draw
             a.out_tokens[(size_t)b * R + i] = t;
-            if (a.probs) a.probs[(size_t)b * R + i] = pr;
+            if (a.probs) a.probs[(size_t)b * R + i] = pr2;
         }
     }
+    __syncthreads();  // sm is reused by the caller
+    return st;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -829,132 +837,43 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
     for (int e = d + tid; e < D; e += kBlock) nodes[e] = -1;
 }
 
-// ---------------------------------------------------------------------------------------
-// block helpers for the final draw
-
-__device__ inline double block_excl_scan(double v, Smem& sm) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    double x = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        double y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    double ex = __shfl_up(x, 1);
-    if (lane == 0) ex = 0.0;
-    if (lane == 63) sm.wtot[wave] = x;
-    __syncthreads();
-    double off = 0.0;
-    for (int w = 0; w < wave; ++w) off += sm.wtot[w];
-    __syncthreads();
-    return off + ex;
-}
-
-// First j in [c0, c1) with w(j) > 0 whose inclusive prefix sum (from c0) reaches tau.
-// If rounding leaves tau beyond the total, the last j with w(j) > 0.  -1 if none is
-// positive.  Every thread of the block must call it; all get the result.
-//
-// The range is taken in LDS tiles of kTile weights: all lanes load and weigh a tile with
-// coalesced accesses, then each lane sums a contiguous run of kTile / kBlock weights, a
-// block exclusive scan of those run sums locates the run that crosses tau, and that
-// run's lane walks it.  Prefix sums are fp64, element by element in ascending order.
-template <typename WF>
-__device__ int scan_find(const WF& wf, int c0, int c1, double tau, const int* excl, int nexcl,
-                         float* tile, Smem& sm) {
-    constexpr int kRun = kTile / kBlock;
-    const int tid = threadIdx.x;
-    double base = 0.0;  // total weight of the tiles before this one
-    int last_pos = -1;  // last positive index seen so far
-    for (int t0 = c0; t0 < c1; t0 += kTile) {
-        const int len = min(kTile, c1 - t0);
-        {  // every lane issues all of its kRun loads before using any (clamped indices)
-            float w[kRun];
-#pragma unroll
-            for (int i = 0; i < kRun; ++i) w[i] = wf(t0 + min(tid + i * kBlock, len - 1));
-#pragma unroll
-            for (int i = 0; i < kRun; ++i)
-                if (tid + i * kBlock < len) tile[tid + i * kBlock] = w[i];
-        }
-        __syncthreads();
-        for (int e = tid; e < nexcl; e += kBlock) {  // excluded tokens weigh nothing
-            const int j = excl[e] - t0;
-            if (j >= 0 && j < len) tile[j] = 0.f;
-        }
-        __syncthreads();
-        const int r0 = tid * kRun;
-        const int r1 = min(len, r0 + kRun);
-        double sum = 0.0;
-        int last = -1;
-        for (int e = r0; e < r1; ++e) {
-            const float w = tile[e];
-            if (w > 0.f) {
-                sum += (double)w;
-                last = t0 + e;
-            }
-        }
-        const double ex = base + block_excl_scan(sum, sm);
-        if (tid == 0) {
-            sm.found = INT_MAX;
-            sm.lastthr = -1;
-        }
-        __syncthreads();
-        if (sum > 0.0 && tau <= ex + sum) atomicMin(&sm.found, tid);
-        if (sum > 0.0) atomicMax(&sm.lastthr, tid);
-        if (tid == kBlock - 1) sm.tau = ex + sum;  // running total through this tile
-        __syncthreads();
-        const int found = sm.found;
-        if (found != INT_MAX) {
-            if (tid == found) {
-                double C = ex;
-                int y = last;
-                for (int e = r0; e < r1; ++e) {
-                    const float w = tile[e];
-                    if (w > 0.f) {
-                        C += (double)w;
-                        if (tau <= C) {
-                            y = t0 + e;
-                            break;
-                        }
-                    }
-                }
-                sm.result = y;
-            }
-            __syncthreads();
-            const int y = sm.result;
-            __syncthreads();
-            return y;
-        }
-        if (sm.lastthr >= 0 && tid == sm.lastthr) sm.result = last;
-        __syncthreads();
-        if (sm.lastthr >= 0) last_pos = sm.result;
-        base = sm.tau;
-        __syncthreads();  // the tile and the scan scratch are reused
-    }
-    return last_pos;
+// Field-wise copy of a draw state from global memory (keeps it in registers).
+__device__ inline DrawState load_state(const DrawState* p) {
+    DrawState st;
+    st.kind = p->kind;
+    st.row = p->row;
+    st.qrow = p->qrow;
+    st.out = p->out;
+    st.coin = p->coin;
+    st.nexcl = p->nexcl;
+    st.M = p->M;
+    st.invZ = p->invZ;
+    st.Z = p->Z;
+    st.T = p->T;
+    return st;
 }
 
 // ---------------------------------------------------------------------------------------
-// the final draw: k_mass sums the weights of each fine chunk of the row the token is drawn
-// from, k_draw locates the chunk that holds u * total and scans it
+// the final draw: k_mass weighs each fine chunk (kFine elements) of the row the token is
+// drawn from, and each of its kSegs segments of kSeg elements; k_draw locates the chunk,
+// then the segment, then the token (inverse CDF in ascending token id)
 //
 // Weights, computed identically in both kernels (fp32, no contraction):
 //   p_j = exp2((l_j - M) * log2(e) / T) * (1/Z)
 //   residual (chain, rejected at k):   w_j = max(0, p_j - q_j)
 //   target (chain bonus, tree):        w_j = p_j, with the excluded tokens at 0 (tree)
 // Fallback when the total weight is not positive: w_j = p_j (the plain target row).
+// Segment and chunk sums are fp64 sums of fp32 sums of four weights.
 
 template <typename T, bool kResidual>
-struct DrawWeight {
-    const T* row;
-    const float* q;  // residual: the draft row; otherwise unused
-    float M, s2, invZ;
-    __device__ float operator()(int j) const {
-        const float p = ex2((Ld<T>::one(row + j) - M) * s2) * invZ;
-        return kResidual ? fmaxf(p - q[j], 0.f) : p;
-    }
-};
+__device__ inline float draw_weight(const T* row, const float* q, int j, float M, float s2,
+                                    float invZ, float& p) {
+    p = ex2((Ld<T>::one(row + j) - M) * s2) * invZ;
+    return kResidual ? fmaxf(p - q[j], 0.f) : p;
+}
 
 // Weights of four consecutive elements: `pw` gets the sum of the plain p_j, `ww` the sum
-// of the draw weights (residual: max(0, p_j - q_j); otherwise p_j).
+// of the draw weights.
 template <typename T, bool kResidual>
 __device__ inline void weigh4(const typename Quad<T>::Raw& lr, const u32x4& qr, float M,
                               float s2, float invZ, float& pw, float& ww) {
@@ -973,56 +892,69 @@ __device__ inline void weigh4(const typename Quad<T>::Raw& lr, const u32x4& qr, 
     ww = kResidual ? ws : ps;
 }
 
-// Sums over the 16-byte aligned part of a fine chunk (4 elements per lane per step,
-// kUnroll steps in flight).  Returns the number of elements covered.
+// Lane t of the block takes elements 4t..4t+3 of each 1024-element quarter u of the chunk
+// and leaves their weight sums in entry u * kBlock + t of `pw` / `ww` (LDS): segment g is
+// then entries 16g .. 16g + 15.
 template <typename T, bool kResidual>
-__device__ inline int mass_vec(const T* rowp, const float* qrow, int n, float M, float s2,
-                               float invZ, double& psum, double& wsum) {
+__device__ inline void chunk_weights(const T* rowp, const float* qrow, int n, bool fast, float M,
+                                     float s2, float invZ, float* pw, float* ww) {
     const int tid = threadIdx.x;
-    const int nv = n / 4;
-    const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
-    const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    int v = tid;
-    for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
-        typename Quad<T>::Raw lr[kUnroll];
-        u32x4 qr[kUnroll];
+    if (fast) {  // full, 16-byte aligned chunk: every load in flight at once
+        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
+        const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        typename Quad<T>::Raw lr[4];
+        u32x4 qr[4];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            lr[u] = lq[v + u * kBlock].raw;
-            qr[u] = kResidual ? ld_stream(qq + v + u * kBlock) : zero;
+        for (int u = 0; u < 4; ++u) {
+            lr[u] = lq[u * kBlock + tid].raw;
+            qr[u] = kResidual ? ld_stream(qq + u * kBlock + tid) : zero;
         }
-        float pw = 0.f, ww = 0.f;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < 4; ++u) {
             float p4, w4;
             weigh4<T, kResidual>(lr[u], qr[u], M, s2, invZ, p4, w4);
-            pw += p4;
-            ww += w4;
+            pw[u * kBlock + tid] = p4;
+            ww[u * kBlock + tid] = w4;
         }
-        psum += (double)pw;
-        wsum += (double)ww;
+        return;
     }
-    for (; v < nv; v += kBlock) {
-        const u32x4 qr = kResidual ? ld_stream(qq + v) : zero;
-        float p4, w4;
-        weigh4<T, kResidual>(lq[v].raw, qr, M, s2, invZ, p4, w4);
-        psum += (double)p4;
-        wsum += (double)w4;
+    for (int u = 0; u < 4; ++u) {
+        float p4 = 0.f, w4 = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int e = u * 4 * kBlock + 4 * tid + i;
+            if (e < n) {
+                float p;
+                const float w = draw_weight<T, kResidual>(rowp, qrow, e, M, s2, invZ, p);
+                p4 += p;
+                w4 += w;
+            }
+        }
+        pw[u * kBlock + tid] = p4;
+        ww[u * kBlock + tid] = kResidual ? w4 : p4;
     }
-    return nv * 4;
+}
+
+// One workgroup per chain request: the acceptance scan, its outputs and the draw state.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
+    __shared__ Smem sm;
+    __shared__ RecSmem rs;
+    const DrawState st = chain_accept<T>(a, blockIdx.x, true, sm, rs);
+    if (threadIdx.x == 0) a.dstate[blockIdx.x] = st;
 }
 
 struct MassSmem {
-    double w[kWaves];
-    double p[kWaves];
+    float pw[4 * kBlock];  // plain target weight of each lane's four elements, per quarter
+    float ww[4 * kBlock];  // draw weight of the same
+    double xs[kSegs];      // excluded weight of each segment
 };
 
 // One workgroup per (request, fine chunk).
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
     __shared__ MassSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int S2 = a.S2, V = a.V;
     const int b = blockIdx.x / S2;
     const int c = blockIdx.x - b * S2;
@@ -1031,154 +963,189 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
     const float* qrow = st.kind == kDrawResidual ? a.q + (size_t)st.qrow * V : nullptr;
     const float s2 = kLog2e / (float)st.T;
-    const int c0 = c * a.fine, c1 = min(V, c0 + a.fine);
-    const int n = c1 > c0 ? c1 - c0 : 0;
-    double wsum = 0.0, psum = 0.0;
-    const bool aligned = (((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0) &&
-                         (!qrow || ((uintptr_t)(qrow + c0)) % 16 == 0);
-    int done = 0;
-    if (aligned) {
-        if (qrow)
-            done = mass_vec<T, true>(rowp + c0, qrow + c0, n, st.M, s2, st.invZ, psum, wsum);
-        else
-            done = mass_vec<T, false>(rowp + c0, nullptr, n, st.M, s2, st.invZ, psum, wsum);
-    }
-    const DrawWeight<T, false> pf{rowp, nullptr, st.M, s2, st.invZ};
-    const DrawWeight<T, true> rf{rowp, qrow, st.M, s2, st.invZ};
-    for (int j = c0 + done + tid; j < c1; j += kBlock) {
-        const float p = pf(j);
-        psum += (double)p;
-        wsum += (double)(qrow ? rf(j) : p);
-    }
-    wsum = wave_sum(wsum);
-    psum = wave_sum(psum);
-    if (lane == 0) {
-        sm.w[wave] = wsum;
-        sm.p[wave] = psum;
-    }
+    const int c0 = c * kFine;
+    const int n = min(kFine, V - c0);
+    const bool fast = n == kFine && ((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0 &&
+                      (!qrow || ((uintptr_t)(qrow + c0)) % 16 == 0);
+    if (qrow)
+        chunk_weights<T, true>(rowp + c0, qrow + c0, n, fast, st.M, s2, st.invZ, sm.pw, sm.ww);
+    else
+        chunk_weights<T, false>(rowp + c0, nullptr, n, fast, st.M, s2, st.invZ, sm.pw, sm.ww);
+    if (tid < kSegs) sm.xs[tid] = 0.0;
     __syncthreads();
-    if (tid == 0) {
-        double W = 0.0, P = 0.0;
-        for (int w = 0; w < kWaves; ++w) {
-            W += sm.w[w];
-            P += sm.p[w];
-        }
-        if (st.nexcl > 0) {  // tree: remove the rejected children's weight from this chunk
+    if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
+        if (tid == 0) {
             const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
-            double x = 0.0;
             for (int e = 0; e < st.nexcl; ++e) {
                 const int t = ex[e];
-                if (t >= c0 && t < c1) x += (double)pf(t);
-            }
-            if (x > 0.0) {
-                const double rem = W - x;
-                W = rem > W * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
+                if (t >= c0 && t < c0 + n) {
+                    float p;
+                    draw_weight<T, false>(rowp, nullptr, t, st.M, s2, st.invZ, p);
+                    sm.xs[(t - c0) / kSeg] += (double)p;
+                }
             }
         }
-        a.mass[(size_t)b * kMaxFine + c] = W;
-        a.massfb[(size_t)b * kMaxFine + c] = P;
+        __syncthreads();
+    }
+    if (tid < kSegs) {  // wave 0: lane g sums segment g in ascending order
+        double W = 0.0, P = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            W += (double)sm.ww[16 * tid + i];
+            P += (double)sm.pw[16 * tid + i];
+        }
+        if (sm.xs[tid] > 0.0) {
+            const double rem = W - sm.xs[tid];
+            W = rem > W * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
+        }
+        a.seg[((size_t)b * S2 + c) * kSegs + tid] = W;
+        W = wave_sum(W);
+        P = wave_sum(P);
+        if (lane == 0) {
+            a.mass[(size_t)b * S2 + c] = W;
+            a.massfb[(size_t)b * S2 + c] = P;
+        }
     }
 }
 
-// First chunk c (of n, weights in LDS) with cm[c] > 0 whose inclusive prefix reaches t;
-// if rounding leaves t beyond the total, the last positive chunk.  Wave 0 only; every
-// lane returns the chunk and the weight before it.
-__device__ inline int wave_locate(const double* cm, int n, double t, double& before) {
+// Result of a wave-wide search over 64 weights (one per lane).
+struct Found {
+    int hit;          // first lane with x > 0 whose inclusive prefix reaches t, or -1
+    double before;    // weight ahead of `hit`
+    int last;         // last lane with x > 0, or -1
+    double last_before;
+    double total;     // sum of the 64 weights
+};
+
+// Among the 64 lanes' values x, counting `carry` ahead of lane 0: the first lane with
+// x > 0 whose inclusive prefix reaches t, and the last positive lane (for when rounding
+// leaves t beyond the total).  Every lane gets the same result.
+__device__ __attribute__((always_inline)) Found wave_find(double x, double t, double carry) {
+    const int lane = threadIdx.x & 63;
+    double incl = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const double excl = incl - x;
+    const unsigned long long hit = __ballot(x > 0.0 && t <= carry + incl);
+    const unsigned long long pos = __ballot(x > 0.0);
+    Found f;
+    f.hit = hit ? __ffsll((long long)hit) - 1 : -1;
+    f.last = pos ? 63 - __clzll((long long)pos) : -1;
+    const double eh = __shfl(excl, f.hit < 0 ? 0 : f.hit);
+    const double el = __shfl(excl, f.last < 0 ? 0 : f.last);
+    f.before = carry + eh;
+    f.last_before = carry + el;
+    f.total = __shfl(incl, 63);
+    return f;
+}
+
+// First entry i of w[0..n) with w[i] > 0 whose inclusive prefix reaches t; if rounding
+// leaves t beyond the total, the last positive entry; -1 if none is positive.  One full
+// wave; every lane returns the entry and the weight before it.
+__device__ __attribute__((always_inline)) int wave_locate(const double* w, int n, double t,
+                                                        double& before) {
     const int lane = threadIdx.x & 63;
     double carry = 0.0, last_before = 0.0;
     int last = -1;
     for (int i0 = 0; i0 < n; i0 += 64) {
-        const int i = i0 + lane;
-        const double x = i < n ? cm[i] : 0.0;
-        double incl = x;
-        for (int o = 1; o < 64; o <<= 1) {
-            const double y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
+        const Found f = wave_find(i0 + lane < n ? w[i0 + lane] : 0.0, t, carry);
+        if (f.hit >= 0) {
+            before = f.before;
+            return i0 + f.hit;
         }
-        const double excl = incl - x;
-        const unsigned long long hit = __ballot(x > 0.0 && t <= carry + incl);
-        if (hit) {
-            const int l = __ffsll((long long)hit) - 1;
-            before = carry + __shfl(excl, l);
-            return i0 + l;
+        if (f.last >= 0) {
+            last = i0 + f.last;
+            last_before = f.last_before;
         }
-        const unsigned long long pos = __ballot(x > 0.0);
-        if (pos) {
-            const int l = 63 - __clzll((long long)pos);
-            last = i0 + l;
-            last_before = carry + __shfl(excl, l);
-        }
-        carry += __shfl(incl, 63);
+        carry += f.total;
     }
     before = last_before;
     return last;
 }
 
-// One workgroup per request.
+// One wave per request: chunk, then segment, then token.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_draw(KArgs a) {
-    __shared__ Smem sm;
-    __shared__ float tile[kTile];
-    const int tid = threadIdx.x, wave = tid >> 6;
+__global__ __launch_bounds__(64) void k_draw(KArgs a) {
+    const int lane = threadIdx.x;
     const int S2 = a.S2, V = a.V;
     const int b = blockIdx.x;
-    const DrawState st = a.dstate[b];
+    const DrawState st = load_state(a.dstate + b);
     if (st.kind == kDrawNone) return;
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
     const float s2 = kLog2e / (float)st.T;
     const double u = (double)a.coins[st.coin];
-    for (int c = tid; c < S2; c += kBlock) sm.cm[c] = a.mass[(size_t)b * kMaxFine + c];
-    __syncthreads();
-    if (wave == 0) {
-        double tot = 0.0;
-        for (int i0 = 0; i0 < S2; i0 += 64) {
-            const int i = i0 + (tid & 63);
-            tot += wave_sum(i < S2 ? sm.cm[i] : 0.0);
-        }
-        const bool fallback = !(tot > 0.0);
-        if (fallback) {  // every lane sees the same total: reload the plain target weights
-            tot = 0.0;
-            for (int i0 = 0; i0 < S2; i0 += 64) {
-                const int i = i0 + (tid & 63);
-                const double x = i < S2 ? a.massfb[(size_t)b * kMaxFine + i] : 0.0;
-                if (i < S2) sm.cm[i] = x;
-                tot += wave_sum(x);
+    double tot = 0.0;
+    for (int i0 = 0; i0 < S2; i0 += 64)
+        tot += wave_sum(i0 + lane < S2 ? a.mass[(size_t)b * S2 + i0 + lane] : 0.0);
+    const bool fallback = !(tot > 0.0);  // plain target weights, nothing excluded
+    if (fallback) {
+        tot = 0.0;
+        for (int i0 = 0; i0 < S2; i0 += 64)
+            tot += wave_sum(i0 + lane < S2 ? a.massfb[(size_t)b * S2 + i0 + lane] : 0.0);
+    }
+    const bool resid = st.kind == kDrawResidual && !fallback;
+    const float* qrow = resid ? a.q + (size_t)st.qrow * V : nullptr;
+    int y = -1;
+    float ly = 0.f;
+    const double t = u * tot;
+    double before = 0.0;
+    const int c = wave_locate((fallback ? a.massfb : a.mass) + (size_t)b * S2, S2, t, before);
+    if (c >= 0) {
+        const double tc = t - before;
+        // segment weights: stored by k_mass, or (fallback) the plain target row, summed here
+        double x;
+        if (!fallback) {
+            x = a.seg[((size_t)b * S2 + c) * kSegs + lane];
+        } else {
+            x = 0.0;
+            for (int g0 = 0; g0 < kSegs; g0 += 8) {  // eight segments' loads in flight
+                float pv[8];
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const int j = c * kFine + (g0 + g) * kSeg + lane;
+                    float p = 0.f;
+                    if (j < V) draw_weight<T, false>(rowp, nullptr, j, st.M, s2, st.invZ, p);
+                    pv[g] = p;
+                }
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const double sg = wave_sum((double)pv[g]);
+                    if (lane == g0 + g) x = sg;
+                }
             }
         }
-        double before = 0.0;
-        const double t = u * tot;
-        const int c = wave_locate(sm.cm, S2, t, before);
-        if (tid == 0) {
-            sm.fallback = fallback;
-            sm.sstar = c;
-            sm.tau = t - before;
+        const Found fs = wave_find(x, tc, 0.0);
+        const int g = fs.hit >= 0 ? fs.hit : fs.last;
+        const double bs = fs.hit >= 0 ? fs.before : fs.last_before;
+        if (g >= 0) {
+            const double tg = tc - bs;
+            const int j = c * kFine + g * kSeg + lane;  // kSeg == 64: one element per lane
+            float l = 0.f, w = 0.f;
+            if (j < V) {
+                l = Ld<T>::one(rowp + j);
+                float p;
+                w = resid ? draw_weight<T, true>(rowp, qrow, j, st.M, s2, st.invZ, p)
+                          : draw_weight<T, false>(rowp, nullptr, j, st.M, s2, st.invZ, p);
+                if (!fallback && st.nexcl > 0) {
+                    const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
+                    for (int e = 0; e < st.nexcl; ++e)
+                        if (ex[e] == j) w = 0.f;
+                }
+            }
+            const Found fe = wave_find((double)w, tg, 0.0);
+            const int f = fe.hit >= 0 ? fe.hit : fe.last;
+            if (f >= 0) {
+                y = c * kFine + g * kSeg + f;
+                ly = __shfl(l, f);
+            }
         }
     }
-    __syncthreads();
-    const int c = sm.sstar;
-    const bool fallback = sm.fallback;
-    int y = -1;
-    if (c >= 0) {
-        const int nx = fallback ? 0 : st.nexcl;
-        const int c0 = c * a.fine, c1 = min(V, c0 + a.fine);
-        const int32_t* ex = nx > 0 ? a.excl + (size_t)b * SPEC_MAX_N : nullptr;
-        if (st.kind == kDrawResidual && !fallback) {
-            const DrawWeight<T, true> wf{rowp, a.q + (size_t)st.qrow * V, st.M, s2, st.invZ};
-            y = scan_find(wf, c0, c1, sm.tau, ex, nx, tile, sm);
-        } else {
-            const DrawWeight<T, false> wf{rowp, nullptr, st.M, s2, st.invZ};
-            y = scan_find(wf, c0, c1, sm.tau, ex, nx, tile, sm);
-        }
-        if (y < 0) y = c0;  // unreachable for a positive chunk weight
-    }
-    if (tid == 0) {
+    if (lane == 0) {
         a.out_tokens[st.out] = y;
-        if (a.probs) {
-            float py = 0.f;
-            if (y >= 0 && y < V)
-                py = (float)(exp(((double)Ld<T>::one(rowp + y) - (double)st.M) / st.T) / st.Z);
-            a.probs[st.out] = py;
-        }
+        if (a.probs)
+            a.probs[st.out] = y >= 0 ? (float)(exp(((double)ly - (double)st.M) / st.T) / st.Z) : 0.f;
     }
 }
 
@@ -1188,35 +1155,42 @@ __global__ __launch_bounds__(kBlock) void k_draw(KArgs a) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t parts, dstate, mass, massfb, excl, total;
+    size_t parts, dstate, mass, massfb, seg, excl, total;
 };
 
+inline long fine_chunks(int V) { return ((long)V + kFine - 1) / kFine; }
+
 // Records are stored with a row stride of S (the split count of the call), but the
-// workspace is sized for the largest split count so that its size depends on op, B, R.
-Layout layout_for(int op, int B, int R) {
+// workspace is sized for the largest split count so that its size depends only on
+// op, B, R and V.
+Layout layout_for(int op, int B, int R, int V) {
     Layout L;
+    const size_t S2 = (size_t)fine_chunks(V);
     size_t off = 0;
     L.parts = off;
     off = align256(off + sizeof(Part) * (size_t)B * R * kMaxSplits);
     L.dstate = off;
     off = align256(off + sizeof(DrawState) * (size_t)B);
     L.mass = off;
-    off = align256(off + sizeof(double) * (size_t)B * kMaxFine);
+    off = align256(off + sizeof(double) * (size_t)B * S2);
     L.massfb = off;
-    off = align256(off + sizeof(double) * (size_t)B * kMaxFine);
+    off = align256(off + sizeof(double) * (size_t)B * S2);
+    L.seg = off;
+    off = align256(off + sizeof(double) * (size_t)B * S2 * kSegs);
     L.excl = off;
     if (op == SPEC_OP_TREE) off = align256(off + sizeof(int32_t) * (size_t)B * SPEC_MAX_N);
     L.total = off;
     return L;
 }
 
-void bind_workspace(KArgs& a, void* ws, int op, int B, int R) {
-    const Layout L = layout_for(op, B, R);
+void bind_workspace(KArgs& a, void* ws, int op) {
+    const Layout L = layout_for(op, a.B, a.R, a.V);
     char* base = static_cast<char*>(ws);
     a.parts = reinterpret_cast<Part*>(base + L.parts);
     a.dstate = reinterpret_cast<DrawState*>(base + L.dstate);
     a.mass = reinterpret_cast<double*>(base + L.mass);
     a.massfb = reinterpret_cast<double*>(base + L.massfb);
+    a.seg = reinterpret_cast<double*>(base + L.seg);
     a.excl = op == SPEC_OP_TREE ? reinterpret_cast<int32_t*>(base + L.excl) : nullptr;
 }
 
@@ -1243,19 +1217,10 @@ void choose_split(long rows, int V, int esize, int* S_out, int* chunk_out) {
     *chunk_out = (int)ch;
 }
 
-// Fine chunks of the final draw: one LDS tile each (kTile elements), or more per chunk
-// when the row has more than kMaxFine tiles.
-void choose_fine(int V, int* S2_out, int* fine_out) {
-    long fine = kTile;
-    if ((long)V > (long)kMaxFine * kTile) fine = (((long)V + kMaxFine - 1) / kMaxFine + 7) / 8 * 8;
-    *fine_out = (int)fine;
-    *S2_out = (int)(((long)V + fine - 1) / fine);
-}
-
 // Launch shapes of a call; SPEC_ERR_SHAPE when a grid would exceed 2^32 work-items.
 int setup_shapes(KArgs& a, int esize) {
     choose_split((long)a.B * a.R, a.V, esize, &a.S, &a.chunk);
-    choose_fine(a.V, &a.S2, &a.fine);
+    a.S2 = (int)fine_chunks(a.V);
     const long long lim = 0xffffffffLL / kBlock;
     if ((long long)a.B * a.R * a.S > lim || (long long)a.B * a.S2 > lim) return SPEC_ERR_SHAPE;
     return SPEC_OK;
@@ -1269,7 +1234,6 @@ int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t w
     const size_t es = dtype == SPEC_F32 ? 4 : 2;
     if (((uintptr_t)logits) % es) return SPEC_ERR_PARAM;
     if ((long long)B * R * kMaxSplits > (long long)INT_MAX) return SPEC_ERR_SHAPE;
-    if ((long long)B * kMaxFine > (long long)INT_MAX) return SPEC_ERR_SHAPE;
     if (B > 0) {
         if (((uintptr_t)ws) % 256) return SPEC_ERR_WORKSPACE;
         if (ws_bytes < spec_workspace_bytes(op, B, R, V)) return SPEC_ERR_WORKSPACE;
@@ -1293,7 +1257,7 @@ int run_draw(KArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_mass<T>), dim3(a.B * a.S2), dim3(kBlock), 0, st, a);
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
-    hipLaunchKernelGGL((k_draw<T>), dim3(a.B), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((k_draw<T>), dim3(a.B), dim3(64), 0, st, a);
     return launch_status();
 }
 
@@ -1336,7 +1300,7 @@ extern "C" size_t spec_workspace_bytes(int op, int B, int R, int V) {
     } else {
         return 0;
     }
-    return layout_for(op, B, R).total;
+    return layout_for(op, B, R, V).total;
 }
 
 extern "C" const char* spec_status_str(int status) {
@@ -1369,7 +1333,7 @@ extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* 
     a.out_tokens = out_tokens;
     rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
     if (rc != SPEC_OK) return rc;
-    bind_workspace(a, workspace, SPEC_OP_GREEDY, B, a.R);
+    bind_workspace(a, workspace, SPEC_OP_GREEDY);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_greedy<float>(a, st) : run_greedy<uint16_t>(a, st);
 }
@@ -1399,7 +1363,7 @@ extern "C" int spec_verify_chain(const void* logits, int dtype, const float* dra
     a.probs = probs_out;
     rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
     if (rc != SPEC_OK) return rc;
-    bind_workspace(a, workspace, SPEC_OP_CHAIN, B, a.R);
+    bind_workspace(a, workspace, SPEC_OP_CHAIN);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_chain<float>(a, st) : run_chain<uint16_t>(a, st);
 }
@@ -1439,7 +1403,7 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     a.probs = probs_out;
     rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
     if (rc != SPEC_OK) return rc;
-    bind_workspace(a, workspace, SPEC_OP_TREE, B, N);
+    bind_workspace(a, workspace, SPEC_OP_TREE);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_tree<float>(a, mode, st) : run_tree<uint16_t>(a, mode, st);
 }
