@@ -47,6 +47,8 @@ def lib():
                                          ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp]
         for f in (L.oracle_verify_greedy, L.oracle_verify_chain, L.oracle_verify_tree):
             f.restype = ctypes.c_int
+        L.oracle_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp]
+        L.oracle_tree_mask.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -139,3 +141,17 @@ def verify_tree(logits, dtype, node_tokens, parents, coins, temperature, D, mode
         raise ValueError(f"oracle_verify_tree rejected its arguments ({rc})")
     return dict(accept_len=acc, out_tokens=out, accepted_nodes=nodes, probs=probs,
                 margin=margin)
+
+
+def tree_mask(parents, base_pos=None):
+    """Returns (mask [B][N][ceil(N/32)] uint32 bit rows, positions [B][N] int32)."""
+    pa = np.ascontiguousarray(parents, dtype=np.int32)
+    B, N = pa.shape
+    W = (N + 31) // 32
+    bp = None if base_pos is None else np.ascontiguousarray(base_pos, dtype=np.int32)
+    mask = np.empty((B, N, W), np.uint32)
+    pos = np.empty((B, N), np.int32)
+    rc = lib().oracle_tree_mask(_ptr(pa), _ptr(bp), B, N, _ptr(mask), _ptr(pos))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_mask rejected its arguments ({rc})")
+    return mask, pos

@@ -460,6 +460,45 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
     return 0;
 }
 
+/* ---- tree attention mask and positions ---------------------------------------------
+ * [origins] SpecInfer, tree attention mask: the token tree is flattened into one sequence
+ * and every node attends only to its ancestors, so one target forward scores every
+ * branch and the branches share one KV.  Readings: a node also attends to itself (the
+ * diagonal of causal attention); the root (node 0) is the last committed token, and a
+ * node's position is the root's position plus its depth.
+ * Row i of the mask is the path from node i up to the root: walk the parent pointers
+ * from i and set the bit of every node met, i included. */
+static void tree_mask_one(const int32_t* par, int32_t base, int N, int W, uint32_t* mask,
+                          int32_t* pos) {
+    int valid = par[0] == -1;
+    for (int i = 1; i < N; ++i)
+        if (par[i] < 0 || par[i] >= i) valid = 0;
+    for (size_t e = 0; e < (size_t)N * (size_t)W; ++e) mask[e] = 0u;
+    for (int i = 0; i < N; ++i) {
+        if (!valid) {
+            if (pos) pos[i] = -1;
+            continue;
+        }
+        int steps = 0;
+        for (int j = i; j >= 0; j = par[j]) {
+            mask[(size_t)i * W + (size_t)(j / 32)] |= 1u << (j % 32);
+            ++steps;
+        }
+        if (pos) pos[i] = base + steps - 1;
+    }
+}
+
+int oracle_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
+                     uint32_t* mask_bits, int32_t* positions) {
+    if (!parents || !mask_bits || B < 0 || N < 1) return -1;
+    int W = (N + 31) / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        tree_mask_one(parents + (size_t)b * N, base_pos ? base_pos[b] : 0, N, W,
+                      mask_bits + (size_t)b * N * W, positions ? positions + (size_t)b * N : NULL);
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -56,6 +56,13 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
                        float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
                        int32_t* accepted_nodes, double* probs_out, double* min_margin);
 
+/* Tree attention mask: mask_bits [B][N][W], W = ceil(N/32); bit (j % 32) of word j / 32 of
+ * row i is set iff node j lies on the path from node i to the root (i included).
+ * positions [B][N] (may be NULL) = base_pos[b] (0 when base_pos is NULL) + depth(i).
+ * A request whose parent array is malformed gets all-zero rows and positions -1. */
+int oracle_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
+                     uint32_t* mask_bits, int32_t* positions);
+
 /* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
 int oracle_num_threads(void);
 

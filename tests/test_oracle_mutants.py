@@ -18,6 +18,7 @@ import oracle
 import test_golden_cases as golden
 import test_oracle_law as law
 import test_oracle_tree_greedy as tg
+import test_oracle_tree_mask as tm
 
 SRC = open(oracle.SRC).read()
 
@@ -47,6 +48,16 @@ MUTANTS = [
     ("tree coin of level 0 reused", "double u = (double)coins[d];", "double u = (double)coins[0];"),
     ("tree greedy follows first child", "par[c] == cur && tok[c] == a", "par[c] == cur"),
     ("accept test on q instead of p", "accept = p > 0.0 && u <= ratio;", "accept = u <= qx;"),
+    ("tree mask without the node itself", "for (int j = i; j >= 0; j = par[j]) {",
+     "for (int j = par[i]; j >= 0; j = par[j]) {"),
+    ("tree mask transposed", "mask[(size_t)i * W + (size_t)(j / 32)] |= 1u << (j % 32);",
+     "mask[(size_t)j * W + (size_t)(i / 32)] |= 1u << (i % 32);"),
+    ("tree mask positions without the base", "if (pos) pos[i] = base + steps - 1;",
+     "if (pos) pos[i] = steps - 1;"),
+    ("tree mask positions count the node twice", "if (pos) pos[i] = base + steps - 1;",
+     "if (pos) pos[i] = base + steps;"),
+    ("tree mask stops below the root", "for (int j = i; j >= 0; j = par[j]) {",
+     "for (int j = i; j > 0; j = par[j]) {"),
 ]
 
 
@@ -69,6 +80,9 @@ def _pins():
         yield lambda case=case: golden.test_chain_hand_case(case)
     for case in golden.CASES["tree"]:
         yield lambda case=case: golden.test_tree_hand_case(case)
+    yield lambda: tm.test_chain_is_lower_triangular(33)
+    yield tm.test_golden_cases
+    yield lambda: tm.test_masked_tree_attention_equals_per_branch_causal_attention(0)
 
 
 @pytest.mark.parametrize("name,orig,mutation", MUTANTS, ids=[m[0] for m in MUTANTS])
