@@ -297,6 +297,26 @@ def _tree_modes(args, torch, dev, api, wl):
                      "GB/s_eager": eager / (d.mean() * 1e-3) / 1e9,
                      "frac_eager": eager / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "path_only_bytes": path, "eager_bytes": eager}
+    # the tree attention mask and positions of the same trees (the step before verify)
+    base = torch.arange(t.B, dtype=torch.int32, device=dev)
+    W = (t.N + 31) // 32
+    outs = (torch.empty(t.B, t.N, W, dtype=torch.int32, device=dev),
+            torch.empty(t.B, t.N, dtype=torch.int32, device=dev))
+    for _ in range(5):
+        api.spec_tree_mask(par, base, out=outs)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(20)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        api.spec_tree_mask(par, base, out=outs)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in ev])
+    nbytes = t.B * t.N * 4 + t.B * 4 + t.B * t.N * W * 4 + t.B * t.N * 4
+    out["tree_mask"] = {"workload": t.name, "avg_ms": float(d.mean()),
+                        "nodes/s": t.B * t.N / (d.mean() * 1e-3), "bytes": nbytes,
+                        "bound": "latency (one workgroup per request)"}
     return out
 
 

@@ -147,6 +147,22 @@ int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
                      int32_t* accepted_nodes, float* probs_out, void* workspace,
                      size_t ws_bytes, void* stream);
 
+/* Tree attention mask and positions (spec_origins, "SpecInfer": the token tree is
+ * flattened into one sequence and each node attends only to its ancestors, so one target
+ * forward scores every branch over a shared KV).  This is the step before verify: it
+ * builds, from the same parent array spec_verify_tree takes, the mask and the position
+ * ids of that forward.  A node also attends to itself (the causal diagonal).
+ *   parents   [B][N]  parents[b][0] = -1 and 0 <= parents[b][i] < i (node 0 = root, the
+ *             last committed token);
+ *   base_pos  [B]     position id of the root, or NULL for 0;
+ *   mask      [B][N][W] uint32 out, W = (N + 31) / 32: bit (j % 32) of word j / 32 of row i
+ *             is set iff node j lies on the path from node i to the root, i included;
+ *   positions [B][N]  out, base_pos[b] + depth of node i; may be NULL.
+ * A request whose parent array is malformed gets all-zero mask rows and positions -1.
+ * 1 <= N <= SPEC_MAX_N.  No workspace; device pointers; enqueued on `stream`. */
+int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
+                   uint32_t* mask, int32_t* positions, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,8 @@ def lib():
         L.spec_verify_tree.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, fp,
                                        vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_tree.restype = ip
+        L.spec_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp, vp]
+        L.spec_tree_mask.restype = ip
         _lib = L
     return _lib
 

@@ -157,3 +157,29 @@ def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: t
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_verify_tree", rc)
     return acc, toks, nodes, probs
+
+
+def spec_tree_mask(parents: torch.Tensor, base_pos=None, *, want_positions: bool = True,
+                   stream=None, out=None):
+    """Tree attention mask.  parents [B][N] int32, base_pos [B] int32 or None.
+
+    Returns (mask [B][N][ceil(N/32)] int32 holding the uint32 bit rows,
+    positions [B][N] int32 or None)."""
+    _check(parents, "parents", torch.int32, 2)
+    B, N = parents.shape
+    if base_pos is not None:
+        _check(base_pos, "base_pos", torch.int32, 1)
+        if base_pos.shape != (B,):
+            raise ValueError("base_pos must be [B]")
+    dev = parents.device
+    W = (N + 31) // 32
+    if out is None:
+        mask = torch.empty(B, N, W, dtype=torch.int32, device=dev)
+        pos = torch.empty(B, N, dtype=torch.int32, device=dev) if want_positions else None
+    else:
+        mask, pos = out
+    rc = L.lib().spec_tree_mask(_ptr(parents), _ptr(base_pos), B, N, _ptr(mask), _ptr(pos),
+                                _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_tree_mask", rc)
+    return mask, pos

@@ -639,6 +639,36 @@ __device__ void tree_row_stats(const KArgs& a, int b, bool sampling, double Td, 
     __syncthreads();
 }
 
+// Depth of every node by pointer jumping (parents[i] < i, so every chain of parents ends
+// at the root): ceil(log2 N) rounds.  par, anc and dep are LDS arrays of N entries; the
+// parent array must already be validated.  Block-wide.
+__device__ void tree_depths(const int* par, int N, int* anc, int* dep) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < N; i += kBlock) {
+        anc[i] = i == 0 ? 0 : par[i];
+        dep[i] = i == 0 ? 0 : 1;
+    }
+    for (int r = 1; r < N; r <<= 1) {
+        __syncthreads();
+        int nd[SPEC_MAX_N / kBlock], na[SPEC_MAX_N / kBlock];
+        int c = 0;
+        for (int i = tid; i < N; i += kBlock, ++c) {
+            const int an = anc[i];
+            nd[c] = dep[i] + (an == i ? 0 : dep[an]);
+            na[c] = anc[an];
+        }
+        __syncthreads();
+        c = 0;
+        for (int i = tid; i < N; i += kBlock, ++c) {
+            if (anc[i] != i) {
+                dep[i] = nd[c];
+                anc[i] = na[c];
+            }
+        }
+    }
+    __syncthreads();
+}
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
     __shared__ TreeSmem ts;
@@ -673,30 +703,7 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
     const double Td = (double)Tf;
     bad = __syncthreads_or(bad);
     if (!bad) {
-        // depths by pointer jumping (parents[i] < i: every chain ends at the root)
-        for (int i = tid; i < N; i += kBlock) {
-            ts.anc[i] = i == 0 ? 0 : ts.par[i];
-            ts.dep[i] = i == 0 ? 0 : 1;
-        }
-        for (int r = 1; r < N; r <<= 1) {
-            __syncthreads();
-            int nd[SPEC_MAX_N / kBlock], na[SPEC_MAX_N / kBlock];
-            int c = 0;
-            for (int i = tid; i < N; i += kBlock, ++c) {
-                const int an = ts.anc[i];
-                nd[c] = ts.dep[i] + (an == i ? 0 : ts.dep[an]);
-                na[c] = ts.anc[an];
-            }
-            __syncthreads();
-            c = 0;
-            for (int i = tid; i < N; i += kBlock, ++c) {
-                if (ts.anc[i] != i) {
-                    ts.dep[i] = nd[c];
-                    ts.anc[i] = na[c];
-                }
-            }
-        }
-        __syncthreads();
+        tree_depths(ts.par, N, ts.anc, ts.dep);
         for (int i = tid; i < N; i += kBlock)
             if (ts.dep[i] > D) bad = true;
         // every row's statistics; each row needs a finite logit
@@ -1150,6 +1157,91 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// k_tree_mask: one workgroup per request -- the ancestor-only attention mask of the
+// flattened token tree and the position of every node (spec_origins, SpecInfer)
+//
+// Row i starts as {i, parent(i)} and its jump pointer as the grandparent; each round ORs
+// in the row of the node the pointer names and doubles the pointer, so after r rounds
+// the row holds every ancestor within 2^(r+1) steps.  Rows only ever gain true ancestors,
+// so a row read while its owner updates it in the same round is still a subset of the
+// answer.  The rows live in LDS when they fit, otherwise in the output itself.
+
+constexpr int kMaskLdsWords = 8192;  // N * W words kept in LDS (N <= 512)
+
+struct MaskSmem {
+    int par[SPEC_MAX_N];
+    int anc[SPEC_MAX_N];
+    int dep[SPEC_MAX_N];
+    int jmp[SPEC_MAX_N];
+    uint32_t rows[kMaskLdsWords];
+};
+
+__global__ __launch_bounds__(kBlock) void k_tree_mask(const int32_t* parents,
+                                                      const int32_t* base_pos, int N,
+                                                      uint32_t* mask, int32_t* positions) {
+    __shared__ MaskSmem sm;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const int W = (N + 31) / 32;
+    const int32_t* par_g = parents + (size_t)b * N;
+    uint32_t* out = mask + (size_t)b * N * W;
+    bool bad = false;
+    for (int i = tid; i < N; i += kBlock) {
+        const int p = par_g[i];
+        sm.par[i] = p;
+        if (i == 0 ? p != -1 : (p < 0 || p >= i)) bad = true;
+    }
+    bad = __syncthreads_or(bad);
+    if (bad) {
+        for (int e = tid; e < N * W; e += kBlock) out[e] = 0u;
+        if (positions)
+            for (int i = tid; i < N; i += kBlock) positions[(size_t)b * N + i] = -1;
+        return;
+    }
+    uint32_t* rows = N * W <= kMaskLdsWords ? sm.rows : out;
+    for (int e = tid; e < N * W; e += kBlock) {
+        const int i = e / W, w = e - i * W;
+        const int p = sm.par[i];
+        uint32_t bits = (i >> 5) == w ? 1u << (i & 31) : 0u;
+        if (p >= 0 && (p >> 5) == w) bits |= 1u << (p & 31);
+        rows[e] = bits;
+    }
+    for (int i = tid; i < N; i += kBlock) {
+        const int p = sm.par[i];
+        sm.jmp[i] = p >= 0 ? sm.par[p] : -1;
+    }
+    bool more = true;
+    while (__syncthreads_or(more)) {
+        for (int e = tid; e < N * W; e += kBlock) {
+            const int i = e / W, w = e - i * W;
+            const int j = sm.jmp[i];
+            if (j >= 0) rows[e] |= rows[j * W + w];
+        }
+        __syncthreads();
+        int nj[SPEC_MAX_N / kBlock];
+        int c = 0;
+        for (int i = tid; i < N; i += kBlock, ++c) {
+            const int j = sm.jmp[i];
+            nj[c] = j >= 0 ? sm.jmp[j] : -1;
+        }
+        __syncthreads();
+        more = false;
+        c = 0;
+        for (int i = tid; i < N; i += kBlock, ++c) {
+            sm.jmp[i] = nj[c];
+            more = more || nj[c] >= 0;
+        }
+    }
+    if (rows != out)
+        for (int e = tid; e < N * W; e += kBlock) out[e] = rows[e];
+    if (positions) {
+        tree_depths(sm.par, N, sm.anc, sm.dep);
+        const int base = base_pos ? base_pos[b] : 0;
+        for (int i = tid; i < N; i += kBlock) positions[(size_t)b * N + i] = base + sm.dep[i];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // host side
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1406,4 +1498,14 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     bind_workspace(a, workspace, SPEC_OP_TREE);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_tree<float>(a, mode, st) : run_tree<uint16_t>(a, mode, st);
+}
+
+extern "C" int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
+                              uint32_t* mask, int32_t* positions, void* stream) {
+    if (!parents || !mask) return SPEC_ERR_NULL;
+    if (B < 0 || N < 1 || N > SPEC_MAX_N) return SPEC_ERR_SHAPE;
+    if (B == 0) return SPEC_OK;
+    hipLaunchKernelGGL(k_tree_mask, dim3(B), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       parents, base_pos, N, mask, positions);
+    return launch_status();
 }

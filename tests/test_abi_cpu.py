@@ -22,7 +22,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.declared_functions()
     assert set(names) >= {"spec_verify_greedy", "spec_verify_chain", "spec_verify_tree",
-                          "spec_workspace_bytes", "spec_status_str"}
+                          "spec_tree_mask", "spec_workspace_bytes", "spec_status_str"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -121,3 +121,13 @@ def test_tree_rejects_bad_arguments(lib):
     # greedy mode needs neither coins nor temperature: check only up to validation
     assert _tree(lib, mode=L.SPEC_TREE_GREEDY, coins=None, temp=None, ws=None) == L.SPEC_ERR_NULL
     assert _tree(lib, B=0, mode=L.SPEC_TREE_GREEDY, coins=None, temp=None) == L.SPEC_OK
+
+
+
+def test_tree_mask_rejects_bad_arguments(lib):
+    assert lib.spec_tree_mask(None, None, 2, 8, P, P, None) == L.SPEC_ERR_NULL
+    assert lib.spec_tree_mask(P, None, 2, 8, None, P, None) == L.SPEC_ERR_NULL
+    assert lib.spec_tree_mask(P, None, -1, 8, P, P, None) == L.SPEC_ERR_SHAPE
+    assert lib.spec_tree_mask(P, None, 2, 0, P, P, None) == L.SPEC_ERR_SHAPE
+    assert lib.spec_tree_mask(P, None, 2, L.SPEC_MAX_N + 1, P, P, None) == L.SPEC_ERR_SHAPE
+    assert lib.spec_tree_mask(P, None, 0, 8, P, None, None) == L.SPEC_OK
