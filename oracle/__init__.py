@@ -49,6 +49,8 @@ def lib():
             f.restype = ctypes.c_int
         L.oracle_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp]
         L.oracle_tree_mask.restype = ctypes.c_int
+        L.oracle_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, ctypes.c_size_t, vp]
+        L.oracle_tree_commit_kv.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -155,3 +157,21 @@ def tree_mask(parents, base_pos=None):
     if rc != 0:
         raise ValueError(f"oracle_tree_mask rejected its arguments ({rc})")
     return mask, pos
+
+
+def tree_commit_kv(accepted_nodes, accept_len, kv_tree, kv_out):
+    """kv_tree [B][N][row_bytes] uint8, kv_out [B][D+1][row_bytes] uint8 (updated in place).
+    Returns slots [B][D+1] int32."""
+    nodes = np.ascontiguousarray(accepted_nodes, dtype=np.int32)
+    acc = np.ascontiguousarray(accept_len, dtype=np.int32)
+    B, D = nodes.shape
+    src = np.ascontiguousarray(kv_tree, dtype=np.uint8)
+    if not (kv_out.flags["C_CONTIGUOUS"] and kv_out.dtype == np.uint8):
+        raise TypeError("kv_out must be a C-contiguous uint8 array")
+    N, row_bytes = src.shape[1], src.shape[2]
+    slots = np.empty((B, D + 1), np.int32)
+    rc = lib().oracle_tree_commit_kv(_ptr(nodes), _ptr(acc), B, D, N, _ptr(src), _ptr(kv_out),
+                                     row_bytes, _ptr(slots))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_commit_kv rejected its arguments ({rc})")
+    return slots

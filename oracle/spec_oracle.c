@@ -499,6 +499,45 @@ int oracle_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int
     return 0;
 }
 
+/* ---- committing the accepted path of a token tree ----------------------------------
+ * [atlas] the tree chapter covers how the KV of a token tree is laid out and rolled
+ * back after a rejection; the serving section lists rolling back the KV of rejected
+ * drafts as a cost that speculation adds.  [origins] SpecInfer: the verify forward
+ * computes every node of the flattened tree over one shared KV.
+ * Readings: the verify forward left one KV row per tree node, node j in row j of the
+ * request's block; committing keeps the root and the accepted nodes in path order, so
+ * output row d is the KV row of the d-th node of the path (row 0 the root) and the KV of
+ * rejected nodes is dropped.  Output rows past the path are left as they were.
+ * slots[d] names the tree node copied into output row d (-1 past the path).  A request
+ * with accept_len outside [0, D] or an accepted node outside [0, N) copies nothing and
+ * gets slots -1. */
+static void commit_one(const int32_t* nodes, int32_t k, int D, int N, const uint8_t* src,
+                       uint8_t* dst, size_t row_bytes, int32_t* slots) {
+    int valid = k >= 0 && k <= D;
+    for (int d = 0; d < k && valid; ++d)
+        if (nodes[d] < 0 || nodes[d] >= N) valid = 0;
+    for (int d = 0; d <= D; ++d) {
+        int node = -1;
+        if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];
+        if (slots) slots[d] = node;
+        if (node >= 0) memcpy(dst + (size_t)d * row_bytes, src + (size_t)node * row_bytes, row_bytes);
+    }
+}
+
+int oracle_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_len, int B,
+                          int D, int N, const void* kv_tree, void* kv_out, size_t row_bytes,
+                          int32_t* slots) {
+    if (!accepted_nodes || !accept_len || !kv_tree || !kv_out || B < 0 || D < 1 || N < 1)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        commit_one(accepted_nodes + (size_t)b * D, accept_len[b], D, N,
+                   (const uint8_t*)kv_tree + (size_t)b * N * row_bytes,
+                   (uint8_t*)kv_out + (size_t)b * (D + 1) * row_bytes, row_bytes,
+                   slots ? slots + (size_t)b * (D + 1) : NULL);
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -23,6 +23,7 @@
  */
 #ifndef SPEC_ORACLE_H
 #define SPEC_ORACLE_H
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -62,6 +63,15 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
  * A request whose parent array is malformed gets all-zero rows and positions -1. */
 int oracle_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
                      uint32_t* mask_bits, int32_t* positions);
+
+/* Commit the accepted path of a token tree: kv_tree [B][N][row_bytes] (one KV row per
+ * node), kv_out [B][D+1][row_bytes]: row d = kv_tree row of the d-th node of the path
+ * (row 0 the root, rows 1..k the accepted nodes); rows past the path untouched.
+ * slots [B][D+1] (may be NULL): the node copied into each row, -1 past the path.
+ * accept_len outside [0, D] or an accepted node outside [0, N): nothing copied, slots -1. */
+int oracle_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_len, int B,
+                          int D, int N, const void* kv_tree, void* kv_out, size_t row_bytes,
+                          int32_t* slots);
 
 /* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
 int oracle_num_threads(void);

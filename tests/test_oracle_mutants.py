@@ -19,6 +19,7 @@ import test_golden_cases as golden
 import test_oracle_law as law
 import test_oracle_tree_greedy as tg
 import test_oracle_tree_mask as tm
+import test_oracle_commit_kv as ck
 
 SRC = open(oracle.SRC).read()
 
@@ -58,6 +59,12 @@ MUTANTS = [
      "if (pos) pos[i] = base + steps;"),
     ("tree mask stops below the root", "for (int j = i; j >= 0; j = par[j]) {",
      "for (int j = i; j > 0; j = par[j]) {"),
+    ("commit takes the node of the same index", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
+     "if (valid && d <= k) node = d == 0 ? 0 : nodes[d < k ? d : d - 1];"),
+    ("commit drops the root row", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
+     "if (valid && d <= k) node = d == 0 ? -1 : nodes[d - 1];"),
+    ("commit writes one row past the path", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
+     "if (valid && d <= k + 1 && d <= D) node = d == 0 ? 0 : nodes[d - 1 < D ? d - 1 : 0];"),
 ]
 
 
@@ -83,6 +90,9 @@ def _pins():
     yield lambda: tm.test_chain_is_lower_triangular(33)
     yield tm.test_golden_cases
     yield lambda: tm.test_masked_tree_attention_equals_per_branch_causal_attention(0)
+    yield lambda: ck.test_committed_rows_equal_sequential_decode_of_the_emitted_prefix(
+        oracle.TREE_SAMPLING, 0)
+    yield ck.test_chain_shaped_tree_commits_in_place_order
 
 
 @pytest.mark.parametrize("name,orig,mutation", MUTANTS, ids=[m[0] for m in MUTANTS])
