@@ -297,6 +297,29 @@ def _tree_modes(args, torch, dev, api, wl):
                      "GB/s_eager": eager / (d.mean() * 1e-3) / 1e9,
                      "frac_eager": eager / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "path_only_bytes": path, "eager_bytes": eager}
+    # committing the accepted paths' KV (the step after verify): 128 KiB per token, the KV
+    # of 32 layers x 8 KV heads x 128 dims x (K, V) in bf16
+    row = 128 * 1024
+    acc, _, nodes, _ = api.spec_verify_tree(copies[0], tok, par, cn, tp, t.D, 1)
+    kv_tree = torch.empty(t.B, t.N, row, dtype=torch.uint8, device=dev).fill_(3)
+    kv_out = torch.empty(t.B, t.D + 1, row, dtype=torch.uint8, device=dev)
+    slots = torch.empty(t.B, t.D + 1, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        api.spec_tree_commit_kv(nodes, acc, kv_tree, kv_out, slots=slots)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(20)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        api.spec_tree_commit_kv(nodes, acc, kv_tree, kv_out, slots=slots)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in ev])
+    moved = int((acc.cpu().numpy() + 1).sum()) * row * 2
+    out["tree_commit_kv"] = {"workload": t.name + ", 128 KiB KV per token",
+                             "avg_ms": float(d.mean()), "bytes_moved": moved,
+                             "GB/s": moved / (d.mean() * 1e-3) / 1e9}
+    del kv_tree, kv_out
     # the tree attention mask and positions of the same trees (the step before verify)
     base = torch.arange(t.B, dtype=torch.int32, device=dev)
     W = (t.N + 31) // 32

@@ -163,6 +163,25 @@ int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
 int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
                    uint32_t* mask, int32_t* positions, void* stream);
 
+/* Commit the accepted path of a token tree (llm-infra-atlas "Speculative Decoding": the
+ * tree chapter covers how a tree's KV is laid out and rolled back after a rejection;
+ * spec_origins, "SpecInfer": one verify forward computes every node of the flattened
+ * tree over a shared KV).  After spec_verify_tree, the KV rows of the root and of the
+ * accepted nodes are gathered, in path order, into a contiguous block; the rows of
+ * rejected branches are dropped.
+ *   accepted_nodes [B][D], accept_len [B]  as written by spec_verify_tree;
+ *   kv_tree  [B][N][row_bytes]  the verify forward's KV, one row per tree node;
+ *   kv_out   [B][D+1][row_bytes] out: row d = kv_tree row of the d-th node of the path
+ *            (row 0 = the root, rows 1..k = the accepted nodes); rows past the path are
+ *            left as they were.  Must not overlap kv_tree;
+ *   slots    [B][D+1] out (may be NULL): the node copied into each row, -1 past the path.
+ * A request with accept_len outside [0, D] or an accepted node outside [0, N) copies
+ * nothing and gets slots -1.  Rows whose size and bases are 16-byte multiples take the
+ * vector path.  No workspace; device pointers; enqueued on `stream`. */
+int spec_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_len, int B, int D,
+                        int N, const void* kv_tree, void* kv_out, size_t row_bytes,
+                        int32_t* slots, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

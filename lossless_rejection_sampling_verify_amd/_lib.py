@@ -57,6 +57,8 @@ def lib():
         L.spec_verify_tree.restype = ip
         L.spec_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp, vp]
         L.spec_tree_mask.restype = ip
+        L.spec_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, sz, vp, vp]
+        L.spec_tree_commit_kv.restype = ip
         _lib = L
     return _lib
 

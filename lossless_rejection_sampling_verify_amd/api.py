@@ -183,3 +183,34 @@ def spec_tree_mask(parents: torch.Tensor, base_pos=None, *, want_positions: bool
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_tree_mask", rc)
     return mask, pos
+
+
+def spec_tree_commit_kv(accepted_nodes: torch.Tensor, accept_len: torch.Tensor,
+                        kv_tree: torch.Tensor, kv_out: torch.Tensor, *, want_slots: bool = True,
+                        stream=None, slots=None):
+    """Commit the accepted tree path.  accepted_nodes [B][D], accept_len [B] int32;
+    kv_tree [B][N][...] and kv_out [B][D+1][...] contiguous, same dtype and row size
+    (kv_out is written in place).  Returns slots [B][D+1] int32 or None."""
+    _check(accepted_nodes, "accepted_nodes", torch.int32, 2)
+    _check(accept_len, "accept_len", torch.int32, 1)
+    if not (kv_tree.is_contiguous() and kv_out.is_contiguous()):
+        raise ValueError("kv_tree and kv_out must be contiguous")
+    if kv_tree.device.type != "cuda" or kv_out.device.type != "cuda":
+        raise ValueError("kv_tree and kv_out must be device tensors")
+    B, D = accepted_nodes.shape
+    if accept_len.shape != (B,) or kv_tree.dim() < 2 or kv_out.dim() < 2 or \
+            kv_tree.shape[0] != B or kv_out.shape[:2] != (B, D + 1) or kv_tree.dtype != kv_out.dtype:
+        raise ValueError("inconsistent shapes")
+    N = kv_tree.shape[1]
+    row_bytes = kv_tree[0, 0].numel() * kv_tree.element_size()
+    if kv_out[0, 0].numel() * kv_out.element_size() != row_bytes:
+        raise ValueError("kv_tree and kv_out rows differ in size")
+    dev = accepted_nodes.device
+    if slots is None and want_slots:
+        slots = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
+    rc = L.lib().spec_tree_commit_kv(_ptr(accepted_nodes), _ptr(accept_len), B, D, N,
+                                     _ptr(kv_tree), _ptr(kv_out), row_bytes, _ptr(slots),
+                                     _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_tree_commit_kv", rc)
+    return slots

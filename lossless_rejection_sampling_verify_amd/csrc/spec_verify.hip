@@ -1242,6 +1242,59 @@ __global__ __launch_bounds__(kBlock) void k_tree_mask(const int32_t* parents,
 }
 
 // ---------------------------------------------------------------------------------------
+// k_commit_kv: commits the accepted path of a token tree -- output row d of a request is
+// the KV row of the d-th node of the path (the root first); one workgroup per (request,
+// output row, chunk of kCommitChunk bytes), so every row is copied by independent,
+// coalesced 16-byte loads and stores.
+
+constexpr int kCommitChunk = 4 * 16 * kBlock;  // 16 KB per workgroup
+
+__global__ __launch_bounds__(kBlock) void k_commit_kv(const int32_t* accepted_nodes,
+                                                      const int32_t* accept_len, int D, int N,
+                                                      const uint8_t* kv_tree, uint8_t* kv_out,
+                                                      size_t row_bytes, int nchunks,
+                                                      int32_t* slots, int vec) {
+    __shared__ int node_sm;
+    const int tid = threadIdx.x;
+    const int blk = blockIdx.x;
+    const int c = blk % nchunks;
+    const int d = (blk / nchunks) % (D + 1);
+    const int b = blk / nchunks / (D + 1);
+    if (tid == 0) {
+        const int32_t* nodes = accepted_nodes + (size_t)b * D;
+        const int k = accept_len[b];
+        bool valid = k >= 0 && k <= D;
+        for (int e = 0; e < k && valid; ++e)
+            if (nodes[e] < 0 || nodes[e] >= N) valid = false;
+        int node = -1;
+        if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];
+        if (slots && c == 0) slots[(size_t)b * (D + 1) + d] = node;
+        node_sm = node;
+    }
+    __syncthreads();
+    const int node = node_sm;
+    if (node < 0) return;
+    const uint8_t* src = kv_tree + ((size_t)b * N + node) * row_bytes;
+    uint8_t* dst = kv_out + ((size_t)b * (D + 1) + d) * row_bytes;
+    const size_t c0 = (size_t)c * kCommitChunk;
+    const size_t c1 = c0 + kCommitChunk < row_bytes ? c0 + kCommitChunk : row_bytes;
+    if (vec) {  // row_bytes and both bases 16-byte aligned
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + c0);
+        u32x4* d4 = reinterpret_cast<u32x4*>(dst + c0);
+        const int nv = (int)((c1 - c0) / 16);
+        u32x4 r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (u * kBlock + tid < nv) r[u] = ld_stream(s4 + u * kBlock + tid);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (u * kBlock + tid < nv) d4[u * kBlock + tid] = r[u];
+    } else {
+        for (size_t e = c0 + tid; e < c1; e += kBlock) dst[e] = src[e];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // host side
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1507,5 +1560,24 @@ extern "C" int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, i
     if (B == 0) return SPEC_OK;
     hipLaunchKernelGGL(k_tree_mask, dim3(B), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
                        parents, base_pos, N, mask, positions);
+    return launch_status();
+}
+
+extern "C" int spec_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_len,
+                                   int B, int D, int N, const void* kv_tree, void* kv_out,
+                                   size_t row_bytes, int32_t* slots, void* stream) {
+    if (!accepted_nodes || !accept_len || !kv_tree || !kv_out) return SPEC_ERR_NULL;
+    if (B < 0 || D < 1 || D > SPEC_MAX_N || N < 1 || N > SPEC_MAX_N || row_bytes < 1)
+        return SPEC_ERR_SHAPE;
+    if (B == 0) return SPEC_OK;
+    const long long nchunks = ((long long)row_bytes + kCommitChunk - 1) / kCommitChunk;
+    const long long grid = (long long)B * (D + 1) * nchunks;
+    if (grid > 0xffffffffLL / kBlock || nchunks > INT_MAX) return SPEC_ERR_SHAPE;
+    const int vec = row_bytes % 16 == 0 && ((uintptr_t)kv_tree) % 16 == 0 &&
+                    ((uintptr_t)kv_out) % 16 == 0;
+    hipLaunchKernelGGL(k_commit_kv, dim3((unsigned)grid), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), accepted_nodes, accept_len, D, N,
+                       static_cast<const uint8_t*>(kv_tree), static_cast<uint8_t*>(kv_out),
+                       row_bytes, (int)nchunks, slots, vec);
     return launch_status();
 }

@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.declared_functions()
     assert set(names) >= {"spec_verify_greedy", "spec_verify_chain", "spec_verify_tree",
-                          "spec_tree_mask", "spec_workspace_bytes", "spec_status_str"}
+                          "spec_tree_mask", "spec_tree_commit_kv", "spec_workspace_bytes",
+                          "spec_status_str"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -131,3 +132,18 @@ def test_tree_mask_rejects_bad_arguments(lib):
     assert lib.spec_tree_mask(P, None, 2, 0, P, P, None) == L.SPEC_ERR_SHAPE
     assert lib.spec_tree_mask(P, None, 2, L.SPEC_MAX_N + 1, P, P, None) == L.SPEC_ERR_SHAPE
     assert lib.spec_tree_mask(P, None, 0, 8, P, None, None) == L.SPEC_OK
+
+
+
+def test_tree_commit_kv_rejects_bad_arguments(lib):
+    f = lib.spec_tree_commit_kv
+    assert f(None, P, 2, 4, 8, P, P, 64, P, None) == L.SPEC_ERR_NULL
+    assert f(P, None, 2, 4, 8, P, P, 64, P, None) == L.SPEC_ERR_NULL
+    assert f(P, P, 2, 4, 8, None, P, 64, P, None) == L.SPEC_ERR_NULL
+    assert f(P, P, 2, 4, 8, P, None, 64, P, None) == L.SPEC_ERR_NULL
+    assert f(P, P, -1, 4, 8, P, P, 64, P, None) == L.SPEC_ERR_SHAPE
+    assert f(P, P, 2, 0, 8, P, P, 64, P, None) == L.SPEC_ERR_SHAPE
+    assert f(P, P, 2, 4, 0, P, P, 64, P, None) == L.SPEC_ERR_SHAPE
+    assert f(P, P, 2, 4, L.SPEC_MAX_N + 1, P, P, 64, P, None) == L.SPEC_ERR_SHAPE
+    assert f(P, P, 2, 4, 8, P, P, 0, P, None) == L.SPEC_ERR_SHAPE
+    assert f(P, P, 0, 4, 8, P, P, 64, None, None) == L.SPEC_OK
