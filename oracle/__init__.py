@@ -51,6 +51,9 @@ def lib():
         L.oracle_tree_mask.restype = ctypes.c_int
         L.oracle_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, ctypes.c_size_t, vp]
         L.oracle_tree_commit_kv.restype = ctypes.c_int
+        L.oracle_verify_chain_filtered.argtypes = [vp, vp, ip, vp, vp, vp, vp, vp, ip, ip, ip,
+                                                   vp, vp, vp, vp]
+        L.oracle_verify_chain_filtered.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,3 +178,27 @@ def tree_commit_kv(accepted_nodes, accept_len, kv_tree, kv_out):
     if rc != 0:
         raise ValueError(f"oracle_tree_commit_kv rejected its arguments ({rc})")
     return slots
+
+
+def verify_chain_filtered(logits, draft_logits, dtype, draft_tokens, coins, temperature,
+                          top_k=None, top_p=None):
+    """Returns dict(accept_len, out_tokens, probs, margin)."""
+    lg = _logits_array(logits, dtype)
+    dl = _logits_array(draft_logits, dtype)
+    dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    cn = np.ascontiguousarray(coins, dtype=np.float32)
+    tp = np.ascontiguousarray(temperature, dtype=np.float32)
+    tk = None if top_k is None else np.ascontiguousarray(top_k, dtype=np.int32)
+    pp = None if top_p is None else np.ascontiguousarray(top_p, dtype=np.float32)
+    B, G = dt.shape
+    V = lg.shape[-1]
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, G + 1), np.int32)
+    probs = np.empty((B, G + 1), np.float64)
+    margin = np.empty(B, np.float64)
+    rc = lib().oracle_verify_chain_filtered(_ptr(lg), _ptr(dl), _dtype_code(dtype), _ptr(dt),
+                                            _ptr(cn), _ptr(tp), _ptr(tk), _ptr(pp), B, G, V,
+                                            _ptr(acc), _ptr(out), _ptr(probs), _ptr(margin))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_chain_filtered rejected its arguments ({rc})")
+    return dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin)

@@ -460,6 +460,176 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
     return 0;
 }
 
+/* ---- chain rejection sampling from logits, with top-k / top-p filtering ------------
+ * [ricardo] mechanism: serving samples with temperature, top-p, top-k and the like, so
+ * "accept if it matches the target's top-1" is not unbiased sampling; correction
+ * sampling keeps the law only when the acceptance test and the residual use the
+ * distributions the drafter and the target actually sample from.
+ * Readings: both rows are filtered the same way before the acceptance rule.
+ *   p = softmax(l / T) from the target logits, q = softmax(d / T) from the draft logits;
+ *   top-k (0 < k < V): keep the tokens whose logit is at least the k-th largest (ties
+ *   kept); top-p (0 < top_p < 1), on the top-k-filtered row: sorted by probability, the
+ *   shortest head whose mass reaches top_p of the kept mass ends at probability tau;
+ *   keep every token with probability >= tau (ties kept); then renormalise.
+ * The acceptance rule, the residual and the bonus then run on the filtered rows exactly
+ * as in the unfiltered chain.  The top-p boundary (the kept-mass fraction before and
+ * after the threshold group, against top_p) is recorded as a margin. */
+static int cmp_desc(const void* a, const void* b) {
+    double x = *(const double*)a, y = *(const double*)b;
+    return x < y ? 1 : (x > y ? -1 : 0);
+}
+
+/* w[x] = exp((l_x - m) / T) for the kept tokens, 0 for the others; returns the kept
+ * mass.  tmp has room for V doubles. */
+static double filter_row(Row r, double m, double T, int top_k, double top_p, double* w,
+                         double* tmp, double* margin) {
+    int V = r.V;
+    for (int x = 0; x < V; ++x) w[x] = exp((logit(r, x) - m) / T);
+    if (top_k > 0 && top_k < V) {
+        for (int x = 0; x < V; ++x) tmp[x] = logit(r, x);
+        qsort(tmp, (size_t)V, sizeof(double), cmp_desc);
+        double th = tmp[top_k - 1];
+        for (int x = 0; x < V; ++x)
+            if (logit(r, x) < th) w[x] = 0.0;
+    }
+    double S = 0.0;
+    for (int x = 0; x < V; ++x) S += w[x];
+    if (top_p < 1.0) {
+        for (int x = 0; x < V; ++x) tmp[x] = w[x];
+        qsort(tmp, (size_t)V, sizeof(double), cmp_desc);
+        double target = top_p * S, cum = 0.0, tau = tmp[0];
+        for (int i = 0; i < V; ++i) {
+            if (cum + tmp[i] >= target) {
+                tau = tmp[i];
+                break;
+            }
+            cum += tmp[i];
+        }
+        double before = 0.0, through = 0.0;
+        for (int i = 0; i < V; ++i) {
+            if (tmp[i] > tau) before += tmp[i];
+            if (tmp[i] >= tau) through += tmp[i];
+        }
+        note_margin(margin, (target - before) / S);
+        note_margin(margin, (through - target) / S);
+        for (int x = 0; x < V; ++x)
+            if (w[x] < tau) w[x] = 0.0;
+        S = through;
+    }
+    return S;
+}
+
+static void chain_filtered_one(const void* logits, const void* dlogits, int dtype,
+                               const int32_t* draft, const float* coins, float temperature,
+                               int top_k, float top_p, int G, int V, size_t b,
+                               int32_t* accept_len, int32_t* out, double* probs,
+                               double* margin, double* wp, double* wq, double* tmp) {
+    int R = G + 1;
+    double T = (double)temperature;
+    double tp = (double)top_p;
+    int valid = temperature_ok(temperature) && top_p > 0.0f && !isnan(top_p);
+    for (int i = 0; i < G; ++i)
+        if (draft[i] < 0 || draft[i] >= V) valid = 0;
+    for (int i = 0; i < R; ++i)
+        if (!coin_ok(coins[i])) valid = 0;
+    double m[R > 0 ? R : 1], mq[R > 0 ? R : 1];
+    for (int i = 0; i < R && valid; ++i) {
+        m[i] = row_max(row_of(logits, dtype, b * (size_t)R + (size_t)i, V));
+        if (m[i] == -INFINITY) valid = 0;
+    }
+    for (int i = 0; i < G && valid; ++i) {
+        mq[i] = row_max(row_of(dlogits, dtype, b * (size_t)G + (size_t)i, V));
+        if (mq[i] == -INFINITY) valid = 0;
+    }
+    *margin = INFINITY;
+    if (!valid) {
+        *accept_len = -1;
+        for (int i = 0; i < R; ++i) out[i] = -1;
+        if (probs)
+            for (int i = 0; i < R; ++i) probs[i] = 0.0;
+        return;
+    }
+    int k = G;
+    double pacc[R > 0 ? R : 1];
+    for (int i = 0; i < G; ++i) {
+        Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
+        Row rq = row_of(dlogits, dtype, b * (size_t)G + (size_t)i, V);
+        double Zp = filter_row(r, m[i], T, top_k, tp, wp, tmp, margin);
+        double Zq = filter_row(rq, mq[i], T, top_k, tp, wq, tmp, margin);
+        int x = draft[i];
+        double p = wp[x] / Zp, qx = wq[x] / Zq;
+        double u = (double)coins[i];
+        int accept;
+        if (qx > 0.0) {
+            double ratio = p / qx;
+            note_margin(margin, fabs(u - ratio));
+            accept = p > 0.0 && u <= ratio;
+        } else {
+            accept = p > 0.0;
+        }
+        if (!accept) {
+            k = i;
+            break;
+        }
+        pacc[i] = p;
+    }
+    Row rk = row_of(logits, dtype, b * (size_t)R + (size_t)k, V);
+    double Zp = filter_row(rk, m[k], T, top_k, tp, wp, tmp, margin);
+    for (int x = 0; x < V; ++x) wp[x] /= Zp;
+    double S = 0.0;
+    if (k < G) {
+        Row rq = row_of(dlogits, dtype, b * (size_t)G + (size_t)k, V);
+        double Zq = filter_row(rq, mq[k], T, top_k, tp, wq, tmp, margin);
+        for (int x = 0; x < V; ++x) {
+            double d = wp[x] - wq[x] / Zq;
+            wq[x] = d > 0.0 ? d : 0.0;
+            S += wq[x];
+        }
+        note_margin(margin, S);
+    }
+    double* w = (k < G && S > 0.0) ? wq : wp;
+    int y = draw_inverse_cdf(w, V, (double)coins[G], margin);
+    for (int i = 0; i < k; ++i) out[i] = draft[i];
+    out[k] = y;
+    for (int i = k + 1; i < R; ++i) out[i] = -1;
+    *accept_len = k;
+    if (probs) {
+        for (int i = 0; i < k; ++i) probs[i] = pacc[i];
+        probs[k] = wp[y];
+        for (int i = k + 1; i < R; ++i) probs[i] = 0.0;
+    }
+}
+
+int oracle_verify_chain_filtered(const void* logits, const void* draft_logits, int dtype,
+                                 const int32_t* draft_tokens, const float* coins,
+                                 const float* temperature, const int32_t* top_k,
+                                 const float* top_p, int B, int G, int V, int32_t* accept_len,
+                                 int32_t* out_tokens, double* probs_out, double* min_margin) {
+    if (!logits || !draft_logits || !draft_tokens || !coins || !temperature || !accept_len ||
+        !out_tokens || !min_margin)
+        return -1;
+    if (B < 0 || G < 1 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    int R = G + 1;
+#pragma omp parallel
+    {
+        double* wp = (double*)malloc(sizeof(double) * (size_t)V);
+        double* wq = (double*)malloc(sizeof(double) * (size_t)V);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; ++b)
+            chain_filtered_one(logits, draft_logits, dtype, draft_tokens + (size_t)b * G,
+                               coins + (size_t)b * R, temperature[b], top_k ? top_k[b] : 0,
+                               top_p ? top_p[b] : 1.0f, G, V, (size_t)b, accept_len + b,
+                               out_tokens + (size_t)b * R,
+                               probs_out ? probs_out + (size_t)b * R : NULL, min_margin + b, wp,
+                               wq, tmp);
+        free(wp);
+        free(wq);
+        free(tmp);
+    }
+    return 0;
+}
+
 /* ---- tree attention mask and positions ---------------------------------------------
  * [origins] SpecInfer, tree attention mask: the token tree is flattened into one sequence
  * and every node attends only to its ancestors, so one target forward scores every

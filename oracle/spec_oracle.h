@@ -57,6 +57,17 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
                        float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
                        int32_t* accepted_nodes, double* probs_out, double* min_margin);
 
+/* Chain rejection sampling from target logits [B][G+1][V] and draft logits [B][G][V]
+ * (same dtype), both at temperature T and both filtered with top_k[b] (NULL or <= 0 or
+ * >= V: off; ties at the k-th largest logit kept) and then top_p[b] (NULL or >= 1: off;
+ * must be > 0; every token at least as probable as the end of the shortest head
+ * reaching top_p of the mass is kept).  Outputs as oracle_verify_chain. */
+int oracle_verify_chain_filtered(const void* logits, const void* draft_logits, int dtype,
+                                 const int32_t* draft_tokens, const float* coins,
+                                 const float* temperature, const int32_t* top_k,
+                                 const float* top_p, int B, int G, int V, int32_t* accept_len,
+                                 int32_t* out_tokens, double* probs_out, double* min_margin);
+
 /* Tree attention mask: mask_bits [B][N][W], W = ceil(N/32); bit (j % 32) of word j / 32 of
  * row i is set iff node j lies on the path from node i to the root (i included).
  * positions [B][N] (may be NULL) = base_pos[b] (0 when base_pos is NULL) + depth(i).

@@ -64,7 +64,22 @@ def segments(eval_many, n: int = LATTICE, fan: int = 256):
 # ---------------------------------------------------------------------------------------
 # chain: one request, fixed rows
 
-def chain_outcomes(logits, dtype, q, x, T, coin_sets):
+def _run_chain(lg, dtype, qq, xx, coin_sets, Ts):
+    return oracle.verify_chain(lg, dtype, qq, xx, coin_sets, Ts)
+
+
+def filtered_runner(top_k, top_p):
+    """Runner for chain_outcomes / chain_round_law: q holds draft logits, and both rows
+    are filtered with top_k / top_p by the oracle."""
+    def run(lg, dtype, dl, xx, coin_sets, Ts):
+        B = len(Ts)
+        return oracle.verify_chain_filtered(lg, dl, dtype, xx, coin_sets, Ts,
+                                            np.full(B, top_k, np.int32),
+                                            np.full(B, top_p, np.float32))
+    return run
+
+
+def chain_outcomes(logits, dtype, q, x, T, coin_sets, runner=_run_chain):
     """Run the oracle on one request under many coin vectors; returns tuples
     (accept_len, emitted tokens...)."""
     coin_sets = np.asarray(coin_sets, dtype=np.float32)
@@ -73,9 +88,8 @@ def chain_outcomes(logits, dtype, q, x, T, coin_sets):
     lg = np.broadcast_to(logits, (B,) + logits.shape)
     qq = np.broadcast_to(q, (B,) + q.shape)
     xx = np.broadcast_to(np.asarray(x, np.int32), (B, G))
-    res = oracle.verify_chain(np.ascontiguousarray(lg), dtype, np.ascontiguousarray(qq),
-                              np.ascontiguousarray(xx), coin_sets,
-                              np.full(B, T, np.float32))
+    res = runner(np.ascontiguousarray(lg), dtype, np.ascontiguousarray(qq),
+                 np.ascontiguousarray(xx), coin_sets, np.full(B, T, np.float32))
     out = []
     for b in range(B):
         k = int(res["accept_len"][b])
@@ -83,7 +97,7 @@ def chain_outcomes(logits, dtype, q, x, T, coin_sets):
     return out
 
 
-def chain_round_law(logits, dtype, q, x, T):
+def chain_round_law(logits, dtype, q, x, T, runner=_run_chain):
     """Exact law of one chain verify with drafts x fixed, over lattice coins.
 
     Returns {(accept_len, tok_0, ..., tok_k): probability}.
@@ -101,7 +115,7 @@ def chain_round_law(logits, dtype, q, x, T):
             def f(ks, i=i):
                 cs = np.repeat(prefix_coins[None, :], len(ks), axis=0)
                 cs[:, i] = coin(ks)
-                return [o[0] > i for o in chain_outcomes(logits, dtype, q, x, T, cs)]
+                return [o[0] > i for o in chain_outcomes(logits, dtype, q, x, T, cs, runner)]
             segs = segments(f)
             acc_pts = sum(e - s for s, e, v in segs if v)
             rej_start = next((s for s, e, v in segs if not v), None)
@@ -118,7 +132,7 @@ def chain_round_law(logits, dtype, q, x, T):
             def g(ks):
                 cs = np.repeat(stop_coins[None, :], len(ks), axis=0)
                 cs[:, G] = coin(ks)
-                return chain_outcomes(logits, dtype, q, x, T, cs)
+                return chain_outcomes(logits, dtype, q, x, T, cs, runner)
             for s, e, v in segments(g):
                 law[v] = law.get(v, 0.0) + stop_mass * (e - s) / LATTICE
         mass *= p_acc

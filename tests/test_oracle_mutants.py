@@ -2,7 +2,7 @@
 
 Each mutant is a copy of the oracle source with one plausible slip planted in it (a
 transposed operand, a wrong sign, a dropped term, an off-by-one row, a reused coin,
-...).  It is compiled into a temporary directory and swapped in for the real library;
+...), at every place the statement occurs.  It is compiled into a temporary directory and swapped in for the real library;
 at least one pin from the law, closed-form, special-case or golden tests must then fail.
 The real oracle is restored afterwards.
 """
@@ -20,6 +20,7 @@ import test_oracle_law as law
 import test_oracle_tree_greedy as tg
 import test_oracle_tree_mask as tm
 import test_oracle_commit_kv as ck
+import test_oracle_filtered as tf
 
 SRC = open(oracle.SRC).read()
 
@@ -61,6 +62,16 @@ MUTANTS = [
      "for (int j = i; j > 0; j = par[j]) {"),
     ("commit takes the node of the same index", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
      "if (valid && d <= k) node = d == 0 ? 0 : nodes[d < k ? d : d - 1];"),
+    ("top-k keeps one token too many", "double th = tmp[top_k - 1];",
+     "double th = tmp[top_k < V - 1 ? top_k : top_k - 1];"),
+    ("draft row left unfiltered",
+     "double Zq = filter_row(rq, mq[i], T, top_k, tp, wq, tmp, margin);",
+     "double Zq = filter_row(rq, mq[i], T, 0, 1.0, wq, tmp, margin);"),
+    ("target filter skipped in the acceptance test",
+     "double Zp = filter_row(r, m[i], T, top_k, tp, wp, tmp, margin);",
+     "double Zp = filter_row(r, m[i], T, 0, 1.0, wp, tmp, margin);"),
+    ("top-p threshold one token late", "                tau = tmp[i];\n                break;",
+     "                tau = tmp[i + 1 < V ? i + 1 : i];\n                break;"),
     ("commit drops the root row", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
      "if (valid && d <= k) node = d == 0 ? -1 : nodes[d - 1];"),
     ("commit writes one row past the path", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
@@ -93,11 +104,15 @@ def _pins():
     yield lambda: ck.test_committed_rows_equal_sequential_decode_of_the_emitted_prefix(
         oracle.TREE_SAMPLING, 0)
     yield ck.test_chain_shaped_tree_commits_in_place_order
+    yield tf.test_top1_is_greedy_verify
+    for case in tf.GOLDEN["cases"]:
+        yield lambda case=case: tf.test_golden(case)
+    yield lambda: tf.test_filtered_round_emits_filtered_target_law(2, 4, 0.8, 0.7)
 
 
 @pytest.mark.parametrize("name,orig,mutation", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(name, orig, mutation, tmp_path):
-    assert SRC.count(orig) == 1, f"mutation anchor not unique/found: {orig}"
+    assert SRC.count(orig) >= 1, f"mutation anchor not found: {orig}"
     src = tmp_path / "spec_oracle.c"
     src.write_text(SRC.replace(orig, mutation))
     hdr = os.path.join(os.path.dirname(oracle.SRC), "spec_oracle.h")
