@@ -75,7 +75,7 @@ enum {
 
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };                   /* target-logit dtype */
 enum { SPEC_TREE_GREEDY = 0, SPEC_TREE_SAMPLING = 1 };  /* spec_verify_tree mode */
-enum { SPEC_OP_GREEDY = 0, SPEC_OP_CHAIN = 1, SPEC_OP_TREE = 2 };
+enum { SPEC_OP_GREEDY = 0, SPEC_OP_CHAIN = 1, SPEC_OP_TREE = 2, SPEC_OP_CHAIN_FILTERED = 3 };
 
 #define SPEC_MAX_G 64     /* drafted positions per request (chain) */
 #define SPEC_MAX_N 1024   /* tree nodes per request, root included */
@@ -117,6 +117,32 @@ int spec_verify_chain(const void* logits, int dtype, const float* draft_probs,
                       const float* temperature, int B, int G, int V, int32_t* accept_len,
                       int32_t* out_tokens, float* probs_out, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* Chain rejection sampling from draft logits, with top-k / top-p filtering
+ * (ricardokevins, "mechanism": serving samples with temperature, top-p and top-k;
+ * "correction sampling", Eq. a(x) and Eq. r(x): acceptance and residual keep the
+ * target's law only on the distributions actually sampled from).
+ *   logits       [B][G+1][V] target logits;
+ *   draft_logits [B][G][V]   draft logits, same dtype (q_i = softmax(draft_logits / T));
+ *   draft_tokens, coins, temperature as spec_verify_chain;
+ *   top_k [B] (NULL: off)    keep the tokens whose logit is at least the k-th largest
+ *                            (ties kept); k <= 0 or k >= V: off;
+ *   top_p [B] (NULL: off)    on the top-k-filtered row, keep every token at least as
+ *                            probable as the last token of the shortest head (in
+ *                            decreasing probability) whose mass reaches top_p of the
+ *                            row's mass (ties kept); top_p >= 1: off; top_p <= 0 or NaN
+ *                            makes the request invalid.
+ * Target and draft rows are filtered alike and renormalised; then the acceptance rule,
+ * the residual and the bonus run as in spec_verify_chain on the filtered rows.  The
+ * filtered masses are summed in fixed point, so the kept sets are deterministic.
+ * Workspace: spec_workspace_bytes(SPEC_OP_CHAIN_FILTERED, B, G+1, V).  Outputs and
+ * probs_out as spec_verify_chain (probabilities under the filtered target rows). */
+int spec_verify_chain_filtered(const void* logits, const void* draft_logits, int dtype,
+                               const int32_t* draft_tokens, const float* coins,
+                               const float* temperature, const int32_t* top_k,
+                               const float* top_p, int B, int G, int V, int32_t* accept_len,
+                               int32_t* out_tokens, float* probs_out, void* workspace,
+                               size_t ws_bytes, void* stream);
 
 /* Token-tree verify (spec_origins, "SpecInfer" and "in SGLang").
  *   logits      [B][N][V] row j = target logits of the token after node j (node 0 is the

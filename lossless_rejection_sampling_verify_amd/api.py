@@ -120,6 +120,48 @@ def spec_verify_chain(logits: torch.Tensor, draft_probs: torch.Tensor, draft_tok
     return acc, toks, probs
 
 
+def spec_verify_chain_filtered(logits: torch.Tensor, draft_logits: torch.Tensor,
+                               draft_tokens: torch.Tensor, coins: torch.Tensor,
+                               temperature: torch.Tensor, top_k=None, top_p=None, *,
+                               want_probs: bool = False, ws=None, stream=None, out=None):
+    """Chain rejection sampling from draft logits with top-k / top-p filtering.
+    logits [B][G+1][V] and draft_logits [B][G][V] (same dtype, fp32 or bf16),
+    draft_tokens [B][G] int32, coins [B][G+1] fp32, temperature [B] fp32,
+    top_k [B] int32 or None, top_p [B] fp32 or None.
+
+    Returns (accept_len [B], out_tokens [B][G+1], probs [B][G+1] or None)."""
+    _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
+    _check(draft_logits, "draft_logits", logits.dtype, 3)
+    _check(draft_tokens, "draft_tokens", torch.int32, 2)
+    _check(coins, "coins", torch.float32, 2)
+    _check(temperature, "temperature", torch.float32, 1)
+    B, R, V = logits.shape
+    G = R - 1
+    if draft_logits.shape != (B, G, V) or draft_tokens.shape != (B, G) or \
+            coins.shape != (B, R) or temperature.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    if top_k is not None:
+        _check(top_k, "top_k", torch.int32, 1)
+    if top_p is not None:
+        _check(top_p, "top_p", torch.float32, 1)
+    dev = logits.device
+    ws = workspace(L.SPEC_OP_CHAIN_FILTERED, B, R, V, dev) if ws is None else ws
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, R, dtype=torch.int32, device=dev)
+        probs = torch.empty(B, R, dtype=torch.float32, device=dev) if want_probs else None
+    else:
+        acc, toks, probs = out
+    rc = L.lib().spec_verify_chain_filtered(_ptr(logits), _ptr(draft_logits), _logit_dtype(logits),
+                                            _ptr(draft_tokens), _ptr(coins), _ptr(temperature),
+                                            _ptr(top_k), _ptr(top_p), B, G, V, _ptr(acc),
+                                            _ptr(toks), _ptr(probs), _ptr(ws), ws.numel(),
+                                            _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_verify_chain_filtered", rc)
+    return acc, toks, probs
+
+
 def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
                      coins, temperature, D: int, mode: int, threshold_single: float = 1.0,
                      threshold_acc: float = 1.0, *, want_probs: bool = False, ws=None,

@@ -72,8 +72,19 @@ struct alignas(16) DrawState {
     int nexcl;   // tree: distinct tokens of the children tried last, in excl[b][...]
     float M;     // row max
     float invZ;  // 1 / Z rounded to fp32 (weights)
-    double Z;    // sum exp((l - M) / T) over the row
+    double Z;    // sum exp((l - M) / T) over the (kept part of the) row
     double T;    // temperature
+    uint32_t thp;  // filtered calls: target tokens whose order key is below thp weigh 0
+    uint32_t thq;  // filtered residual: the same for the draft row qrow of draft_logits
+    float Mq;      // filtered residual: draft row max
+    float invZq;   // filtered residual: 1 / kept draft mass
+};
+
+// Top-k / top-p result of one logit row (filtered calls).
+struct alignas(16) FiltRow {
+    float M;       // row max (-inf: the row has no finite logit)
+    uint32_t th;   // tokens whose order key is below th are removed (0: none)
+    double Z;      // kept mass: sum of exp((l - M) / T) over the kept tokens
 };
 
 struct KArgs {
@@ -96,6 +107,11 @@ struct KArgs {
     double* massfb;      // [B][S2] fallback weight (the plain target row)
     double* seg;         // [B][S2][kSegs] draw weight of each segment
     int32_t* excl;       // [B][SPEC_MAX_N] tree: excluded tokens of the final draw
+    const void* dlogits; // filtered calls: draft logits [B][G][V]
+    const int32_t* top_k;
+    const float* top_p;
+    FiltRow* frows;      // filtered calls: [B*R] target rows, then [B*G] draft rows
+    int fixbits;         // fixed-point fraction bits of the filter's mass histograms
 };
 
 // ---------------------------------------------------------------------------------------
@@ -857,6 +873,10 @@ __device__ inline DrawState load_state(const DrawState* p) {
     st.invZ = p->invZ;
     st.Z = p->Z;
     st.T = p->T;
+    st.thp = p->thp;
+    st.thq = p->thq;
+    st.Mq = p->Mq;
+    st.invZq = p->invZq;
     return st;
 }
 
@@ -872,55 +892,112 @@ __device__ inline DrawState load_state(const DrawState* p) {
 // Fallback when the total weight is not positive: w_j = p_j (the plain target row).
 // Segment and chunk sums are fp64 sums of fp32 sums of four weights.
 
-template <typename T, bool kResidual>
-__device__ inline float draw_weight(const T* row, const float* q, int j, float M, float s2,
-                                    float invZ, float& p) {
-    p = ex2((Ld<T>::one(row + j) - M) * s2) * invZ;
-    return kResidual ? fmaxf(p - q[j], 0.f) : p;
+// Order-preserving integer key of a float: a < b iff key(a) < key(b) (NaN aside).  A bf16
+// value widened to fp32 has the same order through its top 16 key bits.
+__device__ inline uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Weights of four consecutive elements: `pw` gets the sum of the plain p_j, `ww` the sum
-// of the draw weights.
-template <typename T, bool kResidual>
-__device__ inline void weigh4(const typename Quad<T>::Raw& lr, const u32x4& qr, float M,
-                              float s2, float invZ, float& pw, float& ww) {
+// Parameters of the draw weights of one request.
+struct WParams {
+    float M, s2, invZ;  // target row
+    uint32_t thp;       // filtered: target tokens with a key below thp weigh 0
+    float Mq, invZq;    // draft logits row (kQ == 2)
+    uint32_t thq;
+};
+
+// kQ: 0 = no draft row (target weights), 1 = draft probabilities (fp32), 2 = draft logits
+// (same dtype as the target, filtered by thq).  kFilt: the target row is filtered by thp.
+template <typename T, int kQ>
+struct QRow {
+    typedef u32x4 Raw;  // four fp32 probabilities (or unused)
+};
+template <typename T>
+struct QRow<T, 2> {
+    typedef typename Quad<T>::Raw Raw;
+};
+
+template <typename T, int kQ, bool kFilt>
+__device__ inline float draw_weight(const T* row, const void* q, int j, const WParams& W,
+                                    float& p) {
+    const float l = Ld<T>::one(row + j);
+    p = ex2((l - W.M) * W.s2) * W.invZ;
+    if (kFilt && order_key(l) < W.thp) p = 0.f;
+    if (kQ == 0) return p;
+    float qv;
+    if (kQ == 1) {
+        qv = static_cast<const float*>(q)[j];
+    } else {
+        const float d = Ld<T>::one(static_cast<const T*>(q) + j);
+        qv = ex2((d - W.Mq) * W.s2) * W.invZq;
+        if (order_key(d) < W.thq) qv = 0.f;
+    }
+    return fmaxf(p - qv, 0.f);
+}
+
+// Weights of four consecutive elements: `pw` gets the sum of the plain (filtered) p_j,
+// `ww` the sum of the draw weights.
+template <typename T, int kQ, bool kFilt>
+__device__ inline void weigh4(const typename Quad<T>::Raw& lr, const typename QRow<T, kQ>::Raw& qr,
+                              const WParams& W, float& pw, float& ww) {
     float l[4];
     Quad<T>::unpack(lr, l);
-    const float qv[4] = {__uint_as_float(qr.x), __uint_as_float(qr.y), __uint_as_float(qr.z),
-                         __uint_as_float(qr.w)};
+    float qv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (kQ == 1) {
+        const u32x4& r = reinterpret_cast<const u32x4&>(qr);
+        qv[0] = __uint_as_float(r.x);
+        qv[1] = __uint_as_float(r.y);
+        qv[2] = __uint_as_float(r.z);
+        qv[3] = __uint_as_float(r.w);
+    } else if (kQ == 2) {
+        float d[4];
+        Quad<T>::unpack(reinterpret_cast<const typename Quad<T>::Raw&>(qr), d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qv[e] = ex2((d[e] - W.Mq) * W.s2) * W.invZq;
+            if (order_key(d[e]) < W.thq) qv[e] = 0.f;
+        }
+    }
     float ps = 0.f, ws = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float p = ex2((l[e] - M) * s2) * invZ;
+        float p = ex2((l[e] - W.M) * W.s2) * W.invZ;
+        if (kFilt && order_key(l[e]) < W.thp) p = 0.f;
         ps += p;
-        if (kResidual) ws += fmaxf(p - qv[e], 0.f);
+        if (kQ != 0) ws += fmaxf(p - qv[e], 0.f);
     }
     pw = ps;
-    ww = kResidual ? ws : ps;
+    ww = kQ != 0 ? ws : ps;
+}
+
+template <typename V>
+__device__ inline V ld_stream_any(const V* p) {
+    return __builtin_nontemporal_load(p);
 }
 
 // Lane t of the block takes elements 4t..4t+3 of each 1024-element quarter u of the chunk
 // and leaves their weight sums in entry u * kBlock + t of `pw` / `ww` (LDS): segment g is
 // then entries 16g .. 16g + 15.
-template <typename T, bool kResidual>
-__device__ inline void chunk_weights(const T* rowp, const float* qrow, int n, bool fast, float M,
-                                     float s2, float invZ, float* pw, float* ww) {
+template <typename T, int kQ, bool kFilt>
+__device__ inline void chunk_weights(const T* rowp, const void* qrow, int n, bool fast,
+                                     const WParams& W, float* pw, float* ww) {
     const int tid = threadIdx.x;
+    typedef typename QRow<T, kQ>::Raw QR;
     if (fast) {  // full, 16-byte aligned chunk: every load in flight at once
         const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
-        const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
-        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const QR* qq = static_cast<const QR*>(qrow);
         typename Quad<T>::Raw lr[4];
-        u32x4 qr[4];
+        QR qr[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             lr[u] = lq[u * kBlock + tid].raw;
-            qr[u] = kResidual ? ld_stream(qq + u * kBlock + tid) : zero;
+            if (kQ != 0) qr[u] = ld_stream_any(qq + u * kBlock + tid);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             float p4, w4;
-            weigh4<T, kResidual>(lr[u], qr[u], M, s2, invZ, p4, w4);
+            weigh4<T, kQ, kFilt>(lr[u], qr[u], W, p4, w4);
             pw[u * kBlock + tid] = p4;
             ww[u * kBlock + tid] = w4;
         }
@@ -932,13 +1009,13 @@ __device__ inline void chunk_weights(const T* rowp, const float* qrow, int n, bo
             const int e = u * 4 * kBlock + 4 * tid + i;
             if (e < n) {
                 float p;
-                const float w = draw_weight<T, kResidual>(rowp, qrow, e, M, s2, invZ, p);
+                const float w = draw_weight<T, kQ, kFilt>(rowp, qrow, e, W, p);
                 p4 += p;
                 w4 += w;
             }
         }
         pw[u * kBlock + tid] = p4;
-        ww[u * kBlock + tid] = kResidual ? w4 : p4;
+        ww[u * kBlock + tid] = kQ != 0 ? w4 : p4;
     }
 }
 
@@ -957,8 +1034,26 @@ struct MassSmem {
     double xs[kSegs];      // excluded weight of each segment
 };
 
+// The draw weights' parameters and draft row of a request's draw state.
+template <typename T, bool kFilt>
+__device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const void*& qrow) {
+    WParams W;
+    W.M = st.M;
+    W.s2 = kLog2e / (float)st.T;
+    W.invZ = st.invZ;
+    W.thp = kFilt ? st.thp : 0u;
+    W.Mq = st.Mq;
+    W.invZq = st.invZq;
+    W.thq = st.thq;
+    qrow = nullptr;
+    if (st.kind == kDrawResidual)
+        qrow = kFilt ? static_cast<const void*>(static_cast<const T*>(a.dlogits) + (size_t)st.qrow * a.V)
+                     : static_cast<const void*>(a.q + (size_t)st.qrow * a.V);
+    return W;
+}
+
 // One workgroup per (request, fine chunk).
-template <typename T>
+template <typename T, bool kFilt>
 __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
     __shared__ MassSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -968,16 +1063,19 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
     const DrawState st = a.dstate[b];
     if (st.kind == kDrawNone) return;
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
-    const float* qrow = st.kind == kDrawResidual ? a.q + (size_t)st.qrow * V : nullptr;
-    const float s2 = kLog2e / (float)st.T;
+    const void* qrow;
+    const WParams W = draw_params<T, kFilt>(a, st, qrow);
     const int c0 = c * kFine;
     const int n = min(kFine, V - c0);
+    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
     const bool fast = n == kFine && ((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0 &&
-                      (!qrow || ((uintptr_t)(qrow + c0)) % 16 == 0);
+                      (!qrow || ((uintptr_t)qrow + c0 * qes) % (4 * qes) == 0);
+    constexpr int kQr = kFilt ? 2 : 1;
     if (qrow)
-        chunk_weights<T, true>(rowp + c0, qrow + c0, n, fast, st.M, s2, st.invZ, sm.pw, sm.ww);
+        chunk_weights<T, kQr, kFilt>(rowp + c0, static_cast<const char*>(qrow) + c0 * qes, n, fast,
+                                     W, sm.pw, sm.ww);
     else
-        chunk_weights<T, false>(rowp + c0, nullptr, n, fast, st.M, s2, st.invZ, sm.pw, sm.ww);
+        chunk_weights<T, 0, kFilt>(rowp + c0, nullptr, n, fast, W, sm.pw, sm.ww);
     if (tid < kSegs) sm.xs[tid] = 0.0;
     __syncthreads();
     if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
@@ -987,7 +1085,7 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
                 const int t = ex[e];
                 if (t >= c0 && t < c0 + n) {
                     float p;
-                    draw_weight<T, false>(rowp, nullptr, t, st.M, s2, st.invZ, p);
+                    draw_weight<T, 0, kFilt>(rowp, nullptr, t, W, p);
                     sm.xs[(t - c0) / kSeg] += (double)p;
                 }
             }
@@ -995,21 +1093,21 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
         __syncthreads();
     }
     if (tid < kSegs) {  // wave 0: lane g sums segment g in ascending order
-        double W = 0.0, P = 0.0;
+        double Wt = 0.0, P = 0.0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            W += (double)sm.ww[16 * tid + i];
+            Wt += (double)sm.ww[16 * tid + i];
             P += (double)sm.pw[16 * tid + i];
         }
         if (sm.xs[tid] > 0.0) {
-            const double rem = W - sm.xs[tid];
-            W = rem > W * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
+            const double rem = Wt - sm.xs[tid];
+            Wt = rem > Wt * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
         }
-        a.seg[((size_t)b * S2 + c) * kSegs + tid] = W;
-        W = wave_sum(W);
+        a.seg[((size_t)b * S2 + c) * kSegs + tid] = Wt;
+        Wt = wave_sum(Wt);
         P = wave_sum(P);
         if (lane == 0) {
-            a.mass[(size_t)b * S2 + c] = W;
+            a.mass[(size_t)b * S2 + c] = Wt;
             a.massfb[(size_t)b * S2 + c] = P;
         }
     }
@@ -1073,7 +1171,7 @@ __device__ __attribute__((always_inline)) int wave_locate(const double* w, int n
 }
 
 // One wave per request: chunk, then segment, then token.
-template <typename T>
+template <typename T, bool kFilt>
 __global__ __launch_bounds__(64) void k_draw(KArgs a) {
     const int lane = threadIdx.x;
     const int S2 = a.S2, V = a.V;
@@ -1081,7 +1179,8 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
     const DrawState st = load_state(a.dstate + b);
     if (st.kind == kDrawNone) return;
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
-    const float s2 = kLog2e / (float)st.T;
+    const void* qrow;
+    const WParams W = draw_params<T, kFilt>(a, st, qrow);
     const double u = (double)a.coins[st.coin];
     double tot = 0.0;
     for (int i0 = 0; i0 < S2; i0 += 64)
@@ -1092,8 +1191,7 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
         for (int i0 = 0; i0 < S2; i0 += 64)
             tot += wave_sum(i0 + lane < S2 ? a.massfb[(size_t)b * S2 + i0 + lane] : 0.0);
     }
-    const bool resid = st.kind == kDrawResidual && !fallback;
-    const float* qrow = resid ? a.q + (size_t)st.qrow * V : nullptr;
+    const bool resid = qrow != nullptr && !fallback;
     int y = -1;
     float ly = 0.f;
     const double t = u * tot;
@@ -1113,7 +1211,7 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
                 for (int g = 0; g < 8; ++g) {
                     const int j = c * kFine + (g0 + g) * kSeg + lane;
                     float p = 0.f;
-                    if (j < V) draw_weight<T, false>(rowp, nullptr, j, st.M, s2, st.invZ, p);
+                    if (j < V) draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
                     pv[g] = p;
                 }
 #pragma unroll
@@ -1133,8 +1231,9 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
             if (j < V) {
                 l = Ld<T>::one(rowp + j);
                 float p;
-                w = resid ? draw_weight<T, true>(rowp, qrow, j, st.M, s2, st.invZ, p)
-                          : draw_weight<T, false>(rowp, nullptr, j, st.M, s2, st.invZ, p);
+                constexpr int kQr = kFilt ? 2 : 1;
+                w = resid ? draw_weight<T, kQr, kFilt>(rowp, qrow, j, W, p)
+                          : draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
                 if (!fallback && st.nexcl > 0) {
                     const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
                     for (int e = 0; e < st.nexcl; ++e)
@@ -1153,6 +1252,365 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
         a.out_tokens[st.out] = y;
         if (a.probs)
             a.probs[st.out] = y >= 0 ? (float)(exp(((double)ly - (double)st.M) / st.T) / st.Z) : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// k_filter_rows: one workgroup per logit row of a filtered chain call (every target row,
+// then every draft row) -- the row max and normaliser at the request's temperature, then
+// the top-k and top-p thresholds by radix selection over order-preserving keys
+//
+// Each selection walks the key from its top digit down: a histogram pass counts and
+// weighs (fixed point, so sums are exact and independent of order) the tokens that
+// agree with the digits chosen so far, and the walk takes the digit where the count
+// (top-k) or mass (top-p) accumulated from the largest keys reaches what is needed.
+// bf16 keys have 16 significant bits (two 8-bit digits); fp32 keys take 11 + 11 + 10.
+
+constexpr int kHistBins = 2048;
+
+struct FilterSmem {
+    RowSmem rs;
+    uint32_t cnt[kHistBins];
+    unsigned long long mass[kHistBins];
+    unsigned long long wtot[3][kWaves];
+    int pick_thread;
+    int last_thread;
+    int pick;
+    unsigned long long above_cnt, above_mass, bucket_mass, total_cnt, total_mass;
+    double need_mass;
+};
+
+template <typename T>
+struct Digits;
+template <>
+struct Digits<uint16_t> {
+    static constexpr int kLevels = 2;
+    __device__ static int shift(int l) { return l == 0 ? 24 : 16; }
+    __device__ static int bits(int) { return 8; }
+};
+template <>
+struct Digits<float> {
+    static constexpr int kLevels = 3;
+    __device__ static int shift(int l) { return l == 0 ? 21 : (l == 1 ? 10 : 0); }
+    __device__ static int bits(int l) { return l == 2 ? 10 : 11; }
+};
+
+// Exclusive block scan of three u64 values at once (every thread gets its offsets and
+// the totals).
+__device__ inline void block_scan3(unsigned long long v[3], unsigned long long ex[3],
+                                   unsigned long long tot[3], FilterSmem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned long long inc[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        unsigned long long x = v[k];
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        inc[k] = x;
+        if (lane == 63) sm.wtot[k][wave] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        unsigned long long off = 0, all = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            if (w < wave) off += sm.wtot[k][w];
+            all += sm.wtot[k][w];
+        }
+        ex[k] = off + inc[k] - v[k];
+        tot[k] = all;
+    }
+    __syncthreads();
+}
+
+// One histogram pass: the tokens with key >= lo whose key agrees with `prefix` on the
+// bits of `pmask` are counted and weighed by digit (key >> shift) & (nb - 1).  The lanes
+// of a wave that share a digit add their counts and masses before one LDS atomic.
+template <typename T>
+__device__ void hist_pass(const T* rowp, int V, float M, float s2, float fscale, uint32_t lo,
+                          uint32_t prefix, uint32_t pmask, int shift, int nb, FilterSmem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    constexpr int kVec = Ld<T>::kVec;
+    for (int i = tid; i < nb; i += kBlock) {
+        sm.cnt[i] = 0u;
+        sm.mass[i] = 0ull;
+    }
+    __syncthreads();
+    auto visit = [&](float x, bool in) {  // wave-uniform call
+        const uint32_t key = order_key(x);
+        const bool take = in && key >= lo && (key & pmask) == prefix;
+        const uint32_t dg = (key >> shift) & (uint32_t)(nb - 1);
+        const unsigned long long v =
+            take ? (unsigned long long)(ex2((x - M) * s2) * fscale) : 0ull;
+        unsigned long long pending = __ballot(take);
+        while (pending) {
+            const int leader = __ffsll((long long)pending) - 1;
+            const uint32_t dl = __shfl(dg, leader);
+            const bool same = take && dg == dl;
+            const unsigned long long grp = __ballot(same);
+            unsigned long long sv = same ? v : 0ull;
+            for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
+            if (lane == leader) {
+                atomicAdd(&sm.cnt[dl], (uint32_t)__popcll(grp));
+                atomicAdd(&sm.mass[dl], sv);
+            }
+            pending &= ~grp;
+        }
+    };
+    int head = (int)(((16u - ((uint32_t)(uintptr_t)rowp & 15u)) & 15u) / sizeof(T));
+    if (head > V) head = V;
+    const int nv = (V - head) / kVec;
+    const int tail0 = head + nv * kVec;
+    {
+        const bool in = tid < head;
+        visit(in ? Ld<T>::one(rowp + tid) : 0.f, in);
+    }
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + head);
+    for (int v0 = 0; v0 < nv; v0 += kBlock) {
+        const bool in = v0 + tid < nv;
+        float f[kVec];
+        if (in) {
+            Ld<T>::unpack(ld_stream(vp + v0 + tid), f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) f[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) visit(f[e], in);
+    }
+    for (int t0 = tail0; t0 < V; t0 += kBlock) {
+        const bool in = t0 + tid < V;
+        visit(in ? Ld<T>::one(rowp + t0 + tid) : 0.f, in);
+    }
+    __syncthreads();
+}
+
+// The digit, scanning from the top, at which the accumulated count (by_mass false) or
+// mass reaches `need` (the lowest non-empty digit if it never does).  Updates the
+// count / mass above the chosen digit and leaves the chosen digit's mass in
+// sm.bucket_mass; the level's totals go to sm.total_cnt / sm.total_mass.
+__device__ int hist_pick(int nb, bool first, bool by_mass, double need_frac,
+                         unsigned long long need_cnt, FilterSmem& sm) {
+    const int tid = threadIdx.x;
+    const int per = nb >= kBlock ? nb / kBlock : 1;
+    const int hi = nb - 1 - tid * per;  // this thread owns digits hi, hi-1, .., hi-per+1
+    const bool owns = tid * per < nb;
+    unsigned long long v[3] = {0ull, 0ull, 0ull}, ex[3], tot[3];
+    if (owns)
+        for (int d = hi; d > hi - per; --d) {
+            v[0] += sm.cnt[d];
+            v[1] += sm.mass[d];
+        }
+    v[2] = by_mass ? v[1] : v[0];
+    block_scan3(v, ex, tot, sm);
+    const unsigned long long base_sel = by_mass ? sm.above_mass : sm.above_cnt;
+    // by mass the need is a fraction of every candidate's mass, which only the first level
+    // sees (it is fixed there and kept); by count it is given
+    if (first && tid == 0) sm.need_mass = need_frac * (double)tot[1];
+    __syncthreads();
+    const double need = by_mass ? sm.need_mass : (double)need_cnt;
+    if (tid == 0) {
+        sm.pick_thread = INT_MAX;
+        sm.last_thread = -1;
+        sm.pick = 0;
+        sm.bucket_mass = 0ull;
+    }
+    __syncthreads();
+    if (owns && v[0] > 0) {
+        if ((double)(base_sel + ex[2] + v[2]) >= need) atomicMin(&sm.pick_thread, tid);
+        atomicMax(&sm.last_thread, tid);
+    }
+    __syncthreads();
+    const int who = sm.pick_thread != INT_MAX ? sm.pick_thread : sm.last_thread;
+    if (tid == who) {
+        unsigned long long ac = sm.above_cnt + ex[0], am = sm.above_mass + ex[1];
+        int pick = -1;
+        for (int d = hi; d > hi - per; --d) {
+            if (sm.cnt[d] == 0u) continue;
+            const unsigned long long sel = by_mass ? am + sm.mass[d] : ac + sm.cnt[d];
+            pick = d;
+            if (sm.pick_thread != INT_MAX && (double)sel >= need) break;
+            ac += sm.cnt[d];
+            am += sm.mass[d];
+        }
+        if (sm.pick_thread == INT_MAX) {  // never reached: keep every candidate
+            ac -= sm.cnt[pick];
+            am -= sm.mass[pick];
+        }
+        sm.pick = pick;
+        sm.above_cnt = ac;
+        sm.above_mass = am;
+        sm.bucket_mass = sm.mass[pick];
+    }
+    if (tid == 0) {
+        sm.total_cnt = tot[0];
+        sm.total_mass = tot[1];
+    }
+    __syncthreads();
+    return sm.pick;
+}
+
+// Radix selection of a threshold key t over the row's tokens with key >= lo: the largest
+// t whose keys >= t number at least need_cnt (top-k) or weigh at least need_frac of the
+// candidates' mass (top-p).  Returns t; *kept = fixed-point mass of the keys >= t.
+template <typename T>
+__device__ uint32_t radix_select(const T* rowp, int V, float M, float s2, float fscale,
+                                 uint32_t lo, bool by_mass, double need_frac,
+                                 unsigned long long need_cnt, unsigned long long* kept,
+                                 FilterSmem& sm) {
+    if (threadIdx.x == 0) {
+        sm.above_cnt = 0ull;
+        sm.above_mass = 0ull;
+    }
+    __syncthreads();
+    uint32_t prefix = 0u, pmask = 0u;
+    for (int l = 0; l < Digits<T>::kLevels; ++l) {
+        const int shift = Digits<T>::shift(l), nb = 1 << Digits<T>::bits(l);
+        hist_pass<T>(rowp, V, M, s2, fscale, lo, prefix, pmask, shift, nb, sm);
+        const int d = hist_pick(nb, l == 0, by_mass, need_frac, need_cnt, sm);
+        prefix |= (uint32_t)d << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+    }
+    *kept = sm.above_mass + sm.bucket_mass;
+    return prefix;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
+    __shared__ FilterSmem sm;
+    const int R = a.R, G = R - 1, V = a.V;
+    const int r = blockIdx.x;
+    const bool draft = r >= a.B * R;
+    const int b = draft ? (r - a.B * R) / G : r / R;
+    const T* rowp = draft ? reinterpret_cast<const T*>(a.dlogits) + (size_t)(r - a.B * R) * V
+                          : reinterpret_cast<const T*>(a.logits) + (size_t)r * V;
+    const float Tf = a.temperature[b];
+    const float s2 = kLog2e / Tf;
+    const Part st = chunk_record<T, true>(rowp, 0, V, s2, sm.rs);
+    FiltRow fr;
+    fr.M = st.m;
+    fr.th = 0u;
+    fr.Z = st.z;
+    const int k = a.top_k ? a.top_k[b] : 0;
+    const float tp = a.top_p ? a.top_p[b] : 1.f;
+    const bool fk = k > 0 && k < V;
+    const bool fp = tp > 0.f && tp < 1.f;
+    const bool t_ok = isfinite(Tf) && Tf > 0.f;
+    if (st.m != -INFINITY && t_ok && (fk || fp)) {
+        const float fscale = exp2f((float)a.fixbits);
+        unsigned long long kept = 0ull;
+        uint32_t lo = 0u;
+        if (fk) lo = radix_select<T>(rowp, V, st.m, s2, fscale, 0u, false, 0.0,
+                                     (unsigned long long)k, &kept, sm);
+        if (fp) lo = radix_select<T>(rowp, V, st.m, s2, fscale, lo, true, (double)tp, 0ull,
+                                     &kept, sm);
+        fr.th = lo;
+        fr.Z = ldexp((double)kept, -a.fixbits);
+    }
+    if (threadIdx.x == 0) a.frows[r] = fr;
+}
+
+// One workgroup per filtered chain request: the acceptance scan on the filtered rows,
+// its outputs and the draw state.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_filter_accept(KArgs a) {
+    __shared__ Smem sm;
+    __shared__ float dq[kMaxRows];
+    __shared__ FiltRow fq[kMaxRows];
+    __shared__ FiltRow fpp[kMaxRows];
+    const int tid = threadIdx.x;
+    const int R = a.R, G = R - 1, V = a.V;
+    const int b = blockIdx.x;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    const T* dlogits = reinterpret_cast<const T*>(a.dlogits);
+    if (tid < R) {
+        sm.u[tid] = a.coins[(size_t)b * R + tid];
+        fpp[tid] = a.frows[(size_t)b * R + tid];
+    }
+    if (tid < G) {
+        fq[tid] = a.frows[(size_t)a.B * R + (size_t)b * G + tid];
+        const int xi = a.tokens[(size_t)b * G + tid];
+        sm.x[tid] = xi;
+        if (xi >= 0 && xi < V) {
+            sm.l[tid] = Ld<T>::one(logits + ((size_t)b * R + tid) * V + xi);
+            dq[tid] = Ld<T>::one(dlogits + ((size_t)b * G + tid) * V + xi);
+        }
+    }
+    const float Tf = a.temperature[b];
+    const float tp = a.top_p ? a.top_p[b] : 1.f;
+    const bool t_ok = isfinite(Tf) && Tf > 0.f && tp > 0.f && !isnan(tp);
+    const double Td = (double)Tf;
+    __syncthreads();
+    if (tid < R) {  // lane i: is everything position i consults usable, and is x_i kept?
+        bool ok = fpp[tid].M != -INFINITY && sm.u[tid] > 0.f && sm.u[tid] <= 1.f;
+        bool keep = false;
+        if (tid < G) {
+            const int xi = sm.x[tid];
+            ok = ok && xi >= 0 && xi < V && fq[tid].M != -INFINITY;
+            if (ok && t_ok) {
+                const float l = sm.l[tid], d = dq[tid];
+                const double p = order_key(l) >= fpp[tid].th
+                                     ? exp(((double)l - (double)fpp[tid].M) / Td) / fpp[tid].Z
+                                     : 0.0;
+                const double qx = order_key(d) >= fq[tid].th
+                                      ? exp(((double)d - (double)fq[tid].M) / Td) / fq[tid].Z
+                                      : 0.0;
+                keep = qx > 0.0 ? (p > 0.0 && (double)sm.u[tid] <= p / qx) : p > 0.0;
+                sm.p[tid] = p;
+            }
+        }
+        sm.arg[tid] = (ok ? 1 : 0) | (keep ? 2 : 0);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        bool valid = t_ok;
+        for (int i = 0; i < R; ++i)
+            if (!(sm.arg[i] & 1)) valid = false;
+        int k = G;
+        for (int i = 0; i < G && valid; ++i)
+            if (!(sm.arg[i] & 2)) {
+                k = i;
+                break;
+            }
+        sm.k = valid ? k : -1;
+        a.accept_len[b] = sm.k;
+        DrawState st = {};
+        st.kind = kDrawNone;
+        if (valid) {
+            st.kind = k < G ? kDrawResidual : kDrawTarget;
+            st.row = b * R + k;
+            st.qrow = b * G + k;
+            st.out = b * R + k;
+            st.coin = b * R + G;
+            st.nexcl = 0;
+            st.M = fpp[k].M;
+            st.Z = fpp[k].Z;
+            st.invZ = (float)(1.0 / fpp[k].Z);
+            st.T = Td;
+            st.thp = fpp[k].th;
+            if (k < G) {
+                st.thq = fq[k].th;
+                st.Mq = fq[k].M;
+                st.invZq = (float)(1.0 / fq[k].Z);
+            }
+        }
+        a.dstate[b] = st;
+    }
+    __syncthreads();
+    const int k = sm.k;
+    for (int i = tid; i < R; i += kBlock) {
+        int t = -1;
+        float pr = 0.f;
+        if (k >= 0 && i < k) {
+            t = sm.x[i];
+            pr = (float)sm.p[i];
+        }
+        if (i != k) {  // slot k is written by the final draw
+            a.out_tokens[(size_t)b * R + i] = t;
+            if (a.probs) a.probs[(size_t)b * R + i] = pr;
+        }
     }
 }
 
@@ -1300,7 +1758,7 @@ __global__ __launch_bounds__(kBlock) void k_commit_kv(const int32_t* accepted_no
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t parts, dstate, mass, massfb, seg, excl, total;
+    size_t parts, dstate, mass, massfb, seg, excl, frows, total;
 };
 
 inline long fine_chunks(int V) { return ((long)V + kFine - 1) / kFine; }
@@ -1324,6 +1782,8 @@ Layout layout_for(int op, int B, int R, int V) {
     off = align256(off + sizeof(double) * (size_t)B * S2 * kSegs);
     L.excl = off;
     if (op == SPEC_OP_TREE) off = align256(off + sizeof(int32_t) * (size_t)B * SPEC_MAX_N);
+    L.frows = off;
+    if (op == SPEC_OP_CHAIN_FILTERED) off = align256(off + sizeof(FiltRow) * (size_t)B * (2 * R - 1));
     L.total = off;
     return L;
 }
@@ -1337,6 +1797,7 @@ void bind_workspace(KArgs& a, void* ws, int op) {
     a.massfb = reinterpret_cast<double*>(base + L.massfb);
     a.seg = reinterpret_cast<double*>(base + L.seg);
     a.excl = op == SPEC_OP_TREE ? reinterpret_cast<int32_t*>(base + L.excl) : nullptr;
+    a.frows = op == SPEC_OP_CHAIN_FILTERED ? reinterpret_cast<FiltRow*>(base + L.frows) : nullptr;
 }
 
 // Split each row into S chunks of `chunk` elements (a multiple of 8): about 64 KB of
@@ -1397,12 +1858,12 @@ int run_greedy(KArgs& a, hipStream_t st) {
     return launch_status();
 }
 
-template <typename T>
+template <typename T, bool kFilt = false>
 int run_draw(KArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_mass<T>), dim3(a.B * a.S2), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((k_mass<T, kFilt>), dim3(a.B * a.S2), dim3(kBlock), 0, st, a);
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
-    hipLaunchKernelGGL((k_draw<T>), dim3(a.B), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_draw<T, kFilt>), dim3(a.B), dim3(64), 0, st, a);
     return launch_status();
 }
 
@@ -1431,6 +1892,18 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
     return run_draw<T>(a, st);
 }
 
+template <typename T>
+int run_chain_filtered(KArgs& a, hipStream_t st) {
+    const int G = a.R - 1;
+    hipLaunchKernelGGL((k_filter_rows<T>), dim3(a.B * (a.R + G)), dim3(kBlock), 0, st, a);
+    int rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    hipLaunchKernelGGL((k_filter_accept<T>), dim3(a.B), dim3(kBlock), 0, st, a);
+    rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    return run_draw<T, true>(a, st);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -1438,7 +1911,7 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
 
 extern "C" size_t spec_workspace_bytes(int op, int B, int R, int V) {
     if (B < 0 || R < 1 || V < 1) return 0;
-    if (op == SPEC_OP_GREEDY || op == SPEC_OP_CHAIN) {
+    if (op == SPEC_OP_GREEDY || op == SPEC_OP_CHAIN || op == SPEC_OP_CHAIN_FILTERED) {
         if (R - 1 < 1 || R - 1 > SPEC_MAX_G) return 0;
     } else if (op == SPEC_OP_TREE) {
         if (R > SPEC_MAX_N) return 0;
@@ -1580,4 +2053,42 @@ extern "C" int spec_tree_commit_kv(const int32_t* accepted_nodes, const int32_t*
                        static_cast<const uint8_t*>(kv_tree), static_cast<uint8_t*>(kv_out),
                        row_bytes, (int)nchunks, slots, vec);
     return launch_status();
+}
+
+extern "C" int spec_verify_chain_filtered(const void* logits, const void* draft_logits, int dtype,
+                                          const int32_t* draft_tokens, const float* coins,
+                                          const float* temperature, const int32_t* top_k,
+                                          const float* top_p, int B, int G, int V,
+                                          int32_t* accept_len, int32_t* out_tokens,
+                                          float* probs_out, void* workspace, size_t ws_bytes,
+                                          void* stream) {
+    if (!draft_logits || !draft_tokens || !coins || !temperature || !accept_len || !out_tokens)
+        return SPEC_ERR_NULL;
+    if (G < 1 || G > SPEC_MAX_G) return SPEC_ERR_SHAPE;
+    int rc = check_common(logits, dtype, B, V, workspace, ws_bytes, SPEC_OP_CHAIN_FILTERED, G + 1);
+    if (rc != SPEC_OK || B == 0) return rc;
+    if (((uintptr_t)draft_logits) % (dtype == SPEC_F32 ? 4 : 2)) return SPEC_ERR_PARAM;
+    if ((long long)B * (2 * G + 1) > 0xffffffffLL / kBlock) return SPEC_ERR_SHAPE;
+    KArgs a = {};
+    a.logits = logits;
+    a.dlogits = draft_logits;
+    a.tokens = draft_tokens;
+    a.coins = coins;
+    a.temperature = temperature;
+    a.top_k = top_k;
+    a.top_p = top_p;
+    a.B = B;
+    a.R = G + 1;
+    a.V = V;
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.probs = probs_out;
+    int lv = 0;
+    while ((1L << lv) < (long)V) ++lv;
+    a.fixbits = 62 - lv;
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    if (rc != SPEC_OK) return rc;
+    bind_workspace(a, workspace, SPEC_OP_CHAIN_FILTERED);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return dtype == SPEC_F32 ? run_chain_filtered<float>(a, st) : run_chain_filtered<uint16_t>(a, st);
 }

@@ -263,3 +263,70 @@ def make_tree(cfg_id: int = 4, seed: int = 0, *, B: int | None = None, N: int | 
                       parents=parents, coins=coins, temperature=temperature,
                       meta=dict(cfg=cfg_id, seed=seed, sigma=sigma, T=T,
                                 max_children=max_children))
+
+
+@dataclass
+class ChainLogitsInputs:
+    name: str
+    B: int
+    G: int
+    V: int
+    dtype: str
+    logits: np.ndarray          # [B][G+1][V] target logits (float32 or bf16 bits)
+    draft_logits: np.ndarray    # [B][G][V] draft logits, same dtype
+    draft_tokens: np.ndarray    # [B][G] int32, drawn by the drafter from its filtered q
+    coins: np.ndarray           # [B][G+1] float32 in (0, 1]
+    temperature: np.ndarray     # [B] float32
+    top_k: np.ndarray           # [B] int32 (0: off)
+    top_p: np.ndarray           # [B] float32 (1: off)
+
+    @property
+    def R(self) -> int:
+        return self.G + 1
+
+
+def _drafter_sample(rng, d_row: np.ndarray, T: float, k: int, top_p: float) -> int:
+    """How a drafter with top-k / top-p sampling picks its token (input synthesis)."""
+    z = d_row.astype(np.float64) / T
+    z -= z.max()
+    p = np.exp(z)
+    if 0 < k < len(p):
+        p[d_row < np.sort(d_row)[::-1][k - 1]] = 0.0
+    p /= p.sum()
+    if top_p < 1.0:
+        order = np.sort(p)[::-1]
+        tau = order[np.searchsorted(np.cumsum(order), top_p)]
+        p[p < tau] = 0.0
+        p /= p.sum()
+    return int(rng.choice(len(p), p=p))
+
+
+def make_chain_logits(cfg_id: int = 5, seed: int = 0, *, B: int | None = None,
+                      G: int | None = None, V: int | None = None, dtype: str | None = None,
+                      T: float | None = None, top_k=0, top_p=1.0) -> ChainLogitsInputs:
+    """Chain inputs with the draft as logits (draft = target + N(0, var) noise, stored in the
+    target's dtype) and drafts sampled with the given top-k / top-p (scalars or [B])."""
+    c = dict(CONFIGS[cfg_id])
+    B = c["B"] if B is None else B
+    G = c["G"] if G is None else G
+    V = c["V"] if V is None else V
+    dtype = c["dtype"] if dtype is None else dtype
+    T = c["T"] if T is None else T
+    r_logits, r_noise, r_draft, r_coins, _ = _streams(100 + cfg_id, seed, 5)
+    R = G + 1
+    logits = _target_rows(r_logits, B * R, V, c["sigma"], c.get("boost"), dtype).reshape(B, R, V)
+    top_k = np.broadcast_to(np.asarray(top_k, np.int32), (B,)).copy()
+    top_p = np.broadcast_to(np.asarray(top_p, np.float32), (B,)).copy()
+    sd = np.float32(np.sqrt(c["draft_var"]))
+    draft_logits = np.empty((B, G, V), dtype=logits.dtype)
+    draft_tokens = np.empty((B, G), np.int32)
+    for b in range(B):
+        d = logits_as_f32(logits[b, :G], dtype) + r_noise.standard_normal((G, V), dtype=np.float32) * sd
+        draft_logits[b] = f32_to_bf16_bits(d) if dtype == BF16 else d
+        dw = logits_as_f32(draft_logits[b], dtype)
+        for i in range(G):
+            draft_tokens[b, i] = _drafter_sample(r_draft, dw[i], T, int(top_k[b]), float(top_p[b]))
+    return ChainLogitsInputs(name=f"chain from draft logits B={B} G={G} V={V} {dtype}", B=B, G=G,
+                             V=V, dtype=dtype, logits=logits, draft_logits=draft_logits,
+                             draft_tokens=draft_tokens, coins=draw_coins(r_coins, (B, R)),
+                             temperature=np.full((B,), T, np.float32), top_k=top_k, top_p=top_p)

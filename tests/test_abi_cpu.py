@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.declared_functions()
     assert set(names) >= {"spec_verify_greedy", "spec_verify_chain", "spec_verify_tree",
-                          "spec_tree_mask", "spec_tree_commit_kv", "spec_workspace_bytes",
+                          "spec_tree_mask", "spec_tree_commit_kv", "spec_verify_chain_filtered",
+                          "spec_workspace_bytes",
                           "spec_status_str"}
     for n in names:
         assert hasattr(lib, n), n
@@ -147,3 +148,26 @@ def test_tree_commit_kv_rejects_bad_arguments(lib):
     assert f(P, P, 2, 4, L.SPEC_MAX_N + 1, P, P, 64, P, None) == L.SPEC_ERR_SHAPE
     assert f(P, P, 2, 4, 8, P, P, 0, P, None) == L.SPEC_ERR_SHAPE
     assert f(P, P, 0, 4, 8, P, P, 64, None, None) == L.SPEC_OK
+
+
+
+def test_chain_filtered_rejects_bad_arguments(lib):
+    f = lib.spec_verify_chain_filtered
+    ws = L.workspace_bytes(L.SPEC_OP_CHAIN_FILTERED, 2, 5, 1000)
+    assert ws > L.workspace_bytes(L.SPEC_OP_CHAIN, 2, 5, 1000)
+    args = dict(lg=P, dl=P, dt=L.SPEC_BF16, tok=P, coins=P, T=P, k=None, p=None, B=2, G=4,
+                V=1000, acc=P, out=P, probs=None, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["lg"], a["dl"], a["dt"], a["tok"], a["coins"], a["T"], a["k"], a["p"], a["B"],
+                 a["G"], a["V"], a["acc"], a["out"], a["probs"], a["ws"], a["wsb"], None)
+    assert call(lg=None) == L.SPEC_ERR_NULL
+    assert call(dl=None) == L.SPEC_ERR_NULL
+    assert call(coins=None) == L.SPEC_ERR_NULL
+    assert call(G=0) == L.SPEC_ERR_SHAPE
+    assert call(G=65) == L.SPEC_ERR_SHAPE
+    assert call(dt=7) == L.SPEC_ERR_DTYPE
+    assert call(wsb=ws - 1) == L.SPEC_ERR_WORKSPACE
+    assert call(dl=P + 1) == L.SPEC_ERR_PARAM
+    assert call(B=0) == L.SPEC_OK
