@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--tree", action="store_true", help="also time the tree workload")
+    ap.add_argument("--filtered", action="store_true",
+                    help="also time chain verify from draft logits with top-k 50 / top-p 0.9")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB 3 times (counter scale)")
@@ -184,6 +186,8 @@ def main():
 
     if args.tree:
         result["modes"].update(_tree_modes(args, torch, dev, api, wl))
+    if args.filtered:
+        result["modes"].update(_filtered_mode(args, torch, dev, api, wl))
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
@@ -341,6 +345,46 @@ def _tree_modes(args, torch, dev, api, wl):
                         "nodes/s": t.B * t.N / (d.mean() * 1e-3), "bytes": nbytes,
                         "bound": "latency (one workgroup per request)"}
     return out
+
+
+def _filtered_mode(args, torch, dev, api, wl):
+    """spec_verify_chain_filtered on the large-batch shape, draft as bf16 logits, top-k 50
+    and top-p 0.9 for every request."""
+    c = wl.make_chain_logits(args.workload, top_k=50, top_p=0.9)
+
+    def lg(a):
+        a = np.ascontiguousarray(a)
+        if c.dtype == wl.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    base = dict(l=lg(c.logits), d=lg(c.draft_logits), x=torch.from_numpy(c.draft_tokens).to(dev),
+                u=torch.from_numpy(c.coins).to(dev), T=torch.from_numpy(c.temperature).to(dev),
+                k=torch.from_numpy(c.top_k).to(dev), p=torch.from_numpy(c.top_p).to(dev))
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.copies - 1)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(5):
+        d = copies[i % len(copies)]
+        api.spec_verify_chain_filtered(d["l"], d["d"], d["x"], d["u"], d["T"], d["k"], d["p"])
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(20):
+        d = copies[i % len(copies)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        acc, _, _ = api.spec_verify_chain_filtered(d["l"], d["d"], d["x"], d["u"], d["T"], d["k"], d["p"])
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    es = 2 if c.dtype == wl.BF16 else 4
+    once = (c.B * c.R + c.B * c.G) * c.V * es
+    return {"chain_filtered": {"workload": c.name + ", top-k 50, top-p 0.9",
+                               "avg_ms": float(t.mean()),
+                               "positions/s": c.B * c.R / (t.mean() * 1e-3),
+                               "row_bytes_once": once,
+                               "GB/s_rows_once": once / (t.mean() * 1e-3) / 1e9,
+                               "accepted_mean": float(acc.float().mean().item())}}
 
 
 def _cpu_baseline(c, seconds):

@@ -1264,14 +1264,14 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
 // weighs (fixed point, so sums are exact and independent of order) the tokens that
 // agree with the digits chosen so far, and the walk takes the digit where the count
 // (top-k) or mass (top-p) accumulated from the largest keys reaches what is needed.
-// bf16 keys have 16 significant bits (two 8-bit digits); fp32 keys take 11 + 11 + 10.
+// bf16 keys have 16 significant bits (two 8-bit digits); fp32 keys take four.
 
-constexpr int kHistBins = 2048;
+constexpr int kHistBins = 256;  // 8-bit radix digits
 
 struct FilterSmem {
     RowSmem rs;
-    uint32_t cnt[kHistBins];
-    unsigned long long mass[kHistBins];
+    uint32_t cnt[kWaves][kHistBins];            // one private histogram per wave
+    unsigned long long mass[kWaves][kHistBins];
     unsigned long long wtot[3][kWaves];
     int pick_thread;
     int last_thread;
@@ -1283,16 +1283,14 @@ struct FilterSmem {
 template <typename T>
 struct Digits;
 template <>
-struct Digits<uint16_t> {
+struct Digits<uint16_t> {  // a widened bf16 has 16 significant key bits
     static constexpr int kLevels = 2;
-    __device__ static int shift(int l) { return l == 0 ? 24 : 16; }
-    __device__ static int bits(int) { return 8; }
+    __device__ static int shift(int l) { return 24 - 8 * l; }
 };
 template <>
 struct Digits<float> {
-    static constexpr int kLevels = 3;
-    __device__ static int shift(int l) { return l == 0 ? 21 : (l == 1 ? 10 : 0); }
-    __device__ static int bits(int l) { return l == 2 ? 10 : 11; }
+    static constexpr int kLevels = 4;
+    __device__ static int shift(int l) { return 24 - 8 * l; }
 };
 
 // Exclusive block scan of three u64 values at once (every thread gets its offsets and
@@ -1326,63 +1324,56 @@ __device__ inline void block_scan3(unsigned long long v[3], unsigned long long e
 }
 
 // One histogram pass: the tokens with key >= lo whose key agrees with `prefix` on the
-// bits of `pmask` are counted and weighed by digit (key >> shift) & (nb - 1).  The lanes
-// of a wave that share a digit add their counts and masses before one LDS atomic.
+// bits of `pmask` are counted and weighed (fixed point) by digit (key >> shift) & 255,
+// each wave into its own LDS histogram; the four are added up at the end.
 template <typename T>
 __device__ void hist_pass(const T* rowp, int V, float M, float s2, float fscale, uint32_t lo,
-                          uint32_t prefix, uint32_t pmask, int shift, int nb, FilterSmem& sm) {
-    const int tid = threadIdx.x, lane = tid & 63;
+                          uint32_t prefix, uint32_t pmask, int shift, FilterSmem& sm) {
+    const int tid = threadIdx.x, wave = tid >> 6;
     constexpr int kVec = Ld<T>::kVec;
-    for (int i = tid; i < nb; i += kBlock) {
-        sm.cnt[i] = 0u;
-        sm.mass[i] = 0ull;
+    for (int i = tid; i < kWaves * kHistBins; i += kBlock) {
+        (&sm.cnt[0][0])[i] = 0u;
+        (&sm.mass[0][0])[i] = 0ull;
     }
     __syncthreads();
-    auto visit = [&](float x, bool in) {  // wave-uniform call
+    uint32_t* cnt = sm.cnt[wave];
+    unsigned long long* mass = sm.mass[wave];
+    auto visit = [&](float x) {
         const uint32_t key = order_key(x);
-        const bool take = in && key >= lo && (key & pmask) == prefix;
-        const uint32_t dg = (key >> shift) & (uint32_t)(nb - 1);
-        const unsigned long long v =
-            take ? (unsigned long long)(ex2((x - M) * s2) * fscale) : 0ull;
-        unsigned long long pending = __ballot(take);
-        while (pending) {
-            const int leader = __ffsll((long long)pending) - 1;
-            const uint32_t dl = __shfl(dg, leader);
-            const bool same = take && dg == dl;
-            const unsigned long long grp = __ballot(same);
-            unsigned long long sv = same ? v : 0ull;
-            for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
-            if (lane == leader) {
-                atomicAdd(&sm.cnt[dl], (uint32_t)__popcll(grp));
-                atomicAdd(&sm.mass[dl], sv);
-            }
-            pending &= ~grp;
+        if (key >= lo && (key & pmask) == prefix) {
+            const uint32_t dg = (key >> shift) & (uint32_t)(kHistBins - 1);
+            atomicAdd(&cnt[dg], 1u);
+            atomicAdd(&mass[dg], (unsigned long long)(ex2((x - M) * s2) * fscale));
         }
     };
     int head = (int)(((16u - ((uint32_t)(uintptr_t)rowp & 15u)) & 15u) / sizeof(T));
     if (head > V) head = V;
     const int nv = (V - head) / kVec;
     const int tail0 = head + nv * kVec;
-    {
-        const bool in = tid < head;
-        visit(in ? Ld<T>::one(rowp + tid) : 0.f, in);
-    }
+    if (tid < head) visit(Ld<T>::one(rowp + tid));
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + head);
-    for (int v0 = 0; v0 < nv; v0 += kBlock) {
-        const bool in = v0 + tid < nv;
-        float f[kVec];
-        if (in) {
-            Ld<T>::unpack(ld_stream(vp + v0 + tid), f);
-        } else {
+    int v = tid;
+    for (; v + kBlock < nv; v += 2 * kBlock) {
+        const u32x4 r0 = ld_stream(vp + v), r1 = ld_stream(vp + v + kBlock);
+        float f[2 * kVec];
+        Ld<T>::unpack(r0, f);
+        Ld<T>::unpack(r1, f + kVec);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) f[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) visit(f[e], in);
+        for (int e = 0; e < 2 * kVec; ++e) visit(f[e]);
     }
-    for (int t0 = tail0; t0 < V; t0 += kBlock) {
-        const bool in = t0 + tid < V;
-        visit(in ? Ld<T>::one(rowp + t0 + tid) : 0.f, in);
+    for (; v < nv; v += kBlock) {
+        float f[kVec];
+        Ld<T>::unpack(ld_stream(vp + v), f);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) visit(f[e]);
+    }
+    if (tail0 + tid < V) visit(Ld<T>::one(rowp + tail0 + tid));
+    __syncthreads();
+    for (int d = tid; d < kHistBins; d += kBlock) {
+        for (int w = 1; w < kWaves; ++w) {
+            sm.cnt[0][d] += sm.cnt[w][d];
+            sm.mass[0][d] += sm.mass[w][d];
+        }
     }
     __syncthreads();
 }
@@ -1400,8 +1391,8 @@ __device__ int hist_pick(int nb, bool first, bool by_mass, double need_frac,
     unsigned long long v[3] = {0ull, 0ull, 0ull}, ex[3], tot[3];
     if (owns)
         for (int d = hi; d > hi - per; --d) {
-            v[0] += sm.cnt[d];
-            v[1] += sm.mass[d];
+            v[0] += sm.cnt[0][d];
+            v[1] += sm.mass[0][d];
         }
     v[2] = by_mass ? v[1] : v[0];
     block_scan3(v, ex, tot, sm);
@@ -1428,21 +1419,21 @@ __device__ int hist_pick(int nb, bool first, bool by_mass, double need_frac,
         unsigned long long ac = sm.above_cnt + ex[0], am = sm.above_mass + ex[1];
         int pick = -1;
         for (int d = hi; d > hi - per; --d) {
-            if (sm.cnt[d] == 0u) continue;
-            const unsigned long long sel = by_mass ? am + sm.mass[d] : ac + sm.cnt[d];
+            if (sm.cnt[0][d] == 0u) continue;
+            const unsigned long long sel = by_mass ? am + sm.mass[0][d] : ac + sm.cnt[0][d];
             pick = d;
             if (sm.pick_thread != INT_MAX && (double)sel >= need) break;
-            ac += sm.cnt[d];
-            am += sm.mass[d];
+            ac += sm.cnt[0][d];
+            am += sm.mass[0][d];
         }
         if (sm.pick_thread == INT_MAX) {  // never reached: keep every candidate
-            ac -= sm.cnt[pick];
-            am -= sm.mass[pick];
+            ac -= sm.cnt[0][pick];
+            am -= sm.mass[0][pick];
         }
         sm.pick = pick;
         sm.above_cnt = ac;
         sm.above_mass = am;
-        sm.bucket_mass = sm.mass[pick];
+        sm.bucket_mass = sm.mass[0][pick];
     }
     if (tid == 0) {
         sm.total_cnt = tot[0];
@@ -1467,11 +1458,11 @@ __device__ uint32_t radix_select(const T* rowp, int V, float M, float s2, float 
     __syncthreads();
     uint32_t prefix = 0u, pmask = 0u;
     for (int l = 0; l < Digits<T>::kLevels; ++l) {
-        const int shift = Digits<T>::shift(l), nb = 1 << Digits<T>::bits(l);
-        hist_pass<T>(rowp, V, M, s2, fscale, lo, prefix, pmask, shift, nb, sm);
-        const int d = hist_pick(nb, l == 0, by_mass, need_frac, need_cnt, sm);
+        const int shift = Digits<T>::shift(l);
+        hist_pass<T>(rowp, V, M, s2, fscale, lo, prefix, pmask, shift, sm);
+        const int d = hist_pick(kHistBins, l == 0, by_mass, need_frac, need_cnt, sm);
         prefix |= (uint32_t)d << shift;
-        pmask |= (uint32_t)(nb - 1) << shift;
+        pmask |= (uint32_t)(kHistBins - 1) << shift;
     }
     *kept = sm.above_mass + sm.bucket_mass;
     return prefix;
