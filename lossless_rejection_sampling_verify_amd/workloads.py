@@ -266,6 +266,73 @@ def make_tree(cfg_id: int = 4, seed: int = 0, *, B: int | None = None, N: int | 
 
 
 @dataclass
+class TreeMssInputs:
+    name: str
+    B: int
+    N: int
+    V: int
+    D: int
+    dtype: str
+    logits: np.ndarray          # [B][N][V]; row j = target distribution after node j
+    draft_probs: np.ndarray     # [B][N][V] float32; row j = draft distribution after node j
+    node_tokens: np.ndarray     # [B][N] int32; children of j drawn i.i.d. from row j of q
+    parents: np.ndarray         # [B][N] int32; [b][0] = -1, parents[b][i] < i
+    coins: np.ndarray           # [B][N] float32 in (0, 1]; [c-1] tests node c, [N-1] final
+    temperature: np.ndarray     # [B] float32
+    meta: dict = field(default_factory=dict)
+
+
+def make_tree_mss(cfg_id: int = 4, seed: int = 0, *, B: int | None = None, N: int | None = None,
+                  V: int | None = None, D: int | None = None, max_children: int | None = None,
+                  dtype: str | None = None, T: float | None = None, sigma: float | None = None,
+                  draft_var: float = 1.0) -> TreeMssInputs:
+    """Token-tree inputs with draft distributions: the tree workload's shapes, target rows
+    and parent arrays, plus a draft row per node, q_j = softmax((row j + N(0, draft_var)) / T),
+    from which the children of node j are drawn independently (with replacement)."""
+    c = dict(CONFIGS[cfg_id])
+    if c["kind"] != "tree":
+        raise ValueError(f"workload {cfg_id} is not a tree workload")
+    B = c["B"] if B is None else B
+    N = c["N"] if N is None else N
+    V = c["V"] if V is None else V
+    D = c["D"] if D is None else D
+    max_children = c["max_children"] if max_children is None else max_children
+    dtype = c["dtype"] if dtype is None else dtype
+    T = c["T"] if T is None else T
+    sigma = c["sigma"] if sigma is None else sigma
+    r_logits, r_noise, r_draft, r_coins, r_tree = _streams(100 + cfg_id, seed, 5)
+
+    logits = _target_rows(r_logits, B * N, V, sigma, None, dtype).reshape(B, N, V)
+    parents = np.empty((B, N), dtype=np.int32)
+    node_tokens = np.full((B, N), -1, dtype=np.int32)
+    q = np.empty((B, N, V), dtype=np.float32)
+    sd = np.float32(np.sqrt(draft_var))
+    for b in range(B):
+        par = _random_tree(r_tree, N, D, max_children)
+        parents[b] = par
+        for j in range(N):
+            d = logits_as_f32(logits[b, j], dtype) + sd * r_noise.standard_normal(V, dtype=np.float32)
+            qj = _draft_distribution(d, T)
+            q[b, j] = qj
+            kids = np.nonzero(par == j)[0]
+            if len(kids):
+                cdf = np.cumsum(qj)
+                u = r_draft.random(len(kids)) * cdf[-1]
+                node_tokens[b, kids] = np.minimum(np.searchsorted(cdf, u, side="right"),
+                                                  V - 1).astype(np.int32)
+    coins = draw_coins(r_coins, (B, N))
+    temperature = np.full((B,), T, dtype=np.float32)
+    full = (B, N, V, D) == (c["B"], c["N"], c["V"], c["D"])
+    return TreeMssInputs(name=(c["name"] + " with draft rows") if full
+                         else f"tree B={B} N={N} D={D} V={V} {dtype} with draft rows",
+                         B=B, N=N, V=V, D=D, dtype=dtype, logits=logits, draft_probs=q,
+                         node_tokens=node_tokens, parents=parents, coins=coins,
+                         temperature=temperature,
+                         meta=dict(cfg=cfg_id, seed=seed, sigma=sigma, T=T,
+                                   max_children=max_children, draft_var=draft_var))
+
+
+@dataclass
 class ChainLogitsInputs:
     name: str
     B: int

@@ -54,6 +54,9 @@ def lib():
         L.oracle_verify_chain_filtered.argtypes = [vp, vp, ip, vp, vp, vp, vp, vp, ip, ip, ip,
                                                    vp, vp, vp, vp]
         L.oracle_verify_chain_filtered.restype = ctypes.c_int
+        L.oracle_verify_tree_mss.argtypes = [vp, ip, vp, vp, vp, vp, vp, ip, ip, ip, ip,
+                                             vp, vp, vp, vp, vp]
+        L.oracle_verify_tree_mss.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -202,3 +205,28 @@ def verify_chain_filtered(logits, draft_logits, dtype, draft_tokens, coins, temp
     if rc != 0:
         raise ValueError(f"oracle_verify_chain_filtered rejected its arguments ({rc})")
     return dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin)
+
+
+def verify_tree_mss(logits, dtype, draft_probs, node_tokens, parents, coins, temperature, D):
+    """Tree verify by multi-step speculative sampling with draft rows [B][N][V] and per-node
+    coins [B][N].  Returns dict(accept_len, out_tokens, accepted_nodes, probs, margin)."""
+    lg = _logits_array(logits, dtype)
+    q = np.ascontiguousarray(draft_probs, dtype=np.float32)
+    tk = np.ascontiguousarray(node_tokens, dtype=np.int32)
+    pa = np.ascontiguousarray(parents, dtype=np.int32)
+    cn = np.ascontiguousarray(coins, dtype=np.float32)
+    tp = np.ascontiguousarray(temperature, dtype=np.float32)
+    B, N = tk.shape
+    V = lg.shape[-1]
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, D + 1), np.int32)
+    nodes = np.empty((B, D), np.int32)
+    probs = np.empty((B, D + 1), np.float64)
+    margin = np.empty(B, np.float64)
+    rc = lib().oracle_verify_tree_mss(_ptr(lg), _dtype_code(dtype), _ptr(q), _ptr(tk), _ptr(pa),
+                                      _ptr(cn), _ptr(tp), B, N, V, D, _ptr(acc), _ptr(out),
+                                      _ptr(nodes), _ptr(probs), _ptr(margin))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_mss rejected its arguments ({rc})")
+    return dict(accept_len=acc, out_tokens=out, accepted_nodes=nodes, probs=probs,
+                margin=margin)

@@ -460,6 +460,142 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
     return 0;
 }
 
+/* ---- token tree, multi-step speculative sampling with draft distributions ---------
+ * [origins] SpecInfer, multi-step speculative sampling (MSS): the children of a node are
+ * tested one after another with the rule min(1, p(x)/q(x)); when a child is rejected the
+ * target distribution of that node is replaced by the residual norm(max(0, p - q)) and
+ * the next sibling is tested against the updated distribution; once every child has been
+ * rejected the token is drawn from the last updated distribution.  An accepted child
+ * becomes the next node, with its own target row and draft row.
+ * Readings: draft_probs row j is the distribution the children of node j were drawn
+ * from (shared by all of them; used as given, as in the chain); the siblings are tried in
+ * ascending node id; node c is tested with coins[c - 1] and the final draw uses
+ * coins[N - 1]; if the updated distribution has no positive mass the remaining siblings
+ * are not tested and the final token is drawn from the node's target row.  The output
+ * follows the target law when the children of each node are independent draws from
+ * that node's draft row. */
+static void tree_mss_one(const void* logits, int dtype, const float* q, const int32_t* tok,
+                         const int32_t* par, const float* coins, float temperature, int N,
+                         int V, int D, size_t b, int32_t* accept_len, int32_t* out,
+                         int32_t* nodes, double* probs, double* margin, double* w, int* depth) {
+    int valid = par[0] == -1 && temperature_ok(temperature);
+    depth[0] = 0;
+    for (int i = 1; i < N && valid; ++i) {
+        if (par[i] < 0 || par[i] >= i) {
+            valid = 0;
+            break;
+        }
+        depth[i] = depth[par[i]] + 1;
+        if (depth[i] > D) valid = 0;
+        if (tok[i] < 0 || tok[i] >= V) {
+            valid = 0;
+            break;
+        }
+        float qx = q[(size_t)par[i] * V + (size_t)tok[i]];
+        if (!(qx >= 0.0f) || !isfinite(qx)) valid = 0;
+    }
+    for (int c = 0; c < N && valid; ++c)
+        if (!coin_ok(coins[c])) valid = 0;
+    for (int j = 0; j < N && valid; ++j)
+        if (row_max(row_of(logits, dtype, b * (size_t)N + (size_t)j, V)) == -INFINITY) valid = 0;
+    *margin = INFINITY;
+    if (!valid) {
+        *accept_len = -1;
+        for (int d = 0; d <= D; ++d) out[d] = -1;
+        for (int d = 0; d < D; ++d) nodes[d] = -1;
+        if (probs)
+            for (int d = 0; d <= D; ++d) probs[d] = 0.0;
+        return;
+    }
+
+    double T = (double)temperature;
+    int cur = 0, d = 0;
+    double m = 0.0, Z = 0.0;
+    for (;;) {
+        Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
+        const float* qc = q + (size_t)cur * V;
+        m = row_max(r);
+        Z = row_partition(r, m, T);
+        for (int x = 0; x < V; ++x) w[x] = row_prob(r, x, m, Z, T); /* current distribution */
+        int chosen = -1;
+        for (int c = cur + 1; c < N; ++c) {
+            if (par[c] != cur) continue;
+            int x = tok[c];
+            double qx = (double)qc[x];
+            double u = (double)coins[c - 1];
+            int accept;
+            if (qx > 0.0) {
+                double ratio = w[x] / qx;
+                note_margin(margin, fabs(u - ratio));
+                accept = w[x] > 0.0 && u <= ratio;
+            } else {
+                accept = w[x] > 0.0;
+            }
+            if (accept) {
+                chosen = c;
+                break;
+            }
+            /* rejected: the distribution becomes norm(max(0, w - q)) */
+            double S = 0.0;
+            for (int v = 0; v < V; ++v) {
+                double dv = w[v] - (double)qc[v];
+                w[v] = dv > 0.0 ? dv : 0.0;
+                S += w[v];
+            }
+            note_margin(margin, S);
+            if (!(S > 0.0)) { /* no residual mass left: draw from the target row */
+                for (int v = 0; v < V; ++v) w[v] = row_prob(r, v, m, Z, T);
+                break;
+            }
+            for (int v = 0; v < V; ++v) w[v] /= S;
+        }
+        if (chosen < 0) break; /* a leaf, or every child rejected: final draw from w */
+        out[d] = tok[chosen];
+        nodes[d] = chosen;
+        if (probs) probs[d] = row_prob(r, tok[chosen], m, Z, T);
+        cur = chosen;
+        ++d;
+    }
+
+    Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
+    int y = draw_inverse_cdf(w, V, (double)coins[N - 1], margin);
+    out[d] = y;
+    if (probs) probs[d] = row_prob(r, y, m, Z, T);
+    for (int e = d + 1; e <= D; ++e) out[e] = -1;
+    for (int e = d; e < D; ++e) nodes[e] = -1;
+    if (probs)
+        for (int e = d + 1; e <= D; ++e) probs[e] = 0.0;
+    *accept_len = d;
+}
+
+int oracle_verify_tree_mss(const void* logits, int dtype, const float* draft_probs,
+                           const int32_t* node_tokens, const int32_t* parents,
+                           const float* coins, const float* temperature, int B, int N, int V,
+                           int D, int32_t* accept_len, int32_t* out_tokens,
+                           int32_t* accepted_nodes, double* probs_out, double* min_margin) {
+    if (!logits || !draft_probs || !node_tokens || !parents || !coins || !temperature ||
+        !accept_len || !out_tokens || !accepted_nodes || !min_margin)
+        return -1;
+    if (B < 0 || N < 2 || V < 1 || D < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)V);
+        int* depth = (int*)malloc(sizeof(int) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int b = 0; b < B; ++b)
+            tree_mss_one(logits, dtype, draft_probs + (size_t)b * N * V,
+                         node_tokens + (size_t)b * N, parents + (size_t)b * N,
+                         coins + (size_t)b * N, temperature[b], N, V, D, (size_t)b,
+                         accept_len + b, out_tokens + (size_t)b * (D + 1),
+                         accepted_nodes + (size_t)b * D,
+                         probs_out ? probs_out + (size_t)b * (D + 1) : NULL, min_margin + b, w,
+                         depth);
+        free(w);
+        free(depth);
+    }
+    return 0;
+}
+
 /* ---- chain rejection sampling from logits, with top-k / top-p filtering ------------
  * [ricardo] mechanism: serving samples with temperature, top-p, top-k and the like, so
  * "accept if it matches the target's top-1" is not unbiased sampling; correction

@@ -57,6 +57,16 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
                        float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
                        int32_t* accepted_nodes, double* probs_out, double* min_margin);
 
+/* Token-tree verify by multi-step speculative sampling with draft distributions:
+ * draft_probs [B][N][V] fp32 (row j = the distribution the children of node j were drawn
+ * from), coins [B][N] (coins[c-1] tests node c, coins[N-1] drives the final draw).
+ * Outputs as oracle_verify_tree. */
+int oracle_verify_tree_mss(const void* logits, int dtype, const float* draft_probs,
+                           const int32_t* node_tokens, const int32_t* parents,
+                           const float* coins, const float* temperature, int B, int N, int V,
+                           int D, int32_t* accept_len, int32_t* out_tokens,
+                           int32_t* accepted_nodes, double* probs_out, double* min_margin);
+
 /* Chain rejection sampling from target logits [B][G+1][V] and draft logits [B][G][V]
  * (same dtype), both at temperature T and both filtered with top_k[b] (NULL or <= 0 or
  * >= V: off; ties at the k-th largest logit kept) and then top_p[b] (NULL or >= 1: off;

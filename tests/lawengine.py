@@ -197,3 +197,69 @@ def tree_law(logits, dtype, tokens, parents, T, D):
 
     walk(0, coin(np.zeros(D + 1, dtype=np.int64)), 1.0)
     return law
+
+
+# ---------------------------------------------------------------------------------------
+# tree by multi-step speculative sampling: one coin per tested node, one final coin
+
+def mss_outcomes(logits, dtype, q, tokens, parents, T, D, coin_sets):
+    coin_sets = np.asarray(coin_sets, dtype=np.float32)
+    B = coin_sets.shape[0]
+    N = len(parents)
+    lg = np.ascontiguousarray(np.broadcast_to(logits, (B,) + logits.shape))
+    qq = np.ascontiguousarray(np.broadcast_to(q, (B,) + q.shape))
+    tk = np.ascontiguousarray(np.broadcast_to(np.asarray(tokens, np.int32), (B, N)))
+    pa = np.ascontiguousarray(np.broadcast_to(np.asarray(parents, np.int32), (B, N)))
+    res = oracle.verify_tree_mss(lg, dtype, qq, tk, pa, coin_sets, np.full(B, T, np.float32), D)
+    out = []
+    for b in range(B):
+        k = int(res["accept_len"][b])
+        out.append((k,) + tuple(int(t) for t in res["out_tokens"][b, : k + 1]) +
+                   tuple(int(nd) for nd in res["accepted_nodes"][b, :k]))
+    return out
+
+
+def mss_law(logits, dtype, q, tokens, parents, T, D):
+    """Exact law of the multi-step speculative sampling walk over lattice coins.
+
+    Node c is tested with coin c-1 and the final draw uses coin N-1.  Returns
+    {(accept_len, tok_0, ..., tok_k, node_0, ..., node_{k-1}): probability}.
+    """
+    parents = np.asarray(parents)
+    N = len(parents)
+    law = {}
+
+    def outcomes(cs):
+        return mss_outcomes(logits, dtype, q, tokens, parents, T, D, cs)
+
+    def walk(cur, fixed, mass):
+        fixed = fixed.copy()
+        for c in [c for c in range(cur + 1, N) if parents[c] == cur]:
+            def f(ks, c=c, fixed=fixed):
+                cs = np.repeat(fixed[None, :], len(ks), axis=0)
+                cs[:, c - 1] = coin(ks)
+                return [c in o[2 + o[0]:] for o in outcomes(cs)]
+            segs = segments(f)
+            acc = [(s, e) for s, e, v in segs if v]
+            p_acc = sum(e - s for s, e in acc) / LATTICE
+            if p_acc > 0.0:
+                sub = fixed.copy()
+                sub[c - 1] = coin(acc[0][0])
+                walk(c, sub, mass * p_acc)
+            rej = next((s for s, e, v in segs if not v), None)
+            if rej is None:
+                return
+            mass *= 1.0 - p_acc
+            fixed[c - 1] = coin(rej)
+            if mass == 0.0:
+                return
+
+        def g(ks):
+            cs = np.repeat(fixed[None, :], len(ks), axis=0)
+            cs[:, N - 1] = coin(ks)
+            return outcomes(cs)
+        for s, e, v in segments(g):
+            law[v] = law.get(v, 0.0) + mass * (e - s) / LATTICE
+
+    walk(0, coin(np.zeros(N, dtype=np.int64)), 1.0)
+    return law

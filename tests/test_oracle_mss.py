@@ -1,0 +1,305 @@
+"""Pins of the oracle's token-tree verify by multi-step speculative sampling (CPU only).
+
+zdszero spec_origins, SpecInfer: the children of a node are tested in turn with the
+rule min(1, p(x)/q(x)); after a rejection the node's target distribution becomes the
+residual norm(max(0, p - q)) and the next sibling is tested against it; the page states
+that the target distribution is kept.  Reading: q is the node's draft row, shared by its
+children, which are independent draws from it; node c uses coin c-1, the final draw
+coin N-1.
+
+Pins (none re-types the oracle's loop):
+  - exact law over coins and over the drafted children (enumerated), on a toy language
+    model whose rows depend on the token path: the first emitted token follows the root's
+    target row, and each later token, given the tokens before it on an accepted path,
+    follows that path's target row;
+  - a chain-shaped tree equals the chain verify (another code path) on the same coins;
+  - a chain-shaped tree with one-hot draft rows equals the target-only tree walk
+    (another code path): with q = one-hot(x) the residual zeroes x and renormalises;
+  - hand-worked cases; q = p never rejects; invalid inputs.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+import lawengine as le
+import oracle
+from lossless_rejection_sampling_verify_amd import workloads as wl
+
+BAND = 1e-6
+TOL_LAW = 3e-6
+
+
+def softmax64(x, T=1.0):
+    z = np.asarray(x, np.float64) / T
+    z = z - z.max(-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(-1, keepdims=True)
+
+
+def run(logits, q, tokens, parents, coins, T=1.0, D=None, dtype="f32"):
+    logits = np.asarray(logits, np.float32)[None]
+    q = np.asarray(q, np.float32)[None]
+    N = len(parents)
+    D = N - 1 if D is None else D
+    r = oracle.verify_tree_mss(logits, dtype, q, np.asarray(tokens, np.int32)[None],
+                               np.asarray(parents, np.int32)[None],
+                               np.asarray(coins, np.float32)[None], np.array([T], np.float32), D)
+    k = int(r["accept_len"][0])
+    return k, list(r["out_tokens"][0, : k + 1]), list(r["accepted_nodes"][0, :max(k, 0)]), r
+
+
+# ---------------------------------------------------------------------------------------
+# exact law on a toy language model
+
+class ToyLM:
+    """Target and draft rows that depend on the whole token path (so two siblings with the
+    same token see the same rows, as a real model would)."""
+
+    def __init__(self, V, seed, T):
+        self.V, self.T = V, T
+        self.rng = np.random.default_rng(seed)
+        self.tl, self.dl = {}, {}
+
+    def rows(self, path):
+        path = tuple(path)
+        if path not in self.tl:
+            self.tl[path] = (self.rng.standard_normal(self.V) * 1.5).astype(np.float32)
+            self.dl[path] = self.tl[path] + self.rng.standard_normal(self.V).astype(np.float32)
+        return self.tl[path], softmax64(self.dl[path], self.T).astype(np.float32)
+
+    def p(self, path):
+        return softmax64(self.rows(path)[0], self.T)
+
+
+def _paths(parents, tokens):
+    paths = [()]
+    for c in range(1, len(parents)):
+        paths.append(paths[parents[c]] + (int(tokens[c]),))
+    return paths
+
+
+def law_over_drafts(lm, parents, D):
+    """Mixture over every assignment of child tokens (each child an independent draw from
+    its parent's draft row) of the exact law over coins."""
+    parents = np.asarray(parents)
+    N, V = len(parents), lm.V
+    total, wsum = {}, 0.0
+    for assign in itertools.product(range(V), repeat=N - 1):
+        tokens = np.array((0,) + assign, np.int32)
+        paths = _paths(parents, tokens)
+        weight = 1.0
+        for c in range(1, N):
+            weight *= float(lm.rows(paths[parents[c]])[1][tokens[c]])
+        if weight == 0.0:
+            continue
+        wsum += weight
+        logits = np.stack([lm.rows(pt)[0] for pt in paths])
+        q = np.stack([lm.rows(pt)[1] for pt in paths])
+        for out, pr in le.mss_law(logits, "f32", q, tokens, parents, lm.T, D).items():
+            total[out] = total.get(out, 0.0) + weight * pr
+    # the fp32 draft rows sum to 1 only up to rounding: normalise the mixture weights
+    return {out: pr / wsum for out, pr in total.items()}
+
+
+@pytest.mark.parametrize("seed,T,parents", [
+    (0, 1.0, [-1, 0, 0, 1, 1, 2]),
+    (1, 0.7, [-1, 0, 0, 0, 1]),
+    (2, 1.0, [-1, 0, 1, 1, 0]),
+])
+def test_walk_emits_target_law_over_coins_and_drafts(seed, T, parents):
+    V = 3
+    lm = ToyLM(V, seed, T)
+    D = max(len(_paths(parents, np.zeros(len(parents), np.int32))[c]) for c in range(len(parents)))
+    law = law_over_drafts(lm, parents, D)
+    assert abs(sum(law.values()) - 1.0) < 1e-9
+    # first token ~ the root's target row
+    first = np.zeros(V)
+    for out, pr in law.items():
+        first[out[1]] += pr
+    np.testing.assert_allclose(first, lm.p(()), atol=TOL_LAW)
+    # every later token on an accepted path ~ the target row of the path so far
+    for depth in range(1, D + 1):
+        joint, cond = {}, {}
+        for out, pr in law.items():
+            if out[0] >= depth:
+                prefix = tuple(out[1: 1 + depth])
+                cond[prefix] = cond.get(prefix, 0.0) + pr
+                joint[prefix + (out[1 + depth],)] = joint.get(prefix + (out[1 + depth],), 0.0) + pr
+        assert cond, "no accepted path of this depth"
+        for prefix, pm in cond.items():
+            want = pm * lm.p(prefix)
+            got = np.array([joint.get(prefix + (y,), 0.0) for y in range(V)])
+            np.testing.assert_allclose(got, want, atol=TOL_LAW)
+
+
+def test_duplicate_siblings_with_one_hot_draft():
+    """Both root children carry token x and q = one-hot(x): the first test accepts with
+    probability p(x); after a rejection x has no residual mass, so the second sibling is
+    always rejected and the final draw follows p with x removed."""
+    lg = np.array([[0.3, -0.2, 1.1, 0.0], [0, 0, 0, 0], [0, 0, 0, 0]], np.float32)
+    x = 2
+    q = np.zeros((3, 4), np.float32)
+    q[0, x] = 1.0
+    q[1:] = 0.25
+    law = le.mss_law(lg, "f32", q, [0, x, x], [-1, 0, 0], 1.0, 1)
+    p = softmax64(lg[0])
+    acc1 = sum(pr for o, pr in law.items() if o[0] == 1 and o[3] == 1)
+    acc2 = sum(pr for o, pr in law.items() if o[0] == 1 and o[3] == 2)
+    assert abs(acc1 - p[x]) < TOL_LAW and acc2 == 0.0
+    rest = np.zeros(4)
+    for o, pr in law.items():
+        if o[0] == 0:
+            rest[o[1]] += pr
+    want = p.copy()
+    want[x] = 0.0
+    np.testing.assert_allclose(rest, want, atol=TOL_LAW)
+
+
+# ---------------------------------------------------------------------------------------
+# equal to other code paths on chain-shaped trees
+
+@pytest.mark.parametrize("seed,T", [(0, 1.0), (1, 0.7)])
+def test_chain_shaped_tree_equals_chain_verify(seed, T):
+    c = wl.make_chain(2, seed=seed, B=48, G=4, V=400, T=T)
+    N = c.G + 1
+    parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), (c.B, 1))
+    tokens = np.concatenate([np.zeros((c.B, 1), np.int32), c.draft_tokens], axis=1)
+    q = np.concatenate([c.draft_probs, np.full((c.B, 1, c.V), 1.0 / c.V, np.float32)], axis=1)
+    m = oracle.verify_tree_mss(c.logits, c.dtype, q, tokens, parents, c.coins, c.temperature, c.G)
+    ch = oracle.verify_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins,
+                             c.temperature)
+    far = (m["margin"] > BAND) & (ch["margin"] > BAND)
+    assert far.sum() > 30
+    np.testing.assert_array_equal(m["accept_len"][far], ch["accept_len"][far])
+    np.testing.assert_array_equal(m["out_tokens"][far], ch["out_tokens"][far])
+    for b in np.nonzero(far)[0]:
+        k = m["accept_len"][b]
+        assert list(m["accepted_nodes"][b, :k]) == list(range(1, k + 1))
+    np.testing.assert_allclose(m["probs"][far], ch["probs"][far], rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_chain_shaped_one_hot_tree_equals_target_only_walk(seed):
+    t = wl.make_tree(4, seed=seed, B=40, N=5, V=300, D=4, dtype="f32")
+    parents = np.tile(np.arange(-1, 4, dtype=np.int32), (t.B, 1))
+    tokens = np.random.default_rng(seed).integers(0, t.V, (t.B, 5)).astype(np.int32)
+    q = np.zeros((t.B, 5, t.V), np.float32)
+    for b in range(t.B):
+        for j in range(4):
+            q[b, j, tokens[b, j + 1]] = 1.0
+    q[:, 4] = 1.0 / t.V
+    coins = wl.draw_coins(np.random.default_rng(100 + seed), (t.B, 5))
+    # the target-only walk takes coin d at depth d and coin D last: the same array here
+    m = oracle.verify_tree_mss(t.logits, t.dtype, q, tokens, parents, coins, t.temperature, 4)
+    g = oracle.verify_tree(t.logits, t.dtype, tokens, parents, coins, t.temperature, 4,
+                           oracle.TREE_SAMPLING)
+    far = (m["margin"] > BAND) & (g["margin"] > BAND)
+    assert far.sum() > 25
+    for key in ("accept_len", "out_tokens", "accepted_nodes"):
+        np.testing.assert_array_equal(m[key][far], g[key][far])
+
+
+# ---------------------------------------------------------------------------------------
+# hand-worked cases and special cases
+
+# root row: p = (1/2, 1/4, 1/4) from logits (log 2, 0, 0) up to fp32 rounding of log 2;
+# q_root = (1/4, 1/4, 1/2); two leaf children; node 3's row is uniform.
+P_LOGITS = [np.log(2.0), 0.0, 0.0]
+UNIFORM = [0.0, 0.0, 0.0]
+Q_ROOT = [0.25, 0.25, 0.5]
+
+
+def _hand(tok1, tok2, coins):
+    lg = np.array([P_LOGITS, UNIFORM, UNIFORM], np.float32)
+    q = np.array([Q_ROOT, [1 / 3] * 3, [1 / 3] * 3], np.float32)
+    return run(lg, q, [0, tok1, tok2], [-1, 0, 0], coins)
+
+
+def test_hand_first_child_accepted():
+    # node 1 (token 2): ratio p(2)/q(2) = 0.25/0.5 = 0.5 >= 0.3 -> accepted; the bonus comes
+    # from node 1's uniform row with coin 0.5 -> token 1
+    k, out, nodes, _ = _hand(2, 0, [0.3, 0.9, 0.5])
+    assert (k, out, nodes) == (1, [2, 1], [1])
+
+
+def test_hand_second_child_accepted_after_residual():
+    # node 1 (token 2): 0.7 > 0.5 -> rejected; residual max(0, p - q) = (1/4, 0, 0) -> (1, 0, 0);
+    # node 2 (token 0): ratio 1 / (1/4) = 4 -> accepted whatever its coin; bonus from node 2's
+    # uniform row with coin 0.9 -> token 2
+    k, out, nodes, _ = _hand(2, 0, [0.7, 1.0, 0.9])
+    assert (k, out, nodes) == (1, [0, 2], [2])
+
+
+def test_hand_both_rejected_final_draw_from_residual():
+    # node 1 rejected as above; node 2 (token 1): residual mass at 1 is 0 -> ratio 0 ->
+    # rejected; residual max(0, (1,0,0) - q) = (3/4, 0, 0) -> the final draw is token 0
+    k, out, nodes, _ = _hand(2, 1, [0.7, 0.01, 0.99])
+    assert (k, out, nodes) == (0, [0], [])
+
+
+def test_q_equal_p_never_rejects():
+    """With q = p at every node (up to fp32 rounding) the first child is always accepted,
+    outside the near-tie band: the walk follows first children down to a leaf."""
+    t = wl.make_tree_mss(4, seed=5, B=24, N=20, V=200, D=4, dtype="f32")
+    q = softmax64(wl.logits_as_f32(t.logits, t.dtype), 1.0).astype(np.float32)
+    r = oracle.verify_tree_mss(t.logits, t.dtype, q, t.node_tokens, t.parents, t.coins,
+                               t.temperature, t.D)
+    far = r["margin"] > BAND
+    assert far.sum() > 10
+    for b in np.nonzero(far)[0]:
+        par = t.parents[b]
+        cur, want = 0, []
+        while True:
+            kids = [c for c in range(cur + 1, t.N) if par[c] == cur]
+            if not kids:
+                break
+            cur = kids[0]
+            want.append(cur)
+        assert list(r["accepted_nodes"][b, : r["accept_len"][b]]) == want
+
+
+def test_zero_draft_mass_accepts_and_zero_target_mass_rejects():
+    lg = np.array([[0.0, 1.0, -np.inf, 0.5], [0, 0, 0, 0], [0, 0, 0, 0]], np.float32)
+    q = np.array([[0.0, 0.5, 0.5, 0.0], [0.25] * 4, [0.25] * 4], np.float32)
+    # token 0: q = 0 < p -> accepted with any coin
+    k, out, nodes, _ = run(lg, q, [0, 0, 1], [-1, 0, 0], [1.0, 1.0, 0.5])
+    assert (k, nodes, out[0]) == (1, [1], 0)
+    # token 2: p = 0 < q -> rejected with any coin; the residual then tests token 1
+    k, out, nodes, _ = run(lg, q, [0, 2, 1], [-1, 0, 0], [1e-7, 1e-7, 0.5])
+    assert nodes == [2] and out[0] == 1
+
+
+def test_residual_without_mass_falls_back_to_target_row():
+    """q given as 2p (not renormalised, used as given): after a rejection the residual has
+    no mass; the remaining siblings are not tested and the final token is the inverse CDF
+    of p at the final coin."""
+    lg = np.array([[0.2, -0.4, 0.9], [0, 0, 0], [0, 0, 0]], np.float32)
+    p = softmax64(lg[0])
+    q = np.array([2 * p, [1 / 3] * 3, [1 / 3] * 3], np.float32)
+    u = 0.55
+    k, out, nodes, _ = run(lg, q, [0, 1, 2], [-1, 0, 0], [0.9, 1e-7, u])
+    assert k == 0
+    assert out[0] == int(np.searchsorted(np.cumsum(p), u * p.sum()))
+
+
+@pytest.mark.parametrize("what", ["parent", "token", "temperature", "coin", "q"])
+def test_invalid_requests_are_flagged(what):
+    t = wl.make_tree_mss(4, seed=2, B=3, N=8, V=50, D=3, dtype="f32")
+    par, tok, coins, T, q = (t.parents.copy(), t.node_tokens.copy(), t.coins.copy(),
+                             t.temperature.copy(), t.draft_probs.copy())
+    if what == "parent":
+        par[1, 3] = 5
+    elif what == "token":
+        tok[1, 4] = t.V
+    elif what == "temperature":
+        T[1] = 0.0
+    elif what == "coin":
+        coins[1, 0] = 0.0
+    else:
+        q[1, t.parents[1, 2], t.node_tokens[1, 2]] = np.nan
+    r = oracle.verify_tree_mss(t.logits, t.dtype, q, tok, par, coins, T, t.D)
+    assert r["accept_len"][1] == -1 and (r["out_tokens"][1] == -1).all()
+    assert r["accept_len"][0] >= 0 and r["accept_len"][2] >= 0

@@ -21,6 +21,7 @@ import test_oracle_tree_greedy as tg
 import test_oracle_tree_mask as tm
 import test_oracle_commit_kv as ck
 import test_oracle_filtered as tf
+import test_oracle_mss as ms
 
 SRC = open(oracle.SRC).read()
 
@@ -76,6 +77,17 @@ MUTANTS = [
      "if (valid && d <= k) node = d == 0 ? -1 : nodes[d - 1];"),
     ("commit writes one row past the path", "if (valid && d <= k) node = d == 0 ? 0 : nodes[d - 1];",
      "if (valid && d <= k + 1 && d <= D) node = d == 0 ? 0 : nodes[d - 1 < D ? d - 1 : 0];"),
+    ("MSS residual sign flipped", "double dv = w[v] - (double)qc[v];",
+     "double dv = (double)qc[v] - w[v];"),
+    ("MSS residual not renormalised", "for (int v = 0; v < V; ++v) w[v] /= S;", ""),
+    ("MSS siblings tested against the original row", "double ratio = w[x] / qx;",
+     "double ratio = row_prob(r, x, m, Z, T) / qx;"),
+    ("MSS one coin for every sibling", "double u = (double)coins[c - 1];",
+     "double u = (double)coins[0];"),
+    ("MSS final draw from the target row",
+     "int y = draw_inverse_cdf(w, V, (double)coins[N - 1], margin);",
+     "for (int v = 0; v < V; ++v) w[v] = row_prob(r, v, m, Z, T);\n"
+     "    int y = draw_inverse_cdf(w, V, (double)coins[N - 1], margin);"),
 ]
 
 
@@ -108,6 +120,11 @@ def _pins():
     for case in tf.GOLDEN["cases"]:
         yield lambda case=case: tf.test_golden(case)
     yield lambda: tf.test_filtered_round_emits_filtered_target_law(2, 4, 0.8, 0.7)
+    yield ms.test_hand_first_child_accepted
+    yield ms.test_hand_second_child_accepted_after_residual
+    yield ms.test_hand_both_rejected_final_draw_from_residual
+    yield lambda: ms.test_chain_shaped_tree_equals_chain_verify(0, 1.0)
+    yield lambda: ms.test_walk_emits_target_law_over_coins_and_drafts(0, 1.0, [-1, 0, 0, 1, 1, 2])
 
 
 @pytest.mark.parametrize("name,orig,mutation", MUTANTS, ids=[m[0] for m in MUTANTS])
