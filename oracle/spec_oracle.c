@@ -471,7 +471,9 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
  * from (shared by all of them; used as given, as in the chain); the siblings are tried in
  * ascending node id; node c is tested with coins[c - 1] and the final draw uses
  * coins[N - 1]; if the updated distribution has no positive mass the remaining siblings
- * are not tested and the final token is drawn from the node's target row.  The output
+ * are not tested and the final token is drawn from the node's target row; a request is
+ * invalid when a row the walk reaches has no finite logit (rows off the walk are never
+ * read, so they are not checked).  The output
  * follows the target law when the children of each node are independent draws from
  * that node's draft row. */
 static void tree_mss_one(const void* logits, int dtype, const float* q, const int32_t* tok,
@@ -496,25 +498,19 @@ static void tree_mss_one(const void* logits, int dtype, const float* q, const in
     }
     for (int c = 0; c < N && valid; ++c)
         if (!coin_ok(coins[c])) valid = 0;
-    for (int j = 0; j < N && valid; ++j)
-        if (row_max(row_of(logits, dtype, b * (size_t)N + (size_t)j, V)) == -INFINITY) valid = 0;
     *margin = INFINITY;
-    if (!valid) {
-        *accept_len = -1;
-        for (int d = 0; d <= D; ++d) out[d] = -1;
-        for (int d = 0; d < D; ++d) nodes[d] = -1;
-        if (probs)
-            for (int d = 0; d <= D; ++d) probs[d] = 0.0;
-        return;
-    }
 
     double T = (double)temperature;
     int cur = 0, d = 0;
     double m = 0.0, Z = 0.0;
-    for (;;) {
+    for (; valid;) {
         Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
         const float* qc = q + (size_t)cur * V;
         m = row_max(r);
+        if (m == -INFINITY) { /* a row the walk reaches has no finite logit */
+            valid = 0;
+            break;
+        }
         Z = row_partition(r, m, T);
         for (int x = 0; x < V; ++x) w[x] = row_prob(r, x, m, Z, T); /* current distribution */
         int chosen = -1;
@@ -555,6 +551,14 @@ static void tree_mss_one(const void* logits, int dtype, const float* q, const in
         if (probs) probs[d] = row_prob(r, tok[chosen], m, Z, T);
         cur = chosen;
         ++d;
+    }
+    if (!valid) {
+        *accept_len = -1;
+        for (int e = 0; e <= D; ++e) out[e] = -1;
+        for (int e = 0; e < D; ++e) nodes[e] = -1;
+        if (probs)
+            for (int e = 0; e <= D; ++e) probs[e] = 0.0;
+        return;
     }
 
     Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);

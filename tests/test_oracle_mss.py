@@ -285,6 +285,19 @@ def test_residual_without_mass_falls_back_to_target_row():
     assert out[0] == int(np.searchsorted(np.cumsum(p), u * p.sum()))
 
 
+def test_only_rows_on_the_walk_are_checked():
+    """A row with no finite logit makes the request invalid only when the walk reaches it."""
+    lg = np.array([[2.0, 0.0, 0.0], [0.0, 0.0, 0.0], [-np.inf] * 3], np.float32)
+    q = np.array([[0.5, 0.25, 0.25], [1 / 3] * 3, [1 / 3] * 3], np.float32)
+    # node 1 (token 0) accepted with coin 1e-7: node 2's row is never reached
+    k, out, nodes, _ = run(lg, q, [0, 0, 1], [-1, 0, 0], [1e-7, 0.5, 0.5])
+    assert (k, nodes) == (1, [1])
+    # node 1 holds token 2 after the bad row: swap the rows so the accepted child's row is bad
+    lg2 = lg[[0, 2, 1]]
+    k, out, nodes, r = run(lg2, q, [0, 0, 1], [-1, 0, 0], [1e-7, 0.5, 0.5])
+    assert k == -1 and (r["out_tokens"] == -1).all() and (r["accepted_nodes"] == -1).all()
+
+
 @pytest.mark.parametrize("what", ["parent", "token", "temperature", "coin", "q"])
 def test_invalid_requests_are_flagged(what):
     t = wl.make_tree_mss(4, seed=2, B=3, N=8, V=50, D=3, dtype="f32")
