@@ -75,7 +75,8 @@ enum {
 
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };                   /* target-logit dtype */
 enum { SPEC_TREE_GREEDY = 0, SPEC_TREE_SAMPLING = 1 };  /* spec_verify_tree mode */
-enum { SPEC_OP_GREEDY = 0, SPEC_OP_CHAIN = 1, SPEC_OP_TREE = 2, SPEC_OP_CHAIN_FILTERED = 3 };
+enum { SPEC_OP_GREEDY = 0, SPEC_OP_CHAIN = 1, SPEC_OP_TREE = 2, SPEC_OP_CHAIN_FILTERED = 3,
+       SPEC_OP_TREE_MSS = 4 };
 
 #define SPEC_MAX_G 64     /* drafted positions per request (chain) */
 #define SPEC_MAX_N 1024   /* tree nodes per request, root included */
@@ -172,6 +173,35 @@ int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
                      float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
                      int32_t* accepted_nodes, float* probs_out, void* workspace,
                      size_t ws_bytes, void* stream);
+
+/* Token-tree verify by multi-step speculative sampling with draft distributions
+ * (spec_origins, "SpecInfer": the children of a node are tested in turn with
+ * min(1, p(x)/q(x)); after a rejection the node's distribution becomes the residual
+ * norm(max(0, p - q)) and the next sibling is tested against it).
+ *   logits      [B][N][V] row j = target logits of the token after node j;
+ *   draft_probs [B][N][V] fp32, row j = the draft distribution the children of node j were
+ *               drawn from (shared by all of them; used as given).  The result follows the
+ *               target law when the children are independent draws from that row
+ *               (duplicate tokens are then allowed);
+ *   node_tokens, parents [B][N] as spec_verify_tree;
+ *   coins       [B][N]    coins[b][c-1] tests node c; coins[b][N-1] drives the final draw;
+ *   temperature [B];
+ *   D           maximum depth, 1 <= D <= SPEC_MAX_N.
+ * From cur = root, children are tried in ascending node id; the first accepted child
+ * becomes cur.  When every child of cur is rejected, the final token is drawn from the
+ * last residual.  At a leaf, or when a residual has no mass left (remaining siblings
+ * untried), the final token is drawn from p_cur.
+ * Only the rows the walk reaches are read.  A request is invalid (-1) when such a row
+ * has no finite logit, or when parents, tokens, temperature, coins, depth or the
+ * q(token) of any child are bad.
+ * Workspace: spec_workspace_bytes(SPEC_OP_TREE_MSS, B, N, V).  Outputs and probs_out as
+ * spec_verify_tree sampling mode. */
+int spec_verify_tree_mss(const void* logits, int dtype, const float* draft_probs,
+                         const int32_t* node_tokens, const int32_t* parents,
+                         const float* coins, const float* temperature, int B, int N, int V,
+                         int D, int32_t* accept_len, int32_t* out_tokens,
+                         int32_t* accepted_nodes, float* probs_out, void* workspace,
+                         size_t ws_bytes, void* stream);
 
 /* Tree attention mask and positions (spec_origins, "SpecInfer": the token tree is
  * flattened into one sequence and each node attends only to its ancestors, so one target

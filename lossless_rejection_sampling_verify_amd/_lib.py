@@ -17,7 +17,7 @@ SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_DTYPE = 0, -1, -2, -3
 SPEC_ERR_PARAM, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = -4, -5, -6
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_TREE_GREEDY, SPEC_TREE_SAMPLING = 0, 1
-SPEC_OP_GREEDY, SPEC_OP_CHAIN, SPEC_OP_TREE, SPEC_OP_CHAIN_FILTERED = 0, 1, 2, 3
+SPEC_OP_GREEDY, SPEC_OP_CHAIN, SPEC_OP_TREE, SPEC_OP_CHAIN_FILTERED, SPEC_OP_TREE_MSS = 0, 1, 2, 3, 4
 SPEC_MAX_G, SPEC_MAX_N = 64, 1024
 
 _lib = None
@@ -58,6 +58,9 @@ def lib():
         L.spec_verify_chain_filtered.argtypes = [vp, vp, ip, vp, vp, vp, vp, vp, ip, ip, ip, vp, vp,
                                                  vp, vp, sz, vp]
         L.spec_verify_chain_filtered.restype = ip
+        L.spec_verify_tree_mss.argtypes = [vp, ip, vp, vp, vp, vp, vp, ip, ip, ip, ip, vp, vp, vp,
+                                           vp, vp, sz, vp]
+        L.spec_verify_tree_mss.restype = ip
         L.spec_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp, vp]
         L.spec_tree_mask.restype = ip
         L.spec_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, sz, vp, vp]

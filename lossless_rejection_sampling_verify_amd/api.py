@@ -201,6 +201,48 @@ def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: t
     return acc, toks, nodes, probs
 
 
+def spec_verify_tree_mss(logits: torch.Tensor, draft_probs: torch.Tensor,
+                         node_tokens: torch.Tensor, parents: torch.Tensor, coins: torch.Tensor,
+                         temperature: torch.Tensor, D: int, *, want_probs: bool = False, ws=None,
+                         stream=None, out=None):
+    """Token-tree verify by multi-step speculative sampling.  logits [B][N][V],
+    draft_probs [B][N][V] fp32 (row j: the distribution node j's children were drawn from),
+    node_tokens/parents [B][N] int32, coins [B][N] fp32 (coins[b][c-1] tests node c,
+    coins[b][N-1] the final draw), temperature [B] fp32.
+
+    Returns (accept_len [B], out_tokens [B][D+1], accepted_nodes [B][D], probs or None)."""
+    _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
+    _check(draft_probs, "draft_probs", torch.float32, 3)
+    _check(node_tokens, "node_tokens", torch.int32, 2)
+    _check(parents, "parents", torch.int32, 2)
+    _check(coins, "coins", torch.float32, 2)
+    _check(temperature, "temperature", torch.float32, 1)
+    B, N, V = logits.shape
+    if draft_probs.shape != (B, N, V):
+        raise ValueError("draft_probs must be [B][N][V]")
+    if node_tokens.shape != (B, N) or parents.shape != (B, N) or coins.shape != (B, N):
+        raise ValueError("node_tokens / parents / coins must be [B][N]")
+    if temperature.shape != (B,):
+        raise ValueError("temperature must be [B]")
+    dev = logits.device
+    ws = workspace(L.SPEC_OP_TREE_MSS, B, N, V, dev) if ws is None else ws
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
+        nodes = torch.empty(B, D, dtype=torch.int32, device=dev)
+        probs = torch.empty(B, D + 1, dtype=torch.float32, device=dev) if want_probs else None
+    else:
+        acc, toks, nodes, probs = out
+    rc = L.lib().spec_verify_tree_mss(_ptr(logits), _logit_dtype(logits), _ptr(draft_probs),
+                                      _ptr(node_tokens), _ptr(parents), _ptr(coins),
+                                      _ptr(temperature), B, N, V, D, _ptr(acc), _ptr(toks),
+                                      _ptr(nodes), _ptr(probs), _ptr(ws), ws.numel(),
+                                      _stream(dev, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_verify_tree_mss", rc)
+    return acc, toks, nodes, probs
+
+
 def spec_tree_mask(parents: torch.Tensor, base_pos=None, *, want_positions: bool = True,
                    stream=None, out=None):
     """Tree attention mask.  parents [B][N] int32, base_pos [B] int32 or None.

@@ -66,7 +66,7 @@ enum DrawKind { kDrawNone = -1, kDrawResidual = 0, kDrawTarget = 1 };
 struct alignas(16) DrawState {
     int kind;    // kDrawNone: nothing to draw (invalid request, greedy tree)
     int row;     // logit row b * R + k (chain) or b * N + cur (tree)
-    int qrow;    // kDrawResidual: q row b * G + k
+    int qrow;    // kDrawResidual: q row b * G + k (chain), b * N + cur (tree with q)
     int out;     // index of the drawn token in out_tokens / probs_out
     int coin;    // index of its coin in coins
     int nexcl;   // tree: distinct tokens of the children tried last, in excl[b][...]
@@ -78,6 +78,7 @@ struct alignas(16) DrawState {
     uint32_t thq;  // filtered residual: the same for the draft row qrow of draft_logits
     float Mq;      // filtered residual: draft row max
     float invZq;   // filtered residual: 1 / kept draft mass
+    float cq;      // kDrawResidual: weights max(0, p - cq * q) (1 for the chain)
 };
 
 // Top-k / top-p result of one logit row (filtered calls).
@@ -559,6 +560,7 @@ __device__ DrawState chain_accept(const KArgs& a, int b, bool emit, Smem& sm, Re
             st.out = b * R + k;
             st.coin = b * R + G;
             st.nexcl = 0;
+            st.cq = 1.f;
             st.M = sm.M[k];
             st.Z = sm.Z[k];
             st.invZ = (float)(1.0 / sm.Z[k]);
@@ -658,24 +660,25 @@ __device__ void tree_row_stats(const KArgs& a, int b, bool sampling, double Td, 
 // Depth of every node by pointer jumping (parents[i] < i, so every chain of parents ends
 // at the root): ceil(log2 N) rounds.  par, anc and dep are LDS arrays of N entries; the
 // parent array must already be validated.  Block-wide.
+template <int kThreads = kBlock>
 __device__ void tree_depths(const int* par, int N, int* anc, int* dep) {
     const int tid = threadIdx.x;
-    for (int i = tid; i < N; i += kBlock) {
+    for (int i = tid; i < N; i += kThreads) {
         anc[i] = i == 0 ? 0 : par[i];
         dep[i] = i == 0 ? 0 : 1;
     }
     for (int r = 1; r < N; r <<= 1) {
         __syncthreads();
-        int nd[SPEC_MAX_N / kBlock], na[SPEC_MAX_N / kBlock];
+        int nd[SPEC_MAX_N / kThreads], na[SPEC_MAX_N / kThreads];
         int c = 0;
-        for (int i = tid; i < N; i += kBlock, ++c) {
+        for (int i = tid; i < N; i += kThreads, ++c) {
             const int an = anc[i];
             nd[c] = dep[i] + (an == i ? 0 : dep[an]);
             na[c] = anc[an];
         }
         __syncthreads();
         c = 0;
-        for (int i = tid; i < N; i += kBlock, ++c) {
+        for (int i = tid; i < N; i += kThreads, ++c) {
             if (anc[i] != i) {
                 dep[i] = nd[c];
                 anc[i] = na[c];
@@ -860,6 +863,350 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
     for (int e = d + tid; e < D; e += kBlock) nodes[e] = -1;
 }
 
+// ---------------------------------------------------------------------------------------
+// k_mss_walk: a token tree verified by multi-step speculative sampling with draft rows.
+// One workgroup of kWalk threads per request walks the tree and reads only the rows it
+// reaches.
+//
+// At node cur, one pass over the target row gives its max M and normaliser Z.  The
+// children are tested in ascending node id.  After r rejections the node's distribution
+// is p^(r) = max(0, p - c_r q) / N_r, with c_0 = 0 and N_0 = 1.  On the next rejection
+// c_{r+1} = c_r + N_r and N_{r+1} = sum_v max(0, p_v - c_{r+1} q_v).  This works because
+// all children share one draft row q: the repeated residual norm(max(0, p^(r) - q))
+// collapses to one coefficient on q (where p - c_r q <= 0, the next residual is 0 too).
+// Each rejection therefore costs one pass over (target row, draft row), and no vector is
+// kept.  c is rounded to fp32 once per step and that value is used everywhere.
+//
+// Child x is accepted iff p^(r)(x) > 0 and its coin <= p^(r)(x) / q(x); when q(x) = 0,
+// iff p^(r)(x) > 0.  When every child is rejected, k_mass and k_draw draw the last token
+// from max(0, p - c_R q).  They draw from plain p at a leaf, or when a residual has no
+// mass left.
+
+constexpr int kWalk = 1024;
+constexpr int kWalkWaves = kWalk / 64;
+
+struct MssSmem {
+    int par[SPEC_MAX_N];
+    int tok[SPEC_MAX_N];
+    union {
+        struct {  // validation: pointer-jumping state
+            int anc[SPEC_MAX_N];
+            int dep[SPEC_MAX_N];
+        };
+        int kids[SPEC_MAX_N];  // the walk: children of the current node
+    };
+    float qx[SPEC_MAX_N];     // q_parent(token of node c), by node id
+    int path[SPEC_MAX_N];     // accepted nodes, by depth
+    float pathp[SPEC_MAX_N];  // their target probabilities
+    float rm[kWalkWaves];
+    double rz[kWalkWaves];
+    int wcnt[kWalkWaves];
+    int flag;
+    double px;
+};
+
+// Block-wide max / sum over the kWalk threads (every thread gets the same bits).
+__device__ inline float walk_max(float v, MssSmem& sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max(v);
+    __syncthreads();  // the previous reduction has read sm.rm
+    if (lane == 0) sm.rm[wave] = v;
+    __syncthreads();
+    float r = sm.rm[0];
+    for (int w = 1; w < kWalkWaves; ++w) r = fmaxf(r, sm.rm[w]);
+    return r;
+}
+
+__device__ inline double walk_sum(double v, MssSmem& sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) sm.rz[wave] = v;
+    __syncthreads();
+    double r = sm.rz[0];
+    for (int w = 1; w < kWalkWaves; ++w) r += sm.rz[w];
+    return r;
+}
+
+// Max and normaliser of one target row: per thread an online (m, z) over batches of
+// kUnroll 16-byte vectors (fp32 batch sums added in fp64), then a block reduction.
+template <typename T>
+__device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSmem& sm,
+                               float& M_out, double& Z_out) {
+    const int tid = threadIdx.x;
+    constexpr int kVec = Ld<T>::kVec;
+    float m = -INFINITY;
+    double z = 0.0;
+    int done = 0;
+    if (((uintptr_t)rowp) % 16 == 0) {
+        const int nv = V / kVec;
+        const u32x4* rv = reinterpret_cast<const u32x4*>(rowp);
+        for (int i0 = 0; i0 < nv; i0 += kWalk * kUnroll) {
+            u32x4 r[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = i0 + u * kWalk + tid;
+                if (i < nv) r[u] = ld_stream(rv + i);
+            }
+            float l[kUnroll * kVec];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (i0 + u * kWalk + tid < nv) {
+                    Ld<T>::unpack(r[u], l + u * kVec);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) l[u * kVec + e] = -INFINITY;
+                }
+            }
+            float bm = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kUnroll * kVec; ++e) bm = fmaxf(bm, l[e]);
+            if (bm != -INFINITY) {
+                if (bm > m) {
+                    z = m == -INFINITY ? 0.0 : z * (double)ex2((m - bm) * s2);
+                    m = bm;
+                }
+                float bs = 0.f;
+#pragma unroll
+                for (int e = 0; e < kUnroll * kVec; ++e) bs += ex2((l[e] - m) * s2);
+                z += (double)bs;
+            }
+        }
+        done = nv * kVec;
+    }
+    for (int j0 = done; j0 < V; j0 += kWalk) {  // the tail, or an unaligned row
+        const int j = j0 + tid;
+        if (j < V) {
+            const float l = Ld<T>::one(rowp + j);
+            if (l != -INFINITY) {
+                if (l > m) {
+                    z = m == -INFINITY ? 0.0 : z * (double)ex2((m - l) * s2);
+                    m = l;
+                }
+                z += (double)ex2((l - m) * s2);
+            }
+        }
+    }
+    const float M = walk_max(m, sm);
+    const double term = m == -INFINITY ? 0.0 : z * exp(((double)m - (double)M) / Td);
+    M_out = M;
+    Z_out = walk_sum(term, sm);
+}
+
+// N(c) = sum_v max(0, p_v - c q_v) over one (target row, draft row) pair, with the draw
+// kernels' weight formula (p_v = exp2((l_v - M) * s2) * invZ in fp32).
+template <typename T>
+__device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float M, float s2,
+                                 float invZ, float cq, MssSmem& sm) {
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    int done = 0;
+    if (((uintptr_t)rowp) % (4 * sizeof(T)) == 0 && ((uintptr_t)qrow) % 16 == 0) {
+        const int nq = V / 4;
+        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
+        const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
+        for (int i0 = 0; i0 < nq; i0 += kWalk * kUnroll) {
+            typename Quad<T>::Raw lr[kUnroll];
+            u32x4 qr[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = i0 + u * kWalk + tid;
+                if (i < nq) {
+                    lr[u] = lq[i].raw;
+                    qr[u] = ld_stream(qq + i);
+                }
+            }
+            float bs = 0.f;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (i0 + u * kWalk + tid < nq) {
+                    float l[4];
+                    Quad<T>::unpack(lr[u], l);
+                    const float qv[4] = {__uint_as_float(qr[u].x), __uint_as_float(qr[u].y),
+                                         __uint_as_float(qr[u].z), __uint_as_float(qr[u].w)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bs += fmaxf(ex2((l[e] - M) * s2) * invZ - cq * qv[e], 0.f);
+                }
+            }
+            acc += (double)bs;
+        }
+        done = nq * 4;
+    }
+    for (int j0 = done; j0 < V; j0 += kWalk) {
+        const int j = j0 + tid;
+        if (j < V) {
+            const float p = ex2((Ld<T>::one(rowp + j) - M) * s2) * invZ;
+            acc += (double)fmaxf(p - cq * qrow[j], 0.f);
+        }
+    }
+    return walk_sum(acc, sm);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
+    __shared__ MssSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x;
+    const int N = a.R, V = a.V, D = a.D;
+    const int32_t* par_g = a.parents + (size_t)b * N;
+    const int32_t* tok_g = a.tokens + (size_t)b * N;
+    const float* coins = a.coins + (size_t)b * N;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    bool bad = false;
+    for (int i = tid; i < N; i += kWalk) {
+        const int p = par_g[i];
+        const int t = tok_g[i];
+        sm.par[i] = p;
+        sm.tok[i] = t;
+        if (i == 0) {
+            if (p != -1) bad = true;
+        } else {
+            if (p < 0 || p >= i) bad = true;
+            if (t < 0 || t >= V) bad = true;
+        }
+        const float u = coins[i];
+        if (!(u > 0.f && u <= 1.f)) bad = true;
+    }
+    const float Tf = a.temperature[b];
+    if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
+    const double Td = (double)Tf;
+    bad = __syncthreads_or(bad);
+    if (!bad) {  // depths, and q of every child's token under its parent's draft row
+        tree_depths<kWalk>(sm.par, N, sm.anc, sm.dep);
+        for (int i = tid; i < N; i += kWalk) {
+            if (sm.dep[i] > D) bad = true;
+            if (i > 0) {
+                const float q = a.q[((size_t)b * N + sm.par[i]) * V + sm.tok[i]];
+                sm.qx[i] = q;
+                if (!(q >= 0.f && isfinite(q))) bad = true;
+            }
+        }
+        bad = __syncthreads_or(bad);
+    }
+
+    const float s2 = kLog2e / Tf;
+    int cur = 0, d = 0;
+    int kind = kDrawTarget;
+    float cq = 0.f, M = 0.f;
+    double Z = 1.0;
+    while (!bad) {
+        const T* rowp = logits + ((size_t)b * N + cur) * V;
+        walk_row_stats<T>(rowp, V, s2, Td, sm, M, Z);
+        if (M == -INFINITY) {  // a row on the walk with no finite logit
+            bad = true;
+            break;
+        }
+        int count = 0;  // children of cur in ascending node id (ordered compaction)
+        for (int base = cur + 1; base < N; base += kWalk) {
+            const int c = base + tid;
+            const bool f = c < N && sm.par[c] == cur;
+            const unsigned long long m = __ballot(f);
+            if (lane == 0) sm.wcnt[wave] = __popcll(m);
+            __syncthreads();
+            int off = count, total = 0;
+            for (int w = 0; w < kWalkWaves; ++w) {
+                if (w < wave) off += sm.wcnt[w];
+                total += sm.wcnt[w];
+            }
+            if (f) sm.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = c;
+            __syncthreads();
+            count += total;
+        }
+        kind = kDrawTarget;
+        cq = 0.f;
+        if (count == 0) break;  // a leaf: the bonus from its own row
+        const float* qrow = a.q + ((size_t)b * N + cur) * V;
+        const float invZ = (float)(1.0 / Z);
+        double c = 0.0, Nr = 1.0;
+        int chosen = -1;
+        for (int j = 0; j < count; ++j) {
+            const int child = sm.kids[j];
+            if (tid == 0) {
+                const int x = sm.tok[child];
+                const double px = exp(((double)Ld<T>::one(rowp + x) - (double)M) / Td) / Z;
+                const double qx = (double)sm.qx[child];
+                double pr = px - c * qx;
+                pr = pr > 0.0 ? pr / Nr : 0.0;
+                const double u = (double)coins[child - 1];
+                sm.flag = qx > 0.0 ? (pr > 0.0 && u <= pr / qx) : pr > 0.0;
+                sm.px = px;
+            }
+            __syncthreads();
+            const bool accepted = sm.flag != 0;
+            const double px = sm.px;
+            __syncthreads();
+            if (accepted) {
+                chosen = child;
+                if (tid == 0) {
+                    sm.path[d] = child;
+                    sm.pathp[d] = (float)px;
+                }
+                break;
+            }
+            const double cn = (double)(float)(c + Nr);
+            if (j == count - 1) {  // every child rejected: the final residual
+                kind = kDrawResidual;
+                cq = (float)cn;
+                break;
+            }
+            const double Nn = walk_resid_sum<T>(rowp, qrow, V, M, s2, invZ, (float)cn, sm);
+            if (!(Nn > 0.0)) break;  // no residual mass left: draw from the target row
+            c = cn;
+            Nr = Nn;
+        }
+        if (chosen < 0) break;
+        cur = chosen;
+        ++d;
+    }
+    __syncthreads();  // the path is in LDS
+
+    int32_t* out = a.out_tokens + (size_t)b * (D + 1);
+    int32_t* nodes = a.accepted_nodes + (size_t)b * D;
+    float* probs = a.probs ? a.probs + (size_t)b * (D + 1) : nullptr;
+    if (bad) {
+        for (int e = tid; e <= D; e += kWalk) {
+            out[e] = -1;
+            if (e < D) nodes[e] = -1;
+            if (probs) probs[e] = 0.f;
+        }
+        if (tid == 0) {
+            a.accept_len[b] = -1;
+            DrawState st = {};
+            st.kind = kDrawNone;
+            a.dstate[b] = st;
+        }
+        return;
+    }
+    for (int e = tid; e <= D; e += kWalk) {  // slot d is written by the final draw
+        if (e < d) {
+            out[e] = sm.tok[sm.path[e]];
+            nodes[e] = sm.path[e];
+            if (probs) probs[e] = sm.pathp[e];
+        } else if (e > d) {
+            out[e] = -1;
+            if (probs) probs[e] = 0.f;
+        }
+        if (e >= d && e < D) nodes[e] = -1;
+    }
+    if (tid == 0) {
+        a.accept_len[b] = d;
+        DrawState st = {};
+        st.kind = kind;
+        st.row = b * N + cur;
+        st.qrow = b * N + cur;
+        st.out = b * (D + 1) + d;
+        st.coin = b * N + N - 1;
+        st.nexcl = 0;
+        st.cq = cq;
+        st.M = M;
+        st.Z = Z;
+        st.invZ = (float)(1.0 / Z);
+        st.T = Td;
+        a.dstate[b] = st;
+    }
+}
+
 // Field-wise copy of a draw state from global memory (keeps it in registers).
 __device__ inline DrawState load_state(const DrawState* p) {
     DrawState st;
@@ -877,6 +1224,7 @@ __device__ inline DrawState load_state(const DrawState* p) {
     st.thq = p->thq;
     st.Mq = p->Mq;
     st.invZq = p->invZq;
+    st.cq = p->cq;
     return st;
 }
 
@@ -888,6 +1236,7 @@ __device__ inline DrawState load_state(const DrawState* p) {
 // Weights, computed identically in both kernels (fp32, no contraction):
 //   p_j = exp2((l_j - M) * log2(e) / T) * (1/Z)
 //   residual (chain, rejected at k):   w_j = max(0, p_j - q_j)
+//   residual (tree with draft rows):   w_j = max(0, p_j - c * q_j), c from the walk
 //   target (chain bonus, tree):        w_j = p_j, with the excluded tokens at 0 (tree)
 // Fallback when the total weight is not positive: w_j = p_j (the plain target row).
 // Segment and chunk sums are fp64 sums of fp32 sums of four weights.
@@ -902,6 +1251,7 @@ __device__ inline uint32_t order_key(float f) {
 // Parameters of the draw weights of one request.
 struct WParams {
     float M, s2, invZ;  // target row
+    float cq;           // residual coefficient on the draft row
     uint32_t thp;       // filtered: target tokens with a key below thp weigh 0
     float Mq, invZq;    // draft logits row (kQ == 2)
     uint32_t thq;
@@ -933,7 +1283,7 @@ __device__ inline float draw_weight(const T* row, const void* q, int j, const WP
         qv = ex2((d - W.Mq) * W.s2) * W.invZq;
         if (order_key(d) < W.thq) qv = 0.f;
     }
-    return fmaxf(p - qv, 0.f);
+    return fmaxf(p - W.cq * qv, 0.f);
 }
 
 // Weights of four consecutive elements: `pw` gets the sum of the plain (filtered) p_j,
@@ -965,7 +1315,7 @@ __device__ inline void weigh4(const typename Quad<T>::Raw& lr, const typename QR
         float p = ex2((l[e] - W.M) * W.s2) * W.invZ;
         if (kFilt && order_key(l[e]) < W.thp) p = 0.f;
         ps += p;
-        if (kQ != 0) ws += fmaxf(p - qv[e], 0.f);
+        if (kQ != 0) ws += fmaxf(p - W.cq * qv[e], 0.f);
     }
     pw = ps;
     ww = kQ != 0 ? ws : ps;
@@ -1045,6 +1395,7 @@ __device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const
     W.Mq = st.Mq;
     W.invZq = st.invZq;
     W.thq = st.thq;
+    W.cq = st.cq;
     qrow = nullptr;
     if (st.kind == kDrawResidual)
         qrow = kFilt ? static_cast<const void*>(static_cast<const T*>(a.dlogits) + (size_t)st.qrow * a.V)
@@ -1576,6 +1927,7 @@ __global__ __launch_bounds__(kBlock) void k_filter_accept(KArgs a) {
             st.out = b * R + k;
             st.coin = b * R + G;
             st.nexcl = 0;
+            st.cq = 1.f;
             st.M = fpp[k].M;
             st.Z = fpp[k].Z;
             st.invZ = (float)(1.0 / fpp[k].Z);
@@ -1762,7 +2114,7 @@ Layout layout_for(int op, int B, int R, int V) {
     const size_t S2 = (size_t)fine_chunks(V);
     size_t off = 0;
     L.parts = off;
-    off = align256(off + sizeof(Part) * (size_t)B * R * kMaxSplits);
+    if (op != SPEC_OP_TREE_MSS) off = align256(off + sizeof(Part) * (size_t)B * R * kMaxSplits);
     L.dstate = off;
     off = align256(off + sizeof(DrawState) * (size_t)B);
     L.mass = off;
@@ -1884,6 +2236,14 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
 }
 
 template <typename T>
+int run_tree_mss(KArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((k_mss_walk<T>), dim3(a.B), dim3(kWalk), 0, st, a);
+    int rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    return run_draw<T>(a, st);
+}
+
+template <typename T>
 int run_chain_filtered(KArgs& a, hipStream_t st) {
     const int G = a.R - 1;
     hipLaunchKernelGGL((k_filter_rows<T>), dim3(a.B * (a.R + G)), dim3(kBlock), 0, st, a);
@@ -1904,7 +2264,7 @@ extern "C" size_t spec_workspace_bytes(int op, int B, int R, int V) {
     if (B < 0 || R < 1 || V < 1) return 0;
     if (op == SPEC_OP_GREEDY || op == SPEC_OP_CHAIN || op == SPEC_OP_CHAIN_FILTERED) {
         if (R - 1 < 1 || R - 1 > SPEC_MAX_G) return 0;
-    } else if (op == SPEC_OP_TREE) {
+    } else if (op == SPEC_OP_TREE || op == SPEC_OP_TREE_MSS) {
         if (R > SPEC_MAX_N) return 0;
     } else {
         return 0;
@@ -2015,6 +2375,41 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     bind_workspace(a, workspace, SPEC_OP_TREE);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_tree<float>(a, mode, st) : run_tree<uint16_t>(a, mode, st);
+}
+
+extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* draft_probs,
+                                    const int32_t* node_tokens, const int32_t* parents,
+                                    const float* coins, const float* temperature, int B, int N,
+                                    int V, int D, int32_t* accept_len, int32_t* out_tokens,
+                                    int32_t* accepted_nodes, float* probs_out, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+    if (!draft_probs || !node_tokens || !parents || !coins || !temperature || !accept_len ||
+        !out_tokens || !accepted_nodes)
+        return SPEC_ERR_NULL;
+    if (N < 1 || N > SPEC_MAX_N || D < 1 || D > SPEC_MAX_N) return SPEC_ERR_SHAPE;
+    int rc = check_common(logits, dtype, B, V, workspace, ws_bytes, SPEC_OP_TREE_MSS, N);
+    if (rc != SPEC_OK || B == 0) return rc;
+    if (((uintptr_t)draft_probs) % 4) return SPEC_ERR_PARAM;
+    KArgs a = {};
+    a.logits = logits;
+    a.q = draft_probs;
+    a.tokens = node_tokens;
+    a.parents = parents;
+    a.coins = coins;
+    a.temperature = temperature;
+    a.B = B;
+    a.R = N;
+    a.V = V;
+    a.D = D;
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.accepted_nodes = accepted_nodes;
+    a.probs = probs_out;
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    if (rc != SPEC_OK) return rc;
+    bind_workspace(a, workspace, SPEC_OP_TREE_MSS);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return dtype == SPEC_F32 ? run_tree_mss<float>(a, st) : run_tree_mss<uint16_t>(a, st);
 }
 
 extern "C" int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,

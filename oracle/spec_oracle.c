@@ -580,7 +580,7 @@ int oracle_verify_tree_mss(const void* logits, int dtype, const float* draft_pro
     if (!logits || !draft_probs || !node_tokens || !parents || !coins || !temperature ||
         !accept_len || !out_tokens || !accepted_nodes || !min_margin)
         return -1;
-    if (B < 0 || N < 2 || V < 1 || D < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (B < 0 || N < 1 || V < 1 || D < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
 #pragma omp parallel
     {
         double* w = (double*)malloc(sizeof(double) * (size_t)V);

@@ -23,6 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = L.declared_functions()
     assert set(names) >= {"spec_verify_greedy", "spec_verify_chain", "spec_verify_tree",
                           "spec_tree_mask", "spec_tree_commit_kv", "spec_verify_chain_filtered",
+                          "spec_verify_tree_mss",
                           "spec_workspace_bytes",
                           "spec_status_str"}
     for n in names:
@@ -170,4 +171,27 @@ def test_chain_filtered_rejects_bad_arguments(lib):
     assert call(dt=7) == L.SPEC_ERR_DTYPE
     assert call(wsb=ws - 1) == L.SPEC_ERR_WORKSPACE
     assert call(dl=P + 1) == L.SPEC_ERR_PARAM
+    assert call(B=0) == L.SPEC_OK
+
+
+def test_tree_mss_rejects_bad_arguments(lib):
+    f = lib.spec_verify_tree_mss
+    ws = L.workspace_bytes(L.SPEC_OP_TREE_MSS, 2, 64, 1000)
+    assert 0 < ws < L.workspace_bytes(L.SPEC_OP_TREE, 2, 64, 1000)   # no row records
+    assert L.workspace_bytes(L.SPEC_OP_TREE_MSS, 2, L.SPEC_MAX_N + 1, 1000) == 0
+    args = dict(lg=P, dt=L.SPEC_BF16, q=P, tok=P, par=P, coins=P, T=P, B=2, N=64, V=1000, D=6,
+                acc=P, out=P, nodes=P, probs=None, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["lg"], a["dt"], a["q"], a["tok"], a["par"], a["coins"], a["T"], a["B"], a["N"],
+                 a["V"], a["D"], a["acc"], a["out"], a["nodes"], a["probs"], a["ws"], a["wsb"], None)
+    for k in ("lg", "q", "tok", "par", "coins", "T", "acc", "out", "nodes", "ws"):
+        assert call(**{k: None}) == L.SPEC_ERR_NULL, k
+    assert call(N=0) == L.SPEC_ERR_SHAPE
+    assert call(N=L.SPEC_MAX_N + 1) == L.SPEC_ERR_SHAPE
+    assert call(D=0) == L.SPEC_ERR_SHAPE
+    assert call(dt=5) == L.SPEC_ERR_DTYPE
+    assert call(wsb=ws - 1) == L.SPEC_ERR_WORKSPACE
+    assert call(q=P + 2) == L.SPEC_ERR_PARAM
     assert call(B=0) == L.SPEC_OK
