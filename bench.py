@@ -301,6 +301,7 @@ def _tree_modes(args, torch, dev, api, wl):
                      "GB/s_eager": eager / (d.mean() * 1e-3) / 1e9,
                      "frac_eager": eager / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "path_only_bytes": path, "eager_bytes": eager}
+    out["tree_mss"] = _tree_mss_mode(torch, dev, api, wl, stream)
     # committing the accepted paths' KV (the step after verify): 128 KiB per token, the KV
     # of 32 layers x 8 KV heads x 128 dims x (K, V) in bf16
     row = 128 * 1024
@@ -345,6 +346,56 @@ def _tree_modes(args, torch, dev, api, wl):
                         "nodes/s": t.B * t.N / (d.mean() * 1e-3), "bytes": nbytes,
                         "bound": "latency (one workgroup per request)"}
     return out
+
+
+def _mss_path_bytes(t, acc, nodes, wl):
+    """The method's own bytes for a multi-step sampling walk: every row the walk reaches
+    once, plus the draft row of every node where a child was rejected."""
+    es = 2 if t.dtype == wl.BF16 else 4
+    total = 0
+    for b in range(t.B):
+        k = int(acc[b])
+        path = [0] + [int(n) for n in nodes[b, :k]]
+        par = t.parents[b]
+        total += len(path) * t.V * es
+        for i, v in enumerate(path):
+            kids = [c for c in range(v + 1, t.N) if par[c] == v]
+            rejected = (kids.index(path[i + 1]) > 0) if i + 1 < len(path) else bool(kids)
+            if rejected:
+                total += t.V * 4
+    return total
+
+
+def _tree_mss_mode(torch, dev, api, wl, stream):
+    """spec_verify_tree_mss on the tree workload with a draft row per node.  The walk
+    touches only ~100 MB per call, so a 1 GiB buffer is rewritten between timed calls
+    (untimed) to keep earlier calls' rows out of the memory-side cache."""
+    t = wl.make_tree_mss(4)
+    lg = torch.from_numpy(np.ascontiguousarray(t.logits).view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(t.draft_probs).to(dev)
+    tok, par = torch.from_numpy(t.node_tokens).to(dev), torch.from_numpy(t.parents).to(dev)
+    cn, tp = torch.from_numpy(t.coins).to(dev), torch.from_numpy(t.temperature).to(dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(5):
+        api.spec_verify_tree_mss(lg, q, tok, par, cn, tp, t.D)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(20):
+        flush.add_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        acc, _, nodes, _ = api.spec_verify_tree_mss(lg, q, tok, par, cn, tp, t.D)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in ev])
+    acc, nodes = acc.cpu().numpy(), nodes.cpu().numpy()
+    path = _mss_path_bytes(t, acc, nodes, wl)
+    del flush, lg, q
+    return {"workload": t.name, "avg_ms": float(d.mean()),
+            "positions/s": t.B * t.N / (d.mean() * 1e-3),
+            "accepted_mean": float(acc.mean()), "path_only_bytes": path,
+            "GB/s_path_only": path / (d.mean() * 1e-3) / 1e9}
 
 
 def _filtered_mode(args, torch, dev, api, wl):

@@ -893,7 +893,10 @@ struct MssSmem {
             int anc[SPEC_MAX_N];
             int dep[SPEC_MAX_N];
         };
-        int kids[SPEC_MAX_N];  // the walk: children of the current node
+        struct {  // the walk: children of the current node, p_cur of their tokens
+            int kids[SPEC_MAX_N];
+            double pxc[SPEC_MAX_N];
+        };
     };
     float qx[SPEC_MAX_N];     // q_parent(token of node c), by node id
     int path[SPEC_MAX_N];     // accepted nodes, by depth
@@ -902,7 +905,6 @@ struct MssSmem {
     double rz[kWalkWaves];
     int wcnt[kWalkWaves];
     int flag;
-    double px;
 };
 
 // Block-wide max / sum over the kWalk threads (every thread gets the same bits).
@@ -929,7 +931,11 @@ __device__ inline double walk_sum(double v, MssSmem& sm) {
 }
 
 // Max and normaliser of one target row: per thread an online (m, z) over batches of
-// kUnroll 16-byte vectors (fp32 batch sums added in fp64), then a block reduction.
+// kRowVecs 16-byte vectors, all loads of a batch in flight at once (one batch covers a
+// 256 KB row), fp32 batch sums added in fp64; then a block reduction.
+constexpr int kRowVecs = 16;
+constexpr int kResQuads = 8;
+
 template <typename T>
 __device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSmem& sm,
                                float& M_out, double& Z_out) {
@@ -941,26 +947,23 @@ __device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSme
     if (((uintptr_t)rowp) % 16 == 0) {
         const int nv = V / kVec;
         const u32x4* rv = reinterpret_cast<const u32x4*>(rowp);
-        for (int i0 = 0; i0 < nv; i0 += kWalk * kUnroll) {
-            u32x4 r[kUnroll];
+        for (int i0 = 0; i0 < nv; i0 += kWalk * kRowVecs) {
+            u32x4 r[kRowVecs];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kRowVecs; ++u) {
                 const int i = i0 + u * kWalk + tid;
                 if (i < nv) r[u] = ld_stream(rv + i);
             }
-            float l[kUnroll * kVec];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                if (i0 + u * kWalk + tid < nv) {
-                    Ld<T>::unpack(r[u], l + u * kVec);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) l[u * kVec + e] = -INFINITY;
-                }
-            }
             float bm = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kUnroll * kVec; ++e) bm = fmaxf(bm, l[e]);
+            for (int u = 0; u < kRowVecs; ++u) {
+                if (i0 + u * kWalk + tid < nv) {
+                    float l[kVec];
+                    Ld<T>::unpack(r[u], l);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) bm = fmaxf(bm, l[e]);
+                }
+            }
             if (bm != -INFINITY) {
                 if (bm > m) {
                     z = m == -INFINITY ? 0.0 : z * (double)ex2((m - bm) * s2);
@@ -968,7 +971,14 @@ __device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSme
                 }
                 float bs = 0.f;
 #pragma unroll
-                for (int e = 0; e < kUnroll * kVec; ++e) bs += ex2((l[e] - m) * s2);
+                for (int u = 0; u < kRowVecs; ++u) {
+                    if (i0 + u * kWalk + tid < nv) {
+                        float l[kVec];
+                        Ld<T>::unpack(r[u], l);
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) bs += ex2((l[e] - m) * s2);
+                    }
+                }
                 z += (double)bs;
             }
         }
@@ -994,7 +1004,8 @@ __device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSme
 }
 
 // N(c) = sum_v max(0, p_v - c q_v) over one (target row, draft row) pair, with the draw
-// kernels' weight formula (p_v = exp2((l_v - M) * s2) * invZ in fp32).
+// kernels' weight formula (p_v = exp2((l_v - M) * s2) * invZ in fp32).  Batches of
+// kResQuads four-element groups per thread, all loads of a batch in flight.
 template <typename T>
 __device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float M, float s2,
                                  float invZ, float cq, MssSmem& sm) {
@@ -1005,20 +1016,20 @@ __device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float 
         const int nq = V / 4;
         const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
         const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
-        for (int i0 = 0; i0 < nq; i0 += kWalk * kUnroll) {
-            typename Quad<T>::Raw lr[kUnroll];
-            u32x4 qr[kUnroll];
+        for (int i0 = 0; i0 < nq; i0 += kWalk * kResQuads) {
+            typename Quad<T>::Raw lr[kResQuads];
+            u32x4 qr[kResQuads];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kResQuads; ++u) {
                 const int i = i0 + u * kWalk + tid;
                 if (i < nq) {
                     lr[u] = lq[i].raw;
-                    qr[u] = ld_stream(qq + i);
+                    qr[u] = qq[i];
                 }
             }
             float bs = 0.f;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kResQuads; ++u) {
                 if (i0 + u * kWalk + tid < nq) {
                     float l[4];
                     Quad<T>::unpack(lr[u], l);
@@ -1092,11 +1103,6 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
     double Z = 1.0;
     while (!bad) {
         const T* rowp = logits + ((size_t)b * N + cur) * V;
-        walk_row_stats<T>(rowp, V, s2, Td, sm, M, Z);
-        if (M == -INFINITY) {  // a row on the walk with no finite logit
-            bad = true;
-            break;
-        }
         int count = 0;  // children of cur in ascending node id (ordered compaction)
         for (int base = cur + 1; base < N; base += kWalk) {
             const int c = base + tid;
@@ -1113,6 +1119,15 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
             __syncthreads();
             count += total;
         }
+        // thread j gathers child j's logit while the row pass streams
+        const float lx = tid < count ? Ld<T>::one(rowp + sm.tok[sm.kids[tid]]) : 0.f;
+        walk_row_stats<T>(rowp, V, s2, Td, sm, M, Z);
+        if (M == -INFINITY) {  // a row on the walk with no finite logit
+            bad = true;
+            break;
+        }
+        if (tid < count) sm.pxc[tid] = exp(((double)lx - (double)M) / Td) / Z;
+        __syncthreads();
         kind = kDrawTarget;
         cq = 0.f;
         if (count == 0) break;  // a leaf: the bonus from its own row
@@ -1123,24 +1138,21 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
         for (int j = 0; j < count; ++j) {
             const int child = sm.kids[j];
             if (tid == 0) {
-                const int x = sm.tok[child];
-                const double px = exp(((double)Ld<T>::one(rowp + x) - (double)M) / Td) / Z;
+                const double px = sm.pxc[j];
                 const double qx = (double)sm.qx[child];
                 double pr = px - c * qx;
                 pr = pr > 0.0 ? pr / Nr : 0.0;
                 const double u = (double)coins[child - 1];
                 sm.flag = qx > 0.0 ? (pr > 0.0 && u <= pr / qx) : pr > 0.0;
-                sm.px = px;
             }
             __syncthreads();
             const bool accepted = sm.flag != 0;
-            const double px = sm.px;
             __syncthreads();
             if (accepted) {
                 chosen = child;
                 if (tid == 0) {
                     sm.path[d] = child;
-                    sm.pathp[d] = (float)px;
+                    sm.pathp[d] = (float)sm.pxc[j];
                 }
                 break;
             }
