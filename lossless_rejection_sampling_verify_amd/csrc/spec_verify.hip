@@ -249,7 +249,8 @@ __device__ inline int block_min(int v, RowSmem& sm) {
 // Reduces chunk [c0, c1) of a row into one record (valid in every thread).
 template <typename T, bool kSampling>
 __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
-                                                            float s2, RowSmem& sm) {
+                                                            float s2, RowSmem& sm,
+                                                            float* lane_max = nullptr) {
     constexpr int kVec = Ld<T>::kVec;
     constexpr int kN = kUnroll * kVec;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -333,6 +334,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
 
     Part r;
     if (kSampling) {  // block max, then every lane rescales its sum to it once
+        if (lane_max) *lane_max = m;
         const float M = block_max(m, sm);
         double zz = 0.0;
         if (m != -INFINITY) zz = m == M ? z : z * (double)ex2((m - M) * s2);
@@ -1631,10 +1633,19 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
 
 constexpr int kHistBins = 256;  // 8-bit radix digits
 
+constexpr int kCandCap = 2048;  // top-k candidates kept in LDS by the direct selection
+
 struct FilterSmem {
     RowSmem rs;
-    uint32_t cnt[kWaves][kHistBins];            // one private histogram per wave
-    unsigned long long mass[kWaves][kHistBins];
+    union {
+        struct {
+            uint32_t cnt[kWaves][kHistBins];  // one private histogram per wave
+            unsigned long long mass[kWaves][kHistBins];
+        };
+        uint32_t cand[kCandCap];  // direct selection: candidate keys
+    };
+    uint32_t lanekey[kBlock];
+    int ncand;
     unsigned long long wtot[3][kWaves];
     int pick_thread;
     int last_thread;
@@ -1831,6 +1842,129 @@ __device__ uint32_t radix_select(const T* rowp, int V, float M, float s2, float 
     return prefix;
 }
 
+// Block-wide bitonic sort of a[0..n) (n a power of two) into descending order.
+__device__ void bitonic_desc(uint32_t* a, int n) {
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            __syncthreads();
+            for (int t = threadIdx.x; t < n / 2; t += kBlock) {
+                const int lo = 2 * t - (t & (stride - 1));  // the pair (lo, lo + stride)
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint32_t x = a[lo], y = a[hi];
+                if (desc ? x < y : x > y) {
+                    a[lo] = y;
+                    a[hi] = x;
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ inline float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Direct top-k (k <= kBlock) then top-p on the top-k set, for rows whose candidates fit in
+// LDS.  The k-th largest of the lanes' maxima (one per lane from the first pass) is a
+// lower bound of the row's k-th largest logit, so one more pass collects every token at
+// or above it; sorting those keys gives the k-th largest key exactly, and prefix sums of
+// the fixed-point masses over the sorted keys give the top-p threshold.  Thresholds and
+// kept mass are the ones the radix selection finds.  Returns false (nothing decided)
+// when the candidates do not fit.
+template <typename T>
+__device__ bool direct_select(const T* rowp, int V, float M, float s2, float fscale, int k,
+                              bool fp, double tp, float lane_max, uint32_t* th_out,
+                              unsigned long long* kept_out, FilterSmem& sm) {
+    const int tid = threadIdx.x;
+    constexpr int kVec = Ld<T>::kVec;
+    sm.lanekey[tid] = order_key(lane_max);
+    if (tid == 0) sm.ncand = 0;
+    bitonic_desc(sm.lanekey, kBlock);
+    const uint32_t lb = sm.lanekey[k - 1];
+    auto visit = [&](float x) {
+        const uint32_t key = order_key(x);
+        if (key >= lb) {
+            const int slot = atomicAdd(&sm.ncand, 1);
+            if (slot < kCandCap) sm.cand[slot] = key;
+        }
+    };
+    int head = (int)(((16u - ((uint32_t)(uintptr_t)rowp & 15u)) & 15u) / sizeof(T));
+    if (head > V) head = V;
+    const int nv = (V - head) / kVec;
+    const int tail0 = head + nv * kVec;
+    if (tid < head) visit(Ld<T>::one(rowp + tid));
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + head);
+    int v = tid;
+    for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
+        u32x4 r[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) r[u] = ld_stream(vp + v + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float f[kVec];
+            Ld<T>::unpack(r[u], f);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) visit(f[e]);
+        }
+    }
+    for (; v < nv; v += kBlock) {
+        float f[kVec];
+        Ld<T>::unpack(ld_stream(vp + v), f);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) visit(f[e]);
+    }
+    if (tail0 + tid < V) visit(Ld<T>::one(rowp + tail0 + tid));
+    __syncthreads();
+    const int n = sm.ncand;
+    if (n > kCandCap) return false;  // uniform: every thread read the same count
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int j = n + tid; j < n2; j += kBlock) sm.cand[j] = 0u;  // below every real key
+    bitonic_desc(sm.cand, n2);
+    const uint32_t thk = sm.cand[k - 1];
+    int nk = k;  // ties at the k-th key are kept
+    while (nk < n && sm.cand[nk] == thk) ++nk;
+    // fixed-point masses over the sorted keys: lane t owns a contiguous run of them
+    const int per = (nk + kBlock - 1) / kBlock;
+    const int j0 = min(nk, tid * per), j1 = min(nk, j0 + per);
+    unsigned long long v3[3] = {0ull, 0ull, 0ull}, ex[3], tot[3];
+    for (int j = j0; j < j1; ++j)
+        v3[0] += (unsigned long long)(ex2((key_value(sm.cand[j]) - M) * s2) * fscale);
+    block_scan3(v3, ex, tot, sm);
+    uint32_t th = thk;
+    unsigned long long kept = tot[0];
+    if (fp) {
+        const double need = tp * (double)tot[0];
+        if (tid == 0) sm.pick = nk - 1;
+        __syncthreads();
+        // the first sorted position whose inclusive prefix reaches the need
+        unsigned long long acc = ex[0];
+        for (int j = j0; j < j1; ++j) {
+            acc += (unsigned long long)(ex2((key_value(sm.cand[j]) - M) * s2) * fscale);
+            if ((double)acc >= need) {
+                atomicMin(&sm.pick, j);
+                break;
+            }
+        }
+        __syncthreads();
+        const int jp = sm.pick;
+        th = sm.cand[jp];
+        // kept mass: every token with key >= th (ties of the threshold included)
+        unsigned long long part = 0ull;
+        for (int j = j0; j < j1; ++j)
+            if (sm.cand[j] >= th)
+                part += (unsigned long long)(ex2((key_value(sm.cand[j]) - M) * s2) * fscale);
+        unsigned long long p3[3] = {part, 0ull, 0ull}, e3[3], t3[3];
+        block_scan3(p3, e3, t3, sm);
+        kept = t3[0];
+    }
+    *th_out = th;
+    *kept_out = kept;
+    return true;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     __shared__ FilterSmem sm;
@@ -1842,7 +1976,8 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
                           : reinterpret_cast<const T*>(a.logits) + (size_t)r * V;
     const float Tf = a.temperature[b];
     const float s2 = kLog2e / Tf;
-    const Part st = chunk_record<T, true>(rowp, 0, V, s2, sm.rs);
+    float lane_max;
+    const Part st = chunk_record<T, true>(rowp, 0, V, s2, sm.rs, &lane_max);
     FiltRow fr;
     fr.M = st.m;
     fr.th = 0u;
@@ -1856,10 +1991,15 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
         const float fscale = exp2f((float)a.fixbits);
         unsigned long long kept = 0ull;
         uint32_t lo = 0u;
-        if (fk) lo = radix_select<T>(rowp, V, st.m, s2, fscale, 0u, false, 0.0,
-                                     (unsigned long long)k, &kept, sm);
-        if (fp) lo = radix_select<T>(rowp, V, st.m, s2, fscale, lo, true, (double)tp, 0ull,
-                                     &kept, sm);
+        const bool direct = fk && k <= kBlock &&
+                            direct_select<T>(rowp, V, st.m, s2, fscale, k, fp, (double)tp,
+                                             lane_max, &lo, &kept, sm);
+        if (!direct) {
+            if (fk) lo = radix_select<T>(rowp, V, st.m, s2, fscale, 0u, false, 0.0,
+                                         (unsigned long long)k, &kept, sm);
+            if (fp) lo = radix_select<T>(rowp, V, st.m, s2, fscale, lo, true, (double)tp,
+                                         0ull, &kept, sm);
+        }
         fr.th = lo;
         fr.Z = ldexp((double)kept, -a.fixbits);
     }

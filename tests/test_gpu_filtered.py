@@ -98,3 +98,35 @@ def test_invalid_knobs():
     tp = np.array([0.7, 0.0, -1.0, np.nan, 1.5, 0.7], np.float32)
     g, o = check(c, "invalid top_p", top_p=tp)
     assert (g["accept_len"][[1, 2, 3]] == -1).all() and (g["accept_len"][[0, 4, 5]] >= 0).all()
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_candidate_overflow_and_plateaus(dtype):
+    """Rows whose top-k boundary sits on a wide plateau.  With 3000 tokens tied at the top,
+    more candidates reach the lanes' lower bound than LDS holds, so the row is selected by
+    the radix walk instead.  With 1500 tied tokens the direct selection keeps them all
+    (ties at the k-th key are kept).  Target and draft plateaus either differ (every
+    draft is rejected and the correction comes from the residual) or coincide, with the
+    drafts on them (every draft is accepted).  Both must match the oracle."""
+    import dataclasses
+    c = wl.make_chain_logits(2, seed=21, B=8, G=3, V=40000, dtype=dtype, top_k=100, top_p=0.9)
+    rng = np.random.default_rng(5)
+    tl = wl.logits_as_f32(c.logits, dtype)
+    dl = wl.logits_as_f32(c.draft_logits, dtype)
+    enc = (lambda f: wl.f32_to_bf16_bits(f)) if dtype == wl.BF16 else (lambda f: f)
+    for width in (3000, 1500):
+        for shared in (False, True):
+            t2, d2, x2 = tl.copy(), dl.copy(), c.draft_tokens.copy()
+            for b in range(c.B):
+                for i in range(c.R):
+                    ids = rng.choice(c.V, size=width, replace=False)
+                    t2[b, i, ids] = t2[b, i].max() + 1.0
+                    if i < c.G:
+                        dids = ids if shared else rng.choice(c.V, size=width, replace=False)
+                        d2[b, i, dids] = d2[b, i].max() + 1.0
+                        if shared:
+                            x2[b, i] = ids[rng.integers(width)]
+            c2 = dataclasses.replace(c, logits=enc(t2), draft_logits=enc(d2), draft_tokens=x2)
+            g, o = check(c2, f"plateau of {width}, shared={shared}, {dtype}")
+            if shared:
+                assert (o["accept_len"] == c.G).all()
