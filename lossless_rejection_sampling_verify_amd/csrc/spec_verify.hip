@@ -31,6 +31,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -886,6 +889,9 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
 
 constexpr int kWalk = 1024;
 constexpr int kWalkWaves = kWalk / 64;
+constexpr int kMaxCluster = 16;    // workgroups sharing one request's walk
+constexpr int kClusterSlots = 256; // cluster workgroups per call at most (sizes the slots)
+constexpr long kSpinMax = 1 << 18; // bound of a cluster wait (never reached when all run)
 
 struct MssSmem {
     int par[SPEC_MAX_N];
@@ -907,6 +913,8 @@ struct MssSmem {
     double rz[kWalkWaves];
     int wcnt[kWalkWaves];
     int flag;
+    uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
+    int xbad;
 };
 
 // Block-wide max / sum over the kWalk threads (every thread gets the same bits).
@@ -935,8 +943,9 @@ __device__ inline double walk_sum(double v, MssSmem& sm) {
 // Max and normaliser of one target row: per thread an online (m, z) over batches of
 // kRowVecs 16-byte vectors, all loads of a batch in flight at once (one batch covers a
 // 256 KB row), fp32 batch sums added in fp64; then a block reduction.
-constexpr int kRowVecs = 16;
-constexpr int kResQuads = 8;
+constexpr int kRowVecs = 8;
+template <typename T>
+constexpr int res_quads() { return sizeof(T) == 4 ? 4 : 8; }  // four-element groups per batch
 
 template <typename T>
 __device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSmem& sm,
@@ -1007,22 +1016,23 @@ __device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSme
 
 // N(c) = sum_v max(0, p_v - c q_v) over one (target row, draft row) pair, with the draw
 // kernels' weight formula (p_v = exp2((l_v - M) * s2) * invZ in fp32).  Batches of
-// kResQuads four-element groups per thread, all loads of a batch in flight.
+// res_quads<T>() four-element groups per thread, all loads of a batch in flight.
 template <typename T>
 __device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float M, float s2,
                                  float invZ, float cq, MssSmem& sm) {
     const int tid = threadIdx.x;
+    constexpr int kRQ = res_quads<T>();
     double acc = 0.0;
     int done = 0;
     if (((uintptr_t)rowp) % (4 * sizeof(T)) == 0 && ((uintptr_t)qrow) % 16 == 0) {
         const int nq = V / 4;
         const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
         const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
-        for (int i0 = 0; i0 < nq; i0 += kWalk * kResQuads) {
-            typename Quad<T>::Raw lr[kResQuads];
-            u32x4 qr[kResQuads];
+        for (int i0 = 0; i0 < nq; i0 += kWalk * kRQ) {
+            typename Quad<T>::Raw lr[kRQ];
+            u32x4 qr[kRQ];
 #pragma unroll
-            for (int u = 0; u < kResQuads; ++u) {
+            for (int u = 0; u < kRQ; ++u) {
                 const int i = i0 + u * kWalk + tid;
                 if (i < nq) {
                     lr[u] = lq[i].raw;
@@ -1031,7 +1041,7 @@ __device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float 
             }
             float bs = 0.f;
 #pragma unroll
-            for (int u = 0; u < kResQuads; ++u) {
+            for (int u = 0; u < kRQ; ++u) {
                 if (i0 + u * kWalk + tid < nq) {
                     float l[4];
                     Quad<T>::unpack(lr[u], l);
@@ -1056,12 +1066,86 @@ __device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float 
     return walk_sum(acc, sm);
 }
 
+// One step of a cluster: every workgroup of the request hands three 32-bit payloads to
+// the others.  Each payload travels in a 64-bit word whose high half is the call's tag;
+// words are written and read whole with agent-scope atomics, which are coherent across
+// the XCDs, so a reader that sees the tag sees the payload and no fence is needed.  Slot
+// (step, workgroup) is written once per call.  The wait is bounded: if a word never
+// arrives, the step fails and the request is reported invalid instead of hanging.  With
+// W = 1 the payloads stay in LDS.
+__device__ bool cluster_step(unsigned long long* slots, int step, int W, int w, uint32_t tag,
+                             uint32_t p0, uint32_t p1, uint32_t p2, MssSmem& sm) {
+    const int tid = threadIdx.x;
+    if (W == 1) {
+        if (tid == 0) {
+            sm.xp[0][0] = p0;
+            sm.xp[0][1] = p1;
+            sm.xp[0][2] = p2;
+        }
+        __syncthreads();
+        return true;
+    }
+    unsigned long long* base = slots + (size_t)step * W * 3;
+    if (tid == 0) {
+        const unsigned long long t = (unsigned long long)tag << 32;
+        __hip_atomic_store(base + w * 3 + 0, t | p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(base + w * 3 + 1, t | p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(base + w * 3 + 2, t | p2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.xbad = 0;
+    }
+    __syncthreads();
+    if (tid < W) {
+        unsigned long long* q = base + tid * 3;
+        unsigned long long v0 = 0, v1 = 0, v2 = 0;
+        for (long spin = 0;; ++spin) {
+            v0 = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v1 = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v2 = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(v0 >> 32) == tag && (uint32_t)(v1 >> 32) == tag &&
+                (uint32_t)(v2 >> 32) == tag)
+                break;
+            if (spin >= kSpinMax) {
+                sm.xbad = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        sm.xp[tid][0] = (uint32_t)v0;
+        sm.xp[tid][1] = (uint32_t)v1;
+        sm.xp[tid][2] = (uint32_t)v2;
+    }
+    __syncthreads();
+    return sm.xbad == 0;
+}
+
+__device__ inline uint32_t dbl_hi(double x) { return (uint32_t)((unsigned long long)__double_as_longlong(x) >> 32); }
+__device__ inline uint32_t dbl_lo(double x) { return (uint32_t)__double_as_longlong(x); }
+__device__ inline double dbl_of(uint32_t hi, uint32_t lo) {
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// One request per cluster of W workgroups (blockIdx = b * W + w).  Workgroup w owns the
+// vocabulary slice [w * per, (w + 1) * per) of every row.  The row statistics and
+// residual masses are combined across the cluster in workgroup order, so every
+// workgroup of the cluster takes the same decisions, and workgroup 0 writes the outputs.
+//
+// The host picks W so that all B * W workgroups fit on the device at once.  Even when
+// they do not, the waits end: workgroups start in increasing id on every XCD, so the
+// lowest-numbered unfinished cluster always has all its workgroups started.  Every wait
+// is also bounded.
+//
+// A cooperative launch would guarantee residency, but it cost about 17 us more per call.
 template <typename T>
-__global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
+__global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a, int W, uint32_t tag,
+                                                    unsigned long long* xslots, int xstride) {
     __shared__ MssSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x;
+    const int b = blockIdx.x / W, w = blockIdx.x - b * W;
     const int N = a.R, V = a.V, D = a.D;
+    const int per = ((V + W - 1) / W + 7) / 8 * 8;
+    const int lo = min(V, w * per), n = min(V, lo + per) - lo;
+    unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    int step = 0;
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const float* coins = a.coins + (size_t)b * N;
@@ -1123,7 +1207,24 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
         }
         // thread j gathers child j's logit while the row pass streams
         const float lx = tid < count ? Ld<T>::one(rowp + sm.tok[sm.kids[tid]]) : 0.f;
-        walk_row_stats<T>(rowp, V, s2, Td, sm, M, Z);
+        {
+            float Mw;
+            double Zw;
+            walk_row_stats<T>(rowp + lo, n, s2, Td, sm, Mw, Zw);
+            if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(Mw), dbl_hi(Zw),
+                              dbl_lo(Zw), sm)) {
+                bad = true;
+                break;
+            }
+            M = -INFINITY;
+            for (int k = 0; k < W; ++k) M = fmaxf(M, __uint_as_float(sm.xp[k][0]));
+            Z = 0.0;
+            for (int k = 0; k < W; ++k) {
+                const float mk = __uint_as_float(sm.xp[k][0]);
+                if (mk != -INFINITY)
+                    Z += dbl_of(sm.xp[k][1], sm.xp[k][2]) * exp(((double)mk - (double)M) / Td);
+            }
+        }
         if (M == -INFINITY) {  // a row on the walk with no finite logit
             bad = true;
             break;
@@ -1164,16 +1265,23 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a) {
                 cq = (float)cn;
                 break;
             }
-            const double Nn = walk_resid_sum<T>(rowp, qrow, V, M, s2, invZ, (float)cn, sm);
+            const double Nw = walk_resid_sum<T>(rowp + lo, qrow + lo, n, M, s2, invZ, (float)cn, sm);
+            if (!cluster_step(slots, step++, W, w, tag, dbl_hi(Nw), dbl_lo(Nw), 0u, sm)) {
+                bad = true;
+                break;
+            }
+            double Nn = 0.0;
+            for (int k = 0; k < W; ++k) Nn += dbl_of(sm.xp[k][0], sm.xp[k][1]);
             if (!(Nn > 0.0)) break;  // no residual mass left: draw from the target row
             c = cn;
             Nr = Nn;
         }
-        if (chosen < 0) break;
+        if (bad || chosen < 0) break;
         cur = chosen;
         ++d;
     }
     __syncthreads();  // the path is in LDS
+    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
 
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
@@ -2253,8 +2361,19 @@ __global__ __launch_bounds__(kBlock) void k_commit_kv(const int32_t* accepted_no
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t parts, dstate, mass, massfb, seg, excl, frows, total;
+    size_t parts, dstate, mass, massfb, seg, excl, frows, xch, total;
 };
+
+// Workgroups per request that the multi-step tree walk may use (slots are sized for it).
+inline int cluster_max(int B) {
+    if (B <= 0) return 1;
+    const int w = kClusterSlots / B;
+    return w < 2 ? 1 : (w > kMaxCluster ? kMaxCluster : w);
+}
+
+// 64-bit hand-off words per request: at most 2N steps (a row pass per reached node and a
+// residual pass per rejected child), W workgroups, three words each.
+inline size_t cluster_stride(int N, int W) { return (size_t)2 * N * W * 3; }
 
 inline long fine_chunks(int V) { return ((long)V + kFine - 1) / kFine; }
 
@@ -2279,6 +2398,9 @@ Layout layout_for(int op, int B, int R, int V) {
     if (op == SPEC_OP_TREE) off = align256(off + sizeof(int32_t) * (size_t)B * SPEC_MAX_N);
     L.frows = off;
     if (op == SPEC_OP_CHAIN_FILTERED) off = align256(off + sizeof(FiltRow) * (size_t)B * (2 * R - 1));
+    L.xch = off;
+    if (op == SPEC_OP_TREE_MSS && cluster_max(B) > 1)
+        off = align256(off + sizeof(unsigned long long) * (size_t)B * cluster_stride(R, cluster_max(B)));
     L.total = off;
     return L;
 }
@@ -2387,9 +2509,43 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
     return run_draw<T>(a, st);
 }
 
+// k_mss_walk workgroups that the current device holds at once, cached per device.
 template <typename T>
-int run_tree_mss(KArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_mss_walk<T>), dim3(a.B), dim3(kWalk), 0, st, a);
+int cluster_capacity() {
+    static int cache[64];
+    static bool known[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!known[dev]) {
+        int cus = 0, nb = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &nb, reinterpret_cast<const void*>(&k_mss_walk<T>), kWalk, 0) != hipSuccess)
+            nb = 0;
+        cache[dev] = nb * cus;
+        known[dev] = true;
+    }
+    return cache[dev];
+}
+
+// Tags of the multi-step walk's hand-off words: one per call, process-wide, so no two
+// calls through the same workspace share a tag (until 2^32 calls have passed).
+std::atomic<uint32_t> g_walk_epoch{0};
+
+template <typename T>
+int run_tree_mss(KArgs& a, unsigned long long* xslots, hipStream_t st) {
+    uint32_t tag = g_walk_epoch.fetch_add(1u) + 1u;
+    if (tag == 0u) tag = g_walk_epoch.fetch_add(1u) + 1u;  // 0 is what fresh memory most often holds
+    int W = 1;
+    if (xslots) {
+        W = std::min(cluster_max(a.B), cluster_capacity<T>() / a.B);
+        if (const char* env = std::getenv("SPEC_VERIFY_CLUSTER")) W = std::min(W, std::atoi(env));
+        if (W < 2) W = 1;
+    }
+    const int xstride = W > 1 ? (int)cluster_stride(a.R, W) : 0;
+    hipLaunchKernelGGL((k_mss_walk<T>), dim3(a.B * W), dim3(kWalk), 0, st, a, W, tag,
+                       W > 1 ? xslots : (unsigned long long*)nullptr, xstride);
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
     return run_draw<T>(a, st);
@@ -2560,8 +2716,14 @@ extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* 
     rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_TREE_MSS);
+    const Layout L = layout_for(SPEC_OP_TREE_MSS, B, N, V);
+    unsigned long long* xslots =
+        cluster_max(B) > 1
+            ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch)
+            : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return dtype == SPEC_F32 ? run_tree_mss<float>(a, st) : run_tree_mss<uint16_t>(a, st);
+    return dtype == SPEC_F32 ? run_tree_mss<float>(a, xslots, st)
+                             : run_tree_mss<uint16_t>(a, xslots, st);
 }
 
 extern "C" int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,

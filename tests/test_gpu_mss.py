@@ -143,3 +143,13 @@ def test_deterministic_bits():
     b = gpu_mss(t)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("cluster", ["1", "2", "5"])
+def test_cluster_sizes(cluster, monkeypatch):
+    """The walk split over W workgroups per request (W from the device, or capped by
+    SPEC_VERIFY_CLUSTER) matches the oracle for every W, including one workgroup per
+    request and a W that does not divide the vocabulary evenly."""
+    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    t = wl.make_tree_mss(4, seed=13, B=16, N=40, V=30011, D=6, max_children=6, dtype=wl.BF16)
+    check_mss(t, f"cluster cap {cluster}")
