@@ -12,6 +12,13 @@ call (spec_verify_chain: algorithmic HBM bytes per call / call time measured wit
 events on the launch stream), and the CPU oracle timed on a bounded sample of the same
 workload.
 
+Both calls walk each request position by position and stop at the first rejection (or
+mismatch), so the algorithmic bytes of a call are the rows the method consults: for
+request b, rows 0..k_b of its logits, plus the fp32 draft row at k_b when the chain
+rejected there.  The eager passes (every row streamed), selected with
+SPEC_VERIFY_EAGER=1, are timed after the main region and reported under
+modes.*_eager with their own bytes (every row once).
+
 HBM traffic: two rocprofv3 counter passes over this script (FETCH_SIZE, then WRITE_SIZE,
 with --calib-copy-mib so that a plain device copy of known size runs after the timed
 region) are reduced by ``bench.py --traffic-from FETCH_DIR WRITE_DIR``, which scales each
@@ -32,8 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD published peak
-CHAIN_KERNELS = ["k_rows<sampling>", "k_chain_accept", "k_mass", "k_draw"]
-GREEDY_KERNELS = ["k_rows<greedy>", "k_greedy_merge"]
+CHAIN_KERNELS = ["k_chain_walk", "k_draw"]
+GREEDY_KERNELS = ["k_greedy_walk"]
+EAGER_CHAIN_KERNELS = ["k_rows<sampling>", "k_chain_accept", "k_mass", "k_draw"]
+EAGER_GREEDY_KERNELS = ["k_rows<greedy>", "k_greedy_merge"]
 
 
 def parse():
@@ -126,18 +135,35 @@ def main():
     greedy_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     chain_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     acc_c = out_c[0].cpu().numpy()
+    acc_g = out_g[0].cpu().numpy()
     rejected = int((acc_c < G).sum())
 
-    logit_bytes = B * R * V * esize
-    greedy_bytes = logit_bytes + B * G * 4 + B * 4 + B * R * 4
-    chain_bytes = (logit_bytes + rejected * V * 4 +                 # q row at each rejection
-                   B * (G + R + 1) * 4 + B * G * 4 +                 # tokens, coins, T, q gathers
-                   B * 4 + 2 * B * R * 4)                            # outputs
+    small_g = B * G * 4 + B * 4 + B * R * 4                          # drafts, outputs
+    small_c = (B * (G + R + 1) * 4 + B * G * 4 +                     # tokens, coins, T, q gathers
+               B * 4 + 2 * B * R * 4)                                # outputs
+    # the rows each request consults, and the draft row where the chain rejected
+    greedy_bytes = int((acc_g + 1).sum()) * V * esize + small_g
+    chain_bytes = int((acc_c + 1).sum()) * V * esize + rejected * V * 4 + small_c
     positions = 2 * B * R
     value = positions * args.steps / elapsed
 
     chain_gbs = chain_bytes / (chain_ms.mean() * 1e-3) / 1e9
     greedy_gbs = greedy_bytes / (greedy_ms.mean() * 1e-3) / 1e9
+
+    # the eager passes, for comparison (outside the timed region)
+    os.environ["SPEC_VERIFY_EAGER"] = "1"
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    ev_e = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
+    for i in range(20):
+        step(i, ev_e[i])
+    torch.cuda.synchronize()
+    del os.environ["SPEC_VERIFY_EAGER"]
+    greedy_e = np.array([e[0].elapsed_time(e[1]) for e in ev_e])
+    chain_e = np.array([e[1].elapsed_time(e[2]) for e in ev_e])
+    eager_g_bytes = B * R * V * esize + small_g
+    eager_c_bytes = B * R * V * esize + rejected * V * 4 + small_c
 
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -162,7 +188,8 @@ def main():
                    "step": "spec_verify_greedy + spec_verify_chain", "input_copies": args.copies},
         "roofline": {
             "bound": "hbm",
-            "kernel": "spec_verify_chain call: " + " + ".join(CHAIN_KERNELS),
+            "kernel": "spec_verify_chain call: " + " + ".join(CHAIN_KERNELS) +
+                      " (bytes: rows consulted up to the first rejection, plus its draft row)",
             "achieved": chain_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -174,12 +201,20 @@ def main():
         "modes": {
             "greedy": {"avg_ms": float(greedy_ms.mean()), "p90_ms": float(np.percentile(greedy_ms, 90)),
                        "GB/s": greedy_gbs, "frac": greedy_gbs / HBM_PEAK_GBS,
-                       "positions/s": B * R / (greedy_ms.mean() * 1e-3)},
+                       "positions/s": B * R / (greedy_ms.mean() * 1e-3),
+                       "rows_consulted": int((acc_g + 1).sum())},
             "chain": {"avg_ms": float(chain_ms.mean()), "p90_ms": float(np.percentile(chain_ms, 90)),
                       "GB/s": chain_gbs, "frac": chain_gbs / HBM_PEAK_GBS,
                       "positions/s": B * R / (chain_ms.mean() * 1e-3),
                       "rejected_requests": rejected,
+                      "rows_consulted": int((acc_c + 1).sum()),
                       "tokens/s": float((acc_c + 1).sum()) / (chain_ms.mean() * 1e-3)},
+            "greedy_eager": {"avg_ms": float(greedy_e.mean()), "bytes": eager_g_bytes,
+                             "GB/s": eager_g_bytes / (greedy_e.mean() * 1e-3) / 1e9,
+                             "frac": eager_g_bytes / (greedy_e.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "chain_eager": {"avg_ms": float(chain_e.mean()), "bytes": eager_c_bytes,
+                            "GB/s": eager_c_bytes / (chain_e.mean() * 1e-3) / 1e9,
+                            "frac": eager_c_bytes / (chain_e.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS},
         },
         "input_generation_s": gen_s,
     }
@@ -259,7 +294,9 @@ def _traffic_from(args):
     out["calls"] = {
         name: {"bytes": sum(kernels[k]["fetch_bytes"] + kernels[k]["write_bytes"] for k in ks),
                "kernels": ks}
-        for name, ks in (("spec_verify_chain", CHAIN_KERNELS), ("spec_verify_greedy", GREEDY_KERNELS))
+        for name, ks in (("spec_verify_chain", CHAIN_KERNELS), ("spec_verify_greedy", GREEDY_KERNELS),
+                         ("spec_verify_chain eager", EAGER_CHAIN_KERNELS),
+                         ("spec_verify_greedy eager", EAGER_GREEDY_KERNELS))
         if all(k in kernels for k in ks)}
     os.makedirs(os.path.dirname(args.traffic_json), exist_ok=True)
     json.dump(out, open(args.traffic_json, "w"), indent=1)

@@ -116,6 +116,7 @@ struct KArgs {
     const float* top_p;
     FiltRow* frows;      // filtered calls: [B*R] target rows, then [B*G] draft rows
     int fixbits;         // fixed-point fraction bits of the filter's mass histograms
+    int walk_temporal;   // chain walk: row passes with cache-allocating loads (sweeps: 0)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -250,7 +251,7 @@ __device__ inline int block_min(int v, RowSmem& sm) {
 }
 
 // Reduces chunk [c0, c1) of a row into one record (valid in every thread).
-template <typename T, bool kSampling>
+template <typename T, bool kSampling, bool kNT = true>
 __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
                                                             float s2, RowSmem& sm,
                                                             float* lane_max = nullptr) {
@@ -321,14 +322,14 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
     for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
         u32x4 raw[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) raw[u] = ld_stream(vp + v + u * kBlock);
+        for (int u = 0; u < kUnroll; ++u) raw[u] = kNT ? ld_stream(vp + v + u * kBlock) : vp[v + u * kBlock];
         float f[kN];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) Ld<T>::unpack(raw[u], f + u * kVec);
         batch(f, kN, v);
     }
     for (; v < nv; v += kBlock) {
-        const u32x4 raw = ld_stream(vp + v);
+        const u32x4 raw = kNT ? ld_stream(vp + v) : vp[v];
         float f[kVec];
         Ld<T>::unpack(raw, f);
         batch(f, kVec, v);
@@ -427,18 +428,22 @@ __global__ __launch_bounds__(kBlock) void k_greedy_merge(KArgs a) {
     __syncthreads();
     if (tid == 0) {
         const int* x = sm.x;
-        bool valid = true;
-        for (int i = 0; i < G; ++i)
-            if (x[i] < 0 || x[i] >= a.V) valid = false;
-        for (int i = 0; i < R; ++i)
-            if (sm.arg[i] < 0) valid = false;
+        bool valid = true;  // only what the positions up to the first mismatch consult
         int k = G;
-        if (valid) {
-            for (int i = 0; i < G; ++i)
-                if (x[i] != sm.arg[i]) {
-                    k = i;
-                    break;
-                }
+        for (int i = 0; i <= G; ++i) {
+            if (sm.arg[i] < 0) {
+                valid = false;
+                break;
+            }
+            if (i == G) break;
+            if (x[i] < 0 || x[i] >= a.V) {
+                valid = false;
+                break;
+            }
+            if (x[i] != sm.arg[i]) {
+                k = i;
+                break;
+            }
         }
         sm.k = valid ? k : -1;
         a.accept_len[b] = sm.k;
@@ -544,16 +549,19 @@ __device__ DrawState chain_accept(const KArgs& a, int b, bool emit, Smem& sm, Re
         sm.arg[tid] = (ok ? 1 : 0) | (keep ? 2 : 0);
     }
     __syncthreads();
-    if (tid == 0) {
-        bool valid = t_ok;
-        for (int i = 0; i < R; ++i)
-            if (!(sm.arg[i] & 1)) valid = false;
+    if (tid == 0) {  // positions in order up to the first rejection; the final coin always
+        bool valid = t_ok && sm.u[G] > 0.f && sm.u[G] <= 1.f;
         int k = G;
-        for (int i = 0; i < G && valid; ++i)
-            if (!(sm.arg[i] & 2)) {
+        for (int i = 0; i <= G && valid; ++i) {
+            if (!(sm.arg[i] & 1)) {
+                valid = false;
+                break;
+            }
+            if (i < G && !(sm.arg[i] & 2)) {
                 k = i;
                 break;
             }
+        }
         sm.k = valid ? k : -1;
         if (emit) a.accept_len[b] = sm.k;
         DrawState st = {};
@@ -893,6 +901,11 @@ constexpr int kMaxCluster = 16;    // workgroups sharing one request's walk
 constexpr int kClusterSlots = 256; // cluster workgroups per call at most (sizes the slots)
 constexpr long kSpinMax = 1 << 18; // bound of a cluster wait (never reached when all run)
 
+struct XSmem {
+    uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
+    int xbad;
+};
+
 struct MssSmem {
     int par[SPEC_MAX_N];
     int tok[SPEC_MAX_N];
@@ -913,8 +926,7 @@ struct MssSmem {
     double rz[kWalkWaves];
     int wcnt[kWalkWaves];
     int flag;
-    uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
-    int xbad;
+    XSmem x;
 };
 
 // Block-wide max / sum over the kWalk threads (every thread gets the same bits).
@@ -1073,29 +1085,35 @@ __device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float 
 // (step, workgroup) is written once per call.  The wait is bounded: if a word never
 // arrives, the step fails and the request is reported invalid instead of hanging.  With
 // W = 1 the payloads stay in LDS.
-__device__ bool cluster_step(unsigned long long* slots, int step, int W, int w, uint32_t tag,
-                             uint32_t p0, uint32_t p1, uint32_t p2, MssSmem& sm) {
+__device__ void cluster_publish(unsigned long long* slots, int step, int W, int w,
+                                uint32_t tag, uint32_t p0, uint32_t p1, uint32_t p2,
+                                XSmem& sm) {
+    if (threadIdx.x != 0) return;
+    if (W == 1) {  // nothing to hand over: the payloads stay in LDS
+        sm.xp[0][0] = p0;
+        sm.xp[0][1] = p1;
+        sm.xp[0][2] = p2;
+        return;
+    }
+    unsigned long long* base = slots + (size_t)step * W * 3;
+    const unsigned long long t = (unsigned long long)tag << 32;
+    __hip_atomic_store(base + w * 3 + 0, t | p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + w * 3 + 1, t | p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + w * 3 + 2, t | p2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits for the W payloads of `step` (sm.xp[w][0..2] afterwards, in every thread).
+__device__ bool cluster_wait(unsigned long long* slots, int step, int W, uint32_t tag,
+                             XSmem& sm) {
     const int tid = threadIdx.x;
     if (W == 1) {
-        if (tid == 0) {
-            sm.xp[0][0] = p0;
-            sm.xp[0][1] = p1;
-            sm.xp[0][2] = p2;
-        }
         __syncthreads();
         return true;
     }
-    unsigned long long* base = slots + (size_t)step * W * 3;
-    if (tid == 0) {
-        const unsigned long long t = (unsigned long long)tag << 32;
-        __hip_atomic_store(base + w * 3 + 0, t | p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(base + w * 3 + 1, t | p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(base + w * 3 + 2, t | p2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.xbad = 0;
-    }
+    if (tid == 0) sm.xbad = 0;
     __syncthreads();
     if (tid < W) {
-        unsigned long long* q = base + tid * 3;
+        unsigned long long* q = slots + (size_t)step * W * 3 + tid * 3;
         unsigned long long v0 = 0, v1 = 0, v2 = 0;
         for (long spin = 0;; ++spin) {
             v0 = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1116,6 +1134,13 @@ __device__ bool cluster_step(unsigned long long* slots, int step, int W, int w, 
     }
     __syncthreads();
     return sm.xbad == 0;
+}
+
+// Publish then wait (a step with nothing to overlap).
+__device__ bool cluster_step(unsigned long long* slots, int step, int W, int w, uint32_t tag,
+                             uint32_t p0, uint32_t p1, uint32_t p2, XSmem& sm) {
+    cluster_publish(slots, step, W, w, tag, p0, p1, p2, sm);
+    return cluster_wait(slots, step, W, tag, sm);
 }
 
 __device__ inline uint32_t dbl_hi(double x) { return (uint32_t)((unsigned long long)__double_as_longlong(x) >> 32); }
@@ -1212,17 +1237,17 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a, int W, uint32_t tag
             double Zw;
             walk_row_stats<T>(rowp + lo, n, s2, Td, sm, Mw, Zw);
             if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(Mw), dbl_hi(Zw),
-                              dbl_lo(Zw), sm)) {
+                              dbl_lo(Zw), sm.x)) {
                 bad = true;
                 break;
             }
             M = -INFINITY;
-            for (int k = 0; k < W; ++k) M = fmaxf(M, __uint_as_float(sm.xp[k][0]));
+            for (int k = 0; k < W; ++k) M = fmaxf(M, __uint_as_float(sm.x.xp[k][0]));
             Z = 0.0;
             for (int k = 0; k < W; ++k) {
-                const float mk = __uint_as_float(sm.xp[k][0]);
+                const float mk = __uint_as_float(sm.x.xp[k][0]);
                 if (mk != -INFINITY)
-                    Z += dbl_of(sm.xp[k][1], sm.xp[k][2]) * exp(((double)mk - (double)M) / Td);
+                    Z += dbl_of(sm.x.xp[k][1], sm.x.xp[k][2]) * exp(((double)mk - (double)M) / Td);
             }
         }
         if (M == -INFINITY) {  // a row on the walk with no finite logit
@@ -1266,12 +1291,12 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a, int W, uint32_t tag
                 break;
             }
             const double Nw = walk_resid_sum<T>(rowp + lo, qrow + lo, n, M, s2, invZ, (float)cn, sm);
-            if (!cluster_step(slots, step++, W, w, tag, dbl_hi(Nw), dbl_lo(Nw), 0u, sm)) {
+            if (!cluster_step(slots, step++, W, w, tag, dbl_hi(Nw), dbl_lo(Nw), 0u, sm.x)) {
                 bad = true;
                 break;
             }
             double Nn = 0.0;
-            for (int k = 0; k < W; ++k) Nn += dbl_of(sm.xp[k][0], sm.xp[k][1]);
+            for (int k = 0; k < W; ++k) Nn += dbl_of(sm.x.xp[k][0], sm.x.xp[k][1]);
             if (!(Nn > 0.0)) break;  // no residual mass left: draw from the target row
             c = cn;
             Nr = Nn;
@@ -1327,6 +1352,63 @@ __global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a, int W, uint32_t tag
         st.T = Td;
         a.dstate[b] = st;
     }
+}
+
+// k_greedy_walk: greedy chain verify position by position, one cluster of W workgroups
+// per request (blockIdx = b * W + w, workgroup w owning a slice of whole fine chunks of
+// every row).  Each position's slice argmax travels through the cluster hand-off; the
+// walk stops at the first mismatch, so rows after it are never read.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per, uint32_t tag,
+                                                        unsigned long long* xslots, int xstride) {
+    __shared__ RowSmem rs;
+    __shared__ XSmem xs;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / W, w = blockIdx.x - b * W;
+    const int R = a.R, G = R - 1, V = a.V;
+    const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
+    unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    const int32_t* x = a.tokens + (size_t)b * G;
+    int k = G, last = -1;
+    bool bad = false;
+    for (int i = 0; i <= G; ++i) {
+        const Part cur = chunk_record<T, false>(logits + ((size_t)b * R + i) * V, lo, hi, 0.f, rs);
+        if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), (uint32_t)cur.idx, 0u,
+                          xs)) {
+            bad = true;
+            break;
+        }
+        float M = -INFINITY;
+        int idx = INT_MAX;
+        for (int j = 0; j < W; ++j) {  // slices in order: the lowest index among equal maxima
+            const float mj = __uint_as_float(xs.xp[j][0]);
+            if (mj > M) {
+                M = mj;
+                idx = (int)xs.xp[j][1];
+            }
+        }
+        if (M == -INFINITY) {  // a row the walk reaches has no finite logit
+            bad = true;
+            break;
+        }
+        last = idx;
+        if (i == G) break;
+        const int xi = x[i];
+        if (xi < 0 || xi >= V) {
+            bad = true;
+            break;
+        }
+        if (xi != idx) {
+            k = i;
+            break;
+        }
+    }
+    if (w != 0) return;
+    int32_t* out = a.out_tokens + (size_t)b * R;
+    for (int e = tid; e < R; e += kBlock)
+        out[e] = bad ? -1 : (e < k ? x[e] : (e == k ? last : -1));
+    if (tid == 0) a.accept_len[b] = bad ? -1 : k;
 }
 
 // Field-wise copy of a draw state from global memory (keeps it in registers).
@@ -1525,19 +1607,15 @@ __device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const
     return W;
 }
 
-// One workgroup per (request, fine chunk).
+// The draw weights of fine chunk c of the row in `st`: each segment's weight (and the
+// chunk's) in a.seg / a.mass, the plain target weight in a.massfb.  Block-wide.
 template <typename T, bool kFilt>
-__global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
-    __shared__ MassSmem sm;
+__device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const DrawState& st,
+                                                          const WParams& W, const T* rowp,
+                                                          const void* qrow, int b, int c,
+                                                          MassSmem& sm) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int S2 = a.S2, V = a.V;
-    const int b = blockIdx.x / S2;
-    const int c = blockIdx.x - b * S2;
-    const DrawState st = a.dstate[b];
-    if (st.kind == kDrawNone) return;
-    const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
-    const void* qrow;
-    const WParams W = draw_params<T, kFilt>(a, st, qrow);
     const int c0 = c * kFine;
     const int n = min(kFine, V - c0);
     const size_t qes = kFilt ? sizeof(T) : sizeof(float);
@@ -1583,6 +1661,143 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
             a.mass[(size_t)b * S2 + c] = Wt;
             a.massfb[(size_t)b * S2 + c] = P;
         }
+    }
+    __syncthreads();  // LDS is reused by the next chunk
+}
+
+// One workgroup per (request, fine chunk).
+template <typename T, bool kFilt>
+__global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
+    __shared__ MassSmem sm;
+    const int S2 = a.S2;
+    const int b = blockIdx.x / S2;
+    const int c = blockIdx.x - b * S2;
+    const DrawState st = a.dstate[b];
+    if (st.kind == kDrawNone) return;
+    const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * a.V;
+    const void* qrow;
+    const WParams W = draw_params<T, kFilt>(a, st, qrow);
+    mass_chunk<T, kFilt>(a, st, W, rowp, qrow, b, c, sm);
+}
+
+// k_chain_walk: chain rejection sampling position by position, one cluster of W
+// workgroups per request (blockIdx = b * W + w, workgroup w owning a slice of whole fine
+// chunks of every row).  At each position the slices' (max, normaliser) travel through
+// the cluster hand-off and every workgroup takes the same acceptance decision; the walk
+// stops at the first rejection (or after the bonus row), so rows after it are never
+// read.  Each workgroup then weighs its slice of the row the last token is drawn from
+// (the residual against q, or the plain row for the bonus), which k_draw searches.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, uint32_t tag,
+                                                       unsigned long long* xslots, int xstride) {
+    __shared__ RowSmem rs;
+    __shared__ XSmem xs;
+    __shared__ MassSmem ms;
+    __shared__ float sp[kMaxRows];
+    __shared__ int sflag;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / W, w = blockIdx.x - b * W;
+    const int R = a.R, G = R - 1, V = a.V;
+    const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
+    unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    const float Tf = a.temperature[b];
+    const float uG = a.coins[(size_t)b * R + G];
+    bool bad = !(isfinite(Tf) && Tf > 0.f) || !(uG > 0.f && uG <= 1.f);
+    const double Td = (double)Tf;
+    const float s2 = kLog2e / Tf;
+    int k = G;
+    float M = -INFINITY;
+    double Z = 0.0;
+    auto pass = [&](int i) {
+        const T* rowp = logits + ((size_t)b * R + i) * V;
+        return a.walk_temporal ? chunk_record<T, true, false>(rowp, lo, hi, s2, rs)
+                               : chunk_record<T, true, true>(rowp, lo, hi, s2, rs);
+    };
+    for (int i = 0; i <= G && !bad; ++i) {
+        const T* rowp = logits + ((size_t)b * R + i) * V;
+        int xi = -1;
+        float lx = 0.f, qx = 0.f, ui = 0.f;
+        if (i < G && tid == 0) {  // the acceptance test's inputs
+            xi = a.tokens[(size_t)b * G + i];
+            ui = a.coins[(size_t)b * R + i];
+            if (xi >= 0 && xi < V) {
+                lx = Ld<T>::one(rowp + xi);
+                qx = a.q[((size_t)b * G + i) * V + xi];
+            }
+        }
+        const Part cur = pass(i);
+        if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), dbl_hi(cur.z),
+                          dbl_lo(cur.z), xs)) {
+            bad = true;
+            break;
+        }
+        M = -INFINITY;
+        for (int j = 0; j < W; ++j) M = fmaxf(M, __uint_as_float(xs.xp[j][0]));
+        Z = 0.0;
+        for (int j = 0; j < W; ++j) {
+            const float mj = __uint_as_float(xs.xp[j][0]);
+            if (mj != -INFINITY)
+                Z += dbl_of(xs.xp[j][1], xs.xp[j][2]) * exp(((double)mj - (double)M) / Td);
+        }
+        if (M == -INFINITY) {  // a row the walk reaches has no finite logit
+            bad = true;
+            break;
+        }
+        if (i == G) break;  // every draft accepted: the bonus from row G
+        if (tid == 0) {  // 0 = rejected, 1 = accepted, 2 = unusable input
+            int flag;
+            if (xi < 0 || xi >= V || !(ui > 0.f && ui <= 1.f) || !(qx >= 0.f && isfinite(qx))) {
+                flag = 2;
+            } else {
+                const double p = exp(((double)lx - (double)M) / Td) / Z;
+                const double q = (double)qx;
+                flag = (q > 0.0 ? (p > 0.0 && (double)ui <= p / q) : p > 0.0) ? 1 : 0;
+                sp[i] = (float)p;
+            }
+            sflag = flag;
+        }
+        __syncthreads();
+        const int flag = sflag;
+        __syncthreads();
+        if (flag == 2) {
+            bad = true;
+            break;
+        }
+        if (flag == 0) {
+            k = i;
+            break;
+        }
+    }
+    DrawState st = {};
+    st.kind = kDrawNone;
+    if (!bad) {
+        st.kind = k < G ? kDrawResidual : kDrawTarget;
+        st.row = b * R + k;
+        st.qrow = b * G + k;
+        st.out = b * R + k;
+        st.coin = b * R + G;
+        st.nexcl = 0;
+        st.cq = 1.f;
+        st.M = M;
+        st.Z = Z;
+        st.invZ = (float)(1.0 / Z);
+        st.T = Td;
+        const T* rowp = logits + (size_t)st.row * V;
+        const void* qrow;
+        const WParams Wp = draw_params<T, false>(a, st, qrow);
+        for (int c = lo / kFine; c * kFine < hi; ++c)
+            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms);
+    }
+    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
+    for (int e = tid; e < R; e += kBlock) {
+        if (e == k && !bad) continue;  // slot k is written by the final draw
+        a.out_tokens[(size_t)b * R + e] = (!bad && e < k) ? a.tokens[(size_t)b * G + e] : -1;
+        if (a.probs) a.probs[(size_t)b * R + e] = (!bad && e < k) ? sp[e] : 0.f;
+    }
+    if (tid == 0) {
+        a.accept_len[b] = bad ? -1 : k;
+        a.dstate[b] = st;
     }
 }
 
@@ -2399,7 +2614,9 @@ Layout layout_for(int op, int B, int R, int V) {
     L.frows = off;
     if (op == SPEC_OP_CHAIN_FILTERED) off = align256(off + sizeof(FiltRow) * (size_t)B * (2 * R - 1));
     L.xch = off;
-    if (op == SPEC_OP_TREE_MSS && cluster_max(B) > 1)
+    if (op == SPEC_OP_GREEDY || op == SPEC_OP_CHAIN)
+        off = align256(off + sizeof(unsigned long long) * (size_t)B * R * kMaxCluster * 3);
+    else if (op == SPEC_OP_TREE_MSS && cluster_max(B) > 1)
         off = align256(off + sizeof(unsigned long long) * (size_t)B * cluster_stride(R, cluster_max(B)));
     L.total = off;
     return L;
@@ -2465,6 +2682,80 @@ int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t w
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
+
+// Workgroups of `kernel` (kBlock threads) that the current device holds at once.
+inline int resident_blocks(const void* kernel, int slot) {
+    static int cache[8][64];
+    static bool known[8][64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!known[slot][dev]) {
+        int cus = 0, nb = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, 0) != hipSuccess)
+            nb = 0;
+        cache[slot][dev] = nb * cus;
+        known[slot][dev] = true;
+    }
+    return cache[slot][dev];
+}
+
+std::atomic<uint32_t> g_chain_epoch{0};
+
+inline uint32_t next_tag() {
+    uint32_t tag = g_chain_epoch.fetch_add(1u) + 1u;
+    if (tag == 0u) tag = g_chain_epoch.fetch_add(1u) + 1u;  // fresh memory most often holds 0
+    return tag;
+}
+
+// Cluster shape of a position-by-position walk: W workgroups per request, each owning
+// `per_chunks` whole fine chunks of every row, with all B * W workgroups resident at once.
+inline void walk_shape(const KArgs& a, int cap, int* W_out, int* per_chunks_out) {
+    int W = std::min(kMaxCluster, std::max(1, cap / std::max(1, a.B)));
+    if (const char* env = std::getenv("SPEC_VERIFY_CLUSTER"))  // launch-shape sweeps
+        W = std::max(1, std::min(kMaxCluster, std::atoi(env)));
+    W = std::min(W, a.S2);
+    const int per_chunks = (a.S2 + W - 1) / W;
+    *W_out = (a.S2 + per_chunks - 1) / per_chunks;
+    *per_chunks_out = per_chunks;
+}
+
+template <typename T>
+int run_greedy_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
+    const uint32_t tag = next_tag();
+    int W, per;
+    walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_greedy_walk<T>),
+                                  sizeof(T) == 4 ? 0 : 1), &W, &per);
+    hipLaunchKernelGGL((k_greedy_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
+                       per * kFine, tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       a.R * W * 3);
+    return launch_status();
+}
+
+template <typename T>
+int run_chain_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
+    const uint32_t tag = next_tag();
+    a.walk_temporal = 1;  // keeps the slice of the row drawn from near for the final weights
+    if (const char* env = std::getenv("SPEC_VERIFY_TEMPORAL")) a.walk_temporal = std::atoi(env);
+    int W, per;
+    walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_chain_walk<T>),
+                                  sizeof(T) == 4 ? 2 : 3), &W, &per);
+    hipLaunchKernelGGL((k_chain_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
+                       per * kFine, tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       a.R * W * 3);
+    int rc = launch_status();
+    if (rc != SPEC_OK) return rc;
+    hipLaunchKernelGGL((k_draw<T, false>), dim3(a.B), dim3(64), 0, st, a);
+    return launch_status();
+}
+
+// The eager passes (every row streamed, then merged) instead of the walks; kept for
+// comparison and selected by SPEC_VERIFY_EAGER=1.
+inline bool eager_forced() {
+    const char* e = std::getenv("SPEC_VERIFY_EAGER");
+    return e && std::atoi(e) != 0;
+}
 
 template <typename T>
 int run_greedy(KArgs& a, hipStream_t st) {
@@ -2612,6 +2903,13 @@ extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* 
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_GREEDY);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!eager_forced()) {
+        const Layout L = layout_for(SPEC_OP_GREEDY, B, G + 1, V);
+        unsigned long long* xs =
+            reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
+        return dtype == SPEC_F32 ? run_greedy_walk<float>(a, xs, st)
+                                 : run_greedy_walk<uint16_t>(a, xs, st);
+    }
     return dtype == SPEC_F32 ? run_greedy<float>(a, st) : run_greedy<uint16_t>(a, st);
 }
 
@@ -2642,6 +2940,13 @@ extern "C" int spec_verify_chain(const void* logits, int dtype, const float* dra
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_CHAIN);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!eager_forced()) {
+        const Layout L = layout_for(SPEC_OP_CHAIN, B, G + 1, V);
+        unsigned long long* xs =
+            reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
+        return dtype == SPEC_F32 ? run_chain_walk<float>(a, xs, st)
+                                 : run_chain_walk<uint16_t>(a, xs, st);
+    }
     return dtype == SPEC_F32 ? run_chain<float>(a, st) : run_chain<uint16_t>(a, st);
 }
 

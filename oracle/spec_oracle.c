@@ -144,26 +144,31 @@ static int draw_inverse_cdf(const double* w, int V, double u, double* mm) {
 static void greedy_one(const void* logits, int dtype, const int32_t* draft, int G, int V,
                        size_t b, int32_t* accept_len, int32_t* out) {
     int R = G + 1;
-    int valid = 1;
-    for (int i = 0; i < G; ++i)
-        if (draft[i] < 0 || draft[i] >= V) valid = 0;
-    for (int i = 0; i < R && valid; ++i)
-        if (row_max(row_of(logits, dtype, b * (size_t)R + (size_t)i, V)) == -INFINITY) valid = 0;
-    if (!valid) {
-        *accept_len = -1;
-        for (int i = 0; i < R; ++i) out[i] = -1;
-        return;
-    }
-    int k = G;
-    for (int i = 0; i < G; ++i) {
-        int a = row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)i, V));
+    int valid = 1, k = G, a = -1;
+    for (int i = 0; i <= G; ++i) { /* positions in order, up to the first mismatch */
+        Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
+        if (row_max(r) == -INFINITY) { /* a row the verify consults has no finite logit */
+            valid = 0;
+            break;
+        }
+        a = row_argmax(r);
+        if (i == G) break;
+        if (draft[i] < 0 || draft[i] >= V) {
+            valid = 0;
+            break;
+        }
         if (draft[i] != a) {
             k = i;
             break;
         }
     }
+    if (!valid) {
+        *accept_len = -1;
+        for (int i = 0; i < R; ++i) out[i] = -1;
+        return;
+    }
     for (int i = 0; i < k; ++i) out[i] = draft[i];
-    out[k] = row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)k, V));
+    out[k] = a;
     for (int i = k + 1; i < R; ++i) out[i] = -1;
     *accept_len = k;
 }
@@ -192,52 +197,34 @@ static void chain_one(const void* logits, int dtype, const float* q, const int32
     int R = G + 1;
     double T = (double)temperature;
     double m[R > 0 ? R : 1], Z[R > 0 ? R : 1];
-    int valid = temperature_ok(temperature);
-    for (int i = 0; i < G; ++i)
-        if (draft[i] < 0 || draft[i] >= V) valid = 0;
-    for (int i = 0; i < R; ++i)
-        if (!coin_ok(coins[i])) valid = 0;
-    for (int i = 0; i < R && valid; ++i) {
-        m[i] = row_max(row_of(logits, dtype, b * (size_t)R + (size_t)i, V));
-        if (m[i] == -INFINITY) valid = 0;
-    }
-    for (int i = 0; i < G && valid; ++i) {
-        float qx = q[(size_t)i * V + (size_t)draft[i]];
-        if (!(qx >= 0.0f) || !isfinite(qx)) valid = 0;
-    }
-    *margin = INFINITY;
-    if (!valid) {
-        *accept_len = -1;
-        for (int i = 0; i < R; ++i) out[i] = -1;
-        if (probs)
-            for (int i = 0; i < R; ++i) probs[i] = 0.0;
-        if (beta)
-            for (int i = 0; i < G; ++i) beta[i] = 0.0;
-        return;
-    }
-    for (int i = 0; i < R; ++i)
-        Z[i] = row_partition(row_of(logits, dtype, b * (size_t)R + (size_t)i, V), m[i], T);
-
-    if (beta) { /* beta_i = sum_x min(p_i(x), q_i(x)): per-position acceptance rate */
-        for (int i = 0; i < G; ++i) {
-            Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
-            double s = 0.0;
-            for (int x = 0; x < V; ++x) {
-                double p = row_prob(r, x, m[i], Z[i], T);
-                double qq = (double)q[(size_t)i * V + (size_t)x];
-                s += p < qq ? p : qq;
-            }
-            beta[i] = s;
-        }
-    }
-
+    /* Positions are consulted in order up to the first rejection (or the bonus row): only
+     * what is consulted must be usable -- its row, draft token, q(token) and coin -- plus
+     * the temperature and the final coin. */
+    int valid = temperature_ok(temperature) && coin_ok(coins[G]);
     int k = G;
     double pacc[R > 0 ? R : 1];
-    for (int i = 0; i < G; ++i) {
+    *margin = INFINITY;
+    for (int i = 0; i <= G && valid; ++i) {
         Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
+        m[i] = row_max(r);
+        if (m[i] == -INFINITY) {
+            valid = 0;
+            break;
+        }
+        Z[i] = row_partition(r, m[i], T);
+        if (i == G) break;
         int x = draft[i];
+        if (x < 0 || x >= V || !coin_ok(coins[i])) {
+            valid = 0;
+            break;
+        }
+        float qf = q[(size_t)i * V + (size_t)x];
+        if (!(qf >= 0.0f) || !isfinite(qf)) {
+            valid = 0;
+            break;
+        }
         double p = row_prob(r, x, m[i], Z[i], T);
-        double qx = (double)q[(size_t)i * V + (size_t)x];
+        double qx = (double)qf;
         double u = (double)coins[i];
         int accept;
         if (qx > 0.0) {
@@ -252,6 +239,34 @@ static void chain_one(const void* logits, int dtype, const float* q, const int32
             break;
         }
         pacc[i] = p;
+    }
+    if (!valid) {
+        *margin = INFINITY;
+        *accept_len = -1;
+        for (int i = 0; i < R; ++i) out[i] = -1;
+        if (probs)
+            for (int i = 0; i < R; ++i) probs[i] = 0.0;
+        if (beta)
+            for (int i = 0; i < G; ++i) beta[i] = 0.0;
+        return;
+    }
+
+    if (beta) { /* beta_i = sum_x min(p_i(x), q_i(x)): per-position acceptance rate
+                 * (a diagnostic over every position; 0 where a row has no finite logit) */
+        for (int i = 0; i < G; ++i) {
+            Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
+            double mi = row_max(r);
+            double s = 0.0;
+            if (mi != -INFINITY) {
+                double Zi = row_partition(r, mi, T);
+                for (int x = 0; x < V; ++x) {
+                    double p = row_prob(r, x, mi, Zi, T);
+                    double qq = (double)q[(size_t)i * V + (size_t)x];
+                    s += p < qq ? p : qq;
+                }
+            }
+            beta[i] = s;
+        }
     }
 
     /* Weights of the final draw: residual max(0, p_k - q_k) after a rejection, the

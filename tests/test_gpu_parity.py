@@ -292,26 +292,40 @@ def test_chain_shaped_tree_equals_chain_on_gpu():
 # ------------------------------------------------------------------------------------
 # invalid requests, determinism
 
-def test_invalid_requests_match_oracle():
-    c = wl.make_chain(2, seed=2, B=8, G=3, V=3000)
+@pytest.mark.parametrize("eager", [False, True])
+def test_invalid_requests_match_oracle(eager, monkeypatch):
+    """Bad entries at position 0 (always consulted) invalidate the request; bad entries
+    after the first rejection are never consulted (the oracle decides which is which)."""
+    if eager:
+        monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+    c = wl.make_chain(2, seed=2, B=16, G=3, V=3000)
     lg, q, x, u, T = (c.logits.copy(), c.draft_probs.copy(), c.draft_tokens.copy(),
                       c.coins.copy(), c.temperature.copy())
-    x[1, 2] = 3000
+    x[1, 0] = 3000
     T[2] = 0.0
     u[3, 0] = 0.0
-    lg[4, 3, :] = -np.inf
-    q[5, 1, x[5, 1]] = np.nan
+    lg[4, 0, :] = -np.inf
+    q[5, 0, x[5, 0]] = np.nan
     T[6] = np.inf
-    say("invalid chain requests")
+    u[7, 3] = 0.0                   # the final draw's coin
+    x[8, 2] = -5                    # later positions: consulted only if the walk gets there
+    lg[9, 3, :] = -np.inf
+    q[10, 1, x[10, 1]] = np.nan
+    u[11, 2] = 2.0
+    say(f"invalid chain requests, eager={eager}")
     g = gpu_chain(lg, c.dtype, q, x, u, T)
     o = oracle.verify_chain(lg, c.dtype, q, x, u, T)
     compare(g, o, ["accept_len", "out_tokens"], o["margin"], label="invalid chain")
-    assert (g["accept_len"][[1, 2, 3, 4, 5, 6]] == -1).all()
-    assert (g["probs"][[1, 2, 3, 4, 5, 6]] == 0).all()
+    np.testing.assert_array_equal(g["accept_len"], o["accept_len"])
+    assert (g["accept_len"][[1, 2, 3, 4, 5, 6, 7]] == -1).all()
+    assert (g["probs"][[1, 2, 3, 4, 5, 6, 7]] == 0).all()
     ga, go = gpu_greedy(lg, c.dtype, x)
     oa, oo = oracle.verify_greedy(lg, c.dtype, x)
     np.testing.assert_array_equal(ga, oa)
     np.testing.assert_array_equal(go, oo)
+    assert ga[1] == -1 and ga[4] == -1
+    if eager:
+        return
 
     t = wl.make_tree(4, seed=1, B=6, N=12, V=200, D=3, max_children=4)
     par, tok, cn = t.parents.copy(), t.node_tokens.copy(), t.coins.copy()
@@ -335,3 +349,22 @@ def test_deterministic_bits():
     b = gpu_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_eager_passes_match_oracle(cfg, monkeypatch):
+    """The eager passes (every row streamed, then merged), selected by SPEC_VERIFY_EAGER,
+    give the oracle's results too."""
+    monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+    c = chain_cfg(cfg)
+    check_chain(c, f"eager workload {cfg}")
+    check_greedy(c, f"eager workload {cfg}")
+
+
+@pytest.mark.parametrize("cluster", ["1", "3"])
+def test_walk_cluster_widths(cluster, monkeypatch):
+    """The position-by-position walks with one workgroup per request and with three."""
+    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    c = wl.make_chain(3, seed=31, B=24, G=8, V=50021)
+    check_chain(c, f"walk W<={cluster}")
+    check_greedy(c, f"walk W<={cluster}")

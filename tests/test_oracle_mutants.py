@@ -42,9 +42,8 @@ MUTANTS = [
      "for (int x = 1; x < r.V; ++x) Z += exp("),
     ("argmax ties to highest id", "if (logit(r, x) > logit(r, best)) best = x;",
      "if (logit(r, x) >= logit(r, best)) best = x;"),
-    ("greedy emits the draft at the mismatch",
-     "out[k] = row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)k, V));",
-     "out[k] = k < G ? draft[k] : row_argmax(row_of(logits, dtype, b * (size_t)R + (size_t)k, V));"),
+    ("greedy emits the draft at the mismatch", "    out[k] = a;\n",
+     "    out[k] = k < G ? draft[k] : a;\n"),
     ("bucket edge exclusive", "if (t <= C) {", "if (t < C) {"),
     ("tree prob_acc not accumulated", "acc += pc;", "acc = pc;"),
     ("tree exclusions dropped", "for (int e = 0; e < nexcl; ++e) w[excl[e]] = 0.0;", ""),

@@ -9,7 +9,8 @@
     of the node it extends: checked exactly over the coin lattice;
   - a chain-shaped tree with target-only sampling equals chain verify with one-hot draft
     distributions (two independent code paths of the oracle, bit for bit);
-  - invalid inputs give accept_len = -1 and padded rows.
+  - invalid inputs give accept_len = -1 and padded rows; only what the walk consults is
+    checked.
 """
 from __future__ import annotations
 
@@ -221,21 +222,24 @@ def test_threshold_single_accepts_dominant_child():
 # invalid inputs
 
 def test_invalid_requests_are_flagged():
-    c = wl.make_chain(2, seed=2, B=8, G=3, V=100)
+    """What the first position consults is always consulted, so a bad entry there makes
+    the request invalid."""
+    c = wl.make_chain(2, seed=2, B=9, G=3, V=100)
     lg, q, x, u, T = (c.logits.copy(), c.draft_probs.copy(), c.draft_tokens.copy(),
                       c.coins.copy(), c.temperature.copy())
-    x[1, 2] = 100                 # token out of range
+    x[1, 0] = 100                 # token out of range
     T[2] = 0.0                    # temperature not > 0
     u[3, 0] = 0.0                 # coin outside (0, 1]
-    lg[4, 3, :] = -np.inf         # a row with no finite logit
-    q[5, 1, x[5, 1]] = np.nan     # q of a drafted token not finite
+    lg[4, 0, :] = -np.inf         # a row with no finite logit
+    q[5, 0, x[5, 0]] = np.nan     # q of a drafted token not finite
     T[6] = np.inf
+    u[8, 3] = 1.5                 # the final draw's coin
     r = oracle.verify_chain(lg, c.dtype, q, x, u, T)
-    bad = [1, 2, 3, 4, 5, 6]
+    bad = [1, 2, 3, 4, 5, 6, 8]
     assert (r["accept_len"][bad] == -1).all()
     assert (r["out_tokens"][bad] == -1).all()
     assert (r["probs"][bad] == 0).all()
-    assert (r["accept_len"][[0, 7]] >= 0).all()
+    assert r["accept_len"][0] >= 0 and r["accept_len"][7] >= 0
     ga, go = oracle.verify_greedy(lg, c.dtype, x)
     assert ga[1] == -1 and ga[4] == -1 and (go[[1, 4]] == -1).all()
     assert ga[2] >= 0               # greedy ignores temperature and coins
@@ -255,3 +259,46 @@ def test_invalid_requests_are_flagged():
     r2 = oracle.verify_tree(t.logits, t.dtype, t.node_tokens, t.parents, None, None, 2,
                             oracle.TREE_GREEDY)          # depth 3 > D = 2
     assert (r2["accept_len"] == -1).all()
+
+
+def test_only_consulted_positions_are_checked():
+    """Positions after the first rejection (mismatch) are never consulted: a bad row, draft,
+    q or coin there leaves the request valid and its result unchanged; the same entry at
+    a consulted position makes it invalid."""
+    V, G = 50, 3
+    rng = np.random.default_rng(4)
+    lg = (rng.standard_normal((1, G + 1, V)) * 2).astype(np.float32)
+    q = np.full((1, G, V), 1.0 / V, np.float32)
+    x = np.zeros((1, G), np.int32)
+    x[0, 0] = int(np.argmin(lg[0, 0]))        # improbable under p: rejected with coin 1
+    q[0, 0, :] = 0.0
+    q[0, 0, x[0, 0]] = 1.0
+    u = np.array([[1.0, 0.5, 0.5, 0.5]], np.float32)
+    T = np.ones(1, np.float32)
+    ref = oracle.verify_chain(lg, "f32", q, x, u, T)
+    assert ref["accept_len"][0] == 0
+    for what in ("row", "draft", "q", "coin"):
+        lg2, q2, x2, u2 = lg.copy(), q.copy(), x.copy(), u.copy()
+        if what == "row":
+            lg2[0, 2, :] = -np.inf
+        elif what == "draft":
+            x2[0, 1] = V + 7
+        elif what == "q":
+            q2[0, 1, x2[0, 1]] = np.nan
+        else:
+            u2[0, 1] = 0.0
+        r = oracle.verify_chain(lg2, "f32", q2, x2, u2, T)
+        np.testing.assert_array_equal(r["accept_len"], ref["accept_len"])
+        np.testing.assert_array_equal(r["out_tokens"], ref["out_tokens"])
+    # greedy: a mismatch at position 0 leaves the later rows and drafts unconsulted
+    xg = np.array([[int(np.argmax(lg[0, 0])) + 1 if np.argmax(lg[0, 0]) + 1 < V else 0,
+                    V + 3, 0]], np.int32)
+    lg3 = lg.copy()
+    lg3[0, 1:, :] = -np.inf
+    a, o = oracle.verify_greedy(lg3, "f32", xg)
+    assert a[0] == 0 and o[0, 0] == int(np.argmax(lg[0, 0]))
+    # ... while a bad row the walk reaches invalidates it
+    xg2 = np.array([[int(np.argmax(lg[0, 0])), 1, 1]], np.int32)
+    a, o = oracle.verify_greedy(lg3, "f32", xg2)
+    assert a[0] == -1 and (o == -1).all()
+
