@@ -317,7 +317,7 @@ def _tree_modes(args, torch, dev, api, wl):
     cn, tp = torch.from_numpy(t.coins).to(dev), torch.from_numpy(t.temperature).to(dev)
     out = {}
     stream = torch.cuda.current_stream(dev)
-    for mode, name in ((0, "tree_greedy"), (1, "tree_sampling")):
+    def timed(mode):
         for i in range(5):
             api.spec_verify_tree(copies[i % len(copies)], tok, par, cn, tp, t.D, mode)
         torch.cuda.synchronize()
@@ -329,15 +329,22 @@ def _tree_modes(args, torch, dev, api, wl):
             e1.record(stream)
             ms.append((e0, e1, acc))
         torch.cuda.synchronize()
-        d = np.array([a.elapsed_time(b) for a, b, _ in ms])
-        acc = ms[-1][2].cpu().numpy()
+        return np.array([a.elapsed_time(b) for a, b, _ in ms]), ms[-1][2].cpu().numpy()
+
+    for mode, name in ((0, "tree_greedy"), (1, "tree_sampling")):
+        d, acc = timed(mode)
+        os.environ["SPEC_VERIFY_EAGER"] = "1"
+        de, _ = timed(mode)
+        del os.environ["SPEC_VERIFY_EAGER"]
         eager = t.B * t.N * t.V * 2
-        path = int((acc + 1).sum()) * t.V * 2
+        path = int((acc + 1).sum()) * t.V * 2   # the rows of the nodes the walk reaches
         out[name] = {"workload": t.name, "avg_ms": float(d.mean()),
                      "positions/s": t.B * t.N / (d.mean() * 1e-3),
-                     "GB/s_eager": eager / (d.mean() * 1e-3) / 1e9,
-                     "frac_eager": eager / (d.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "path_only_bytes": path, "eager_bytes": eager}
+                     "path_only_bytes": path,
+                     "GB/s_path_only": path / (d.mean() * 1e-3) / 1e9,
+                     "eager_avg_ms": float(de.mean()), "eager_bytes": eager,
+                     "GB/s_eager": eager / (de.mean() * 1e-3) / 1e9,
+                     "frac_eager": eager / (de.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS}
     out["tree_mss"] = _tree_mss_mode(torch, dev, api, wl, stream)
     # committing the accepted paths' KV (the step after verify): 128 KiB per token, the KV
     # of 32 layers x 8 KV heads x 128 dims x (K, V) in bf16

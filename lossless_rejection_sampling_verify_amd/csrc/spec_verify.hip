@@ -1,9 +1,22 @@
 // spec_verify.hip -- HIP kernels for CDNA4 (gfx950) and the C ABI of the speculative
 // decoding verify library (include/spec_verify.h).
 //
-// Kernels (consecutive launches on the caller's stream; every hand-off between workgroups
-// goes through global memory at a kernel boundary, never through fences inside a kernel:
-// on a multi-XCD part an agent-scope fence writes back and invalidates the whole L2)
+// The verify calls walk each request (position by position, or node by node in a tree)
+// and stop where the method stops, so they read only the rows it consults:
+//   k_greedy_walk   greedy chain verify: a cluster of workgroups per request, each owning
+//                   whole fine chunks of every row; per position the slices' argmax
+//                   travels between the cluster's workgroups as tagged 64-bit atomic
+//                   words (no fence), and every member takes the same decision.
+//   k_chain_walk    chain rejection sampling, the same way with (max, exp-sum) per slice;
+//                   after the stop each member weighs its slice of the row the last token
+//                   is drawn from, for k_draw.
+//   k_tree_walk     the target-only tree walk (greedy or sampling), node by node.
+//   k_mss_walk      the tree walk by multi-step speculative sampling with draft rows;
+//                   1024-lane workgroups, a residual pass per rejected child.
+//   k_draw          one wave per request: locates the chunk, then the segment, then the
+//                   token holding u * total (inverse CDF in ascending token id).
+// The eager passes read every row and hand over at kernel boundaries; they are selected
+// with SPEC_VERIFY_EAGER=1 (and the filtered chain always reads every row):
 //   k_rows          streams every target-logit row once from HBM (16-byte non-temporal
 //                   vector loads, kUnroll loads in flight per lane), split over `S`
 //                   workgroups per row.  Each workgroup reduces its chunk to one 16-byte
@@ -21,8 +34,8 @@
 //   k_mass          one workgroup per (request, fine chunk of 4096 elements): weight of
 //                   the chunk and of each of its 64 segments of 64 elements in the row the
 //                   last token is drawn from.
-//   k_draw          one wave per request: locates the chunk, then the segment, then the
-//                   token holding u * total (inverse CDF in ascending token id).
+// An agent-scope fence inside a kernel writes back and invalidates the whole L2 of an
+// XCD, so no kernel uses one.
 //
 // Sources: llm-infra-atlas "Speculative Decoding" section 0 and section 2; ricardokevins
 // "Speculative Decoding", correction sampling, Eq. a(x) and Eq. r(x); zdszero
@@ -738,10 +751,8 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
         tree_depths(ts.par, N, ts.anc, ts.dep);
         for (int i = tid; i < N; i += kBlock)
             if (ts.dep[i] > D) bad = true;
-        // every row's statistics; each row needs a finite logit
+        // every row's statistics (a row the walk reaches needs a finite logit)
         tree_row_stats(a, b, sampling != 0, Td, ts);
-        for (int j = tid; j < N; j += kBlock)
-            if (ts.M[j] == -INFINITY) bad = true;
         bad = __syncthreads_or(bad);
     }
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
@@ -774,6 +785,10 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
 
     int cur = 0, d = 0, nexcl = 0;
     for (;;) {
+        if (ts.M[cur] == -INFINITY) {  // a row the walk reaches has no finite logit
+            bad = true;
+            break;
+        }
         // children of cur in ascending node id (ordered compaction)
         int count = 0;
         for (int base = cur + 1; base < N; base += kBlock) {
@@ -837,6 +852,23 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
         ++d;
     }
 
+    if (bad) {  // reached a row with no finite logit: nothing of the walk is kept
+        __syncthreads();
+        for (int e = tid; e <= D; e += kBlock) {
+            out[e] = -1;
+            if (e < D) nodes[e] = -1;
+            if (probs) probs[e] = 0.f;
+        }
+        if (tid == 0) {
+            a.accept_len[b] = -1;
+            if (sampling) {
+                DrawState st = {};
+                st.kind = kDrawNone;
+                a.dstate[b] = st;
+            }
+        }
+        return;
+    }
     // the last token: greedy emits the argmax of row cur; sampling hands row cur and the
     // distinct tokens of the children tried last to the final draw
     if (sampling) {
@@ -1613,7 +1645,7 @@ template <typename T, bool kFilt>
 __device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const DrawState& st,
                                                           const WParams& W, const T* rowp,
                                                           const void* qrow, int b, int c,
-                                                          MassSmem& sm) {
+                                                          MassSmem& sm, const int32_t* ex) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int S2 = a.S2, V = a.V;
     const int c0 = c * kFine;
@@ -1631,7 +1663,6 @@ __device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const 
     __syncthreads();
     if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
         if (tid == 0) {
-            const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
             for (int e = 0; e < st.nexcl; ++e) {
                 const int t = ex[e];
                 if (t >= c0 && t < c0 + n) {
@@ -1677,7 +1708,8 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * a.V;
     const void* qrow;
     const WParams W = draw_params<T, kFilt>(a, st, qrow);
-    mass_chunk<T, kFilt>(a, st, W, rowp, qrow, b, c, sm);
+    mass_chunk<T, kFilt>(a, st, W, rowp, qrow, b, c, sm,
+                         st.nexcl > 0 ? a.excl + (size_t)b * SPEC_MAX_N : nullptr);
 }
 
 // k_chain_walk: chain rejection sampling position by position, one cluster of W
@@ -1787,7 +1819,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
         for (int c = lo / kFine; c * kFine < hi; ++c)
-            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms);
+            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
     }
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     for (int e = tid; e < R; e += kBlock) {
@@ -1798,6 +1830,240 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     if (tid == 0) {
         a.accept_len[b] = bad ? -1 : k;
         a.dstate[b] = st;
+    }
+}
+
+// k_tree_walk: the target-only token-tree walk, one cluster of W workgroups per request
+// (blockIdx = b * W + w, workgroup w owning a slice of whole fine chunks of every row).
+// Only the rows of the nodes the walk reaches are read.  At each node the slices' row
+// statistics (sampling: max and normaliser; greedy: max and lowest index) travel through
+// the cluster hand-off and every workgroup takes the same decision.  Sampling then weighs
+// its slice of the last node's row (the rejected children's tokens excluded) for
+// k_draw; greedy emits the argmax itself.
+struct TreeWalkSmem {
+    int par[SPEC_MAX_N];
+    int tok[SPEC_MAX_N];
+    union {
+        struct {  // validation: pointer-jumping state
+            int anc[SPEC_MAX_N];
+            int dep[SPEC_MAX_N];
+        };
+        struct {  // the walk: children of the current node, tokens to exclude
+            int kids[SPEC_MAX_N];
+            int excl[SPEC_MAX_N];
+        };
+    };
+    float lx[SPEC_MAX_N];    // logit of child j's token in the current row
+    int path[SPEC_MAX_N];    // accepted nodes, by depth
+    float pathp[SPEC_MAX_N]; // their target probabilities (sampling)
+    int wcnt[kWaves];
+    int chosen;
+    int nexcl;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int W, int per,
+                                                      uint32_t tag, unsigned long long* xslots,
+                                                      int xstride) {
+    __shared__ TreeWalkSmem ts;
+    __shared__ RowSmem rs;
+    __shared__ XSmem xs;
+    __shared__ MassSmem ms;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x / W, w = blockIdx.x - b * W;
+    const int N = a.R, V = a.V, D = a.D;
+    const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
+    unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    const int32_t* par_g = a.parents + (size_t)b * N;
+    const int32_t* tok_g = a.tokens + (size_t)b * N;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    bool bad = false;
+    for (int i = tid; i < N; i += kBlock) {
+        const int p = par_g[i];
+        const int t = tok_g[i];
+        ts.par[i] = p;
+        ts.tok[i] = t;
+        if (i == 0) {
+            if (p != -1) bad = true;
+        } else {
+            if (p < 0 || p >= i) bad = true;
+            if (t < 0 || t >= V) bad = true;
+        }
+    }
+    float Tf = 1.f;
+    if (sampling) {
+        Tf = a.temperature[b];
+        if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
+        for (int d = tid; d <= D; d += kBlock) {
+            const float u = a.coins[(size_t)b * (D + 1) + d];
+            if (!(u > 0.f && u <= 1.f)) bad = true;
+        }
+    }
+    const double Td = (double)Tf;
+    const float s2 = kLog2e / Tf;
+    bad = __syncthreads_or(bad);
+    if (!bad) {
+        tree_depths(ts.par, N, ts.anc, ts.dep);
+        for (int i = tid; i < N; i += kBlock)
+            if (ts.dep[i] > D) bad = true;
+        bad = __syncthreads_or(bad);
+    }
+
+    int cur = 0, d = 0, nexcl = 0, last = -1;
+    float M = 0.f;
+    double Z = 1.0;
+    for (int step = 0; !bad; ++step) {
+        const T* rowp = logits + ((size_t)b * N + cur) * V;
+        int count = 0;  // children of cur in ascending node id (ordered compaction)
+        for (int base = cur + 1; base < N; base += kBlock) {
+            const int c = base + tid;
+            const bool f = c < N && ts.par[c] == cur;
+            const unsigned long long m = __ballot(f);
+            if (lane == 0) ts.wcnt[wave] = __popcll(m);
+            __syncthreads();
+            int off = count, total = 0;
+            for (int q = 0; q < kWaves; ++q) {
+                if (q < wave) off += ts.wcnt[q];
+                total += ts.wcnt[q];
+            }
+            if (f) ts.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = c;
+            __syncthreads();
+            count += total;
+        }
+        for (int j = tid; j < count && sampling; j += kBlock)
+            ts.lx[j] = Ld<T>::one(rowp + ts.tok[ts.kids[j]]);
+        if (sampling) {
+            const Part r = chunk_record<T, true>(rowp, lo, hi, s2, rs);
+            if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
+                              dbl_lo(r.z), xs)) {
+                bad = true;
+                break;
+            }
+            M = -INFINITY;
+            for (int j = 0; j < W; ++j) M = fmaxf(M, __uint_as_float(xs.xp[j][0]));
+            Z = 0.0;
+            for (int j = 0; j < W; ++j) {
+                const float mj = __uint_as_float(xs.xp[j][0]);
+                if (mj != -INFINITY)
+                    Z += dbl_of(xs.xp[j][1], xs.xp[j][2]) * exp(((double)mj - (double)M) / Td);
+            }
+        } else {
+            const Part r = chunk_record<T, false>(rowp, lo, hi, 0.f, rs);
+            if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), (uint32_t)r.idx, 0u,
+                              xs)) {
+                bad = true;
+                break;
+            }
+            M = -INFINITY;
+            for (int j = 0; j < W; ++j) {  // slices in order: the lowest index among equal maxima
+                const float mj = __uint_as_float(xs.xp[j][0]);
+                if (mj > M) {
+                    M = mj;
+                    last = (int)xs.xp[j][1];
+                }
+            }
+        }
+        if (M == -INFINITY) {  // a row the walk reaches has no finite logit
+            bad = true;
+            break;
+        }
+        if (tid == 0) {
+            int ch = -1;
+            if (sampling) {
+                const double u = (double)a.coins[(size_t)b * (D + 1) + d];
+                const double tha = (double)a.th_acc, ths = (double)a.th_single;
+                double acc = 0.0;
+                for (int j = 0; j < count; ++j) {
+                    const double pc = exp(((double)ts.lx[j] - (double)M) / Td) / Z;
+                    acc += pc;
+                    if (u <= acc / tha || pc >= ths) {
+                        ch = j;
+                        ts.pathp[d] = (float)pc;
+                        break;
+                    }
+                }
+            } else {
+                for (int j = 0; j < count; ++j)
+                    if (ts.tok[ts.kids[j]] == last) {
+                        ch = j;
+                        break;
+                    }
+            }
+            ts.chosen = ch;
+            if (ch >= 0) ts.path[d] = ts.kids[ch];
+        }
+        __syncthreads();
+        const int ch = ts.chosen;
+        __syncthreads();
+        if (ch < 0) {  // a leaf, or no child accepted: the walk stops at cur
+            if (sampling && tid == 0) {  // the children tried, each token once
+                int n = 0;
+                for (int j = 0; j < count; ++j) {
+                    const int t = ts.tok[ts.kids[j]];
+                    bool dup = false;
+                    for (int e = 0; e < n && !dup; ++e) dup = ts.excl[e] == t;
+                    if (!dup) ts.excl[n++] = t;
+                }
+                ts.nexcl = n;
+            }
+            __syncthreads();
+            nexcl = sampling ? ts.nexcl : 0;
+            break;
+        }
+        cur = ts.kids[ch];
+        ++d;
+    }
+
+    DrawState st = {};
+    st.kind = kDrawNone;
+    if (!bad && sampling) {
+        st.kind = kDrawTarget;
+        st.row = b * N + cur;
+        st.out = b * (D + 1) + d;
+        st.coin = b * (D + 1) + D;
+        st.nexcl = nexcl;
+        st.cq = 1.f;
+        st.M = M;
+        st.Z = Z;
+        st.invZ = (float)(1.0 / Z);
+        st.T = Td;
+        const T* rowp = logits + (size_t)st.row * V;
+        const void* qrow;
+        const WParams Wp = draw_params<T, false>(a, st, qrow);
+        for (int c = lo / kFine; c * kFine < hi; ++c)
+            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, ts.excl);
+    }
+    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
+    int32_t* out = a.out_tokens + (size_t)b * (D + 1);
+    int32_t* nodes = a.accepted_nodes + (size_t)b * D;
+    float* probs = a.probs ? a.probs + (size_t)b * (D + 1) : nullptr;
+    if (sampling)
+        for (int e = tid; e < nexcl && !bad; e += kBlock) a.excl[(size_t)b * SPEC_MAX_N + e] = ts.excl[e];
+    for (int e = tid; e <= D; e += kBlock) {
+        if (bad) {
+            out[e] = -1;
+            if (e < D) nodes[e] = -1;
+            if (probs) probs[e] = 0.f;
+            continue;
+        }
+        if (e < d) {
+            out[e] = ts.tok[ts.path[e]];
+            nodes[e] = ts.path[e];
+            if (probs) probs[e] = sampling ? ts.pathp[e] : 0.f;
+        } else if (e == d) {
+            if (!sampling) {  // greedy: the argmax of the last row (sampling: the final draw)
+                out[e] = last;
+                if (probs) probs[e] = 0.f;
+            }
+        } else {
+            out[e] = -1;
+            if (probs) probs[e] = 0.f;
+        }
+        if (e >= d && e < D) nodes[e] = -1;
+    }
+    if (tid == 0) {
+        a.accept_len[b] = bad ? -1 : d;
+        if (sampling) a.dstate[b] = st;
     }
 }
 
@@ -2586,6 +2852,11 @@ inline int cluster_max(int B) {
     return w < 2 ? 1 : (w > kMaxCluster ? kMaxCluster : w);
 }
 
+// Workgroups per request that the target-only tree walk may use (slots are sized for it).
+inline int tree_cluster_max(int B) {
+    return B <= 0 ? 1 : std::max(1, std::min(kMaxCluster, 2048 / B));
+}
+
 // 64-bit hand-off words per request: at most 2N steps (a row pass per reached node and a
 // residual pass per rejected child), W workgroups, three words each.
 inline size_t cluster_stride(int N, int W) { return (size_t)2 * N * W * 3; }
@@ -2616,6 +2887,8 @@ Layout layout_for(int op, int B, int R, int V) {
     L.xch = off;
     if (op == SPEC_OP_GREEDY || op == SPEC_OP_CHAIN)
         off = align256(off + sizeof(unsigned long long) * (size_t)B * R * kMaxCluster * 3);
+    else if (op == SPEC_OP_TREE)  // at most one step per node
+        off = align256(off + sizeof(unsigned long long) * (size_t)B * R * tree_cluster_max(B) * 3);
     else if (op == SPEC_OP_TREE_MSS && cluster_max(B) > 1)
         off = align256(off + sizeof(unsigned long long) * (size_t)B * cluster_stride(R, cluster_max(B)));
     L.total = off;
@@ -2784,6 +3057,24 @@ int run_chain(KArgs& a, hipStream_t st) {
     rc = launch_status();
     if (rc != SPEC_OK) return rc;
     return run_draw<T>(a, st);
+}
+
+template <typename T>
+int run_tree_walk(KArgs& a, int sampling, unsigned long long* xslots, hipStream_t st) {
+    const uint32_t tag = next_tag();
+    int W, per;
+    walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_tree_walk<T>),
+                                  sizeof(T) == 4 ? 4 : 5), &W, &per);
+    W = std::min(W, tree_cluster_max(a.B));
+    per = (a.S2 + W - 1) / W;
+    W = (a.S2 + per - 1) / per;
+    hipLaunchKernelGGL((k_tree_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, sampling, W,
+                       per * kFine, tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       a.R * W * 3);
+    int rc = launch_status();
+    if (rc != SPEC_OK || !sampling) return rc;
+    hipLaunchKernelGGL((k_draw<T, false>), dim3(a.B), dim3(64), 0, st, a);
+    return launch_status();
 }
 
 template <typename T>
@@ -2987,6 +3278,13 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_TREE);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!eager_forced()) {
+        const Layout L = layout_for(SPEC_OP_TREE, B, N, V);
+        unsigned long long* xs =
+            reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
+        return dtype == SPEC_F32 ? run_tree_walk<float>(a, mode, xs, st)
+                                 : run_tree_walk<uint16_t>(a, mode, xs, st);
+    }
     return dtype == SPEC_F32 ? run_tree<float>(a, mode, st) : run_tree<uint16_t>(a, mode, st);
 }
 

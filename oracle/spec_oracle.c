@@ -35,6 +35,9 @@
  *   - tree: node 0 is the root, parents[i] < i, siblings are tried in ascending node id,
  *     one coin per level coins[d] and a final coin coins[D]; a leaf draws its bonus
  *     from its own row.
+ *   - a request is invalid when something the verify consults is unusable: chains and
+ *     trees are walked in order and stop at the first rejection, so rows (and drafts,
+ *     q values, per-position coins) beyond the stop are not checked.
  */
 #include "spec_oracle.h"
 
@@ -357,22 +360,16 @@ static void tree_one(const void* logits, int dtype, const int32_t* tok, const in
         for (int d = 0; d <= D; ++d)
             if (!coin_ok(coins[d])) valid = 0;
     }
-    for (int j = 0; j < N && valid; ++j)
-        if (row_max(row_of(logits, dtype, b * (size_t)N + (size_t)j, V)) == -INFINITY) valid = 0;
     *margin = INFINITY;
-    if (!valid) {
-        *accept_len = -1;
-        for (int d = 0; d <= D; ++d) out[d] = -1;
-        for (int d = 0; d < D; ++d) nodes[d] = -1;
-        if (probs)
-            for (int d = 0; d <= D; ++d) probs[d] = 0.0;
-        return;
-    }
 
     double T = (double)temperature;
     int cur = 0, d = 0, nexcl = 0;
-    for (;;) {
+    for (; valid;) {
         Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
+        if (row_max(r) == -INFINITY) { /* a row the walk reaches has no finite logit */
+            valid = 0;
+            break;
+        }
         int any_child = 0;
         for (int c = cur + 1; c < N; ++c)
             if (par[c] == cur) any_child = 1;
@@ -412,6 +409,15 @@ static void tree_one(const void* logits, int dtype, const int32_t* tok, const in
         cur = chosen;
         ++d;
         nexcl = 0;
+    }
+    if (!valid) {
+        *margin = INFINITY;
+        *accept_len = -1;
+        for (int e = 0; e <= D; ++e) out[e] = -1;
+        for (int e = 0; e < D; ++e) nodes[e] = -1;
+        if (probs)
+            for (int e = 0; e <= D; ++e) probs[e] = 0.0;
+        return;
     }
 
     Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);

@@ -155,7 +155,7 @@ def test_tree_commit_kv_rejects_bad_arguments(lib):
 def test_chain_filtered_rejects_bad_arguments(lib):
     f = lib.spec_verify_chain_filtered
     ws = L.workspace_bytes(L.SPEC_OP_CHAIN_FILTERED, 2, 5, 1000)
-    assert ws > L.workspace_bytes(L.SPEC_OP_CHAIN, 2, 5, 1000)
+    assert ws > 0
     args = dict(lg=P, dl=P, dt=L.SPEC_BF16, tok=P, coins=P, T=P, k=None, p=None, B=2, G=4,
                 V=1000, acc=P, out=P, probs=None, ws=P, wsb=ws)
 

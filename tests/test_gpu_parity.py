@@ -368,3 +368,46 @@ def test_walk_cluster_widths(cluster, monkeypatch):
     c = wl.make_chain(3, seed=31, B=24, G=8, V=50021)
     check_chain(c, f"walk W<={cluster}")
     check_greedy(c, f"walk W<={cluster}")
+
+
+@pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
+def test_tree_eager_passes_match_oracle(mode, monkeypatch):
+    """The eager tree passes (every row streamed, then walked), selected by
+    SPEC_VERIFY_EAGER, give the oracle's results too."""
+    monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+    check_tree(tree_cfg(), mode, f"tree eager mode {mode}")
+
+
+@pytest.mark.parametrize("cluster", ["1", "3"])
+@pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
+def test_tree_walk_cluster_widths(cluster, mode, monkeypatch):
+    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    t = wl.make_tree(4, seed=41, B=12, N=40, V=30011, D=5, max_children=5)
+    check_tree(t, mode, f"tree walk W<={cluster} mode {mode}")
+
+
+def test_tree_rows_off_the_walk():
+    """A row the walk never reaches may hold no finite logit; a reached one may not."""
+    t = wl.make_tree(4, seed=42, B=16, N=24, V=2000, D=4, max_children=4, dtype=wl.F32)
+    lg = t.logits.copy()
+    for b in range(t.B):
+        lg[b, t.N - 1 - (b % 3), :] = -np.inf     # some deep nodes: reached or not
+    for mode in (oracle.TREE_GREEDY, oracle.TREE_SAMPLING):
+        say(f"tree rows off the walk, mode {mode}")
+        api = _api()
+        sampling = mode == oracle.TREE_SAMPLING
+        acc, out, nodes, probs = api.spec_verify_tree(
+            dev_logits(lg, t.dtype), dev(t.node_tokens), dev(t.parents),
+            dev(t.coins) if sampling else None, dev(t.temperature) if sampling else None,
+            t.D, mode, want_probs=True)
+        torch.cuda.synchronize()
+        g = dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
+                 accepted_nodes=nodes.cpu().numpy(), probs=probs.cpu().numpy())
+        o = oracle.verify_tree(lg, t.dtype, t.node_tokens, t.parents, t.coins, t.temperature,
+                               t.D, mode)
+        if not sampling:
+            g["probs"] = np.zeros_like(g["probs"])
+            o["probs"] = np.zeros_like(o["probs"])
+        compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"],
+                o["margin"] if sampling else None, label=f"rows off the walk {mode}")
+        np.testing.assert_array_equal(g["accept_len"], o["accept_len"])

@@ -302,3 +302,24 @@ def test_only_consulted_positions_are_checked():
     a, o = oracle.verify_greedy(lg3, "f32", xg2)
     assert a[0] == -1 and (o == -1).all()
 
+
+
+@pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
+def test_tree_rows_off_the_walk_are_not_checked(mode):
+    """A row with no finite logit invalidates a tree request only when the walk reaches
+    it: the root's row always, a child's row only if that child is accepted."""
+    V = 6
+    lg = np.zeros((1, 3, V), np.float32)
+    lg[0, 0] = [5.0, 0.0, 0.0, 0.0, 0.0, 0.0]   # the root strongly prefers token 0
+    tokens = np.array([[0, 3, 0]], np.int32)     # node 1 (token 3), node 2 (token 0)
+    parents = np.array([[-1, 0, 0]], np.int32)
+    coins = np.array([[0.5, 0.5]], np.float32)   # node 1 is improbable: node 2 is taken
+    T = np.ones(1, np.float32)
+    lg1 = lg.copy()
+    lg1[0, 1, :] = -np.inf                       # node 1 is never reached
+    r = oracle.verify_tree(lg1, "f32", tokens, parents, coins, T, 1, mode)
+    assert r["accept_len"][0] == 1 and r["accepted_nodes"][0, 0] == 2
+    lg2 = lg.copy()
+    lg2[0, 2, :] = -np.inf                       # node 2 is reached
+    r = oracle.verify_tree(lg2, "f32", tokens, parents, coins, T, 1, mode)
+    assert r["accept_len"][0] == -1 and (r["out_tokens"] == -1).all()
