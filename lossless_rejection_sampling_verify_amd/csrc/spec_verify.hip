@@ -909,206 +909,17 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
 }
 
 // ---------------------------------------------------------------------------------------
-// k_mss_walk: a token tree verified by multi-step speculative sampling with draft rows.
-// One workgroup of kWalk threads per request walks the tree and reads only the rows it
-// reaches.
-//
-// At node cur, one pass over the target row gives its max M and normaliser Z.  The
-// children are tested in ascending node id.  After r rejections the node's distribution
-// is p^(r) = max(0, p - c_r q) / N_r, with c_0 = 0 and N_0 = 1.  On the next rejection
-// c_{r+1} = c_r + N_r and N_{r+1} = sum_v max(0, p_v - c_{r+1} q_v).  This works because
-// all children share one draft row q: the repeated residual norm(max(0, p^(r) - q))
-// collapses to one coefficient on q (where p - c_r q <= 0, the next residual is 0 too).
-// Each rejection therefore costs one pass over (target row, draft row), and no vector is
-// kept.  c is rounded to fp32 once per step and that value is used everywhere.
-//
-// Child x is accepted iff p^(r)(x) > 0 and its coin <= p^(r)(x) / q(x); when q(x) = 0,
-// iff p^(r)(x) > 0.  When every child is rejected, k_mass and k_draw draw the last token
-// from max(0, p - c_R q).  They draw from plain p at a leaf, or when a residual has no
-// mass left.
+// The cluster hand-off used by the walks (k_greedy_walk, k_chain_walk, k_tree_walk,
+// k_mss_walk): W workgroups share one request, each owning a slice of every row, and
+// after every pass they exchange three 32-bit payloads per workgroup.
 
-constexpr int kWalk = 1024;
-constexpr int kWalkWaves = kWalk / 64;
 constexpr int kMaxCluster = 16;    // workgroups sharing one request's walk
-constexpr int kClusterSlots = 256; // cluster workgroups per call at most (sizes the slots)
 constexpr long kSpinMax = 1 << 18; // bound of a cluster wait (never reached when all run)
 
 struct XSmem {
     uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
     int xbad;
 };
-
-struct MssSmem {
-    int par[SPEC_MAX_N];
-    int tok[SPEC_MAX_N];
-    union {
-        struct {  // validation: pointer-jumping state
-            int anc[SPEC_MAX_N];
-            int dep[SPEC_MAX_N];
-        };
-        struct {  // the walk: children of the current node, p_cur of their tokens
-            int kids[SPEC_MAX_N];
-            double pxc[SPEC_MAX_N];
-        };
-    };
-    float qx[SPEC_MAX_N];     // q_parent(token of node c), by node id
-    int path[SPEC_MAX_N];     // accepted nodes, by depth
-    float pathp[SPEC_MAX_N];  // their target probabilities
-    float rm[kWalkWaves];
-    double rz[kWalkWaves];
-    int wcnt[kWalkWaves];
-    int flag;
-    XSmem x;
-};
-
-// Block-wide max / sum over the kWalk threads (every thread gets the same bits).
-__device__ inline float walk_max(float v, MssSmem& sm) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_max(v);
-    __syncthreads();  // the previous reduction has read sm.rm
-    if (lane == 0) sm.rm[wave] = v;
-    __syncthreads();
-    float r = sm.rm[0];
-    for (int w = 1; w < kWalkWaves; ++w) r = fmaxf(r, sm.rm[w]);
-    return r;
-}
-
-__device__ inline double walk_sum(double v, MssSmem& sm) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_sum(v);
-    __syncthreads();
-    if (lane == 0) sm.rz[wave] = v;
-    __syncthreads();
-    double r = sm.rz[0];
-    for (int w = 1; w < kWalkWaves; ++w) r += sm.rz[w];
-    return r;
-}
-
-// Max and normaliser of one target row: per thread an online (m, z) over batches of
-// kRowVecs 16-byte vectors, all loads of a batch in flight at once (one batch covers a
-// 256 KB row), fp32 batch sums added in fp64; then a block reduction.
-constexpr int kRowVecs = 8;
-template <typename T>
-constexpr int res_quads() { return sizeof(T) == 4 ? 4 : 8; }  // four-element groups per batch
-
-template <typename T>
-__device__ void walk_row_stats(const T* rowp, int V, float s2, double Td, MssSmem& sm,
-                               float& M_out, double& Z_out) {
-    const int tid = threadIdx.x;
-    constexpr int kVec = Ld<T>::kVec;
-    float m = -INFINITY;
-    double z = 0.0;
-    int done = 0;
-    if (((uintptr_t)rowp) % 16 == 0) {
-        const int nv = V / kVec;
-        const u32x4* rv = reinterpret_cast<const u32x4*>(rowp);
-        for (int i0 = 0; i0 < nv; i0 += kWalk * kRowVecs) {
-            u32x4 r[kRowVecs];
-#pragma unroll
-            for (int u = 0; u < kRowVecs; ++u) {
-                const int i = i0 + u * kWalk + tid;
-                if (i < nv) r[u] = ld_stream(rv + i);
-            }
-            float bm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < kRowVecs; ++u) {
-                if (i0 + u * kWalk + tid < nv) {
-                    float l[kVec];
-                    Ld<T>::unpack(r[u], l);
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) bm = fmaxf(bm, l[e]);
-                }
-            }
-            if (bm != -INFINITY) {
-                if (bm > m) {
-                    z = m == -INFINITY ? 0.0 : z * (double)ex2((m - bm) * s2);
-                    m = bm;
-                }
-                float bs = 0.f;
-#pragma unroll
-                for (int u = 0; u < kRowVecs; ++u) {
-                    if (i0 + u * kWalk + tid < nv) {
-                        float l[kVec];
-                        Ld<T>::unpack(r[u], l);
-#pragma unroll
-                        for (int e = 0; e < kVec; ++e) bs += ex2((l[e] - m) * s2);
-                    }
-                }
-                z += (double)bs;
-            }
-        }
-        done = nv * kVec;
-    }
-    for (int j0 = done; j0 < V; j0 += kWalk) {  // the tail, or an unaligned row
-        const int j = j0 + tid;
-        if (j < V) {
-            const float l = Ld<T>::one(rowp + j);
-            if (l != -INFINITY) {
-                if (l > m) {
-                    z = m == -INFINITY ? 0.0 : z * (double)ex2((m - l) * s2);
-                    m = l;
-                }
-                z += (double)ex2((l - m) * s2);
-            }
-        }
-    }
-    const float M = walk_max(m, sm);
-    const double term = m == -INFINITY ? 0.0 : z * exp(((double)m - (double)M) / Td);
-    M_out = M;
-    Z_out = walk_sum(term, sm);
-}
-
-// N(c) = sum_v max(0, p_v - c q_v) over one (target row, draft row) pair, with the draw
-// kernels' weight formula (p_v = exp2((l_v - M) * s2) * invZ in fp32).  Batches of
-// res_quads<T>() four-element groups per thread, all loads of a batch in flight.
-template <typename T>
-__device__ double walk_resid_sum(const T* rowp, const float* qrow, int V, float M, float s2,
-                                 float invZ, float cq, MssSmem& sm) {
-    const int tid = threadIdx.x;
-    constexpr int kRQ = res_quads<T>();
-    double acc = 0.0;
-    int done = 0;
-    if (((uintptr_t)rowp) % (4 * sizeof(T)) == 0 && ((uintptr_t)qrow) % 16 == 0) {
-        const int nq = V / 4;
-        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp);
-        const u32x4* qq = reinterpret_cast<const u32x4*>(qrow);
-        for (int i0 = 0; i0 < nq; i0 += kWalk * kRQ) {
-            typename Quad<T>::Raw lr[kRQ];
-            u32x4 qr[kRQ];
-#pragma unroll
-            for (int u = 0; u < kRQ; ++u) {
-                const int i = i0 + u * kWalk + tid;
-                if (i < nq) {
-                    lr[u] = lq[i].raw;
-                    qr[u] = qq[i];
-                }
-            }
-            float bs = 0.f;
-#pragma unroll
-            for (int u = 0; u < kRQ; ++u) {
-                if (i0 + u * kWalk + tid < nq) {
-                    float l[4];
-                    Quad<T>::unpack(lr[u], l);
-                    const float qv[4] = {__uint_as_float(qr[u].x), __uint_as_float(qr[u].y),
-                                         __uint_as_float(qr[u].z), __uint_as_float(qr[u].w)};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        bs += fmaxf(ex2((l[e] - M) * s2) * invZ - cq * qv[e], 0.f);
-                }
-            }
-            acc += (double)bs;
-        }
-        done = nq * 4;
-    }
-    for (int j0 = done; j0 < V; j0 += kWalk) {
-        const int j = j0 + tid;
-        if (j < V) {
-            const float p = ex2((Ld<T>::one(rowp + j) - M) * s2) * invZ;
-            acc += (double)fmaxf(p - cq * qrow[j], 0.f);
-        }
-    }
-    return walk_sum(acc, sm);
-}
 
 // One step of a cluster: every workgroup of the request hands three 32-bit payloads to
 // the others.  Each payload travels in a 64-bit word whose high half is the call's tag;
@@ -1179,211 +990,6 @@ __device__ inline uint32_t dbl_hi(double x) { return (uint32_t)((unsigned long l
 __device__ inline uint32_t dbl_lo(double x) { return (uint32_t)__double_as_longlong(x); }
 __device__ inline double dbl_of(uint32_t hi, uint32_t lo) {
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
-// One request per cluster of W workgroups (blockIdx = b * W + w).  Workgroup w owns the
-// vocabulary slice [w * per, (w + 1) * per) of every row.  The row statistics and
-// residual masses are combined across the cluster in workgroup order, so every
-// workgroup of the cluster takes the same decisions, and workgroup 0 writes the outputs.
-//
-// The host picks W so that all B * W workgroups fit on the device at once.  Even when
-// they do not, the waits end: workgroups start in increasing id on every XCD, so the
-// lowest-numbered unfinished cluster always has all its workgroups started.  Every wait
-// is also bounded.
-//
-// A cooperative launch would guarantee residency, but it cost about 17 us more per call.
-template <typename T>
-__global__ __launch_bounds__(kWalk) void k_mss_walk(KArgs a, int W, uint32_t tag,
-                                                    unsigned long long* xslots, int xstride) {
-    __shared__ MssSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x / W, w = blockIdx.x - b * W;
-    const int N = a.R, V = a.V, D = a.D;
-    const int per = ((V + W - 1) / W + 7) / 8 * 8;
-    const int lo = min(V, w * per), n = min(V, lo + per) - lo;
-    unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
-    int step = 0;
-    const int32_t* par_g = a.parents + (size_t)b * N;
-    const int32_t* tok_g = a.tokens + (size_t)b * N;
-    const float* coins = a.coins + (size_t)b * N;
-    const T* logits = reinterpret_cast<const T*>(a.logits);
-    bool bad = false;
-    for (int i = tid; i < N; i += kWalk) {
-        const int p = par_g[i];
-        const int t = tok_g[i];
-        sm.par[i] = p;
-        sm.tok[i] = t;
-        if (i == 0) {
-            if (p != -1) bad = true;
-        } else {
-            if (p < 0 || p >= i) bad = true;
-            if (t < 0 || t >= V) bad = true;
-        }
-        const float u = coins[i];
-        if (!(u > 0.f && u <= 1.f)) bad = true;
-    }
-    const float Tf = a.temperature[b];
-    if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
-    const double Td = (double)Tf;
-    bad = __syncthreads_or(bad);
-    if (!bad) {  // depths, and q of every child's token under its parent's draft row
-        tree_depths<kWalk>(sm.par, N, sm.anc, sm.dep);
-        for (int i = tid; i < N; i += kWalk) {
-            if (sm.dep[i] > D) bad = true;
-            if (i > 0) {
-                const float q = a.q[((size_t)b * N + sm.par[i]) * V + sm.tok[i]];
-                sm.qx[i] = q;
-                if (!(q >= 0.f && isfinite(q))) bad = true;
-            }
-        }
-        bad = __syncthreads_or(bad);
-    }
-
-    const float s2 = kLog2e / Tf;
-    int cur = 0, d = 0;
-    int kind = kDrawTarget;
-    float cq = 0.f, M = 0.f;
-    double Z = 1.0;
-    while (!bad) {
-        const T* rowp = logits + ((size_t)b * N + cur) * V;
-        int count = 0;  // children of cur in ascending node id (ordered compaction)
-        for (int base = cur + 1; base < N; base += kWalk) {
-            const int c = base + tid;
-            const bool f = c < N && sm.par[c] == cur;
-            const unsigned long long m = __ballot(f);
-            if (lane == 0) sm.wcnt[wave] = __popcll(m);
-            __syncthreads();
-            int off = count, total = 0;
-            for (int w = 0; w < kWalkWaves; ++w) {
-                if (w < wave) off += sm.wcnt[w];
-                total += sm.wcnt[w];
-            }
-            if (f) sm.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = c;
-            __syncthreads();
-            count += total;
-        }
-        // thread j gathers child j's logit while the row pass streams
-        const float lx = tid < count ? Ld<T>::one(rowp + sm.tok[sm.kids[tid]]) : 0.f;
-        {
-            float Mw;
-            double Zw;
-            walk_row_stats<T>(rowp + lo, n, s2, Td, sm, Mw, Zw);
-            if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(Mw), dbl_hi(Zw),
-                              dbl_lo(Zw), sm.x)) {
-                bad = true;
-                break;
-            }
-            M = -INFINITY;
-            for (int k = 0; k < W; ++k) M = fmaxf(M, __uint_as_float(sm.x.xp[k][0]));
-            Z = 0.0;
-            for (int k = 0; k < W; ++k) {
-                const float mk = __uint_as_float(sm.x.xp[k][0]);
-                if (mk != -INFINITY)
-                    Z += dbl_of(sm.x.xp[k][1], sm.x.xp[k][2]) * exp(((double)mk - (double)M) / Td);
-            }
-        }
-        if (M == -INFINITY) {  // a row on the walk with no finite logit
-            bad = true;
-            break;
-        }
-        if (tid < count) sm.pxc[tid] = exp(((double)lx - (double)M) / Td) / Z;
-        __syncthreads();
-        kind = kDrawTarget;
-        cq = 0.f;
-        if (count == 0) break;  // a leaf: the bonus from its own row
-        const float* qrow = a.q + ((size_t)b * N + cur) * V;
-        const float invZ = (float)(1.0 / Z);
-        double c = 0.0, Nr = 1.0;
-        int chosen = -1;
-        for (int j = 0; j < count; ++j) {
-            const int child = sm.kids[j];
-            if (tid == 0) {
-                const double px = sm.pxc[j];
-                const double qx = (double)sm.qx[child];
-                double pr = px - c * qx;
-                pr = pr > 0.0 ? pr / Nr : 0.0;
-                const double u = (double)coins[child - 1];
-                sm.flag = qx > 0.0 ? (pr > 0.0 && u <= pr / qx) : pr > 0.0;
-            }
-            __syncthreads();
-            const bool accepted = sm.flag != 0;
-            __syncthreads();
-            if (accepted) {
-                chosen = child;
-                if (tid == 0) {
-                    sm.path[d] = child;
-                    sm.pathp[d] = (float)sm.pxc[j];
-                }
-                break;
-            }
-            const double cn = (double)(float)(c + Nr);
-            if (j == count - 1) {  // every child rejected: the final residual
-                kind = kDrawResidual;
-                cq = (float)cn;
-                break;
-            }
-            const double Nw = walk_resid_sum<T>(rowp + lo, qrow + lo, n, M, s2, invZ, (float)cn, sm);
-            if (!cluster_step(slots, step++, W, w, tag, dbl_hi(Nw), dbl_lo(Nw), 0u, sm.x)) {
-                bad = true;
-                break;
-            }
-            double Nn = 0.0;
-            for (int k = 0; k < W; ++k) Nn += dbl_of(sm.x.xp[k][0], sm.x.xp[k][1]);
-            if (!(Nn > 0.0)) break;  // no residual mass left: draw from the target row
-            c = cn;
-            Nr = Nn;
-        }
-        if (bad || chosen < 0) break;
-        cur = chosen;
-        ++d;
-    }
-    __syncthreads();  // the path is in LDS
-    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
-
-    int32_t* out = a.out_tokens + (size_t)b * (D + 1);
-    int32_t* nodes = a.accepted_nodes + (size_t)b * D;
-    float* probs = a.probs ? a.probs + (size_t)b * (D + 1) : nullptr;
-    if (bad) {
-        for (int e = tid; e <= D; e += kWalk) {
-            out[e] = -1;
-            if (e < D) nodes[e] = -1;
-            if (probs) probs[e] = 0.f;
-        }
-        if (tid == 0) {
-            a.accept_len[b] = -1;
-            DrawState st = {};
-            st.kind = kDrawNone;
-            a.dstate[b] = st;
-        }
-        return;
-    }
-    for (int e = tid; e <= D; e += kWalk) {  // slot d is written by the final draw
-        if (e < d) {
-            out[e] = sm.tok[sm.path[e]];
-            nodes[e] = sm.path[e];
-            if (probs) probs[e] = sm.pathp[e];
-        } else if (e > d) {
-            out[e] = -1;
-            if (probs) probs[e] = 0.f;
-        }
-        if (e >= d && e < D) nodes[e] = -1;
-    }
-    if (tid == 0) {
-        a.accept_len[b] = d;
-        DrawState st = {};
-        st.kind = kind;
-        st.row = b * N + cur;
-        st.qrow = b * N + cur;
-        st.out = b * (D + 1) + d;
-        st.coin = b * N + N - 1;
-        st.nexcl = 0;
-        st.cq = cq;
-        st.M = M;
-        st.Z = Z;
-        st.invZ = (float)(1.0 / Z);
-        st.T = Td;
-        a.dstate[b] = st;
-    }
 }
 
 // k_greedy_walk: greedy chain verify position by position, one cluster of W workgroups
@@ -2064,6 +1670,285 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     if (tid == 0) {
         a.accept_len[b] = bad ? -1 : d;
         if (sampling) a.dstate[b] = st;
+    }
+}
+
+// Residual mass of a row slice, sum over [lo, hi) of max(0, p_v - cq q_v) with the draw
+// kernels' weights (p_v = exp2((l_v - M) * s2) * invZ in fp32), fp32 sums of four-element
+// groups added in fp64; block-wide, every lane gets the same bits.
+template <typename T>
+__device__ double slice_resid_sum(const T* rowp, const float* qrow, int lo, int hi, float M,
+                                  float s2, float invZ, float cq, RowSmem& rs) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double acc = 0.0;
+    int done = lo;
+    if (((uintptr_t)(rowp + lo)) % (4 * sizeof(T)) == 0 && ((uintptr_t)(qrow + lo)) % 16 == 0) {
+        const int nq = (hi - lo) / 4;
+        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp + lo);
+        const u32x4* qq = reinterpret_cast<const u32x4*>(qrow + lo);
+        for (int i0 = 0; i0 < nq; i0 += 4 * kBlock) {
+            typename Quad<T>::Raw lr[4];
+            u32x4 qr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kBlock + tid;
+                if (i < nq) {
+                    lr[u] = lq[i].raw;
+                    qr[u] = ld_stream(qq + i);
+                }
+            }
+            float bs = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (i0 + u * kBlock + tid < nq) {
+                    float l[4];
+                    Quad<T>::unpack(lr[u], l);
+                    const float qv[4] = {__uint_as_float(qr[u].x), __uint_as_float(qr[u].y),
+                                         __uint_as_float(qr[u].z), __uint_as_float(qr[u].w)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bs += fmaxf(ex2((l[e] - M) * s2) * invZ - cq * qv[e], 0.f);
+                }
+            }
+            acc += (double)bs;
+        }
+        done = lo + nq * 4;
+    }
+    for (int j = done + tid; j < hi; j += kBlock) {
+        const float p = ex2((Ld<T>::one(rowp + j) - M) * s2) * invZ;
+        acc += (double)fmaxf(p - cq * qrow[j], 0.f);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) rs.rz[wave] = acc;
+    __syncthreads();
+    double r = rs.rz[0];
+    for (int q = 1; q < kWaves; ++q) r += rs.rz[q];
+    __syncthreads();  // rs is reused by the next pass
+    return r;
+}
+
+// k_mss_walk: a token tree verified by multi-step speculative sampling with draft rows,
+// one cluster of W workgroups per request (blockIdx = b * W + w, workgroup w owning a slice
+// of whole fine chunks of every row).  Only the rows the walk reaches are read.
+//
+// At node cur the slices' (max, normaliser) travel through the cluster hand-off.  The
+// children are tested in ascending node id.  After r rejections the node's distribution
+// is p^(r) = max(0, p - c_r q) / N_r, with c_0 = 0 and N_0 = 1; on the next rejection
+// c_{r+1} = c_r + N_r and N_{r+1} = sum_v max(0, p_v - c_{r+1} q_v).  This holds because
+// all children share one draft row q: the repeated residual norm(max(0, p^(r) - q))
+// collapses to one coefficient on q (where p - c_r q <= 0 the next residual is 0 too).  So
+// each rejection costs one pass over the (target, draft) slices and one hand-off, and no
+// vector is kept.  c is rounded to fp32 once per step and that value is used everywhere.
+//
+// Child x is accepted iff p^(r)(x) > 0 and its coin <= p^(r)(x) / q(x) (q(x) = 0: iff
+// p^(r)(x) > 0).  When every child is rejected each member weighs its slice of
+// max(0, p - c_R q) for k_draw; at a leaf, or when a residual has no mass left, it weighs
+// plain p.
+struct MssWalkSmem {
+    int par[SPEC_MAX_N];
+    int tok[SPEC_MAX_N];
+    union {
+        struct {  // validation: pointer-jumping state
+            int anc[SPEC_MAX_N];
+            int dep[SPEC_MAX_N];
+        };
+        int kids[SPEC_MAX_N];  // the walk: children of the current node
+    };
+    float qx[SPEC_MAX_N];     // q_parent(token of node c), by node id
+    float lx[SPEC_MAX_N];     // logit of child j's token in the current row
+    int path[SPEC_MAX_N];     // accepted nodes, by depth
+    float pathp[SPEC_MAX_N];  // their target probabilities
+    int wcnt[kWaves];
+    int flag;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, uint32_t tag,
+                                                     unsigned long long* xslots, int xstride) {
+    __shared__ MssWalkSmem sm;
+    __shared__ RowSmem rs;
+    __shared__ XSmem xs;
+    __shared__ MassSmem ms;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x / W, w = blockIdx.x - b * W;
+    const int N = a.R, V = a.V, D = a.D;
+    const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
+    unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    const int32_t* par_g = a.parents + (size_t)b * N;
+    const int32_t* tok_g = a.tokens + (size_t)b * N;
+    const float* coins = a.coins + (size_t)b * N;
+    const T* logits = reinterpret_cast<const T*>(a.logits);
+    bool bad = false;
+    for (int i = tid; i < N; i += kBlock) {
+        const int p = par_g[i];
+        const int t = tok_g[i];
+        sm.par[i] = p;
+        sm.tok[i] = t;
+        if (i == 0) {
+            if (p != -1) bad = true;
+        } else {
+            if (p < 0 || p >= i) bad = true;
+            if (t < 0 || t >= V) bad = true;
+        }
+        const float u = coins[i];
+        if (!(u > 0.f && u <= 1.f)) bad = true;
+    }
+    const float Tf = a.temperature[b];
+    if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
+    const double Td = (double)Tf;
+    const float s2 = kLog2e / Tf;
+    bad = __syncthreads_or(bad);
+    if (!bad) {  // depths, and q of every child's token under its parent's draft row
+        tree_depths(sm.par, N, sm.anc, sm.dep);
+        for (int i = tid; i < N; i += kBlock) {
+            if (sm.dep[i] > D) bad = true;
+            if (i > 0) {
+                const float q = a.q[((size_t)b * N + sm.par[i]) * V + sm.tok[i]];
+                sm.qx[i] = q;
+                if (!(q >= 0.f && isfinite(q))) bad = true;
+            }
+        }
+        bad = __syncthreads_or(bad);
+    }
+
+    int cur = 0, d = 0, step = 0;
+    int kind = kDrawTarget;
+    float cq = 0.f, M = 0.f;
+    double Z = 1.0;
+    while (!bad) {
+        const T* rowp = logits + ((size_t)b * N + cur) * V;
+        int count = 0;  // children of cur in ascending node id (ordered compaction)
+        for (int base = cur + 1; base < N; base += kBlock) {
+            const int c = base + tid;
+            const bool f = c < N && sm.par[c] == cur;
+            const unsigned long long m = __ballot(f);
+            if (lane == 0) sm.wcnt[wave] = __popcll(m);
+            __syncthreads();
+            int off = count, total = 0;
+            for (int q = 0; q < kWaves; ++q) {
+                if (q < wave) off += sm.wcnt[q];
+                total += sm.wcnt[q];
+            }
+            if (f) sm.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = c;
+            __syncthreads();
+            count += total;
+        }
+        for (int j = tid; j < count; j += kBlock) sm.lx[j] = Ld<T>::one(rowp + sm.tok[sm.kids[j]]);
+        {
+            const Part r = chunk_record<T, true>(rowp, lo, hi, s2, rs);
+            if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
+                              dbl_lo(r.z), xs)) {
+                bad = true;
+                break;
+            }
+            M = -INFINITY;
+            for (int k = 0; k < W; ++k) M = fmaxf(M, __uint_as_float(xs.xp[k][0]));
+            Z = 0.0;
+            for (int k = 0; k < W; ++k) {
+                const float mk = __uint_as_float(xs.xp[k][0]);
+                if (mk != -INFINITY)
+                    Z += dbl_of(xs.xp[k][1], xs.xp[k][2]) * exp(((double)mk - (double)M) / Td);
+            }
+        }
+        if (M == -INFINITY) {  // a row on the walk with no finite logit
+            bad = true;
+            break;
+        }
+        kind = kDrawTarget;
+        cq = 0.f;
+        if (count == 0) break;  // a leaf: the bonus from its own row
+        const float* qrow = a.q + ((size_t)b * N + cur) * V;
+        const float invZ = (float)(1.0 / Z);
+        double c = 0.0, Nr = 1.0;
+        int chosen = -1;
+        for (int j = 0; j < count; ++j) {
+            const int child = sm.kids[j];
+            if (tid == 0) {
+                const double px = exp(((double)sm.lx[j] - (double)M) / Td) / Z;
+                const double qx = (double)sm.qx[child];
+                double pr = px - c * qx;
+                pr = pr > 0.0 ? pr / Nr : 0.0;
+                const double u = (double)coins[child - 1];
+                const bool acc = qx > 0.0 ? (pr > 0.0 && u <= pr / qx) : pr > 0.0;
+                sm.flag = acc;
+                if (acc) {
+                    sm.path[d] = child;
+                    sm.pathp[d] = (float)px;
+                }
+            }
+            __syncthreads();
+            const bool accepted = sm.flag != 0;
+            __syncthreads();
+            if (accepted) {
+                chosen = child;
+                break;
+            }
+            const double cn = (double)(float)(c + Nr);
+            if (j == count - 1) {  // every child rejected: the final residual
+                kind = kDrawResidual;
+                cq = (float)cn;
+                break;
+            }
+            const double Nw = slice_resid_sum<T>(rowp, qrow, lo, hi, M, s2, invZ, (float)cn, rs);
+            if (!cluster_step(slots, step++, W, w, tag, dbl_hi(Nw), dbl_lo(Nw), 0u, xs)) {
+                bad = true;
+                break;
+            }
+            double Nn = 0.0;
+            for (int k = 0; k < W; ++k) Nn += dbl_of(xs.xp[k][0], xs.xp[k][1]);
+            if (!(Nn > 0.0)) break;  // no residual mass left: draw from the target row
+            c = cn;
+            Nr = Nn;
+        }
+        if (bad || chosen < 0) break;
+        cur = chosen;
+        ++d;
+    }
+
+    DrawState st = {};
+    st.kind = kDrawNone;
+    if (!bad) {
+        st.kind = kind;
+        st.row = b * N + cur;
+        st.qrow = b * N + cur;
+        st.out = b * (D + 1) + d;
+        st.coin = b * N + N - 1;
+        st.nexcl = 0;
+        st.cq = cq;
+        st.M = M;
+        st.Z = Z;
+        st.invZ = (float)(1.0 / Z);
+        st.T = Td;
+        const T* rowp = logits + (size_t)st.row * V;
+        const void* qrow;
+        const WParams Wp = draw_params<T, false>(a, st, qrow);
+        for (int c = lo / kFine; c * kFine < hi; ++c)
+            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
+    }
+    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
+    int32_t* out = a.out_tokens + (size_t)b * (D + 1);
+    int32_t* nodes = a.accepted_nodes + (size_t)b * D;
+    float* probs = a.probs ? a.probs + (size_t)b * (D + 1) : nullptr;
+    for (int e = tid; e <= D; e += kBlock) {
+        if (bad) {
+            out[e] = -1;
+            if (e < D) nodes[e] = -1;
+            if (probs) probs[e] = 0.f;
+            continue;
+        }
+        if (e < d) {  // slot d is written by the final draw
+            out[e] = sm.tok[sm.path[e]];
+            nodes[e] = sm.path[e];
+            if (probs) probs[e] = sm.pathp[e];
+        } else if (e > d) {
+            out[e] = -1;
+            if (probs) probs[e] = 0.f;
+        }
+        if (e >= d && e < D) nodes[e] = -1;
+    }
+    if (tid == 0) {
+        a.accept_len[b] = bad ? -1 : d;
+        a.dstate[b] = st;
     }
 }
 
@@ -2845,14 +2730,7 @@ struct Layout {
     size_t parts, dstate, mass, massfb, seg, excl, frows, xch, total;
 };
 
-// Workgroups per request that the multi-step tree walk may use (slots are sized for it).
-inline int cluster_max(int B) {
-    if (B <= 0) return 1;
-    const int w = kClusterSlots / B;
-    return w < 2 ? 1 : (w > kMaxCluster ? kMaxCluster : w);
-}
-
-// Workgroups per request that the target-only tree walk may use (slots are sized for it).
+// Workgroups per request that the tree walks may use (the hand-off slots are sized for it).
 inline int tree_cluster_max(int B) {
     return B <= 0 ? 1 : std::max(1, std::min(kMaxCluster, 2048 / B));
 }
@@ -2889,8 +2767,8 @@ Layout layout_for(int op, int B, int R, int V) {
         off = align256(off + sizeof(unsigned long long) * (size_t)B * R * kMaxCluster * 3);
     else if (op == SPEC_OP_TREE)  // at most one step per node
         off = align256(off + sizeof(unsigned long long) * (size_t)B * R * tree_cluster_max(B) * 3);
-    else if (op == SPEC_OP_TREE_MSS && cluster_max(B) > 1)
-        off = align256(off + sizeof(unsigned long long) * (size_t)B * cluster_stride(R, cluster_max(B)));
+    else if (op == SPEC_OP_TREE_MSS)
+        off = align256(off + sizeof(unsigned long long) * (size_t)B * cluster_stride(R, tree_cluster_max(B)));
     L.total = off;
     return L;
 }
@@ -2974,6 +2852,8 @@ inline int resident_blocks(const void* kernel, int slot) {
     return cache[slot][dev];
 }
 
+// Tags of the walks' hand-off words: one per call, process-wide, so no two calls through
+// the same workspace share a tag (until 2^32 calls have passed).
 std::atomic<uint32_t> g_chain_epoch{0};
 
 inline uint32_t next_tag() {
@@ -3091,46 +2971,22 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
     return run_draw<T>(a, st);
 }
 
-// k_mss_walk workgroups that the current device holds at once, cached per device.
-template <typename T>
-int cluster_capacity() {
-    static int cache[64];
-    static bool known[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (!known[dev]) {
-        int cus = 0, nb = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, reinterpret_cast<const void*>(&k_mss_walk<T>), kWalk, 0) != hipSuccess)
-            nb = 0;
-        cache[dev] = nb * cus;
-        known[dev] = true;
-    }
-    return cache[dev];
-}
-
-// Tags of the multi-step walk's hand-off words: one per call, process-wide, so no two
-// calls through the same workspace share a tag (until 2^32 calls have passed).
-std::atomic<uint32_t> g_walk_epoch{0};
-
 template <typename T>
 int run_tree_mss(KArgs& a, unsigned long long* xslots, hipStream_t st) {
-    uint32_t tag = g_walk_epoch.fetch_add(1u) + 1u;
-    if (tag == 0u) tag = g_walk_epoch.fetch_add(1u) + 1u;  // 0 is what fresh memory most often holds
-    int W = 1;
-    if (xslots) {
-        W = std::min(cluster_max(a.B), cluster_capacity<T>() / a.B);
-        if (const char* env = std::getenv("SPEC_VERIFY_CLUSTER")) W = std::min(W, std::atoi(env));
-        if (W < 2) W = 1;
-    }
-    const int xstride = W > 1 ? (int)cluster_stride(a.R, W) : 0;
-    hipLaunchKernelGGL((k_mss_walk<T>), dim3(a.B * W), dim3(kWalk), 0, st, a, W, tag,
-                       W > 1 ? xslots : (unsigned long long*)nullptr, xstride);
+    const uint32_t tag = next_tag();
+    int W, per;
+    walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_mss_walk<T>),
+                                  sizeof(T) == 4 ? 6 : 7), &W, &per);
+    W = std::min(W, tree_cluster_max(a.B));
+    per = (a.S2 + W - 1) / W;
+    W = (a.S2 + per - 1) / per;
+    hipLaunchKernelGGL((k_mss_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W, per * kFine,
+                       tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       (int)cluster_stride(a.R, W));
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
-    return run_draw<T>(a, st);
+    hipLaunchKernelGGL((k_draw<T, false>), dim3(a.B), dim3(64), 0, st, a);
+    return launch_status();
 }
 
 template <typename T>
@@ -3321,9 +3177,7 @@ extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* 
     bind_workspace(a, workspace, SPEC_OP_TREE_MSS);
     const Layout L = layout_for(SPEC_OP_TREE_MSS, B, N, V);
     unsigned long long* xslots =
-        cluster_max(B) > 1
-            ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch)
-            : nullptr;
+        reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_tree_mss<float>(a, xslots, st)
                              : run_tree_mss<uint16_t>(a, xslots, st);
