@@ -36,16 +36,22 @@
  *     host before anything is enqueued (nothing is written), or SPEC_ERR_HIP if a launch
  *     failed.  Errors in the data are reported in-band per request: accept_len[b] = -1,
  *     token / node rows of that request filled with -1 and probability rows with 0.
- *     A request is invalid when a token id is outside [0, V), the temperature is not
- *     finite and > 0, a coin is outside (0, 1], a row has no finite logit (all -inf),
- *     a drafted token's q is negative or not finite, or (tree) the parent array is
- *     malformed or a node lies deeper than D.  NaN or +inf logits are undefined.
+ *     A request is invalid when something the verify consults is unusable: a token id
+ *     outside [0, V), a temperature that is not finite and > 0, a coin outside (0, 1], a
+ *     row with no finite logit (all -inf), a drafted token's q that is negative or not
+ *     finite, or (tree) a malformed parent array or a node deeper than D.  Chains and
+ *     trees are walked in order and stop at the first rejection (or mismatch), so
+ *     positions, rows and coins after the stop are not consulted and not checked (the
+ *     temperature and the final draw's coin always are; spec_verify_chain_filtered
+ *     checks every row).  NaN or +inf logits are undefined.
  *   - Workspace: a device buffer of at least spec_workspace_bytes(op, B, R, V) bytes,
- *     256-byte aligned, owned by the caller.  Its contents need no initialisation: each
- *     call writes what it reads later in the same call (per-row partial records, the
- *     per-request acceptance state and residual chunk sums).  Calls that may run at the
- *     same time (on different streams) need separate workspaces; calls issued in order
- *     on one stream can share one.
+ *     256-byte aligned, owned by the caller, ZERO-FILLED ONCE before its first use
+ *     (hipMemset).  Its first 256 bytes hold a call counter that tags the words the
+ *     workgroups of one request hand to each other; each call advances it on the
+ *     device, so a call captured into a HIP graph replays correctly.  Everything else in
+ *     it is written before it is read within a call.  Calls that may run at the same time
+ *     (on different streams) need separate workspaces; calls issued in order on one
+ *     stream can share one.
  *   - Determinism: identical inputs give bitwise-identical outputs.
  *   - Coin convention: every comparison is coin <= threshold.  The final draw (the
  *     correction, the bonus, or the tree's last token) is the inverse CDF in ascending

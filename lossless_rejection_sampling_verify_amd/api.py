@@ -47,15 +47,16 @@ def _stream(device, stream):
 def workspace(op: int, B: int, R: int, V: int, device) -> torch.Tensor:
     """A workspace big enough for the call, cached per device and kind.
 
-    The library needs no initialised contents, so one cached buffer serves every later
-    call issued on the same stream."""
+    Zero-filled when allocated (the library keeps a call counter in its first bytes and
+    leaves it ready for the next call), so one cached buffer serves every later call
+    issued on the same stream."""
     need = L.workspace_bytes(op, B, R, V)
     if need == 0:
         raise ValueError("unsupported sizes")
     key = (torch.device(device), op)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 

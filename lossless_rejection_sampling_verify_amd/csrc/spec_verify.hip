@@ -130,6 +130,7 @@ struct KArgs {
     FiltRow* frows;      // filtered calls: [B*R] target rows, then [B*G] draft rows
     int fixbits;         // fixed-point fraction bits of the filter's mass histograms
     int walk_temporal;   // chain walk: row passes with cache-allocating loads (sweeps: 0)
+    unsigned* hdr;       // workspace header: the walks' call counter and finished count
 };
 
 // ---------------------------------------------------------------------------------------
@@ -919,7 +920,36 @@ constexpr long kSpinMax = 1 << 18; // bound of a cluster wait (never reached whe
 struct XSmem {
     uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
     int xbad;
+    uint32_t epoch;               // the workspace's call counter when this call started
 };
+
+// The tag of a call's hand-off words comes from a counter in the workspace header
+// (hdr[0]; hdr[1] counts the requests whose walk has ended).  Every workgroup reads the
+// counter when it starts; workgroup 0 of each request reports at its end, and the last
+// report advances the counter.  A request's workgroup 0 ends after its first completed
+// hand-off, so by then every workgroup of the request has read the counter (each
+// published under the tag made from it); a request found invalid before any hand-off
+// never uses its tag.  All of a call's hand-offs therefore carry one tag, and the next
+// call on the stream sees the next one: the tag changes from call to call with no host
+// state, so a captured graph replays correctly.  One report per request (not per
+// workgroup) keeps the same-address atomics few.  The header must be zero before the
+// first call.
+__device__ inline uint32_t walk_begin(const unsigned* hdr, XSmem& xs) {
+    if (threadIdx.x == 0)
+        xs.epoch = hdr ? __hip_atomic_load(hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    __syncthreads();
+    return xs.epoch % 0xffffffffu + 1u;  // never 0, the value zeroed slots hold
+}
+
+__device__ inline void walk_end(unsigned* hdr, const XSmem& xs, int w, int W) {
+    if (!hdr || w != 0 || threadIdx.x != 0) return;
+    const unsigned done = __hip_atomic_fetch_add(hdr + 1, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x / W - 1) {  // the call's last request
+        __hip_atomic_store(hdr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(hdr, xs.epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 // One step of a cluster: every workgroup of the request hands three 32-bit payloads to
 // the others.  Each payload travels in a 64-bit word whose high half is the call's tag;
@@ -997,7 +1027,7 @@ __device__ inline double dbl_of(uint32_t hi, uint32_t lo) {
 // every row).  Each position's slice argmax travels through the cluster hand-off; the
 // walk stops at the first mismatch, so rows after it are never read.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per, uint32_t tag,
+__global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per, unsigned* hdr,
                                                         unsigned long long* xslots, int xstride) {
     __shared__ RowSmem rs;
     __shared__ XSmem xs;
@@ -1006,6 +1036,8 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     const int R = a.R, G = R - 1, V = a.V;
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    if (!slots) hdr = nullptr;  // no hand-off words, no tag
+    const uint32_t tag = walk_begin(hdr, xs);
     const T* logits = reinterpret_cast<const T*>(a.logits);
     const int32_t* x = a.tokens + (size_t)b * G;
     int k = G, last = -1;
@@ -1042,6 +1074,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
             break;
         }
     }
+    walk_end(hdr, xs, w, W);
     if (w != 0) return;
     int32_t* out = a.out_tokens + (size_t)b * R;
     for (int e = tid; e < R; e += kBlock)
@@ -1326,7 +1359,7 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
 // read.  Each workgroup then weighs its slice of the row the last token is drawn from
 // (the residual against q, or the plain row for the bonus), which k_draw searches.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, uint32_t tag,
+__global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, unsigned* hdr,
                                                        unsigned long long* xslots, int xstride) {
     __shared__ RowSmem rs;
     __shared__ XSmem xs;
@@ -1338,6 +1371,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     const int R = a.R, G = R - 1, V = a.V;
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    if (!slots) hdr = nullptr;  // no hand-off words, no tag
+    const uint32_t tag = walk_begin(hdr, xs);
     const T* logits = reinterpret_cast<const T*>(a.logits);
     const float Tf = a.temperature[b];
     const float uG = a.coins[(size_t)b * R + G];
@@ -1427,6 +1462,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         for (int c = lo / kFine; c * kFine < hi; ++c)
             mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
     }
+    walk_end(hdr, xs, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     for (int e = tid; e < R; e += kBlock) {
         if (e == k && !bad) continue;  // slot k is written by the final draw
@@ -1469,7 +1505,7 @@ struct TreeWalkSmem {
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int W, int per,
-                                                      uint32_t tag, unsigned long long* xslots,
+                                                      unsigned* hdr, unsigned long long* xslots,
                                                       int xstride) {
     __shared__ TreeWalkSmem ts;
     __shared__ RowSmem rs;
@@ -1480,6 +1516,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     const int N = a.R, V = a.V, D = a.D;
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    if (!slots) hdr = nullptr;  // no hand-off words, no tag
+    const uint32_t tag = walk_begin(hdr, xs);
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const T* logits = reinterpret_cast<const T*>(a.logits);
@@ -1639,6 +1677,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         for (int c = lo / kFine; c * kFine < hi; ++c)
             mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, ts.excl);
     }
+    walk_end(hdr, xs, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
@@ -1763,7 +1802,7 @@ struct MssWalkSmem {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, uint32_t tag,
+__global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, unsigned* hdr,
                                                      unsigned long long* xslots, int xstride) {
     __shared__ MssWalkSmem sm;
     __shared__ RowSmem rs;
@@ -1774,6 +1813,8 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, ui
     const int N = a.R, V = a.V, D = a.D;
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
+    if (!slots) hdr = nullptr;  // no hand-off words, no tag
+    const uint32_t tag = walk_begin(hdr, xs);
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const float* coins = a.coins + (size_t)b * N;
@@ -1925,6 +1966,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, ui
         for (int c = lo / kFine; c * kFine < hi; ++c)
             mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
     }
+    walk_end(hdr, xs, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
@@ -2726,6 +2768,8 @@ __global__ __launch_bounds__(kBlock) void k_commit_kv(const int32_t* accepted_no
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr size_t kHeaderBytes = 256;
+
 struct Layout {
     size_t parts, dstate, mass, massfb, seg, excl, frows, xch, total;
 };
@@ -2747,7 +2791,7 @@ inline long fine_chunks(int V) { return ((long)V + kFine - 1) / kFine; }
 Layout layout_for(int op, int B, int R, int V) {
     Layout L;
     const size_t S2 = (size_t)fine_chunks(V);
-    size_t off = 0;
+    size_t off = kHeaderBytes;  // the header: the walks' call counter (zero before first use)
     L.parts = off;
     if (op != SPEC_OP_TREE_MSS) off = align256(off + sizeof(Part) * (size_t)B * R * kMaxSplits);
     L.dstate = off;
@@ -2776,6 +2820,7 @@ Layout layout_for(int op, int B, int R, int V) {
 void bind_workspace(KArgs& a, void* ws, int op) {
     const Layout L = layout_for(op, a.B, a.R, a.V);
     char* base = static_cast<char*>(ws);
+    a.hdr = reinterpret_cast<unsigned*>(base);
     a.parts = reinterpret_cast<Part*>(base + L.parts);
     a.dstate = reinterpret_cast<DrawState*>(base + L.dstate);
     a.mass = reinterpret_cast<double*>(base + L.mass);
@@ -2852,16 +2897,6 @@ inline int resident_blocks(const void* kernel, int slot) {
     return cache[slot][dev];
 }
 
-// Tags of the walks' hand-off words: one per call, process-wide, so no two calls through
-// the same workspace share a tag (until 2^32 calls have passed).
-std::atomic<uint32_t> g_chain_epoch{0};
-
-inline uint32_t next_tag() {
-    uint32_t tag = g_chain_epoch.fetch_add(1u) + 1u;
-    if (tag == 0u) tag = g_chain_epoch.fetch_add(1u) + 1u;  // fresh memory most often holds 0
-    return tag;
-}
-
 // Cluster shape of a position-by-position walk: W workgroups per request, each owning
 // `per_chunks` whole fine chunks of every row, with all B * W workgroups resident at once.
 inline void walk_shape(const KArgs& a, int cap, int* W_out, int* per_chunks_out) {
@@ -2876,26 +2911,24 @@ inline void walk_shape(const KArgs& a, int cap, int* W_out, int* per_chunks_out)
 
 template <typename T>
 int run_greedy_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
-    const uint32_t tag = next_tag();
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_greedy_walk<T>),
                                   sizeof(T) == 4 ? 0 : 1), &W, &per);
     hipLaunchKernelGGL((k_greedy_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
-                       per * kFine, tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       per * kFine, a.hdr, W > 1 ? xslots : (unsigned long long*)nullptr,
                        a.R * W * 3);
     return launch_status();
 }
 
 template <typename T>
 int run_chain_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
-    const uint32_t tag = next_tag();
     a.walk_temporal = 1;  // keeps the slice of the row drawn from near for the final weights
     if (const char* env = std::getenv("SPEC_VERIFY_TEMPORAL")) a.walk_temporal = std::atoi(env);
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_chain_walk<T>),
                                   sizeof(T) == 4 ? 2 : 3), &W, &per);
     hipLaunchKernelGGL((k_chain_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
-                       per * kFine, tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       per * kFine, a.hdr, W > 1 ? xslots : (unsigned long long*)nullptr,
                        a.R * W * 3);
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
@@ -2941,7 +2974,6 @@ int run_chain(KArgs& a, hipStream_t st) {
 
 template <typename T>
 int run_tree_walk(KArgs& a, int sampling, unsigned long long* xslots, hipStream_t st) {
-    const uint32_t tag = next_tag();
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_tree_walk<T>),
                                   sizeof(T) == 4 ? 4 : 5), &W, &per);
@@ -2949,7 +2981,7 @@ int run_tree_walk(KArgs& a, int sampling, unsigned long long* xslots, hipStream_
     per = (a.S2 + W - 1) / W;
     W = (a.S2 + per - 1) / per;
     hipLaunchKernelGGL((k_tree_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, sampling, W,
-                       per * kFine, tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       per * kFine, a.hdr, W > 1 ? xslots : (unsigned long long*)nullptr,
                        a.R * W * 3);
     int rc = launch_status();
     if (rc != SPEC_OK || !sampling) return rc;
@@ -2973,7 +3005,6 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
 
 template <typename T>
 int run_tree_mss(KArgs& a, unsigned long long* xslots, hipStream_t st) {
-    const uint32_t tag = next_tag();
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_mss_walk<T>),
                                   sizeof(T) == 4 ? 6 : 7), &W, &per);
@@ -2981,7 +3012,7 @@ int run_tree_mss(KArgs& a, unsigned long long* xslots, hipStream_t st) {
     per = (a.S2 + W - 1) / W;
     W = (a.S2 + per - 1) / per;
     hipLaunchKernelGGL((k_mss_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W, per * kFine,
-                       tag, W > 1 ? xslots : (unsigned long long*)nullptr,
+                       a.hdr, W > 1 ? xslots : (unsigned long long*)nullptr,
                        (int)cluster_stride(a.R, W));
     int rc = launch_status();
     if (rc != SPEC_OK) return rc;
