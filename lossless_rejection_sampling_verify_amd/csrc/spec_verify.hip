@@ -59,6 +59,7 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kUnroll = 4;
+constexpr int kWalkUnroll = 4;  // loads in flight per lane in the walks' row passes
 constexpr int kMaxSplits = 64;
 constexpr long kChunkBytes = 64 * 1024;  // target logit bytes per row-pass workgroup
 constexpr int kFine = 4 * 4 * kBlock;  // elements per fine chunk of the final draw (4096)
@@ -227,7 +228,7 @@ struct Smem {  // per-request merges: row statistics, drafts, coins, decisions
 // ---------------------------------------------------------------------------------------
 // the row pass of one chunk: per-thread streaming state, then a block reduction
 //
-// Each lane takes kUnroll 16-byte vectors per batch, strided by the block so that every
+// Each lane takes kU 16-byte vectors per batch, strided by the block so that every
 // load instruction of the wave is one contiguous 1 KB segment.  Within a lane, batches
 // arrive in ascending index order, and so do the vectors within a batch.
 //   sampling: online (m, z): per batch the batch max, one rescale of z if it grew, then
@@ -265,12 +266,11 @@ __device__ inline int block_min(int v, RowSmem& sm) {
 }
 
 // Reduces chunk [c0, c1) of a row into one record (valid in every thread).
-template <typename T, bool kSampling, bool kNT = true>
+template <typename T, bool kSampling, bool kNT = true, int kU = kUnroll>
 __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
                                                             float s2, RowSmem& sm,
                                                             float* lane_max = nullptr) {
     constexpr int kVec = Ld<T>::kVec;
-    constexpr int kN = kUnroll * kVec;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = c1 > c0 ? c1 - c0 : 0;
     const T* p = rowp + c0;
@@ -284,7 +284,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
     float m = -INFINITY;   // running max (sampling: reference of z)
     double z = 0.0;        // sampling: sum exp2((l - m) * s2)
     int bfirst = -1;       // greedy: first vector of the batch that first reached m
-    int bcount = 0;        //         vectors in that batch (kUnroll, or 1 in the remainder)
+    int bcount = 0;        //         vectors in that batch (kU, or 1 in the remainder)
     float ms = -INFINITY;  // greedy: max over this lane's scalar head / tail elements
     int is = INT_MAX;      //         lowest index attaining ms
 
@@ -301,9 +301,24 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             is = c0 + e;
         }
     };
-    auto batch = [&](const float* f, int cnt, int vfirst) {
-        float bm = f[0];
-        for (int e = 1; e < cnt; ++e) bm = fmaxf(bm, f[e]);
+    // One batch of nvec 16-byte vectors, unpacked on the fly (once for the batch max, once
+    // for the exp-sum) so that only the raw vectors stay live while the loads are in flight.
+    auto batch = [&](u32x4* raw, int nvec, int vfirst) {
+        float bm;
+        {
+            float f[kVec];
+            Ld<T>::unpack(raw[0], f);
+            bm = f[0];
+#pragma unroll
+            for (int e = 1; e < kVec; ++e) bm = fmaxf(bm, f[e]);
+        }
+#pragma unroll
+        for (int u = 1; u < nvec; ++u) {
+            float f[kVec];
+            Ld<T>::unpack(raw[u], f);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) bm = fmaxf(bm, f[e]);
+        }
         if (kSampling) {
             if (bm > m) {
                 z *= (double)ex2((m - bm) * s2);
@@ -311,10 +326,15 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             }
             if (m != -INFINITY) {
                 float acc = 0.f;
-                for (int u = 0; u < cnt / kVec; ++u) {
-                    float e8[kVec];
 #pragma unroll
-                    for (int e = 0; e < kVec; ++e) e8[e] = ex2((f[u * kVec + e] - m) * s2);
+                for (int u = 0; u < nvec; ++u) {
+                    // deep batches: unpack again rather than keep the first unpacking
+                    // live (emits no code)
+                    if constexpr (kU > 4) asm volatile("" : "+v"(raw[u]));
+                    float f[kVec], e8[kVec];
+                    Ld<T>::unpack(raw[u], f);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) e8[e] = ex2((f[e] - m) * s2);
                     float t;
                     if (kVec == 8)
                         t = ((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7]));
@@ -327,26 +347,21 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
         } else if (bm > m) {
             m = bm;
             bfirst = vfirst;
-            bcount = cnt / kVec;
+            bcount = nvec;
         }
     };
 
     if (tid < head) scalar(tid);
     int v = tid;
-    for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
-        u32x4 raw[kUnroll];
+    for (; v + (kU - 1) * kBlock < nv; v += kU * kBlock) {
+        u32x4 raw[kU];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) raw[u] = kNT ? ld_stream(vp + v + u * kBlock) : vp[v + u * kBlock];
-        float f[kN];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) Ld<T>::unpack(raw[u], f + u * kVec);
-        batch(f, kN, v);
+        for (int u = 0; u < kU; ++u) raw[u] = kNT ? ld_stream(vp + v + u * kBlock) : vp[v + u * kBlock];
+        batch(raw, kU, v);
     }
     for (; v < nv; v += kBlock) {
-        const u32x4 raw = kNT ? ld_stream(vp + v) : vp[v];
-        float f[kVec];
-        Ld<T>::unpack(raw, f);
-        batch(f, kVec, v);
+        u32x4 raw = kNT ? ld_stream(vp + v) : vp[v];
+        batch(&raw, 1, v);
     }
     if (tail0 + tid < n) scalar(tail0 + tid);
 
@@ -920,7 +935,6 @@ constexpr long kSpinMax = 1 << 18; // bound of a cluster wait (never reached whe
 struct XSmem {
     uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
     int xbad;
-    uint32_t epoch;               // the workspace's call counter when this call started
 };
 
 // The tag of a call's hand-off words comes from a counter in the workspace header
@@ -934,20 +948,25 @@ struct XSmem {
 // state, so a captured graph replays correctly.  One report per request (not per
 // workgroup) keeps the same-address atomics few.  The header must be zero before the
 // first call.
-__device__ inline uint32_t walk_begin(const unsigned* hdr, XSmem& xs) {
-    if (threadIdx.x == 0)
-        xs.epoch = hdr ? __hip_atomic_load(hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-    __syncthreads();
-    return xs.epoch % 0xffffffffu + 1u;  // never 0, the value zeroed slots hold
+//
+// Only wave 0 reads the counter (thread 0 publishes, lanes below W wait), and nothing
+// waits for the read until the first hand-off, so it overlaps the first row pass.
+__device__ inline uint32_t walk_epoch(const unsigned* hdr) {
+    return (hdr && threadIdx.x < 64)
+               ? __hip_atomic_load(hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : 0u;
+}
+__device__ inline uint32_t walk_tag(uint32_t epoch) {
+    return epoch % 0xffffffffu + 1u;  // never 0, the value zeroed slots hold
 }
 
-__device__ inline void walk_end(unsigned* hdr, const XSmem& xs, int w, int W) {
+__device__ inline void walk_end(unsigned* hdr, uint32_t epoch, int w, int W) {
     if (!hdr || w != 0 || threadIdx.x != 0) return;
     const unsigned done = __hip_atomic_fetch_add(hdr + 1, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (done == gridDim.x / W - 1) {  // the call's last request
         __hip_atomic_store(hdr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(hdr, xs.epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(hdr, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1037,13 +1056,16 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
     if (!slots) hdr = nullptr;  // no hand-off words, no tag
-    const uint32_t tag = walk_begin(hdr, xs);
+    const uint32_t epoch = walk_epoch(hdr), tag = walk_tag(epoch);
     const T* logits = reinterpret_cast<const T*>(a.logits);
     const int32_t* x = a.tokens + (size_t)b * G;
+    // lane l of every wave holds draft token l (read once, while the first row streams)
+    const int px = (tid & 63) < G ? x[tid & 63] : -1;
     int k = G, last = -1;
     bool bad = false;
     for (int i = 0; i <= G; ++i) {
-        const Part cur = chunk_record<T, false>(logits + ((size_t)b * R + i) * V, lo, hi, 0.f, rs);
+        const Part cur = chunk_record<T, false, true, kWalkUnroll>(logits + ((size_t)b * R + i) * V,
+                                                                    lo, hi, 0.f, rs);
         if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), (uint32_t)cur.idx, 0u,
                           xs)) {
             bad = true;
@@ -1064,7 +1086,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
         }
         last = idx;
         if (i == G) break;
-        const int xi = x[i];
+        const int xi = __shfl(px, i);
         if (xi < 0 || xi >= V) {
             bad = true;
             break;
@@ -1074,7 +1096,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
             break;
         }
     }
-    walk_end(hdr, xs, w, W);
+    walk_end(hdr, epoch, w, W);
     if (w != 0) return;
     int32_t* out = a.out_tokens + (size_t)b * R;
     for (int e = tid; e < R; e += kBlock)
@@ -1278,26 +1300,18 @@ __device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const
     return W;
 }
 
-// The draw weights of fine chunk c of the row in `st`: each segment's weight (and the
-// chunk's) in a.seg / a.mass, the plain target weight in a.massfb.  Block-wide.
+// Segment and chunk sums of fine chunk c, whose per-quad weights `chunk_weights` left in
+// sm.pw / sm.ww: each segment's weight (and the chunk's) in a.seg / a.mass, the plain
+// target weight in a.massfb.  Block-wide.
 template <typename T, bool kFilt>
-__device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const DrawState& st,
-                                                          const WParams& W, const T* rowp,
-                                                          const void* qrow, int b, int c,
-                                                          MassSmem& sm, const int32_t* ex) {
+__device__ __attribute__((always_inline)) void mass_reduce(const KArgs& a, const DrawState& st,
+                                                           const WParams& W, const T* rowp,
+                                                           int b, int c, MassSmem& sm,
+                                                           const int32_t* ex) {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int S2 = a.S2, V = a.V;
+    const int S2 = a.S2;
     const int c0 = c * kFine;
-    const int n = min(kFine, V - c0);
-    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
-    const bool fast = n == kFine && ((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0 &&
-                      (!qrow || ((uintptr_t)qrow + c0 * qes) % (4 * qes) == 0);
-    constexpr int kQr = kFilt ? 2 : 1;
-    if (qrow)
-        chunk_weights<T, kQr, kFilt>(rowp + c0, static_cast<const char*>(qrow) + c0 * qes, n, fast,
-                                     W, sm.pw, sm.ww);
-    else
-        chunk_weights<T, 0, kFilt>(rowp + c0, nullptr, n, fast, W, sm.pw, sm.ww);
+    const int n = min(kFine, a.V - c0);
     if (tid < kSegs) sm.xs[tid] = 0.0;
     __syncthreads();
     if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
@@ -1333,6 +1347,34 @@ __device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const 
         }
     }
     __syncthreads();  // LDS is reused by the next chunk
+}
+
+// Whether fine chunk c takes chunk_weights' fast path (full and 16-byte aligned).
+template <typename T, bool kFilt>
+__device__ inline bool chunk_fast(const T* rowp, const void* qrow, int c, int V) {
+    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
+    const int c0 = c * kFine;
+    return V - c0 >= kFine && ((uintptr_t)(rowp + c0)) % (4 * sizeof(T)) == 0 &&
+           (!qrow || ((uintptr_t)qrow + c0 * qes) % (4 * qes) == 0);
+}
+
+// The draw weights of fine chunk c of the row in `st` (see mass_reduce).  Block-wide.
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const DrawState& st,
+                                                          const WParams& W, const T* rowp,
+                                                          const void* qrow, int b, int c,
+                                                          MassSmem& sm, const int32_t* ex) {
+    const int c0 = c * kFine;
+    const int n = min(kFine, a.V - c0);
+    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
+    const bool fast = chunk_fast<T, kFilt>(rowp, qrow, c, a.V);
+    constexpr int kQr = kFilt ? 2 : 1;
+    if (qrow)
+        chunk_weights<T, kQr, kFilt>(rowp + c0, static_cast<const char*>(qrow) + c0 * qes, n, fast,
+                                     W, sm.pw, sm.ww);
+    else
+        chunk_weights<T, 0, kFilt>(rowp + c0, nullptr, n, fast, W, sm.pw, sm.ww);
+    mass_reduce<T, kFilt>(a, st, W, rowp, b, c, sm, ex);
 }
 
 // One workgroup per (request, fine chunk).
@@ -1372,11 +1414,20 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
     if (!slots) hdr = nullptr;  // no hand-off words, no tag
-    const uint32_t tag = walk_begin(hdr, xs);
+    const uint32_t epoch = walk_epoch(hdr), tag = walk_tag(epoch);
     const T* logits = reinterpret_cast<const T*>(a.logits);
+    // Every per-request input is read up front and waited for only where it is used, so
+    // the reads overlap the first row pass: the temperature and the final coin (checked
+    // after the first hand-off), and in wave 0, lane l's draft token and coin.
     const float Tf = a.temperature[b];
     const float uG = a.coins[(size_t)b * R + G];
-    bool bad = !(isfinite(Tf) && Tf > 0.f) || !(uG > 0.f && uG <= 1.f);
+    int px = -1;
+    float pu = 0.f;
+    if (tid < G) {
+        px = a.tokens[(size_t)b * G + tid];
+        pu = a.coins[(size_t)b * R + tid];
+    }
+    bool bad = false;
     const double Td = (double)Tf;
     const float s2 = kLog2e / Tf;
     int k = G;
@@ -1384,24 +1435,28 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     double Z = 0.0;
     auto pass = [&](int i) {
         const T* rowp = logits + ((size_t)b * R + i) * V;
-        return a.walk_temporal ? chunk_record<T, true, false>(rowp, lo, hi, s2, rs)
-                               : chunk_record<T, true, true>(rowp, lo, hi, s2, rs);
+        return a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll>(rowp, lo, hi, s2, rs)
+                               : chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
     };
-    for (int i = 0; i <= G && !bad; ++i) {
+    for (int i = 0; i <= G; ++i) {
         const T* rowp = logits + ((size_t)b * R + i) * V;
+        const Part cur = pass(i);
         int xi = -1;
         float lx = 0.f, qx = 0.f, ui = 0.f;
-        if (i < G && tid == 0) {  // the acceptance test's inputs
-            xi = a.tokens[(size_t)b * G + i];
-            ui = a.coins[(size_t)b * R + i];
-            if (xi >= 0 && xi < V) {
+        if (i < G && tid < 64) {  // the acceptance test's inputs, gathered during the hand-off
+            xi = __shfl(px, i);
+            ui = __shfl(pu, i);
+            if (tid == 0 && xi >= 0 && xi < V) {
                 lx = Ld<T>::one(rowp + xi);
                 qx = a.q[((size_t)b * G + i) * V + xi];
             }
         }
-        const Part cur = pass(i);
         if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), dbl_hi(cur.z),
                           dbl_lo(cur.z), xs)) {
+            bad = true;
+            break;
+        }
+        if (i == 0 && (!(isfinite(Tf) && Tf > 0.f) || !(uG > 0.f && uG <= 1.f))) {
             bad = true;
             break;
         }
@@ -1462,7 +1517,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         for (int c = lo / kFine; c * kFine < hi; ++c)
             mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
     }
-    walk_end(hdr, xs, w, W);
+    walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     for (int e = tid; e < R; e += kBlock) {
         if (e == k && !bad) continue;  // slot k is written by the final draw
@@ -1517,7 +1572,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
     if (!slots) hdr = nullptr;  // no hand-off words, no tag
-    const uint32_t tag = walk_begin(hdr, xs);
+    const uint32_t epoch = walk_epoch(hdr), tag = walk_tag(epoch);
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const T* logits = reinterpret_cast<const T*>(a.logits);
@@ -1577,7 +1632,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         for (int j = tid; j < count && sampling; j += kBlock)
             ts.lx[j] = Ld<T>::one(rowp + ts.tok[ts.kids[j]]);
         if (sampling) {
-            const Part r = chunk_record<T, true>(rowp, lo, hi, s2, rs);
+            const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
             if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
                               dbl_lo(r.z), xs)) {
                 bad = true;
@@ -1592,7 +1647,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
                     Z += dbl_of(xs.xp[j][1], xs.xp[j][2]) * exp(((double)mj - (double)M) / Td);
             }
         } else {
-            const Part r = chunk_record<T, false>(rowp, lo, hi, 0.f, rs);
+            const Part r = chunk_record<T, false, true, kWalkUnroll>(rowp, lo, hi, 0.f, rs);
             if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), (uint32_t)r.idx, 0u,
                               xs)) {
                 bad = true;
@@ -1677,7 +1732,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         for (int c = lo / kFine; c * kFine < hi; ++c)
             mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, ts.excl);
     }
-    walk_end(hdr, xs, w, W);
+    walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
@@ -1814,7 +1869,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     const int lo = (int)min((long)V, (long)w * per), hi = (int)min((long)V, (long)lo + per);
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
     if (!slots) hdr = nullptr;  // no hand-off words, no tag
-    const uint32_t tag = walk_begin(hdr, xs);
+    const uint32_t epoch = walk_epoch(hdr), tag = walk_tag(epoch);
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const float* coins = a.coins + (size_t)b * N;
@@ -1876,7 +1931,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         }
         for (int j = tid; j < count; j += kBlock) sm.lx[j] = Ld<T>::one(rowp + sm.tok[sm.kids[j]]);
         {
-            const Part r = chunk_record<T, true>(rowp, lo, hi, s2, rs);
+            const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
             if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
                               dbl_lo(r.z), xs)) {
                 bad = true;
@@ -1966,7 +2021,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         for (int c = lo / kFine; c * kFine < hi; ++c)
             mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
     }
-    walk_end(hdr, xs, w, W);
+    walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
@@ -2879,7 +2934,12 @@ int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t w
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
 
-// Workgroups of `kernel` (kBlock threads) that the current device holds at once.
+// Workgroups of `kernel` (kBlock threads) that the current device holds at once, counting
+// at most kWalkPerCu per compute unit.  Above five per CU the walks slowed down on the
+// large batch (greedy 52 -> 55-62 us, chain 101 -> 118-124 us at six to eight), although
+// the occupancy query allows seven (greedy) or five (chain): the later workgroups then
+// start only as earlier ones finish, and their clusters wait for them.
+constexpr int kWalkPerCu = 5;
 inline int resident_blocks(const void* kernel, int slot) {
     static int cache[8][64];
     static bool known[8][64];
@@ -2891,7 +2951,7 @@ inline int resident_blocks(const void* kernel, int slot) {
             cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, 0) != hipSuccess)
             nb = 0;
-        cache[slot][dev] = nb * cus;
+        cache[slot][dev] = std::min(nb, kWalkPerCu) * cus;
         known[slot][dev] = true;
     }
     return cache[slot][dev];
