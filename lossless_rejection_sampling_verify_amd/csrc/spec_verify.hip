@@ -59,7 +59,8 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kUnroll = 4;
-constexpr int kWalkUnroll = 4;  // loads in flight per lane in the walks' row passes
+constexpr int kWalkUnroll = 4;  // loads per lane and batch in the walks' row passes
+constexpr bool kWalkPipe = true;  // ... with the next batch in flight while one is reduced
 constexpr int kMaxSplits = 64;
 constexpr long kChunkBytes = 64 * 1024;  // target logit bytes per row-pass workgroup
 constexpr int kFine = 4 * 4 * kBlock;  // elements per fine chunk of the final draw (4096)
@@ -233,9 +234,9 @@ struct Smem {  // per-request merges: row statistics, drafts, coins, decisions
 // arrive in ascending index order, and so do the vectors within a batch.
 //   sampling: online (m, z): per batch the batch max, one rescale of z if it grew, then
 //             sum exp2((l - m) * log2(e) / T) in fp32 over the batch, added to z in fp64.
-//   greedy:   only the running max and the first batch that reached it; the exact lowest
-//             index is resolved once per workgroup, after the block max is known, by the
-//             lanes that hold it re-reading that one batch.
+//   greedy:   the running max and, when a batch raises it, the first element of that
+//             batch equal to it (from the registers already loaded): the lane's lowest
+//             index of its max, since a lane's elements arrive in index order.
 
 struct RowSmem {
     float rm[kWaves];
@@ -266,7 +267,10 @@ __device__ inline int block_min(int v, RowSmem& sm) {
 }
 
 // Reduces chunk [c0, c1) of a row into one record (valid in every thread).
-template <typename T, bool kSampling, bool kNT = true, int kU = kUnroll>
+// kPipe: the loads of batch j + 1 are issued before batch j is reduced (kU more registers
+// per lane), so the reduction's arithmetic overlaps the memory latency; that matters when a
+// workgroup has its SIMDs to itself, as in the walks' later positions.
+template <typename T, bool kSampling, bool kNT = true, int kU = kUnroll, bool kPipe = false>
 __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
                                                             float s2, RowSmem& sm,
                                                             float* lane_max = nullptr) {
@@ -283,8 +287,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
 
     float m = -INFINITY;   // running max (sampling: reference of z)
     double z = 0.0;        // sampling: sum exp2((l - m) * s2)
-    int bfirst = -1;       // greedy: first vector of the batch that first reached m
-    int bcount = 0;        //         vectors in that batch (kU, or 1 in the remainder)
+    int im = INT_MAX;      // greedy: lowest index attaining m among this lane's vectors
     float ms = -INFINITY;  // greedy: max over this lane's scalar head / tail elements
     int is = INT_MAX;      //         lowest index attaining ms
 
@@ -344,20 +347,57 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
                 }
                 z += (double)acc;
             }
-        } else if (bm > m) {
+        } else if (bm > m) {  // a new maximum: its first element in this batch (index order)
             m = bm;
-            bfirst = vfirst;
-            bcount = nvec;
+            int first = INT_MAX;
+#pragma unroll
+            for (int u = nvec - 1; u >= 0; --u) {
+                float f[kVec];
+                Ld<T>::unpack(raw[u], f);
+#pragma unroll
+                for (int e = kVec - 1; e >= 0; --e)
+                    if (f[e] == bm) first = (vfirst + u * kBlock) * kVec + e;
+            }
+            im = ebase + first;
         }
     };
 
+    auto load = [&](u32x4* raw, int v0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) raw[u] = kNT ? ld_stream(vp + v0 + u * kBlock) : vp[v0 + u * kBlock];
+    };
     if (tid < head) scalar(tid);
     int v = tid;
-    for (; v + (kU - 1) * kBlock < nv; v += kU * kBlock) {
-        u32x4 raw[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) raw[u] = kNT ? ld_stream(vp + v + u * kBlock) : vp[v + u * kBlock];
-        batch(raw, kU, v);
+    if (kPipe) {
+        // Two named buffers take turns, so no register copy waits for a load, and the next
+        // batch is loaded unconditionally (past the last full batch it re-reads the
+        // current one, already in cache, and is discarded): under a branch, the compiler
+        // could not tell which loads are outstanding and would wait for all of them.
+        u32x4 ra[kU], rb[kU];
+        const int step = kU * kBlock;
+        auto full = [&](int v0) { return v0 + (kU - 1) * kBlock < nv; };
+        if (full(v)) load(ra, v);
+        while (full(v)) {
+            load(rb, full(v + step) ? v + step : v);
+            __builtin_amdgcn_sched_barrier(0);  // batch j + 1 in flight before batch j is reduced
+            batch(ra, kU, v);
+            v += step;
+            if (!full(v)) break;
+            load(ra, full(v + step) ? v + step : v);
+            __builtin_amdgcn_sched_barrier(0);
+            batch(rb, kU, v);
+            v += step;
+        }
+    } else {
+        for (; v + (kU - 1) * kBlock < nv; v += kU * kBlock) {
+            u32x4 raw[kU];
+            load(raw, v);
+            // every load of the batch is issued before the first is waited for (left
+            // alone, the scheduler interleaves the unpacking with the loads and waits
+            // after two)
+            __builtin_amdgcn_sched_barrier(0);
+            batch(raw, kU, v);
+        }
     }
     for (; v < nv; v += kBlock) {
         u32x4 raw = kNT ? ld_stream(vp + v) : vp[v];
@@ -385,20 +425,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
     int idx = INT_MAX;
     if (M != -INFINITY) {
         if (ms == M) idx = is;
-        if (m == M) {  // re-read the batch that first reached M; the lowest index wins
-            for (int u = 0; u < bcount; ++u) {
-                const int vv = bfirst + u * kBlock;
-                float f[kVec];
-                Ld<T>::unpack(vp[vv], f);
-                int hit = -1;
-                for (int e = kVec - 1; e >= 0; --e)
-                    if (f[e] == M) hit = e;
-                if (hit >= 0) {
-                    idx = min(idx, ebase + vv * kVec + hit);
-                    break;
-                }
-            }
-        }
+        if (m == M) idx = min(idx, im);
     }
     r.m = M;
     r.idx = block_min(idx, sm);
@@ -1064,7 +1091,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     int k = G, last = -1;
     bool bad = false;
     for (int i = 0; i <= G; ++i) {
-        const Part cur = chunk_record<T, false, true, kWalkUnroll>(logits + ((size_t)b * R + i) * V,
+        const Part cur = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(logits + ((size_t)b * R + i) * V,
                                                                     lo, hi, 0.f, rs);
         if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), (uint32_t)cur.idx, 0u,
                           xs)) {
@@ -1435,8 +1462,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     double Z = 0.0;
     auto pass = [&](int i) {
         const T* rowp = logits + ((size_t)b * R + i) * V;
-        return a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll>(rowp, lo, hi, s2, rs)
-                               : chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
+        return a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs)
+                               : chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
     };
     for (int i = 0; i <= G; ++i) {
         const T* rowp = logits + ((size_t)b * R + i) * V;
@@ -1632,7 +1659,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         for (int j = tid; j < count && sampling; j += kBlock)
             ts.lx[j] = Ld<T>::one(rowp + ts.tok[ts.kids[j]]);
         if (sampling) {
-            const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
+            const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
             if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
                               dbl_lo(r.z), xs)) {
                 bad = true;
@@ -1647,7 +1674,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
                     Z += dbl_of(xs.xp[j][1], xs.xp[j][2]) * exp(((double)mj - (double)M) / Td);
             }
         } else {
-            const Part r = chunk_record<T, false, true, kWalkUnroll>(rowp, lo, hi, 0.f, rs);
+            const Part r = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, 0.f, rs);
             if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), (uint32_t)r.idx, 0u,
                               xs)) {
                 bad = true;
@@ -1931,7 +1958,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         }
         for (int j = tid; j < count; j += kBlock) sm.lx[j] = Ld<T>::one(rowp + sm.tok[sm.kids[j]]);
         {
-            const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
+            const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
             if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
                               dbl_lo(r.z), xs)) {
                 bad = true;
