@@ -1268,6 +1268,7 @@ __device__ inline void chunk_weights(const T* rowp, const void* qrow, int n, boo
             lr[u] = lq[u * kBlock + tid].raw;
             if (kQ != 0) qr[u] = ld_stream_any(qq + u * kBlock + tid);
         }
+        __builtin_amdgcn_sched_barrier(0);  // all of the chunk's loads before the first use
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             float p4, w4;
@@ -1402,6 +1403,67 @@ __device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const 
     else
         chunk_weights<T, 0, kFilt>(rowp + c0, nullptr, n, fast, W, sm.pw, sm.ww);
     mass_reduce<T, kFilt>(a, st, W, rowp, b, c, sm, ex);
+}
+
+// The draw weights of fine chunks [cb, ce) of the row in `st`, as mass_chunk computes
+// them chunk by chunk, with the loads of chunk c + 1 in flight while chunk c's segment
+// sums are formed: a chunk's registers are free once its weights are in LDS.  Block-wide.
+template <typename T, int kQ, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_slice_q(const KArgs& a, const DrawState& st,
+                                                            const WParams& W, const T* rowp,
+                                                            const void* qrow, int b, int cb,
+                                                            int ce, MassSmem& sm,
+                                                            const int32_t* ex) {
+    typedef typename Quad<T>::Raw LR;
+    typedef typename QRow<T, kQ>::Raw QR;
+    const int tid = threadIdx.x;
+    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
+    LR lr[4];
+    QR qr[4];
+    auto load = [&](int c) {
+        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp + c * kFine);
+        const QR* qq = kQ != 0 ? reinterpret_cast<const QR*>(static_cast<const char*>(qrow) +
+                                                             (size_t)c * kFine * qes)
+                               : nullptr;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            lr[u] = lq[u * kBlock + tid].raw;
+            if (kQ != 0) qr[u] = ld_stream_any(qq + u * kBlock + tid);
+        }
+    };
+    bool fast = cb < ce && chunk_fast<T, kFilt>(rowp, qrow, cb, a.V);
+    if (fast) load(cb);
+    for (int c = cb; c < ce; ++c) {
+        if (fast) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float p4, w4;
+                weigh4<T, kQ, kFilt>(lr[u], qr[u], W, p4, w4);
+                sm.pw[u * kBlock + tid] = p4;
+                sm.ww[u * kBlock + tid] = w4;
+            }
+        } else {
+            const int c0 = c * kFine;
+            chunk_weights<T, kQ, kFilt>(rowp + c0,
+                                        kQ != 0 ? static_cast<const char*>(qrow) + c0 * qes : nullptr,
+                                        min(kFine, a.V - c0), false, W, sm.pw, sm.ww);
+        }
+        fast = c + 1 < ce && chunk_fast<T, kFilt>(rowp, qrow, c + 1, a.V);
+        if (fast) load(c + 1);
+        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads before this one's sums
+        mass_reduce<T, kFilt>(a, st, W, rowp, b, c, sm, ex);
+    }
+}
+
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_slice(const KArgs& a, const DrawState& st,
+                                                          const WParams& W, const T* rowp,
+                                                          const void* qrow, int b, int cb, int ce,
+                                                          MassSmem& sm, const int32_t* ex) {
+    if (qrow)
+        mass_slice_q<T, kFilt ? 2 : 1, kFilt>(a, st, W, rowp, qrow, b, cb, ce, sm, ex);
+    else
+        mass_slice_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex);
 }
 
 // One workgroup per (request, fine chunk).
@@ -1541,8 +1603,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         const T* rowp = logits + (size_t)st.row * V;
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
-        for (int c = lo / kFine; c * kFine < hi; ++c)
-            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
+        mass_slice<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
+                             nullptr);
     }
     walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
@@ -1756,8 +1818,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         const T* rowp = logits + (size_t)st.row * V;
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
-        for (int c = lo / kFine; c * kFine < hi; ++c)
-            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, ts.excl);
+        mass_slice<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
+                             ts.excl);
     }
     walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
@@ -1807,17 +1869,9 @@ __device__ double slice_resid_sum(const T* rowp, const float* qrow, int lo, int 
         const int nq = (hi - lo) / 4;
         const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp + lo);
         const u32x4* qq = reinterpret_cast<const u32x4*>(qrow + lo);
-        for (int i0 = 0; i0 < nq; i0 += 4 * kBlock) {
-            typename Quad<T>::Raw lr[4];
-            u32x4 qr[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * kBlock + tid;
-                if (i < nq) {
-                    lr[u] = lq[i].raw;
-                    qr[u] = ld_stream(qq + i);
-                }
-            }
+        typedef typename Quad<T>::Raw LR;
+        // a batch: quads i0 + u * kBlock + tid, u < 4, summed in fp32, added in fp64
+        auto weigh = [&](const LR* lr, const u32x4* qr, int i0) {
             float bs = 0.f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1832,6 +1886,50 @@ __device__ double slice_resid_sum(const T* rowp, const float* qrow, int lo, int 
                 }
             }
             acc += (double)bs;
+        };
+        auto load = [&](LR* lr, u32x4* qr, int i0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                lr[u] = lq[i0 + u * kBlock + tid].raw;
+                qr[u] = ld_stream(qq + i0 + u * kBlock + tid);
+            }
+        };
+        // Full batches (every lane in range) with the next one in flight while one is
+        // weighed: two named buffers take turns, and the next batch is loaded
+        // unconditionally (past the last full batch it re-reads the current one), so the
+        // compiler waits only for the batch it is about to weigh.
+        const int step = 4 * kBlock;
+        const int nfull = nq / step * step;
+        int i0 = 0;
+        if (nfull > 0) {
+            LR la[4], lb[4];
+            u32x4 qa[4], qb[4];
+            load(la, qa, 0);
+            for (;;) {
+                load(lb, qb, i0 + step < nfull ? i0 + step : i0);
+                __builtin_amdgcn_sched_barrier(0);
+                weigh(la, qa, i0);
+                i0 += step;
+                if (i0 >= nfull) break;
+                load(la, qa, i0 + step < nfull ? i0 + step : i0);
+                __builtin_amdgcn_sched_barrier(0);
+                weigh(lb, qb, i0);
+                i0 += step;
+                if (i0 >= nfull) break;
+            }
+        }
+        if (i0 < nq) {  // the partial last batch
+            LR lr[4];
+            u32x4 qr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kBlock + tid;
+                if (i < nq) {
+                    lr[u] = lq[i].raw;
+                    qr[u] = ld_stream(qq + i);
+                }
+            }
+            weigh(lr, qr, i0);
         }
         done = lo + nq * 4;
     }
@@ -2045,8 +2143,8 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         const T* rowp = logits + (size_t)st.row * V;
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
-        for (int c = lo / kFine; c * kFine < hi; ++c)
-            mass_chunk<T, false>(a, st, Wp, rowp, qrow, b, c, ms, nullptr);
+        mass_slice<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
+                             nullptr);
     }
     walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs

@@ -226,20 +226,27 @@ def test_chain_temperatures_boosted(T):
     check_chain(c, f"boosted T={T}")
 
 
-def test_greedy_ties_bf16():
-    """Many tied maxima (small-integer logits in bf16): lowest id must win everywhere."""
+@pytest.mark.parametrize("dtype,V,eager", [(wl.BF16, 70000, False), (wl.BF16, 70000, True),
+                                           (wl.F32, 70001, False), (wl.F32, 70001, True)])
+def test_greedy_ties(dtype, V, eager, monkeypatch):
+    """Many tied maxima (small-integer logits): the lowest id must win everywhere, in the
+    walk and in the eager passes, in both dtypes; V = 70001 leaves a ragged last chunk."""
+    if eager:
+        monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
     rng = np.random.default_rng(17)
-    B, G, V = 64, 4, 70000
+    B, G = 64, 4
     lg = rng.integers(0, 4, size=(B, G + 1, V)).astype(np.float32)
-    bits = wl.f32_to_bf16_bits(lg)
+    data = wl.f32_to_bf16_bits(lg) if dtype == wl.BF16 else lg
     want = np.argmax(lg, -1)
     x = want[:, :G].copy()
     flip = rng.random((B, G)) < 0.25
     x[flip] = (x[flip] + 1) % V
-    ga, go = gpu_greedy(bits, wl.BF16, x.astype(np.int32))
-    oa, oo = oracle.verify_greedy(bits, wl.BF16, x.astype(np.int32))
+    say(f"greedy ties {dtype} V={V} eager={eager}")
+    ga, go = gpu_greedy(data, dtype, x.astype(np.int32))
+    oa, oo = oracle.verify_greedy(data, dtype, x.astype(np.int32))
     np.testing.assert_array_equal(ga, oa)
     np.testing.assert_array_equal(go, oo)
+    assert (oa == G).sum() > 0 and (oa < G).sum() > 0
 
 
 def test_tree_low_entropy_deep_walks():
