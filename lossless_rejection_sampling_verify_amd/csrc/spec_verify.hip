@@ -1090,11 +1090,14 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     const int px = (tid & 63) < G ? x[tid & 63] : -1;
     int k = G, last = -1;
     bool bad = false;
+    auto pass = [&](int r) {
+        const Part cur = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(
+            logits + ((size_t)b * R + r) * V, lo, hi, 0.f, rs);
+        cluster_publish(slots, r, W, w, tag, __float_as_uint(cur.m), (uint32_t)cur.idx, 0u, xs);
+    };
+    pass(0);
     for (int i = 0; i <= G; ++i) {
-        const Part cur = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(logits + ((size_t)b * R + i) * V,
-                                                                    lo, hi, 0.f, rs);
-        if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), (uint32_t)cur.idx, 0u,
-                          xs)) {
+        if (!cluster_wait(slots, i, W, tag, xs)) {
             bad = true;
             break;
         }
@@ -1122,6 +1125,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
             k = i;
             break;
         }
+        pass(i + 1);
     }
     walk_end(hdr, epoch, w, W);
     if (w != 0) return;
@@ -1522,14 +1526,17 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     int k = G;
     float M = -INFINITY;
     double Z = 0.0;
-    auto pass = [&](int i) {
-        const T* rowp = logits + ((size_t)b * R + i) * V;
-        return a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs)
-                               : chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+    auto pass = [&](int r) {
+        const T* rowp = logits + ((size_t)b * R + r) * V;
+        const Part cur =
+            a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs)
+                            : chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+        cluster_publish(slots, r, W, w, tag, __float_as_uint(cur.m), dbl_hi(cur.z), dbl_lo(cur.z),
+                        xs);
     };
+    pass(0);
     for (int i = 0; i <= G; ++i) {
         const T* rowp = logits + ((size_t)b * R + i) * V;
-        const Part cur = pass(i);
         int xi = -1;
         float lx = 0.f, qx = 0.f, ui = 0.f;
         if (i < G && tid < 64) {  // the acceptance test's inputs, gathered during the hand-off
@@ -1540,8 +1547,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
                 qx = a.q[((size_t)b * G + i) * V + xi];
             }
         }
-        if (!cluster_step(slots, i, W, w, tag, __float_as_uint(cur.m), dbl_hi(cur.z),
-                          dbl_lo(cur.z), xs)) {
+        if (!cluster_wait(slots, i, W, tag, xs)) {
             bad = true;
             break;
         }
@@ -1585,6 +1591,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             k = i;
             break;
         }
+        pass(i + 1);
     }
     DrawState st = {};
     st.kind = kDrawNone;
