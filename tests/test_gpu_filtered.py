@@ -130,3 +130,23 @@ def test_candidate_overflow_and_plateaus(dtype):
             g, o = check(c2, f"plateau of {width}, shared={shared}, {dtype}")
             if shared:
                 assert (o["accept_len"] == c.G).all()
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_top_keys_crowded_in_one_lane(dtype):
+    """The first pass keeps each lane's four largest keys; when one lane holds more of the
+    row's top-k than that (here its first two 16-byte vectors carry the eight largest
+    logits of every row), the selection must fall back to a second pass over the row and
+    still match the oracle."""
+    import dataclasses
+    c = wl.make_chain_logits(2, seed=31, B=8, G=3, V=40000, dtype=dtype, top_k=50, top_p=0.9)
+    kvec = 8 if dtype == wl.BF16 else 4
+    ids = np.array([0, 1, 2, 3, 256 * kvec, 256 * kvec + 1, 256 * kvec + 2, 256 * kvec + 3])
+    tl = wl.logits_as_f32(c.logits, dtype).copy()
+    dl = wl.logits_as_f32(c.draft_logits, dtype).copy()
+    enc = (lambda f: wl.f32_to_bf16_bits(f)) if dtype == wl.BF16 else (lambda f: f)
+    for arr in (tl, dl):
+        top = arr.max(axis=-1, keepdims=True)
+        arr[..., ids] = top + np.arange(1, 9, dtype=np.float32)
+    c2 = dataclasses.replace(c, logits=enc(tl), draft_logits=enc(dl))
+    check(c2, f"top keys crowded in lane 0, {dtype}")
