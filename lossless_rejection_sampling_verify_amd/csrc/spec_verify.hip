@@ -132,6 +132,7 @@ struct KArgs {
     FiltRow* frows;      // filtered calls: [B*R] target rows, then [B*G] draft rows
     int fixbits;         // fixed-point fraction bits of the filter's mass histograms
     int walk_temporal;   // chain walk: row passes with cache-allocating loads (sweeps: 0)
+    int coin_stride;     // coins per request in `coins`; the final draw's coin is the last
     unsigned* hdr;       // workspace header: the walks' call counter and finished count
 };
 
@@ -1249,14 +1250,22 @@ __device__ inline void weigh4(const typename Quad<T>::Raw& lr, const typename QR
     ww = kQ != 0 ? ws : ps;
 }
 
+// LDS slot of quad q (0..1023) of a fine chunk in the weight staging arrays: the 16 quads of
+// segment g (q = 16 g + i) sit in column g of a 16 x 65 array, so the lane summing segment g
+// reads consecutive words across lanes (no bank conflicts; rows padded to 65 so that the
+// writers, 16 consecutive lanes per row, spread over the banks too).
+constexpr int kStageRow = 65;
+static_assert(kSegs == 64 && kFine / 4 == 16 * kSegs, "a chunk is 1024 quads in 64 segments of 16");
+__device__ inline int stage_slot(int q) { return (q & 15) * kStageRow + (q >> 4); }
+
 template <typename V>
 __device__ inline V ld_stream_any(const V* p) {
     return __builtin_nontemporal_load(p);
 }
 
 // Lane t of the block takes elements 4t..4t+3 of each 1024-element quarter u of the chunk
-// and leaves their weight sums in entry u * kBlock + t of `pw` / `ww` (LDS): segment g is
-// then entries 16g .. 16g + 15.
+// (quad q = u * kBlock + t) and leaves their weight sums in slot stage_slot(q) of `pw` /
+// `ww` (LDS): segment g is quads 16g .. 16g + 15.
 template <typename T, int kQ, bool kFilt>
 __device__ inline void chunk_weights(const T* rowp, const void* qrow, int n, bool fast,
                                      const WParams& W, float* pw, float* ww) {
@@ -1277,8 +1286,8 @@ __device__ inline void chunk_weights(const T* rowp, const void* qrow, int n, boo
         for (int u = 0; u < 4; ++u) {
             float p4, w4;
             weigh4<T, kQ, kFilt>(lr[u], qr[u], W, p4, w4);
-            pw[u * kBlock + tid] = p4;
-            ww[u * kBlock + tid] = w4;
+            pw[stage_slot(u * kBlock + tid)] = p4;
+            ww[stage_slot(u * kBlock + tid)] = w4;
         }
         return;
     }
@@ -1293,8 +1302,8 @@ __device__ inline void chunk_weights(const T* rowp, const void* qrow, int n, boo
                 w4 += w;
             }
         }
-        pw[u * kBlock + tid] = p4;
-        ww[u * kBlock + tid] = kQ != 0 ? w4 : p4;
+        pw[stage_slot(u * kBlock + tid)] = p4;
+        ww[stage_slot(u * kBlock + tid)] = kQ != 0 ? w4 : p4;
     }
 }
 
@@ -1308,8 +1317,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
 }
 
 struct MassSmem {
-    float pw[4 * kBlock];  // plain target weight of each lane's four elements, per quarter
-    float ww[4 * kBlock];  // draw weight of the same
+    float pw[16 * kStageRow];  // plain target weight of each quad of a chunk (stage_slot)
+    float ww[16 * kStageRow];  // draw weight of the same
     double xs[kSegs];      // excluded weight of each segment
 };
 
@@ -1363,8 +1372,8 @@ __device__ __attribute__((always_inline)) void mass_reduce(const KArgs& a, const
         double Wt = 0.0, P = 0.0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            Wt += (double)sm.ww[16 * tid + i];
-            P += (double)sm.pw[16 * tid + i];
+            Wt += (double)sm.ww[i * kStageRow + tid];  // quad 16 * tid + i
+            P += (double)sm.pw[i * kStageRow + tid];
         }
         if (sm.xs[tid] > 0.0) {
             const double rem = Wt - sm.xs[tid];
@@ -1443,8 +1452,8 @@ __device__ __attribute__((always_inline)) void mass_slice_q(const KArgs& a, cons
             for (int u = 0; u < 4; ++u) {
                 float p4, w4;
                 weigh4<T, kQ, kFilt>(lr[u], qr[u], W, p4, w4);
-                sm.pw[u * kBlock + tid] = p4;
-                sm.ww[u * kBlock + tid] = w4;
+                sm.pw[stage_slot(u * kBlock + tid)] = p4;
+                sm.ww[stage_slot(u * kBlock + tid)] = w4;
             }
         } else {
             const int c0 = c * kFine;
@@ -2244,14 +2253,19 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
     const int lane = threadIdx.x;
     const int S2 = a.S2, V = a.V;
     const int b = blockIdx.x;
+    // the first 64 chunk masses and the request's last coin (the final draw's) do not depend
+    // on the draw state: read them alongside it
+    const double m0 = lane < S2 ? a.mass[(size_t)b * S2 + lane] : 0.0;
+    const bool coin_known = a.coins != nullptr && a.coin_stride > 0;
+    const float u0 = coin_known ? a.coins[(size_t)b * a.coin_stride + a.coin_stride - 1] : 0.f;
     const DrawState st = load_state(a.dstate + b);
     if (st.kind == kDrawNone) return;
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * V;
     const void* qrow;
     const WParams W = draw_params<T, kFilt>(a, st, qrow);
-    const double u = (double)a.coins[st.coin];
-    double tot = 0.0;
-    for (int i0 = 0; i0 < S2; i0 += 64)
+    const double u = (double)(coin_known ? u0 : a.coins[st.coin]);
+    double tot = wave_sum(m0);
+    for (int i0 = 64; i0 < S2; i0 += 64)
         tot += wave_sum(i0 + lane < S2 ? a.mass[(size_t)b * S2 + i0 + lane] : 0.0);
     const bool fallback = !(tot > 0.0);  // plain target weights, nothing excluded
     if (fallback) {
@@ -2264,7 +2278,14 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
     float ly = 0.f;
     const double t = u * tot;
     double before = 0.0;
-    const int c = wave_locate((fallback ? a.massfb : a.mass) + (size_t)b * S2, S2, t, before);
+    int c;
+    if (!fallback && S2 <= 64) {  // the masses are in registers already (as wave_locate finds)
+        const Found f = wave_find(m0, t, 0.0);
+        c = f.hit >= 0 ? f.hit : f.last;
+        before = f.hit >= 0 ? f.before : f.last_before;
+    } else {
+        c = wave_locate((fallback ? a.massfb : a.mass) + (size_t)b * S2, S2, t, before);
+    }
     if (c >= 0) {
         const double tc = t - before;
         // segment weights: stored by k_mass, or (fallback) the plain target row, summed here
@@ -3299,6 +3320,7 @@ extern "C" int spec_verify_chain(const void* logits, int dtype, const float* dra
     a.q = draft_probs;
     a.tokens = draft_tokens;
     a.coins = coins;
+    a.coin_stride = G + 1;  // [B][G + 1] coins, the last one for the final draw
     a.temperature = temperature;
     a.B = B;
     a.R = G + 1;
@@ -3342,6 +3364,7 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     a.tokens = node_tokens;
     a.parents = parents;
     a.coins = coins;
+    a.coin_stride = D + 1;  // [B][D + 1] coins, the last one for the final draw
     a.temperature = temperature;
     a.B = B;
     a.R = N;
@@ -3386,6 +3409,7 @@ extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* 
     a.tokens = node_tokens;
     a.parents = parents;
     a.coins = coins;
+    a.coin_stride = N;  // [B][N] coins, the last one for the final draw
     a.temperature = temperature;
     a.B = B;
     a.R = N;
@@ -3454,6 +3478,7 @@ extern "C" int spec_verify_chain_filtered(const void* logits, const void* draft_
     a.dlogits = draft_logits;
     a.tokens = draft_tokens;
     a.coins = coins;
+    a.coin_stride = G + 1;  // [B][G + 1] coins, the last one for the final draw
     a.temperature = temperature;
     a.top_k = top_k;
     a.top_p = top_p;
