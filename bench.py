@@ -202,7 +202,8 @@ def main():
             "greedy": {"avg_ms": float(greedy_ms.mean()), "p90_ms": float(np.percentile(greedy_ms, 90)),
                        "GB/s": greedy_gbs, "frac": greedy_gbs / HBM_PEAK_GBS,
                        "positions/s": B * R / (greedy_ms.mean() * 1e-3),
-                       "rows_consulted": int((acc_g + 1).sum())},
+                       "rows_consulted": int((acc_g + 1).sum()),
+                       "tokens/s": float((acc_g + 1).sum()) / (greedy_ms.mean() * 1e-3)},
             "chain": {"avg_ms": float(chain_ms.mean()), "p90_ms": float(np.percentile(chain_ms, 90)),
                       "GB/s": chain_gbs, "frac": chain_gbs / HBM_PEAK_GBS,
                       "positions/s": B * R / (chain_ms.mean() * 1e-3),
@@ -219,6 +220,10 @@ def main():
         "input_generation_s": gen_s,
     }
 
+    # exponentials per chain call: one per element of every consulted row and of the row
+    # the last token is drawn from
+    result["calibration"] = _calibration(torch, dev, api,
+                                         exps_chain=(int((acc_c + 1).sum()) + B) * V)
     if args.tree:
         result["modes"].update(_tree_modes(args, torch, dev, api, wl))
     if args.filtered:
@@ -480,6 +485,40 @@ def _filtered_mode(args, torch, dev, api, wl):
                                "row_bytes_once": once,
                                "GB/s_rows_once": once / (t.mean() * 1e-3) / 1e9,
                                "accepted_mean": float(acc.float().mean().item())}}
+
+
+def _calibration(torch, dev, api, exps_chain):
+    """This device's own ceilings, measured after the timed region: the read bandwidth
+    of the row passes' access pattern (16-byte non-temporal loads over 2 GiB) and the
+    v_exp_f32 throughput, with the time the chain call's exponentials alone would take."""
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    read_ms = timed(lambda: api.spec_calib_read(buf, sink), 7)
+    del buf
+    blocks, iters = 4096, 1024
+    exp_ms = timed(lambda: api.spec_calib_exp(blocks, iters, sink), 5)
+    exp_rate = blocks * 256 * iters * 8 / (exp_ms * 1e-3)
+    read_gbs = nbytes / (read_ms * 1e-3) / 1e9
+    return {"read_GB/s": read_gbs, "read_frac_of_peak": read_gbs / HBM_PEAK_GBS,
+            "read_bytes": nbytes, "exp_per_s": exp_rate,
+            "chain_exps_per_call": exps_chain,
+            "chain_exp_floor_ms": exps_chain / exp_rate * 1e3}
 
 
 def _cpu_baseline(c, seconds):

@@ -244,6 +244,26 @@ int spec_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_len
                         int N, const void* kv_tree, void* kv_out, size_t row_bytes,
                         int32_t* slots, void* stream);
 
+/* Measurement utilities (not part of the verify path).  They calibrate the figures the
+ * verify kernels are judged against on the device at hand.
+ *
+ * spec_calib_read: streams `bytes` bytes of device memory from `data` with 16-byte loads
+ * that do not allocate in the caches, the access pattern of the row passes, and reduces
+ * them to nothing observable; the caller times the call to get the achievable read
+ * bandwidth.  `data` 16-byte aligned, `bytes` a multiple of 16 (SPEC_ERR_PARAM
+ * otherwise), 0 is a no-op.  `sink` (one float, device) is written only in the
+ * impossible case that the reduction hits a sentinel, which keeps the reads from being
+ * optimised away.
+ *
+ * spec_calib_exp: `blocks` workgroups of 256 lanes each evaluate iters * 8 independent
+ * v_exp_f32 (the row passes' exponential), so the caller gets the exponential throughput
+ * as blocks * 256 * iters * 8 / time.  1 <= blocks <= 65535, 1 <= iters <= 1 << 20
+ * (SPEC_ERR_PARAM otherwise).  `sink` as above.
+ *
+ * Both enqueue on `stream` and return SPEC_OK, an argument error, or SPEC_ERR_HIP. */
+int spec_calib_read(const void* data, size_t bytes, float* sink, void* stream);
+int spec_calib_exp(int blocks, int iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

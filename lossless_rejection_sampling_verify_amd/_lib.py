@@ -65,6 +65,10 @@ def lib():
         L.spec_tree_mask.restype = ip
         L.spec_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, sz, vp, vp]
         L.spec_tree_commit_kv.restype = ip
+        L.spec_calib_read.argtypes = [vp, sz, vp, vp]
+        L.spec_calib_read.restype = ip
+        L.spec_calib_exp.argtypes = [ip, ip, vp, vp]
+        L.spec_calib_exp.restype = ip
         _lib = L
     return _lib
 

@@ -299,3 +299,24 @@ def spec_tree_commit_kv(accepted_nodes: torch.Tensor, accept_len: torch.Tensor,
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_tree_commit_kv", rc)
     return slots
+
+
+def spec_calib_read(data: torch.Tensor, sink: torch.Tensor, *, stream=None):
+    """Read-bandwidth calibration: streams every byte of the contiguous device tensor
+    `data` (16-byte aligned, nbytes a multiple of 16).  `sink` is a one-element fp32
+    device tensor the kernel writes only on an impossible sentinel."""
+    if data.device.type != "cuda" or not data.is_contiguous():
+        raise ValueError("data must be a contiguous device tensor")
+    _check(sink, "sink", torch.float32, 1)
+    rc = L.lib().spec_calib_read(_ptr(data), data.numel() * data.element_size(), _ptr(sink),
+                                 _stream(data.device, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_calib_read", rc)
+
+
+def spec_calib_exp(blocks: int, iters: int, sink: torch.Tensor, *, stream=None):
+    """Exponential-throughput calibration: blocks * 256 * iters * 8 v_exp_f32."""
+    _check(sink, "sink", torch.float32, 1)
+    rc = L.lib().spec_calib_exp(int(blocks), int(iters), _ptr(sink), _stream(sink.device, stream))
+    if rc != L.SPEC_OK:
+        raise L.SpecVerifyError("spec_calib_exp", rc)

@@ -3245,6 +3245,49 @@ int run_chain_filtered(KArgs& a, hipStream_t st) {
     return run_draw<T, true>(a, st);
 }
 
+// ---------------------------------------------------------------------------------------
+// measurement utilities: the read ceiling and the exponential throughput of this device
+
+// Each workgroup streams kCalibChunk bytes (the last one the rest) with 16-byte
+// non-temporal loads, 8 in flight per lane, and folds them into one value; the sink is
+// written only if that value equals a sentinel, so no load can be dropped.
+constexpr size_t kCalibChunk = 256 * 1024;
+__global__ __launch_bounds__(kBlock) void k_calib_read(const u32x4* data, size_t nvec,
+                                                      float* sink) {
+    const size_t v0 = (size_t)blockIdx.x * (kCalibChunk / 16);
+    const size_t v1 = min(nvec, v0 + kCalibChunk / 16);
+    uint32_t acc = 0u;
+    size_t v = v0 + threadIdx.x;
+    for (; v + 7 * kBlock < v1; v += 8 * kBlock) {
+        u32x4 r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r[u] = ld_stream(data + v + u * kBlock);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+    }
+    for (; v < v1; v += kBlock) {
+        const u32x4 r = ld_stream(data + v);
+        acc ^= r.x ^ r.y ^ r.z ^ r.w;
+    }
+    if (acc == 0x7fc0deadu) sink[0] = __uint_as_float(acc);
+}
+
+// Eight independent exponential chains per lane; the sink is written only on a sentinel.
+__global__ __launch_bounds__(kBlock) void k_calib_exp(int iters, float* sink) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = -0.001f * (float)(threadIdx.x + e);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ex2(x[e]) - 1.0f;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += x[e];
+    if (s == 12345.5f) sink[0] = s;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -3496,4 +3539,24 @@ extern "C" int spec_verify_chain_filtered(const void* logits, const void* draft_
     bind_workspace(a, workspace, SPEC_OP_CHAIN_FILTERED);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return dtype == SPEC_F32 ? run_chain_filtered<float>(a, st) : run_chain_filtered<uint16_t>(a, st);
+}
+
+extern "C" int spec_calib_read(const void* data, size_t bytes, float* sink, void* stream) {
+    if (bytes == 0) return SPEC_OK;
+    if (!data || !sink) return SPEC_ERR_NULL;
+    if (((uintptr_t)data) % 16 || bytes % 16) return SPEC_ERR_PARAM;
+    const size_t blocks = (bytes + kCalibChunk - 1) / kCalibChunk;
+    if (blocks > 0x7fffffffULL) return SPEC_ERR_SHAPE;
+    hipLaunchKernelGGL(k_calib_read, dim3((unsigned)blocks), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(data),
+                       bytes / 16, sink);
+    return launch_status();
+}
+
+extern "C" int spec_calib_exp(int blocks, int iters, float* sink, void* stream) {
+    if (!sink) return SPEC_ERR_NULL;
+    if (blocks < 1 || blocks > 65535 || iters < 1 || iters > (1 << 20)) return SPEC_ERR_PARAM;
+    hipLaunchKernelGGL(k_calib_exp, dim3(blocks), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
+    return launch_status();
 }

@@ -195,3 +195,17 @@ def test_tree_mss_rejects_bad_arguments(lib):
     assert call(wsb=ws - 1) == L.SPEC_ERR_WORKSPACE
     assert call(q=P + 2) == L.SPEC_ERR_PARAM
     assert call(B=0) == L.SPEC_OK
+
+
+def test_calibration_utilities_reject_bad_arguments(lib):
+    """Argument errors of the measurement utilities are found on the host, before any
+    launch (these pointers are never dereferenced)."""
+    fake = ctypes.c_void_p(1 << 20)  # 16-byte aligned, non-null, never read
+    assert lib.spec_calib_read(None, 0, None, None) == L.SPEC_OK        # nothing to read
+    assert lib.spec_calib_read(None, 16, fake, None) == L.SPEC_ERR_NULL
+    assert lib.spec_calib_read(fake, 16, None, None) == L.SPEC_ERR_NULL
+    assert lib.spec_calib_read(ctypes.c_void_p((1 << 20) + 4), 16, fake, None) == L.SPEC_ERR_PARAM
+    assert lib.spec_calib_read(fake, 24, fake, None) == L.SPEC_ERR_PARAM
+    assert lib.spec_calib_exp(1, 1, None, None) == L.SPEC_ERR_NULL
+    for blocks, iters in ((0, 1), (65536, 1), (1, 0), (1, (1 << 20) + 1)):
+        assert lib.spec_calib_exp(blocks, iters, fake, None) == L.SPEC_ERR_PARAM
