@@ -1322,6 +1322,11 @@ struct MassSmem {
     double xs[kSegs];      // excluded weight of each segment
 };
 
+// Two chunks' staging, weighed together and summed by waves 0 and 1 (the walks).
+struct MassSmem2 {
+    MassSmem s[2];
+};
+
 // The draw weights' parameters and draft row of a request's draw state.
 template <typename T, bool kFilt>
 __device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const void*& qrow) {
@@ -1418,6 +1423,58 @@ __device__ __attribute__((always_inline)) void mass_chunk(const KArgs& a, const 
     mass_reduce<T, kFilt>(a, st, W, rowp, b, c, sm, ex);
 }
 
+// Segment and chunk sums of chunks cA (staged in sm.s[0], summed by wave 0) and cB (in
+// sm.s[1], wave 1; -1 for none), each exactly as mass_reduce sums one chunk.  Block-wide.
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_reduce_pair(const KArgs& a,
+                                                                const DrawState& st,
+                                                                const WParams& W, const T* rowp,
+                                                                int b, int cA, int cB,
+                                                                MassSmem2& sm,
+                                                                const int32_t* ex) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int S2 = a.S2;
+    const int c = wv == 0 ? cA : (wv == 1 ? cB : -1);  // the chunk this wave sums
+    MassSmem& ms = sm.s[wv & 1];
+    if (wv < 2) ms.xs[lane] = 0.0;
+    __syncthreads();
+    if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
+        if (lane == 0 && c >= 0) {
+            const int c0 = c * kFine;
+            const int n = min(kFine, a.V - c0);
+            for (int e = 0; e < st.nexcl; ++e) {
+                const int t = ex[e];
+                if (t >= c0 && t < c0 + n) {
+                    float p;
+                    draw_weight<T, 0, kFilt>(rowp, nullptr, t, W, p);
+                    ms.xs[(t - c0) / kSeg] += (double)p;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (c >= 0) {  // lane g sums segment g in ascending order
+        double Wt = 0.0, P = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Wt += (double)ms.ww[i * kStageRow + lane];  // quad 16 * lane + i
+            P += (double)ms.pw[i * kStageRow + lane];
+        }
+        if (ms.xs[lane] > 0.0) {
+            const double rem = Wt - ms.xs[lane];
+            Wt = rem > Wt * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
+        }
+        a.seg[((size_t)b * S2 + c) * kSegs + lane] = Wt;
+        Wt = wave_sum(Wt);
+        P = wave_sum(P);
+        if (lane == 0) {
+            a.mass[(size_t)b * S2 + c] = Wt;
+            a.massfb[(size_t)b * S2 + c] = P;
+        }
+    }
+    __syncthreads();  // the staging is reused by the next pair
+}
+
 // The draw weights of fine chunks [cb, ce) of the row in `st`, as mass_chunk computes
 // them chunk by chunk, with the loads of chunk c + 1 in flight while chunk c's segment
 // sums are formed: a chunk's registers are free once its weights are in LDS.  Block-wide.
@@ -1477,6 +1534,72 @@ __device__ __attribute__((always_inline)) void mass_slice(const KArgs& a, const 
         mass_slice_q<T, kFilt ? 2 : 1, kFilt>(a, st, W, rowp, qrow, b, cb, ce, sm, ex);
     else
         mass_slice_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex);
+}
+
+// The draw weights of fine chunks [cb, ce) of the row in `st`, as mass_chunk computes them,
+// two chunks per round: both chunks' loads are in flight together, and waves 0 and 1 sum
+// one chunk each.  Block-wide.
+template <typename T, int kQ, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_slice2_q(const KArgs& a, const DrawState& st,
+                                                            const WParams& W, const T* rowp,
+                                                            const void* qrow, int b, int cb,
+                                                            int ce, MassSmem2& sm,
+                                                            const int32_t* ex) {
+    typedef typename Quad<T>::Raw LR;
+    typedef typename QRow<T, kQ>::Raw QR;
+    const int tid = threadIdx.x;
+    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
+    LR la[4], lb[4];
+    QR qa[4], qb[4];
+    auto load = [&](int c, LR* lr, QR* qr) {
+        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp + c * kFine);
+        const QR* qq = kQ != 0 ? reinterpret_cast<const QR*>(static_cast<const char*>(qrow) +
+                                                             (size_t)c * kFine * qes)
+                               : nullptr;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            lr[u] = lq[u * kBlock + tid].raw;
+            if (kQ != 0) qr[u] = ld_stream_any(qq + u * kBlock + tid);
+        }
+    };
+    auto stage = [&](int c, bool fast, const LR* lr, const QR* qr, MassSmem& ms) {
+        if (fast) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float p4, w4;
+                weigh4<T, kQ, kFilt>(lr[u], qr[u], W, p4, w4);
+                ms.pw[stage_slot(u * kBlock + tid)] = p4;
+                ms.ww[stage_slot(u * kBlock + tid)] = w4;
+            }
+        } else {
+            const int c0 = c * kFine;
+            chunk_weights<T, kQ, kFilt>(rowp + c0,
+                                        kQ != 0 ? static_cast<const char*>(qrow) + c0 * qes : nullptr,
+                                        min(kFine, a.V - c0), false, W, ms.pw, ms.ww);
+        }
+    };
+    for (int c = cb; c < ce; c += 2) {
+        const bool two = c + 1 < ce;
+        const bool fa = chunk_fast<T, kFilt>(rowp, qrow, c, a.V);
+        const bool fb = two && chunk_fast<T, kFilt>(rowp, qrow, c + 1, a.V);
+        if (fa) load(c, la, qa);
+        if (fb) load(c + 1, lb, qb);
+        __builtin_amdgcn_sched_barrier(0);  // both chunks' loads before the first use
+        stage(c, fa, la, qa, sm.s[0]);
+        if (two) stage(c + 1, fb, lb, qb, sm.s[1]);
+        mass_reduce_pair<T, kFilt>(a, st, W, rowp, b, c, two ? c + 1 : -1, sm, ex);
+    }
+}
+
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_slice2(const KArgs& a, const DrawState& st,
+                                                          const WParams& W, const T* rowp,
+                                                          const void* qrow, int b, int cb, int ce,
+                                                          MassSmem2& sm, const int32_t* ex) {
+    if (qrow)
+        mass_slice2_q<T, kFilt ? 2 : 1, kFilt>(a, st, W, rowp, qrow, b, cb, ce, sm, ex);
+    else
+        mass_slice2_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex);
 }
 
 // One workgroup per (request, fine chunk).
@@ -2003,7 +2126,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     __shared__ MssWalkSmem sm;
     __shared__ RowSmem rs;
     __shared__ XSmem xs;
-    __shared__ MassSmem ms;
+    __shared__ MassSmem2 ms;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x / W, w = blockIdx.x - b * W;
     const int N = a.R, V = a.V, D = a.D;
@@ -2159,7 +2282,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         const T* rowp = logits + (size_t)st.row * V;
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
-        mass_slice<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
+        mass_slice2<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
                              nullptr);
     }
     walk_end(hdr, epoch, w, W);
