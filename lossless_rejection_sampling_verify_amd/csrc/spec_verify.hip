@@ -1327,6 +1327,11 @@ struct MassSmem2 {
     MassSmem s[2];
 };
 
+// Four chunks' staging, summed by the four waves (one chunk each).
+struct MassSmem4 {
+    MassSmem s[kWaves];
+};
+
 // The draw weights' parameters and draft row of a request's draw state.
 template <typename T, bool kFilt>
 __device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const void*& qrow) {
@@ -1602,6 +1607,127 @@ __device__ __attribute__((always_inline)) void mass_slice2(const KArgs& a, const
         mass_slice2_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex);
 }
 
+// Segment and chunk sums of chunks c0 .. cend - 1 (at most kWaves), chunk c0 + w staged in
+// sm.s[w] and summed by wave w exactly as mass_reduce sums one chunk.  Block-wide.
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_reduce_quad(const KArgs& a,
+                                                                const DrawState& st,
+                                                                const WParams& W, const T* rowp,
+                                                                int b, int c0, int cend,
+                                                                MassSmem4& sm,
+                                                                const int32_t* ex) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int S2 = a.S2;
+    const int c = c0 + wv < cend ? c0 + wv : -1;  // the chunk this wave sums
+    MassSmem& ms = sm.s[wv];
+    ms.xs[lane] = 0.0;
+    __syncthreads();
+    if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
+        if (lane == 0 && c >= 0) {
+            const int cc0 = c * kFine;
+            const int n = min(kFine, a.V - cc0);
+            for (int e = 0; e < st.nexcl; ++e) {
+                const int t = ex[e];
+                if (t >= cc0 && t < cc0 + n) {
+                    float p;
+                    draw_weight<T, 0, kFilt>(rowp, nullptr, t, W, p);
+                    ms.xs[(t - cc0) / kSeg] += (double)p;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (c >= 0) {  // lane g sums segment g in ascending order
+        double Wt = 0.0, P = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Wt += (double)ms.ww[i * kStageRow + lane];  // quad 16 * lane + i
+            P += (double)ms.pw[i * kStageRow + lane];
+        }
+        if (ms.xs[lane] > 0.0) {
+            const double rem = Wt - ms.xs[lane];
+            Wt = rem > Wt * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
+        }
+        a.seg[((size_t)b * S2 + c) * kSegs + lane] = Wt;
+        Wt = wave_sum(Wt);
+        P = wave_sum(P);
+        if (lane == 0) {
+            a.mass[(size_t)b * S2 + c] = Wt;
+            a.massfb[(size_t)b * S2 + c] = P;
+        }
+    }
+    __syncthreads();  // the staging is reused by the next four chunks
+}
+
+// The draw weights of fine chunks [cb, ce) of the row in `st`, as mass_chunk computes them:
+// chunks are weighed one after another into four LDS stagings, and every four chunks the
+// four waves sum one chunk each, so the barriers and the sums are paid once per four
+// chunks instead of once per chunk.  Block-wide.
+template <typename T, int kQ, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_slice4_q(const KArgs& a, const DrawState& st,
+                                                             const WParams& W, const T* rowp,
+                                                             const void* qrow, int b, int cb,
+                                                             int ce, MassSmem4& sm,
+                                                             const int32_t* ex) {
+    typedef typename Quad<T>::Raw LR;
+    typedef typename QRow<T, kQ>::Raw QR;
+    const int tid = threadIdx.x;
+    const size_t qes = kFilt ? sizeof(T) : sizeof(float);
+    LR la[4];
+    QR qa[4];
+    auto load = [&](int c, LR* lr, QR* qr) {
+        const Quad<T>* lq = reinterpret_cast<const Quad<T>*>(rowp + c * kFine);
+        const QR* qq = kQ != 0 ? reinterpret_cast<const QR*>(static_cast<const char*>(qrow) +
+                                                             (size_t)c * kFine * qes)
+                               : nullptr;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            lr[u] = lq[u * kBlock + tid].raw;
+            if (kQ != 0) qr[u] = ld_stream_any(qq + u * kBlock + tid);
+        }
+    };
+    auto stage = [&](int c, bool fast, const LR* lr, const QR* qr, MassSmem& ms) {
+        if (fast) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float p4, w4;
+                weigh4<T, kQ, kFilt>(lr[u], qr[u], W, p4, w4);
+                ms.pw[stage_slot(u * kBlock + tid)] = p4;
+                ms.ww[stage_slot(u * kBlock + tid)] = w4;
+            }
+        } else {
+            const int c0 = c * kFine;
+            chunk_weights<T, kQ, kFilt>(rowp + c0,
+                                        kQ != 0 ? static_cast<const char*>(qrow) + c0 * qes : nullptr,
+                                        min(kFine, a.V - c0), false, W, ms.pw, ms.ww);
+        }
+    };
+    for (int c0 = cb; c0 < ce; c0 += kWaves) {
+#pragma unroll
+        for (int j = 0; j < kWaves; ++j) {
+            const int c = c0 + j;
+            if (c < ce) {
+                const bool f = chunk_fast<T, kFilt>(rowp, qrow, c, a.V);
+                if (f) load(c, la, qa);
+                __builtin_amdgcn_sched_barrier(0);
+                stage(c, f, la, qa, sm.s[j]);
+            }
+        }
+        mass_reduce_quad<T, kFilt>(a, st, W, rowp, b, c0, min(ce, c0 + kWaves), sm, ex);
+    }
+}
+
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void mass_slice4(const KArgs& a, const DrawState& st,
+                                                           const WParams& W, const T* rowp,
+                                                           const void* qrow, int b, int cb, int ce,
+                                                           MassSmem4& sm, const int32_t* ex) {
+    if (qrow)
+        mass_slice4_q<T, kFilt ? 2 : 1, kFilt>(a, st, W, rowp, qrow, b, cb, ce, sm, ex);
+    else
+        mass_slice4_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex);
+}
+
 // One workgroup per (request, fine chunk).
 template <typename T, bool kFilt>
 __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
@@ -1630,7 +1756,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
                                                        unsigned long long* xslots, int xstride) {
     __shared__ RowSmem rs;
     __shared__ XSmem xs;
-    __shared__ MassSmem ms;
+    __shared__ MassSmem4 ms;
     __shared__ float sp[kMaxRows];
     __shared__ int sflag;
     const int tid = threadIdx.x;
@@ -1742,7 +1868,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         const T* rowp = logits + (size_t)st.row * V;
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
-        mass_slice<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
+        mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
                              nullptr);
     }
     walk_end(hdr, epoch, w, W);
