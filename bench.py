@@ -39,7 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD published peak
-CHAIN_KERNELS = ["k_chain_walk", "k_draw"]
+CHAIN_KERNELS = ["k_chain_walk"]  # the final draw runs inside the walk (k_draw only past 64 chunks a slice)
 GREEDY_KERNELS = ["k_greedy_walk"]
 EAGER_CHAIN_KERNELS = ["k_rows<sampling>", "k_chain_accept", "k_mass", "k_draw"]
 EAGER_GREEDY_KERNELS = ["k_rows<greedy>", "k_greedy_merge"]

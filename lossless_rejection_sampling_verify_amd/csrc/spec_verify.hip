@@ -133,6 +133,7 @@ struct KArgs {
     int fixbits;         // fixed-point fraction bits of the filter's mass histograms
     int walk_temporal;   // chain walk: row passes with cache-allocating loads (sweeps: 0)
     int coin_stride;     // coins per request in `coins`; the final draw's coin is the last
+    int walk_draw;       // chain walk: the final draw happens in the walk (no k_draw)
     unsigned* hdr;       // workspace header: the walks' call counter and finished count
 };
 
@@ -1744,6 +1745,126 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
                          st.nexcl > 0 ? a.excl + (size_t)b * SPEC_MAX_N : nullptr);
 }
 
+// Result of a wave-wide search over 64 weights (one per lane).
+struct Found {
+    int hit;          // first lane with x > 0 whose inclusive prefix reaches t, or -1
+    double before;    // weight ahead of `hit`
+    int last;         // last lane with x > 0, or -1
+    double last_before;
+    double total;     // sum of the 64 weights
+};
+
+// Among the 64 lanes' values x, counting `carry` ahead of lane 0: the first lane with
+// x > 0 whose inclusive prefix reaches t, and the last positive lane (for when rounding
+// leaves t beyond the total).  Every lane gets the same result.
+__device__ __attribute__((always_inline)) Found wave_find(double x, double t, double carry) {
+    const int lane = threadIdx.x & 63;
+    double incl = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const double excl = incl - x;
+    const unsigned long long hit = __ballot(x > 0.0 && t <= carry + incl);
+    const unsigned long long pos = __ballot(x > 0.0);
+    Found f;
+    f.hit = hit ? __ffsll((long long)hit) - 1 : -1;
+    f.last = pos ? 63 - __clzll((long long)pos) : -1;
+    const double eh = __shfl(excl, f.hit < 0 ? 0 : f.hit);
+    const double el = __shfl(excl, f.last < 0 ? 0 : f.last);
+    f.before = carry + eh;
+    f.last_before = carry + el;
+    f.total = __shfl(incl, 63);
+    return f;
+}
+
+// First entry i of w[0..n) with w[i] > 0 whose inclusive prefix reaches t; if rounding
+// leaves t beyond the total, the last positive entry; -1 if none is positive.  One full
+// wave; every lane returns the entry and the weight before it.
+__device__ __attribute__((always_inline)) int wave_locate(const double* w, int n, double t,
+                                                        double& before) {
+    const int lane = threadIdx.x & 63;
+    double carry = 0.0, last_before = 0.0;
+    int last = -1;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const Found f = wave_find(i0 + lane < n ? w[i0 + lane] : 0.0, t, carry);
+        if (f.hit >= 0) {
+            before = f.before;
+            return i0 + f.hit;
+        }
+        if (f.last >= 0) {
+            last = i0 + f.last;
+            last_before = f.last_before;
+        }
+        carry += f.total;
+    }
+    before = last_before;
+    return last;
+}
+
+// The token inside fine chunk c of the row in `st` whose cumulative weight reaches tc
+// (measured from the start of the chunk): its segment from the segment weights (stored by
+// the chunk's weighing, or, in the fallback, the plain target row summed here), then the
+// element.  One full wave (lanes 0..63); y = -1 if nothing is positive.
+template <typename T, bool kFilt>
+__device__ __attribute__((always_inline)) void draw_in_chunk(const KArgs& a, const DrawState& st,
+                                                             const WParams& W, const T* rowp,
+                                                             const void* qrow, int b, int c,
+                                                             double tc, bool fallback, int& y,
+                                                             float& ly) {
+    const int lane = threadIdx.x & 63;
+    const int S2 = a.S2, V = a.V;
+    const bool resid = qrow != nullptr && !fallback;
+    // segment weights: stored by k_mass, or (fallback) the plain target row, summed here
+    double x;
+    if (!fallback) {
+        x = a.seg[((size_t)b * S2 + c) * kSegs + lane];
+    } else {
+        x = 0.0;
+        for (int g0 = 0; g0 < kSegs; g0 += 8) {  // eight segments' loads in flight
+            float pv[8];
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const int j = c * kFine + (g0 + g) * kSeg + lane;
+                float p = 0.f;
+                if (j < V) draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
+                pv[g] = p;
+            }
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const double sg = wave_sum((double)pv[g]);
+                if (lane == g0 + g) x = sg;
+            }
+        }
+    }
+    const Found fs = wave_find(x, tc, 0.0);
+    const int g = fs.hit >= 0 ? fs.hit : fs.last;
+    const double bs = fs.hit >= 0 ? fs.before : fs.last_before;
+    if (g >= 0) {
+        const double tg = tc - bs;
+        const int j = c * kFine + g * kSeg + lane;  // kSeg == 64: one element per lane
+        float l = 0.f, w = 0.f;
+        if (j < V) {
+            l = Ld<T>::one(rowp + j);
+            float p;
+            constexpr int kQr = kFilt ? 2 : 1;
+            w = resid ? draw_weight<T, kQr, kFilt>(rowp, qrow, j, W, p)
+                      : draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
+            if (!fallback && st.nexcl > 0) {
+                const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
+                for (int e = 0; e < st.nexcl; ++e)
+                    if (ex[e] == j) w = 0.f;
+            }
+        }
+        const Found fe = wave_find((double)w, tg, 0.0);
+        const int f = fe.hit >= 0 ? fe.hit : fe.last;
+        if (f >= 0) {
+            y = c * kFine + g * kSeg + f;
+            ly = __shfl(l, f);
+        }
+    }
+}
+
 // k_chain_walk: chain rejection sampling position by position, one cluster of W
 // workgroups per request (blockIdx = b * W + w, workgroup w owning a slice of whole fine
 // chunks of every row).  At each position the slices' (max, normaliser) travel through
@@ -1868,8 +1989,84 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         const T* rowp = logits + (size_t)st.row * V;
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
-        mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
-                             nullptr);
+        const int cb = lo / kFine, ce = (hi + kFine - 1) / kFine;
+        mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, cb, ce, ms, nullptr);
+        if (a.walk_draw) {
+            // The draw, within the cluster (the host sets walk_draw when every slice has at
+            // most 64 chunks).  Each member's slice total, as wave 0's scan adds its chunk
+            // masses, goes through one more hand-off; the member whose slice holds
+            // u * total then locates the chunk, segment and token as k_draw does.  A total
+            // that is not positive repeats this with the plain target weights.
+            const int nc = ce - cb;
+            const size_t mrow = (size_t)b * a.S2 + cb;
+            double tw = 0.0, pw = 0.0, mw = 0.0, mf = 0.0;  // wave 0: lane i holds chunk cb + i
+            if (tid < 64) {
+                mw = tid < nc ? a.mass[mrow + tid] : 0.0;
+                mf = tid < nc ? a.massfb[mrow + tid] : 0.0;
+                tw = wave_find(mw, 0.0, 0.0).total;
+                pw = wave_find(mf, 0.0, 0.0).total;
+            }
+            bool fallback = false;
+            double tot = 0.0;
+            if (!cluster_step(slots, R, W, w, tag, dbl_hi(tw), dbl_lo(tw), 0u, xs)) {
+                bad = true;
+            } else {
+                for (int j = 0; j < W; ++j) tot += dbl_of(xs.xp[j][0], xs.xp[j][1]);
+                fallback = !(tot > 0.0);
+                if (fallback) {
+                    if (!cluster_step(slots, R + 1, W, w, tag, dbl_hi(pw), dbl_lo(pw), 0u, xs)) {
+                        bad = true;
+                    } else {
+                        tot = 0.0;
+                        for (int j = 0; j < W; ++j) tot += dbl_of(xs.xp[j][0], xs.xp[j][1]);
+                    }
+                }
+            }
+            if (!bad) {
+                // the owner: the first member with a positive total whose inclusive prefix
+                // reaches t, else (rounding) the last positive one
+                const double t = (double)uG * tot;
+                int owner = -1, last = -1;
+                double carry = 0.0, before = 0.0, last_before = 0.0;
+                for (int j = 0; j < W; ++j) {
+                    const double tj = dbl_of(xs.xp[j][0], xs.xp[j][1]);
+                    if (tj > 0.0) {
+                        if (owner < 0 && t <= carry + tj) {
+                            owner = j;
+                            before = carry;
+                        }
+                        last = j;
+                        last_before = carry;
+                    }
+                    carry += tj;
+                }
+                if (owner < 0) {
+                    owner = last;
+                    before = last_before;
+                }
+                if (w == owner && tid < 64) {
+                    const double t1 = t - before;
+                    const Found f = wave_find(fallback ? mf : mw, t1, 0.0);
+                    const int cl = f.hit >= 0 ? f.hit : f.last;
+                    const double bc = f.hit >= 0 ? f.before : f.last_before;
+                    int y = -1;
+                    float ly = 0.f;
+                    if (cl >= 0)
+                        draw_in_chunk<T, false>(a, st, Wp, rowp, qrow, b, cb + cl, t1 - bc,
+                                                fallback, y, ly);
+                    if (tid == 0) {
+                        a.out_tokens[st.out] = y;
+                        if (a.probs)
+                            a.probs[st.out] =
+                                y >= 0 ? (float)(exp(((double)ly - (double)st.M) / st.T) / st.Z) : 0.f;
+                    }
+                }
+                if (owner < 0 && w == 0 && tid == 0) {  // no positive weight anywhere
+                    a.out_tokens[st.out] = -1;
+                    if (a.probs) a.probs[st.out] = 0.f;
+                }
+            }
+        }
     }
     walk_end(hdr, epoch, w, W);
     if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
@@ -2439,63 +2636,6 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     }
 }
 
-// Result of a wave-wide search over 64 weights (one per lane).
-struct Found {
-    int hit;          // first lane with x > 0 whose inclusive prefix reaches t, or -1
-    double before;    // weight ahead of `hit`
-    int last;         // last lane with x > 0, or -1
-    double last_before;
-    double total;     // sum of the 64 weights
-};
-
-// Among the 64 lanes' values x, counting `carry` ahead of lane 0: the first lane with
-// x > 0 whose inclusive prefix reaches t, and the last positive lane (for when rounding
-// leaves t beyond the total).  Every lane gets the same result.
-__device__ __attribute__((always_inline)) Found wave_find(double x, double t, double carry) {
-    const int lane = threadIdx.x & 63;
-    double incl = x;
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    const double excl = incl - x;
-    const unsigned long long hit = __ballot(x > 0.0 && t <= carry + incl);
-    const unsigned long long pos = __ballot(x > 0.0);
-    Found f;
-    f.hit = hit ? __ffsll((long long)hit) - 1 : -1;
-    f.last = pos ? 63 - __clzll((long long)pos) : -1;
-    const double eh = __shfl(excl, f.hit < 0 ? 0 : f.hit);
-    const double el = __shfl(excl, f.last < 0 ? 0 : f.last);
-    f.before = carry + eh;
-    f.last_before = carry + el;
-    f.total = __shfl(incl, 63);
-    return f;
-}
-
-// First entry i of w[0..n) with w[i] > 0 whose inclusive prefix reaches t; if rounding
-// leaves t beyond the total, the last positive entry; -1 if none is positive.  One full
-// wave; every lane returns the entry and the weight before it.
-__device__ __attribute__((always_inline)) int wave_locate(const double* w, int n, double t,
-                                                        double& before) {
-    const int lane = threadIdx.x & 63;
-    double carry = 0.0, last_before = 0.0;
-    int last = -1;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-        const Found f = wave_find(i0 + lane < n ? w[i0 + lane] : 0.0, t, carry);
-        if (f.hit >= 0) {
-            before = f.before;
-            return i0 + f.hit;
-        }
-        if (f.last >= 0) {
-            last = i0 + f.last;
-            last_before = f.last_before;
-        }
-        carry += f.total;
-    }
-    before = last_before;
-    return last;
-}
-
 // One wave per request: chunk, then segment, then token.
 template <typename T, bool kFilt>
 __global__ __launch_bounds__(64) void k_draw(KArgs a) {
@@ -2522,7 +2662,6 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
         for (int i0 = 0; i0 < S2; i0 += 64)
             tot += wave_sum(i0 + lane < S2 ? a.massfb[(size_t)b * S2 + i0 + lane] : 0.0);
     }
-    const bool resid = qrow != nullptr && !fallback;
     int y = -1;
     float ly = 0.f;
     const double t = u * tot;
@@ -2535,57 +2674,7 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
     } else {
         c = wave_locate((fallback ? a.massfb : a.mass) + (size_t)b * S2, S2, t, before);
     }
-    if (c >= 0) {
-        const double tc = t - before;
-        // segment weights: stored by k_mass, or (fallback) the plain target row, summed here
-        double x;
-        if (!fallback) {
-            x = a.seg[((size_t)b * S2 + c) * kSegs + lane];
-        } else {
-            x = 0.0;
-            for (int g0 = 0; g0 < kSegs; g0 += 8) {  // eight segments' loads in flight
-                float pv[8];
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    const int j = c * kFine + (g0 + g) * kSeg + lane;
-                    float p = 0.f;
-                    if (j < V) draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
-                    pv[g] = p;
-                }
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    const double sg = wave_sum((double)pv[g]);
-                    if (lane == g0 + g) x = sg;
-                }
-            }
-        }
-        const Found fs = wave_find(x, tc, 0.0);
-        const int g = fs.hit >= 0 ? fs.hit : fs.last;
-        const double bs = fs.hit >= 0 ? fs.before : fs.last_before;
-        if (g >= 0) {
-            const double tg = tc - bs;
-            const int j = c * kFine + g * kSeg + lane;  // kSeg == 64: one element per lane
-            float l = 0.f, w = 0.f;
-            if (j < V) {
-                l = Ld<T>::one(rowp + j);
-                float p;
-                constexpr int kQr = kFilt ? 2 : 1;
-                w = resid ? draw_weight<T, kQr, kFilt>(rowp, qrow, j, W, p)
-                          : draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
-                if (!fallback && st.nexcl > 0) {
-                    const int32_t* ex = a.excl + (size_t)b * SPEC_MAX_N;
-                    for (int e = 0; e < st.nexcl; ++e)
-                        if (ex[e] == j) w = 0.f;
-                }
-            }
-            const Found fe = wave_find((double)w, tg, 0.0);
-            const int f = fe.hit >= 0 ? fe.hit : fe.last;
-            if (f >= 0) {
-                y = c * kFine + g * kSeg + f;
-                ly = __shfl(l, f);
-            }
-        }
-    }
+    if (c >= 0) draw_in_chunk<T, kFilt>(a, st, W, rowp, qrow, b, c, t - before, fallback, y, ly);
     if (lane == 0) {
         a.out_tokens[st.out] = y;
         if (a.probs)
@@ -3264,8 +3353,10 @@ Layout layout_for(int op, int B, int R, int V) {
     L.frows = off;
     if (op == SPEC_OP_CHAIN_FILTERED) off = align256(off + sizeof(FiltRow) * (size_t)B * (2 * R - 1));
     L.xch = off;
-    if (op == SPEC_OP_GREEDY || op == SPEC_OP_CHAIN)
+    if (op == SPEC_OP_GREEDY)
         off = align256(off + sizeof(unsigned long long) * (size_t)B * R * kMaxCluster * 3);
+    else if (op == SPEC_OP_CHAIN)  // a step per position, then the draw's slice totals (2)
+        off = align256(off + sizeof(unsigned long long) * (size_t)B * (R + 2) * kMaxCluster * 3);
     else if (op == SPEC_OP_TREE)  // at most one step per node
         off = align256(off + sizeof(unsigned long long) * (size_t)B * R * tree_cluster_max(B) * 3);
     else if (op == SPEC_OP_TREE_MSS)
@@ -3389,11 +3480,13 @@ int run_chain_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_chain_walk<T>),
                                   sizeof(T) == 4 ? 2 : 3), &W, &per);
+    a.walk_draw = per <= 64 ? 1 : 0;  // a slice's chunk masses fit one wave: draw in the walk
+    // hand-off steps: one per position, then the slice totals (and their fallback)
     hipLaunchKernelGGL((k_chain_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
                        per * kFine, a.hdr, W > 1 ? xslots : (unsigned long long*)nullptr,
-                       a.R * W * 3);
+                       (a.R + 2) * W * 3);
     int rc = launch_status();
-    if (rc != SPEC_OK) return rc;
+    if (rc != SPEC_OK || a.walk_draw) return rc;
     hipLaunchKernelGGL((k_draw<T, false>), dim3(a.B), dim3(64), 0, st, a);
     return launch_status();
 }

@@ -418,3 +418,42 @@ def test_tree_rows_off_the_walk():
         compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"],
                 o["margin"] if sampling else None, label=f"rows off the walk {mode}")
         np.testing.assert_array_equal(g["accept_len"], o["accept_len"])
+
+
+@pytest.mark.parametrize("dtype,eager", [(wl.F32, False), (wl.F32, True), (wl.BF16, False)])
+def test_chain_residual_without_mass_falls_back(dtype, eager, monkeypatch):
+    """q = 2p, used as given: every draft is accepted with probability 1/2 and, after a
+    rejection, max(0, p - q) has no mass, so the correction is drawn from the target row
+    itself (the bonus rule).  The oracle reports the empty residual as a zero margin, so
+    the check is direct: accept_len and every emitted token equal the oracle's wherever no
+    acceptance coin lies within 1e-6 of 1/2 and the final coin's target lies more than 1e-6
+    from every step of the drawn row's cumulative distribution; in the walk and in the
+    eager passes."""
+    import dataclasses
+    if eager:
+        monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+    c = wl.make_chain(2, seed=41, B=32, G=4, V=9000, dtype=dtype)
+    lg = wl.logits_as_f32(c.logits, c.dtype).astype(np.float64)
+    z = lg / c.temperature.astype(np.float64)[:, None, None]
+    p = np.exp(z - z.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    c2 = dataclasses.replace(c, draft_probs=(2.0 * p[:, :c.G]).astype(np.float32))
+    say(f"chain q = 2p {dtype} eager={eager}")
+    g = gpu_chain(c2.logits, c2.dtype, c2.draft_probs, c2.draft_tokens, c2.coins, c2.temperature)
+    o = oracle.verify_chain(c2.logits, c2.dtype, c2.draft_probs, c2.draft_tokens, c2.coins,
+                            c2.temperature)
+    checked = 0
+    for b in range(c.B):
+        k = int(o["accept_len"][b])
+        if np.any(np.abs(c2.coins[b, :min(k + 1, c.G)].astype(np.float64) - 0.5) <= 1e-6):
+            continue
+        cdf = np.cumsum(p[b, k])
+        target = float(c2.coins[b, c.G]) * cdf[-1]
+        if np.abs(cdf - target).min() <= 1e-6:
+            continue
+        assert g["accept_len"][b] == k, b
+        np.testing.assert_array_equal(g["out_tokens"][b], o["out_tokens"][b])
+        assert o["out_tokens"][b, k] == int(np.searchsorted(cdf, target)), b  # the plain-row draw
+        checked += 1
+    assert (o["accept_len"] < c.G).sum() >= c.B // 2   # most requests draw a correction
+    assert checked >= c.B - 2, checked
