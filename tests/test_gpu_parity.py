@@ -377,6 +377,17 @@ def test_walk_cluster_widths(cluster, monkeypatch):
     check_greedy(c, f"walk W<={cluster}")
 
 
+@pytest.mark.parametrize("cluster,dtype", [("1", wl.F32), ("2", wl.BF16), ("5", wl.F32)])
+def test_chain_walk_wide_slices_take_the_draw_kernel(cluster, dtype, monkeypatch):
+    """V = 300001 (74 fine chunks, a ragged last one): with one workgroup per request the
+    slice holds more chunks than one wave scans, so the chain walk leaves the final draw to
+    k_draw; with two it just fits the in-walk draw (37 chunks), and with five the slices
+    are short.  All must match the oracle."""
+    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    c = wl.make_chain(2, seed=43, B=6, G=2, V=300001, dtype=dtype)
+    check_chain(c, f"wide slices W<={cluster} {dtype}")
+
+
 @pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
 def test_tree_eager_passes_match_oracle(mode, monkeypatch):
     """The eager tree passes (every row streamed, then walked), selected by
