@@ -1887,6 +1887,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     unsigned long long* slots = xslots ? xslots + (size_t)b * xstride : nullptr;
     if (!slots) hdr = nullptr;  // no hand-off words, no tag
     const uint32_t epoch = walk_epoch(hdr), tag = walk_tag(epoch);
+    // The walking waves issue ahead of the final-weight waves of requests that have
+    // stopped (the priority drops again before the weights): the walks of the longest
+    // requests are the call's critical path, the weights of the others are not.
+    __builtin_amdgcn_s_setprio(3);
     const T* logits = reinterpret_cast<const T*>(a.logits);
     // Every per-request input is read up front and waited for only where it is used, so
     // the reads overlap the first row pass: the temperature and the final coin (checked
@@ -1990,6 +1994,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         const void* qrow;
         const WParams Wp = draw_params<T, false>(a, st, qrow);
         const int cb = lo / kFine, ce = (hi + kFine - 1) / kFine;
+        __builtin_amdgcn_s_setprio(0);
         mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, cb, ce, ms, nullptr);
         if (a.walk_draw) {
             // The draw, within the cluster (the host sets walk_draw when every slice has at
