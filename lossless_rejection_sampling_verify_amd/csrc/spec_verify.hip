@@ -272,10 +272,16 @@ __device__ inline int block_min(int v, RowSmem& sm) {
 // kPipe: the loads of batch j + 1 are issued before batch j is reduced (kU more registers
 // per lane), so the reduction's arithmetic overlaps the memory latency; that matters when a
 // workgroup has its SIMDs to itself, as in the walks' later positions.
+//
+// bkey (optional, unpipelined passes): batch j of this lane (its vectors v = tid +
+// kBlock * (kU * j + u)) leaves the top 16 bits of its maximum's order key in
+// bkey[j * kBlock + tid], for the first kMaxBatchRec batches.
+constexpr int kMaxBatchRec = 24;
 template <typename T, bool kSampling, bool kNT = true, int kU = kUnroll, bool kPipe = false>
 __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
                                                             float s2, RowSmem& sm,
-                                                            float* lane_max = nullptr) {
+                                                            float* lane_max = nullptr,
+                                                            uint16_t* bkey = nullptr) {
     constexpr int kVec = Ld<T>::kVec;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = c1 > c0 ? c1 - c0 : 0;
@@ -308,7 +314,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
     };
     // One batch of nvec 16-byte vectors, unpacked on the fly (once for the batch max, once
     // for the exp-sum) so that only the raw vectors stay live while the loads are in flight.
-    auto batch = [&](u32x4* raw, int nvec, int vfirst) {
+    auto batch = [&](u32x4* raw, int nvec, int vfirst) -> float {
         float bm;
         {
             float f[kVec];
@@ -362,6 +368,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             }
             im = ebase + first;
         }
+        return bm;
     };
 
     auto load = [&](u32x4* raw, int v0) {
@@ -398,7 +405,15 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             // alone, the scheduler interleaves the unpacking with the loads and waits
             // after two)
             __builtin_amdgcn_sched_barrier(0);
-            batch(raw, kU, v);
+            const float bm = batch(raw, kU, v);
+            if (bkey) {
+                const int j = (v - tid) / (kU * kBlock);
+                // +0.0f: a -0.0 maximum stands for +0.0 too (fmaxf may return either)
+                const uint32_t u = __float_as_uint(bm + 0.0f);
+                if (j < kMaxBatchRec)
+                    bkey[j * kBlock + tid] =
+                        (uint16_t)(((u & 0x80000000u) ? ~u : (u | 0x80000000u)) >> 16);
+            }
         }
     }
     for (; v < nv; v += kBlock) {
@@ -1171,10 +1186,11 @@ __device__ inline DrawState load_state(const DrawState* p) {
 // Fallback when the total weight is not positive: w_j = p_j (the plain target row).
 // Segment and chunk sums are fp64 sums of fp32 sums of four weights.
 
-// Order-preserving integer key of a float: a < b iff key(a) < key(b) (NaN aside).  A bf16
-// value widened to fp32 has the same order through its top 16 key bits.
+// Order-preserving integer key of a float: a < b iff key(a) < key(b), and a == b iff
+// key(a) == key(b) (NaN aside; -0.0 and +0.0 share the key of +0.0, as they compare
+// equal).  A bf16 value widened to fp32 has the same order through its top 16 key bits.
 __device__ inline uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
+    const uint32_t u = __float_as_uint(f + 0.0f);  // -0.0 + 0.0 is +0.0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -2712,6 +2728,7 @@ struct FilterSmem {
         uint32_t cand[kCandCap];  // direct selection: candidate keys
     };
     uint32_t lanekey[kBlock];
+    uint16_t bkey[kMaxBatchRec * kBlock];  // batch maxima of the first pass (key top bits)
     int ncand;
     unsigned long long wtot[3][kWaves];
     int pick_thread;
@@ -2940,9 +2957,13 @@ __device__ inline float key_value(uint32_t key) {
 // the fixed-point masses over the sorted keys give the top-p threshold.  Thresholds and
 // kept mass are the ones the radix selection finds.  Returns false (nothing decided)
 // when the candidates do not fit.
+//
+// With `rec` the first pass left every batch's maximum in sm.bkey (a row without NaN whose
+// full batches fit the record): only batches whose maximum reaches the bound are read
+// again, so the row is read about once instead of twice.
 template <typename T>
 __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fscale, int k,
-                              bool fp, double tp, float lane_max, uint32_t* th_out,
+                              bool fp, double tp, float lane_max, bool rec, uint32_t* th_out,
                               unsigned long long* kept_out, FilterSmem& sm) {
     const int tid = threadIdx.x;
     constexpr int kVec = Ld<T>::kVec;
@@ -2964,7 +2985,9 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
     if (tid < head) visit(Ld<T>::one(rowp + tid));
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + head);
     int v = tid;
-    for (; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock) {
+    const uint32_t lb16 = lb >> 16;  // key >= lb implies key >> 16 >= lb16
+    for (int j = 0; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock, ++j) {
+        if (rec && sm.bkey[j * kBlock + tid] < lb16) continue;  // nothing here reaches lb
         u32x4 r[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) r[u] = ld_stream(vp + v + u * kBlock);
@@ -3044,7 +3067,12 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     const float Tf = a.temperature[b];
     const float s2 = kLog2e / Tf;
     float lane_max;
-    const Part st = chunk_record<T, true>(rowp, 0, V, s2, sm.rs, &lane_max);
+    // the batch record covers every full batch of a lane when the row has at most
+    // kMaxBatchRec of them (the vector count bounds it: the head shifts it by less than one)
+    const long nvec = (long)V * sizeof(T) / 16;
+    const bool fits = nvec / (kUnroll * kBlock) + 1 <= kMaxBatchRec;
+    const Part st = chunk_record<T, true>(rowp, 0, V, s2, sm.rs, &lane_max,
+                                          fits ? sm.bkey : nullptr);
     FiltRow fr;
     fr.M = st.m;
     fr.th = 0u;
@@ -3060,7 +3088,7 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
         uint32_t lo = 0u;
         const bool direct = fk && k <= kBlock &&
                             direct_select<T>(rowp, V, st.m, s2, fscale, k, fp, (double)tp,
-                                             lane_max, &lo, &kept, sm);
+                                             lane_max, fits && isfinite(st.z), &lo, &kept, sm);
         if (!direct) {
             if (fk) lo = radix_select<T>(rowp, V, st.m, s2, fscale, 0u, false, 0.0,
                                          (unsigned long long)k, &kept, sm);

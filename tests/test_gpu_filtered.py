@@ -134,10 +134,10 @@ def test_candidate_overflow_and_plateaus(dtype):
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
 def test_top_keys_crowded_in_one_lane(dtype):
-    """The first pass keeps each lane's four largest keys; when one lane holds more of the
-    row's top-k than that (here its first two 16-byte vectors carry the eight largest
-    logits of every row), the selection must fall back to a second pass over the row and
-    still match the oracle."""
+    """The row's eight largest logits sit in lane 0's first two 16-byte vectors (its first
+    batch of the first pass): the lanes' maxima then bound the top-k loosely, and the
+    second pass must still read that batch back (its recorded maximum reaches the bound)
+    and match the oracle."""
     import dataclasses
     c = wl.make_chain_logits(2, seed=31, B=8, G=3, V=40000, dtype=dtype, top_k=50, top_p=0.9)
     kvec = 8 if dtype == wl.BF16 else 4
@@ -150,3 +150,41 @@ def test_top_keys_crowded_in_one_lane(dtype):
         arr[..., ids] = top + np.arange(1, 9, dtype=np.float32)
     c2 = dataclasses.replace(c, logits=enc(tl), draft_logits=enc(dl))
     check(c2, f"top keys crowded in lane 0, {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_signed_zero_at_the_top_k_boundary(dtype):
+    """Rows whose top-k boundary is 0.0 with both signs of zero among the tied tokens:
+    -0.0 and +0.0 compare equal, so every zero is kept (ties at the k-th logit), as in the
+    oracle.  Target and draft share the plateau and the drafts sit on -0.0 tokens, so the
+    kept set decides every acceptance."""
+    import dataclasses
+    c = wl.make_chain_logits(2, seed=41, B=8, G=3, V=4099, dtype=dtype, top_k=20, top_p=1.0)
+    rng = np.random.default_rng(9)
+    enc = (lambda f: wl.f32_to_bf16_bits(f)) if dtype == wl.BF16 else (lambda f: f)
+    t = wl.logits_as_f32(c.logits, dtype)
+    d = wl.logits_as_f32(c.draft_logits, dtype)
+    t = (t - t.max(axis=-1, keepdims=True) - 1.0).astype(np.float32)  # every logit below 0
+    d = (d - d.max(axis=-1, keepdims=True) - 1.0).astype(np.float32)
+    x2 = c.draft_tokens.copy()
+    for b in range(c.B):
+        for i in range(c.R):
+            ids = rng.choice(c.V, size=30, replace=False)
+            t[b, i, ids[:18]] = 0.0
+            t[b, i, ids[18:]] = -0.0
+            if i < c.G:
+                d[b, i, ids[:18]] = 0.0
+                d[b, i, ids[18:]] = -0.0
+                x2[b, i] = ids[20 + (b + i) % 10]                # a draft on a -0.0 token
+    assert (np.signbit(t) & (t == 0)).sum() == c.B * c.R * 12
+    c2 = dataclasses.replace(c, logits=enc(t), draft_logits=enc(d), draft_tokens=x2)
+    g, o = check(c2, f"signed zeros at the top-k boundary, {dtype}")
+    assert (o["accept_len"] >= 1).all()
+
+
+@pytest.mark.parametrize("V", [152064, 131072 + 7])
+def test_fp32_rows_beyond_the_batch_record(V):
+    """fp32 rows of this length have more first-pass batches per lane than the record
+    holds, so the second pass reads the whole row again."""
+    c = wl.make_chain_logits(5, seed=V % 97, B=3, G=2, V=V, dtype=wl.F32, top_k=50, top_p=0.9)
+    check(c, f"fp32 V={V} k=50 p=0.9")
