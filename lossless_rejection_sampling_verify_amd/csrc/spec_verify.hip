@@ -1680,12 +1680,16 @@ __device__ __attribute__((always_inline)) void mass_reduce_quad(const KArgs& a,
 // chunks are weighed one after another into four LDS stagings, and every four chunks the
 // four waves sum one chunk each, so the barriers and the sums are paid once per four
 // chunks instead of once per chunk.  Block-wide.
+//
+// stop_at >= 0: stop after the first group of four chunks with which the chunk masses,
+// added in chunk order, reach stop_at; returns the end of the chunks weighed.
 template <typename T, int kQ, bool kFilt>
-__device__ __attribute__((always_inline)) void mass_slice4_q(const KArgs& a, const DrawState& st,
-                                                             const WParams& W, const T* rowp,
-                                                             const void* qrow, int b, int cb,
-                                                             int ce, MassSmem4& sm,
-                                                             const int32_t* ex) {
+__device__ __attribute__((always_inline)) int mass_slice4_q(const KArgs& a, const DrawState& st,
+                                                            const WParams& W, const T* rowp,
+                                                            const void* qrow, int b, int cb,
+                                                            int ce, MassSmem4& sm,
+                                                            const int32_t* ex,
+                                                            double stop_at = -1.0) {
     typedef typename Quad<T>::Raw LR;
     typedef typename QRow<T, kQ>::Raw QR;
     const int tid = threadIdx.x;
@@ -1730,19 +1734,27 @@ __device__ __attribute__((always_inline)) void mass_slice4_q(const KArgs& a, con
                 stage(c, f, la, qa, sm.s[j]);
             }
         }
-        mass_reduce_quad<T, kFilt>(a, st, W, rowp, b, c0, min(ce, c0 + kWaves), sm, ex);
+        const int c1 = min(ce, c0 + kWaves);
+        mass_reduce_quad<T, kFilt>(a, st, W, rowp, b, c0, c1, sm, ex);
+        if (stop_at >= 0.0) {  // the masses were written before the reduction's last barrier
+            double cum = 0.0;
+            for (int c = cb; c < c1; ++c) cum += a.mass[(size_t)b * a.S2 + c];
+            if (cum >= stop_at) return c1;
+        }
     }
+    return ce;
 }
 
 template <typename T, bool kFilt>
-__device__ __attribute__((always_inline)) void mass_slice4(const KArgs& a, const DrawState& st,
-                                                           const WParams& W, const T* rowp,
-                                                           const void* qrow, int b, int cb, int ce,
-                                                           MassSmem4& sm, const int32_t* ex) {
+__device__ __attribute__((always_inline)) int mass_slice4(const KArgs& a, const DrawState& st,
+                                                          const WParams& W, const T* rowp,
+                                                          const void* qrow, int b, int cb, int ce,
+                                                          MassSmem4& sm, const int32_t* ex,
+                                                          double stop_at = -1.0) {
     if (qrow)
-        mass_slice4_q<T, kFilt ? 2 : 1, kFilt>(a, st, W, rowp, qrow, b, cb, ce, sm, ex);
-    else
-        mass_slice4_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex);
+        return mass_slice4_q<T, kFilt ? 2 : 1, kFilt>(a, st, W, rowp, qrow, b, cb, ce, sm, ex,
+                                                      stop_at);
+    return mass_slice4_q<T, 0, kFilt>(a, st, W, rowp, nullptr, b, cb, ce, sm, ex, stop_at);
 }
 
 // One workgroup per (request, fine chunk).
@@ -2011,8 +2023,73 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         const WParams Wp = draw_params<T, false>(a, st, qrow);
         const int cb = lo / kFine, ce = (hi + kFine - 1) / kFine;
         __builtin_amdgcn_s_setprio(0);
-        mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, cb, ce, ms, nullptr);
-        if (a.walk_draw) {
+        // The bonus draws from the plain target row, whose slice totals the last hand-off
+        // already gave: slice j holds z_j exp((m_j - M) / T) / Z of the mass.  Every member
+        // finds the owner of u * total from them, and only the owner weighs its slice and
+        // draws; the others are done.
+        int bonus_owner = -2;  // -2: not taken here
+        double bonus_t1 = 0.0;
+        if (a.walk_draw && st.kind == kDrawTarget) {
+            auto slice_total = [&](int j) {
+                const float mj = __uint_as_float(xs.xp[j][0]);
+                return mj == -INFINITY ? 0.0
+                                       : dbl_of(xs.xp[j][1], xs.xp[j][2]) *
+                                             exp(((double)mj - (double)M) / Td) / Z;
+            };
+            double tot = 0.0;
+            for (int j = 0; j < W; ++j) tot += slice_total(j);
+            const double t = (double)uG * tot;
+            double carry = 0.0, before = 0.0, last_before = 0.0;
+            int owner = -1, last = -1;
+            for (int j = 0; j < W; ++j) {
+                const double tj = slice_total(j);
+                if (tj > 0.0) {
+                    if (owner < 0 && t <= carry + tj) {
+                        owner = j;
+                        before = carry;
+                    }
+                    last = j;
+                    last_before = carry;
+                }
+                carry += tj;
+            }
+            if (owner < 0) {  // rounding left u past the total: the last positive slice
+                owner = last;
+                before = last_before;
+            }
+            bonus_owner = owner;
+            bonus_t1 = t - before;
+        }
+        int cw = ce;  // end of the chunks weighed
+        if (bonus_owner == -2)
+            mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, cb, ce, ms, nullptr);
+        else if (bonus_owner == w)  // the owner weighs its chunks until they pass its target
+            cw = mass_slice4<T, false>(a, st, Wp, rowp, qrow, b, cb, ce, ms, nullptr, bonus_t1);
+        if (bonus_owner >= -1) {
+            if (w == bonus_owner && tid < 64) {
+                const int nc = cw - cb;
+                const size_t mrow = (size_t)b * a.S2 + cb;
+                const double mw = tid < nc ? a.mass[mrow + tid] : 0.0;
+                const Found f = wave_find(mw, bonus_t1, 0.0);
+                const int cl = f.hit >= 0 ? f.hit : f.last;
+                const double bc = f.hit >= 0 ? f.before : f.last_before;
+                int y = -1;
+                float ly = 0.f;
+                if (cl >= 0)
+                    draw_in_chunk<T, false>(a, st, Wp, rowp, qrow, b, cb + cl, bonus_t1 - bc,
+                                            false, y, ly);
+                if (tid == 0) {
+                    a.out_tokens[st.out] = y;
+                    if (a.probs)
+                        a.probs[st.out] =
+                            y >= 0 ? (float)(exp(((double)ly - (double)st.M) / st.T) / st.Z) : 0.f;
+                }
+            }
+            if (bonus_owner == -1 && w == 0 && tid == 0) {  // no positive weight anywhere
+                a.out_tokens[st.out] = -1;
+                if (a.probs) a.probs[st.out] = 0.f;
+            }
+        } else if (a.walk_draw) {
             // The draw, within the cluster (the host sets walk_draw when every slice has at
             // most 64 chunks).  Each member's slice total, as wave 0's scan adds its chunk
             // masses, goes through one more hand-off; the member whose slice holds

@@ -468,3 +468,31 @@ def test_chain_residual_without_mass_falls_back(dtype, eager, monkeypatch):
         checked += 1
     assert (o["accept_len"] < c.G).sum() >= c.B // 2   # most requests draw a correction
     assert checked >= c.B - 2, checked
+
+
+@pytest.mark.parametrize("cluster", [None, "1", "2", "4"])
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_chain_bonus_draws(cluster, dtype, monkeypatch):
+    """Every draft accepted (q is the target row itself), so every request draws its bonus
+    token from the last row; the walk finds the slice holding u * total from the slices'
+    (max, normaliser) pairs and only that slice's workgroup weighs and draws.  Final coins
+    at the ends of (0, 1] and in between, at several cluster widths."""
+    if cluster is not None:
+        monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    c = wl.make_chain(5, seed=77, B=40, G=3, V=70001, dtype=dtype)
+    lg = wl.logits_as_f32(c.logits, dtype).astype(np.float64)
+    z = (lg[:, :c.G] - lg[:, :c.G].max(-1, keepdims=True)) / c.temperature[:, None, None]
+    q = np.exp(z)
+    q = (q / q.sum(-1, keepdims=True)).astype(np.float32)
+    rng = np.random.default_rng(3)
+    coins = c.coins.copy()
+    coins[:, :c.G] = np.minimum(coins[:, :c.G], np.float32(0.99))
+    coins[:, c.G] = wl.draw_coins(rng, c.B)
+    coins[0, c.G] = 1.0
+    coins[1, c.G] = np.float32(2.0 ** -24)
+    coins[2, c.G] = np.float32(0.5)
+    say(f"chain bonus draws {dtype} cluster={cluster}")
+    g = gpu_chain(c.logits, dtype, q, c.draft_tokens, coins, c.temperature)
+    o = oracle.verify_chain(c.logits, dtype, q, c.draft_tokens, coins, c.temperature)
+    compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=f"bonus {dtype} W={cluster}")
+    assert (o["accept_len"] == c.G).sum() >= c.B - 2
