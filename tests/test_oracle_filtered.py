@@ -135,3 +135,22 @@ def test_knob_edges():
     bad = oracle.verify_chain_filtered(c.logits, d, c.dtype, c.draft_tokens, c.coins, c.temperature,
                                        None, np.array([0.0, -0.5, np.nan, 0.5, 1.0, 1.0], np.float32))
     assert (bad["accept_len"][:3] == -1).all() and (bad["accept_len"][3:] >= 0).all()
+
+
+def test_signed_zeros_tie_at_the_top_k_boundary():
+    """-0.0 and +0.0 are the same logit: with the k-th largest logit at zero, every zero is
+    kept whatever its sign, so the filtered row is uniform over them.  A draft on the -0.0
+    token (q uniform over the same three zeros) is then accepted at any coin, and the
+    bonus token is drawn uniformly from the three zeros (coins at thirds)."""
+    row = np.array([-1.0, 0.0, -0.0, -2.0, 0.0, -3.0], np.float32)
+    assert np.signbit(row[2])
+    lg = np.broadcast_to(row, (3, 2, 6)).copy()
+    dl = np.broadcast_to(row, (3, 1, 6)).copy()
+    x = np.array([[2], [2], [2]], np.int32)
+    coins = np.array([[0.999, 0.2], [0.999, 0.5], [0.999, 0.9]], np.float32)
+    o = oracle.verify_chain_filtered(lg, dl, wl.F32, x, coins, np.ones(3, np.float32),
+                                     top_k=np.full(3, 2, np.int32), top_p=np.ones(3, np.float32))
+    assert (o["accept_len"] == 1).all()
+    # inverse CDF over the kept zeros in ascending id: tokens 1, 2, 4 at thirds
+    assert o["out_tokens"][:, 1].tolist() == [1, 2, 4]
+    np.testing.assert_allclose(o["probs"][:, 0], 1.0 / 3.0, rtol=1e-6)
