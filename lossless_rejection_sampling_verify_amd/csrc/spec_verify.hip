@@ -1142,6 +1142,14 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
             k = i;
             break;
         }
+        // a request that walks on is more likely to be among the last to finish: its
+        // waves issue ahead of those of requests at earlier positions on the same CU
+        if (i == 0)
+            __builtin_amdgcn_s_setprio(1);
+        else if (i == 1)
+            __builtin_amdgcn_s_setprio(2);
+        else
+            __builtin_amdgcn_s_setprio(3);
         pass(i + 1);
     }
     walk_end(hdr, epoch, w, W);
