@@ -245,7 +245,7 @@ int spec_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_len
                         int32_t* slots, void* stream);
 
 /* Measurement utilities (not part of the verify path).  They calibrate the figures the
- * verify kernels are judged against on the device at hand.
+ * verify kernels are measured against on the device at hand.
  *
  * spec_calib_read: streams `bytes` bytes of device memory from `data` with 16-byte loads
  * that do not allocate in the caches, the access pattern of the row passes, and reduces
