@@ -496,3 +496,17 @@ def test_chain_bonus_draws(cluster, dtype, monkeypatch):
     o = oracle.verify_chain(c.logits, dtype, q, c.draft_tokens, coins, c.temperature)
     compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=f"bonus {dtype} W={cluster}")
     assert (o["accept_len"] == c.G).sum() >= c.B - 2
+
+
+@pytest.mark.parametrize("B,G,V,dtype,T", [
+    (1, 1, 2, wl.F32, 1.0), (3, 7, 4097, wl.BF16, 0.8), (63, 2, 9001, wl.BF16, 1.0),
+    (65, 3, 8192, wl.F32, 1.3), (200, 4, 6000, wl.BF16, 1.0), (257, 2, 5000, wl.BF16, 0.6),
+    (342, 1, 4100, wl.F32, 1.0), (513, 3, 3000, wl.BF16, 1.0), (1100, 2, 2500, wl.BF16, 1.0),
+])
+def test_walk_shapes_across_cluster_widths(B, G, V, dtype, T):
+    """Batches on both sides of the cluster-width steps (one workgroup per request up to
+    sixteen; a grid larger than the device holds at once above the last step), with
+    ragged and tiny vocabularies, both dtypes, several temperatures: greedy and chain."""
+    c = wl.make_chain(2, seed=B * 7 + G, B=B, G=G, V=V, dtype=dtype, T=T)
+    check_chain(c, f"shape B={B} G={G} V={V} {dtype} T={T}")
+    check_greedy(c, f"shape B={B} G={G} V={V} {dtype}")
