@@ -122,3 +122,40 @@ def test_tree_replays(kind):
                          accepted_nodes=nodes.cpu().numpy(), probs=probs.cpu().numpy()), o,
                     ["accept_len", "out_tokens", "accepted_nodes"], o["margin"],
                     label=f"{kind} replay {rep}/{k}")
+
+
+def test_filtered_chain_replays():
+    """The chain verify from draft logits with top-k / top-p, captured once and replayed on
+    input sets whose rows, drafts and coins differ (the knobs stay those of the capture)."""
+    api = _api()
+    sets = [wl.make_chain_logits(2, seed=s, B=12, G=3, V=20000, top_k=40, top_p=0.85)
+            for s in (71, 72, 73)]
+    c0 = sets[0]
+    lg, dl = dev_logits(c0.logits, c0.dtype), dev_logits(c0.draft_logits, c0.dtype)
+    x, u, T = dev(c0.draft_tokens), dev(c0.coins), dev(c0.temperature)
+    B, R = c0.B, c0.R
+    tk = dev(np.asarray(np.broadcast_to(c0.top_k, (B,)), np.int32).copy())
+    tp = dev(np.asarray(np.broadcast_to(c0.top_p, (B,)), np.float32).copy())
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, R, dtype=torch.int32, device="cuda")
+    probs = torch.empty(B, R, dtype=torch.float32, device="cuda")
+
+    def call():
+        api.spec_verify_chain_filtered(lg, dl, x, u, T, tk, tp, out=(acc, out, probs))
+
+    g = _capture(call)
+    for rep in range(2):
+        for k, c in enumerate(sets):
+            say(f"graph replay {rep} of filtered input set {k}")
+            lg.copy_(dev_logits(c.logits, c.dtype))
+            dl.copy_(dev_logits(c.draft_logits, c.dtype))
+            x.copy_(dev(c.draft_tokens))
+            u.copy_(dev(c.coins))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            o = oracle.verify_chain_filtered(c.logits, c.draft_logits, c.dtype, c.draft_tokens,
+                                             c.coins, c.temperature, c.top_k, c.top_p)
+            compare(dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
+                         probs=probs.cpu().numpy()), o, ["accept_len", "out_tokens"],
+                    o["margin"], label=f"filtered replay {rep}/{k}")
