@@ -510,3 +510,16 @@ def test_walk_shapes_across_cluster_widths(B, G, V, dtype, T):
     c = wl.make_chain(2, seed=B * 7 + G, B=B, G=G, V=V, dtype=dtype, T=T)
     check_chain(c, f"shape B={B} G={G} V={V} {dtype} T={T}")
     check_greedy(c, f"shape B={B} G={G} V={V} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("cluster", [None, "1"])
+def test_large_vocabulary(dtype, cluster, monkeypatch):
+    """A vocabulary of a million tokens (ragged: 1,000,003): 245 fine chunks per row, spread
+    over up to sixteen workgroups, or all in one (the final draw then searches 245 chunk
+    masses in k_draw)."""
+    if cluster is not None:
+        monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    c = wl.make_chain(2, seed=11, B=3, G=2, V=1_000_003, dtype=dtype)
+    check_chain(c, f"V=1000003 {dtype} W={cluster}")
+    check_greedy(c, f"V=1000003 {dtype} W={cluster}")
