@@ -2038,11 +2038,16 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         int bonus_owner = -2;  // -2: not taken here
         double bonus_t1 = 0.0;
         if (a.walk_draw && st.kind == kDrawTarget) {
+            // A slice holding less than 1e-30 of the mass counts as empty: its weights could
+            // underflow in fp32 where the owner weighs them (a slice above it has an element
+            // of at least 1e-30 over its at most 64 chunks' 262144 elements, well inside
+            // fp32's normal range).
             auto slice_total = [&](int j) {
                 const float mj = __uint_as_float(xs.xp[j][0]);
-                return mj == -INFINITY ? 0.0
-                                       : dbl_of(xs.xp[j][1], xs.xp[j][2]) *
-                                             exp(((double)mj - (double)M) / Td) / Z;
+                const double tj = mj == -INFINITY ? 0.0
+                                                  : dbl_of(xs.xp[j][1], xs.xp[j][2]) *
+                                                        exp(((double)mj - (double)M) / Td) / Z;
+                return tj >= 1e-30 ? tj : 0.0;
             };
             double tot = 0.0;
             for (int j = 0; j < W; ++j) tot += slice_total(j);
