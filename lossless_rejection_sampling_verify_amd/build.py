@@ -23,15 +23,34 @@ HIPCC_FLAGS = [
 ]
 
 
+DEMO_SRC = os.path.join(HERE, "csrc", "abi_demo.c")
+DEMO_PATH = os.path.join(HERE, "abi_demo")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
 def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    hipcc = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
+    build_demo(verbose)
     return LIB_PATH
+
+
+def build_demo(verbose: bool = False) -> str:
+    """The plain C consumer of the ABI (gcc, linked against the library next to it)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-o", DEMO_PATH + ".tmp", DEMO_SRC,
+           "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-L", HERE, "-lspecverify",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(DEMO_PATH + ".tmp", DEMO_PATH)
+    return DEMO_PATH
 
 
 if __name__ == "__main__":
