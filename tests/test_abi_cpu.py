@@ -6,6 +6,7 @@ placeholders that are never dereferenced)."""
 from __future__ import annotations
 
 import ctypes
+import os
 
 import pytest
 
@@ -209,3 +210,14 @@ def test_calibration_utilities_reject_bad_arguments(lib):
     assert lib.spec_calib_exp(1, 1, None, None) == L.SPEC_ERR_NULL
     for blocks, iters in ((0, 1), (65536, 1), (1, 0), (1, (1 << 20) + 1)):
         assert lib.spec_calib_exp(blocks, iters, fake, None) == L.SPEC_ERR_PARAM
+
+
+def test_c_consumer_is_built_and_checks_its_arguments():
+    """The plain C consumer of the ABI links against the library and rejects a bad command
+    line before any device call (no GPU needed)."""
+    import subprocess
+    demo = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "lossless_rejection_sampling_verify_amd", "abi_demo")
+    assert os.path.exists(demo), "build the package first"
+    r = subprocess.run([demo], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
