@@ -523,3 +523,45 @@ def test_large_vocabulary(dtype, cluster, monkeypatch):
     c = wl.make_chain(2, seed=11, B=3, G=2, V=1_000_003, dtype=dtype)
     check_chain(c, f"V=1000003 {dtype} W={cluster}")
     check_greedy(c, f"V=1000003 {dtype} W={cluster}")
+
+
+def test_tree_walk_first_token_law():
+    """The target-only tree walk at thresholds 1 / 1 is lossless: over many coin draws the
+    first emitted token (an accepted child of the root, or the draw from the root's row
+    with the rejected children removed) follows the root's target row.  20000 trials of
+    one small tree (root with three children drafted as its top three tokens, two of them
+    with children of their own), chi-square on the GPU's tokens; the first 2000 trials are
+    also compared with the oracle."""
+    rng = np.random.default_rng(808)
+    V, N, D, trials = 24, 7, 2, 20000
+    rows = (rng.standard_normal((N, V)) * 1.5).astype(np.float32)
+    parents = np.array([-1, 0, 0, 0, 1, 1, 2], np.int32)
+    tokens = np.zeros(N, np.int32)
+    tokens[1:4] = np.argsort(-rows[0])[:3]
+    tokens[4:6] = np.argsort(-rows[1])[:2]
+    tokens[6] = np.argsort(-rows[2])[0]
+    T = 1.0
+    t = wl.TreeInputs(name="law tree", B=trials, N=N, V=V, D=D, dtype=wl.F32,
+                      logits=np.ascontiguousarray(np.broadcast_to(rows, (trials, N, V))),
+                      node_tokens=np.ascontiguousarray(np.broadcast_to(tokens, (trials, N))),
+                      parents=np.ascontiguousarray(np.broadcast_to(parents, (trials, N))),
+                      coins=wl.draw_coins(rng, (trials, D + 1)),
+                      temperature=np.full(trials, T, np.float32))
+    say("tree walk first-token law, 20000 trials")
+    g = gpu_tree(t, oracle.TREE_SAMPLING)
+    assert (g["accept_len"] >= 0).all()
+    p0 = scipy.special.softmax(rows[0].astype(np.float64) / T)
+    counts = np.bincount(g["out_tokens"][:, 0], minlength=V)
+    exp = p0 * trials
+    keep = exp >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    ex = np.append(exp[keep], exp[~keep].sum())
+    assert scipy.stats.chisquare(obs, ex).pvalue > 1e-3
+    sub = wl.TreeInputs(name="law tree head", B=2000, N=N, V=V, D=D, dtype=wl.F32,
+                        logits=t.logits[:2000], node_tokens=t.node_tokens[:2000],
+                        parents=t.parents[:2000], coins=t.coins[:2000],
+                        temperature=t.temperature[:2000])
+    o = oracle.verify_tree(sub.logits, sub.dtype, sub.node_tokens, sub.parents, sub.coins,
+                           sub.temperature, D, oracle.TREE_SAMPLING)
+    compare({k: v[:2000] for k, v in g.items()}, o,
+            ["accept_len", "out_tokens", "accepted_nodes"], o["margin"], label="law tree")
