@@ -153,3 +153,46 @@ def test_cluster_sizes(cluster, monkeypatch):
     monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
     t = wl.make_tree_mss(4, seed=13, B=16, N=40, V=30011, D=6, max_children=6, dtype=wl.BF16)
     check_mss(t, f"cluster cap {cluster}")
+
+
+def test_first_token_law_with_iid_children():
+    """Multi-step speculative sampling is lossless when a node's children are independent
+    draws from its draft row: over 20000 trials, each drawing the root's three children
+    afresh from q (duplicates allowed), the first emitted token follows the root's target
+    row (chi-square on the GPU's tokens); the first 2000 trials are also compared with the
+    oracle."""
+    import scipy.special
+    import scipy.stats
+    rng = np.random.default_rng(909)
+    V, N, D, trials = 20, 4, 1, 20000
+    rows = (rng.standard_normal((N, V)) * 1.5).astype(np.float32)
+    drafts = rows + rng.standard_normal((N, V)).astype(np.float32)
+    q = scipy.special.softmax(drafts.astype(np.float64), axis=-1).astype(np.float32)
+    parents = np.array([-1, 0, 0, 0], np.int32)
+    tokens = np.zeros((trials, N), np.int32)
+    qq = q[0].astype(np.float64) / q[0].astype(np.float64).sum()
+    tokens[:, 1:] = rng.choice(V, size=(trials, 3), p=qq)
+    t = wl.TreeMssInputs(name="law tree", B=trials, N=N, V=V, D=D, dtype=wl.F32,
+                         logits=np.ascontiguousarray(np.broadcast_to(rows, (trials, N, V))),
+                         draft_probs=np.ascontiguousarray(np.broadcast_to(q, (trials, N, V))),
+                         node_tokens=tokens,
+                         parents=np.ascontiguousarray(np.broadcast_to(parents, (trials, N))),
+                         coins=wl.draw_coins(rng, (trials, N)),
+                         temperature=np.ones(trials, np.float32))
+    say("mss first-token law, 20000 trials")
+    g = gpu_mss(t)
+    assert (g["accept_len"] >= 0).all()
+    p0 = scipy.special.softmax(rows[0].astype(np.float64))
+    counts = np.bincount(g["out_tokens"][:, 0], minlength=V)
+    exp = p0 * trials
+    keep = exp >= 5
+    obs, ex = counts[keep], exp[keep]
+    if (~keep).any():  # the rare tokens pooled into one bin
+        obs, ex = np.append(obs, counts[~keep].sum()), np.append(ex, exp[~keep].sum())
+    assert scipy.stats.chisquare(obs, ex).pvalue > 1e-3
+    head = {k: v for k, v in dict(logits=t.logits[:2000], q=t.draft_probs[:2000],
+                                   tokens=t.node_tokens[:2000], parents=t.parents[:2000],
+                                   coins=t.coins[:2000], temperature=t.temperature[:2000]).items()}
+    o = oracle_mss(t, **head)
+    compare({k: v[:2000] for k, v in g.items()}, o,
+            ["accept_len", "out_tokens", "accepted_nodes"], o["margin"], label="mss law tree")
