@@ -273,7 +273,7 @@ __device__ inline int block_min(int v, RowSmem& sm) {
 // per lane), so the reduction's arithmetic overlaps the memory latency; that matters when a
 // workgroup has its SIMDs to itself, as in the walks' later positions.
 //
-// bkey (optional, unpipelined passes): batch j of this lane (its vectors v = tid +
+// bkey (optional): batch j of this lane (its vectors v = tid +
 // kBlock * (kU * j + u)) leaves the top 16 bits of its maximum's order key in
 // bkey[j * kBlock + tid], for the first kMaxBatchRec batches.
 constexpr int kMaxBatchRec = 24;
@@ -375,6 +375,15 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
 #pragma unroll
         for (int u = 0; u < kU; ++u) raw[u] = kNT ? ld_stream(vp + v0 + u * kBlock) : vp[v0 + u * kBlock];
     };
+    auto record = [&](float bm, int v0) {
+        if (bkey) {
+            const int j = (v0 - tid) / (kU * kBlock);
+            // +0.0f: a -0.0 maximum stands for +0.0 too (fmaxf may return either)
+            const uint32_t u = __float_as_uint(bm + 0.0f);
+            if (j < kMaxBatchRec)
+                bkey[j * kBlock + tid] = (uint16_t)(((u & 0x80000000u) ? ~u : (u | 0x80000000u)) >> 16);
+        }
+    };
     if (tid < head) scalar(tid);
     int v = tid;
     if (kPipe) {
@@ -389,12 +398,12 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
         while (full(v)) {
             load(rb, full(v + step) ? v + step : v);
             __builtin_amdgcn_sched_barrier(0);  // batch j + 1 in flight before batch j is reduced
-            batch(ra, kU, v);
+            record(batch(ra, kU, v), v);
             v += step;
             if (!full(v)) break;
             load(ra, full(v + step) ? v + step : v);
             __builtin_amdgcn_sched_barrier(0);
-            batch(rb, kU, v);
+            record(batch(rb, kU, v), v);
             v += step;
         }
     } else {
@@ -405,15 +414,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             // alone, the scheduler interleaves the unpacking with the loads and waits
             // after two)
             __builtin_amdgcn_sched_barrier(0);
-            const float bm = batch(raw, kU, v);
-            if (bkey) {
-                const int j = (v - tid) / (kU * kBlock);
-                // +0.0f: a -0.0 maximum stands for +0.0 too (fmaxf may return either)
-                const uint32_t u = __float_as_uint(bm + 0.0f);
-                if (j < kMaxBatchRec)
-                    bkey[j * kBlock + tid] =
-                        (uint16_t)(((u & 0x80000000u) ? ~u : (u | 0x80000000u)) >> 16);
-            }
+            record(batch(raw, kU, v), v);
         }
     }
     for (; v < nv; v += kBlock) {
@@ -3161,8 +3162,8 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     // kMaxBatchRec of them (the vector count bounds it: the head shifts it by less than one)
     const long nvec = (long)V * sizeof(T) / 16;
     const bool fits = nvec / (kUnroll * kBlock) + 1 <= kMaxBatchRec;
-    const Part st = chunk_record<T, true>(rowp, 0, V, s2, sm.rs, &lane_max,
-                                          fits ? sm.bkey : nullptr);
+    const Part st = chunk_record<T, true, true, kUnroll, true>(rowp, 0, V, s2, sm.rs, &lane_max,
+                                                              fits ? sm.bkey : nullptr);
     FiltRow fr;
     fr.M = st.m;
     fr.th = 0u;
