@@ -1248,6 +1248,16 @@ __device__ inline void weigh4(const typename Quad<T>::Raw& lr, const typename QR
                               const WParams& W, float& pw, float& ww) {
     float l[4];
     Quad<T>::unpack(lr, l);
+    if (kFilt) {  // every target weight filtered out: both sums are +0, no exponential needed
+        bool kept = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kept = kept || order_key(l[e]) >= W.thp;
+        if (!kept) {
+            pw = 0.f;
+            ww = 0.f;
+            return;
+        }
+    }
     float qv[4] = {0.f, 0.f, 0.f, 0.f};
     if (kQ == 1) {
         const u32x4& r = reinterpret_cast<const u32x4&>(qr);
