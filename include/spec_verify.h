@@ -34,8 +34,10 @@
  *     probabilities q are used exactly as given (already at temperature T).
  *   - Return value: SPEC_OK, or a negative status for an argument error found on the
  *     host before anything is enqueued (nothing is written), or SPEC_ERR_HIP if a launch
- *     failed.  Errors in the data are reported in-band per request: accept_len[b] = -1,
- *     token / node rows of that request filled with -1 and probability rows with 0.
+ *     failed.  Errors in the data are reported in-band per request: accept_len[b] =
+ *     SPEC_ROW_INVALID (-1), token / node rows of that request filled with -1 and
+ *     probability rows with 0.  accept_len[b] = SPEC_ROW_RETRY (-2) means the request
+ *     was not verified (see "Walks" below); its other output rows are then unspecified.
  *     A request is invalid when something the verify consults is unusable: a token id
  *     outside [0, V), a temperature that is not finite and > 0, a coin outside (0, 1], a
  *     row with no finite logit (all -inf), a drafted token's q that is negative or not
@@ -46,12 +48,23 @@
  *     checks every row).  NaN or +inf logits are undefined.
  *   - Workspace: a device buffer of at least spec_workspace_bytes(op, B, R, V) bytes,
  *     256-byte aligned, owned by the caller, ZERO-FILLED ONCE before its first use
- *     (hipMemset).  Its first 256 bytes hold a call counter that tags the words the
- *     workgroups of one request hand to each other; each call advances it on the
- *     device, so a call captured into a HIP graph replays correctly.  Everything else in
+ *     (hipMemset).  Its header holds a call counter that tags the words the workgroups
+ *     of one request hand to each other, and one exit word per request; each call
+ *     advances the counter on the device once every workgroup of the call has finished,
+ *     and leaves the exit words at zero, so a call captured into a HIP graph replays
+ *     correctly and one workspace serves calls of any shape in turn.  Everything else in
  *     it is written before it is read within a call.  Calls that may run at the same time
  *     (on different streams) need separate workspaces; calls issued in order on one
  *     stream can share one.
+ *   - Walks: by default the greedy, chain and tree calls spread each request over a
+ *     cluster of workgroups that walk it position by position (node by node) and stop
+ *     where the method stops, handing row statistics to each other through the
+ *     workspace.  Every wait for another workgroup is bounded (spec_options.spin_limit
+ *     polls, 2^18 by default: far longer than a walk takes while its workgroups run).  A
+ *     wait that runs out, which only happens when other work keeps a cluster's
+ *     workgroups off the device for that long, ends that request with accept_len =
+ *     SPEC_ROW_RETRY instead of hanging; the other requests are unaffected, the next
+ *     call on the same workspace is unaffected, and calling again verifies the request.
  *   - Determinism: identical inputs give bitwise-identical outputs.
  *   - Coin convention: every comparison is coin <= threshold.  The final draw (the
  *     correction, the bonus, or the tree's last token) is the inverse CDF in ascending
@@ -68,6 +81,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* In-band results of a request (accept_len[b]) other than an accepted length. */
+#define SPEC_ROW_INVALID (-1) /* something the verify consults is unusable */
+#define SPEC_ROW_RETRY (-2)   /* not verified: a wait between the request's workgroups ran out */
 
 enum {
     SPEC_OK = 0,
@@ -87,6 +104,37 @@ enum { SPEC_OP_GREEDY = 0, SPEC_OP_CHAIN = 1, SPEC_OP_TREE = 2, SPEC_OP_CHAIN_FI
 #define SPEC_MAX_G 64     /* drafted positions per request (chain) */
 #define SPEC_MAX_N 1024   /* tree nodes per request, root included */
 
+enum { SPEC_PATH_WALK = 0, SPEC_PATH_EAGER = 1 };
+enum { SPEC_LOADS_DEFAULT = 0, SPEC_LOADS_CACHED = 1, SPEC_LOADS_STREAMING = 2 };
+
+/* Launch options of the *_opt entry points.  Zero-initialise and set what you need: a
+ * field left at 0 keeps the library's own choice, which is all the plain entry points use.
+ * The same options give the same kernels and launch shapes on the same device, whatever
+ * the process environment.  Greedy results never depend on them.  Sampling results agree
+ * across options except where a coin lies within rounding of a threshold (the paths add
+ * the same fp32 terms in different groupings); timing and the SPEC_ROW_RETRY behaviour
+ * depend on them.
+ *   path        SPEC_PATH_WALK: walk each request and read only the rows the method
+ *               consults (default); SPEC_PATH_EAGER: stream every row once, then decide
+ *               in separate kernels (greedy, chain and tree; the multi-step tree always
+ *               walks).
+ *   cluster     walks: workgroups per request.  0: the largest width at which every
+ *               request's workgroups are resident at once.  A request is never spread
+ *               over more workgroups than the device holds at once for the batch, nor
+ *               over more than 16.
+ *   splits      eager row passes: workgroups per row (0: about 64 KB of logits each).
+ *   row_loads   chain walk's row loads: SPEC_LOADS_CACHED (the default) or
+ *               SPEC_LOADS_STREAMING (non-temporal).
+ *   spin_limit  walks: polls before a wait for another workgroup gives up (0: 2^18);
+ *               a tiny value forces SPEC_ROW_RETRY, for tests of that path. */
+typedef struct spec_options {
+    int path;
+    int cluster;
+    int splits;
+    int row_loads;
+    int spin_limit;
+} spec_options;
+
 /* Bytes of workspace a call of kind `op` needs for B requests, R logit rows per request
  * (G+1 for the chain calls, N for the tree) and vocabulary V.  0 for unusable sizes. */
 size_t spec_workspace_bytes(int op, int B, int R, int V);
@@ -104,6 +152,11 @@ const char* spec_status_str(int status);
 int spec_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
                        int B, int G, int V, int32_t* accept_len, int32_t* out_tokens,
                        void* workspace, size_t ws_bytes, void* stream);
+/* The same with launch options (NULL: the defaults). */
+int spec_verify_greedy_opt(const void* logits, int dtype, const int32_t* draft_tokens,
+                           int B, int G, int V, int32_t* accept_len, int32_t* out_tokens,
+                           void* workspace, size_t ws_bytes, void* stream,
+                           const spec_options* opt);
 
 /* Chain rejection sampling (spec_origins, "Speculative Decoding", acceptance rule;
  * ricardokevins, "correction sampling", Eq. a(x) and Eq. r(x)).
@@ -124,6 +177,12 @@ int spec_verify_chain(const void* logits, int dtype, const float* draft_probs,
                       const float* temperature, int B, int G, int V, int32_t* accept_len,
                       int32_t* out_tokens, float* probs_out, void* workspace,
                       size_t ws_bytes, void* stream);
+/* The same with launch options (NULL: the defaults). */
+int spec_verify_chain_opt(const void* logits, int dtype, const float* draft_probs,
+                          const int32_t* draft_tokens, const float* coins,
+                          const float* temperature, int B, int G, int V, int32_t* accept_len,
+                          int32_t* out_tokens, float* probs_out, void* workspace,
+                          size_t ws_bytes, void* stream, const spec_options* opt);
 
 /* Chain rejection sampling from draft logits, with top-k / top-p filtering
  * (ricardokevins, "mechanism": serving samples with temperature, top-p and top-k;
@@ -179,6 +238,13 @@ int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
                      float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
                      int32_t* accepted_nodes, float* probs_out, void* workspace,
                      size_t ws_bytes, void* stream);
+/* The same with launch options (NULL: the defaults). */
+int spec_verify_tree_opt(const void* logits, int dtype, const int32_t* node_tokens,
+                         const int32_t* parents, const float* coins, const float* temperature,
+                         int B, int N, int V, int D, int mode, float threshold_single,
+                         float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
+                         int32_t* accepted_nodes, float* probs_out, void* workspace,
+                         size_t ws_bytes, void* stream, const spec_options* opt);
 
 /* Token-tree verify by multi-step speculative sampling with draft distributions
  * (spec_origins, "SpecInfer": the children of a node are tested in turn with
@@ -208,6 +274,13 @@ int spec_verify_tree_mss(const void* logits, int dtype, const float* draft_probs
                          int D, int32_t* accept_len, int32_t* out_tokens,
                          int32_t* accepted_nodes, float* probs_out, void* workspace,
                          size_t ws_bytes, void* stream);
+/* The same with launch options (NULL: the defaults; `path` is ignored). */
+int spec_verify_tree_mss_opt(const void* logits, int dtype, const float* draft_probs,
+                             const int32_t* node_tokens, const int32_t* parents,
+                             const float* coins, const float* temperature, int B, int N,
+                             int V, int D, int32_t* accept_len, int32_t* out_tokens,
+                             int32_t* accepted_nodes, float* probs_out, void* workspace,
+                             size_t ws_bytes, void* stream, const spec_options* opt);
 
 /* Tree attention mask and positions (spec_origins, "SpecInfer": the token tree is
  * flattened into one sequence and each node attends only to its ancestors, so one target

@@ -19,6 +19,32 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_TREE_GREEDY, SPEC_TREE_SAMPLING = 0, 1
 SPEC_OP_GREEDY, SPEC_OP_CHAIN, SPEC_OP_TREE, SPEC_OP_CHAIN_FILTERED, SPEC_OP_TREE_MSS = 0, 1, 2, 3, 4
 SPEC_MAX_G, SPEC_MAX_N = 64, 1024
+SPEC_ROW_INVALID, SPEC_ROW_RETRY = -1, -2
+SPEC_PATH_WALK, SPEC_PATH_EAGER = 0, 1
+SPEC_LOADS_DEFAULT, SPEC_LOADS_CACHED, SPEC_LOADS_STREAMING = 0, 1, 2
+
+
+class SpecOptions(ctypes.Structure):
+    """struct spec_options of include/spec_verify.h (every field 0: the defaults)."""
+    _fields_ = [("path", ctypes.c_int), ("cluster", ctypes.c_int), ("splits", ctypes.c_int),
+                ("row_loads", ctypes.c_int), ("spin_limit", ctypes.c_int)]
+
+
+def options(opts) -> "SpecOptions | None":
+    """A SpecOptions from None, a SpecOptions, or a dict of its fields (path may be
+    'walk' / 'eager'; row_loads may be 'cached' / 'streaming')."""
+    if opts is None or isinstance(opts, SpecOptions):
+        return opts
+    d = dict(opts)
+    unknown = set(d) - {f for f, _ in SpecOptions._fields_}
+    if unknown:
+        raise ValueError(f"unknown option(s) {sorted(unknown)}")
+    if isinstance(d.get("path"), str):
+        d["path"] = {"walk": SPEC_PATH_WALK, "eager": SPEC_PATH_EAGER}[d["path"]]
+    if isinstance(d.get("row_loads"), str):
+        d["row_loads"] = {"default": SPEC_LOADS_DEFAULT, "cached": SPEC_LOADS_CACHED,
+                          "streaming": SPEC_LOADS_STREAMING}[d["row_loads"]]
+    return SpecOptions(**{k: int(v) for k, v in d.items()})
 
 _lib = None
 
@@ -48,19 +74,28 @@ def lib():
         L.spec_workspace_bytes.restype = sz
         L.spec_status_str.argtypes = [ip]
         L.spec_status_str.restype = ctypes.c_char_p
+        op = ctypes.POINTER(SpecOptions)
         L.spec_verify_greedy.argtypes = [vp, ip, vp, ip, ip, ip, vp, vp, vp, sz, vp]
         L.spec_verify_greedy.restype = ip
+        L.spec_verify_greedy_opt.argtypes = L.spec_verify_greedy.argtypes + [op]
+        L.spec_verify_greedy_opt.restype = ip
         L.spec_verify_chain.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp, vp, sz, vp]
         L.spec_verify_chain.restype = ip
+        L.spec_verify_chain_opt.argtypes = L.spec_verify_chain.argtypes + [op]
+        L.spec_verify_chain_opt.restype = ip
         L.spec_verify_tree.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, fp,
                                        vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_tree.restype = ip
+        L.spec_verify_tree_opt.argtypes = L.spec_verify_tree.argtypes + [op]
+        L.spec_verify_tree_opt.restype = ip
         L.spec_verify_chain_filtered.argtypes = [vp, vp, ip, vp, vp, vp, vp, vp, ip, ip, ip, vp, vp,
                                                  vp, vp, sz, vp]
         L.spec_verify_chain_filtered.restype = ip
         L.spec_verify_tree_mss.argtypes = [vp, ip, vp, vp, vp, vp, vp, ip, ip, ip, ip, vp, vp, vp,
                                            vp, vp, sz, vp]
         L.spec_verify_tree_mss.restype = ip
+        L.spec_verify_tree_mss_opt.argtypes = L.spec_verify_tree_mss.argtypes + [op]
+        L.spec_verify_tree_mss_opt.restype = ip
         L.spec_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp, vp]
         L.spec_tree_mask.restype = ip
         L.spec_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, sz, vp, vp]

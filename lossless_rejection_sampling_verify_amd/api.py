@@ -7,6 +7,8 @@ temperatures, int32 tokens and parents); nothing is converted or computed here.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib as L
@@ -39,31 +41,47 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _torch_stream(device, stream):
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
 def _stream(device, stream):
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return s.cuda_stream
+    return _torch_stream(device, stream).cuda_stream
 
 
-def workspace(op: int, B: int, R: int, V: int, device) -> torch.Tensor:
-    """A workspace big enough for the call, cached per device and kind.
+def _opts(opts):
+    o = L.options(opts)
+    return None if o is None else ctypes.byref(o)
 
-    Zero-filled when allocated (the library keeps a call counter in its first bytes and
-    leaves it ready for the next call), so one cached buffer serves every later call
-    issued on the same stream."""
+
+def workspace(op: int, B: int, R: int, V: int, device, stream=None) -> torch.Tensor:
+    """A workspace big enough for the call, cached per device, kind and stream.
+
+    Calls that may run at the same time need separate workspaces, and calls issued in
+    order on one stream can share one, so the cache keeps one buffer per stream.  A buffer
+    is allocated on the stream it serves and zero-filled there (the library keeps a call
+    counter and per-request exit words in its header and leaves them ready for the next
+    call).  When a call needs a larger one, the old buffer is released to torch's caching
+    allocator, which hands that memory out again only in that stream's order, after the
+    calls already enqueued on it."""
     need = L.workspace_bytes(op, B, R, V)
     if need == 0:
         raise ValueError("unsupported sizes")
-    key = (torch.device(device), op)
+    dev = torch.device(device)
+    s = _torch_stream(dev, stream)
+    key = (dev, op, s.cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
         _WORKSPACES[key] = ws
     return ws
 
 
 def spec_verify_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, *, ws=None,
-                       stream=None, out=None):
+                       stream=None, out=None, opts=None):
     """Greedy chain verify.  logits [B][G+1][V] fp32/bf16, draft_tokens [B][G] int32.
+    ``opts``: launch options (a dict of spec_options fields, or None for the defaults).
 
     Returns (accept_len [B] int32, out_tokens [B][G+1] int32)."""
     _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
@@ -73,15 +91,15 @@ def spec_verify_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, *, ws=N
     if draft_tokens.shape != (B, G):
         raise ValueError("draft_tokens must be [B][G]")
     dev = logits.device
-    ws = workspace(L.SPEC_OP_GREEDY, B, R, V, dev) if ws is None else ws
+    ws = workspace(L.SPEC_OP_GREEDY, B, R, V, dev, stream) if ws is None else ws
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=dev)
         toks = torch.empty(B, R, dtype=torch.int32, device=dev)
     else:
         acc, toks = out
-    rc = L.lib().spec_verify_greedy(_ptr(logits), _logit_dtype(logits), _ptr(draft_tokens), B, G, V,
-                                    _ptr(acc), _ptr(toks), _ptr(ws), ws.numel(),
-                                    _stream(dev, stream))
+    rc = L.lib().spec_verify_greedy_opt(_ptr(logits), _logit_dtype(logits), _ptr(draft_tokens), B,
+                                        G, V, _ptr(acc), _ptr(toks), _ptr(ws), ws.numel(),
+                                        _stream(dev, stream), _opts(opts))
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_verify_greedy", rc)
     return acc, toks
@@ -89,9 +107,10 @@ def spec_verify_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, *, ws=N
 
 def spec_verify_chain(logits: torch.Tensor, draft_probs: torch.Tensor, draft_tokens: torch.Tensor,
                       coins: torch.Tensor, temperature: torch.Tensor, *, want_probs: bool = False,
-                      ws=None, stream=None, out=None):
+                      ws=None, stream=None, out=None, opts=None):
     """Chain rejection sampling.  logits [B][G+1][V], draft_probs [B][G][V] fp32,
     draft_tokens [B][G] int32, coins [B][G+1] fp32, temperature [B] fp32.
+    ``opts``: launch options (a dict of spec_options fields, or None for the defaults).
 
     Returns (accept_len [B], out_tokens [B][G+1], probs [B][G+1] or None)."""
     _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
@@ -105,17 +124,17 @@ def spec_verify_chain(logits: torch.Tensor, draft_probs: torch.Tensor, draft_tok
             coins.shape != (B, R) or temperature.shape != (B,):
         raise ValueError("inconsistent shapes")
     dev = logits.device
-    ws = workspace(L.SPEC_OP_CHAIN, B, R, V, dev) if ws is None else ws
+    ws = workspace(L.SPEC_OP_CHAIN, B, R, V, dev, stream) if ws is None else ws
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=dev)
         toks = torch.empty(B, R, dtype=torch.int32, device=dev)
         probs = torch.empty(B, R, dtype=torch.float32, device=dev) if want_probs else None
     else:
         acc, toks, probs = out
-    rc = L.lib().spec_verify_chain(_ptr(logits), _logit_dtype(logits), _ptr(draft_probs),
-                                   _ptr(draft_tokens), _ptr(coins), _ptr(temperature), B, G, V,
-                                   _ptr(acc), _ptr(toks), _ptr(probs), _ptr(ws), ws.numel(),
-                                   _stream(dev, stream))
+    rc = L.lib().spec_verify_chain_opt(_ptr(logits), _logit_dtype(logits), _ptr(draft_probs),
+                                       _ptr(draft_tokens), _ptr(coins), _ptr(temperature), B, G,
+                                       V, _ptr(acc), _ptr(toks), _ptr(probs), _ptr(ws),
+                                       ws.numel(), _stream(dev, stream), _opts(opts))
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_verify_chain", rc)
     return acc, toks, probs
@@ -146,7 +165,7 @@ def spec_verify_chain_filtered(logits: torch.Tensor, draft_logits: torch.Tensor,
     if top_p is not None:
         _check(top_p, "top_p", torch.float32, 1)
     dev = logits.device
-    ws = workspace(L.SPEC_OP_CHAIN_FILTERED, B, R, V, dev) if ws is None else ws
+    ws = workspace(L.SPEC_OP_CHAIN_FILTERED, B, R, V, dev, stream) if ws is None else ws
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=dev)
         toks = torch.empty(B, R, dtype=torch.int32, device=dev)
@@ -166,9 +185,10 @@ def spec_verify_chain_filtered(logits: torch.Tensor, draft_logits: torch.Tensor,
 def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
                      coins, temperature, D: int, mode: int, threshold_single: float = 1.0,
                      threshold_acc: float = 1.0, *, want_probs: bool = False, ws=None,
-                     stream=None, out=None):
+                     stream=None, out=None, opts=None):
     """Token-tree verify.  logits [B][N][V], node_tokens/parents [B][N] int32,
     coins [B][D+1] fp32 and temperature [B] fp32 (sampling mode; None in greedy mode).
+    ``opts``: launch options (a dict of spec_options fields, or None for the defaults).
 
     Returns (accept_len [B], out_tokens [B][D+1], accepted_nodes [B][D], probs or None)."""
     _check(logits, "logits", (torch.float32, torch.bfloat16), 3)
@@ -184,7 +204,7 @@ def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: t
     if temperature is not None:
         _check(temperature, "temperature", torch.float32, 1)
     dev = logits.device
-    ws = workspace(L.SPEC_OP_TREE, B, N, V, dev) if ws is None else ws
+    ws = workspace(L.SPEC_OP_TREE, B, N, V, dev, stream) if ws is None else ws
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=dev)
         toks = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
@@ -192,11 +212,11 @@ def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: t
         probs = torch.empty(B, D + 1, dtype=torch.float32, device=dev) if want_probs else None
     else:
         acc, toks, nodes, probs = out
-    rc = L.lib().spec_verify_tree(_ptr(logits), _logit_dtype(logits), _ptr(node_tokens),
-                                  _ptr(parents), _ptr(coins), _ptr(temperature), B, N, V, D,
-                                  int(mode), float(threshold_single), float(threshold_acc),
-                                  _ptr(acc), _ptr(toks), _ptr(nodes), _ptr(probs), _ptr(ws),
-                                  ws.numel(), _stream(dev, stream))
+    rc = L.lib().spec_verify_tree_opt(_ptr(logits), _logit_dtype(logits), _ptr(node_tokens),
+                                      _ptr(parents), _ptr(coins), _ptr(temperature), B, N, V, D,
+                                      int(mode), float(threshold_single), float(threshold_acc),
+                                      _ptr(acc), _ptr(toks), _ptr(nodes), _ptr(probs), _ptr(ws),
+                                      ws.numel(), _stream(dev, stream), _opts(opts))
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_verify_tree", rc)
     return acc, toks, nodes, probs
@@ -205,7 +225,7 @@ def spec_verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: t
 def spec_verify_tree_mss(logits: torch.Tensor, draft_probs: torch.Tensor,
                          node_tokens: torch.Tensor, parents: torch.Tensor, coins: torch.Tensor,
                          temperature: torch.Tensor, D: int, *, want_probs: bool = False, ws=None,
-                         stream=None, out=None):
+                         stream=None, out=None, opts=None):
     """Token-tree verify by multi-step speculative sampling.  logits [B][N][V],
     draft_probs [B][N][V] fp32 (row j: the distribution node j's children were drawn from),
     node_tokens/parents [B][N] int32, coins [B][N] fp32 (coins[b][c-1] tests node c,
@@ -226,7 +246,7 @@ def spec_verify_tree_mss(logits: torch.Tensor, draft_probs: torch.Tensor,
     if temperature.shape != (B,):
         raise ValueError("temperature must be [B]")
     dev = logits.device
-    ws = workspace(L.SPEC_OP_TREE_MSS, B, N, V, dev) if ws is None else ws
+    ws = workspace(L.SPEC_OP_TREE_MSS, B, N, V, dev, stream) if ws is None else ws
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=dev)
         toks = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
@@ -234,11 +254,11 @@ def spec_verify_tree_mss(logits: torch.Tensor, draft_probs: torch.Tensor,
         probs = torch.empty(B, D + 1, dtype=torch.float32, device=dev) if want_probs else None
     else:
         acc, toks, nodes, probs = out
-    rc = L.lib().spec_verify_tree_mss(_ptr(logits), _logit_dtype(logits), _ptr(draft_probs),
-                                      _ptr(node_tokens), _ptr(parents), _ptr(coins),
-                                      _ptr(temperature), B, N, V, D, _ptr(acc), _ptr(toks),
-                                      _ptr(nodes), _ptr(probs), _ptr(ws), ws.numel(),
-                                      _stream(dev, stream))
+    rc = L.lib().spec_verify_tree_mss_opt(_ptr(logits), _logit_dtype(logits), _ptr(draft_probs),
+                                          _ptr(node_tokens), _ptr(parents), _ptr(coins),
+                                          _ptr(temperature), B, N, V, D, _ptr(acc), _ptr(toks),
+                                          _ptr(nodes), _ptr(probs), _ptr(ws), ws.numel(),
+                                          _stream(dev, stream), _opts(opts))
     if rc != L.SPEC_OK:
         raise L.SpecVerifyError("spec_verify_tree_mss", rc)
     return acc, toks, nodes, probs

@@ -16,7 +16,7 @@
 //   k_draw          one wave per request: locates the chunk, then the segment, then the
 //                   token holding u * total (inverse CDF in ascending token id).
 // The eager passes read every row and hand over at kernel boundaries; they are selected
-// with SPEC_VERIFY_EAGER=1 (and the filtered chain always reads every row):
+// with spec_options.path = SPEC_PATH_EAGER (the filtered chain always reads every row):
 //   k_rows          streams every target-logit row once from HBM (16-byte non-temporal
 //                   vector loads, kUnroll loads in flight per lane), split over `S`
 //                   workgroups per row.  Each workgroup reduces its chunk to one 16-byte
@@ -134,6 +134,7 @@ struct KArgs {
     int walk_temporal;   // chain walk: row passes with cache-allocating loads (sweeps: 0)
     int coin_stride;     // coins per request in `coins`; the final draw's coin is the last
     int walk_draw;       // chain walk: the final draw happens in the walk (no k_draw)
+    int spin;            // walks: polls before a hand-off wait gives up
     unsigned* hdr;       // workspace header: the walks' call counter and finished count
 };
 
@@ -975,7 +976,7 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
 // after every pass they exchange three 32-bit payloads per workgroup.
 
 constexpr int kMaxCluster = 16;    // workgroups sharing one request's walk
-constexpr long kSpinMax = 1 << 18; // bound of a cluster wait (never reached when all run)
+constexpr int kSpinMax = 1 << 18;  // default bound of a cluster wait (never reached when all run)
 
 struct XSmem {
     uint32_t xp[kMaxCluster][3];  // payloads of a cluster step, by workgroup
@@ -983,19 +984,30 @@ struct XSmem {
 };
 
 // The tag of a call's hand-off words comes from a counter in the workspace header
-// (hdr[0]; hdr[1] counts the requests whose walk has ended).  Every workgroup reads the
-// counter when it starts; workgroup 0 of each request reports at its end, and the last
-// report advances the counter.  A request's workgroup 0 ends after its first completed
-// hand-off, so by then every workgroup of the request has read the counter (each
-// published under the tag made from it); a request found invalid before any hand-off
-// never uses its tag.  All of a call's hand-offs therefore carry one tag, and the next
-// call on the stream sees the next one: the tag changes from call to call with no host
-// state, so a captured graph replays correctly.  One report per request (not per
-// workgroup) keeps the same-address atomics few.  The header must be zero before the
-// first call.
+// (hdr[0]); hdr[1] counts the requests whose workgroups have all finished, and word
+// kExitBase + b is request b's exit word.  Every workgroup reads the counter when it
+// starts, and the counter advances only when every workgroup of the call has finished:
+// each workgroup counts itself out of its request's exit word, the last one out of a
+// request reports the request, and the last report advances the counter.  No workgroup
+// can therefore read a later value than the one its call started with, whenever it
+// starts, so all of a call's hand-offs carry one tag and the next call on the stream
+// carries the next one: the tag changes from call to call with no host state, and a
+// captured graph replays correctly.  The header must be zero before the first call;
+// every exit word is reset by the last workgroup out of its request, so the header is
+// zero again (except hdr[0]) between calls, whatever the shapes of the calls.
+//
+// The exit word also carries the request's result.  Bits 0-5 count the workgroups out,
+// bits 6-11 those whose hand-off wait ran out, and bits 12-31 hold workgroup 0's result
+// plus 2 (accept_len, or -1 for an invalid request).  The last workgroup out writes
+// accept_len: workgroup 0's result, or SPEC_ROW_RETRY when any member gave up, since a
+// member that gave up may have left its part of the request undone (its slice's final
+// weights, or the final token) even where workgroup 0 saw every word it waited for.
 //
 // Only wave 0 reads the counter (thread 0 publishes, lanes below W wait), and nothing
 // waits for the read until the first hand-off, so it overlaps the first row pass.
+constexpr int kExitBase = 64;      // first exit word (byte 256 of the header)
+constexpr int kExitWords = 4096;   // requests per call that a walk with W > 1 can take
+
 __device__ inline uint32_t walk_epoch(const unsigned* hdr) {
     return (hdr && threadIdx.x < 64)
                ? __hip_atomic_load(hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
@@ -1005,8 +1017,25 @@ __device__ inline uint32_t walk_tag(uint32_t epoch) {
     return epoch % 0xffffffffu + 1u;  // never 0, the value zeroed slots hold
 }
 
-__device__ inline void walk_end(unsigned* hdr, uint32_t epoch, int w, int W) {
-    if (!hdr || w != 0 || threadIdx.x != 0) return;
+// Called once by every workgroup of a walk, after its last hand-off and its share of the
+// outputs.  `result` is workgroup 0's accept_len (-1: invalid request); `gaveup` is true
+// when one of this workgroup's waits ran out.  Without hand-off words (W = 1, hdr null)
+// workgroup 0 writes accept_len itself.
+__device__ inline void walk_end(unsigned* hdr, uint32_t epoch, int b, int w, int W,
+                                bool gaveup, int result, int32_t* accept_len) {
+    if (threadIdx.x != 0) return;
+    if (!hdr) {
+        if (w == 0) accept_len[b] = gaveup ? SPEC_ROW_RETRY : result;
+        return;
+    }
+    const unsigned inc = 1u | (gaveup ? 1u << 6 : 0u) |
+                         (w == 0 ? (unsigned)(result + 2) << 12 : 0u);
+    unsigned* ex = hdr + kExitBase + b;
+    const unsigned now =
+        __hip_atomic_fetch_add(ex, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+    if ((int)(now & 63u) != W) return;  // not the last workgroup of the request out
+    __hip_atomic_store(ex, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    accept_len[b] = ((now >> 6) & 63u) ? SPEC_ROW_RETRY : (int)(now >> 12) - 2;
     const unsigned done = __hip_atomic_fetch_add(hdr + 1, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (done == gridDim.x / W - 1) {  // the call's last request
@@ -1019,9 +1048,9 @@ __device__ inline void walk_end(unsigned* hdr, uint32_t epoch, int w, int W) {
 // the others.  Each payload travels in a 64-bit word whose high half is the call's tag;
 // words are written and read whole with agent-scope atomics, which are coherent across
 // the XCDs, so a reader that sees the tag sees the payload and no fence is needed.  Slot
-// (step, workgroup) is written once per call.  The wait is bounded: if a word never
-// arrives, the step fails and the request is reported invalid instead of hanging.  With
-// W = 1 the payloads stay in LDS.
+// (step, workgroup) is written once per call.  The wait is bounded (`spin` polls): if a
+// word never arrives, the step fails, and the request reports SPEC_ROW_RETRY instead of
+// hanging.  With W = 1 the payloads stay in LDS.
 __device__ void cluster_publish(unsigned long long* slots, int step, int W, int w,
                                 uint32_t tag, uint32_t p0, uint32_t p1, uint32_t p2,
                                 XSmem& sm) {
@@ -1041,7 +1070,7 @@ __device__ void cluster_publish(unsigned long long* slots, int step, int W, int 
 
 // Waits for the W payloads of `step` (sm.xp[w][0..2] afterwards, in every thread).
 __device__ bool cluster_wait(unsigned long long* slots, int step, int W, uint32_t tag,
-                             XSmem& sm) {
+                             int spin_max, XSmem& sm) {
     const int tid = threadIdx.x;
     if (W == 1) {
         __syncthreads();
@@ -1052,14 +1081,14 @@ __device__ bool cluster_wait(unsigned long long* slots, int step, int W, uint32_
     if (tid < W) {
         unsigned long long* q = slots + (size_t)step * W * 3 + tid * 3;
         unsigned long long v0 = 0, v1 = 0, v2 = 0;
-        for (long spin = 0;; ++spin) {
+        for (int spin = 1;; ++spin) {
             v0 = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             v1 = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             v2 = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((uint32_t)(v0 >> 32) == tag && (uint32_t)(v1 >> 32) == tag &&
                 (uint32_t)(v2 >> 32) == tag)
                 break;
-            if (spin >= kSpinMax) {
+            if (spin >= spin_max) {
                 sm.xbad = 1;
                 break;
             }
@@ -1075,9 +1104,9 @@ __device__ bool cluster_wait(unsigned long long* slots, int step, int W, uint32_
 
 // Publish then wait (a step with nothing to overlap).
 __device__ bool cluster_step(unsigned long long* slots, int step, int W, int w, uint32_t tag,
-                             uint32_t p0, uint32_t p1, uint32_t p2, XSmem& sm) {
+                             int spin_max, uint32_t p0, uint32_t p1, uint32_t p2, XSmem& sm) {
     cluster_publish(slots, step, W, w, tag, p0, p1, p2, sm);
-    return cluster_wait(slots, step, W, tag, sm);
+    return cluster_wait(slots, step, W, tag, spin_max, sm);
 }
 
 __device__ inline uint32_t dbl_hi(double x) { return (uint32_t)((unsigned long long)__double_as_longlong(x) >> 32); }
@@ -1107,7 +1136,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     // lane l of every wave holds draft token l (read once, while the first row streams)
     const int px = (tid & 63) < G ? x[tid & 63] : -1;
     int k = G, last = -1;
-    bool bad = false;
+    bool bad = false, gaveup = false;
     auto pass = [&](int r) {
         const Part cur = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(
             logits + ((size_t)b * R + r) * V, lo, hi, 0.f, rs);
@@ -1115,8 +1144,8 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     };
     pass(0);
     for (int i = 0; i <= G; ++i) {
-        if (!cluster_wait(slots, i, W, tag, xs)) {
-            bad = true;
+        if (!cluster_wait(slots, i, W, tag, a.spin, xs)) {
+            bad = gaveup = true;
             break;
         }
         float M = -INFINITY;
@@ -1153,12 +1182,12 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
             __builtin_amdgcn_s_setprio(3);
         pass(i + 1);
     }
-    walk_end(hdr, epoch, w, W);
-    if (w != 0) return;
-    int32_t* out = a.out_tokens + (size_t)b * R;
-    for (int e = tid; e < R; e += kBlock)
-        out[e] = bad ? -1 : (e < k ? x[e] : (e == k ? last : -1));
-    if (tid == 0) a.accept_len[b] = bad ? -1 : k;
+    if (w == 0) {  // workgroup 0 of the cluster writes the request's tokens
+        int32_t* out = a.out_tokens + (size_t)b * R;
+        for (int e = tid; e < R; e += kBlock)
+            out[e] = bad ? -1 : (e < k ? x[e] : (e == k ? last : -1));
+    }
+    walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : k, a.accept_len);
 }
 
 // Field-wise copy of a draw state from global memory (keeps it in registers).
@@ -1950,7 +1979,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         px = a.tokens[(size_t)b * G + tid];
         pu = a.coins[(size_t)b * R + tid];
     }
-    bool bad = false;
+    bool bad = false, gaveup = false;
     const double Td = (double)Tf;
     const float s2 = kLog2e / Tf;
     int k = G;
@@ -1977,8 +2006,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
                 qx = a.q[((size_t)b * G + i) * V + xi];
             }
         }
-        if (!cluster_wait(slots, i, W, tag, xs)) {
-            bad = true;
+        if (!cluster_wait(slots, i, W, tag, a.spin, xs)) {
+            bad = gaveup = true;
             break;
         }
         if (i == 0 && (!(isfinite(Tf) && Tf > 0.f) || !(uG > 0.f && uG <= 1.f))) {
@@ -2130,14 +2159,15 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             }
             bool fallback = false;
             double tot = 0.0;
-            if (!cluster_step(slots, R, W, w, tag, dbl_hi(tw), dbl_lo(tw), 0u, xs)) {
-                bad = true;
+            if (!cluster_step(slots, R, W, w, tag, a.spin, dbl_hi(tw), dbl_lo(tw), 0u, xs)) {
+                bad = gaveup = true;
             } else {
                 for (int j = 0; j < W; ++j) tot += dbl_of(xs.xp[j][0], xs.xp[j][1]);
                 fallback = !(tot > 0.0);
                 if (fallback) {
-                    if (!cluster_step(slots, R + 1, W, w, tag, dbl_hi(pw), dbl_lo(pw), 0u, xs)) {
-                        bad = true;
+                    if (!cluster_step(slots, R + 1, W, w, tag, a.spin, dbl_hi(pw), dbl_lo(pw), 0u,
+                                      xs)) {
+                        bad = gaveup = true;
                     } else {
                         tot = 0.0;
                         for (int j = 0; j < W; ++j) tot += dbl_of(xs.xp[j][0], xs.xp[j][1]);
@@ -2190,17 +2220,15 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             }
         }
     }
-    walk_end(hdr, epoch, w, W);
-    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
-    for (int e = tid; e < R; e += kBlock) {
-        if (e == k && !bad) continue;  // slot k is written by the final draw
-        a.out_tokens[(size_t)b * R + e] = (!bad && e < k) ? a.tokens[(size_t)b * G + e] : -1;
-        if (a.probs) a.probs[(size_t)b * R + e] = (!bad && e < k) ? sp[e] : 0.f;
+    if (w == 0) {  // workgroup 0 of the cluster writes the request's outputs
+        for (int e = tid; e < R; e += kBlock) {
+            if (e == k && !bad) continue;  // slot k is written by the final draw
+            a.out_tokens[(size_t)b * R + e] = (!bad && e < k) ? a.tokens[(size_t)b * G + e] : -1;
+            if (a.probs) a.probs[(size_t)b * R + e] = (!bad && e < k) ? sp[e] : 0.f;
+        }
+        if (tid == 0) a.dstate[b] = st;
     }
-    if (tid == 0) {
-        a.accept_len[b] = bad ? -1 : k;
-        a.dstate[b] = st;
-    }
+    walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : k, a.accept_len);
 }
 
 // k_tree_walk: the target-only token-tree walk, one cluster of W workgroups per request
@@ -2249,7 +2277,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     const int32_t* par_g = a.parents + (size_t)b * N;
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const T* logits = reinterpret_cast<const T*>(a.logits);
-    bool bad = false;
+    bool bad = false, gaveup = false;
     for (int i = tid; i < N; i += kBlock) {
         const int p = par_g[i];
         const int t = tok_g[i];
@@ -2306,9 +2334,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
             ts.lx[j] = Ld<T>::one(rowp + ts.tok[ts.kids[j]]);
         if (sampling) {
             const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
-            if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
+            if (!cluster_step(slots, step, W, w, tag, a.spin, __float_as_uint(r.m), dbl_hi(r.z),
                               dbl_lo(r.z), xs)) {
-                bad = true;
+                bad = gaveup = true;
                 break;
             }
             M = -INFINITY;
@@ -2321,9 +2349,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
             }
         } else {
             const Part r = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, 0.f, rs);
-            if (!cluster_step(slots, step, W, w, tag, __float_as_uint(r.m), (uint32_t)r.idx, 0u,
-                              xs)) {
-                bad = true;
+            if (!cluster_step(slots, step, W, w, tag, a.spin, __float_as_uint(r.m),
+                              (uint32_t)r.idx, 0u, xs)) {
+                bad = gaveup = true;
                 break;
             }
             M = -INFINITY;
@@ -2405,8 +2433,10 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         mass_slice<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
                              ts.excl);
     }
-    walk_end(hdr, epoch, w, W);
-    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
+    if (w != 0) {  // workgroup 0 of the cluster writes the request's outputs
+        walk_end(hdr, epoch, b, w, W, gaveup, 0, a.accept_len);
+        return;
+    }
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
     float* probs = a.probs ? a.probs + (size_t)b * (D + 1) : nullptr;
@@ -2434,10 +2464,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         }
         if (e >= d && e < D) nodes[e] = -1;
     }
-    if (tid == 0) {
-        a.accept_len[b] = bad ? -1 : d;
-        if (sampling) a.dstate[b] = st;
-    }
+    if (tid == 0 && sampling) a.dstate[b] = st;
+    walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : d, a.accept_len);
 }
 
 // Residual mass of a row slice, sum over [lo, hi) of max(0, p_v - cq q_v) with the draw
@@ -2583,7 +2611,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const float* coins = a.coins + (size_t)b * N;
     const T* logits = reinterpret_cast<const T*>(a.logits);
-    bool bad = false;
+    bool bad = false, gaveup = false;
     for (int i = tid; i < N; i += kBlock) {
         const int p = par_g[i];
         const int t = tok_g[i];
@@ -2641,9 +2669,9 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         for (int j = tid; j < count; j += kBlock) sm.lx[j] = Ld<T>::one(rowp + sm.tok[sm.kids[j]]);
         {
             const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
-            if (!cluster_step(slots, step++, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
-                              dbl_lo(r.z), xs)) {
-                bad = true;
+            if (!cluster_step(slots, step++, W, w, tag, a.spin, __float_as_uint(r.m),
+                              dbl_hi(r.z), dbl_lo(r.z), xs)) {
+                bad = gaveup = true;
                 break;
             }
             M = -INFINITY;
@@ -2695,8 +2723,8 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
                 break;
             }
             const double Nw = slice_resid_sum<T>(rowp, qrow, lo, hi, M, s2, invZ, (float)cn, rs);
-            if (!cluster_step(slots, step++, W, w, tag, dbl_hi(Nw), dbl_lo(Nw), 0u, xs)) {
-                bad = true;
+            if (!cluster_step(slots, step++, W, w, tag, a.spin, dbl_hi(Nw), dbl_lo(Nw), 0u, xs)) {
+                bad = gaveup = true;
                 break;
             }
             double Nn = 0.0;
@@ -2730,8 +2758,10 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         mass_slice2<T, false>(a, st, Wp, rowp, qrow, b, lo / kFine, (hi + kFine - 1) / kFine, ms,
                              nullptr);
     }
-    walk_end(hdr, epoch, w, W);
-    if (w != 0) return;  // workgroup 0 of the cluster writes the request's outputs
+    if (w != 0) {  // workgroup 0 of the cluster writes the request's outputs
+        walk_end(hdr, epoch, b, w, W, gaveup, 0, a.accept_len);
+        return;
+    }
     int32_t* out = a.out_tokens + (size_t)b * (D + 1);
     int32_t* nodes = a.accepted_nodes + (size_t)b * D;
     float* probs = a.probs ? a.probs + (size_t)b * (D + 1) : nullptr;
@@ -2752,10 +2782,8 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         }
         if (e >= d && e < D) nodes[e] = -1;
     }
-    if (tid == 0) {
-        a.accept_len[b] = bad ? -1 : d;
-        a.dstate[b] = st;
-    }
+    if (tid == 0) a.dstate[b] = st;
+    walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : d, a.accept_len);
 }
 
 // One wave per request: chunk, then segment, then token.
@@ -3448,7 +3476,9 @@ __global__ __launch_bounds__(kBlock) void k_commit_kv(const int32_t* accepted_no
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr size_t kHeaderBytes = 256;
+// The walks' call counter (first 256 bytes), then one exit word per request.
+constexpr size_t kHeaderBytes = 256 + 4 * (size_t)kExitWords;
+static_assert(kHeaderBytes % 256 == 0, "the header keeps the regions after it aligned");
 
 struct Layout {
     size_t parts, dstate, mass, massfb, seg, excl, frows, xch, total;
@@ -3471,7 +3501,7 @@ inline long fine_chunks(int V) { return ((long)V + kFine - 1) / kFine; }
 Layout layout_for(int op, int B, int R, int V) {
     Layout L;
     const size_t S2 = (size_t)fine_chunks(V);
-    size_t off = kHeaderBytes;  // the header: the walks' call counter (zero before first use)
+    size_t off = kHeaderBytes;  // the header: the walks' call counter and exit words
     L.parts = off;
     if (op != SPEC_OP_TREE_MSS) off = align256(off + sizeof(Part) * (size_t)B * R * kMaxSplits);
     L.dstate = off;
@@ -3514,18 +3544,15 @@ void bind_workspace(KArgs& a, void* ws, int op) {
 
 // Split each row into S chunks of `chunk` elements (a multiple of 8): about 64 KB of
 // logits per workgroup, at least ~2048 workgroups in flight, and at least 1024
-// elements per chunk.  SPEC_VERIFY_SPLITS overrides the count (launch-shape sweeps).
-void choose_split(long rows, int V, int esize, int* S_out, int* chunk_out) {
+// elements per chunk.  `want` > 0 (spec_options.splits) sets the count instead.
+void choose_split(long rows, int V, int esize, int want, int* S_out, int* chunk_out) {
     const long row_bytes = (long)V * esize;
     long s = (row_bytes + kChunkBytes - 1) / kChunkBytes;
     const long min_wgs = 2048;
     if (rows * s < min_wgs) s = (min_wgs + rows - 1) / rows;
     const long by_size = V / 1024 > 1 ? V / 1024 : 1;
     if (s > by_size) s = by_size;
-    if (const char* env = std::getenv("SPEC_VERIFY_SPLITS")) {
-        const long e = std::atol(env);
-        if (e >= 1) s = e;
-    }
+    if (want >= 1) s = want;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
     long ch = ((long)V + s - 1) / s;
@@ -3535,9 +3562,36 @@ void choose_split(long rows, int V, int esize, int* S_out, int* chunk_out) {
     *chunk_out = (int)ch;
 }
 
+// Launch options with every field the library chooses filled in.
+struct Opts {
+    bool eager;
+    int cluster;    // 0: from the occupancy
+    int splits;     // 0: from the row size
+    bool cached;    // chain walk: cache-allocating row loads
+    int spin;
+};
+
+Opts resolve(const spec_options* o) {
+    Opts r;
+    r.eager = o && o->path == SPEC_PATH_EAGER;
+    r.cluster = o && o->cluster > 0 ? o->cluster : 0;
+    r.splits = o && o->splits > 0 ? o->splits : 0;
+    r.cached = !(o && o->row_loads == SPEC_LOADS_STREAMING);
+    r.spin = o && o->spin_limit > 0 ? o->spin_limit : kSpinMax;
+    return r;
+}
+
+int check_opts(const spec_options* o) {
+    if (!o) return SPEC_OK;
+    if (o->path != SPEC_PATH_WALK && o->path != SPEC_PATH_EAGER) return SPEC_ERR_PARAM;
+    if (o->row_loads < SPEC_LOADS_DEFAULT || o->row_loads > SPEC_LOADS_STREAMING) return SPEC_ERR_PARAM;
+    if (o->cluster < 0 || o->splits < 0 || o->spin_limit < 0) return SPEC_ERR_PARAM;
+    return SPEC_OK;
+}
+
 // Launch shapes of a call; SPEC_ERR_SHAPE when a grid would exceed 2^32 work-items.
-int setup_shapes(KArgs& a, int esize) {
-    choose_split((long)a.B * a.R, a.V, esize, &a.S, &a.chunk);
+int setup_shapes(KArgs& a, int esize, const Opts& o) {
+    choose_split((long)a.B * a.R, a.V, esize, o.splits, &a.S, &a.chunk);
     a.S2 = (int)fine_chunks(a.V);
     const long long lim = 0xffffffffLL / kBlock;
     if ((long long)a.B * a.R * a.S > lim || (long long)a.B * a.S2 > lim) return SPEC_ERR_SHAPE;
@@ -3561,35 +3615,45 @@ int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t w
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
 
-// Workgroups of `kernel` (kBlock threads) that the current device holds at once, counting
-// at most kWalkPerCu per compute unit.  Above five per CU the walks slowed down on the
-// large batch (greedy 52 -> 55-62 us, chain 101 -> 118-124 us at six to eight), although
-// the occupancy query allows seven (greedy) or five (chain): the later workgroups then
-// start only as earlier ones finish, and their clusters wait for them.
+// Workgroups of `kernel` (kBlock threads) that the current device holds at once: `all`
+// counts what the occupancy query allows, `walk` at most kWalkPerCu per compute unit.
+// Above five per CU the walks slowed down on the large batch (greedy 52 -> 55-62 us,
+// chain 101 -> 118-124 us at six to eight), although the occupancy query allows seven
+// (greedy) or five (chain): the later workgroups then start only as earlier ones finish,
+// and their clusters wait for them.  The figures are cached per (kernel, device); a
+// cached value is written whole by whichever thread gets there first, and every thread
+// computes the same one, so concurrent first calls agree.
 constexpr int kWalkPerCu = 5;
-inline int resident_blocks(const void* kernel, int slot) {
-    static int cache[8][64];
-    static bool known[8][64];
+struct Resident {
+    int all, walk;
+};
+inline Resident resident_blocks(const void* kernel, int slot) {
+    static std::atomic<long long> cache[8][64];  // 0: not known; else (all << 32) | walk
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (!known[slot][dev]) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {0, 0};
+    long long v = cache[slot][dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0, nb = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, 0) != hipSuccess)
             nb = 0;
-        cache[slot][dev] = std::min(nb, kWalkPerCu) * cus;
-        known[slot][dev] = true;
+        const long long all = (long long)std::max(0, nb) * std::max(0, cus);
+        const long long walk = (long long)std::min(std::max(0, nb), kWalkPerCu) * std::max(0, cus);
+        v = (all << 32) | walk | (1LL << 62);  // bit 62: known (a zero device count stays known)
+        cache[slot][dev].store(v, std::memory_order_relaxed);
     }
-    return cache[slot][dev];
+    return {(int)((v >> 32) & 0x3fffffff), (int)(v & 0xffffffff)};
 }
 
 // Cluster shape of a position-by-position walk: W workgroups per request, each owning
 // `per_chunks` whole fine chunks of every row, with all B * W workgroups resident at once.
-inline void walk_shape(const KArgs& a, int cap, int* W_out, int* per_chunks_out) {
-    int W = std::min(kMaxCluster, std::max(1, cap / std::max(1, a.B)));
-    if (const char* env = std::getenv("SPEC_VERIFY_CLUSTER"))  // launch-shape sweeps
-        W = std::max(1, std::min(kMaxCluster, std::atoi(env)));
+// A requested width (spec_options.cluster) is clamped to what the device holds for the
+// batch.  A batch too large for the exit words walks with W = 1 (no hand-offs).
+inline void walk_shape(const KArgs& a, Resident cap, int want, int* W_out, int* per_chunks_out) {
+    int W = std::min(kMaxCluster, std::max(1, cap.walk / std::max(1, a.B)));
+    if (want > 0) W = std::max(1, std::min({kMaxCluster, want, cap.all / std::max(1, a.B)}));
+    if (a.B > kExitWords) W = 1;
     W = std::min(W, a.S2);
     const int per_chunks = (a.S2 + W - 1) / W;
     *W_out = (a.S2 + per_chunks - 1) / per_chunks;
@@ -3597,10 +3661,10 @@ inline void walk_shape(const KArgs& a, int cap, int* W_out, int* per_chunks_out)
 }
 
 template <typename T>
-int run_greedy_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
+int run_greedy_walk(KArgs& a, unsigned long long* xslots, const Opts& o, hipStream_t st) {
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_greedy_walk<T>),
-                                  sizeof(T) == 4 ? 0 : 1), &W, &per);
+                                  sizeof(T) == 4 ? 0 : 1), o.cluster, &W, &per);
     hipLaunchKernelGGL((k_greedy_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
                        per * kFine, a.hdr, W > 1 ? xslots : (unsigned long long*)nullptr,
                        a.R * W * 3);
@@ -3608,12 +3672,13 @@ int run_greedy_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
 }
 
 template <typename T>
-int run_chain_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
-    a.walk_temporal = 1;  // keeps the slice of the row drawn from near for the final weights
-    if (const char* env = std::getenv("SPEC_VERIFY_TEMPORAL")) a.walk_temporal = std::atoi(env);
+int run_chain_walk(KArgs& a, unsigned long long* xslots, const Opts& o, hipStream_t st) {
+    // cache-allocating row loads keep the slice of the row drawn from near for the final
+    // weights (the default)
+    a.walk_temporal = o.cached ? 1 : 0;
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_chain_walk<T>),
-                                  sizeof(T) == 4 ? 2 : 3), &W, &per);
+                                  sizeof(T) == 4 ? 2 : 3), o.cluster, &W, &per);
     a.walk_draw = per <= 64 ? 1 : 0;  // a slice's chunk masses fit one wave: draw in the walk
     // hand-off steps: one per position, then the slice totals (and their fallback)
     hipLaunchKernelGGL((k_chain_walk<T>), dim3(a.B * W), dim3(kBlock), 0, st, a, W,
@@ -3625,13 +3690,8 @@ int run_chain_walk(KArgs& a, unsigned long long* xslots, hipStream_t st) {
     return launch_status();
 }
 
-// The eager passes (every row streamed, then merged) instead of the walks; kept for
-// comparison and selected by SPEC_VERIFY_EAGER=1.
-inline bool eager_forced() {
-    const char* e = std::getenv("SPEC_VERIFY_EAGER");
-    return e && std::atoi(e) != 0;
-}
-
+// The eager passes (every row streamed, then merged) instead of the walks: selected with
+// spec_options.path = SPEC_PATH_EAGER.
 template <typename T>
 int run_greedy(KArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_rows<T, false>), dim3(a.B * a.R * a.S), dim3(kBlock), 0, st, a);
@@ -3662,10 +3722,11 @@ int run_chain(KArgs& a, hipStream_t st) {
 }
 
 template <typename T>
-int run_tree_walk(KArgs& a, int sampling, unsigned long long* xslots, hipStream_t st) {
+int run_tree_walk(KArgs& a, int sampling, unsigned long long* xslots, const Opts& o,
+                  hipStream_t st) {
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_tree_walk<T>),
-                                  sizeof(T) == 4 ? 4 : 5), &W, &per);
+                                  sizeof(T) == 4 ? 4 : 5), o.cluster, &W, &per);
     W = std::min(W, tree_cluster_max(a.B));
     per = (a.S2 + W - 1) / W;
     W = (a.S2 + per - 1) / per;
@@ -3693,10 +3754,10 @@ int run_tree(KArgs& a, int sampling, hipStream_t st) {
 }
 
 template <typename T>
-int run_tree_mss(KArgs& a, unsigned long long* xslots, hipStream_t st) {
+int run_tree_mss(KArgs& a, unsigned long long* xslots, const Opts& o, hipStream_t st) {
     int W, per;
     walk_shape(a, resident_blocks(reinterpret_cast<const void*>(&k_mss_walk<T>),
-                                  sizeof(T) == 4 ? 6 : 7), &W, &per);
+                                  sizeof(T) == 4 ? 6 : 7), o.cluster, &W, &per);
     W = std::min(W, tree_cluster_max(a.B));
     per = (a.S2 + W - 1) / W;
     W = (a.S2 + per - 1) / per;
@@ -3794,13 +3855,16 @@ extern "C" const char* spec_status_str(int status) {
     }
 }
 
-extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
-                                  int B, int G, int V, int32_t* accept_len, int32_t* out_tokens,
-                                  void* workspace, size_t ws_bytes, void* stream) {
+extern "C" int spec_verify_greedy_opt(const void* logits, int dtype,
+                                      const int32_t* draft_tokens, int B, int G, int V,
+                                      int32_t* accept_len, int32_t* out_tokens, void* workspace,
+                                      size_t ws_bytes, void* stream, const spec_options* opt) {
     if (!draft_tokens || !accept_len || !out_tokens) return SPEC_ERR_NULL;
     if (G < 1 || G > SPEC_MAX_G) return SPEC_ERR_SHAPE;
     int rc = check_common(logits, dtype, B, V, workspace, ws_bytes, SPEC_OP_GREEDY, G + 1);
+    if (rc == SPEC_OK) rc = check_opts(opt);
     if (rc != SPEC_OK || B == 0) return rc;
+    const Opts o = resolve(opt);
     KArgs a = {};
     a.logits = logits;
     a.tokens = draft_tokens;
@@ -3809,30 +3873,41 @@ extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* 
     a.V = V;
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
-    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    a.spin = o.spin;
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2, o);
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_GREEDY);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!eager_forced()) {
+    if (!o.eager) {
         const Layout L = layout_for(SPEC_OP_GREEDY, B, G + 1, V);
         unsigned long long* xs =
             reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
-        return dtype == SPEC_F32 ? run_greedy_walk<float>(a, xs, st)
-                                 : run_greedy_walk<uint16_t>(a, xs, st);
+        return dtype == SPEC_F32 ? run_greedy_walk<float>(a, xs, o, st)
+                                 : run_greedy_walk<uint16_t>(a, xs, o, st);
     }
     return dtype == SPEC_F32 ? run_greedy<float>(a, st) : run_greedy<uint16_t>(a, st);
 }
 
-extern "C" int spec_verify_chain(const void* logits, int dtype, const float* draft_probs,
-                                 const int32_t* draft_tokens, const float* coins,
-                                 const float* temperature, int B, int G, int V,
-                                 int32_t* accept_len, int32_t* out_tokens, float* probs_out,
-                                 void* workspace, size_t ws_bytes, void* stream) {
+extern "C" int spec_verify_greedy(const void* logits, int dtype, const int32_t* draft_tokens,
+                                  int B, int G, int V, int32_t* accept_len, int32_t* out_tokens,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+    return spec_verify_greedy_opt(logits, dtype, draft_tokens, B, G, V, accept_len, out_tokens,
+                                  workspace, ws_bytes, stream, nullptr);
+}
+
+extern "C" int spec_verify_chain_opt(const void* logits, int dtype, const float* draft_probs,
+                                     const int32_t* draft_tokens, const float* coins,
+                                     const float* temperature, int B, int G, int V,
+                                     int32_t* accept_len, int32_t* out_tokens, float* probs_out,
+                                     void* workspace, size_t ws_bytes, void* stream,
+                                     const spec_options* opt) {
     if (!draft_probs || !draft_tokens || !coins || !temperature || !accept_len || !out_tokens)
         return SPEC_ERR_NULL;
     if (G < 1 || G > SPEC_MAX_G) return SPEC_ERR_SHAPE;
     int rc = check_common(logits, dtype, B, V, workspace, ws_bytes, SPEC_OP_CHAIN, G + 1);
+    if (rc == SPEC_OK) rc = check_opts(opt);
     if (rc != SPEC_OK || B == 0) return rc;
+    const Opts o = resolve(opt);
     if (((uintptr_t)draft_probs) % 4) return SPEC_ERR_PARAM;
     KArgs a = {};
     a.logits = logits;
@@ -3847,27 +3922,38 @@ extern "C" int spec_verify_chain(const void* logits, int dtype, const float* dra
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
     a.probs = probs_out;
-    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    a.spin = o.spin;
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2, o);
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_CHAIN);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!eager_forced()) {
+    if (!o.eager) {
         const Layout L = layout_for(SPEC_OP_CHAIN, B, G + 1, V);
         unsigned long long* xs =
             reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
-        return dtype == SPEC_F32 ? run_chain_walk<float>(a, xs, st)
-                                 : run_chain_walk<uint16_t>(a, xs, st);
+        return dtype == SPEC_F32 ? run_chain_walk<float>(a, xs, o, st)
+                                 : run_chain_walk<uint16_t>(a, xs, o, st);
     }
     return dtype == SPEC_F32 ? run_chain<float>(a, st) : run_chain<uint16_t>(a, st);
 }
 
-extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
-                                const int32_t* parents, const float* coins,
-                                const float* temperature, int B, int N, int V, int D, int mode,
-                                float threshold_single, float threshold_acc,
-                                int32_t* accept_len, int32_t* out_tokens,
-                                int32_t* accepted_nodes, float* probs_out, void* workspace,
-                                size_t ws_bytes, void* stream) {
+extern "C" int spec_verify_chain(const void* logits, int dtype, const float* draft_probs,
+                                 const int32_t* draft_tokens, const float* coins,
+                                 const float* temperature, int B, int G, int V,
+                                 int32_t* accept_len, int32_t* out_tokens, float* probs_out,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+    return spec_verify_chain_opt(logits, dtype, draft_probs, draft_tokens, coins, temperature, B,
+                                 G, V, accept_len, out_tokens, probs_out, workspace, ws_bytes,
+                                 stream, nullptr);
+}
+
+extern "C" int spec_verify_tree_opt(const void* logits, int dtype, const int32_t* node_tokens,
+                                    const int32_t* parents, const float* coins,
+                                    const float* temperature, int B, int N, int V, int D,
+                                    int mode, float threshold_single, float threshold_acc,
+                                    int32_t* accept_len, int32_t* out_tokens,
+                                    int32_t* accepted_nodes, float* probs_out, void* workspace,
+                                    size_t ws_bytes, void* stream, const spec_options* opt) {
     if (!node_tokens || !parents || !accept_len || !out_tokens || !accepted_nodes)
         return SPEC_ERR_NULL;
     if (mode != SPEC_TREE_GREEDY && mode != SPEC_TREE_SAMPLING) return SPEC_ERR_PARAM;
@@ -3877,7 +3963,9 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     }
     if (N < 1 || N > SPEC_MAX_N || D < 1 || D > SPEC_MAX_N) return SPEC_ERR_SHAPE;
     int rc = check_common(logits, dtype, B, V, workspace, ws_bytes, SPEC_OP_TREE, N);
+    if (rc == SPEC_OK) rc = check_opts(opt);
     if (rc != SPEC_OK || B == 0) return rc;
+    const Opts o = resolve(opt);
     KArgs a = {};
     a.logits = logits;
     a.tokens = node_tokens;
@@ -3895,32 +3983,48 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* no
     a.out_tokens = out_tokens;
     a.accepted_nodes = accepted_nodes;
     a.probs = probs_out;
-    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    a.spin = o.spin;
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2, o);
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_TREE);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!eager_forced()) {
+    if (!o.eager) {
         const Layout L = layout_for(SPEC_OP_TREE, B, N, V);
         unsigned long long* xs =
             reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
-        return dtype == SPEC_F32 ? run_tree_walk<float>(a, mode, xs, st)
-                                 : run_tree_walk<uint16_t>(a, mode, xs, st);
+        return dtype == SPEC_F32 ? run_tree_walk<float>(a, mode, xs, o, st)
+                                 : run_tree_walk<uint16_t>(a, mode, xs, o, st);
     }
     return dtype == SPEC_F32 ? run_tree<float>(a, mode, st) : run_tree<uint16_t>(a, mode, st);
 }
 
-extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* draft_probs,
-                                    const int32_t* node_tokens, const int32_t* parents,
-                                    const float* coins, const float* temperature, int B, int N,
-                                    int V, int D, int32_t* accept_len, int32_t* out_tokens,
-                                    int32_t* accepted_nodes, float* probs_out, void* workspace,
-                                    size_t ws_bytes, void* stream) {
+extern "C" int spec_verify_tree(const void* logits, int dtype, const int32_t* node_tokens,
+                                const int32_t* parents, const float* coins,
+                                const float* temperature, int B, int N, int V, int D, int mode,
+                                float threshold_single, float threshold_acc,
+                                int32_t* accept_len, int32_t* out_tokens,
+                                int32_t* accepted_nodes, float* probs_out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    return spec_verify_tree_opt(logits, dtype, node_tokens, parents, coins, temperature, B, N, V,
+                                D, mode, threshold_single, threshold_acc, accept_len, out_tokens,
+                                accepted_nodes, probs_out, workspace, ws_bytes, stream, nullptr);
+}
+
+extern "C" int spec_verify_tree_mss_opt(const void* logits, int dtype, const float* draft_probs,
+                                        const int32_t* node_tokens, const int32_t* parents,
+                                        const float* coins, const float* temperature, int B,
+                                        int N, int V, int D, int32_t* accept_len,
+                                        int32_t* out_tokens, int32_t* accepted_nodes,
+                                        float* probs_out, void* workspace, size_t ws_bytes,
+                                        void* stream, const spec_options* opt) {
     if (!draft_probs || !node_tokens || !parents || !coins || !temperature || !accept_len ||
         !out_tokens || !accepted_nodes)
         return SPEC_ERR_NULL;
     if (N < 1 || N > SPEC_MAX_N || D < 1 || D > SPEC_MAX_N) return SPEC_ERR_SHAPE;
     int rc = check_common(logits, dtype, B, V, workspace, ws_bytes, SPEC_OP_TREE_MSS, N);
+    if (rc == SPEC_OK) rc = check_opts(opt);
     if (rc != SPEC_OK || B == 0) return rc;
+    const Opts o = resolve(opt);
     if (((uintptr_t)draft_probs) % 4) return SPEC_ERR_PARAM;
     KArgs a = {};
     a.logits = logits;
@@ -3938,15 +4042,28 @@ extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* 
     a.out_tokens = out_tokens;
     a.accepted_nodes = accepted_nodes;
     a.probs = probs_out;
-    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    a.spin = o.spin;
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2, o);
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_TREE_MSS);
     const Layout L = layout_for(SPEC_OP_TREE_MSS, B, N, V);
     unsigned long long* xslots =
         reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + L.xch);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return dtype == SPEC_F32 ? run_tree_mss<float>(a, xslots, st)
-                             : run_tree_mss<uint16_t>(a, xslots, st);
+    return dtype == SPEC_F32 ? run_tree_mss<float>(a, xslots, o, st)
+                             : run_tree_mss<uint16_t>(a, xslots, o, st);
+}
+
+extern "C" int spec_verify_tree_mss(const void* logits, int dtype, const float* draft_probs,
+                                    const int32_t* node_tokens, const int32_t* parents,
+                                    const float* coins, const float* temperature, int B, int N,
+                                    int V, int D, int32_t* accept_len, int32_t* out_tokens,
+                                    int32_t* accepted_nodes, float* probs_out, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+    return spec_verify_tree_mss_opt(logits, dtype, draft_probs, node_tokens, parents, coins,
+                                    temperature, B, N, V, D, accept_len, out_tokens,
+                                    accepted_nodes, probs_out, workspace, ws_bytes, stream,
+                                    nullptr);
 }
 
 extern "C" int spec_tree_mask(const int32_t* parents, const int32_t* base_pos, int B, int N,
@@ -4010,7 +4127,7 @@ extern "C" int spec_verify_chain_filtered(const void* logits, const void* draft_
     int lv = 0;
     while ((1L << lv) < (long)V) ++lv;
     a.fixbits = 62 - lv;
-    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2);
+    rc = setup_shapes(a, dtype == SPEC_F32 ? 4 : 2, resolve(nullptr));
     if (rc != SPEC_OK) return rc;
     bind_workspace(a, workspace, SPEC_OP_CHAIN_FILTERED);
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -42,9 +42,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, ip = ctypes.c_void_p, ctypes.c_int
         L.oracle_verify_greedy.argtypes = [vp, ip, vp, ip, ip, ip, vp, vp]
-        L.oracle_verify_chain.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp, vp, vp]
+        L.oracle_verify_chain.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp, vp, vp,
+                                          vp]
         L.oracle_verify_tree.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, ip,
-                                         ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp]
+                                         ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp, vp]
         for f in (L.oracle_verify_greedy, L.oracle_verify_chain, L.oracle_verify_tree):
             f.restype = ctypes.c_int
         L.oracle_tree_mask.argtypes = [vp, vp, ip, ip, vp, vp]
@@ -52,18 +53,25 @@ def lib():
         L.oracle_tree_commit_kv.argtypes = [vp, vp, ip, ip, ip, vp, vp, ctypes.c_size_t, vp]
         L.oracle_tree_commit_kv.restype = ctypes.c_int
         L.oracle_verify_chain_filtered.argtypes = [vp, vp, ip, vp, vp, vp, vp, vp, ip, ip, ip,
-                                                   vp, vp, vp, vp]
+                                                   vp, vp, vp, vp, vp]
         L.oracle_verify_chain_filtered.restype = ctypes.c_int
         L.oracle_verify_tree_mss.argtypes = [vp, ip, vp, vp, vp, vp, vp, ip, ip, ip, ip,
-                                             vp, vp, vp, vp, vp]
+                                             vp, vp, vp, vp, vp, vp]
         L.oracle_verify_tree_mss.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ip]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for this Python thread's later oracle calls."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _ptr(a):
@@ -102,7 +110,7 @@ def verify_greedy(logits, dtype, draft_tokens, B=None, G=None, V=None):
 
 
 def verify_chain(logits, dtype, draft_probs, draft_tokens, coins, temperature, *, beta=False):
-    """Returns dict(accept_len, out_tokens, probs, margin[, beta])."""
+    """Returns dict(accept_len, out_tokens, probs, margin, accept_margin[, beta])."""
     lg = _logits_array(logits, dtype)
     q = np.ascontiguousarray(draft_probs, dtype=np.float32)
     dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
@@ -114,13 +122,14 @@ def verify_chain(logits, dtype, draft_probs, draft_tokens, coins, temperature, *
     out = np.empty((B, G + 1), np.int32)
     probs = np.empty((B, G + 1), np.float64)
     margin = np.empty(B, np.float64)
+    amargin = np.empty(B, np.float64)
     bt = np.empty((B, G), np.float64) if beta else None
     rc = lib().oracle_verify_chain(_ptr(lg), _dtype_code(dtype), _ptr(q), _ptr(dt), _ptr(cn),
                                    _ptr(tp), B, G, V, _ptr(acc), _ptr(out), _ptr(probs),
-                                   _ptr(margin), _ptr(bt))
+                                   _ptr(margin), _ptr(bt), _ptr(amargin))
     if rc != 0:
         raise ValueError(f"oracle_verify_chain rejected its arguments ({rc})")
-    res = dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin)
+    res = dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin, accept_margin=amargin)
     if beta:
         res["beta"] = bt
     return res
@@ -128,7 +137,7 @@ def verify_chain(logits, dtype, draft_probs, draft_tokens, coins, temperature, *
 
 def verify_tree(logits, dtype, node_tokens, parents, coins, temperature, D, mode,
                 threshold_single=1.0, threshold_acc=1.0):
-    """Returns dict(accept_len, out_tokens, accepted_nodes, probs, margin)."""
+    """Returns dict(accept_len, out_tokens, accepted_nodes, probs, margin, accept_margin)."""
     lg = _logits_array(logits, dtype)
     tk = np.ascontiguousarray(node_tokens, dtype=np.int32)
     pa = np.ascontiguousarray(parents, dtype=np.int32)
@@ -141,14 +150,15 @@ def verify_tree(logits, dtype, node_tokens, parents, coins, temperature, D, mode
     nodes = np.empty((B, D), np.int32)
     probs = np.empty((B, D + 1), np.float64)
     margin = np.empty(B, np.float64)
+    amargin = np.empty(B, np.float64)
     rc = lib().oracle_verify_tree(_ptr(lg), _dtype_code(dtype), _ptr(tk), _ptr(pa), _ptr(cn),
                                   _ptr(tp), B, N, V, D, mode, float(threshold_single),
                                   float(threshold_acc), _ptr(acc), _ptr(out), _ptr(nodes),
-                                  _ptr(probs), _ptr(margin))
+                                  _ptr(probs), _ptr(margin), _ptr(amargin))
     if rc != 0:
         raise ValueError(f"oracle_verify_tree rejected its arguments ({rc})")
     return dict(accept_len=acc, out_tokens=out, accepted_nodes=nodes, probs=probs,
-                margin=margin)
+                margin=margin, accept_margin=amargin)
 
 
 def tree_mask(parents, base_pos=None):
@@ -185,7 +195,7 @@ def tree_commit_kv(accepted_nodes, accept_len, kv_tree, kv_out):
 
 def verify_chain_filtered(logits, draft_logits, dtype, draft_tokens, coins, temperature,
                           top_k=None, top_p=None):
-    """Returns dict(accept_len, out_tokens, probs, margin)."""
+    """Returns dict(accept_len, out_tokens, probs, margin, accept_margin)."""
     lg = _logits_array(logits, dtype)
     dl = _logits_array(draft_logits, dtype)
     dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
@@ -199,17 +209,20 @@ def verify_chain_filtered(logits, draft_logits, dtype, draft_tokens, coins, temp
     out = np.empty((B, G + 1), np.int32)
     probs = np.empty((B, G + 1), np.float64)
     margin = np.empty(B, np.float64)
+    amargin = np.empty(B, np.float64)
     rc = lib().oracle_verify_chain_filtered(_ptr(lg), _ptr(dl), _dtype_code(dtype), _ptr(dt),
                                             _ptr(cn), _ptr(tp), _ptr(tk), _ptr(pp), B, G, V,
-                                            _ptr(acc), _ptr(out), _ptr(probs), _ptr(margin))
+                                            _ptr(acc), _ptr(out), _ptr(probs), _ptr(margin),
+                                            _ptr(amargin))
     if rc != 0:
         raise ValueError(f"oracle_verify_chain_filtered rejected its arguments ({rc})")
-    return dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin)
+    return dict(accept_len=acc, out_tokens=out, probs=probs, margin=margin, accept_margin=amargin)
 
 
 def verify_tree_mss(logits, dtype, draft_probs, node_tokens, parents, coins, temperature, D):
     """Tree verify by multi-step speculative sampling with draft rows [B][N][V] and per-node
-    coins [B][N].  Returns dict(accept_len, out_tokens, accepted_nodes, probs, margin)."""
+    coins [B][N].  Returns dict(accept_len, out_tokens, accepted_nodes, probs, margin,
+    accept_margin)."""
     lg = _logits_array(logits, dtype)
     q = np.ascontiguousarray(draft_probs, dtype=np.float32)
     tk = np.ascontiguousarray(node_tokens, dtype=np.int32)
@@ -223,10 +236,11 @@ def verify_tree_mss(logits, dtype, draft_probs, node_tokens, parents, coins, tem
     nodes = np.empty((B, D), np.int32)
     probs = np.empty((B, D + 1), np.float64)
     margin = np.empty(B, np.float64)
+    amargin = np.empty(B, np.float64)
     rc = lib().oracle_verify_tree_mss(_ptr(lg), _dtype_code(dtype), _ptr(q), _ptr(tk), _ptr(pa),
                                       _ptr(cn), _ptr(tp), B, N, V, D, _ptr(acc), _ptr(out),
-                                      _ptr(nodes), _ptr(probs), _ptr(margin))
+                                      _ptr(nodes), _ptr(probs), _ptr(margin), _ptr(amargin))
     if rc != 0:
         raise ValueError(f"oracle_verify_tree_mss rejected its arguments ({rc})")
     return dict(accept_len=acc, out_tokens=out, accepted_nodes=nodes, probs=probs,
-                margin=margin)
+                margin=margin, accept_margin=amargin)

@@ -196,7 +196,7 @@ int oracle_verify_greedy(const void* logits, int dtype, const int32_t* draft_tok
 static void chain_one(const void* logits, int dtype, const float* q, const int32_t* draft,
                       const float* coins, float temperature, int G, int V, size_t b,
                       int32_t* accept_len, int32_t* out, double* probs, double* margin,
-                      double* beta, double* w) {
+                      double* amargin, double* beta, double* w) {
     int R = G + 1;
     double T = (double)temperature;
     double m[R > 0 ? R : 1], Z[R > 0 ? R : 1];
@@ -207,6 +207,7 @@ static void chain_one(const void* logits, int dtype, const float* q, const int32
     int k = G;
     double pacc[R > 0 ? R : 1];
     *margin = INFINITY;
+    if (amargin) *amargin = INFINITY;
     for (int i = 0; i <= G && valid; ++i) {
         Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);
         m[i] = row_max(r);
@@ -245,6 +246,7 @@ static void chain_one(const void* logits, int dtype, const float* q, const int32
     }
     if (!valid) {
         *margin = INFINITY;
+        if (amargin) *amargin = INFINITY;
         *accept_len = -1;
         for (int i = 0; i < R; ++i) out[i] = -1;
         if (probs)
@@ -287,6 +289,7 @@ static void chain_one(const void* logits, int dtype, const float* q, const int32
         S += w[x];
     }
     if (k < G) note_margin(margin, S);
+    if (amargin) *amargin = *margin; /* every margin so far: the tests before the draw */
     if (!(S > 0.0))
         for (int x = 0; x < V; ++x) w[x] = row_prob(rk, x, m[k], Z[k], T);
     int y = draw_inverse_cdf(w, V, (double)coins[G], margin);
@@ -306,7 +309,7 @@ int oracle_verify_chain(const void* logits, int dtype, const float* draft_probs,
                         const int32_t* draft_tokens, const float* coins,
                         const float* temperature, int B, int G, int V,
                         int32_t* accept_len, int32_t* out_tokens, double* probs_out,
-                        double* min_margin, double* beta_out) {
+                        double* min_margin, double* beta_out, double* accept_margin) {
     if (!logits || !draft_probs || !draft_tokens || !coins || !temperature || !accept_len ||
         !out_tokens || !min_margin)
         return -1;
@@ -320,7 +323,8 @@ int oracle_verify_chain(const void* logits, int dtype, const float* draft_probs,
             chain_one(logits, dtype, draft_probs + (size_t)b * G * V, draft_tokens + (size_t)b * G,
                       coins + (size_t)b * R, temperature[b], G, V, (size_t)b, accept_len + b,
                       out_tokens + (size_t)b * R, probs_out ? probs_out + (size_t)b * R : NULL,
-                      min_margin + b, beta_out ? beta_out + (size_t)b * G : NULL, w);
+                      min_margin + b, accept_margin ? accept_margin + b : NULL,
+                      beta_out ? beta_out + (size_t)b * G : NULL, w);
         free(w);
     }
     return 0;
@@ -341,8 +345,8 @@ int oracle_verify_chain(const void* logits, int dtype, const float* draft_probs,
 static void tree_one(const void* logits, int dtype, const int32_t* tok, const int32_t* par,
                      const float* coins, float temperature, int N, int V, int D, int mode,
                      double th_single, double th_acc, size_t b, int32_t* accept_len,
-                     int32_t* out, int32_t* nodes, double* probs, double* margin, double* w,
-                     int* depth, int32_t* excl) {
+                     int32_t* out, int32_t* nodes, double* probs, double* margin,
+                     double* amargin, double* w, int* depth, int32_t* excl) {
     int sampling = mode == ORACLE_TREE_SAMPLING;
     int valid = par[0] == -1;
     depth[0] = 0;
@@ -361,6 +365,7 @@ static void tree_one(const void* logits, int dtype, const int32_t* tok, const in
             if (!coin_ok(coins[d])) valid = 0;
     }
     *margin = INFINITY;
+    if (amargin) *amargin = INFINITY;
 
     double T = (double)temperature;
     int cur = 0, d = 0, nexcl = 0;
@@ -432,6 +437,7 @@ static void tree_one(const void* logits, int dtype, const int32_t* tok, const in
         for (int e = 0; e < nexcl; ++e) w[excl[e]] = 0.0;
         for (int x = 0; x < V; ++x) S += w[x];
         if (nexcl > 0) note_margin(margin, S);
+        if (amargin) *amargin = *margin; /* every margin so far: the tests before the draw */
         if (!(S > 0.0))
             for (int x = 0; x < V; ++x) w[x] = row_prob(r, x, m, Z, T);
         y = draw_inverse_cdf(w, V, (double)coins[D], margin);
@@ -450,7 +456,8 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
                        const int32_t* parents, const float* coins, const float* temperature,
                        int B, int N, int V, int D, int mode, float threshold_single,
                        float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
-                       int32_t* accepted_nodes, double* probs_out, double* min_margin) {
+                       int32_t* accepted_nodes, double* probs_out, double* min_margin,
+                       double* accept_margin) {
     if (!logits || !node_tokens || !parents || !accept_len || !out_tokens || !accepted_nodes ||
         !min_margin)
         return -1;
@@ -472,8 +479,8 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
                      (double)threshold_single, (double)threshold_acc, (size_t)b,
                      accept_len + b, out_tokens + (size_t)b * (D + 1),
                      accepted_nodes + (size_t)b * D,
-                     probs_out ? probs_out + (size_t)b * (D + 1) : NULL, min_margin + b, w,
-                     depth, excl);
+                     probs_out ? probs_out + (size_t)b * (D + 1) : NULL, min_margin + b,
+                     accept_margin ? accept_margin + b : NULL, w, depth, excl);
         free(w);
         free(depth);
         free(excl);
@@ -500,7 +507,8 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
 static void tree_mss_one(const void* logits, int dtype, const float* q, const int32_t* tok,
                          const int32_t* par, const float* coins, float temperature, int N,
                          int V, int D, size_t b, int32_t* accept_len, int32_t* out,
-                         int32_t* nodes, double* probs, double* margin, double* w, int* depth) {
+                         int32_t* nodes, double* probs, double* margin, double* amargin,
+                         double* w, int* depth) {
     int valid = par[0] == -1 && temperature_ok(temperature);
     depth[0] = 0;
     for (int i = 1; i < N && valid; ++i) {
@@ -520,6 +528,7 @@ static void tree_mss_one(const void* logits, int dtype, const float* q, const in
     for (int c = 0; c < N && valid; ++c)
         if (!coin_ok(coins[c])) valid = 0;
     *margin = INFINITY;
+    if (amargin) *amargin = INFINITY;
 
     double T = (double)temperature;
     int cur = 0, d = 0;
@@ -583,6 +592,7 @@ static void tree_mss_one(const void* logits, int dtype, const float* q, const in
     }
 
     Row r = row_of(logits, dtype, b * (size_t)N + (size_t)cur, V);
+    if (amargin) *amargin = *margin; /* every margin so far: the tests before the draw */
     int y = draw_inverse_cdf(w, V, (double)coins[N - 1], margin);
     out[d] = y;
     if (probs) probs[d] = row_prob(r, y, m, Z, T);
@@ -597,7 +607,8 @@ int oracle_verify_tree_mss(const void* logits, int dtype, const float* draft_pro
                            const int32_t* node_tokens, const int32_t* parents,
                            const float* coins, const float* temperature, int B, int N, int V,
                            int D, int32_t* accept_len, int32_t* out_tokens,
-                           int32_t* accepted_nodes, double* probs_out, double* min_margin) {
+                           int32_t* accepted_nodes, double* probs_out, double* min_margin,
+                           double* accept_margin) {
     if (!logits || !draft_probs || !node_tokens || !parents || !coins || !temperature ||
         !accept_len || !out_tokens || !accepted_nodes || !min_margin)
         return -1;
@@ -613,8 +624,8 @@ int oracle_verify_tree_mss(const void* logits, int dtype, const float* draft_pro
                          coins + (size_t)b * N, temperature[b], N, V, D, (size_t)b,
                          accept_len + b, out_tokens + (size_t)b * (D + 1),
                          accepted_nodes + (size_t)b * D,
-                         probs_out ? probs_out + (size_t)b * (D + 1) : NULL, min_margin + b, w,
-                         depth);
+                         probs_out ? probs_out + (size_t)b * (D + 1) : NULL, min_margin + b,
+                         accept_margin ? accept_margin + b : NULL, w, depth);
         free(w);
         free(depth);
     }
@@ -684,7 +695,8 @@ static void chain_filtered_one(const void* logits, const void* dlogits, int dtyp
                                const int32_t* draft, const float* coins, float temperature,
                                int top_k, float top_p, int G, int V, size_t b,
                                int32_t* accept_len, int32_t* out, double* probs,
-                               double* margin, double* wp, double* wq, double* tmp) {
+                               double* margin, double* amargin, double* wp, double* wq,
+                               double* tmp) {
     int R = G + 1;
     double T = (double)temperature;
     double tp = (double)top_p;
@@ -703,6 +715,7 @@ static void chain_filtered_one(const void* logits, const void* dlogits, int dtyp
         if (mq[i] == -INFINITY) valid = 0;
     }
     *margin = INFINITY;
+    if (amargin) *amargin = INFINITY;
     if (!valid) {
         *accept_len = -1;
         for (int i = 0; i < R; ++i) out[i] = -1;
@@ -748,6 +761,7 @@ static void chain_filtered_one(const void* logits, const void* dlogits, int dtyp
         }
         note_margin(margin, S);
     }
+    if (amargin) *amargin = *margin; /* every margin so far: the tests before the draw */
     double* w = (k < G && S > 0.0) ? wq : wp;
     int y = draw_inverse_cdf(w, V, (double)coins[G], margin);
     for (int i = 0; i < k; ++i) out[i] = draft[i];
@@ -765,7 +779,8 @@ int oracle_verify_chain_filtered(const void* logits, const void* draft_logits, i
                                  const int32_t* draft_tokens, const float* coins,
                                  const float* temperature, const int32_t* top_k,
                                  const float* top_p, int B, int G, int V, int32_t* accept_len,
-                                 int32_t* out_tokens, double* probs_out, double* min_margin) {
+                                 int32_t* out_tokens, double* probs_out, double* min_margin,
+                                 double* accept_margin) {
     if (!logits || !draft_logits || !draft_tokens || !coins || !temperature || !accept_len ||
         !out_tokens || !min_margin)
         return -1;
@@ -782,8 +797,8 @@ int oracle_verify_chain_filtered(const void* logits, const void* draft_logits, i
                                coins + (size_t)b * R, temperature[b], top_k ? top_k[b] : 0,
                                top_p ? top_p[b] : 1.0f, G, V, (size_t)b, accept_len + b,
                                out_tokens + (size_t)b * R,
-                               probs_out ? probs_out + (size_t)b * R : NULL, min_margin + b, wp,
-                               wq, tmp);
+                               probs_out ? probs_out + (size_t)b * R : NULL, min_margin + b,
+                               accept_margin ? accept_margin + b : NULL, wp, wq, tmp);
         free(wp);
         free(wq);
         free(tmp);
@@ -874,5 +889,13 @@ int oracle_num_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

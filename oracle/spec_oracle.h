@@ -8,11 +8,26 @@
  * (dtype 0) or as raw bf16 bit patterns (dtype 1).  Everything is widened to double;
  * sums run sequentially in ascending index order; exp() is libm's double exp.
  *
- * min_margin[b] receives the smallest distance, in probability units, between a coin
- * and the threshold it was compared against along request b's decision trace (the
- * accept tests, the tree's sibling tests and the final inverse-CDF step), or +inf when
- * no coin decided anything (greedy).  A request whose margin is below a small band can
+ * min_margin[b] receives the smallest distance between a coin and the threshold it was
+ * compared against along request b's decision trace, or +inf when no coin decided
+ * anything (greedy, invalid requests).  The distances are: |u - p/q| for an acceptance
+ * test (ratio units, the coin's own scale); |u - prob_acc/threshold_acc| and
+ * |p - threshold_single| for a tree sibling; the residual mass S itself where a residual
+ * is formed (a mass near 0 decides between the residual and the fallback); the distance
+ * of the top-p target to the ends of its boundary group (filtered calls, as a fraction
+ * of the row's mass); and for the final inverse-CDF draw, the distances from t = u * S
+ * to both ends of the chosen token's step, in WEIGHT units (probability mass), i.e. S
+ * times the coin-space distance.  The draw's distance is kept in weight units because
+ * that is the scale on which another implementation's rounding acts: a prefix sum of
+ * fp32 weights is off by a small absolute amount of mass, whatever S is; and since
+ * S <= 1 it is never larger than the coin-space distance, so the band it defines
+ * contains every coin-space near-tie.  A request whose margin is below a small band can
  * legitimately come out differently under another rounding order.
+ *
+ * accept_margin[b] (every verify call; may be NULL) receives the same minimum over the
+ * decision trace without the final draw's distances: the margin of everything that
+ * decides how many drafts are accepted and which row and weights the last token is drawn
+ * from.  min_margin[b] = min(accept_margin[b], the final draw's distance).
  *
  * Invalid requests (a token outside [0,V), a temperature that is not finite and > 0, a
  * coin outside (0,1], a row whose maximum is -inf, a drafted token whose q is negative
@@ -47,7 +62,7 @@ int oracle_verify_chain(const void* logits, int dtype, const float* draft_probs,
                         const int32_t* draft_tokens, const float* coins,
                         const float* temperature, int B, int G, int V,
                         int32_t* accept_len, int32_t* out_tokens, double* probs_out,
-                        double* min_margin, double* beta_out);
+                        double* min_margin, double* beta_out, double* accept_margin);
 
 /* Token-tree verify, target-only.  mode 0 = greedy, mode 1 = sampling.
  * out_tokens [B][D+1], accepted_nodes [B][D], probs_out [B][D+1] (may be NULL). */
@@ -55,7 +70,8 @@ int oracle_verify_tree(const void* logits, int dtype, const int32_t* node_tokens
                        const int32_t* parents, const float* coins, const float* temperature,
                        int B, int N, int V, int D, int mode, float threshold_single,
                        float threshold_acc, int32_t* accept_len, int32_t* out_tokens,
-                       int32_t* accepted_nodes, double* probs_out, double* min_margin);
+                       int32_t* accepted_nodes, double* probs_out, double* min_margin,
+                       double* accept_margin);
 
 /* Token-tree verify by multi-step speculative sampling with draft distributions:
  * draft_probs [B][N][V] fp32 (row j = the distribution the children of node j were drawn
@@ -65,7 +81,8 @@ int oracle_verify_tree_mss(const void* logits, int dtype, const float* draft_pro
                            const int32_t* node_tokens, const int32_t* parents,
                            const float* coins, const float* temperature, int B, int N, int V,
                            int D, int32_t* accept_len, int32_t* out_tokens,
-                           int32_t* accepted_nodes, double* probs_out, double* min_margin);
+                           int32_t* accepted_nodes, double* probs_out, double* min_margin,
+                           double* accept_margin);
 
 /* Chain rejection sampling from target logits [B][G+1][V] and draft logits [B][G][V]
  * (same dtype), both at temperature T and both filtered with top_k[b] (NULL or <= 0 or
@@ -76,7 +93,8 @@ int oracle_verify_chain_filtered(const void* logits, const void* draft_logits, i
                                  const int32_t* draft_tokens, const float* coins,
                                  const float* temperature, const int32_t* top_k,
                                  const float* top_p, int B, int G, int V, int32_t* accept_len,
-                                 int32_t* out_tokens, double* probs_out, double* min_margin);
+                                 int32_t* out_tokens, double* probs_out, double* min_margin,
+                                 double* accept_margin);
 
 /* Tree attention mask: mask_bits [B][N][W], W = ceil(N/32); bit (j % 32) of word j / 32 of
  * row i is set iff node j lies on the path from node i to the root (i included).
@@ -96,6 +114,9 @@ int oracle_tree_commit_kv(const int32_t* accepted_nodes, const int32_t* accept_l
 
 /* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
 int oracle_num_threads(void);
+
+/* Threads for the calling thread's later oracle calls (n >= 1; no effect without OpenMP). */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -221,3 +221,52 @@ def test_c_consumer_is_built_and_checks_its_arguments():
     assert os.path.exists(demo), "build the package first"
     r = subprocess.run([demo], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+def test_options_are_checked_on_the_host(lib):
+    """The *_opt entry points reject bad launch options before anything is enqueued; NULL
+    options and all-zero options are the defaults."""
+    ws = L.workspace_bytes(L.SPEC_OP_CHAIN, 3, 5, 2000)
+
+    def chain(o):
+        return lib.spec_verify_chain_opt(P, L.SPEC_BF16, P, P, P, P, 0, 4, 2000, P, P, None, P, ws,
+                                         None, o)
+    assert chain(None) == L.SPEC_OK
+    assert chain(ctypes.byref(L.SpecOptions())) == L.SPEC_OK
+    for bad in (dict(path=2), dict(path=-1), dict(cluster=-1), dict(splits=-3),
+                dict(row_loads=3), dict(spin_limit=-1)):
+        o = L.SpecOptions(**bad)
+        assert chain(ctypes.byref(o)) == L.SPEC_ERR_PARAM, bad
+        assert lib.spec_verify_greedy_opt(P, L.SPEC_BF16, P, 0, 4, 1000, P, P, P,
+                                          L.workspace_bytes(L.SPEC_OP_GREEDY, 1, 5, 1000), None,
+                                          ctypes.byref(o)) == L.SPEC_ERR_PARAM, bad
+        assert lib.spec_verify_tree_opt(P, L.SPEC_F32, P, P, P, P, 0, 8, 500, 3, 1, 1.0, 1.0,
+                                        P, P, P, None, P,
+                                        L.workspace_bytes(L.SPEC_OP_TREE, 1, 8, 500), None,
+                                        ctypes.byref(o)) == L.SPEC_ERR_PARAM, bad
+        assert lib.spec_verify_tree_mss_opt(P, L.SPEC_F32, P, P, P, P, P, 0, 8, 500, 3, P, P, P,
+                                            None, P,
+                                            L.workspace_bytes(L.SPEC_OP_TREE_MSS, 1, 8, 500),
+                                            None, ctypes.byref(o)) == L.SPEC_ERR_PARAM, bad
+    # argument errors still come first
+    assert lib.spec_verify_chain_opt(None, L.SPEC_BF16, P, P, P, P, 3, 4, 2000, P, P, None, P, ws,
+                                     None, ctypes.byref(L.SpecOptions(path=9))) == L.SPEC_ERR_NULL
+
+
+def test_python_options_helper():
+    o = L.options(dict(path="eager", cluster=3, row_loads="streaming", spin_limit=7))
+    assert (o.path, o.cluster, o.splits, o.row_loads, o.spin_limit) == \
+        (L.SPEC_PATH_EAGER, 3, 0, L.SPEC_LOADS_STREAMING, 7)
+    assert L.options(None) is None
+    with pytest.raises(ValueError):
+        L.options(dict(eager=1))
+
+
+def test_workspace_header_is_shape_independent(lib):
+    """The walks' call counter and per-request exit words sit in a header of fixed size at
+    the start of every workspace, so one zero-filled buffer can serve calls of any shape
+    in turn: the smallest workspace of every kind is at least that header."""
+    sizes = [L.workspace_bytes(op, 1, r, 1) for op, r in
+             ((L.SPEC_OP_GREEDY, 2), (L.SPEC_OP_CHAIN, 2), (L.SPEC_OP_TREE, 1),
+              (L.SPEC_OP_CHAIN_FILTERED, 2), (L.SPEC_OP_TREE_MSS, 1))]
+    assert min(sizes) >= 256 + 4 * 4096

@@ -19,6 +19,7 @@ import scipy.special
 import scipy.stats
 
 import oracle
+import parity_log
 from lossless_rejection_sampling_verify_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -26,6 +27,21 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 BAND = 1e-6
 PROB_RTOL = 1e-5
+
+# Launch options the runners below pass to the library (spec_options fields); the
+# `launch` fixture sets them for one test and clears them afterwards.
+RUN_OPTS: dict = {}
+
+
+@pytest.fixture
+def launch():
+    RUN_OPTS.clear()
+    yield RUN_OPTS
+    RUN_OPTS.clear()
+
+
+def _opts():
+    return dict(RUN_OPTS) or None
 
 
 def _api():
@@ -55,7 +71,8 @@ def say(msg):
 
 def gpu_greedy(logits, dtype, tokens):
     api = _api()
-    acc, out = api.spec_verify_greedy(dev_logits(logits, dtype), dev(tokens.astype(np.int32)))
+    acc, out = api.spec_verify_greedy(dev_logits(logits, dtype), dev(tokens.astype(np.int32)),
+                                      opts=_opts())
     torch.cuda.synchronize()
     return acc.cpu().numpy(), out.cpu().numpy()
 
@@ -64,7 +81,8 @@ def gpu_chain(logits, dtype, q, x, coins, T):
     api = _api()
     acc, out, probs = api.spec_verify_chain(dev_logits(logits, dtype), dev(q.astype(np.float32)),
                                             dev(x.astype(np.int32)), dev(coins.astype(np.float32)),
-                                            dev(T.astype(np.float32)), want_probs=True)
+                                            dev(T.astype(np.float32)), want_probs=True,
+                                            opts=_opts())
     torch.cuda.synchronize()
     return dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
                 probs=probs.cpu().numpy())
@@ -83,7 +101,7 @@ def gpu_tree(t, mode, D=None, th_single=1.0, th_acc=1.0, parents=None, tokens=No
         dev_logits(t.logits, t.dtype), dev(tokens.astype(np.int32)), dev(parents.astype(np.int32)),
         dev(coins.astype(np.float32)) if sampling else None,
         dev(temperature.astype(np.float32)) if sampling else None, D, mode, th_single, th_acc,
-        want_probs=True)
+        want_probs=True, opts=_opts())
     torch.cuda.synchronize()
     return dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
                 accepted_nodes=nodes.cpu().numpy(), probs=probs.cpu().numpy())
@@ -92,14 +110,70 @@ def gpu_tree(t, mode, D=None, th_single=1.0, th_acc=1.0, parents=None, tokens=No
 # ------------------------------------------------------------------------------------
 # comparison
 
-def compare(g, o, keys, margin=None, probs=True, label=""):
-    """Bit-exact on `keys` outside the near-tie band; probs within 1e-5 relative."""
+def near_tie_bound(B):
+    """Most acceptance-side near-ties a call of B requests may have.  Those margins are the
+    distances of coins (uniform on (0, 1]) to the thresholds of the tests they decide, so
+    a request lands within 1e-6 of one with probability about 2e-6 per test, and a request
+    takes at most a few dozen tests: the expected count per call is well under 1e-3 * B,
+    and more than 2 + B/100 would mean the band is hiding a systematic difference, not
+    rounding.  The final draw's margin is different: at V = 152064 the steps of its
+    inverse CDF average 6.6e-6, so a coin often lies within 1e-6 of a step's end; those
+    near-ties are counted, and every one that differs is checked by NUDGE below."""
+    return 2 + B // 100
+
+
+# A near-tie that differs must be the oracle's own result for a coin moved by a rounding-
+# sized amount: at most this far, in coin units (the band, 1e-6, is in weight units for the
+# final draw, i.e. 1e-6 / S in coin units for a draw of total weight S).
+NUDGES = (1e-7, 3e-7, 1e-6, 3e-6, 1e-5)
+
+
+def nudge_reaches(run, coins_b, want):
+    """True when the oracle, run on one request (run(coin_matrix) -> list of output tuples)
+    with one of its coins moved by +-d for d in NUDGES, gives the output `want`."""
+    coins_b = np.asarray(coins_b, np.float64)
+    rows = []
+    for i in range(len(coins_b)):
+        for d in NUDGES:
+            for sgn in (-1.0, 1.0):
+                c = coins_b.copy()
+                c[i] = min(1.0, max(2.0 ** -24, c[i] + sgn * d))
+                rows.append(c)
+    return any(o == want for o in run(np.array(rows, np.float32)))
+
+
+def compare(g, o, keys, margin=None, probs=True, label="", max_near=None, accept_margin=None,
+            recheck=None):
+    """Bit-exact on `keys` outside the near-tie band; probs within 1e-5 relative.
+
+    The near-ties (oracle margin <= 1e-6) are counted and reported in the run's parity
+    summary, split into those on the acceptance side (oracle accept_margin <= 1e-6;
+    bounded by `max_near`, default near_tie_bound(B)) and those of the final draw only.
+    When `recheck(b)` is given, every near-tie that differs must pass it (the oracle
+    reaches the GPU's output with a coin nudged by a rounding-sized amount)."""
     B = len(o["accept_len"])
     mism = np.zeros(B, bool)
     for k in keys:
         a, b = np.asarray(g[k]), np.asarray(o[k])
-        mism |= (a != b).reshape(B, -1).any(1)
+        if B:
+            mism |= (a != b).reshape(B, -1).any(1)
+    if accept_margin is None and margin is not None and margin is o.get("margin"):
+        accept_margin = o.get("accept_margin")
     near = np.zeros(B, bool) if margin is None else margin <= BAND
+    near_acc = near if accept_margin is None else (accept_margin <= BAND)
+    stats = dict(n=B, near=int(near.sum()), near_accept=int(near_acc.sum()),
+                 near_mismatch=int((mism & near).sum()), mismatch=int((mism & ~near).sum()))
+    rechecked = 0
+    if recheck is not None:
+        for b in np.nonzero(mism & near)[0][:20]:
+            assert recheck(int(b)), f"{label}: request {b} differs inside the band, and no " \
+                                    f"coin nudge of at most {NUDGES[-1]} reaches the GPU's output"
+            rechecked += 1
+    stats["near_mismatch_rechecked"] = rechecked
+    parity_log.record(label, stats)
+    limit = near_tie_bound(B) if max_near is None else max_near
+    assert stats["near_accept"] <= limit, \
+        f"{label}: {stats['near_accept']} acceptance-side near-ties > {limit} ({stats})"
     bad = mism & ~near
     if bad.any():
         i = int(np.nonzero(bad)[0][0])
@@ -113,16 +187,56 @@ def compare(g, o, keys, margin=None, probs=True, label=""):
         rel = np.abs(gp[big] - op[big]) / np.abs(op[big])
         assert rel.size == 0 or rel.max() <= PROB_RTOL, f"{label}: prob rel err {rel.max():.3g}"
         assert np.all(np.abs(gp[~big] - op[~big]) <= 1e-30), f"{label}: tiny probs differ"
-    stats = dict(n=B, near=int(near.sum()), near_mismatch=int((mism & near).sum()))
     say(f"{label}: {stats}")
     return stats
+
+
+def _chain_out(res, b):
+    k = int(res["accept_len"][b])
+    return (k,) + tuple(int(t) for t in np.asarray(res["out_tokens"])[b, :max(k, 0) + 1])
+
+
+def chain_recheck(logits, dtype, q, x, coins, T, g):
+    """recheck for compare(): request b of a chain call."""
+    def run_b(b):
+        def run(cs):
+            n = len(cs)
+            r = oracle.verify_chain(np.ascontiguousarray(np.broadcast_to(logits[b], (n,) + logits.shape[1:])),
+                                    dtype,
+                                    np.ascontiguousarray(np.broadcast_to(q[b], (n,) + q.shape[1:])),
+                                    np.ascontiguousarray(np.broadcast_to(x[b], (n,) + x.shape[1:])),
+                                    cs, np.full(n, T[b], np.float32))
+            return [_chain_out(r, i) for i in range(n)]
+        return nudge_reaches(run, coins[b], _chain_out(g, b))
+    return run_b
+
+
+def _tree_out(res, b):
+    k = int(res["accept_len"][b])
+    return (k,) + tuple(int(t) for t in np.asarray(res["out_tokens"])[b, :max(k, 0) + 1]) + \
+        tuple(int(nd) for nd in np.asarray(res["accepted_nodes"])[b, :max(k, 0)])
+
+
+def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperature, g):
+    def run_b(b):
+        def run(cs):
+            n = len(cs)
+            rep = lambda a: np.ascontiguousarray(np.broadcast_to(a[b], (n,) + a.shape[1:]))
+            r = oracle.verify_tree(rep(t.logits), t.dtype, rep(tokens), rep(parents), cs,
+                                   np.full(n, temperature[b], np.float32), D, mode, th_single,
+                                   th_acc)
+            return [_tree_out(r, i) for i in range(n)]
+        return nudge_reaches(run, coins[b], _tree_out(g, b))
+    return run_b
 
 
 def check_chain(c, label):
     say(f"chain {label}: B={c.B} G={c.G} V={c.V} {c.dtype}")
     g = gpu_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
     o = oracle.verify_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
-    return compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=label)
+    return compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=label,
+                   recheck=chain_recheck(c.logits, c.dtype, c.draft_probs, c.draft_tokens,
+                                         c.coins, c.temperature, g))
 
 
 def check_greedy(c, label, tokens=None):
@@ -145,8 +259,12 @@ def check_tree(t, mode, label, **kw):
     if mode == oracle.TREE_GREEDY:
         g["probs"] = np.zeros_like(g["probs"])
         o["probs"] = np.zeros_like(o["probs"])
-    return compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"],
-                   o["margin"] if mode == oracle.TREE_SAMPLING else None, label=label)
+        return compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"], None, label=label)
+    return compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"], o["margin"], label=label,
+                   recheck=tree_recheck(t, mode, D, kw.get("th_single", 1.0), kw.get("th_acc", 1.0),
+                                        kw.get("parents", t.parents), kw.get("tokens", t.node_tokens),
+                                        kw.get("coins", t.coins),
+                                        kw.get("temperature", t.temperature), g))
 
 
 # ------------------------------------------------------------------------------------
@@ -228,11 +346,11 @@ def test_chain_temperatures_boosted(T):
 
 @pytest.mark.parametrize("dtype,V,eager", [(wl.BF16, 70000, False), (wl.BF16, 70000, True),
                                            (wl.F32, 70001, False), (wl.F32, 70001, True)])
-def test_greedy_ties(dtype, V, eager, monkeypatch):
+def test_greedy_ties(dtype, V, eager, launch):
     """Many tied maxima (small-integer logits): the lowest id must win everywhere, in the
     walk and in the eager passes, in both dtypes; V = 70001 leaves a ragged last chunk."""
     if eager:
-        monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+        launch.update(path="eager")
     rng = np.random.default_rng(17)
     B, G = 64, 4
     lg = rng.integers(0, 4, size=(B, G + 1, V)).astype(np.float32)
@@ -300,11 +418,11 @@ def test_chain_shaped_tree_equals_chain_on_gpu():
 # invalid requests, determinism
 
 @pytest.mark.parametrize("eager", [False, True])
-def test_invalid_requests_match_oracle(eager, monkeypatch):
+def test_invalid_requests_match_oracle(eager, launch):
     """Bad entries at position 0 (always consulted) invalidate the request; bad entries
     after the first rejection are never consulted (the oracle decides which is which)."""
     if eager:
-        monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+        launch.update(path="eager")
     c = wl.make_chain(2, seed=2, B=16, G=3, V=3000)
     lg, q, x, u, T = (c.logits.copy(), c.draft_probs.copy(), c.draft_tokens.copy(),
                       c.coins.copy(), c.temperature.copy())
@@ -359,47 +477,47 @@ def test_deterministic_bits():
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_eager_passes_match_oracle(cfg, monkeypatch):
-    """The eager passes (every row streamed, then merged), selected by SPEC_VERIFY_EAGER,
+def test_eager_passes_match_oracle(cfg, launch):
+    """The eager passes (every row streamed, then merged), selected with path = eager,
     give the oracle's results too."""
-    monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+    launch.update(path="eager")
     c = chain_cfg(cfg)
     check_chain(c, f"eager workload {cfg}")
     check_greedy(c, f"eager workload {cfg}")
 
 
 @pytest.mark.parametrize("cluster", ["1", "3"])
-def test_walk_cluster_widths(cluster, monkeypatch):
+def test_walk_cluster_widths(cluster, launch):
     """The position-by-position walks with one workgroup per request and with three."""
-    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    launch.update(cluster=int(cluster))
     c = wl.make_chain(3, seed=31, B=24, G=8, V=50021)
     check_chain(c, f"walk W<={cluster}")
     check_greedy(c, f"walk W<={cluster}")
 
 
 @pytest.mark.parametrize("cluster,dtype", [("1", wl.F32), ("2", wl.BF16), ("5", wl.F32)])
-def test_chain_walk_wide_slices_take_the_draw_kernel(cluster, dtype, monkeypatch):
+def test_chain_walk_wide_slices_take_the_draw_kernel(cluster, dtype, launch):
     """V = 300001 (74 fine chunks, a ragged last one): with one workgroup per request the
     slice holds more chunks than one wave scans, so the chain walk leaves the final draw to
     k_draw; with two it just fits the in-walk draw (37 chunks), and with five the slices
     are short.  All must match the oracle."""
-    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+    launch.update(cluster=int(cluster))
     c = wl.make_chain(2, seed=43, B=6, G=2, V=300001, dtype=dtype)
     check_chain(c, f"wide slices W<={cluster} {dtype}")
 
 
 @pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
-def test_tree_eager_passes_match_oracle(mode, monkeypatch):
-    """The eager tree passes (every row streamed, then walked), selected by
-    SPEC_VERIFY_EAGER, give the oracle's results too."""
-    monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+def test_tree_eager_passes_match_oracle(mode, launch):
+    """The eager tree passes (every row streamed, then walked), selected with path =
+    eager, give the oracle's results too."""
+    launch.update(path="eager")
     check_tree(tree_cfg(), mode, f"tree eager mode {mode}")
 
 
 @pytest.mark.parametrize("cluster", ["1", "3"])
 @pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
-def test_tree_walk_cluster_widths(cluster, mode, monkeypatch):
-    monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+def test_tree_walk_cluster_widths(cluster, mode, launch):
+    launch.update(cluster=int(cluster))
     t = wl.make_tree(4, seed=41, B=12, N=40, V=30011, D=5, max_children=5)
     check_tree(t, mode, f"tree walk W<={cluster} mode {mode}")
 
@@ -432,7 +550,7 @@ def test_tree_rows_off_the_walk():
 
 
 @pytest.mark.parametrize("dtype,eager", [(wl.F32, False), (wl.F32, True), (wl.BF16, False)])
-def test_chain_residual_without_mass_falls_back(dtype, eager, monkeypatch):
+def test_chain_residual_without_mass_falls_back(dtype, eager, launch):
     """q = 2p, used as given: every draft is accepted with probability 1/2 and, after a
     rejection, max(0, p - q) has no mass, so the correction is drawn from the target row
     itself (the bonus rule).  The oracle reports the empty residual as a zero margin, so
@@ -442,7 +560,7 @@ def test_chain_residual_without_mass_falls_back(dtype, eager, monkeypatch):
     eager passes."""
     import dataclasses
     if eager:
-        monkeypatch.setenv("SPEC_VERIFY_EAGER", "1")
+        launch.update(path="eager")
     c = wl.make_chain(2, seed=41, B=32, G=4, V=9000, dtype=dtype)
     lg = wl.logits_as_f32(c.logits, c.dtype).astype(np.float64)
     z = lg / c.temperature.astype(np.float64)[:, None, None]
@@ -472,13 +590,13 @@ def test_chain_residual_without_mass_falls_back(dtype, eager, monkeypatch):
 
 @pytest.mark.parametrize("cluster", [None, "1", "2", "4"])
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
-def test_chain_bonus_draws(cluster, dtype, monkeypatch):
+def test_chain_bonus_draws(cluster, dtype, launch):
     """Every draft accepted (q is the target row itself), so every request draws its bonus
     token from the last row; the walk finds the slice holding u * total from the slices'
     (max, normaliser) pairs and only that slice's workgroup weighs and draws.  Final coins
     at the ends of (0, 1] and in between, at several cluster widths."""
     if cluster is not None:
-        monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+        launch.update(cluster=int(cluster))
     c = wl.make_chain(5, seed=77, B=40, G=3, V=70001, dtype=dtype)
     lg = wl.logits_as_f32(c.logits, dtype).astype(np.float64)
     z = (lg[:, :c.G] - lg[:, :c.G].max(-1, keepdims=True)) / c.temperature[:, None, None]
@@ -494,7 +612,9 @@ def test_chain_bonus_draws(cluster, dtype, monkeypatch):
     say(f"chain bonus draws {dtype} cluster={cluster}")
     g = gpu_chain(c.logits, dtype, q, c.draft_tokens, coins, c.temperature)
     o = oracle.verify_chain(c.logits, dtype, q, c.draft_tokens, coins, c.temperature)
-    compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=f"bonus {dtype} W={cluster}")
+    # coins 1.0 and 2^-24 sit at the ends of the draw's range: near-ties by construction
+    compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=f"bonus {dtype} W={cluster}",
+            max_near=4)
     assert (o["accept_len"] == c.G).sum() >= c.B - 2
 
 
@@ -514,12 +634,12 @@ def test_walk_shapes_across_cluster_widths(B, G, V, dtype, T):
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("cluster", [None, "1"])
-def test_large_vocabulary(dtype, cluster, monkeypatch):
+def test_large_vocabulary(dtype, cluster, launch):
     """A vocabulary of a million tokens (ragged: 1,000,003): 245 fine chunks per row, spread
     over up to sixteen workgroups, or all in one (the final draw then searches 245 chunk
     masses in k_draw)."""
     if cluster is not None:
-        monkeypatch.setenv("SPEC_VERIFY_CLUSTER", cluster)
+        launch.update(cluster=int(cluster))
     c = wl.make_chain(2, seed=11, B=3, G=2, V=1_000_003, dtype=dtype)
     check_chain(c, f"V=1000003 {dtype} W={cluster}")
     check_greedy(c, f"V=1000003 {dtype} W={cluster}")

@@ -22,6 +22,7 @@ import test_oracle_tree_mask as tm
 import test_oracle_commit_kv as ck
 import test_oracle_filtered as tf
 import test_oracle_mss as ms
+import test_oracle_margins as mg
 
 SRC = open(oracle.SRC).read()
 
@@ -87,6 +88,32 @@ MUTANTS = [
      "int y = draw_inverse_cdf(w, V, (double)coins[N - 1], margin);",
      "for (int v = 0; v < V; ++v) w[v] = row_prob(r, v, m, Z, T);\n"
      "    int y = draw_inverse_cdf(w, V, (double)coins[N - 1], margin);"),
+    # the near-tie margins and the acceptance-rate diagnostic
+    ("draw margin in coin units", "                note_margin(mm, t - before);\n"
+     "                note_margin(mm, C - t);",
+     "                note_margin(mm, (t - before) / S);\n"
+     "                note_margin(mm, (C - t) / S);"),
+    ("draw margin dropped", "                note_margin(mm, t - before);\n"
+     "                note_margin(mm, C - t);", ""),
+    ("draw margin on one side only", "                note_margin(mm, C - t);\n", ""),
+    ("acceptance margin against p instead of p/q", "note_margin(margin, fabs(u - ratio));",
+     "note_margin(margin, fabs(u - ratio * qx));"),
+    ("acceptance margin dropped", "note_margin(margin, fabs(u - ratio));", ""),
+    ("residual mass not a margin", "    if (k < G) note_margin(margin, S);\n", ""),
+    ("tree sibling margin dropped", "note_margin(margin, fabs(u - acc / th_acc));", ""),
+    ("tree single-threshold margin dropped", "note_margin(margin, fabs(pc - th_single));", ""),
+    ("accept margin includes the draw",
+     "    if (amargin) *amargin = *margin; /* every margin so far: the tests before the draw */\n"
+     "    if (!(S > 0.0))\n        for (int x = 0; x < V; ++x) w[x] = row_prob(rk, x, m[k], Z[k], T);\n"
+     "    int y = draw_inverse_cdf(w, V, (double)coins[G], margin);\n",
+     "    if (!(S > 0.0))\n        for (int x = 0; x < V; ++x) w[x] = row_prob(rk, x, m[k], Z[k], T);\n"
+     "    int y = draw_inverse_cdf(w, V, (double)coins[G], margin);\n"
+     "    if (amargin) *amargin = *margin;\n"),
+    ("beta sums the larger of p and q", "s += p < qq ? p : qq;", "s += p > qq ? p : qq;"),
+    ("beta from the next row", "Row r = row_of(logits, dtype, b * (size_t)R + (size_t)i, V);\n"
+     "            double mi = row_max(r);",
+     "Row r = row_of(logits, dtype, b * (size_t)R + (size_t)(i + 1), V);\n"
+     "            double mi = row_max(r);"),
 ]
 
 
@@ -124,6 +151,11 @@ def _pins():
     yield ms.test_hand_both_rejected_final_draw_from_residual
     yield lambda: ms.test_chain_shaped_tree_equals_chain_verify(0, 1.0)
     yield lambda: ms.test_walk_emits_target_law_over_coins_and_drafts(0, 1.0, [-1, 0, 0, 1, 1, 2])
+    yield lambda: mg.test_chain_margins_equal_breakpoint_distances(0, 1.0)
+    yield mg.test_chain_margin_is_small_exactly_when_a_nudge_flips_the_result
+    yield lambda: mg.test_beta_equals_lattice_acceptance_rate(0)
+    yield lambda: mg.test_tree_margins_equal_breakpoint_distances(0, 1.5)
+    yield lambda: mg.test_tree_margins_equal_breakpoint_distances(2, 6.0)
 
 
 @pytest.mark.parametrize("name,orig,mutation", MUTANTS, ids=[m[0] for m in MUTANTS])
