@@ -93,7 +93,8 @@ enum {
     SPEC_ERR_DTYPE = -3,     /* unknown logit dtype */
     SPEC_ERR_PARAM = -4,     /* bad mode / threshold / misaligned pointer */
     SPEC_ERR_WORKSPACE = -5, /* workspace too small or not 256-byte aligned */
-    SPEC_ERR_HIP = -6        /* a HIP launch failed */
+    SPEC_ERR_HIP = -6,       /* a HIP launch failed */
+    SPEC_ERR_TOO_LARGE = -7  /* spec_verify_chain_noalloc: sizes beyond its static scratch */
 };
 
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };                   /* target-logit dtype */
@@ -183,6 +184,25 @@ int spec_verify_chain_opt(const void* logits, int dtype, const float* draft_prob
                           const float* temperature, int B, int G, int V, int32_t* accept_len,
                           int32_t* out_tokens, float* probs_out, void* workspace,
                           size_t ws_bytes, void* stream, const spec_options* opt);
+
+/* Chain rejection sampling (as spec_verify_chain, same arguments and results) for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid hipMalloc.  There is no workspace argument: the call uses a
+ * static scratch array of 32 MiB inside the library (each GPU the library runs on holds
+ * its own copy until the process ends; zero when the library is loaded), and allocates
+ * nothing.  Calls whose spec_workspace_bytes(SPEC_OP_CHAIN, B, G+1, V) exceeds 32 MiB
+ * return SPEC_ERR_TOO_LARGE before anything is enqueued (B = 256, G = 4 fits up to
+ * V ~ 700k; at V = 152064, B up to ~1200).  Every call on one GPU shares that GPU's
+ * array: calls on one stream run in turn and may differ in shape, but calls that overlap
+ * on one GPU (other streams, other host threads) race and give wrong results.  The
+ * array's header (the walks' call counter and exit words) is left ready by every call;
+ * everything else in it is written before it is read within a call.  SPEC_ERR_HIP if the
+ * array's device address cannot be obtained. */
+int spec_verify_chain_noalloc(const void* logits, int dtype, const float* draft_probs,
+                              const int32_t* draft_tokens, const float* coins,
+                              const float* temperature, int B, int G, int V,
+                              int32_t* accept_len, int32_t* out_tokens, float* probs_out,
+                              void* stream);
 
 /* Chain rejection sampling from draft logits, with top-k / top-p filtering
  * (ricardokevins, "mechanism": serving samples with temperature, top-p and top-k;

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "spec_verify.h")
 
 SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_DTYPE = 0, -1, -2, -3
-SPEC_ERR_PARAM, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = -4, -5, -6
+SPEC_ERR_PARAM, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP, SPEC_ERR_TOO_LARGE = -4, -5, -6, -7
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_TREE_GREEDY, SPEC_TREE_SAMPLING = 0, 1
 SPEC_OP_GREEDY, SPEC_OP_CHAIN, SPEC_OP_TREE, SPEC_OP_CHAIN_FILTERED, SPEC_OP_TREE_MSS = 0, 1, 2, 3, 4
@@ -83,6 +83,9 @@ def lib():
         L.spec_verify_chain.restype = ip
         L.spec_verify_chain_opt.argtypes = L.spec_verify_chain.argtypes + [op]
         L.spec_verify_chain_opt.restype = ip
+        L.spec_verify_chain_noalloc.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, vp, vp, vp,
+                                                vp]
+        L.spec_verify_chain_noalloc.restype = ip
         L.spec_verify_tree.argtypes = [vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, fp,
                                        vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_tree.restype = ip

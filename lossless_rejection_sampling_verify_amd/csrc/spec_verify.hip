@@ -46,6 +46,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include <climits>
 #include <cmath>
@@ -3828,6 +3829,35 @@ __global__ __launch_bounds__(kBlock) void k_calib_exp(int iters, float* sink) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
+// The static scratch of spec_verify_chain_noalloc: a chain call's workspace in the
+// library's own device memory, zero at load.  Each device holds its own copy until the
+// process ends.  Host code never uses this name as an address (on the host it stands for
+// a host-side shadow): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The device address of `scratch` on the current device (nullptr if HIP cannot give it).
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
 // C ABI
 
 extern "C" size_t spec_workspace_bytes(int op, int B, int R, int V) {
@@ -3851,6 +3881,8 @@ extern "C" const char* spec_status_str(int status) {
         case SPEC_ERR_PARAM: return "bad mode, threshold or pointer alignment";
         case SPEC_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
         case SPEC_ERR_HIP: return "HIP launch failed";
+        case SPEC_ERR_TOO_LARGE:
+            return "the call needs more scratch than the library's static 32 MiB holds";
         default: return "unknown status";
     }
 }
@@ -3944,6 +3976,28 @@ extern "C" int spec_verify_chain(const void* logits, int dtype, const float* dra
                                  void* workspace, size_t ws_bytes, void* stream) {
     return spec_verify_chain_opt(logits, dtype, draft_probs, draft_tokens, coins, temperature, B,
                                  G, V, accept_len, out_tokens, probs_out, workspace, ws_bytes,
+                                 stream, nullptr);
+}
+
+extern "C" int spec_verify_chain_noalloc(const void* logits, int dtype, const float* draft_probs,
+                                         const int32_t* draft_tokens, const float* coins,
+                                         const float* temperature, int B, int G, int V,
+                                         int32_t* accept_len, int32_t* out_tokens,
+                                         float* probs_out, void* stream) {
+    // every argument check first (as a call with no requests, which enqueues nothing)
+    int rc = spec_verify_chain_opt(logits, dtype, draft_probs, draft_tokens, coins, temperature,
+                                   0, G, V, accept_len, out_tokens, probs_out, nullptr, 0, stream,
+                                   nullptr);
+    if (rc != SPEC_OK) return rc;
+    if (B < 0) return SPEC_ERR_SHAPE;
+    if (B == 0) return SPEC_OK;
+    const size_t need = spec_workspace_bytes(SPEC_OP_CHAIN, B, G + 1, V);
+    if (need == 0) return SPEC_ERR_SHAPE;
+    if (need > kScratchBytes) return SPEC_ERR_TOO_LARGE;
+    void* ws = scratch_ptr();
+    if (!ws) return SPEC_ERR_HIP;
+    return spec_verify_chain_opt(logits, dtype, draft_probs, draft_tokens, coins, temperature, B,
+                                 G, V, accept_len, out_tokens, probs_out, ws, kScratchBytes,
                                  stream, nullptr);
 }
 

@@ -1,7 +1,7 @@
 // abi_driver.cpp -- exercises the host side of the verify library's C ABI with arguments
 // that every entry point must reject before it touches the device: NULL pointers, sizes
-// outside the supported ranges, unknown dtypes and modes, misaligned or short workspaces
-// and bad launch options.  Built with the
+// outside the supported ranges, unknown dtypes and modes, misaligned or short workspaces,
+// bad launch options, and the static-scratch entry point's size limit.  Built with the
 // address and undefined-behaviour sanitizers on the host pass only (tests/test_sanitizers.py);
 // no GPU is needed, since no call gets as far as a launch.  Exit status 0 when every call
 // returned the expected status.
@@ -60,6 +60,10 @@ int main() {
     bad.spin_limit = -3;
     CHECK(spec_verify_greedy_opt(P, SPEC_BF16, Pi, 3, 4, 2000, Po, Po, P, wsg, nullptr, &bad) ==
           SPEC_ERR_PARAM);
+    CHECK(spec_verify_chain_noalloc(P, SPEC_BF16, Pf, Pi, Pf, Pf, 4096, 4, 152064, Po, Po, nullptr,
+                                    nullptr) == SPEC_ERR_TOO_LARGE);
+    CHECK(spec_verify_chain_noalloc(P, SPEC_BF16, Pf, Pi, Pf, Pf, 0, 4, 2000, Po, Po, nullptr,
+                                    nullptr) == SPEC_OK);
     // tree
     CHECK(spec_verify_tree(P, SPEC_F32, Pi, Pi, Pf, Pf, 3, 16, 2000, 4, 3, 1.f, 1.f, Po, Po, Po,
                            nullptr, P, wst, nullptr) == SPEC_ERR_PARAM);
