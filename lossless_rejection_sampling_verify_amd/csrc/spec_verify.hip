@@ -3628,10 +3628,15 @@ constexpr int kWalkPerCu = 5;
 struct Resident {
     int all, walk;
 };
+// one cache slot per (kernel, dtype): greedy walk 0/1, chain walk 2/3, tree walk 4/5,
+// multi-step tree walk 6/7 (fp32 / bf16)
+constexpr int kResidentSlots = 8;
 inline Resident resident_blocks(const void* kernel, int slot) {
-    static std::atomic<long long> cache[8][64];  // 0: not known; else (all << 32) | walk
+    static std::atomic<long long> cache[kResidentSlots][64];  // 0: not known; else (all << 32) | walk
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {0, 0};
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || slot < 0 ||
+        slot >= kResidentSlots)
+        return {0, 0};
     long long v = cache[slot][dev].load(std::memory_order_relaxed);
     if (v == 0) {
         int cus = 0, nb = 0;
