@@ -1116,6 +1116,30 @@ __device__ inline double dbl_of(uint32_t hi, uint32_t lo) {
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// Lane j's value of v, in every lane of the wave (j the same in all lanes).
+__device__ inline double lane_dbl(double v, int j) {
+    return dbl_of((uint32_t)__builtin_amdgcn_readlane((int)dbl_hi(v), j),
+                  (uint32_t)__builtin_amdgcn_readlane((int)dbl_lo(v), j));
+}
+
+// A row's normaliser from its slices' (max, sum) records after a cluster step (xp[j][0]
+// the max, xp[j][1..2] the fp64 sum of exp2((l - max) * s2)): the sum over members j, in
+// member order, of z_j exp((m_j - M) / T).  Lane j of each wave evaluates member j's
+// term, so the W exponentials run side by side instead of one after another; every lane
+// then adds the terms in the same order, so all threads of all members hold the same bits.
+__device__ inline double cluster_norm(const XSmem& xs, int W, float M, double Td) {
+    const int lane = threadIdx.x & 63;
+    double term = 0.0;
+    if (lane < W) {
+        const float mj = __uint_as_float(xs.xp[lane][0]);
+        if (mj != -INFINITY)
+            term = dbl_of(xs.xp[lane][1], xs.xp[lane][2]) * exp(((double)mj - (double)M) / Td);
+    }
+    double Z = 0.0;
+    for (int j = 0; j < W; ++j) Z += lane_dbl(term, j);
+    return Z;
+}
+
 // k_greedy_walk: greedy chain verify position by position, one cluster of W workgroups
 // per request (blockIdx = b * W + w, workgroup w owning a slice of whole fine chunks of
 // every row).  Each position's slice argmax travels through the cluster hand-off; the
@@ -2017,12 +2041,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         }
         M = -INFINITY;
         for (int j = 0; j < W; ++j) M = fmaxf(M, __uint_as_float(xs.xp[j][0]));
-        Z = 0.0;
-        for (int j = 0; j < W; ++j) {
-            const float mj = __uint_as_float(xs.xp[j][0]);
-            if (mj != -INFINITY)
-                Z += dbl_of(xs.xp[j][1], xs.xp[j][2]) * exp(((double)mj - (double)M) / Td);
-        }
+        Z = cluster_norm(xs, W, M, Td);
         if (M == -INFINITY) {  // a row the walk reaches has no finite logit
             bad = true;
             break;
@@ -2083,20 +2102,22 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             // underflow in fp32 where the owner weighs them (a slice above it has an element
             // of at least 1e-30 over its at most 64 chunks' 262144 elements, well inside
             // fp32's normal range).
-            auto slice_total = [&](int j) {
-                const float mj = __uint_as_float(xs.xp[j][0]);
+            // Lane j of each wave evaluates slice j's total.
+            double mine = 0.0;
+            if ((tid & 63) < W) {
+                const float mj = __uint_as_float(xs.xp[tid & 63][0]);
                 const double tj = mj == -INFINITY ? 0.0
-                                                  : dbl_of(xs.xp[j][1], xs.xp[j][2]) *
+                                                  : dbl_of(xs.xp[tid & 63][1], xs.xp[tid & 63][2]) *
                                                         exp(((double)mj - (double)M) / Td) / Z;
-                return tj >= 1e-30 ? tj : 0.0;
-            };
+                mine = tj >= 1e-30 ? tj : 0.0;
+            }
             double tot = 0.0;
-            for (int j = 0; j < W; ++j) tot += slice_total(j);
+            for (int j = 0; j < W; ++j) tot += lane_dbl(mine, j);
             const double t = (double)uG * tot;
             double carry = 0.0, before = 0.0, last_before = 0.0;
             int owner = -1, last = -1;
             for (int j = 0; j < W; ++j) {
-                const double tj = slice_total(j);
+                const double tj = lane_dbl(mine, j);
                 if (tj > 0.0) {
                     if (owner < 0 && t <= carry + tj) {
                         owner = j;
@@ -2279,29 +2300,56 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     const int32_t* tok_g = a.tokens + (size_t)b * N;
     const T* logits = reinterpret_cast<const T*>(a.logits);
     bool bad = false, gaveup = false;
-    for (int i = tid; i < N; i += kBlock) {
-        const int p = par_g[i];
-        const int t = tok_g[i];
-        ts.par[i] = p;
-        ts.tok[i] = t;
-        if (i == 0) {
-            if (p != -1) bad = true;
+    const float Tf = sampling ? a.temperature[b] : 1.f;
+    const double Td = (double)Tf;
+    const float s2 = kLog2e / Tf;
+
+    // One step's slice pass over node `node`'s row, handed to the cluster (the wait comes
+    // later, so that what does not need the row statistics overlaps the hand-off).
+    auto pass = [&](int step, int node) {
+        const T* rowp = logits + ((size_t)b * N + node) * V;
+        if (sampling) {
+            const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+            cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
+                            dbl_lo(r.z), xs);
         } else {
-            if (p < 0 || p >= i) bad = true;
-            if (t < 0 || t >= V) bad = true;
+            const Part r = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, 0.f, rs);
+            cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), (uint32_t)r.idx, 0u, xs);
+        }
+    };
+
+    // The tree's arrays are loaded first and the root's pass runs while they arrive; the
+    // tree is checked while the pass's hand-off travels.  The root row is in bounds
+    // whatever the tree holds, and a request found invalid never waits for its words.
+    constexpr int kPer = SPEC_MAX_N / kBlock;
+    int pr[kPer], tr[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int i = tid + c * kBlock;
+        pr[c] = i < N ? par_g[i] : 0;
+        tr[c] = i < N ? tok_g[i] : 0;
+    }
+    pass(0, 0);
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int i = tid + c * kBlock;
+        if (i >= N) break;
+        ts.par[i] = pr[c];
+        ts.tok[i] = tr[c];
+        if (i == 0) {
+            if (pr[c] != -1) bad = true;
+        } else {
+            if (pr[c] < 0 || pr[c] >= i) bad = true;
+            if (tr[c] < 0 || tr[c] >= V) bad = true;
         }
     }
-    float Tf = 1.f;
     if (sampling) {
-        Tf = a.temperature[b];
         if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
         for (int d = tid; d <= D; d += kBlock) {
             const float u = a.coins[(size_t)b * (D + 1) + d];
             if (!(u > 0.f && u <= 1.f)) bad = true;
         }
     }
-    const double Td = (double)Tf;
-    const float s2 = kLog2e / Tf;
     bad = __syncthreads_or(bad);
     if (!bad) {
         tree_depths(ts.par, N, ts.anc, ts.dep);
@@ -2315,7 +2363,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     double Z = 1.0;
     for (int step = 0; !bad; ++step) {
         const T* rowp = logits + ((size_t)b * N + cur) * V;
-        int count = 0;  // children of cur in ascending node id (ordered compaction)
+        // while this step's words travel: the children of cur in ascending node id (ordered
+        // compaction) and, for sampling, their tokens' logits
+        int count = 0;
         for (int base = cur + 1; base < N; base += kBlock) {
             const int c = base + tid;
             const bool f = c < N && ts.par[c] == cur;
@@ -2333,29 +2383,15 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         }
         for (int j = tid; j < count && sampling; j += kBlock)
             ts.lx[j] = Ld<T>::one(rowp + ts.tok[ts.kids[j]]);
+        if (!cluster_wait(slots, step, W, tag, a.spin, xs)) {
+            bad = gaveup = true;
+            break;
+        }
+        M = -INFINITY;
         if (sampling) {
-            const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
-            if (!cluster_step(slots, step, W, w, tag, a.spin, __float_as_uint(r.m), dbl_hi(r.z),
-                              dbl_lo(r.z), xs)) {
-                bad = gaveup = true;
-                break;
-            }
-            M = -INFINITY;
             for (int j = 0; j < W; ++j) M = fmaxf(M, __uint_as_float(xs.xp[j][0]));
-            Z = 0.0;
-            for (int j = 0; j < W; ++j) {
-                const float mj = __uint_as_float(xs.xp[j][0]);
-                if (mj != -INFINITY)
-                    Z += dbl_of(xs.xp[j][1], xs.xp[j][2]) * exp(((double)mj - (double)M) / Td);
-            }
+            Z = cluster_norm(xs, W, M, Td);
         } else {
-            const Part r = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, 0.f, rs);
-            if (!cluster_step(slots, step, W, w, tag, a.spin, __float_as_uint(r.m),
-                              (uint32_t)r.idx, 0u, xs)) {
-                bad = gaveup = true;
-                break;
-            }
-            M = -INFINITY;
             for (int j = 0; j < W; ++j) {  // slices in order: the lowest index among equal maxima
                 const float mj = __uint_as_float(xs.xp[j][0]);
                 if (mj > M) {
@@ -2368,28 +2404,43 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
             bad = true;
             break;
         }
-        if (tid == 0) {
+        if (sampling && tid < 64) {
+            // wave 0: lane i evaluates the probability of child c0 + i, 64 children at a
+            // time, and every lane adds them up in child order (the same bits in all lanes)
+            const double u = (double)a.coins[(size_t)b * (D + 1) + d];
+            const double tha = (double)a.th_acc, ths = (double)a.th_single;
+            double acc = 0.0, pch = 0.0;
             int ch = -1;
-            if (sampling) {
-                const double u = (double)a.coins[(size_t)b * (D + 1) + d];
-                const double tha = (double)a.th_acc, ths = (double)a.th_single;
-                double acc = 0.0;
-                for (int j = 0; j < count; ++j) {
-                    const double pc = exp(((double)ts.lx[j] - (double)M) / Td) / Z;
+            for (int c0 = 0; c0 < count && ch < 0; c0 += 64) {
+                const int j = c0 + lane;
+                const double mine =
+                    j < count ? exp(((double)ts.lx[j] - (double)M) / Td) / Z : 0.0;
+                const int n = min(64, count - c0);
+                for (int e = 0; e < n; ++e) {
+                    const double pc = lane_dbl(mine, e);
                     acc += pc;
                     if (u <= acc / tha || pc >= ths) {
-                        ch = j;
-                        ts.pathp[d] = (float)pc;
+                        ch = c0 + e;
+                        pch = pc;
                         break;
                     }
                 }
-            } else {
-                for (int j = 0; j < count; ++j)
-                    if (ts.tok[ts.kids[j]] == last) {
-                        ch = j;
-                        break;
-                    }
             }
+            if (tid == 0) {
+                ts.chosen = ch;
+                if (ch >= 0) {
+                    ts.path[d] = ts.kids[ch];
+                    ts.pathp[d] = (float)pch;
+                }
+            }
+        }
+        if (!sampling && tid == 0) {  // greedy: the child whose token is the argmax
+            int ch = -1;
+            for (int j = 0; j < count; ++j)
+                if (ts.tok[ts.kids[j]] == last) {
+                    ch = j;
+                    break;
+                }
             ts.chosen = ch;
             if (ch >= 0) ts.path[d] = ts.kids[ch];
         }
@@ -2413,6 +2464,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         }
         cur = ts.kids[ch];
         ++d;
+        pass(step + 1, cur);
     }
 
     DrawState st = {};
@@ -2677,12 +2729,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
             }
             M = -INFINITY;
             for (int k = 0; k < W; ++k) M = fmaxf(M, __uint_as_float(xs.xp[k][0]));
-            Z = 0.0;
-            for (int k = 0; k < W; ++k) {
-                const float mk = __uint_as_float(xs.xp[k][0]);
-                if (mk != -INFINITY)
-                    Z += dbl_of(xs.xp[k][1], xs.xp[k][2]) * exp(((double)mk - (double)M) / Td);
-            }
+            Z = cluster_norm(xs, W, M, Td);
         }
         if (M == -INFINITY) {  // a row on the walk with no finite logit
             bad = true;
