@@ -2894,6 +2894,7 @@ __global__ __launch_bounds__(64) void k_draw(KArgs a) {
 constexpr int kHistBins = 256;  // 8-bit radix digits
 
 constexpr int kCandCap = 2048;  // top-k candidates kept in LDS by the direct selection
+constexpr int kItemCap = 1024;  // recorded batches the candidate pass can list
 
 struct FilterSmem {
     RowSmem rs;
@@ -2904,13 +2905,15 @@ struct FilterSmem {
         };
         uint32_t cand[kCandCap];  // direct selection: candidate keys
     };
-    uint32_t lanekey[kBlock];
+    uint32_t lanekey[kBlock];  // lane maxima's keys; then the sorted candidates (n <= kBlock)
     uint16_t bkey[kMaxBatchRec * kBlock];  // batch maxima of the first pass (key top bits)
+    uint16_t item[kItemCap];               // the batches the candidate pass reads (j * kBlock + t)
     int ncand;
     unsigned long long wtot[3][kWaves];
     int pick_thread;
     int last_thread;
     int pick;
+    uint32_t lbkey;  // direct selection: the k-th largest lane maximum's key
     unsigned long long above_cnt, above_mass, bucket_mass, total_cnt, total_mass;
     double need_mass;
 };
@@ -3127,6 +3130,18 @@ __device__ inline float key_value(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
+// Descending rank of this thread's key among the n keys a[0..n) (this thread's being a[i]):
+// the keys above it, plus the equal keys at lower positions, so the ranks of the n keys
+// are 0..n-1 without repeats, and placing each key at its rank sorts them descending.
+__device__ inline int desc_rank(const uint32_t* a, int n, int i, uint32_t key) {
+    int r = 0;
+    for (int j = 0; j < n; ++j) {
+        const uint32_t o = a[j];
+        r += (o > key || (o == key && j < i)) ? 1 : 0;
+    }
+    return r;
+}
+
 // Direct top-k (k <= kBlock) then top-p on the top-k set, for rows whose candidates fit in
 // LDS.  The k-th largest of the lanes' maxima (one per lane from the first pass) is a
 // lower bound of the row's k-th largest logit, so one more pass collects every token at
@@ -3135,19 +3150,29 @@ __device__ inline float key_value(uint32_t key) {
 // kept mass are the ones the radix selection finds.  Returns false (nothing decided)
 // when the candidates do not fit.
 //
+// The k-th lane maximum, and the order of at most kBlock candidates, come from ranks
+// (each thread counts the keys above its own) rather than from a sorting network: a few
+// hundred LDS reads per thread instead of dozens of barrier-separated stages.
+//
 // With `rec` the first pass left every batch's maximum in sm.bkey (a row without NaN whose
 // full batches fit the record): only batches whose maximum reaches the bound are read
-// again, so the row is read about once instead of twice.
+// again, so the row is read about once instead of twice.  Those batches are listed in LDS
+// first and their loads dealt out over the whole workgroup, all in flight at once: a
+// lane walking its own batches would wait one memory round trip per batch that any lane
+// of its wave needs.
 template <typename T>
 __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fscale, int k,
                               bool fp, double tp, float lane_max, bool rec, uint32_t* th_out,
                               unsigned long long* kept_out, FilterSmem& sm) {
     const int tid = threadIdx.x;
     constexpr int kVec = Ld<T>::kVec;
-    sm.lanekey[tid] = order_key(lane_max);
+    const uint32_t mykey = order_key(lane_max);
+    sm.lanekey[tid] = mykey;
     if (tid == 0) sm.ncand = 0;
-    bitonic_desc(sm.lanekey, kBlock);
-    const uint32_t lb = sm.lanekey[k - 1];
+    __syncthreads();
+    if (desc_rank(sm.lanekey, kBlock, tid, mykey) == k - 1) sm.lbkey = mykey;  // one thread
+    __syncthreads();
+    const uint32_t lb = sm.lbkey;
     auto visit = [&](float x) {
         const uint32_t key = order_key(x);
         if (key >= lb) {
@@ -3163,20 +3188,64 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + head);
     int v = tid;
     const uint32_t lb16 = lb >> 16;  // key >= lb implies key >> 16 >= lb16
-    for (int j = 0; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock, ++j) {
-        if (rec && sm.bkey[j * kBlock + tid] < lb16) continue;  // nothing here reaches lb
-        u32x4 r[kUnroll];
+    bool listed = false;
+    if (rec) {
+        // this lane's full batches whose recorded maximum reaches the bound
+        int nfull = 0, q = 0;
+        for (int j = 0; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock, ++j, ++nfull)
+            if (sm.bkey[j * kBlock + tid] >= lb16) ++q;
+        unsigned long long c3[3] = {(unsigned long long)q, 0ull, 0ull}, e3[3], t3[3];
+        block_scan3(c3, e3, t3, sm);
+        const int total = (int)t3[0];
+        if (total <= kItemCap) {  // uniform: every thread has the same total
+            listed = true;
+            int o = (int)e3[0];
+            for (int j = 0; j < nfull; ++j)
+                if (sm.bkey[j * kBlock + tid] >= lb16) sm.item[o++] = (uint16_t)(j * kBlock + tid);
+            __syncthreads();
+            // one vector per (batch, u): up to four per thread in flight at once
+            const int nvis = total * kUnroll;
+            for (int base = 0; base < nvis; base += 4 * kBlock) {
+                u32x4 r[4];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) r[u] = ld_stream(vp + v + u * kBlock);
+                for (int e = 0; e < 4; ++e) {
+                    const int it = base + e * kBlock + tid;
+                    if (it < nvis) {
+                        const int bt = sm.item[it / kUnroll];
+                        const int vv = (bt % kBlock) + kBlock * (kUnroll * (bt / kBlock) + it % kUnroll);
+                        r[e] = ld_stream(vp + vv);
+                    }
+                }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float f[kVec];
-            Ld<T>::unpack(r[u], f);
+                for (int e = 0; e < 4; ++e) {
+                    if (base + e * kBlock + tid < nvis) {
+                        float f[kVec];
+                        Ld<T>::unpack(r[e], f);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) visit(f[e]);
+                        for (int x = 0; x < kVec; ++x) visit(f[x]);
+                    }
+                }
+            }
+        } else {
+            v = tid;  // too many to list: the batches one by one below
         }
     }
-    for (; v < nv; v += kBlock) {
+    if (!listed) {
+        for (int j = 0; v + (kUnroll - 1) * kBlock < nv; v += kUnroll * kBlock, ++j) {
+            if (rec && sm.bkey[j * kBlock + tid] < lb16) continue;  // nothing here reaches lb
+            u32x4 r[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) r[u] = ld_stream(vp + v + u * kBlock);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                float f[kVec];
+                Ld<T>::unpack(r[u], f);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) visit(f[e]);
+            }
+        }
+    }
+    for (; v < nv; v += kBlock) {  // the vectors after a lane's last full batch
         float f[kVec];
         Ld<T>::unpack(ld_stream(vp + v), f);
 #pragma unroll
@@ -3186,19 +3255,29 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
     __syncthreads();
     const int n = sm.ncand;
     if (n > kCandCap) return false;  // uniform: every thread read the same count
-    int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (int j = n + tid; j < n2; j += kBlock) sm.cand[j] = 0u;  // below every real key
-    bitonic_desc(sm.cand, n2);
-    const uint32_t thk = sm.cand[k - 1];
+    const uint32_t* srt;  // the candidates' keys in descending order
+    if (n <= kBlock) {
+        const uint32_t key = tid < n ? sm.cand[tid] : 0u;
+        const int rk = tid < n ? desc_rank(sm.cand, n, tid, key) : 0;
+        if (tid < n) sm.lanekey[rk] = key;  // the lane maxima are no longer needed
+        __syncthreads();
+        srt = sm.lanekey;
+    } else {
+        int n2 = 1;
+        while (n2 < n) n2 <<= 1;
+        for (int j = n + tid; j < n2; j += kBlock) sm.cand[j] = 0u;  // below every real key
+        bitonic_desc(sm.cand, n2);
+        srt = sm.cand;
+    }
+    const uint32_t thk = srt[k - 1];
     int nk = k;  // ties at the k-th key are kept
-    while (nk < n && sm.cand[nk] == thk) ++nk;
+    while (nk < n && srt[nk] == thk) ++nk;
     // fixed-point masses over the sorted keys: lane t owns a contiguous run of them
     const int per = (nk + kBlock - 1) / kBlock;
     const int j0 = min(nk, tid * per), j1 = min(nk, j0 + per);
     unsigned long long v3[3] = {0ull, 0ull, 0ull}, ex[3], tot[3];
     for (int j = j0; j < j1; ++j)
-        v3[0] += (unsigned long long)(ex2((key_value(sm.cand[j]) - M) * s2) * fscale);
+        v3[0] += (unsigned long long)(ex2((key_value(srt[j]) - M) * s2) * fscale);
     block_scan3(v3, ex, tot, sm);
     uint32_t th = thk;
     unsigned long long kept = tot[0];
@@ -3209,7 +3288,7 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
         // the first sorted position whose inclusive prefix reaches the need
         unsigned long long acc = ex[0];
         for (int j = j0; j < j1; ++j) {
-            acc += (unsigned long long)(ex2((key_value(sm.cand[j]) - M) * s2) * fscale);
+            acc += (unsigned long long)(ex2((key_value(srt[j]) - M) * s2) * fscale);
             if ((double)acc >= need) {
                 atomicMin(&sm.pick, j);
                 break;
@@ -3217,12 +3296,12 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
         }
         __syncthreads();
         const int jp = sm.pick;
-        th = sm.cand[jp];
+        th = srt[jp];
         // kept mass: every token with key >= th (ties of the threshold included)
         unsigned long long part = 0ull;
         for (int j = j0; j < j1; ++j)
-            if (sm.cand[j] >= th)
-                part += (unsigned long long)(ex2((key_value(sm.cand[j]) - M) * s2) * fscale);
+            if (srt[j] >= th)
+                part += (unsigned long long)(ex2((key_value(srt[j]) - M) * s2) * fscale);
         unsigned long long p3[3] = {part, 0ull, 0ull}, e3[3], t3[3];
         block_scan3(p3, e3, t3, sm);
         kept = t3[0];

@@ -188,3 +188,35 @@ def test_fp32_rows_beyond_the_batch_record(V):
     holds, so the second pass reads the whole row again."""
     c = wl.make_chain_logits(5, seed=V % 97, B=3, G=2, V=V, dtype=wl.F32, top_k=50, top_p=0.9)
     check(c, f"fp32 V={V} k=50 p=0.9")
+
+
+@pytest.mark.parametrize("width", [200, 600, 1800])
+def test_recorded_batches_beyond_the_list(width):
+    """Long bf16 rows with `width` tied tokens at the top, scattered at random: every
+    batch of the first pass that holds one of them is read back by the candidate pass.
+    About 200 and 550 such batches fit the list that spreads their loads over the
+    workgroup; about 1500 (width 1800) do not, and the lanes read their batches one by
+    one instead.  200 candidates are ordered by rank, 600 and 1800 by the sorting
+    network.  All must match the oracle."""
+    import dataclasses
+    c = wl.make_chain_logits(5, seed=width, B=4, G=2, top_k=100, top_p=0.9)
+    rng = np.random.default_rng(width)
+    tl = wl.logits_as_f32(c.logits, c.dtype).copy()
+    dl = wl.logits_as_f32(c.draft_logits, c.dtype).copy()
+    for b in range(c.B):
+        for i in range(c.R):
+            ids = rng.choice(c.V, size=width, replace=False)
+            tl[b, i, ids] = tl[b, i].max() + 1.0
+            if i < c.G:
+                dids = rng.choice(c.V, size=width, replace=False)
+                dl[b, i, dids] = dl[b, i].max() + 1.0
+    c2 = dataclasses.replace(c, logits=wl.f32_to_bf16_bits(tl), draft_logits=wl.f32_to_bf16_bits(dl))
+    check(c2, f"{width} tied top tokens scattered over V={c.V}")
+
+
+def test_bench_shape():
+    """The benchmark's filtered workload itself: B=256, G=4, V=152064 bf16, top-k 50 and
+    top-p 0.9 for every request, at the launch configuration the benchmark times."""
+    c = wl.make_chain_logits(5, top_k=50, top_p=0.9)
+    assert c.B == 256
+    check(c, "bench shape B=256 k=50 p=0.9")
