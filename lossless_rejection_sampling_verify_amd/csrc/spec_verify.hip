@@ -2903,9 +2903,9 @@ struct FilterSmem {
             uint32_t cnt[kWaves][kHistBins];  // one private histogram per wave
             unsigned long long mass[kWaves][kHistBins];
         };
-        uint32_t cand[kCandCap];  // direct selection: candidate keys
+        alignas(16) uint32_t cand[kCandCap];  // direct selection: candidate keys
     };
-    uint32_t lanekey[kBlock];  // lane maxima's keys; then the sorted candidates (n <= kBlock)
+    alignas(16) uint32_t lanekey[kBlock];  // lane maxima's keys; then the sorted candidates (n <= kBlock)
     uint16_t bkey[kMaxBatchRec * kBlock];  // batch maxima of the first pass (key top bits)
     uint16_t item[kItemCap];               // the batches the candidate pass reads (j * kBlock + t)
     int ncand;
@@ -3133,13 +3133,47 @@ __device__ inline float key_value(uint32_t key) {
 // Descending rank of this thread's key among the n keys a[0..n) (this thread's being a[i]):
 // the keys above it, plus the equal keys at lower positions, so the ranks of the n keys
 // are 0..n-1 without repeats, and placing each key at its rank sorts them descending.
+// `a` is 16-byte aligned; the keys are read four at a time.
 __device__ inline int desc_rank(const uint32_t* a, int n, int i, uint32_t key) {
+    auto above = [&](uint32_t o, int j) { return (o > key) | ((o == key) & (j < i)); };
     int r = 0;
-    for (int j = 0; j < n; ++j) {
-        const uint32_t o = a[j];
-        r += (o > key || (o == key && j < i)) ? 1 : 0;
+    const int n4 = n & ~3;
+#pragma unroll 8
+    for (int j = 0; j < n4; j += 4) {
+        const uint4 o = *reinterpret_cast<const uint4*>(a + j);
+        r += above(o.x, j) + above(o.y, j + 1) + above(o.z, j + 2) + above(o.w, j + 3);
     }
+    for (int j = n4; j < n; ++j) r += above(a[j], j);
     return r;
+}
+
+// The wave's 64 keys sorted in descending order across its lanes (lane 0 the largest), by
+// a bitonic network of cross-lane exchanges.
+__device__ inline uint32_t wave_sort_desc(uint32_t key) {
+    const int lane = threadIdx.x & 63;
+    for (int size = 2; size <= 64; size <<= 1) {
+        const bool desc = (lane & size) == 0;  // this lane's block of `size` runs descending
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)key, stride);
+            const bool lower = (lane & stride) == 0;
+            key = (lower == desc) ? max(key, other) : min(key, other);
+        }
+    }
+    return key;
+}
+
+// Number of entries of the descending list a[0..64) above `key` (strict: > key; else >= key).
+__device__ inline int count_above(const uint32_t* a, uint32_t key, bool strict) {
+    int lo = 0, hi = 64;  // a[i] is above key for every i < lo, for no i >= hi
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const bool above = strict ? a[mid] > key : a[mid] >= key;
+        if (above)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
 }
 
 // Direct top-k (k <= kBlock) then top-p on the top-k set, for rows whose candidates fit in
@@ -3150,9 +3184,11 @@ __device__ inline int desc_rank(const uint32_t* a, int n, int i, uint32_t key) {
 // kept mass are the ones the radix selection finds.  Returns false (nothing decided)
 // when the candidates do not fit.
 //
-// The k-th lane maximum, and the order of at most kBlock candidates, come from ranks
-// (each thread counts the keys above its own) rather than from a sorting network: a few
-// hundred LDS reads per thread instead of dozens of barrier-separated stages.
+// The k-th lane maximum comes from ranks: each wave sorts its 64 lane maxima across its
+// lanes, and a key's rank among all 256 is its place in its own wave's list plus, from
+// each other wave's list, a binary search for the keys above it.  The order of at most
+// kBlock candidates also comes from ranks (each thread counts the candidates above its
+// own).  Either replaces a sorting network's dozens of barrier-separated stages.
 //
 // With `rec` the first pass left every batch's maximum in sm.bkey (a row without NaN whose
 // full batches fit the record): only batches whose maximum reaches the bound are read
@@ -3166,12 +3202,19 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
                               unsigned long long* kept_out, FilterSmem& sm) {
     const int tid = threadIdx.x;
     constexpr int kVec = Ld<T>::kVec;
-    const uint32_t mykey = order_key(lane_max);
-    sm.lanekey[tid] = mykey;
-    if (tid == 0) sm.ncand = 0;
-    __syncthreads();
-    if (desc_rank(sm.lanekey, kBlock, tid, mykey) == k - 1) sm.lbkey = mykey;  // one thread
-    __syncthreads();
+    {
+        // keys ordered by value, then wave, then place in the wave: every rank is unique
+        const int lane = tid & 63, wave = tid >> 6;
+        const uint32_t mykey = wave_sort_desc(order_key(lane_max));
+        sm.lanekey[tid] = mykey;
+        if (tid == 0) sm.ncand = 0;
+        __syncthreads();
+        int rk = lane;
+        for (int o = 0; o < kWaves; ++o)
+            if (o != wave) rk += count_above(sm.lanekey + 64 * o, mykey, o > wave);
+        if (rk == k - 1) sm.lbkey = mykey;  // one thread
+        __syncthreads();
+    }
     const uint32_t lb = sm.lbkey;
     auto visit = [&](float x) {
         const uint32_t key = order_key(x);
@@ -3320,7 +3363,10 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     const int b = draft ? (r - a.B * R) / G : r / R;
     const T* rowp = draft ? reinterpret_cast<const T*>(a.dlogits) + (size_t)(r - a.B * R) * V
                           : reinterpret_cast<const T*>(a.logits) + (size_t)r * V;
+    // the request's knobs are read before the pass and waited for after it
     const float Tf = a.temperature[b];
+    const int k = a.top_k ? a.top_k[b] : 0;
+    const float tp = a.top_p ? a.top_p[b] : 1.f;
     const float s2 = kLog2e / Tf;
     float lane_max;
     // the batch record covers every full batch of a lane when the row has at most
@@ -3333,8 +3379,6 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     fr.M = st.m;
     fr.th = 0u;
     fr.Z = st.z;
-    const int k = a.top_k ? a.top_k[b] : 0;
-    const float tp = a.top_p ? a.top_p[b] : 1.f;
     const bool fk = k > 0 && k < V;
     const bool fp = tp > 0.f && tp < 1.f;
     const bool t_ok = isfinite(Tf) && Tf > 0.f;
