@@ -385,13 +385,18 @@ def _workload_modes(torch, dev, api, wl, stream):
         g_ms, c_ms, acc_g, acc_c = _timed_pair(torch, api, d, stream, reps, warm=10)
         esize = 2 if c.dtype == wl.BF16 else 4
         gb, cb, egb, ecb, rej = _path_bytes(c, acc_g, acc_c, esize)
+        # medians: these calls are a few microseconds, and a stray slow launch skews a mean
+        gm, cm = float(np.median(g_ms)), float(np.median(c_ms))
         out[c.name] = {
             "greedy": dict(_stats(g_ms), path_bytes=gb,
-                           frac_path=gb / (g_ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           positions_per_s=c.B * c.R / (g_ms.mean() * 1e-3)),
+                           frac_path=gb / (gm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           positions_per_s=c.B * c.R / (gm * 1e-3),
+                           tokens_per_s=int((acc_g + 1).sum()) / (gm * 1e-3),
+                           rows_consulted=int((acc_g + 1).sum()), of=c.B * c.R),
             "chain": dict(_stats(c_ms), path_bytes=cb,
-                          frac_path=cb / (c_ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                          positions_per_s=c.B * c.R / (c_ms.mean() * 1e-3),
+                          frac_path=cb / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          positions_per_s=c.B * c.R / (cm * 1e-3),
+                          tokens_per_s=int((acc_c + 1).sum()) / (cm * 1e-3),
                           rows_consulted=int((acc_c + 1).sum()), of=c.B * c.R),
             "bound": "latency (a few rows per request)" if cfg < 3 else "hbm + latency tail",
         }
@@ -496,13 +501,18 @@ def _tree_modes(args, torch, dev, api, wl):
         de, _ = timed(mode, {"path": "eager"})
         eager = t.B * t.N * t.V * 2
         path = int((acc + 1).sum()) * t.V * 2   # the rows of the nodes the walk reaches
-        out[name] = {"workload": t.name, "avg_ms": float(d.mean()),
-                     "positions/s": t.B * t.N / (d.mean() * 1e-3),
+        # medians: under a profiler the first calls of each kernel run much longer
+        md, mde = float(np.median(d)), float(np.median(de))
+        out[name] = {"workload": t.name, "avg_ms": float(d.mean()), "median_ms": md,
+                     "positions/s": t.B * t.N / (md * 1e-3),
                      "path_only_bytes": path,
-                     "GB/s_path_only": path / (d.mean() * 1e-3) / 1e9,
-                     "eager_avg_ms": float(de.mean()), "eager_bytes": eager,
-                     "GB/s_eager": eager / (de.mean() * 1e-3) / 1e9,
-                     "frac_eager": eager / (de.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                     "GB/s_path_only": path / (md * 1e-3) / 1e9,
+                     "frac_path_only": path / (md * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "levels_walked_max": int(acc.max()) + 1,
+                     "us_per_level_longest": md * 1e3 / (int(acc.max()) + 1),
+                     "eager_median_ms": mde, "eager_bytes": eager,
+                     "GB/s_eager": eager / (mde * 1e-3) / 1e9,
+                     "frac_eager": eager / (mde * 1e-3) / 1e9 / HBM_PEAK_GBS}
     out["tree_mss"] = _tree_mss_mode(torch, dev, api, wl, stream)
     # committing the accepted paths' KV (the step after verify): 128 KiB per token, the KV
     # of 32 layers x 8 KV heads x 128 dims x (K, V) in bf16
@@ -594,10 +604,12 @@ def _tree_mss_mode(torch, dev, api, wl, stream):
     acc, nodes = acc.cpu().numpy(), nodes.cpu().numpy()
     path = _mss_path_bytes(t, acc, nodes, wl)
     del flush, lg, q
-    return {"workload": t.name, "avg_ms": float(d.mean()),
-            "positions/s": t.B * t.N / (d.mean() * 1e-3),
+    md = float(np.median(d))
+    return {"workload": t.name, "avg_ms": float(d.mean()), "median_ms": md,
+            "positions/s": t.B * t.N / (md * 1e-3),
             "accepted_mean": float(acc.mean()), "path_only_bytes": path,
-            "GB/s_path_only": path / (d.mean() * 1e-3) / 1e9}
+            "GB/s_path_only": path / (md * 1e-3) / 1e9,
+            "frac_path_only": path / (md * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def _filtered_mode(args, torch, dev, api, wl):
@@ -632,11 +644,13 @@ def _filtered_mode(args, torch, dev, api, wl):
     t = np.array([a.elapsed_time(b) for a, b in ev])
     es = 2 if c.dtype == wl.BF16 else 4
     once = (c.B * c.R + c.B * c.G) * c.V * es
+    md = float(np.median(t))
     return {"chain_filtered": {"workload": c.name + ", top-k 50, top-p 0.9",
-                               "avg_ms": float(t.mean()),
-                               "positions/s": c.B * c.R / (t.mean() * 1e-3),
+                               "avg_ms": float(t.mean()), "median_ms": md,
+                               "positions/s": c.B * c.R / (md * 1e-3),
                                "row_bytes_once": once,
-                               "GB/s_rows_once": once / (t.mean() * 1e-3) / 1e9,
+                               "GB/s_rows_once": once / (md * 1e-3) / 1e9,
+                               "frac_rows_once": once / (md * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "accepted_mean": float(acc.float().mean().item())}}
 
 
