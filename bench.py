@@ -265,23 +265,23 @@ def main():
             "avg_launch_ms": float(chain_ms.mean()),
         },
         "modes": {
-            "greedy": {"avg_ms": float(greedy_ms.mean()), "p90_ms": float(np.percentile(greedy_ms, 90)),
+            "greedy": {"avg_ms": float(greedy_ms.mean()), "median_ms": float(np.median(greedy_ms)), "p90_ms": float(np.percentile(greedy_ms, 90)),
                        "GB/s": greedy_gbs, "frac": greedy_gbs / HBM_PEAK_GBS,
                        "bytes": greedy_bytes,
                        "positions/s": B * R / (greedy_ms.mean() * 1e-3),
                        "rows_consulted": int((acc_g + 1).sum()),
                        "tokens/s": float((acc_g + 1).sum()) / (greedy_ms.mean() * 1e-3)},
-            "chain": {"avg_ms": float(chain_ms.mean()), "p90_ms": float(np.percentile(chain_ms, 90)),
+            "chain": {"avg_ms": float(chain_ms.mean()), "median_ms": float(np.median(chain_ms)), "p90_ms": float(np.percentile(chain_ms, 90)),
                       "GB/s": chain_gbs, "frac": chain_gbs / HBM_PEAK_GBS,
                       "bytes": chain_bytes,
                       "positions/s": B * R / (chain_ms.mean() * 1e-3),
                       "rejected_requests": rejected,
                       "rows_consulted": int((acc_c + 1).sum()),
                       "tokens/s": float((acc_c + 1).sum()) / (chain_ms.mean() * 1e-3)},
-            "greedy_eager": {"avg_ms": float(ge.mean()), "bytes": eager_g_bytes,
+            "greedy_eager": {"avg_ms": float(ge.mean()), "median_ms": float(np.median(ge)), "bytes": eager_g_bytes,
                              "GB/s": eager_g_bytes / (ge.mean() * 1e-3) / 1e9,
                              "frac": eager_g_bytes / (ge.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS},
-            "chain_eager": {"avg_ms": float(ce.mean()), "bytes": eager_c_bytes,
+            "chain_eager": {"avg_ms": float(ce.mean()), "median_ms": float(np.median(ce)), "bytes": eager_c_bytes,
                             "GB/s": eager_c_bytes / (ce.mean() * 1e-3) / 1e9,
                             "frac": eager_c_bytes / (ce.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS},
         },
