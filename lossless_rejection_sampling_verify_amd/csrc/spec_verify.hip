@@ -2665,24 +2665,49 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     const float* coins = a.coins + (size_t)b * N;
     const T* logits = reinterpret_cast<const T*>(a.logits);
     bool bad = false, gaveup = false;
-    for (int i = tid; i < N; i += kBlock) {
-        const int p = par_g[i];
-        const int t = tok_g[i];
-        sm.par[i] = p;
-        sm.tok[i] = t;
-        if (i == 0) {
-            if (p != -1) bad = true;
-        } else {
-            if (p < 0 || p >= i) bad = true;
-            if (t < 0 || t >= V) bad = true;
-        }
-        const float u = coins[i];
-        if (!(u > 0.f && u <= 1.f)) bad = true;
-    }
     const float Tf = a.temperature[b];
-    if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
     const double Td = (double)Tf;
     const float s2 = kLog2e / Tf;
+    int step = 0;  // the next hand-off step
+
+    // A node's slice pass, handed to the cluster; the wait comes later, so that what does
+    // not need the row statistics overlaps the hand-off.
+    auto pass = [&](int node) {
+        const T* rowp = logits + ((size_t)b * N + node) * V;
+        const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+        cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z), dbl_lo(r.z), xs);
+    };
+
+    // The tree's arrays are loaded first and the root's pass runs while they arrive; the
+    // tree is checked, and the drafted tokens' q values gathered, while the root's
+    // hand-off travels.  The root row is in bounds whatever the tree holds, and a request
+    // found invalid never waits for its words.
+    constexpr int kPer = SPEC_MAX_N / kBlock;
+    int pr[kPer], tr[kPer];
+    float ur[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int i = tid + c * kBlock;
+        pr[c] = i < N ? par_g[i] : 0;
+        tr[c] = i < N ? tok_g[i] : 0;
+        ur[c] = i < N ? coins[i] : 1.f;
+    }
+    pass(0);
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int i = tid + c * kBlock;
+        if (i >= N) break;
+        sm.par[i] = pr[c];
+        sm.tok[i] = tr[c];
+        if (i == 0) {
+            if (pr[c] != -1) bad = true;
+        } else {
+            if (pr[c] < 0 || pr[c] >= i) bad = true;
+            if (tr[c] < 0 || tr[c] >= V) bad = true;
+        }
+        if (!(ur[c] > 0.f && ur[c] <= 1.f)) bad = true;
+    }
+    if (!(isfinite(Tf) && Tf > 0.f)) bad = true;
     bad = __syncthreads_or(bad);
     if (!bad) {  // depths, and q of every child's token under its parent's draft row
         tree_depths(sm.par, N, sm.anc, sm.dep);
@@ -2697,13 +2722,15 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         bad = __syncthreads_or(bad);
     }
 
-    int cur = 0, d = 0, step = 0;
+    int cur = 0, d = 0;
     int kind = kDrawTarget;
     float cq = 0.f, M = 0.f;
     double Z = 1.0;
     while (!bad) {
         const T* rowp = logits + ((size_t)b * N + cur) * V;
-        int count = 0;  // children of cur in ascending node id (ordered compaction)
+        // while cur's words travel: its children in ascending node id (ordered compaction)
+        // and their tokens' logits
+        int count = 0;
         for (int base = cur + 1; base < N; base += kBlock) {
             const int c = base + tid;
             const bool f = c < N && sm.par[c] == cur;
@@ -2721,9 +2748,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         }
         for (int j = tid; j < count; j += kBlock) sm.lx[j] = Ld<T>::one(rowp + sm.tok[sm.kids[j]]);
         {
-            const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
-            if (!cluster_step(slots, step++, W, w, tag, a.spin, __float_as_uint(r.m),
-                              dbl_hi(r.z), dbl_lo(r.z), xs)) {
+            if (!cluster_wait(slots, step++, W, tag, a.spin, xs)) {
                 bad = gaveup = true;
                 break;
             }
@@ -2784,6 +2809,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         if (bad || chosen < 0) break;
         cur = chosen;
         ++d;
+        pass(cur);
     }
 
     DrawState st = {};
