@@ -1124,16 +1124,19 @@ __device__ inline double lane_dbl(double v, int j) {
 
 // A row's normaliser from its slices' (max, sum) records after a cluster step (xp[j][0]
 // the max, xp[j][1..2] the fp64 sum of exp2((l - max) * s2)): the sum over members j, in
-// member order, of z_j exp((m_j - M) / T).  Lane j of each wave evaluates member j's
+// member order, of z_j exp2((m_j - M) * s2).  Lane j of each wave evaluates member j's
 // term, so the W exponentials run side by side instead of one after another; every lane
 // then adds the terms in the same order, so all threads of all members hold the same bits.
+// The exponential is the row passes' own fp32 one: each z_j is a sum of such
+// exponentials, so an fp64 one here would add latency, not accuracy.
 __device__ inline double cluster_norm(const XSmem& xs, int W, float M, double Td) {
     const int lane = threadIdx.x & 63;
+    const float s2 = kLog2e / (float)Td;
     double term = 0.0;
     if (lane < W) {
         const float mj = __uint_as_float(xs.xp[lane][0]);
         if (mj != -INFINITY)
-            term = dbl_of(xs.xp[lane][1], xs.xp[lane][2]) * exp(((double)mj - (double)M) / Td);
+            term = dbl_of(xs.xp[lane][1], xs.xp[lane][2]) * (double)ex2((mj - M) * s2);
     }
     double Z = 0.0;
     for (int j = 0; j < W; ++j) Z += lane_dbl(term, j);
@@ -2052,7 +2055,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             if (xi < 0 || xi >= V || !(ui > 0.f && ui <= 1.f) || !(qx >= 0.f && isfinite(qx))) {
                 flag = 2;
             } else {
-                const double p = exp(((double)lx - (double)M) / Td) / Z;
+                const double p = (double)ex2((lx - M) * s2) / Z;
                 const double q = (double)qx;
                 flag = (q > 0.0 ? (p > 0.0 && (double)ui <= p / q) : p > 0.0) ? 1 : 0;
                 sp[i] = (float)p;
@@ -2108,7 +2111,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
                 const float mj = __uint_as_float(xs.xp[tid & 63][0]);
                 const double tj = mj == -INFINITY ? 0.0
                                                   : dbl_of(xs.xp[tid & 63][1], xs.xp[tid & 63][2]) *
-                                                        exp(((double)mj - (double)M) / Td) / Z;
+                                                        (double)ex2((mj - M) * s2) / Z;
                 mine = tj >= 1e-30 ? tj : 0.0;
             }
             double tot = 0.0;
@@ -2413,8 +2416,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
             int ch = -1;
             for (int c0 = 0; c0 < count && ch < 0; c0 += 64) {
                 const int j = c0 + lane;
-                const double mine =
-                    j < count ? exp(((double)ts.lx[j] - (double)M) / Td) / Z : 0.0;
+                const double mine = j < count ? (double)ex2((ts.lx[j] - M) * s2) / Z : 0.0;
                 const int n = min(64, count - c0);
                 for (int e = 0; e < n; ++e) {
                     const double pc = lane_dbl(mine, e);
@@ -2770,7 +2772,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         for (int j = 0; j < count; ++j) {
             const int child = sm.kids[j];
             if (tid == 0) {
-                const double px = exp(((double)sm.lx[j] - (double)M) / Td) / Z;
+                const double px = (double)ex2((sm.lx[j] - M) * s2) / Z;
                 const double qx = (double)sm.qx[child];
                 double pr = px - c * qx;
                 pr = pr > 0.0 ? pr / Nr : 0.0;
