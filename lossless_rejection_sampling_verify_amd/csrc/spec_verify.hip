@@ -9,10 +9,11 @@
 //                   words (no fence), and every member takes the same decision.
 //   k_chain_walk    chain rejection sampling, the same way with (max, exp-sum) per slice;
 //                   after the stop each member weighs its slice of the row the last token
-//                   is drawn from, for k_draw.
+//                   is drawn from, and the cluster draws it (k_draw does when a slice
+//                   spans more than 64 fine chunks).
 //   k_tree_walk     the target-only tree walk (greedy or sampling), node by node.
 //   k_mss_walk      the tree walk by multi-step speculative sampling with draft rows;
-//                   1024-lane workgroups, a residual pass per rejected child.
+//                   a residual pass and a hand-off per rejected child.
 //   k_draw          one wave per request: locates the chunk, then the segment, then the
 //                   token holding u * total (inverse CDF in ascending token id).
 // The eager passes read every row and hand over at kernel boundaries; they are selected
