@@ -1413,7 +1413,6 @@ __global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
 struct MassSmem {
     float pw[16 * kStageRow];  // plain target weight of each quad of a chunk (stage_slot)
     float ww[16 * kStageRow];  // draw weight of the same
-    double xs[kSegs];      // excluded weight of each segment
 };
 
 // Two chunks' staging, weighed together and summed by waves 0 and 1 (the walks).
@@ -1445,6 +1444,38 @@ __device__ inline WParams draw_params(const KArgs& a, const DrawState& st, const
     return W;
 }
 
+// Tree draws: the rejected children's tokens weigh nothing.  Every quad of fine chunk c
+// that holds one of them (ex[0 .. st.nexcl)) is weighed again without them: the other
+// elements' weights added in weigh4's order, which gives the bits weigh4 gives with the
+// excluded weights at zero.  Its staged draw weight (ms.ww) is replaced; the plain target
+// weight (ms.pw, for the fallback) keeps every token.  One wave; two lanes that share a
+// quad write the same value.  The caller syncs before the segment sums.
+template <typename T, bool kFilt>
+__device__ inline void exclude_quads(const KArgs& a, const DrawState& st, const WParams& W,
+                                     const T* rowp, int c, MassSmem& ms, const int32_t* ex) {
+    const int lane = threadIdx.x & 63;
+    const int c0 = c * kFine;
+    const int n = min(kFine, a.V - c0);
+    for (int e = lane; e < st.nexcl; e += 64) {
+        const int t = ex[e];
+        if (t < c0 || t >= c0 + n) continue;
+        const int q = (t - c0) >> 2;
+        float w4 = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int j = c0 + 4 * q + i;
+            if (j >= c0 + n) break;
+            bool out = false;
+            for (int f = 0; f < st.nexcl && !out; ++f) out = ex[f] == j;
+            if (!out) {
+                float p;
+                draw_weight<T, 0, kFilt>(rowp, nullptr, j, W, p);
+                w4 += p;
+            }
+        }
+        ms.ww[stage_slot(q)] = w4;
+    }
+}
+
 // Segment and chunk sums of fine chunk c, whose per-quad weights `chunk_weights` left in
 // sm.pw / sm.ww: each segment's weight (and the chunk's) in a.seg / a.mass, the plain
 // target weight in a.massfb.  Block-wide.
@@ -1455,21 +1486,9 @@ __device__ __attribute__((always_inline)) void mass_reduce(const KArgs& a, const
                                                            const int32_t* ex) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int S2 = a.S2;
-    const int c0 = c * kFine;
-    const int n = min(kFine, a.V - c0);
-    if (tid < kSegs) sm.xs[tid] = 0.0;
-    __syncthreads();
-    if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
-        if (tid == 0) {
-            for (int e = 0; e < st.nexcl; ++e) {
-                const int t = ex[e];
-                if (t >= c0 && t < c0 + n) {
-                    float p;
-                    draw_weight<T, 0, kFilt>(rowp, nullptr, t, W, p);
-                    sm.xs[(t - c0) / kSeg] += (double)p;
-                }
-            }
-        }
+    __syncthreads();  // the staging is complete
+    if (st.nexcl > 0) {  // tree: the rejected children's quads, weighed again without them
+        if (tid < 64) exclude_quads<T, kFilt>(a, st, W, rowp, c, sm, ex);
         __syncthreads();
     }
     if (tid < kSegs) {  // wave 0: lane g sums segment g in ascending order
@@ -1478,10 +1497,6 @@ __device__ __attribute__((always_inline)) void mass_reduce(const KArgs& a, const
         for (int i = 0; i < 16; ++i) {
             Wt += (double)sm.ww[i * kStageRow + tid];  // quad 16 * tid + i
             P += (double)sm.pw[i * kStageRow + tid];
-        }
-        if (sm.xs[tid] > 0.0) {
-            const double rem = Wt - sm.xs[tid];
-            Wt = rem > Wt * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
         }
         a.seg[((size_t)b * S2 + c) * kSegs + tid] = Wt;
         Wt = wave_sum(Wt);
@@ -1535,21 +1550,9 @@ __device__ __attribute__((always_inline)) void mass_reduce_pair(const KArgs& a,
     const int S2 = a.S2;
     const int c = wv == 0 ? cA : (wv == 1 ? cB : -1);  // the chunk this wave sums
     MassSmem& ms = sm.s[wv & 1];
-    if (wv < 2) ms.xs[lane] = 0.0;
-    __syncthreads();
-    if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
-        if (lane == 0 && c >= 0) {
-            const int c0 = c * kFine;
-            const int n = min(kFine, a.V - c0);
-            for (int e = 0; e < st.nexcl; ++e) {
-                const int t = ex[e];
-                if (t >= c0 && t < c0 + n) {
-                    float p;
-                    draw_weight<T, 0, kFilt>(rowp, nullptr, t, W, p);
-                    ms.xs[(t - c0) / kSeg] += (double)p;
-                }
-            }
-        }
+    __syncthreads();  // the staging is complete
+    if (st.nexcl > 0) {  // tree: the rejected children's quads, weighed again without them
+        if (c >= 0) exclude_quads<T, kFilt>(a, st, W, rowp, c, ms, ex);
         __syncthreads();
     }
     if (c >= 0) {  // lane g sums segment g in ascending order
@@ -1558,10 +1561,6 @@ __device__ __attribute__((always_inline)) void mass_reduce_pair(const KArgs& a,
         for (int i = 0; i < 16; ++i) {
             Wt += (double)ms.ww[i * kStageRow + lane];  // quad 16 * lane + i
             P += (double)ms.pw[i * kStageRow + lane];
-        }
-        if (ms.xs[lane] > 0.0) {
-            const double rem = Wt - ms.xs[lane];
-            Wt = rem > Wt * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
         }
         a.seg[((size_t)b * S2 + c) * kSegs + lane] = Wt;
         Wt = wave_sum(Wt);
@@ -1714,21 +1713,9 @@ __device__ __attribute__((always_inline)) void mass_reduce_quad(const KArgs& a,
     const int S2 = a.S2;
     const int c = c0 + wv < cend ? c0 + wv : -1;  // the chunk this wave sums
     MassSmem& ms = sm.s[wv];
-    ms.xs[lane] = 0.0;
-    __syncthreads();
-    if (st.nexcl > 0) {  // tree: the rejected children's weight, per segment
-        if (lane == 0 && c >= 0) {
-            const int cc0 = c * kFine;
-            const int n = min(kFine, a.V - cc0);
-            for (int e = 0; e < st.nexcl; ++e) {
-                const int t = ex[e];
-                if (t >= cc0 && t < cc0 + n) {
-                    float p;
-                    draw_weight<T, 0, kFilt>(rowp, nullptr, t, W, p);
-                    ms.xs[(t - cc0) / kSeg] += (double)p;
-                }
-            }
-        }
+    __syncthreads();  // the staging is complete
+    if (st.nexcl > 0) {  // tree: the rejected children's quads, weighed again without them
+        if (c >= 0) exclude_quads<T, kFilt>(a, st, W, rowp, c, ms, ex);
         __syncthreads();
     }
     if (c >= 0) {  // lane g sums segment g in ascending order
@@ -1737,10 +1724,6 @@ __device__ __attribute__((always_inline)) void mass_reduce_quad(const KArgs& a,
         for (int i = 0; i < 16; ++i) {
             Wt += (double)ms.ww[i * kStageRow + lane];  // quad 16 * lane + i
             P += (double)ms.pw[i * kStageRow + lane];
-        }
-        if (ms.xs[lane] > 0.0) {
-            const double rem = Wt - ms.xs[lane];
-            Wt = rem > Wt * 1e-6 ? rem : 0.0;  // below that it is only rounding residue
         }
         a.seg[((size_t)b * S2 + c) * kSegs + lane] = Wt;
         Wt = wave_sum(Wt);

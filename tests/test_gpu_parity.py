@@ -248,7 +248,7 @@ def check_greedy(c, label, tokens=None):
                    ["accept_len", "out_tokens"], None, probs=False, label=label)
 
 
-def check_tree(t, mode, label, **kw):
+def check_tree(t, mode, label, max_near=None, **kw):
     say(f"tree {label}: B={t.B} N={t.N} D={kw.get('D', t.D)} V={t.V} mode={mode}")
     g = gpu_tree(t, mode, **kw)
     D = kw.get("D", t.D)
@@ -261,6 +261,7 @@ def check_tree(t, mode, label, **kw):
         o["probs"] = np.zeros_like(o["probs"])
         return compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"], None, label=label)
     return compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"], o["margin"], label=label,
+                   max_near=max_near,
                    recheck=tree_recheck(t, mode, D, kw.get("th_single", 1.0), kw.get("th_acc", 1.0),
                                         kw.get("parents", t.parents), kw.get("tokens", t.node_tokens),
                                         kw.get("coins", t.coins),
@@ -520,6 +521,44 @@ def test_tree_walk_cluster_widths(cluster, mode, launch):
     launch.update(cluster=int(cluster))
     t = wl.make_tree(4, seed=41, B=12, N=40, V=30011, D=5, max_children=5)
     check_tree(t, mode, f"tree walk W<={cluster} mode {mode}")
+
+
+@pytest.mark.parametrize("dtype,eager", [(wl.F32, False), (wl.BF16, False), (wl.F32, True)])
+def test_tree_residual_of_one_tiny_token(dtype, eager, launch):
+    """Every token but one is a rejected child of the root, and the remaining token holds
+    about 2e-9 of the row's mass: the final draw must emit that token, as the oracle does.
+    (The excluded tokens' quads are weighed again without them; a residual formed by
+    subtracting their weights from the segment's would be rounding noise of that size.)"""
+    import dataclasses
+    if eager:
+        launch["path"] = "eager"
+    V, N, B = 64, 64, 4
+    t = wl.make_tree(4, seed=5, B=B, N=2, V=V, D=1, dtype=dtype)
+    rng = np.random.default_rng(17)
+    logits = rng.standard_normal((B, N, V)).astype(np.float32)
+    parents = np.zeros((B, N), np.int32)
+    parents[:, 0] = -1
+    tokens = np.full((B, N), -1, np.int32)
+    rest = np.zeros(B, np.int64)
+    for b in range(B):
+        row = logits[b, 0]
+        keep = int(rng.integers(0, V))
+        row[keep] = row.min() - 20.0          # exp(-20): about 2e-9 of the mass
+        rest[b] = keep
+        tokens[b, 1:] = [j for j in range(V) if j != keep]
+    enc = (lambda f: wl.f32_to_bf16_bits(f)) if dtype == wl.BF16 else (lambda f: f)
+    # coin 1 against prob_acc / 1.5 <= 2/3: every child is rejected, far from the threshold
+    coins = np.ones((B, 2), np.float32)
+    coins[:, 1] = rng.uniform(0.05, 1.0, B).astype(np.float32)
+    t2 = dataclasses.replace(t, N=N, logits=enc(logits), node_tokens=tokens, parents=parents,
+                             coins=coins, temperature=np.ones(B, np.float32))
+    say(f"tree, one tiny token left {dtype} eager={eager}")
+    g = gpu_tree(t2, oracle.TREE_SAMPLING, th_acc=1.5)
+    o = oracle.verify_tree(t2.logits, dtype, tokens, parents, coins, t2.temperature, 1,
+                           oracle.TREE_SAMPLING, 1.0, 1.5)
+    assert (o["accept_len"] == 0).all() and (o["out_tokens"][:, 0] == rest).all()
+    np.testing.assert_array_equal(g["accept_len"], o["accept_len"])
+    np.testing.assert_array_equal(g["out_tokens"], o["out_tokens"])
 
 
 def test_tree_rows_off_the_walk():

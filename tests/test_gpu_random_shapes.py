@@ -1,0 +1,131 @@
+"""Seeded random shapes and launch options: the HIP path against the oracle.
+
+Each case draws its shape (batch, draft length or tree size and depth, a vocabulary
+between 1 and 60000 tokens, log-uniform), dtype, temperature, logit spread and launch
+options (walk or eager path, cluster width, split count, row loads) from a generator
+seeded with the case number, builds the inputs with the workload generators, and holds
+every output to the bar of test_gpu_parity.compare: bit-exact outside the near-tie band,
+near-ties counted and bounded, and every near-tie that differs reached by the oracle with
+a coin nudged by a rounding-sized amount.  The shapes are small, so the file runs in
+seconds; the cases are fixed by their seeds, so a failure names its case and repeats.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_rejection_sampling_verify_amd import workloads as wl
+
+from test_gpu_parity import (check_chain, check_greedy, check_tree, launch,  # noqa: F401
+                             say)
+from test_gpu_mss import check_mss
+from test_gpu_filtered import check as check_filtered
+
+pytestmark = pytest.mark.gpu
+
+SEED = 20261203
+
+
+def _rng(kind: str, i: int) -> np.random.Generator:
+    return np.random.default_rng([SEED, sum(map(ord, kind)), i])
+
+
+def _vocab(rng, hi=60000) -> int:
+    return int(np.exp(rng.uniform(0.0, np.log(hi))))
+
+
+def _dtype(rng) -> str:
+    return wl.BF16 if rng.random() < 0.6 else wl.F32
+
+
+def _chain_opts(rng) -> dict:
+    """One launch configuration: the default walk, a given cluster width, streaming row
+    loads, or the eager passes with a given split count."""
+    pick = int(rng.integers(0, 4))
+    if pick == 0:
+        return {}
+    if pick == 1:
+        return {"cluster": int(rng.choice([1, 2, 3, 5, 7, 16]))}
+    if pick == 2:
+        return {"row_loads": "streaming"}
+    return {"path": "eager", "splits": int(rng.choice([1, 3, 8, 64]))}
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_chain_and_greedy(i, launch):
+    rng = _rng("chain", i)
+    B, G, V = int(rng.integers(1, 49)), int(rng.integers(1, 11)), _vocab(rng)
+    dtype, T = _dtype(rng), float(rng.uniform(0.25, 2.5))
+    sigma, dv = float(rng.uniform(0.5, 4.0)), float(rng.uniform(0.05, 3.0))
+    opts = _chain_opts(rng)
+    launch.update(opts)
+    c = wl.make_chain(2, seed=i, B=B, G=G, V=V, dtype=dtype, T=T, sigma=sigma, draft_var=dv,
+                      boost=None)
+    label = f"random chain {i}: B={B} G={G} V={V} {dtype} T={T:.2f} {opts}"
+    say(label)
+    check_chain(c, label)
+    check_greedy(c, label.replace("chain", "greedy", 1))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_tree(i, launch):
+    rng = _rng("tree", i)
+    B, N = int(rng.integers(1, 17)), int(rng.integers(1, 81))
+    D = int(rng.integers(1 if N > 1 else 0, min(N - 1, 12) + 1))
+    kids = int(rng.integers(2, 9))
+    V, dtype = _vocab(rng, 40000), _dtype(rng)
+    T, sigma = float(rng.uniform(0.3, 2.0)), float(rng.uniform(0.5, 5.0))
+    th_single = float(rng.choice([1.0, 0.5, 0.1]))
+    th_acc = float(rng.choice([1.0, 0.7, 1.5]))
+    if rng.random() < 0.3:
+        launch.update({"path": "eager"})
+    elif rng.random() < 0.5:
+        launch.update({"cluster": int(rng.choice([1, 2, 4, 16]))})
+    try:
+        t = wl.make_tree(4, seed=i, B=B, N=N, V=max(V, N), D=D, max_children=kids, dtype=dtype,
+                         T=T, sigma=sigma)
+    except ValueError:  # the tree shape cannot hold N nodes: a wider one can
+        t = wl.make_tree(4, seed=i, B=B, N=N, V=max(V, N), D=D, max_children=N, dtype=dtype,
+                         T=T, sigma=sigma)
+    # With a vocabulary not much larger than the tree, the rejected children can cover
+    # nearly all of it, and the final draw's residual mass is then itself near zero in
+    # every such request: those margins are not a coin's distance to a threshold, so the
+    # per-call bound on near-ties does not apply (each one that differs is still checked).
+    max_near = B if t.V <= 2 * N else None
+    for mode in (oracle.TREE_GREEDY, oracle.TREE_SAMPLING):
+        label = (f"random tree {i} mode {mode}: B={B} N={N} D={D} V={t.V} {dtype} "
+                 f"th={th_single},{th_acc} {dict(launch)}")
+        check_tree(t, mode, label, max_near=max_near, th_single=th_single, th_acc=th_acc)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_multi_step_tree(i, launch):
+    rng = _rng("mss", i)
+    B, N = int(rng.integers(1, 9)), int(rng.integers(1, 41))
+    D = int(rng.integers(1 if N > 1 else 0, min(N - 1, 8) + 1))
+    kids = int(rng.integers(2, 7))
+    V, dtype = _vocab(rng, 20000), _dtype(rng)
+    T, sigma = float(rng.uniform(0.3, 2.0)), float(rng.uniform(0.5, 4.0))
+    dv = float(rng.uniform(0.05, 2.0))
+    if rng.random() < 0.5:
+        launch.update({"cluster": int(rng.choice([1, 2, 5, 16]))})
+    try:
+        t = wl.make_tree_mss(4, seed=i, B=B, N=N, V=max(V, N), D=D, max_children=kids,
+                             dtype=dtype, T=T, sigma=sigma, draft_var=dv)
+    except ValueError:
+        t = wl.make_tree_mss(4, seed=i, B=B, N=N, V=max(V, N), D=D, max_children=N,
+                             dtype=dtype, T=T, sigma=sigma, draft_var=dv)
+    check_mss(t, f"random multi-step tree {i}: B={B} N={N} D={D} V={t.V} {dtype} {dict(launch)}")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_filtered(i):
+    rng = _rng("filtered", i)
+    B, G, V = int(rng.integers(1, 25)), int(rng.integers(1, 7)), _vocab(rng)
+    dtype, T = _dtype(rng), float(rng.uniform(0.3, 2.0))
+    top_k = rng.choice([0, 1, 5, 50, 300, 5000], size=B).astype(np.int32)
+    top_p = rng.choice([1.0, 0.95, 0.8, 0.3], size=B).astype(np.float32)
+    c = wl.make_chain_logits(2, seed=i, B=B, G=G, V=V, dtype=dtype, T=T, top_k=top_k,
+                             top_p=top_p)
+    check_filtered(c, f"random filtered {i}: B={B} G={G} V={V} {dtype} T={T:.2f}")
