@@ -230,11 +230,11 @@ def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperat
     return run_b
 
 
-def check_chain(c, label):
+def check_chain(c, label, max_near=None):
     say(f"chain {label}: B={c.B} G={c.G} V={c.V} {c.dtype}")
     g = gpu_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
     o = oracle.verify_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.coins, c.temperature)
-    return compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=label,
+    return compare(g, o, ["accept_len", "out_tokens"], o["margin"], label=label, max_near=max_near,
                    recheck=chain_recheck(c.logits, c.dtype, c.draft_probs, c.draft_tokens,
                                          c.coins, c.temperature, g))
 

@@ -6,8 +6,11 @@ options (walk or eager path, cluster width, split count, row loads) from a gener
 seeded with the case number, builds the inputs with the workload generators, and holds
 every output to the bar of test_gpu_parity.compare: bit-exact outside the near-tie band,
 near-ties counted and bounded, and every near-tie that differs reached by the oracle with
-a coin nudged by a rounding-sized amount.  The shapes are small, so the file runs in
-seconds; the cases are fixed by their seeds, so a failure names its case and repeats.
+a coin nudged by a rounding-sized amount.  A second set draws from the edges of the
+input space (near-uniform bf16 rows full of ties, nearly one-hot rows, very low and high
+temperatures, drafts equal to the target, coins next to 1 or at 2^-24, extreme tree
+thresholds).  The shapes are small, so the file runs in seconds; the cases are fixed by
+their seeds, so a failure names its case and repeats.
 """
 from __future__ import annotations
 
@@ -129,3 +132,86 @@ def test_random_filtered(i):
     c = wl.make_chain_logits(2, seed=i, B=B, G=G, V=V, dtype=dtype, T=T, top_k=top_k,
                              top_p=top_p)
     check_filtered(c, f"random filtered {i}: B={B} G={G} V={V} {dtype} T={T:.2f}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_chain_extremes(i, launch):
+    """Chains at the edges of the input space: logits nearly equal (bf16 ties) or spread
+    far apart at a low or high temperature (nearly one-hot rows, underflowing weights),
+    drafts equal to the target (every residual empty: the fallback draw) or far from it,
+    and coins pinned next to 1 or to 2^-24.  Such inputs put coins at the thresholds by
+    construction (a draft equal to the target makes p/q one up to rounding), so the
+    per-call bound on near-ties does not apply; every near-tie that differs is still
+    checked against the oracle with the coin nudged.  (A coin of exactly 1 is avoided only
+    because a nudge could not move it up.)"""
+    rng = _rng("extreme", i)
+    B, G, V = int(rng.integers(1, 33)), int(rng.integers(1, 9)), _vocab(rng, 40000)
+    dtype = _dtype(rng)
+    sigma = float(rng.choice([0.01, 0.3, 8.0, 15.0]))
+    T = float(rng.choice([0.05, 0.2, 1.0, 5.0]))
+    dv = float(rng.choice([0.0, 1e-4, 1.0, 10.0]))
+    opts = _chain_opts(rng)
+    launch.update(opts)
+    c = wl.make_chain(2, seed=100 + i, B=B, G=G, V=V, dtype=dtype, T=T, sigma=sigma,
+                      draft_var=dv, boost=None)
+    pin = rng.random(c.coins.shape) < 0.2
+    c.coins[pin] = np.where(rng.random(int(pin.sum())) < 0.5, 1.0 - 2.0 ** -24,
+                            2.0 ** -24).astype(np.float32)
+    label = (f"extreme chain {i}: B={B} G={G} V={V} {dtype} sigma={sigma} T={T} "
+             f"draft_var={dv} {opts}")
+    say(label)
+    check_chain(c, label, max_near=B)
+    check_greedy(c, label.replace("chain", "greedy", 1))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_tree_extremes(i, launch):
+    """Trees on nearly uniform (bf16 ties) or nearly one-hot rows, at a very low or high
+    temperature, with extreme thresholds; near-ties by construction, as above."""
+    rng = _rng("tree-extreme", i)
+    B, N = int(rng.integers(1, 13)), int(rng.integers(2, 65))
+    D = int(rng.integers(1, min(N - 1, 10) + 1))
+    V, dtype = _vocab(rng, 30000), _dtype(rng)
+    sigma = float(rng.choice([0.01, 0.3, 10.0]))
+    T = float(rng.choice([0.05, 1.0, 5.0]))
+    th_single = float(rng.choice([1.0, 1e-3, 0.99]))
+    th_acc = float(rng.choice([1.0, 0.05, 3.0]))
+    if rng.random() < 0.3:
+        launch.update({"path": "eager"})
+    try:
+        t = wl.make_tree(4, seed=200 + i, B=B, N=N, V=max(V, N), D=D,
+                         max_children=int(rng.integers(2, 9)), dtype=dtype, T=T, sigma=sigma)
+    except ValueError:
+        t = wl.make_tree(4, seed=200 + i, B=B, N=N, V=max(V, N), D=D, max_children=N,
+                         dtype=dtype, T=T, sigma=sigma)
+    for mode in (oracle.TREE_GREEDY, oracle.TREE_SAMPLING):
+        label = (f"extreme tree {i} mode {mode}: B={B} N={N} D={D} V={t.V} {dtype} "
+                 f"sigma={sigma} T={T} th={th_single},{th_acc} {dict(launch)}")
+        check_tree(t, mode, label, max_near=B, th_single=th_single, th_acc=th_acc)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_multi_step_tree_extremes(i, launch):
+    """Multi-step trees whose draft rows equal the target (every child accepted, up to
+    rounding) or are far from it, on peaked or flat rows."""
+    rng = _rng("mss-extreme", i)
+    B, N = int(rng.integers(1, 7)), int(rng.integers(2, 33))
+    D = int(rng.integers(1, min(N - 1, 8) + 1))
+    V, dtype = _vocab(rng, 8000), _dtype(rng)
+    sigma = float(rng.choice([0.01, 0.3, 10.0]))
+    T = float(rng.choice([0.1, 1.0, 4.0]))
+    dv = float(rng.choice([0.0, 1e-3, 8.0]))
+    try:
+        t = wl.make_tree_mss(4, seed=300 + i, B=B, N=N, V=max(V, N), D=D,
+                             max_children=int(rng.integers(2, 7)), dtype=dtype, T=T,
+                             sigma=sigma, draft_var=dv)
+    except ValueError:
+        t = wl.make_tree_mss(4, seed=300 + i, B=B, N=N, V=max(V, N), D=D, max_children=N,
+                             dtype=dtype, T=T, sigma=sigma, draft_var=dv)
+    label = f"extreme multi-step tree {i}: B={B} N={N} D={D} V={t.V} {dtype} sigma={sigma} T={T} dv={dv}"
+    say(label)
+    from test_gpu_mss import gpu_mss, mss_recheck, oracle_mss
+    from test_gpu_parity import compare
+    g, o = gpu_mss(t), oracle_mss(t)
+    compare(g, o, ["accept_len", "out_tokens", "accepted_nodes"], o["margin"], label=label,
+            max_near=B, recheck=mss_recheck(t, g))
