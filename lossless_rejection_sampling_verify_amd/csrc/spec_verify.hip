@@ -101,6 +101,28 @@ struct alignas(16) DrawState {
     float cq;      // kDrawResidual: weights max(0, p - cq * q) (1 for the chain)
 };
 
+// Field-wise store of a draw state to global memory.  A whole-struct copy of a state that
+// the kernel also passes by reference becomes a private array of its zero fields, which the
+// compiler may move into LDS: 3 KiB per workgroup, enough to cost the tree walk a resident
+// workgroup per compute unit (and half its cluster width on the large batch).
+__device__ inline void store_state(DrawState* p, const DrawState& st) {
+    p->kind = st.kind;
+    p->row = st.row;
+    p->qrow = st.qrow;
+    p->out = st.out;
+    p->coin = st.coin;
+    p->nexcl = st.nexcl;
+    p->M = st.M;
+    p->invZ = st.invZ;
+    p->Z = st.Z;
+    p->T = st.T;
+    p->thp = st.thp;
+    p->thq = st.thq;
+    p->Mq = st.Mq;
+    p->invZq = st.invZq;
+    p->cq = st.cq;
+}
+
 // Top-k / top-p result of one logit row (filtered calls).
 struct alignas(16) FiltRow {
     float M;       // row max (-inf: the row has no finite logit)
@@ -833,7 +855,7 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
             if (sampling) {
                 DrawState st = {};
                 st.kind = kDrawNone;
-                a.dstate[b] = st;
+                store_state(a.dstate + b, st);
             }
         }
         return;
@@ -928,7 +950,7 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
             if (sampling) {
                 DrawState st = {};
                 st.kind = kDrawNone;
-                a.dstate[b] = st;
+                store_state(a.dstate + b, st);
             }
         }
         return;
@@ -958,7 +980,7 @@ __global__ __launch_bounds__(kBlock) void k_tree(KArgs a, int sampling) {
             st.Z = ts.Z[cur];
             st.invZ = (float)(1.0 / ts.Z[cur]);
             st.T = Td;
-            a.dstate[b] = st;
+            store_state(a.dstate + b, st);
         }
     } else if (tid == 0) {
         out[d] = ts.arg[cur];
@@ -2235,7 +2257,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             a.out_tokens[(size_t)b * R + e] = (!bad && e < k) ? a.tokens[(size_t)b * G + e] : -1;
             if (a.probs) a.probs[(size_t)b * R + e] = (!bad && e < k) ? sp[e] : 0.f;
         }
-        if (tid == 0) a.dstate[b] = st;
+        if (tid == 0) store_state(a.dstate + b, st);
     }
     walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : k, a.accept_len);
 }
@@ -2503,7 +2525,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         }
         if (e >= d && e < D) nodes[e] = -1;
     }
-    if (tid == 0 && sampling) a.dstate[b] = st;
+    if (tid == 0 && sampling) store_state(a.dstate + b, st);
     walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : d, a.accept_len);
 }
 
@@ -2842,7 +2864,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
         }
         if (e >= d && e < D) nodes[e] = -1;
     }
-    if (tid == 0) a.dstate[b] = st;
+    if (tid == 0) store_state(a.dstate + b, st);
     walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : d, a.accept_len);
 }
 
@@ -3498,7 +3520,7 @@ __global__ __launch_bounds__(kBlock) void k_filter_accept(KArgs a) {
                 st.invZq = (float)(1.0 / fq[k].Z);
             }
         }
-        a.dstate[b] = st;
+        store_state(a.dstate + b, st);
     }
     __syncthreads();
     const int k = sm.k;
