@@ -154,6 +154,8 @@ struct KArgs {
     const int32_t* top_k;
     const float* top_p;
     FiltRow* frows;      // filtered calls: [B*R] target rows, then [B*G] draft rows
+    int32_t* kept;       // filtered calls: per target row, [kBlock + 1] words: the count of
+                         // tokens the filter keeps (-1: not listed), then their ids
     int fixbits;         // fixed-point fraction bits of the filter's mass histograms
     int walk_temporal;   // chain walk: row passes with cache-allocating loads (sweeps: 0)
     int coin_stride;     // coins per request in `coins`; the final draw's coin is the last
@@ -2942,7 +2944,9 @@ struct FilterSmem {
     alignas(16) uint32_t lanekey[kBlock];  // lane maxima's keys; then the sorted candidates (n <= kBlock)
     uint16_t bkey[kMaxBatchRec * kBlock];  // batch maxima of the first pass (key top bits)
     uint16_t item[kItemCap];               // the batches the candidate pass reads (j * kBlock + t)
+    uint32_t candidx[kBlock];              // the first kBlock candidates' token ids
     int ncand;
+    int nkept;
     unsigned long long wtot[3][kWaves];
     int pick_thread;
     int last_thread;
@@ -3233,7 +3237,7 @@ __device__ inline int count_above(const uint32_t* a, uint32_t key, bool strict) 
 template <typename T>
 __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fscale, int k,
                               bool fp, double tp, float lane_max, bool rec, uint32_t* th_out,
-                              unsigned long long* kept_out, FilterSmem& sm) {
+                              unsigned long long* kept_out, int32_t* ids_out, FilterSmem& sm) {
     const int tid = threadIdx.x;
     constexpr int kVec = Ld<T>::kVec;
     {
@@ -3250,18 +3254,19 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
         __syncthreads();
     }
     const uint32_t lb = sm.lbkey;
-    auto visit = [&](float x) {
+    auto visit = [&](float x, int idx) {
         const uint32_t key = order_key(x);
         if (key >= lb) {
             const int slot = atomicAdd(&sm.ncand, 1);
             if (slot < kCandCap) sm.cand[slot] = key;
+            if (slot < kBlock) sm.candidx[slot] = (uint32_t)idx;
         }
     };
     int head = (int)(((16u - ((uint32_t)(uintptr_t)rowp & 15u)) & 15u) / sizeof(T));
     if (head > V) head = V;
     const int nv = (V - head) / kVec;
     const int tail0 = head + nv * kVec;
-    if (tid < head) visit(Ld<T>::one(rowp + tid));
+    if (tid < head) visit(Ld<T>::one(rowp + tid), tid);
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + head);
     int v = tid;
     const uint32_t lb16 = lb >> 16;  // key >= lb implies key >> 16 >= lb16
@@ -3295,11 +3300,14 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (base + e * kBlock + tid < nvis) {
+                    const int it = base + e * kBlock + tid;
+                    if (it < nvis) {
+                        const int bt = sm.item[it / kUnroll];
+                        const int vv = (bt % kBlock) + kBlock * (kUnroll * (bt / kBlock) + it % kUnroll);
                         float f[kVec];
                         Ld<T>::unpack(r[e], f);
 #pragma unroll
-                        for (int x = 0; x < kVec; ++x) visit(f[x]);
+                        for (int x = 0; x < kVec; ++x) visit(f[x], head + vv * kVec + x);
                     }
                 }
             }
@@ -3318,7 +3326,7 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
                 float f[kVec];
                 Ld<T>::unpack(r[u], f);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) visit(f[e]);
+                for (int e = 0; e < kVec; ++e) visit(f[e], head + (v + u * kBlock) * kVec + e);
             }
         }
     }
@@ -3326,9 +3334,9 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
         float f[kVec];
         Ld<T>::unpack(ld_stream(vp + v), f);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) visit(f[e]);
+        for (int e = 0; e < kVec; ++e) visit(f[e], head + v * kVec + e);
     }
-    if (tail0 + tid < V) visit(Ld<T>::one(rowp + tail0 + tid));
+    if (tail0 + tid < V) visit(Ld<T>::one(rowp + tail0 + tid), tail0 + tid);
     __syncthreads();
     const int n = sm.ncand;
     if (n > kCandCap) return false;  // uniform: every thread read the same count
@@ -3385,6 +3393,21 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
     }
     *th_out = th;
     *kept_out = kept;
+    if (ids_out) {
+        // The kept tokens (key >= th) are all among the candidates (th >= lb).  When their
+        // ids were all recorded (n <= kBlock, the candidates still in visiting order), the
+        // list goes to the row's kept words; otherwise the count -1 says there is none.
+        if (n <= kBlock) {
+            if (tid == 0) sm.nkept = 0;
+            __syncthreads();
+            if (tid < n && sm.cand[tid] >= th)
+                ids_out[1 + atomicAdd(&sm.nkept, 1)] = (int32_t)sm.candidx[tid];
+            __syncthreads();
+            if (tid == 0) ids_out[0] = sm.nkept;
+        } else if (tid == 0) {
+            ids_out[0] = -1;
+        }
+    }
     return true;
 }
 
@@ -3409,6 +3432,9 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     const bool fits = nvec / (kUnroll * kBlock) + 1 <= kMaxBatchRec;
     const Part st = chunk_record<T, true, true, kUnroll, true>(rowp, 0, V, s2, sm.rs, &lane_max,
                                                               fits ? sm.bkey : nullptr);
+    // a target row's kept-token list (the final draw reads it instead of the row)
+    int32_t* ids = !draft && a.kept ? a.kept + (size_t)r * (kBlock + 1) : nullptr;
+    bool listed = false;
     FiltRow fr;
     fr.M = st.m;
     fr.th = 0u;
@@ -3422,7 +3448,8 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
         uint32_t lo = 0u;
         const bool direct = fk && k <= kBlock &&
                             direct_select<T>(rowp, V, st.m, s2, fscale, k, fp, (double)tp,
-                                             lane_max, fits && isfinite(st.z), &lo, &kept, sm);
+                                             lane_max, fits && isfinite(st.z), &lo, &kept, ids, sm);
+        listed = direct;
         if (!direct) {
             if (fk) lo = radix_select<T>(rowp, V, st.m, s2, fscale, 0u, false, 0.0,
                                          (unsigned long long)k, &kept, sm);
@@ -3432,17 +3459,29 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
         fr.th = lo;
         fr.Z = ldexp((double)kept, -a.fixbits);
     }
-    if (threadIdx.x == 0) a.frows[r] = fr;
+    if (threadIdx.x == 0) {
+        a.frows[r] = fr;
+        if (ids && !listed) ids[0] = -1;
+    }
 }
 
 // One workgroup per filtered chain request: the acceptance scan on the filtered rows,
-// its outputs and the draw state.
+// its outputs and the draw state.  When k_filter_rows listed the tokens the filter keeps in
+// the drawn row, the final draw happens here from that list (every other token weighs 0,
+// the draft-row residual included, as its weights are at most the target's): each listed
+// token is weighed with the same fp32 weights as the full draw, the weights are put in
+// ascending token order, and the token whose cumulative weight reaches u * total is found
+// as k_draw finds it (the plain kept weights if the residual has no mass).  The request's
+// draw state is then left empty, so k_mass and k_draw pass over it.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_filter_accept(KArgs a) {
     __shared__ Smem sm;
     __shared__ float dq[kMaxRows];
     __shared__ FiltRow fq[kMaxRows];
     __shared__ FiltRow fpp[kMaxRows];
+    __shared__ int kid[kBlock];      // listed token ids, then in ascending order
+    __shared__ double kw[kBlock];    // their draw weights, in that order
+    __shared__ double kp[kBlock];    // their plain (filtered) target weights
     const int tid = threadIdx.x;
     const int R = a.R, G = R - 1, V = a.V;
     const int b = blockIdx.x;
@@ -3520,10 +3559,63 @@ __global__ __launch_bounds__(kBlock) void k_filter_accept(KArgs a) {
                 st.invZq = (float)(1.0 / fq[k].Z);
             }
         }
-        store_state(a.dstate + b, st);
+        store_state(&sm.st, st);
     }
     __syncthreads();
     const int k = sm.k;
+    {
+        const DrawState st = load_state(&sm.st);
+        const int kn = st.kind != kDrawNone && a.kept ? a.kept[(size_t)st.row * (kBlock + 1)] : -1;
+        if (kn >= 1 && kn <= kBlock) {  // uniform: every thread read the same word
+            const int32_t* ids = a.kept + (size_t)st.row * (kBlock + 1) + 1;
+            const T* rowp = logits + (size_t)st.row * V;
+            const void* qrow;
+            const WParams Wp = draw_params<T, true>(a, st, qrow);
+            const int my = tid < kn ? ids[tid] : 0x7fffffff;
+            float p = 0.f, w = 0.f;
+            if (tid < kn)
+                w = qrow ? draw_weight<T, 2, true>(rowp, qrow, my, Wp, p)
+                         : draw_weight<T, 0, true>(rowp, nullptr, my, Wp, p);
+            kid[tid] = my;
+            __syncthreads();
+            int rk = 0;  // ascending position of this token (the ids are distinct)
+            for (int j = 0; j < kn; ++j) rk += kid[j] < my ? 1 : 0;
+            __syncthreads();
+            if (tid < kn) {
+                kid[rk] = my;
+                kw[rk] = (double)w;
+                kp[rk] = (double)p;
+            }
+            __syncthreads();
+            if (tid < 64) {
+                double tw = 0.0, tpl = 0.0;  // totals, added as the search adds them
+                for (int i0 = 0; i0 < kn; i0 += 64) {
+                    tw += wave_find(i0 + tid < kn ? kw[i0 + tid] : 0.0, 0.0, 0.0).total;
+                    tpl += wave_find(i0 + tid < kn ? kp[i0 + tid] : 0.0, 0.0, 0.0).total;
+                }
+                const bool fallback = !(tw > 0.0);
+                const double t = (double)sm.u[G] * (fallback ? tpl : tw);
+                double before;
+                const int e = wave_locate(fallback ? kp : kw, kn, t, before);
+                if (tid == 0) {
+                    const int y = e >= 0 ? kid[e] : -1;
+                    a.out_tokens[st.out] = y;
+                    if (a.probs) {
+                        const float ly = y >= 0 ? Ld<T>::one(rowp + y) : 0.f;
+                        a.probs[st.out] =
+                            y >= 0 ? (float)(exp(((double)ly - (double)st.M) / st.T) / st.Z) : 0.f;
+                    }
+                }
+            }
+            if (tid == 0) {
+                DrawState done = st;
+                done.kind = kDrawNone;
+                store_state(a.dstate + b, done);
+            }
+        } else if (tid == 0) {
+            store_state(a.dstate + b, st);
+        }
+    }
     for (int i = tid; i < R; i += kBlock) {
         int t = -1;
         float pr = 0.f;
@@ -3686,7 +3778,7 @@ constexpr size_t kHeaderBytes = 256 + 4 * (size_t)kExitWords;
 static_assert(kHeaderBytes % 256 == 0, "the header keeps the regions after it aligned");
 
 struct Layout {
-    size_t parts, dstate, mass, massfb, seg, excl, frows, xch, total;
+    size_t parts, dstate, mass, massfb, seg, excl, frows, kept, xch, total;
 };
 
 // Workgroups per request that the tree walks may use (the hand-off slots are sized for it).
@@ -3721,6 +3813,8 @@ Layout layout_for(int op, int B, int R, int V) {
     if (op == SPEC_OP_TREE) off = align256(off + sizeof(int32_t) * (size_t)B * SPEC_MAX_N);
     L.frows = off;
     if (op == SPEC_OP_CHAIN_FILTERED) off = align256(off + sizeof(FiltRow) * (size_t)B * (2 * R - 1));
+    L.kept = off;
+    if (op == SPEC_OP_CHAIN_FILTERED) off = align256(off + sizeof(int32_t) * (size_t)B * R * (kBlock + 1));
     L.xch = off;
     if (op == SPEC_OP_GREEDY)
         off = align256(off + sizeof(unsigned long long) * (size_t)B * R * kMaxCluster * 3);
@@ -3745,6 +3839,7 @@ void bind_workspace(KArgs& a, void* ws, int op) {
     a.seg = reinterpret_cast<double*>(base + L.seg);
     a.excl = op == SPEC_OP_TREE ? reinterpret_cast<int32_t*>(base + L.excl) : nullptr;
     a.frows = op == SPEC_OP_CHAIN_FILTERED ? reinterpret_cast<FiltRow*>(base + L.frows) : nullptr;
+    a.kept = op == SPEC_OP_CHAIN_FILTERED ? reinterpret_cast<int32_t*>(base + L.kept) : nullptr;
 }
 
 // Split each row into S chunks of `chunk` elements (a multiple of 8): about 64 KB of

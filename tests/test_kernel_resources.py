@@ -11,7 +11,8 @@ results.  Each walk is held to
   - a register limit for the residency its clusters are sized for, with one 256-lane
     workgroup per CU putting one wave on each SIMD: 512 VGPRs per SIMD lane slot give
     four waves at up to 128 and five at up to 96 (granules of 8).  The greedy walk runs
-    five workgroups per CU, the chain and tree walks four, the multi-step walk three.
+    five workgroups per CU, the chain and tree walks four, the multi-step walk three; the
+    filtered calls' row kernel (not a walk) keeps five for its two rounds of rows.
 
 The metadata is read with the ROCm LLVM tools from the library built here (the code-object
 notes that the loader itself reads); the test skips when the library or a tool is missing.
@@ -37,6 +38,7 @@ LIMITS = {
     "k_chain_walk": (34 * 1024, 128),
     "k_tree_walk": (37 * 1024 + 512, 128),
     "k_mss_walk": (49 * 1024, 168),
+    "k_filter_rows": (29 * 1024, 96),  # one row per workgroup, five per CU
 }
 
 
