@@ -134,6 +134,31 @@ def test_random_filtered(i):
     check_filtered(c, f"random filtered {i}: B={B} G={G} V={V} {dtype} T={T:.2f}")
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_random_filtered_extremes(i):
+    """Filtered chains at the edges of the kept-token list that the final draw reads: top-k
+    at 1, 2, 255 and 256 (the list's limit; ties on bf16 rows can push the kept set past
+    it, and then the full draw runs), with or without top-p, drafts equal to the target
+    (every residual near empty, the plain kept weights drawn instead) or perturbed by a
+    rounding-sized amount, and coins pinned next to 1 or to 2^-24."""
+    rng = _rng("filtered-extreme", i)
+    B, G, V = int(rng.integers(1, 25)), int(rng.integers(1, 6)), _vocab(rng, 40000)
+    V = max(V, 300)
+    dtype, T = _dtype(rng), float(rng.choice([0.3, 1.0, 3.0]))
+    top_k = rng.choice([1, 2, 255, 256], size=B).astype(np.int32)
+    top_p = rng.choice([1.0, 0.99, 0.5], size=B).astype(np.float32)
+    c = wl.make_chain_logits(2, seed=400 + i, B=B, G=G, V=V, dtype=dtype, T=T, top_k=top_k,
+                             top_p=top_p)
+    eps = float(rng.choice([0.0, 1e-3]))
+    d = wl.logits_as_f32(c.logits[:, :G], dtype) + np.float32(eps) * rng.standard_normal(
+        (B, G, V), dtype=np.float32)
+    c.draft_logits[:] = wl.f32_to_bf16_bits(d) if dtype == wl.BF16 else d
+    pin = rng.random(c.coins.shape) < 0.3
+    c.coins[pin] = np.where(rng.random(int(pin.sum())) < 0.5, 1.0 - 2.0 ** -24,
+                            2.0 ** -24).astype(np.float32)
+    check_filtered(c, f"extreme filtered {i}: B={B} G={G} V={V} {dtype} T={T} eps={eps}")
+
+
 @pytest.mark.parametrize("i", range(12))
 def test_random_chain_extremes(i, launch):
     """Chains at the edges of the input space: logits nearly equal (bf16 ties) or spread
