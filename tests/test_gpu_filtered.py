@@ -220,3 +220,24 @@ def test_bench_shape():
     c = wl.make_chain_logits(5, top_k=50, top_p=0.9)
     assert c.B == 256
     check(c, "bench shape B=256 k=50 p=0.9")
+
+
+def test_repeated_calls_are_bit_identical():
+    """The candidates and the kept-token lists are filled in the order the atomics land, and
+    the draw from a list sorts it by token id first: 20 calls on the same inputs (top-k 50
+    with and without top-p, and top-k off, which takes the full draw) give the same bits."""
+    api = _api()
+    c = wl.make_chain_logits(5, seed=7, B=64, top_k=np.where(np.arange(64) % 3 == 2, 0, 50),
+                             top_p=np.where(np.arange(64) % 2 == 0, 0.9, 1.0))
+    args = (dev_logits(c.logits, c.dtype), dev_logits(c.draft_logits, c.dtype),
+            dev(c.draft_tokens), dev(c.coins), dev(c.temperature),
+            dev(np.asarray(c.top_k, np.int32)), dev(np.asarray(c.top_p, np.float32)))
+    first = None
+    for _ in range(20):
+        out = [x.cpu().numpy() for x in api.spec_verify_chain_filtered(*args, want_probs=True)]
+        if first is None:
+            first = out
+            continue
+        for a, b in zip(first, out):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    check(c, "repeated calls, mixed knobs")
