@@ -52,7 +52,7 @@ EAGER_GREEDY_KERNELS = ["k_rows<greedy>", "k_greedy_merge"]
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--copies", type=int, default=4,
