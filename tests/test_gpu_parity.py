@@ -296,6 +296,15 @@ def test_greedy_workloads(cfg):
     check_greedy(chain_cfg(cfg), f"workload {cfg}")
 
 
+def test_large_batch_in_fp32():
+    """The large batch's shape (B=256, gamma=4, V=152064) with fp32 logits: the fp32 walks
+    run at their own residency (their register counts differ from the bf16 walks'), and the
+    rows are twice as long in bytes."""
+    c = wl.make_chain(5, seed=31, dtype=wl.F32)
+    check_chain(c, "large batch fp32")
+    check_greedy(c, "large batch fp32")
+
+
 @pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
 def test_tree_workload(mode):
     check_tree(tree_cfg(), mode, f"workload 4 mode {mode}")
