@@ -70,6 +70,13 @@ def check_mss(t, label, **kw):
     return stats, g, o
 
 
+def test_tree_workload_with_draft_rows_in_fp32():
+    """The same shape with fp32 logits (the draft rows are fp32 either way)."""
+    t = wl.make_tree_mss(4, seed=33, dtype=wl.F32)
+    stats, g, o = check_mss(t, "tree workload with draft rows, fp32")
+    assert stats["near_accept"] <= 2
+
+
 def test_tree_workload_with_draft_rows_full_size():
     t = wl.make_tree_mss(4)
     stats, g, o = check_mss(t, "tree workload with draft rows")

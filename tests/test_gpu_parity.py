@@ -306,6 +306,12 @@ def test_large_batch_in_fp32():
 
 
 @pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
+def test_tree_workload_in_fp32(mode):
+    """The tree workload's shape (B=32, N=64, D=6, V=128256) with fp32 logits."""
+    check_tree(wl.make_tree(4, seed=32, dtype=wl.F32), mode, f"tree workload fp32 mode {mode}")
+
+
+@pytest.mark.parametrize("mode", [oracle.TREE_GREEDY, oracle.TREE_SAMPLING])
 def test_tree_workload(mode):
     check_tree(tree_cfg(), mode, f"workload 4 mode {mode}")
 
