@@ -101,7 +101,7 @@ struct alignas(16) DrawState {
     float cq;      // kDrawResidual: weights max(0, p - cq * q) (1 for the chain)
 };
 
-// Field-wise store of a draw state to global memory.  A whole-struct copy of a state that
+// Field-wise store of a draw state (to global memory or LDS).  A whole-struct copy of a state that
 // the kernel also passes by reference becomes a private array of its zero fields, which the
 // compiler may move into LDS (3 KiB per workgroup); in the tree walk that array cost tree
 // sampling 10 us, with residency unchanged.
@@ -121,6 +121,27 @@ __device__ inline void store_state(DrawState* p, const DrawState& st) {
     p->Mq = st.Mq;
     p->invZq = st.invZq;
     p->cq = st.cq;
+}
+
+// Field-wise copy of a draw state (from global memory or LDS; keeps it in registers).
+__device__ inline DrawState load_state(const DrawState* p) {
+    DrawState st;
+    st.kind = p->kind;
+    st.row = p->row;
+    st.qrow = p->qrow;
+    st.out = p->out;
+    st.coin = p->coin;
+    st.nexcl = p->nexcl;
+    st.M = p->M;
+    st.invZ = p->invZ;
+    st.Z = p->Z;
+    st.T = p->T;
+    st.thp = p->thp;
+    st.thq = p->thq;
+    st.Mq = p->Mq;
+    st.invZq = p->invZq;
+    st.cq = p->cq;
+    return st;
 }
 
 // Top-k / top-p result of one logit row (filtered calls).
@@ -680,10 +701,10 @@ __device__ DrawState chain_accept(const KArgs& a, int b, bool emit, Smem& sm, Re
             st.invZ = (float)(1.0 / sm.Z[k]);
             st.T = Td;
         }
-        sm.st = st;
+        store_state(&sm.st, st);
     }
     __syncthreads();
-    const DrawState st = sm.st;
+    const DrawState st = load_state(&sm.st);
     const int k = sm.k;
     for (int i = tid; i < R && emit; i += kBlock) {
         int t = -1;
@@ -1243,26 +1264,6 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     walk_end(hdr, epoch, b, w, W, gaveup, bad ? -1 : k, a.accept_len);
 }
 
-// Field-wise copy of a draw state from global memory (keeps it in registers).
-__device__ inline DrawState load_state(const DrawState* p) {
-    DrawState st;
-    st.kind = p->kind;
-    st.row = p->row;
-    st.qrow = p->qrow;
-    st.out = p->out;
-    st.coin = p->coin;
-    st.nexcl = p->nexcl;
-    st.M = p->M;
-    st.invZ = p->invZ;
-    st.Z = p->Z;
-    st.T = p->T;
-    st.thp = p->thp;
-    st.thq = p->thq;
-    st.Mq = p->Mq;
-    st.invZq = p->invZq;
-    st.cq = p->cq;
-    return st;
-}
 
 // ---------------------------------------------------------------------------------------
 // the final draw: k_mass weighs each fine chunk (kFine elements) of the row the token is
@@ -1431,7 +1432,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_accept(KArgs a) {
     __shared__ Smem sm;
     __shared__ RecSmem rs;
     const DrawState st = chain_accept<T>(a, blockIdx.x, true, sm, rs);
-    if (threadIdx.x == 0) a.dstate[blockIdx.x] = st;
+    if (threadIdx.x == 0) store_state(a.dstate + blockIdx.x, st);
 }
 
 struct MassSmem {
@@ -1848,7 +1849,7 @@ __global__ __launch_bounds__(kBlock) void k_mass(KArgs a) {
     const int S2 = a.S2;
     const int b = blockIdx.x / S2;
     const int c = blockIdx.x - b * S2;
-    const DrawState st = a.dstate[b];
+    const DrawState st = load_state(a.dstate + b);
     if (st.kind == kDrawNone) return;
     const T* rowp = reinterpret_cast<const T*>(a.logits) + (size_t)st.row * a.V;
     const void* qrow;

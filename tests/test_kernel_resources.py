@@ -14,6 +14,8 @@ results.  Each walk is held to
     five workgroups per CU, the chain and tree walks four, the multi-step walk three; the
     filtered calls' row kernel (not a walk) keeps five for its two rounds of rows.
 
+No other kernel of the library may use scratch either.
+
 The metadata is read with the ROCm LLVM tools from the library built here (the code-object
 notes that the loader itself reads); the test skips when the library or a tool is missing.
 """
@@ -83,3 +85,12 @@ def test_walk_kernels_keep_their_budgets(tmp_path):
             assert r["lds"] <= lds_max, f"LDS above its {lds_max}-byte budget: {what}"
             assert r["vgpr"] + r["agpr"] <= vgpr_max, f"registers above {vgpr_max}: {what}"
     assert seen == set(LIMITS), f"walk kernels not found in the code object: {set(LIMITS) - seen}"
+
+
+def test_no_kernel_uses_scratch(tmp_path):
+    """No kernel of the library keeps anything in private (scratch) memory: a spill or a
+    private array there costs a memory round trip per access."""
+    ks = _kernels(tmp_path)
+    assert ks
+    bad = {n: r for n, r in ks.items() if r["scratch"] != 0}
+    assert not bad, f"kernels with scratch: {bad}"
