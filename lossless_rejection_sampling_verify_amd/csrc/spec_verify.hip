@@ -465,9 +465,19 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             record(batch(raw, kU, v), v);
         }
     }
-    for (; v < nv; v += kBlock) {
-        u32x4 raw = kNT ? ld_stream(vp + v) : vp[v];
-        batch(&raw, 1, v);
+    {
+        // The fewer than kU vectors after a lane's last full batch: all their loads are in
+        // flight before the first is reduced (one after another, they cost a memory round
+        // trip each, and the last slice of a row usually ends in such a partial batch),
+        // then they are reduced one by one in index order.
+        constexpr int kT = kU > 1 ? kU - 1 : 1;
+        u32x4 raw[kT];
+#pragma unroll
+        for (int u = 0; u < kT; ++u)
+            if (v + u * kBlock < nv) raw[u] = kNT ? ld_stream(vp + v + u * kBlock) : vp[v + u * kBlock];
+#pragma unroll
+        for (int u = 0; u < kT; ++u)
+            if (v + u * kBlock < nv) batch(&raw[u], 1, v + u * kBlock);
     }
     if (tail0 + tid < n) scalar(tail0 + tid);
 
@@ -3331,11 +3341,22 @@ __device__ bool direct_select(const T* rowp, int V, float M, float s2, float fsc
             }
         }
     }
-    for (; v < nv; v += kBlock) {  // the vectors after a lane's last full batch
-        float f[kVec];
-        Ld<T>::unpack(ld_stream(vp + v), f);
+    {
+        // the fewer than kUnroll vectors after a lane's last full batch, all loads in flight
+        // before the first is visited
+        u32x4 r[kUnroll - 1];
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) visit(f[e], head + v * kVec + e);
+        for (int u = 0; u < kUnroll - 1; ++u)
+            if (v + u * kBlock < nv) r[u] = ld_stream(vp + v + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kUnroll - 1; ++u) {
+            if (v + u * kBlock < nv) {
+                float f[kVec];
+                Ld<T>::unpack(r[u], f);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) visit(f[e], head + (v + u * kBlock) * kVec + e);
+            }
+        }
     }
     if (tail0 + tid < V) visit(Ld<T>::one(rowp + tail0 + tid), tail0 + tid);
     __syncthreads();
