@@ -28,7 +28,8 @@
  *     fp32 (SPEC_F32) or bf16 (SPEC_BF16, raw 16-bit patterns) and must be aligned to
  *     their element size; rows need not be 16-byte aligned (a scalar head/tail handles
  *     that), but 16-byte aligned rows (V * element size a multiple of 16 and an aligned
- *     base) take the fast path.  Draft probabilities are fp32.  Token ids and parents
+ *     base) take the fast path.  A row holds at most 2^31 - 1 bytes (V * element size;
+ *     SPEC_ERR_SHAPE beyond).  Draft probabilities are fp32.  Token ids and parents
  *     are int32.  Coins are fp32 uniforms in (0, 1] supplied by the caller.
  *   - Target distribution: p = softmax(logits / T) per row, T > 0 per request.  Draft
  *     probabilities q are used exactly as given (already at temperature T).

@@ -192,6 +192,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming 16-byte load that does not displace reusable lines from the caches.
 __device__ inline u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+// Buffer loads: the fourth word of a raw buffer resource (32-bit data format, no stride
+// swizzle), and the cache-policy bit of a non-temporal load.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kCacheNT = 2;
+// s_waitcnt immediate of vmcnt(n) alone, n < 64 (expcnt and lgkmcnt at their maxima; vmcnt's
+// low four bits at 3:0, its high two at 15:14)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <typename T>
 struct Ld;
@@ -435,24 +442,65 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
     if (tid < head) scalar(tid);
     int v = tid;
     if (kPipe) {
-        // Two named buffers take turns, so no register copy waits for a load, and the next
-        // batch is loaded unconditionally (past the last full batch it re-reads the
-        // current one, already in cache, and is discarded): under a branch, the compiler
-        // could not tell which loads are outstanding and would wait for all of them.
-        u32x4 ra[kU], rb[kU];
+        // Two named buffers take turns, so no register copy waits for a load.  The loads are
+        // buffer loads over the slice's nv vectors (the base in scalar registers, one 32-bit
+        // offset per lane): a load past the end reads zeros and is discarded, so every load is
+        // issued unconditionally (under a branch the compiler could not tell which loads are
+        // outstanding and would wait for all of them), and no 64-bit per-lane address is kept
+        // whose registers a load in flight could overwrite (the compiler then waited for that
+        // load before computing the next address, once every two batches).  A lane's last
+        // batch may be partial; its loads are in flight during the batch before it like any
+        // other, and its vectors are reduced one by one in index order.
         const int step = kU * kBlock;
         auto full = [&](int v0) { return v0 + (kU - 1) * kBlock < nv; };
-        if (full(v)) load(ra, v);
-        while (full(v)) {
-            load(rb, full(v + step) ? v + step : v);
-            __builtin_amdgcn_sched_barrier(0);  // batch j + 1 in flight before batch j is reduced
-            record(batch(ra, kU, v), v);
-            v += step;
-            if (!full(v)) break;
-            load(ra, full(v + step) ? v + step : v);
-            __builtin_amdgcn_sched_barrier(0);
-            record(batch(rb, kU, v), v);
-            v += step;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, nv * 16, kBufWord3);
+        auto loadc = [&](u32x4* raw, int v0) {
+            // the whole offset in the lane's operand: the range check covers it (the scalar
+            // offset would be added after the check)
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                raw[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rsrc, (int)((uint32_t)(v0 + u * kBlock) * 16u), 0, kNT ? kCacheNT : 0);
+        };
+        auto reduce = [&](u32x4* raw, int v0) {
+            if (full(v0)) {
+                record(batch(raw, kU, v0), v0);
+            } else {
+#pragma unroll
+                for (int u = 0; u < kU; ++u)
+                    if (v0 + u * kBlock < nv) batch(&raw[u], 1, v0 + u * kBlock);
+            }
+        };
+        // Every thread runs the same number of batches (those of thread 0, which has the
+        // most), so the loop is uniform; a thread's batches past its end are empty.  Before
+        // a batch is reduced exactly the next batch's kU loads are still in flight, which
+        // the explicit wait states for the compiler: otherwise it merges the paths where a
+        // wave reduced nothing and waits at the top of the loop for every load (the
+        // pipeline drained once every two batches).
+        // (A loop over pairs of batches with no exit in between: an exit after the first of
+        // a pair left a path back to the top, never taken, on which the compiler also
+        // waited for every load.)
+        const int nb = (nv + step - 1) / step;  // the same in every thread
+        if (nb > 0) {
+            u32x4 ra[kU], rb[kU];
+            loadc(ra, v);
+            for (int j = 0; j + 1 < nb; j += 2) {
+                loadc(rb, v + step);
+                __builtin_amdgcn_sched_barrier(0);  // batch j + 1 in flight before batch j is reduced
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(kU));
+                reduce(ra, v);
+                v += step;
+                loadc(ra, v + step);  // past the last batch: zeros, discarded
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(kU));
+                reduce(rb, v);
+                v += step;
+            }
+            if (nb & 1) {  // the last batch, loaded by the pair before it (or first)
+                reduce(ra, v);
+                v += step;
+            }
         }
     } else {
         for (; v + (kU - 1) * kBlock < nv; v += kU * kBlock) {
@@ -464,12 +512,9 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
             __builtin_amdgcn_sched_barrier(0);
             record(batch(raw, kU, v), v);
         }
-    }
-    {
         // The fewer than kU vectors after a lane's last full batch: all their loads are in
         // flight before the first is reduced (one after another, they cost a memory round
-        // trip each, and the last slice of a row usually ends in such a partial batch),
-        // then they are reduced one by one in index order.
+        // trip each), then they are reduced one by one in index order.
         constexpr int kT = kU > 1 ? kU - 1 : 1;
         u32x4 raw[kT];
 #pragma unroll
@@ -3926,6 +3971,8 @@ int check_common(const void* logits, int dtype, int B, int V, void* ws, size_t w
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
     if (B < 0 || V < 1) return SPEC_ERR_SHAPE;
     const size_t es = dtype == SPEC_F32 ? 4 : 2;
+    // a row's bytes fit a 32-bit signed offset (the row passes' buffer loads)
+    if ((long long)V * (long long)es > (long long)INT_MAX) return SPEC_ERR_SHAPE;
     if (((uintptr_t)logits) % es) return SPEC_ERR_PARAM;
     if ((long long)B * R * kMaxSplits > (long long)INT_MAX) return SPEC_ERR_SHAPE;
     if (B > 0) {

@@ -67,6 +67,8 @@ def test_greedy_rejects_bad_arguments(lib):
     assert _greedy(lib, G=0) == L.SPEC_ERR_SHAPE
     assert _greedy(lib, G=65) == L.SPEC_ERR_SHAPE
     assert _greedy(lib, V=0) == L.SPEC_ERR_SHAPE
+    assert _greedy(lib, V=1 << 30) == L.SPEC_ERR_SHAPE                    # 2^31 bytes a row
+    assert _greedy(lib, V=1 << 29, dtype=L.SPEC_F32) == L.SPEC_ERR_SHAPE
     assert _greedy(lib, B=-1) == L.SPEC_ERR_SHAPE
     assert _greedy(lib, logits=P + 1) == L.SPEC_ERR_PARAM                 # not bf16-aligned
     assert _greedy(lib, logits=P + 2, dtype=L.SPEC_F32) == L.SPEC_ERR_PARAM
