@@ -62,7 +62,6 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kUnroll = 4;
 constexpr int kWalkUnroll = 4;  // loads per lane and batch in the walks' row passes
-constexpr bool kWalkPipe = true;  // ... with the next batch in flight while one is reduced
 constexpr int kMaxSplits = 64;
 constexpr long kChunkBytes = 64 * 1024;  // target logit bytes per row-pass workgroup
 constexpr int kFine = 4 * 4 * kBlock;  // elements per fine chunk of the final draw (4096)
@@ -323,16 +322,16 @@ __device__ inline int block_min(int v, RowSmem& sm) {
     return r;
 }
 
-// Reduces chunk [c0, c1) of a row into one record (valid in every thread).
-// kPipe: the loads of batch j + 1 are issued before batch j is reduced (kU more registers
-// per lane), so the reduction's arithmetic overlaps the memory latency; that matters when a
-// workgroup has its SIMDs to itself, as in the walks' later positions.
+// Reduces chunk [c0, c1) of a row into one record (valid in every thread).  The loads of
+// batch j + 1 (kU 16-byte vectors per lane) are issued before batch j is reduced, so the
+// reduction's arithmetic overlaps the memory latency; that matters most when a workgroup
+// has its SIMDs to itself, as in the walks' later positions.
 //
 // bkey (optional): batch j of this lane (its vectors v = tid +
 // kBlock * (kU * j + u)) leaves the top 16 bits of its maximum's order key in
 // bkey[j * kBlock + tid], for the first kMaxBatchRec batches.
 constexpr int kMaxBatchRec = 24;
-template <typename T, bool kSampling, bool kNT = true, int kU = kUnroll, bool kPipe = false>
+template <typename T, bool kSampling, bool kNT = true, int kU = kUnroll>
 __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c0, int c1,
                                                             float s2, RowSmem& sm,
                                                             float* lane_max = nullptr,
@@ -426,10 +425,6 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
         return bm;
     };
 
-    auto load = [&](u32x4* raw, int v0) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u) raw[u] = kNT ? ld_stream(vp + v0 + u * kBlock) : vp[v0 + u * kBlock];
-    };
     auto record = [&](float bm, int v0) {
         if (bkey) {
             const int j = (v0 - tid) / (kU * kBlock);
@@ -441,7 +436,7 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
     };
     if (tid < head) scalar(tid);
     int v = tid;
-    if (kPipe) {
+    {
         // Two named buffers take turns, so no register copy waits for a load.  The loads are
         // buffer loads over the slice's nv vectors (the base in scalar registers, one 32-bit
         // offset per lane): a load past the end reads zeros and is discarded, so every load is
@@ -502,27 +497,6 @@ __device__ __attribute__((always_inline)) Part chunk_record(const T* rowp, int c
                 v += step;
             }
         }
-    } else {
-        for (; v + (kU - 1) * kBlock < nv; v += kU * kBlock) {
-            u32x4 raw[kU];
-            load(raw, v);
-            // every load of the batch is issued before the first is waited for (left
-            // alone, the scheduler interleaves the unpacking with the loads and waits
-            // after two)
-            __builtin_amdgcn_sched_barrier(0);
-            record(batch(raw, kU, v), v);
-        }
-        // The fewer than kU vectors after a lane's last full batch: all their loads are in
-        // flight before the first is reduced (one after another, they cost a memory round
-        // trip each), then they are reduced one by one in index order.
-        constexpr int kT = kU > 1 ? kU - 1 : 1;
-        u32x4 raw[kT];
-#pragma unroll
-        for (int u = 0; u < kT; ++u)
-            if (v + u * kBlock < nv) raw[u] = kNT ? ld_stream(vp + v + u * kBlock) : vp[v + u * kBlock];
-#pragma unroll
-        for (int u = 0; u < kT; ++u)
-            if (v + u * kBlock < nv) batch(&raw[u], 1, v + u * kBlock);
     }
     if (tail0 + tid < n) scalar(tail0 + tid);
 
@@ -570,7 +544,8 @@ __global__ __launch_bounds__(kBlock) void k_rows(KArgs a) {
     const int c1 = min(a.V, c0 + a.chunk);
     float s2 = 0.f;
     if (kSampling) s2 = kLog2e / a.temperature[b];
-    const Part r = chunk_record<T, kSampling>(rowp, c0, c1, s2, sm);
+    // the pipelined pass: 64.5 against 66.8 us for the eager greedy call on the large batch
+    const Part r = chunk_record<T, kSampling, true, kUnroll>(rowp, c0, c1, s2, sm);
     if (threadIdx.x == 0) a.parts[(size_t)row * S + s] = r;
 }
 
@@ -1267,7 +1242,7 @@ __global__ __launch_bounds__(kBlock) void k_greedy_walk(KArgs a, int W, int per,
     int k = G, last = -1;
     bool bad = false, gaveup = false;
     auto pass = [&](int r) {
-        const Part cur = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(
+        const Part cur = chunk_record<T, false, true, kWalkUnroll>(
             logits + ((size_t)b * R + r) * V, lo, hi, 0.f, rs);
         cluster_publish(slots, r, W, w, tag, __float_as_uint(cur.m), (uint32_t)cur.idx, 0u, xs);
     };
@@ -2080,8 +2055,8 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
     auto pass = [&](int r) {
         const T* rowp = logits + ((size_t)b * R + r) * V;
         const Part cur =
-            a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs)
-                            : chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+            a.walk_temporal ? chunk_record<T, true, false, kWalkUnroll>(rowp, lo, hi, s2, rs)
+                            : chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
         cluster_publish(slots, r, W, w, tag, __float_as_uint(cur.m), dbl_hi(cur.z), dbl_lo(cur.z),
                         xs);
     };
@@ -2376,11 +2351,11 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     auto pass = [&](int step, int node) {
         const T* rowp = logits + ((size_t)b * N + node) * V;
         if (sampling) {
-            const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+            const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
             cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
                             dbl_lo(r.z), xs);
         } else {
-            const Part r = chunk_record<T, false, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, 0.f, rs);
+            const Part r = chunk_record<T, false, true, kWalkUnroll>(rowp, lo, hi, 0.f, rs);
             cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), (uint32_t)r.idx, 0u, xs);
         }
     };
@@ -2740,7 +2715,7 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     // not need the row statistics overlaps the hand-off.
     auto pass = [&](int node) {
         const T* rowp = logits + ((size_t)b * N + node) * V;
-        const Part r = chunk_record<T, true, true, kWalkUnroll, kWalkPipe>(rowp, lo, hi, s2, rs);
+        const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
         cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z), dbl_lo(r.z), xs);
     };
 
@@ -3497,7 +3472,7 @@ __global__ __launch_bounds__(kBlock) void k_filter_rows(KArgs a) {
     // kMaxBatchRec of them (the vector count bounds it: the head shifts it by less than one)
     const long nvec = (long)V * sizeof(T) / 16;
     const bool fits = nvec / (kUnroll * kBlock) + 1 <= kMaxBatchRec;
-    const Part st = chunk_record<T, true, true, kUnroll, true>(rowp, 0, V, s2, sm.rs, &lane_max,
+    const Part st = chunk_record<T, true, true, kUnroll>(rowp, 0, V, s2, sm.rs, &lane_max,
                                                               fits ? sm.bkey : nullptr);
     // a target row's kept-token list (the final draw reads it instead of the row)
     int32_t* ids = !draft && a.kept ? a.kept + (size_t)r * (kBlock + 1) : nullptr;
