@@ -55,11 +55,22 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+# Elements between the start of the logits' allocation and the logits (0: the allocation's
+# own, 256-byte aligned, start).  A test sets 1 to put every row off a 16-byte boundary.
+_LOGIT_OFFSET = 0
+
+
 def dev_logits(arr, dtype):
     a = np.ascontiguousarray(arr)
     if dtype == wl.BF16:
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(a.astype(np.float32, copy=False)).cuda()
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        t = torch.from_numpy(a.astype(np.float32, copy=False)).cuda()
+    if _LOGIT_OFFSET:
+        buf = torch.empty(t.numel() + _LOGIT_OFFSET, dtype=t.dtype, device=t.device)
+        buf[_LOGIT_OFFSET:].copy_(t.reshape(-1))
+        t = buf[_LOGIT_OFFSET:].view(t.shape)
+    return t
 
 
 def say(msg):
@@ -352,6 +363,25 @@ def test_chain_ragged(dtype, B, G, V):
     c = wl.make_chain(2, seed=B * 1000 + G, B=B, G=G, V=V, dtype=dtype)
     check_chain(c, f"ragged {dtype} B={B} G={G} V={V}")
     check_greedy(c, f"ragged {dtype} B={B} G={G} V={V}")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_logits_off_a_16_byte_boundary(dtype, monkeypatch, launch):
+    """Logits one element past an aligned start, with V a multiple of 8: every row and every
+    slice of a walk begins off a 16-byte boundary (a head of 3 or 7 elements read one by one
+    before the vector loads), for the chain, greedy and tree walks and the eager passes."""
+    import sys
+    monkeypatch.setattr(sys.modules[__name__], "_LOGIT_OFFSET", 1)
+    c = wl.make_chain(2, seed=77, B=12, G=4, V=32000, dtype=dtype)
+    check_chain(c, f"offset logits {dtype}")
+    check_greedy(c, f"offset logits {dtype}")
+    launch.update(path="eager")
+    check_chain(c, f"offset logits eager {dtype}")
+    check_greedy(c, f"offset logits eager {dtype}")
+    launch.clear()
+    t = wl.make_tree(4, seed=78, B=6, V=24000, dtype=dtype)
+    for mode in (oracle.TREE_GREEDY, oracle.TREE_SAMPLING):
+        check_tree(t, mode, f"offset logits tree {dtype} mode {mode}")
 
 
 @pytest.mark.parametrize("T", [0.3, 0.7, 2.0])
