@@ -1475,9 +1475,14 @@ struct MassSmem2 {
     MassSmem s[2];
 };
 
-// Four chunks' staging, summed by the four waves (one chunk each).
+// Four chunks' staging, summed by the four waves (one chunk each), and a copy of the chunk
+// masses of the first kLdsChunks chunks of the slice (the walk's draw reads them there
+// instead of reading back what the workgroup has just written to memory).
+constexpr int kLdsChunks = 64;
 struct MassSmem4 {
     MassSmem s[kWaves];
+    double cm[kLdsChunks];   // mass of chunk cb + i
+    double cmf[kLdsChunks];  // its plain target weight (the fallback)
 };
 
 // The draw weights' parameters and draft row of a request's draw state.
@@ -1763,7 +1768,7 @@ __device__ __attribute__((always_inline)) void mass_reduce_quad(const KArgs& a,
                                                                 const WParams& W, const T* rowp,
                                                                 int b, int c0, int cend,
                                                                 MassSmem4& sm,
-                                                                const int32_t* ex) {
+                                                                const int32_t* ex, int cb) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int S2 = a.S2;
     const int c = c0 + wv < cend ? c0 + wv : -1;  // the chunk this wave sums
@@ -1786,9 +1791,13 @@ __device__ __attribute__((always_inline)) void mass_reduce_quad(const KArgs& a,
         if (lane == 0) {
             a.mass[(size_t)b * S2 + c] = Wt;
             a.massfb[(size_t)b * S2 + c] = P;
+            if (c - cb < kLdsChunks) {
+                sm.cm[c - cb] = Wt;
+                sm.cmf[c - cb] = P;
+            }
         }
     }
-    __syncthreads();  // the staging is reused by the next four chunks
+    __syncthreads();  // the staging is reused by the next four chunks (and cm is complete)
 }
 
 // The draw weights of fine chunks [cb, ce) of the row in `st`, as mass_chunk computes them:
@@ -1850,10 +1859,11 @@ __device__ __attribute__((always_inline)) int mass_slice4_q(const KArgs& a, cons
             }
         }
         const int c1 = min(ce, c0 + kWaves);
-        mass_reduce_quad<T, kFilt>(a, st, W, rowp, b, c0, c1, sm, ex);
+        mass_reduce_quad<T, kFilt>(a, st, W, rowp, b, c0, c1, sm, ex, cb);
         if (stop_at >= 0.0) {  // the masses were written before the reduction's last barrier
             double cum = 0.0;
-            for (int c = cb; c < c1; ++c) cum += a.mass[(size_t)b * a.S2 + c];
+            for (int c = cb; c < c1; ++c)
+                cum += c - cb < kLdsChunks ? sm.cm[c - cb] : a.mass[(size_t)b * a.S2 + c];
             if (cum >= stop_at) return c1;
         }
     }
@@ -2185,8 +2195,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
         if (bonus_owner >= -1) {
             if (w == bonus_owner && tid < 64) {
                 const int nc = cw - cb;
-                const size_t mrow = (size_t)b * a.S2 + cb;
-                const double mw = tid < nc ? a.mass[mrow + tid] : 0.0;
+                const double mw = tid < nc ? ms.cm[tid] : 0.0;
                 const Found f = wave_find(mw, bonus_t1, 0.0);
                 const int cl = f.hit >= 0 ? f.hit : f.last;
                 const double bc = f.hit >= 0 ? f.before : f.last_before;
@@ -2213,11 +2222,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_walk(KArgs a, int W, int per, 
             // u * total then locates the chunk, segment and token as k_draw does.  A total
             // that is not positive repeats this with the plain target weights.
             const int nc = ce - cb;
-            const size_t mrow = (size_t)b * a.S2 + cb;
             double tw = 0.0, pw = 0.0, mw = 0.0, mf = 0.0;  // wave 0: lane i holds chunk cb + i
             if (tid < 64) {
-                mw = tid < nc ? a.mass[mrow + tid] : 0.0;
-                mf = tid < nc ? a.massfb[mrow + tid] : 0.0;
+                mw = tid < nc ? ms.cm[tid] : 0.0;
+                mf = tid < nc ? ms.cmf[tid] : 0.0;
                 tw = wave_find(mw, 0.0, 0.0).total;
                 pw = wave_find(mf, 0.0, 0.0).total;
             }
