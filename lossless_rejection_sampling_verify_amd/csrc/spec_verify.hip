@@ -2497,15 +2497,20 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
         const int ch = ts.chosen;
         __syncthreads();
         if (ch < 0) {  // a leaf, or no child accepted: the walk stops at cur
-            if (sampling && tid == 0) {  // the children tried, each token once
+            if (sampling && tid < 64) {  // the children tried, each token once, in child order
+                // wave 0, 64 children at a time: a child is listed when no earlier child has
+                // its token; the listed ones keep their order (ballot prefix)
                 int n = 0;
-                for (int j = 0; j < count; ++j) {
-                    const int t = ts.tok[ts.kids[j]];
-                    bool dup = false;
-                    for (int e = 0; e < n && !dup; ++e) dup = ts.excl[e] == t;
-                    if (!dup) ts.excl[n++] = t;
+                for (int c0 = 0; c0 < count; c0 += 64) {
+                    const int j = c0 + lane;
+                    const int t = j < count ? ts.tok[ts.kids[j]] : -1;
+                    bool first = j < count;
+                    for (int e = 0; e < j && first; ++e) first = ts.tok[ts.kids[e]] != t;
+                    const unsigned long long m = __ballot(first);
+                    if (first) ts.excl[n + __popcll(m & ((1ull << lane) - 1ull))] = t;
+                    n += __popcll(m);
                 }
-                ts.nexcl = n;
+                if (tid == 0) ts.nexcl = n;
             }
             __syncthreads();
             nexcl = sampling ? ts.nexcl : 0;
