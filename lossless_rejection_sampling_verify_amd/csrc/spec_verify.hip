@@ -19,7 +19,7 @@
 // The eager passes read every row and hand over at kernel boundaries; they are selected
 // with spec_options.path = SPEC_PATH_EAGER (the filtered chain always reads every row):
 //   k_rows          streams every target-logit row once from HBM (16-byte non-temporal
-//                   vector loads, kUnroll loads in flight per lane), split over `S`
+//                   buffer loads, two batches of kUnroll per lane in flight), split over `S`
 //                   workgroups per row.  Each workgroup reduces its chunk to one 16-byte
 //                   record: the chunk max, the lowest index attaining it (greedy) and
 //                   sum exp((l - m)/T) relative to the chunk max (sampling).
@@ -2358,8 +2358,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(KArgs a, int sampling, int
     // later, so that what does not need the row statistics overlaps the hand-off).
     auto pass = [&](int step, int node) {
         const T* rowp = logits + ((size_t)b * N + node) * V;
-        if (sampling) {
-            const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
+        if (sampling) {  // cache-allocating: the last row's slice is weighed again
+            const Part r = chunk_record<T, true, false, kWalkUnroll>(rowp, lo, hi, s2, rs);
             cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z),
                             dbl_lo(r.z), xs);
         } else {
@@ -2728,7 +2728,8 @@ __global__ __launch_bounds__(kBlock) void k_mss_walk(KArgs a, int W, int per, un
     // not need the row statistics overlaps the hand-off.
     auto pass = [&](int node) {
         const T* rowp = logits + ((size_t)b * N + node) * V;
-        const Part r = chunk_record<T, true, true, kWalkUnroll>(rowp, lo, hi, s2, rs);
+        // cache-allocating: a node's residual sums and final weights read its row again
+        const Part r = chunk_record<T, true, false, kWalkUnroll>(rowp, lo, hi, s2, rs);
         cluster_publish(slots, step, W, w, tag, __float_as_uint(r.m), dbl_hi(r.z), dbl_lo(r.z), xs);
     };
 
