@@ -94,6 +94,7 @@ def test_chain_rejects_bad_arguments(lib):
     assert _chain(lib, dtype=2) == L.SPEC_ERR_DTYPE
     assert _chain(lib, G=0) == L.SPEC_ERR_SHAPE
     assert _chain(lib, G=65) == L.SPEC_ERR_SHAPE
+    assert _chain(lib, V=1 << 30) == L.SPEC_ERR_SHAPE  # a bf16 row of 2^31 bytes
     assert _chain(lib, q=P + 2) == L.SPEC_ERR_PARAM
     assert _chain(lib, ws_bytes=1024) == L.SPEC_ERR_WORKSPACE
     assert _chain(lib, B=0) == L.SPEC_OK
@@ -116,6 +117,7 @@ def test_tree_rejects_bad_arguments(lib):
     for k in ("logits", "tok", "par", "acc", "out", "nodes", "ws", "coins", "temp"):
         assert _tree(lib, **{k: None}) == L.SPEC_ERR_NULL, k
     assert _tree(lib, mode=2) == L.SPEC_ERR_PARAM
+    assert _tree(lib, V=1 << 29) == L.SPEC_ERR_SHAPE  # an fp32 row of 2^31 bytes
     assert _tree(lib, ts=0.0) == L.SPEC_ERR_PARAM
     assert _tree(lib, ta=-1.0) == L.SPEC_ERR_PARAM
     assert _tree(lib, ta=float("nan")) == L.SPEC_ERR_PARAM
