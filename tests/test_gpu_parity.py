@@ -139,9 +139,19 @@ def near_tie_bound(B):
 NUDGES = (1e-7, 3e-7, 1e-6, 3e-6, 1e-5)
 
 
-def nudge_reaches(run, coins_b, want):
+# The band in weight units.  A final draw whose total weight S is below it has every
+# boundary of its inverse CDF within the band of every coin (1e-6 / S > 1 in coin units):
+# such a draw is rounding residue (a draft equal to the target up to fp32 rounding, or a
+# row whose mass outside the excluded children underflows), and only its token's range
+# can be checked.
+BAND = 1e-6
+
+
+def nudge_reaches(run, coins_b, want, last_free=None):
     """True when the oracle, run on one request (run(coin_matrix) -> list of output tuples)
-    with one of its coins moved by +-d for d in NUDGES, gives the output `want`."""
+    with one of its coins moved by +-d for d in NUDGES, gives the output `want`; or, with
+    last_free(o) (True when output o stops where `want` does, agrees with it up to the
+    final token, and that final draw has total weight below BAND), gives such an output."""
     coins_b = np.asarray(coins_b, np.float64)
     rows = []
     for i in range(len(coins_b)):
@@ -150,7 +160,17 @@ def nudge_reaches(run, coins_b, want):
                 c = coins_b.copy()
                 c[i] = min(1.0, max(2.0 ** -24, c[i] + sgn * d))
                 rows.append(c)
-    return any(o == want for o in run(np.array(rows, np.float32)))
+    outs = run(np.array(rows, np.float32))
+    if any(o == want for o in outs):
+        return True
+    return last_free is not None and any(last_free(o) for o in outs)
+
+
+def _target_row(logits_row, dtype, T):
+    """p = softmax(l / T) in fp64 (the target row of one position or node)."""
+    z = wl.logits_as_f32(logits_row, dtype).astype(np.float64) / float(T)
+    e = np.exp(z - z.max())
+    return e / e.sum()
 
 
 def compare(g, o, keys, margin=None, probs=True, label="", max_near=None, accept_margin=None,
@@ -218,7 +238,38 @@ def chain_recheck(logits, dtype, q, x, coins, T, g):
                                     np.ascontiguousarray(np.broadcast_to(x[b], (n,) + x.shape[1:])),
                                     cs, np.full(n, T[b], np.float32))
             return [_chain_out(r, i) for i in range(n)]
-        return nudge_reaches(run, coins[b], _chain_out(g, b))
+        want = _chain_out(g, b)
+        V = logits.shape[-1]
+
+        def last_free(o):  # stopped at the same k < G, same drafts kept, residual below BAND
+            k = want[0]
+            if o[0] != k or k < 0 or k >= q.shape[1] or o[1:-1] != want[1:-1]:
+                return False
+            if not 0 <= want[-1] < V:
+                return False
+            resid = np.maximum(0.0, _target_row(logits[b, k], dtype, T[b]) -
+                               q[b, k].astype(np.float64)).sum()
+            return resid < BAND
+
+        def residue_stop():
+            # The GPU rejected at k where the oracle accepts whatever the coin (p/q at least
+            # 1, the coin within the band of it: no nudge can reject there), and the residual
+            # at k is rounding residue: the stop is a near-tie and its token only range-checked.
+            k = want[0]
+            if k < 0 or k >= q.shape[1] or not 0 <= want[-1] < V:
+                return False
+            o = run(np.asarray(coins[b], np.float32)[None, :])[0]
+            if o[0] <= k or o[1:1 + k] != want[1:1 + k]:
+                return False
+            pk = _target_row(logits[b, k], dtype, T[b])
+            xk = int(x[b, k])
+            qx = float(q[b, k, xk])
+            if not 0 <= xk < V or not qx > 0.0:
+                return False
+            near = abs(float(coins[b, k]) - pk[xk] / qx) < BAND
+            resid = np.maximum(0.0, pk - q[b, k].astype(np.float64)).sum()
+            return near and resid < BAND
+        return nudge_reaches(run, coins[b], want, last_free) or residue_stop()
     return run_b
 
 
@@ -237,7 +288,21 @@ def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperat
                                    np.full(n, temperature[b], np.float32), D, mode, th_single,
                                    th_acc)
             return [_tree_out(r, i) for i in range(n)]
-        return nudge_reaches(run, coins[b], _tree_out(g, b))
+        want = _tree_out(g, b)
+        V = t.logits.shape[-1]
+
+        def last_free(o):  # same stop and path; the stop node's row outside its children's
+            k = want[0]     # tokens holds less than BAND
+            if mode != oracle.TREE_SAMPLING or o[0] != k or k < 0:
+                return False
+            f = 1 + k  # index of the final token in the tuple
+            if o[:f] != want[:f] or o[f + 1:] != want[f + 1:] or not 0 <= want[f] < V:
+                return False
+            node = want[f + k] if k > 0 else 0  # the last accepted node, else the root
+            excl = {int(tokens[b, c]) for c in range(1, t.N) if parents[b, c] == node}
+            p = _target_row(t.logits[b, node], t.dtype, temperature[b])
+            return p.sum() - sum(p[e] for e in excl if 0 <= e < V) < BAND
+        return nudge_reaches(run, coins[b], want, last_free)
     return run_b
 
 

@@ -14,6 +14,8 @@ their seeds, so a failure names its case and repeats.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -24,6 +26,10 @@ from test_gpu_parity import (check_chain, check_greedy, check_tree, launch,  # n
                              say)
 from test_gpu_mss import check_mss
 from test_gpu_filtered import check as check_filtered
+
+# SPEC_RANDOM_SCALE=k runs k times as many cases per test (new seeds, new shapes); 1 by
+# default.
+_SCALE = max(1, int(os.environ.get("SPEC_RANDOM_SCALE", "1")))
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +61,7 @@ def _chain_opts(rng) -> dict:
     return {"path": "eager", "splits": int(rng.choice([1, 3, 8, 64]))}
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(16 * _SCALE))
 def test_random_chain_and_greedy(i, launch):
     rng = _rng("chain", i)
     B, G, V = int(rng.integers(1, 49)), int(rng.integers(1, 11)), _vocab(rng)
@@ -71,7 +77,7 @@ def test_random_chain_and_greedy(i, launch):
     check_greedy(c, label.replace("chain", "greedy", 1))
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(12 * _SCALE))
 def test_random_tree(i, launch):
     rng = _rng("tree", i)
     B, N = int(rng.integers(1, 17)), int(rng.integers(1, 81))
@@ -102,7 +108,7 @@ def test_random_tree(i, launch):
         check_tree(t, mode, label, max_near=max_near, th_single=th_single, th_acc=th_acc)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(8 * _SCALE))
 def test_random_multi_step_tree(i, launch):
     rng = _rng("mss", i)
     B, N = int(rng.integers(1, 9)), int(rng.integers(1, 41))
@@ -122,7 +128,7 @@ def test_random_multi_step_tree(i, launch):
     check_mss(t, f"random multi-step tree {i}: B={B} N={N} D={D} V={t.V} {dtype} {dict(launch)}")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(8 * _SCALE))
 def test_random_filtered(i):
     rng = _rng("filtered", i)
     B, G, V = int(rng.integers(1, 25)), int(rng.integers(1, 7)), _vocab(rng)
@@ -134,7 +140,7 @@ def test_random_filtered(i):
     check_filtered(c, f"random filtered {i}: B={B} G={G} V={V} {dtype} T={T:.2f}")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(8 * _SCALE))
 def test_random_filtered_extremes(i):
     """Filtered chains at the edges of the kept-token list that the final draw reads: top-k
     at 1, 2, 255 and 256 (the list's limit; ties on bf16 rows can push the kept set past
@@ -159,7 +165,7 @@ def test_random_filtered_extremes(i):
     check_filtered(c, f"extreme filtered {i}: B={B} G={G} V={V} {dtype} T={T} eps={eps}")
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(12 * _SCALE))
 def test_random_chain_extremes(i, launch):
     """Chains at the edges of the input space: logits nearly equal (bf16 ties) or spread
     far apart at a low or high temperature (nearly one-hot rows, underflowing weights),
@@ -189,7 +195,7 @@ def test_random_chain_extremes(i, launch):
     check_greedy(c, label.replace("chain", "greedy", 1))
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(8 * _SCALE))
 def test_random_tree_extremes(i, launch):
     """Trees on nearly uniform (bf16 ties) or nearly one-hot rows, at a very low or high
     temperature, with extreme thresholds; near-ties by construction, as above."""
@@ -215,7 +221,7 @@ def test_random_tree_extremes(i, launch):
         check_tree(t, mode, label, max_near=B, th_single=th_single, th_acc=th_acc)
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(6 * _SCALE))
 def test_random_multi_step_tree_extremes(i, launch):
     """Multi-step trees whose draft rows equal the target (every child accepted, up to
     rounding) or are far from it, on peaked or flat rows."""
