@@ -269,7 +269,27 @@ def chain_recheck(logits, dtype, q, x, coins, T, g):
             near = abs(float(coins[b, k]) - pk[xk] / qx) < BAND
             resid = np.maximum(0.0, pk - q[b, k].astype(np.float64)).sum()
             return near and resid < BAND
-        return nudge_reaches(run, coins[b], want, last_free) or residue_stop()
+        def draw_in_band():
+            # Same stop and prefix as the oracle; the GPU's final token holds, in the oracle's
+            # fp64 weights of that draw, an interval within the band of the coin's target
+            # t = u * S (a coin nudge samples this test; a token of very small weight can fall
+            # between the nudges).
+            k, G = want[0], q.shape[1]
+            if k < 0 or not 0 <= want[-1] < V:
+                return False
+            o = run(np.asarray(coins[b], np.float32)[None, :])[0]
+            if o[0] != k or o[1:-1] != want[1:-1]:
+                return False
+            pk = _target_row(logits[b, k], dtype, T[b])
+            w = pk if k >= G else np.maximum(0.0, pk - q[b, k].astype(np.float64))
+            if not w.sum() > 0.0:
+                w = pk  # the residual without mass: the plain target row
+            cum = np.cumsum(w)
+            y = want[-1]
+            t = float(coins[b, G]) * cum[-1]
+            return bool(w[y] > 0.0 and cum[y] - w[y] - BAND <= t <= cum[y] + BAND)
+        return (nudge_reaches(run, coins[b], want, last_free) or residue_stop() or
+                draw_in_band())
     return run_b
 
 
@@ -302,7 +322,31 @@ def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperat
             excl = {int(tokens[b, c]) for c in range(1, t.N) if parents[b, c] == node}
             p = _target_row(t.logits[b, node], t.dtype, temperature[b])
             return p.sum() - sum(p[e] for e in excl if 0 <= e < V) < BAND
-        return nudge_reaches(run, coins[b], want, last_free)
+
+        def draw_in_band():
+            # Sampling mode, same stop and path as the oracle; the GPU's final token holds, in
+            # the stop node's fp64 row with its children's tokens removed, an interval within
+            # the band of the coin's target t = u * S (the chain's test, on the tree's draw).
+            k = want[0]
+            if mode != oracle.TREE_SAMPLING or k < 0:
+                return False
+            f = 1 + k
+            o = run(np.asarray(coins[b], np.float32)[None, :])[0]
+            if o[:f] != want[:f] or o[f + 1:] != want[f + 1:] or not 0 <= want[f] < V:
+                return False
+            node = want[f + k] if k > 0 else 0
+            p = _target_row(t.logits[b, node], t.dtype, temperature[b])
+            w = p.copy()
+            for c in range(1, t.N):
+                if parents[b, c] == node and 0 <= tokens[b, c] < V:
+                    w[int(tokens[b, c])] = 0.0
+            if not w.sum() > 0.0:
+                w = p
+            cum = np.cumsum(w)
+            y = want[f]
+            u = float(coins[b, D]) * cum[-1]
+            return bool(w[y] > 0.0 and cum[y] - w[y] - BAND <= u <= cum[y] + BAND)
+        return nudge_reaches(run, coins[b], want, last_free) or draw_in_band()
     return run_b
 
 

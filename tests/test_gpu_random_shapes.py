@@ -81,7 +81,7 @@ def test_random_chain_and_greedy(i, launch):
 def test_random_tree(i, launch):
     rng = _rng("tree", i)
     B, N = int(rng.integers(1, 17)), int(rng.integers(1, 81))
-    D = int(rng.integers(1 if N > 1 else 0, min(N - 1, 12) + 1))
+    D = int(rng.integers(1, max(min(N - 1, 12), 1) + 1))  # D >= 1 (a root alone: D = 1)
     kids = int(rng.integers(2, 9))
     V, dtype = _vocab(rng, 40000), _dtype(rng)
     T, sigma = float(rng.uniform(0.3, 2.0)), float(rng.uniform(0.5, 5.0))
@@ -112,7 +112,7 @@ def test_random_tree(i, launch):
 def test_random_multi_step_tree(i, launch):
     rng = _rng("mss", i)
     B, N = int(rng.integers(1, 9)), int(rng.integers(1, 41))
-    D = int(rng.integers(1 if N > 1 else 0, min(N - 1, 8) + 1))
+    D = int(rng.integers(1, max(min(N - 1, 8), 1) + 1))  # D >= 1 (a root alone: D = 1)
     kids = int(rng.integers(2, 7))
     V, dtype = _vocab(rng, 20000), _dtype(rng)
     T, sigma = float(rng.uniform(0.3, 2.0)), float(rng.uniform(0.5, 4.0))
