@@ -80,7 +80,7 @@ def say(msg):
 # ------------------------------------------------------------------------------------
 # runners
 
-def gpu_greedy(logits, dtype, tokens):
+def _gpu_greedy_once(logits, dtype, tokens):
     api = _api()
     acc, out = api.spec_verify_greedy(dev_logits(logits, dtype), dev(tokens.astype(np.int32)),
                                       opts=_opts())
@@ -88,7 +88,7 @@ def gpu_greedy(logits, dtype, tokens):
     return acc.cpu().numpy(), out.cpu().numpy()
 
 
-def gpu_chain(logits, dtype, q, x, coins, T):
+def _gpu_chain_once(logits, dtype, q, x, coins, T):
     api = _api()
     acc, out, probs = api.spec_verify_chain(dev_logits(logits, dtype), dev(q.astype(np.float32)),
                                             dev(x.astype(np.int32)), dev(coins.astype(np.float32)),
@@ -99,7 +99,7 @@ def gpu_chain(logits, dtype, q, x, coins, T):
                 probs=probs.cpu().numpy())
 
 
-def gpu_tree(t, mode, D=None, th_single=1.0, th_acc=1.0, parents=None, tokens=None, coins=None,
+def _gpu_tree_once(t, mode, D=None, th_single=1.0, th_acc=1.0, parents=None, tokens=None, coins=None,
              temperature=None):
     api = _api()
     D = t.D if D is None else D
@@ -116,6 +116,35 @@ def gpu_tree(t, mode, D=None, th_single=1.0, th_acc=1.0, parents=None, tokens=No
     torch.cuda.synchronize()
     return dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
                 accepted_nodes=nodes.cpu().numpy(), probs=probs.cpu().numpy())
+
+
+RETRY = -2  # SPEC_ROW_RETRY: a request whose wait between its workgroups ran out (not verified)
+
+
+def _retrying(call):
+    """call() once; when a request reports SPEC_ROW_RETRY, once more, as the ABI prescribes
+    (the retry is printed), and the second call must verify every request."""
+    r = call()
+    acc = r[0] if isinstance(r, tuple) else r["accept_len"]
+    n = int((np.asarray(acc) == RETRY).sum())
+    if n:
+        say(f"[retry] {n} request(s) reported SPEC_ROW_RETRY; calling again")
+        r = call()
+        acc = r[0] if isinstance(r, tuple) else r["accept_len"]
+        assert not (np.asarray(acc) == RETRY).any(), "SPEC_ROW_RETRY on the second call too"
+    return r
+
+
+def gpu_greedy(*args, **kw):
+    return _retrying(lambda: _gpu_greedy_once(*args, **kw))
+
+
+def gpu_chain(*args, **kw):
+    return _retrying(lambda: _gpu_chain_once(*args, **kw))
+
+
+def gpu_tree(*args, **kw):
+    return _retrying(lambda: _gpu_tree_once(*args, **kw))
 
 
 # ------------------------------------------------------------------------------------
@@ -269,16 +298,13 @@ def chain_recheck(logits, dtype, q, x, coins, T, g):
             near = abs(float(coins[b, k]) - pk[xk] / qx) < BAND
             resid = np.maximum(0.0, pk - q[b, k].astype(np.float64)).sum()
             return near and resid < BAND
-        def draw_in_band():
-            # Same stop and prefix as the oracle; the GPU's final token holds, in the oracle's
-            # fp64 weights of that draw, an interval within the band of the coin's target
-            # t = u * S (a coin nudge samples this test; a token of very small weight can fall
-            # between the nudges).
+        def draw_ok(o, u):
+            # Output o has the GPU's stop and prefix; the GPU's final token holds, in the
+            # oracle's fp64 weights of that draw, an interval within the band of the coin's
+            # target t = u * S (a coin nudge samples this test; a token of very small weight
+            # can fall between the nudges).
             k, G = want[0], q.shape[1]
-            if k < 0 or not 0 <= want[-1] < V:
-                return False
-            o = run(np.asarray(coins[b], np.float32)[None, :])[0]
-            if o[0] != k or o[1:-1] != want[1:-1]:
+            if k < 0 or not 0 <= want[-1] < V or o[0] != k or o[1:-1] != want[1:-1]:
                 return False
             pk = _target_row(logits[b, k], dtype, T[b])
             w = pk if k >= G else np.maximum(0.0, pk - q[b, k].astype(np.float64))
@@ -286,10 +312,51 @@ def chain_recheck(logits, dtype, q, x, coins, T, g):
                 w = pk  # the residual without mass: the plain target row
             cum = np.cumsum(w)
             y = want[-1]
-            t = float(coins[b, G]) * cum[-1]
+            t = u * cum[-1]
             return bool(w[y] > 0.0 and cum[y] - w[y] - BAND <= t <= cum[y] + BAND)
-        return (nudge_reaches(run, coins[b], want, last_free) or residue_stop() or
-                draw_in_band())
+
+        def follow():
+            # Several decisions of one request can lie within the band (drafts equal to the
+            # target with coins pinned near 1), and the GPU's fp32 ratio may take the other
+            # side of each. Walk the oracle toward the GPU's path: at the first position where
+            # the two decide differently, if the coin lies within the band of p/q, move it to
+            # the nearest fp32 value on the GPU's side of p/q, and run again (one move per
+            # position at most). The final draw is then checked as above.
+            G = q.shape[1]
+            c = np.asarray(coins[b], np.float32).copy()
+            kg = want[0]
+            for _ in range(G + 1):
+                o = run(c[None, :])[0]
+                if o == want or last_free(o) or draw_ok(o, float(c[G])):
+                    return True
+                ko = o[0]
+                if ko < 0 or kg < 0 or ko == kg:
+                    return False
+                j = min(ko, kg)
+                if o[1:1 + j] != want[1:1 + j]:
+                    return False
+                pj = _target_row(logits[b, j], dtype, T[b])
+                xj = int(x[b, j])
+                if not 0 <= xj < V or not float(q[b, j, xj]) > 0.0:
+                    return False
+                r = pj[xj] / float(q[b, j, xj])
+                if not abs(float(c[j]) - r) < BAND:
+                    return False
+                if ko < kg:  # the GPU keeps x_j: a coin at or below p/q
+                    f = np.float32(min(r, 1.0))
+                    while float(f) > r:
+                        f = np.nextafter(f, np.float32(0.0))
+                    if float(f) < 2.0 ** -24:
+                        return False
+                else:  # the GPU rejects x_j: a coin above p/q, if there is one
+                    if r >= 1.0:  # none: the stop is rounding residue if its residual is
+                        return bool(np.maximum(0.0, pj - q[b, j].astype(np.float64)).sum() < BAND)
+                    f = np.float32(r)
+                    while float(f) <= r:
+                        f = np.nextafter(f, np.float32(2.0))
+                c[j] = f
+            return False
+        return nudge_reaches(run, coins[b], want, last_free) or residue_stop() or follow()
     return run_b
 
 
@@ -301,11 +368,11 @@ def _tree_out(res, b):
 
 def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperature, g):
     def run_b(b):
-        def run(cs):
+        def run(cs, ths=th_single):
             n = len(cs)
             rep = lambda a: np.ascontiguousarray(np.broadcast_to(a[b], (n,) + a.shape[1:]))
             r = oracle.verify_tree(rep(t.logits), t.dtype, rep(tokens), rep(parents), cs,
-                                   np.full(n, temperature[b], np.float32), D, mode, th_single,
+                                   np.full(n, temperature[b], np.float32), D, mode, ths,
                                    th_acc)
             return [_tree_out(r, i) for i in range(n)]
         want = _tree_out(g, b)
@@ -323,15 +390,15 @@ def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperat
             p = _target_row(t.logits[b, node], t.dtype, temperature[b])
             return p.sum() - sum(p[e] for e in excl if 0 <= e < V) < BAND
 
-        def draw_in_band():
-            # Sampling mode, same stop and path as the oracle; the GPU's final token holds, in
-            # the stop node's fp64 row with its children's tokens removed, an interval within
-            # the band of the coin's target t = u * S (the chain's test, on the tree's draw).
+        def draw_ok(o):
+            # Sampling mode, output o has the GPU's stop and path; the GPU's final token holds,
+            # in the stop node's fp64 row with its children's tokens removed, an interval
+            # within the band of the coin's target t = u * S (the chain's test, on the tree's
+            # draw).
             k = want[0]
             if mode != oracle.TREE_SAMPLING or k < 0:
                 return False
             f = 1 + k
-            o = run(np.asarray(coins[b], np.float32)[None, :])[0]
             if o[:f] != want[:f] or o[f + 1:] != want[f + 1:] or not 0 <= want[f] < V:
                 return False
             node = want[f + k] if k > 0 else 0
@@ -346,7 +413,18 @@ def tree_recheck(t, mode, D, th_single, th_acc, parents, tokens, coins, temperat
             y = want[f]
             u = float(coins[b, D]) * cum[-1]
             return bool(w[y] > 0.0 and cum[y] - w[y] - BAND <= u <= cum[y] + BAND)
-        return nudge_reaches(run, coins[b], want, last_free) or draw_in_band()
+        def threshold_near():
+            # A child's probability within the band of threshold_single: the fp32 test and the
+            # fp64 one may differ, as if the threshold were moved by less than the band.
+            c0 = np.asarray(coins[b], np.float32)[None, :]
+            for d in NUDGES:
+                for sgn in (-1.0, 1.0):
+                    o = run(c0, th_single + sgn * d)[0]
+                    if o == want or last_free(o) or draw_ok(o):
+                        return True
+            return False
+        return (nudge_reaches(run, coins[b], want, last_free) or
+                draw_ok(run(np.asarray(coins[b], np.float32)[None, :])[0]) or threshold_near())
     return run_b
 
 

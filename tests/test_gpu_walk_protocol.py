@@ -19,7 +19,10 @@ from lossless_rejection_sampling_verify_amd import _lib as L
 from lossless_rejection_sampling_verify_amd import workloads as wl
 
 from test_gpu_parity import (_api, compare, dev, dev_logits, launch, say, torch,  # noqa: F401
-                             gpu_chain, gpu_greedy, gpu_tree, chain_cfg, BAND)
+                             chain_cfg, BAND)
+# one call each, no retry: these tests force give-ups and check how they are reported
+from test_gpu_parity import (_gpu_chain_once as gpu_chain, _gpu_greedy_once as gpu_greedy,
+                             _gpu_tree_once as gpu_tree)
 
 pytestmark = pytest.mark.gpu
 
